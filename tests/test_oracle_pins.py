@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against things other than itself: the numbers the
+pages print, finite differences, closed forms and special cases, and torch's
+float64 library routines.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from transformer_lm_step_flat_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_printed.json")
+
+
+def rand_params(cfg, seed, scale=0.3):
+    """General-position parameters (not the training init): every tensor
+    random, LayerNorm gains near 1, non-zero biases, wte pad rows 0."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shp in synth.param_shapes(cfg).items():
+        a = rng.standard_normal(shp) * scale
+        if name in ("ln1w", "ln2w", "lnfw"):
+            a = 1.0 + 0.2 * rng.standard_normal(shp)
+        if name == "wte":
+            a[cfg["V"]:] = 0.0
+        out[name] = a
+    return out
+
+
+TINY_FD = [
+    dict(L=1, C=8, NH=2, T=4, B=2, V=7, maxT=5),
+    dict(L=2, C=12, NH=3, T=5, B=2, V=11, maxT=6, Vp=16),
+]
+
+
+# ------------------------------------------------------------ printed numbers
+
+def test_num_parameters_matches_printed_header(oracle_lib):
+    g = json.load(open(GOLDEN))["model_header"]
+    cfg = dict(maxT=g["max_seq_len"], V=g["vocab_size"], Vp=g["vocab_size"], L=g["num_layers"],
+               NH=g["num_heads"], C=g["channels"])
+    assert oracle_lib.num_parameters(cfg) == g["num_parameters"]
+    # the padded head (Vp = 50304) adds exactly (Vp - V) rows of C
+    cfgp = dict(cfg, Vp=synth.padded_vocab(cfg["V"]))
+    assert cfgp["Vp"] == 50304
+    assert oracle_lib.num_parameters(cfgp) == g["num_parameters"] + (50304 - 50257) * 768
+
+
+def test_num_activations_matches_printed_header(oracle_lib):
+    g = json.load(open(GOLDEN))
+    h = g["model_header"]
+    # B*T from the printed batch counts: floor(train/(B*T)) and val/(B*T)
+    tc = g["dataset_token_counts"]
+    bts = [bt for bt in range(1, 4097)
+           if tc["train_tokens"] // bt == h["train_num_batches"] and tc["val_tokens"] // bt == h["val_num_batches"]]
+    assert bts == [256]
+    cfg = dict(maxT=h["max_seq_len"], V=h["vocab_size"], Vp=h["vocab_size"], L=h["num_layers"],
+               NH=h["num_heads"], C=h["channels"])
+    hits = [(B, 256 // B) for B in (1, 2, 4, 8, 16, 32, 64, 128, 256)
+            if oracle_lib.num_activations(cfg, B, 256 // B) == h["num_activations"]]
+    assert hits == [(4, 64)]
+
+
+def test_gelu_constant_reading_matches_printed_digits():
+    g = json.load(open(GOLDEN))["gelu_macro_constants"]
+    # the printed constant is sqrt(2/pi) = 0.79788456... cut after 7 digits
+    k = math.sqrt(2 / math.pi)
+    assert math.floor(k * 1e7) / 1e7 == float(g["k_printed"])
+    assert abs(k - float(g["k_printed"])) < 1e-7
+    assert float(g["a_printed"]) == 0.044715
+
+
+def test_layout_is_contiguous_and_ordered(oracle_lib):
+    cfg = synth.config("tiny")
+    lay = oracle_lib.param_layout(cfg)
+    assert [n for n, _, _ in lay] == list(synth.PARAM_NAMES)
+    off = 0
+    for name, o, c in lay:
+        assert o == off
+        assert c == int(np.prod(synth.param_shapes(cfg)[name]))
+        off += c
+    assert off == oracle_lib.num_parameters(cfg)
+
+
+# ------------------------------------------------------------ finite differences
+
+@pytest.mark.parametrize("cfgi", range(len(TINY_FD)))
+def test_gradients_match_central_differences_every_element(oracle_lib, cfgi):
+    cfg = synth.config(TINY_FD[cfgi])
+    B, T = cfg["B"], cfg["T"]
+    tensors = rand_params(cfg, 10 + cfgi)
+    params = oracle_lib.pack(cfg, tensors)
+    rng = np.random.default_rng(20 + cfgi)
+    inp = rng.integers(0, cfg["V"], size=(B, T)).astype(np.int32)
+    tgt = rng.integers(0, cfg["V"], size=(B, T)).astype(np.int32)
+    M = oracle_lib.RefModel(cfg, B, T)
+    M.forward(params, inp, tgt)
+    grads = np.zeros_like(params)
+    M.backward(params, grads)
+    h = 1e-5
+    fd = np.empty_like(params)
+    p = params.copy()
+    for i in range(params.size):
+        p[i] = params[i] + h
+        lp = M.forward(p, inp, tgt)
+        p[i] = params[i] - h
+        lm = M.forward(p, inp, tgt)
+        p[i] = params[i]
+        fd[i] = (lp - lm) / (2 * h)
+    for name, off, cnt in oracle_lib.param_layout(cfg):
+        g, f = grads[off:off + cnt], fd[off:off + cnt]
+        scale = max(np.abs(f).max(), 1e-12)
+        assert np.abs(g - f).max() <= 1e-6 * scale + 1e-12, name
+    # pad rows of wte and unused wpe rows take no gradient
+    wte = grads[:cfg["Vp"] * cfg["C"]].reshape(cfg["Vp"], cfg["C"])
+    assert np.all(wte[cfg["V"]:] == 0.0)
+
+
+def test_backward_accumulates(oracle_lib):
+    cfg = synth.config(TINY_FD[0])
+    params = oracle_lib.pack(cfg, rand_params(cfg, 3))
+    rng = np.random.default_rng(4)
+    inp = rng.integers(0, cfg["V"], size=(2, 4)).astype(np.int32)
+    tgt = rng.integers(0, cfg["V"], size=(2, 4)).astype(np.int32)
+    M = oracle_lib.RefModel(cfg, 2, 4)
+    M.forward(params, inp, tgt)
+    g1 = np.zeros_like(params)
+    M.backward(params, g1)
+    g2 = g1.copy()
+    M.backward(params, g2)
+    np.testing.assert_allclose(g2, 2 * g1, rtol=1e-14, atol=0)
+
+
+# ------------------------------------------------------------ torch library routines
+
+@pytest.mark.parametrize("which", ["fd0", "fd1", "tiny"])
+def test_whole_model_matches_torch_float64(oracle_lib, which):
+    import torch
+    from tests import torch_ref
+    cfg = synth.config(TINY_FD[int(which[-1])]) if which.startswith("fd") else synth.config("tiny", B=2, T=16)
+    B, T = cfg["B"], cfg["T"]
+    tensors = rand_params(cfg, 7, scale=0.2)
+    params = oracle_lib.pack(cfg, tensors)
+    rng = np.random.default_rng(8)
+    inp = rng.integers(0, cfg["V"], size=(B, T)).astype(np.int32)
+    tgt = rng.integers(0, cfg["V"], size=(B, T)).astype(np.int32)
+    M = oracle_lib.RefModel(cfg, B, T)
+    loss = M.forward(params, inp, tgt)
+    grads = np.zeros_like(params)
+    M.backward(params, grads)
+
+    P = torch_ref.params_to_torch(tensors)
+    logits, tloss = torch_ref.forward(cfg, P, inp, tgt)
+    tloss.backward()
+    assert abs(loss - tloss.item()) <= 1e-12 * abs(tloss.item())
+    np.testing.assert_allclose(M.get("logits"), logits.detach().numpy().reshape(-1), rtol=0, atol=1e-12)
+    tg = oracle_lib.pack(cfg, {k: v.grad.numpy() for k, v in P.items()})
+    for name, off, cnt in oracle_lib.param_layout(cfg):
+        ref = tg[off:off + cnt]
+        assert np.abs(grads[off:off + cnt] - ref).max() <= 1e-10 * max(np.abs(ref).max(), 1e-30), name
+
+
+def test_layers_match_torch_library(oracle_lib):
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(0)
+    N, C = 37, 24
+    x = rng.standard_normal(N * C) * 3 + 1
+    w = rng.standard_normal(C)
+    b = rng.standard_normal(C)
+    out, mean, rstd = oracle_lib.layernorm_forward(x, w, b, N, C)
+    ref = F.layer_norm(torch.tensor(x).view(N, C), (C,), torch.tensor(w), torch.tensor(b), eps=1e-5)
+    np.testing.assert_allclose(out, ref.numpy().reshape(-1), rtol=0, atol=1e-12)
+    # linear against numpy's matmul
+    K, OC = 19, 23
+    A = rng.standard_normal(N * K)
+    W = rng.standard_normal(OC * K)
+    bias = rng.standard_normal(OC)
+    y = oracle_lib.matmul_forward(A, W, bias, N, K, OC)
+    np.testing.assert_allclose(y, (A.reshape(N, K) @ W.reshape(OC, K).T + bias).reshape(-1), atol=1e-12)
+    y0 = oracle_lib.matmul_forward(A, W, None, N, K, OC)
+    np.testing.assert_allclose(y0, (A.reshape(N, K) @ W.reshape(OC, K).T).reshape(-1), atol=1e-12)
+    # matmul backward against numpy (dinp = dout W, dW = dout^T inp, db = colsum)
+    dout = rng.standard_normal(N * OC)
+    dA, dW, db = np.zeros(N * K), np.zeros(OC * K), np.zeros(OC)
+    oracle_lib.matmul_backward(dA, dW, db, dout, A, W, N, K, OC)
+    D = dout.reshape(N, OC)
+    np.testing.assert_allclose(dA, (D @ W.reshape(OC, K)).reshape(-1), atol=1e-12)
+    np.testing.assert_allclose(dW, (D.T @ A.reshape(N, K)).reshape(-1), atol=1e-12)
+    np.testing.assert_allclose(db, D.sum(0), atol=1e-12)
+    # gelu against torch's tanh-approximate gelu
+    g = np.linspace(-9, 9, 1001)
+    np.testing.assert_allclose(oracle_lib.gelu_forward(g),
+                               F.gelu(torch.tensor(g), approximate="tanh").numpy(), rtol=0, atol=1e-15)
+    # attention against torch's causal scaled-dot-product attention
+    B, T, NH, hd = 2, 9, 3, 4
+    Cc = NH * hd
+    qkv = rng.standard_normal(B * T * 3 * Cc)
+    y, pre, att = oracle_lib.attention_forward(qkv, B, T, Cc, NH)
+    t = torch.tensor(qkv).view(B, T, 3, NH, hd)
+    q, k, v = (t[:, :, i].transpose(1, 2) for i in range(3))
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True).transpose(1, 2).reshape(-1)
+    np.testing.assert_allclose(y, ref.numpy(), atol=1e-12)
+    # softmax cross-entropy against torch.cross_entropy (mean over rows)
+    Nr, V, ld = 13, 29, 32
+    z = rng.standard_normal(Nr * ld) * 4
+    tg = rng.integers(0, V, size=Nr).astype(np.int32)
+    losses, probs = oracle_lib.softmax_crossentropy_forward(z, tg, Nr, V, ld)
+    zt = torch.tensor(z).view(Nr, ld)[:, :V]
+    ref = F.cross_entropy(zt, torch.tensor(tg, dtype=torch.long), reduction="none")
+    np.testing.assert_allclose(losses, ref.numpy(), atol=1e-12)
+    np.testing.assert_allclose(probs.reshape(Nr, V), torch.softmax(zt, -1).numpy(), atol=1e-15)
+
+
+def test_adamw_matches_torch_optimizer(oracle_lib):
+    import torch
+    rng = np.random.default_rng(5)
+    n = 1000
+    p0 = rng.standard_normal(n)
+    gs = [rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 0, n) for _ in range(4)]
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.999, 1e-8, 0.1
+    p, m, v = p0.copy(), np.zeros(n), np.zeros(n)
+    tp = torch.tensor(p0.copy(), requires_grad=True)
+    opt = torch.optim.AdamW([tp], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd)
+    for t, g in enumerate(gs, start=1):
+        oracle_lib.adamw(p, g, m, v, lr, b1, b2, eps, wd, t)
+        tp.grad = torch.tensor(g)
+        opt.step()
+    np.testing.assert_allclose(p, tp.detach().numpy(), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_zero_embeddings_give_uniform_logits_and_ln_v(oracle_lib):
+    for V in (65, 1000, 50257):
+        cfg = synth.config(dict(L=1, C=8, NH=2, T=3, B=2, V=V, maxT=3))
+        tensors = rand_params(cfg, 1)
+        tensors["wte"][:] = 0.0
+        params = oracle_lib.pack(cfg, tensors)
+        rng = np.random.default_rng(2)
+        inp = rng.integers(0, V, size=(2, 3)).astype(np.int32)
+        tgt = rng.integers(0, V, size=(2, 3)).astype(np.int32)
+        M = oracle_lib.RefModel(cfg, 2, 3)
+        loss = M.forward(params, inp, tgt)
+        assert abs(loss - math.log(V)) <= 1e-12 * math.log(V)
+        assert np.all(M.get("logits") == 0.0)
+        g = np.zeros_like(params)
+        M.backward(params, g)
+        onehot = np.zeros((6, V))
+        onehot[np.arange(6), tgt.reshape(-1)] = 1.0
+        np.testing.assert_allclose(M.get("dlogits").reshape(6, V), (1.0 / V - onehot) / 6, rtol=0, atol=1e-15)
+    assert f"{math.log(50257):.6f}" == "10.824905"
+
+
+def test_default_init_loss_near_ln_v(oracle_lib):
+    cfg = synth.config("tiny")
+    params = oracle_lib.pack(cfg, synth.init_params(cfg))
+    inp, tgt = synth.batch(cfg)
+    M = oracle_lib.RefModel(cfg, cfg["B"], cfg["T"])
+    loss = M.forward(params, inp, tgt)
+    expect = math.log(cfg["V"]) + cfg["C"] * 0.02 ** 2 / 2
+    assert abs(loss - expect) <= 0.02 * expect
+    p = M.get("probs").reshape(cfg["B"] * cfg["T"], cfg["V"])
+    np.testing.assert_allclose(p.sum(1), 1.0, atol=1e-12)
+    att = M.get("att").reshape(cfg["L"], cfg["B"], cfg["NH"], cfg["T"], cfg["T"])
+    np.testing.assert_allclose(att.sum(-1), 1.0, atol=1e-12)
+    assert np.all(np.triu(att, 1) == 0.0)
+
+
+def test_layernorm_statistics_before_affine(oracle_lib):
+    rng = np.random.default_rng(9)
+    N, C = 50, 64
+    x = rng.standard_normal((N, C)) * rng.uniform(0.01, 10, (N, 1)) + rng.uniform(-5, 5, (N, 1))
+    x[3] = 2.5  # a constant row
+    out, mean, rstd = oracle_lib.layernorm_forward(x.reshape(-1).copy(), np.ones(C), np.zeros(C), N, C)
+    y = out.reshape(N, C)
+    np.testing.assert_allclose(y.mean(1), 0.0, atol=1e-12)
+    var = x.var(1)
+    np.testing.assert_allclose(y.var(1), var / (var + 1e-5), rtol=1e-10)
+    beta = rng.standard_normal(C)
+    out2, _, _ = oracle_lib.layernorm_forward(x.reshape(-1).copy(), rng.standard_normal(C), beta, N, C)
+    np.testing.assert_array_equal(out2.reshape(N, C)[3], beta)
+
+
+def test_attention_special_cases(oracle_lib):
+    rng = np.random.default_rng(11)
+    B, NH, hd = 2, 2, 4
+    C = NH * hd
+    # T = 1: the output is v itself
+    qkv = rng.standard_normal(B * 1 * 3 * C)
+    y, _, att = oracle_lib.attention_forward(qkv, B, 1, C, NH)
+    np.testing.assert_allclose(y.reshape(B, C), qkv.reshape(B, 3, C)[:, 2], atol=1e-15)
+    # q = 0: uniform weights over the past, output = running mean of v
+    T = 7
+    qkv = rng.standard_normal((B, T, 3, C))
+    qkv[:, :, 0] = 0.0
+    y, _, att = oracle_lib.attention_forward(qkv.reshape(-1).copy(), B, T, C, NH)
+    att = att.reshape(B, NH, T, T)
+    for t in range(T):
+        np.testing.assert_allclose(att[:, :, t, :t + 1], 1.0 / (t + 1), atol=1e-15)
+    run = np.cumsum(qkv[:, :, 2], axis=1) / np.arange(1, T + 1)[None, :, None]
+    np.testing.assert_allclose(y.reshape(B, T, C), run, atol=1e-14)
+
+
+def test_gelu_limits_and_exact_gelu_bound(oracle_lib):
+    from scipy.special import erf
+    x = np.array([0.0, 30.0, -30.0])
+    y = oracle_lib.gelu_forward(x)
+    assert y[0] == 0.0 and abs(y[1] - 30.0) < 1e-12 and abs(y[2]) < 1e-12
+    d = np.zeros(1)
+    oracle_lib.gelu_backward(d, np.zeros(1), np.ones(1))
+    assert abs(d[0] - 0.5) < 1e-15
+    # the tanh form approximates x * Phi(x) to within 1e-3 everywhere
+    g = np.linspace(-8, 8, 4001)
+    exact = 0.5 * g * (1 + erf(g / math.sqrt(2)))
+    assert np.abs(oracle_lib.gelu_forward(g) - exact).max() < 1e-3
+
+
+def test_encoder_backward_all_tokens_equal(oracle_lib):
+    rng = np.random.default_rng(12)
+    B, T, C, V = 3, 5, 6, 9
+    tok = np.full(B * T, 4, dtype=np.int32)
+    dout = rng.standard_normal(B * T * C)
+    dwte, dwpe = np.zeros(V * C), np.zeros(T * C)
+    oracle_lib.encoder_backward(dwte, dwpe, dout, tok, B, T, C)
+    D = dout.reshape(B, T, C)
+    W = dwte.reshape(V, C)
+    np.testing.assert_allclose(W[4], D.sum((0, 1)), atol=1e-14)
+    assert np.all(np.delete(W, 4, axis=0) == 0.0)
+    np.testing.assert_allclose(dwpe.reshape(T, C), D.sum(0), atol=1e-14)
+
+
+def test_adamw_first_step_closed_form(oracle_lib):
+    rng = np.random.default_rng(13)
+    n = 500
+    p0 = rng.standard_normal(n)
+    g = rng.standard_normal(n) * 10.0 ** rng.uniform(-5, 1, n)
+    g[:10] = 0.0
+    p, m, v = p0.copy(), np.zeros(n), np.zeros(n)
+    oracle_lib.adamw(p, g, m, v, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1)
+    np.testing.assert_allclose(p, p0 - 1e-4 * g / (np.abs(g) + 1e-8), rtol=0, atol=1e-15)
+    assert np.all(p[:10] == p0[:10])
+
+
+def test_result_independent_of_thread_count(oracle_lib):
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np, oracle\n"
+        "from transformer_lm_step_flat_amd import synth\n"
+        "cfg = synth.config('tiny', B=2, T=32)\n"
+        "p = oracle.pack(cfg, synth.init_params(cfg))\n"
+        "i, t = synth.batch(cfg)\n"
+        "M = oracle.RefModel(cfg, 2, 32)\n"
+        "l = M.forward(p, i, t); g = np.zeros_like(p); M.backward(p, g)\n"
+        "print(repr(l), float(np.abs(g).sum()).hex(), oracle.num_threads())\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = []
+    for n in ("1", "3"):
+        env = dict(os.environ, OMP_NUM_THREADS=n, PYTHONPATH=root)
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, cwd=root)
+        assert r.returncode == 0, r.stderr
+        outs.append(r.stdout.split())
+    assert outs[0][:2] == outs[1][:2]
+    assert outs[0][2] == "1" and outs[1][2] == "3"
