@@ -1,0 +1,161 @@
+/*
+ * gpt2.h -- C ABI of libgpt2mi: one fp32 GPT-2 training step (forward,
+ * backward, AdamW) on one AMD Instinct MI355X (gfx950), over flat 1-D device
+ * buffers with fixed offsets.
+ *
+ * What the step computes is described on these pages:
+ *  - "OpenAI創始大神手搓千行C代碼訓練GPT，附PyTorch遷移教程" (QbitAI), section
+ *    "手動實現每個層前向/反向傳播": memory is allocated once as one 1-D array
+ *    that every weight and activation points into; the footprint stays
+ *    constant while batches flow through; each layer has a hand-written
+ *    forward and backward, chained into one forward/backward/update loop.
+ *  - "“真男人就應該用 C 編程”！用 1000 行 C 代碼手搓了一個大模型…" (InfoQ): the
+ *    layer list (encoder, layernorm, matmul, self-attention, gelu, residual,
+ *    softmax, cross-entropy), fp32 throughout, int32 token streams, Adam at
+ *    lr 1e-4, and the GPT-2 124M header (1024 / 50257 / 12 / 12 / 768,
+ *    124439808 parameters).
+ *  - "Bản sao ChatGPT dựa trên GPT-2 được triển khai bằng 3000 byte C (2023)"
+ *    (GeekNews), sections "Triển khai các lớp mạng nơ-ron" and
+ *    "Phần lõi Transformer": the layer definitions and the block dataflow,
+ *    including the tied token-embedding head.
+ *
+ * Conventions for every call:
+ *  - Device memory is owned by the caller (allocated once, e.g. through
+ *    PyTorch) and borrowed by the library for the handle's lifetime.  The
+ *    library never allocates or frees device memory.
+ *  - All work is enqueued, in order, on the HIP stream given to gpt2_build;
+ *    calls return before the work finishes unless stated otherwise.
+ *  - Calls return a gpt2_status; on failure gpt2_last_error(model) holds a
+ *    message.  Nothing is printed, no exception crosses the ABI, and the
+ *    process is never exited.
+ *  - All floating-point data is IEEE fp32, row-major; tokens are int32.
+ */
+#ifndef GPT2_MI_H
+#define GPT2_MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GPT2_OK = 0,
+    GPT2_EINVAL = -1,  /* bad argument, shape or configuration                 */
+    GPT2_ERANGE = -2,  /* a token or target outside [0, vocab_size)            */
+    GPT2_ESTATE = -3,  /* call out of order (e.g. backward before forward)     */
+    GPT2_EDEVICE = -4  /* a HIP runtime call or kernel launch failed           */
+} gpt2_status;
+
+/* Model shape.  padded_vocab_size >= vocab_size is the row count of wte and
+ * the column count of the logits (the extra rows/columns are zero and take
+ * no part in the softmax).  channels % num_heads == 0; channels and the head
+ * dimension must be multiples of 4; channels <= 2048. */
+typedef struct {
+    int max_seq_len;       /* rows of the position embedding wpe          */
+    int vocab_size;        /* V                                            */
+    int padded_vocab_size; /* Vp                                           */
+    int num_layers;        /* L                                            */
+    int num_heads;         /* NH                                           */
+    int channels;          /* C                                            */
+} gpt2_config;
+
+/* Element counts of the caller-allocated buffers for one (config, B, T). */
+typedef struct {
+    size_t params;    /* floats; grads, adam_m and adam_v have the same count */
+    size_t acts;      /* floats: saved forward activations and the logits     */
+    size_t work;      /* floats: backward temporaries and reduction scratch   */
+    size_t iwork;     /* int32s: token order and the error flag               */
+} gpt2_sizes;
+
+/* Device pointers (all 256-byte aligned) of the caller-allocated buffers. */
+typedef struct {
+    float *params;    /* [params] the 16 parameter tensors, see gpt2_layout   */
+    float *grads;     /* [params] same offsets as params                      */
+    float *adam_m;    /* [params] AdamW first moment                          */
+    float *adam_v;    /* [params] AdamW second moment                         */
+    float *acts;      /* [acts]                                               */
+    float *work;      /* [work]                                               */
+    int32_t *iwork;   /* [iwork]                                              */
+} gpt2_buffers;
+
+typedef struct gpt2_model gpt2_model; /* opaque handle */
+
+/* Which table gpt2_layout reads. */
+enum { GPT2_PARAMS = 0, GPT2_ACTS = 1 };
+
+/* Buffer sizes for (cfg, B, T).  Host only; B >= 1, 1 <= T <= max_seq_len. */
+gpt2_status gpt2_query_sizes(const gpt2_config *cfg, int B, int T, gpt2_sizes *out);
+
+/* Entry idx of a layout table (host only).  GPT2_PARAMS has 16 entries, in
+ * this order, each stacked over layers where it is per layer:
+ *   wte[Vp][C] wpe[maxT][C] ln1w[L][C] ln1b[L][C] qkvw[L][3C][C] qkvb[L][3C]
+ *   attprojw[L][C][C] attprojb[L][C] ln2w[L][C] ln2b[L][C] fcw[L][4C][C]
+ *   fcb[L][4C] fcprojw[L][C][4C] fcprojb[L][C] lnfw[C] lnfb[C]
+ * (weights are out x in: row o holds the input weights of output o; qkv rows
+ * are q | k | v blocks of C, head h owning columns h*hd..h*hd+hd-1 of each.)
+ * The tensors are packed with no gaps: params = their sum (124439808 for
+ * GPT-2 124M with Vp = V).  GPT2_ACTS lists the named activation tensors in
+ * the acts buffer (offsets are padded to 64 floats):
+ *   encoded[BT][C]; per layer ln1[BT][C] ln1_mean[BT] ln1_rstd[BT]
+ *   qkv[BT][3C] att[B][NH][T][T] atty[BT][C] residual2[BT][C] ln2[BT][C]
+ *   ln2_mean[BT] ln2_rstd[BT] fch[BT][4C] fch_gelu[BT][4C] residual3[BT][C]
+ *   (each stacked over layers); lnf[BT][C] lnf_mean[BT] lnf_rstd[BT]
+ *   logits[BT][Vp] losses[BT] loss[1].
+ * att holds the softmax probabilities: row t is meaningful for u <= t and
+ * zero for t < u < round_up(t+1, 128).  After a forward with targets,
+ * logits holds d(mean loss)/d(logits) instead (columns >= V are zero).
+ * Returns GPT2_EINVAL for idx out of range; *name, *offset, *count may be
+ * NULL.  The returned name is a static string. */
+gpt2_status gpt2_layout(const gpt2_config *cfg, int B, int T, int which, int idx,
+                        const char **name, size_t *offset, size_t *count);
+
+/* Create a handle over caller buffers for fixed (B, T).  If init_params_host
+ * is non-NULL it is copied (params floats, host memory) into dev->params;
+ * otherwise dev->params is left as is.  grads, adam_m and adam_v are set to
+ * zero.  hip_stream is a hipStream_t (NULL = the null stream).  The buffers
+ * must hold at least the counts of gpt2_query_sizes. */
+gpt2_status gpt2_build(const gpt2_config *cfg, int B, int T, const gpt2_buffers *dev,
+                       const float *init_params_host, void *hip_stream, gpt2_model **out);
+
+/* Forward pass over one batch.  inputs and targets are DEVICE pointers to
+ * B*T int32 token ids, row-major [B][T], already resident in HBM (targets
+ * may be NULL: logits only).  With targets, the per-position losses, their
+ * mean, and d(mean loss)/d(logits) (in place of the logits) are produced,
+ * which enables gpt2_backward.  If mean_loss is non-NULL the call waits for
+ * the stream and stores the mean loss (host float); it then also reports
+ * GPT2_ERANGE if any id was outside [0, V).  Ids are checked on the device:
+ * out-of-range ids are clamped for memory safety and raise a flag that the
+ * next waiting call (this one with mean_loss, or gpt2_sync) reports. */
+gpt2_status gpt2_forward(gpt2_model *model, const int32_t *inputs, const int32_t *targets,
+                         float *mean_loss);
+
+/* grads = 0 over the whole parameter buffer. */
+gpt2_status gpt2_zero_grad(gpt2_model *model);
+
+/* Backward pass of the mean loss of the last forward-with-targets:
+ * grads += d(mean loss)/d(params).  GPT2_ESTATE without such a forward. */
+gpt2_status gpt2_backward(gpt2_model *model);
+
+/* AdamW over all params: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+ * theta -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + weight_decay theta).
+ * t is the 1-based step count (GPT2_EINVAL if t < 1). */
+gpt2_status gpt2_update(gpt2_model *model, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, int t);
+
+/* Wait for the stream; GPT2_ERANGE if an out-of-range id was seen since the
+ * last report, GPT2_EDEVICE on a HIP error. */
+gpt2_status gpt2_sync(gpt2_model *model);
+
+/* Release the handle (not the caller's buffers). */
+void gpt2_free(gpt2_model *model);
+
+/* Message of the last failure on this handle ("" if none); with a NULL
+ * handle, of the last failure of a call that had no handle to report on. */
+const char *gpt2_last_error(const gpt2_model *model);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_MI_H */

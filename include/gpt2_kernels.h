@@ -1,0 +1,84 @@
+/*
+ * gpt2_kernels.h -- kernel-level entry points of libgpt2mi, for testing and
+ * timing one step of the training path in isolation, at any shape.  They run
+ * the same kernels, with the same launch planning, that gpt2_forward /
+ * gpt2_backward / gpt2_update run.
+ *
+ * All pointers are DEVICE pointers (fp32 row-major unless noted, int32 ids),
+ * 16-byte aligned; `stream` is a hipStream_t (NULL = null stream).  Calls are
+ * asynchronous and return gpt2_status (GPT2_EINVAL for shapes a kernel cannot
+ * take, GPT2_EDEVICE for a launch failure; message in gpt2_last_error(NULL)).
+ * Sizes must be multiples of 4 where a row is read with 16-byte loads (C, K,
+ * OC, T, Vp).  Where a call needs scratch it takes `work` with the float
+ * count returned by the matching *_work function.
+ */
+#ifndef GPT2_MI_KERNELS_H
+#define GPT2_MI_KERNELS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gpt2.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Linear layer forward (GeekNews 3000-byte GPT-2 page, section on the layers:
+ * matmul, then the bias on every row): out[N][OC] = inp[N][K] W[OC][K]^T (+ bias[OC]). */
+gpt2_status gpt2k_linear_forward(float *out, const float *inp, const float *W, const float *bias, int N, int K,
+                                 int OC, void *stream);
+
+/* Linear layer backward: dinp[N][K] = dout W (overwritten; may be NULL to skip),
+ * dW[OC][K] += dout^T inp, dbias[OC] += column sums of dout (may be NULL). */
+size_t gpt2k_linear_backward_work(int N, int K, int OC);
+gpt2_status gpt2k_linear_backward(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
+                                  const float *W, int N, int K, int OC, float *work, void *stream);
+
+/* LayerNorm over rows of C (mean, biased variance, eps 1e-5, affine). */
+gpt2_status gpt2k_layernorm_forward(float *out, float *mean, float *rstd, const float *inp, const float *w,
+                                    const float *b, int N, int C, void *stream);
+/* dinp = (accumulate ? dinp + : ) LayerNorm input gradient; dw, db += parameter gradients. */
+size_t gpt2k_layernorm_backward_work(int N, int C);
+gpt2_status gpt2k_layernorm_backward(float *dinp, float *dw, float *db, const float *dout, const float *inp,
+                                     const float *w, const float *mean, const float *rstd, int N, int C,
+                                     int accumulate, float *work, void *stream);
+
+/* Causal multi-head attention over qkv[B][T][3C] (q | k | v, heads of C/NH):
+ * att[B][NH][T][T] = softmax probabilities (zero above the diagonal up to the
+ * next multiple of 128 columns), atty[B][T][C] = heads concatenated. */
+gpt2_status gpt2k_attention_forward(float *atty, float *att, const float *qkv, int B, int T, int C, int NH,
+                                    void *stream);
+/* dqkv[B][T][3C] = gradient of the forward above (overwritten) given datty;
+ * work holds B*NH*T*T floats (the score gradient). */
+size_t gpt2k_attention_backward_work(int B, int T, int C, int NH);
+gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const float *qkv, const float *att, int B,
+                                     int T, int C, int NH, float *work, void *stream);
+
+/* tanh-GELU forward / backward (dinp = dout * gelu'(inp)), n % 4 == 0. */
+gpt2_status gpt2k_gelu_forward(float *out, const float *inp, size_t n, void *stream);
+gpt2_status gpt2k_gelu_backward(float *dinp, const float *inp, const float *dout, size_t n, void *stream);
+
+/* Fused softmax cross-entropy over logits[BT][Vp] (first V columns real):
+ * losses[BT], mean loss in loss[0], logits <- (softmax - onehot(target)) / BT. */
+gpt2_status gpt2k_crossentropy(float *logits, float *losses, float *loss, const int32_t *targets, int BT, int V,
+                               int Vp, void *stream);
+
+/* Encoder: out[B][T][C] = wte[ids] + wpe[t].  Backward: dwte[id] += rows of
+ * dout with that id, dwpe[t] += sum over b.  The backward needs the position
+ * order computed by gpt2k_token_order (iwork of BT int32s + 1 flag). */
+gpt2_status gpt2k_encoder_forward(float *out, const int32_t *ids, const float *wte, const float *wpe, int B, int T,
+                                  int C, int V, void *stream);
+gpt2_status gpt2k_token_order(int32_t *order, int32_t *err_flag, const int32_t *ids, const int32_t *targets,
+                              int BT, int V, void *stream);
+gpt2_status gpt2k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *ids,
+                                   const int32_t *order, int B, int T, int C, int V, void *stream);
+
+/* AdamW over n floats (n % 4 == 0), t >= 1; same update as gpt2_update. */
+gpt2_status gpt2k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float beta1,
+                        float beta2, float eps, float weight_decay, int t, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_MI_KERNELS_H */

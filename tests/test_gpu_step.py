@@ -1,0 +1,211 @@
+"""Whole-step parity on the GPU through the C ABI (gpt2_build / gpt2_forward /
+gpt2_zero_grad / gpt2_backward / gpt2_update) against the oracle model.
+
+Bars (fp32 GPU vs float64 oracle, on the same seeded fp32 inputs):
+  loss: |L - L_ref| / |L_ref| <= 1e-5
+  logits (v < V), per row: max|z - z_ref| / max|z_ref| <= 1e-4
+  grads, per tensor: max|g - g_ref| / max|g_ref| <= 2e-3
+  AdamW state m, v, per tensor, normwise <= 2e-3.  The update and the
+  updated parameters, per tensor, normwise <= 2e-3 over the elements whose
+  reference gradient is above fp32 noise (|g_ref| >= 1e-5 max|g_ref|).  The
+  other elements are ill-conditioned at t = 1: AdamW moves each by
+  lr g/(|g| + eps), so rounding noise in a gradient that is zero in exact
+  arithmetic (the key bias: softmax ignores a shift common to a row) becomes a
+  move of up to lr.  For them the check is |theta_1 - theta_ref| <= lr.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from transformer_lm_step_flat_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_LOSS, TOL_LOGITS, TOL_GRAD = 1e-5, 1e-4, 2e-3
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from transformer_lm_step_flat_amd import gpt2
+    gpt2.lib()
+    return gpt2
+
+
+def dev_ids(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32).ravel()).cuda()
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def nrel(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
+
+
+CASES = {
+    "tiny": synth.config("tiny"),
+    # ragged: nothing a multiple of a tile; V = Vp (no padded columns)
+    "ragged": synth.config(dict(L=1, C=48, NH=3, T=20, B=3, V=36, Vp=36, maxT=24)),
+    # one sequence of four tokens; every id the same
+    "degenerate": synth.config(dict(L=2, C=32, NH=2, T=4, B=1, V=11, maxT=4)),
+    "small_b4": synth.config("small", B=4),
+    "hd64": synth.config(dict(L=2, C=128, NH=2, T=132, B=2, V=300, maxT=132, tokens="zipf")),
+}
+
+
+def run_case(g, oracle_lib, cfg, step_seed=0, same_ids=False):
+    B, T = cfg["B"], cfg["T"]
+    tensors = synth.init_params(cfg)
+    inp, tgt = synth.batch(cfg, step=step_seed)
+    if same_ids:
+        inp[:] = 5
+    flat32 = g.pack_params(cfg, tensors, B, T)
+    M = g.Model(cfg, B, T, init_params=flat32)
+    di, dt = dev_ids(inp), dev_ids(tgt)
+    M.forward(di, None)
+    logits = host(M.act("logits")).reshape(B * T, cfg["Vp"])
+    loss = M.forward(di, dt)
+    M.zero_grad()
+    M.backward()
+    grads = host(M.grads)
+    M.update(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, t=1)
+    params1, m1, v1 = host(M.params), host(M.adam_m), host(M.adam_v)
+
+    R = oracle_lib.RefModel(cfg, B, T)
+    p0 = oracle_lib.pack(cfg, tensors)
+    rloss = R.forward(p0, inp, tgt)
+    rlogits = R.get("logits").reshape(B * T, cfg["V"])
+    rgrads = np.zeros_like(p0)
+    R.backward(p0, rgrads)
+    rp, rm, rv = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+    oracle_lib.adamw(rp, rgrads, rm, rv, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1)
+    return dict(M=M, loss=loss, logits=logits, grads=grads, params1=params1, m1=m1, v1=v1, rloss=rloss,
+                rlogits=rlogits, rgrads=rgrads, rp=rp, rm=rm, rv=rv, p0=p0)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_step_matches_oracle(g, oracle_lib, case):
+    cfg = CASES[case]
+    r = run_case(g, oracle_lib, cfg, same_ids=(case == "degenerate"))
+    V = cfg["V"]
+    assert abs(r["loss"] - r["rloss"]) <= TOL_LOSS * abs(r["rloss"]), (r["loss"], r["rloss"])
+    z, zr = r["logits"][:, :V], r["rlogits"]
+    per_row = np.abs(z - zr).max(1) / np.maximum(np.abs(zr).max(1), 1e-30)
+    assert per_row.max() <= TOL_LOGITS
+    if cfg["Vp"] > V:
+        assert np.all(r["logits"][:, V:] == 0.0)
+    for name, off, cnt in oracle_lib.param_layout(cfg):
+        gg, gr = r["grads"][off:off + cnt], r["rgrads"][off:off + cnt]
+        assert nrel(gg, gr) <= TOL_GRAD, name
+        # AdamW state
+        assert nrel(r["m1"][off:off + cnt], r["rm"][off:off + cnt]) <= TOL_GRAD, name
+        assert nrel(r["v1"][off:off + cnt], r["rv"][off:off + cnt]) <= TOL_GRAD, name
+        keep = np.abs(gr) >= 1e-5 * max(np.abs(gr).max(), 1e-30)
+        p1, rp = r["params1"][off:off + cnt], r["rp"][off:off + cnt]
+        if keep.any():
+            du = p1 - r["p0"][off:off + cnt]
+            dur = rp - r["p0"][off:off + cnt]
+            assert nrel(du[keep], dur[keep]) <= TOL_GRAD, name
+            assert np.abs(p1 - rp)[keep].max() <= TOL_GRAD * max(np.abs(rp).max(), 1e-30), name
+        assert np.all(np.abs(p1 - rp)[~keep] <= 1e-4 * (1 + 1e-5)), name
+    # padded rows of wte take no gradient and stay zero
+    C = cfg["C"]
+    wte_g = r["grads"][:cfg["Vp"] * C].reshape(cfg["Vp"], C)
+    assert np.all(wte_g[V:] == 0.0)
+    assert np.all(r["params1"][:cfg["Vp"] * C].reshape(cfg["Vp"], C)[V:] == 0.0)
+    r["M"].close()
+
+
+def test_small_config_loss_curve_matches_oracle(g, oracle_lib):
+    """The small config, 3 consecutive AdamW steps on fresh batches: every
+    step's loss within 1e-5 of the oracle's."""
+    cfg = synth.config("small", B=8)
+    B, T = cfg["B"], cfg["T"]
+    tensors = synth.init_params(cfg)
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, tensors, B, T))
+    R = oracle_lib.RefModel(cfg, B, T)
+    p = oracle_lib.pack(cfg, tensors)
+    m, v = np.zeros_like(p), np.zeros_like(p)
+    for step in range(3):
+        inp, tgt = synth.batch(cfg, step=step)
+        loss = M.forward(dev_ids(inp), dev_ids(tgt))
+        M.zero_grad()
+        M.backward()
+        M.update(lr=1e-4, t=step + 1)
+        rl = R.forward(p, inp, tgt)
+        gr = np.zeros_like(p)
+        R.backward(p, gr)
+        oracle_lib.adamw(p, gr, m, v, 1e-4, 0.9, 0.999, 1e-8, 0.0, step + 1)
+        assert abs(loss - rl) <= TOL_LOSS * abs(rl), (step, loss, rl)
+    M.close()
+
+
+def test_backward_accumulates_and_is_deterministic(g):
+    cfg = CASES["tiny"]
+    B, T = cfg["B"], cfg["T"]
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, synth.init_params(cfg), B, T))
+    inp, tgt = synth.batch(cfg)
+    M.forward(dev_ids(inp), dev_ids(tgt))
+    M.zero_grad()
+    M.backward()
+    g1 = host(M.grads)
+    M.backward()
+    g2 = host(M.grads)
+    assert nrel(g2, 2 * g1) <= 1e-6
+    M.zero_grad()
+    M.backward()
+    assert np.array_equal(host(M.grads), g1)  # bitwise reproducible
+    M.close()
+
+
+def test_errors_are_reported(g):
+    import torch
+    cfg = CASES["tiny"]
+    B, T = cfg["B"], cfg["T"]
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, synth.init_params(cfg), B, T))
+    with pytest.raises(g.Gpt2Error) as e:
+        M.backward()
+    assert e.value.status == g.GPT2_ESTATE
+    inp, tgt = synth.batch(cfg)
+    bad = inp.copy()
+    bad[1, 7] = cfg["V"]
+    with pytest.raises(g.Gpt2Error) as e:
+        M.forward(dev_ids(bad), dev_ids(tgt))
+    assert e.value.status == g.GPT2_ERANGE
+    badt = tgt.copy()
+    badt[0, 0] = -3
+    with pytest.raises(g.Gpt2Error) as e:
+        M.forward(dev_ids(inp), dev_ids(badt))
+    assert e.value.status == g.GPT2_ERANGE
+    # the flag was reported and cleared: a good batch goes through
+    loss = M.forward(dev_ids(inp), dev_ids(tgt))
+    assert math.isfinite(loss)
+    with pytest.raises(g.Gpt2Error) as e:
+        M.update(t=0)
+    assert e.value.status == g.GPT2_EINVAL
+    M.close()
+
+
+def test_zero_embeddings_give_ln_v(g):
+    """wte = 0 makes every logit 0: loss = ln V exactly and dlogits = (1/V - onehot)/BT."""
+    cfg = CASES["tiny"]
+    B, T, V, Vp = cfg["B"], cfg["T"], cfg["V"], cfg["Vp"]
+    t = synth.init_params(cfg)
+    t["wte"][:] = 0.0
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, t, B, T))
+    inp, tgt = synth.batch(cfg)
+    loss = M.forward(dev_ids(inp), dev_ids(tgt))
+    assert abs(loss - math.log(V)) <= 1e-6 * math.log(V)
+    d = host(M.act("logits")).reshape(B * T, Vp)
+    onehot = np.zeros((B * T, V))
+    onehot[np.arange(B * T), tgt.ravel()] = 1
+    assert np.abs(d[:, :V] - (1.0 / V - onehot) / (B * T)).max() < 1e-9
+    M.close()

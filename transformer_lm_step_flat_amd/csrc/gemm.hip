@@ -1,0 +1,287 @@
+// fp32 MFMA GEMM for gfx950.  See gemm.h for the contract.
+//
+// One workgroup = 4 wavefronts (2 x 2) computes a BM x BN tile of C; each
+// wavefront owns a (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA blocks with
+// the accumulators held in registers.  The K loop stages BK = 32 slices of A
+// and B through LDS: while the MFMAs consume the current slice, the next one
+// is already on its way from global memory into registers.
+//
+// K-index assignment inside a slice: v_mfma_f32_32x32x2_f32 takes two k
+// values per instruction, one from each half of the wavefront (lanes 0-31
+// and 32-63).  Lane half h feeds k = h*16 + j for the j-th instruction of the
+// slice, so each lane walks 16 consecutive k: for a K-contiguous operand that
+// is four 16-byte LDS reads per 32 x 32 block per slice.  Any pairing of k to
+// instruction slots gives the same sum, so this only changes rounding order.
+//
+// LDS layouts: a K-contiguous operand is kept [mn][k] with a row pitch of
+// BK + 4 floats (16-byte reads by 8 consecutive lanes hit all 32 banks once);
+// an MN-contiguous operand is kept [k][mn] and read one float per lane along
+// mn (32 consecutive words per half-wave).
+#include "common.h"
+#include "gemm.h"
+
+namespace {
+
+constexpr int GEMM_BK = 32;
+constexpr int GEMM_THREADS = 256;
+
+struct GemmArgs {
+    const float *A, *B;
+    float *C, *C2;
+    const float *bias, *aux;
+    long long lda, ldb, ldc, ldaux;
+    long long sAo, sAi, sBo, sBi, sCo, sCi, sCs;
+    float alpha;
+    int M, N, K;
+    int epi, causal;
+    int nbi, ksplit, kchunk;
+    int tiles_m, tiles_n, group_m;
+};
+
+// Workgroups are handed to the 8 XCDs round-robin by id.  Renumber so that
+// each XCD works on one contiguous run of tiles (which then share operand
+// tiles in that XCD's L2).  The map is a bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    const int X = 8;
+    int q = n / X, r = n % X;
+    int x = bid % X, loc = bid / X;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + loc;
+}
+
+// Tile order: groups of `g` tile-rows walked column by column.
+__device__ __forceinline__ void group_order(int bid, int tiles_m, int tiles_n, int g, int &tm, int &tn) {
+    int width = g * tiles_n;
+    int grp = bid / width;
+    int first = grp * g;
+    int gs = min(tiles_m - first, g);
+    int r = bid - grp * width;
+    tm = first + r % gs;
+    tn = r / gs;
+}
+
+template <int BM, int BN, bool AK, bool BKC>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs p) {
+    constexpr int BK = GEMM_BK;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int KP = BK + 4;  // pitch of a K-contiguous LDS tile
+    constexpr int A_LDS = AK ? BM * KP : BK * BM;
+    constexpr int B_LDS = BKC ? BN * KP : BK * BN;
+    constexpr int A_F4 = BM * BK / 4 / GEMM_THREADS;
+    constexpr int B_F4 = BN * BK / 4 / GEMM_THREADS;
+    static_assert(A_F4 >= 1 && B_F4 >= 1, "tile too small for 256 threads");
+    __shared__ __attribute__((aligned(16))) float As[A_LDS];
+    __shared__ __attribute__((aligned(16))) float Bs[B_LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    int tm, tn;
+    group_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int z = blockIdx.z;
+    const int s = z % p.ksplit, zb = z / p.ksplit;
+    const int zo = zb / p.nbi, zi = zb % p.nbi;
+    const float *__restrict__ A = p.A + zo * p.sAo + zi * p.sAi;
+    const float *__restrict__ B = p.B + zo * p.sBo + zi * p.sBi;
+    float *__restrict__ C = p.C + zo * p.sCo + zi * p.sCi + s * p.sCs;
+
+    const int m0 = tm * BM, n0 = tn * BN;
+    if (p.causal == CAUSAL_SKIP_UPPER && n0 >= m0 + BM) return;
+    int kbeg = s * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
+    if (p.causal == CAUSAL_KEND) kend = min(kend, m0 + BM);
+    if (p.causal == CAUSAL_KSTART) kbeg = max(kbeg, m0);
+
+    floatx16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; i++)
+#pragma unroll
+        for (int j = 0; j < NI; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    floatx4 ra[A_F4], rb[B_F4];
+    const int M = p.M, N = p.N;
+    const long long lda = p.lda, ldb = p.ldb;
+
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_F4; i++) {
+            int f = tid + GEMM_THREADS * i;
+            int gm, gk;
+            if (AK) { gm = m0 + f / (BK / 4); gk = k0 + 4 * (f % (BK / 4)); }
+            else    { gk = k0 + f / (BM / 4); gm = m0 + 4 * (f % (BM / 4)); }
+            if (gm < M && gk < kend)
+                ra[i] = *(const floatx4 *)(AK ? A + gm * lda + gk : A + gk * lda + gm);
+            else
+                ra[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < B_F4; i++) {
+            int f = tid + GEMM_THREADS * i;
+            int gn, gk;
+            if (BKC) { gn = n0 + f / (BK / 4); gk = k0 + 4 * (f % (BK / 4)); }
+            else     { gk = k0 + f / (BN / 4); gn = n0 + 4 * (f % (BN / 4)); }
+            if (gn < N && gk < kend)
+                rb[i] = *(const floatx4 *)(BKC ? B + gn * ldb + gk : B + gk * ldb + gn);
+            else
+                rb[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < A_F4; i++) {
+            int f = tid + GEMM_THREADS * i;
+            if (AK) *(floatx4 *)&As[(f / (BK / 4)) * KP + 4 * (f % (BK / 4))] = ra[i];
+            else    *(floatx4 *)&As[(f / (BM / 4)) * BM + 4 * (f % (BM / 4))] = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_F4; i++) {
+            int f = tid + GEMM_THREADS * i;
+            if (BKC) *(floatx4 *)&Bs[(f / (BK / 4)) * KP + 4 * (f % (BK / 4))] = rb[i];
+            else     *(floatx4 *)&Bs[(f / (BN / 4)) * BN + 4 * (f % (BN / 4))] = rb[i];
+        }
+    };
+
+    if (kbeg < kend) gload(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+        __syncthreads();
+        lstore();
+        __syncthreads();
+        if (k0 + BK < kend) gload(k0 + BK);
+#pragma unroll
+        for (int q = 0; q < BK / 8; q++) {
+            floatx4 a[MI], b[NI];
+#pragma unroll
+            for (int i = 0; i < MI; i++) {
+                const int mm = wm * WM + i * 32 + l32;
+                if (AK) {
+                    a[i] = *(const floatx4 *)&As[mm * KP + h * (BK / 2) + 4 * q];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) a[i][e] = As[(h * (BK / 2) + 4 * q + e) * BM + mm];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NI; j++) {
+                const int nn = wn * WN + j * 32 + l32;
+                if (BKC) {
+                    b[j] = *(const floatx4 *)&Bs[nn * KP + h * (BK / 2) + 4 * q];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) b[j][e] = Bs[(h * (BK / 2) + 4 * q + e) * BN + nn];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+#pragma unroll
+                for (int i = 0; i < MI; i++)
+#pragma unroll
+                    for (int j = 0; j < NI; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and
+    // rows 8*(r/4) + 4*(l/32) + r%4 for its registers r = 0..15.
+    const int epi = p.epi;
+#pragma unroll
+    for (int i = 0; i < MI; i++)
+#pragma unroll
+        for (int j = 0; j < NI; j++) {
+            const int n = n0 + wn * WN + j * 32 + l32;
+            if (n >= N) continue;
+            const float bn = p.bias ? p.bias[n] : 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                if (m >= M) continue;
+                const float v = p.alpha * acc[i][j][r];
+                const long long off = (long long)m * p.ldc + n;
+                switch (epi) {
+                    case EPI_STORE: C[off] = v + bn; break;
+                    case EPI_ACCUM: C[off] += v; break;
+                    case EPI_RESID: C[off] = v + bn + p.aux[(long long)m * p.ldaux + n]; break;
+                    case EPI_GELU: {
+                        const float pre = v + bn;
+                        C[off] = pre;
+                        p.C2[off] = gelu_fwd(pre);
+                        break;
+                    }
+                    case EPI_GELU_BWD: C[off] = v * gelu_grad(p.aux[(long long)m * p.ldaux + n]); break;
+                }
+            }
+        }
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream) {
+    GemmArgs a = a0;
+    a.tiles_m = (d.M + BM - 1) / BM;
+    a.tiles_n = (d.N + BN - 1) / BN;
+    a.group_m = 8;
+    long long nb = (long long)d.nbo * d.nbi * d.ksplit;
+    if (nb > 65535) return hipErrorInvalidValue;
+    dim3 grid(a.tiles_m * a.tiles_n, 1, (unsigned)nb);
+    if (d.a_kcontig && d.b_kcontig)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true>), grid, dim3(GEMM_THREADS), 0, stream, a);
+    else if (d.a_kcontig && !d.b_kcontig)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false>), grid, dim3(GEMM_THREADS), 0, stream, a);
+    else if (!d.a_kcontig && !d.b_kcontig)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false>), grid, dim3(GEMM_THREADS), 0, stream, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
+    if (d.M <= 0 || d.N <= 0 || d.K < 0 || !d.A || !d.B || !d.C) return hipErrorInvalidValue;
+    if (d.ksplit < 1 || d.nbo < 1 || d.nbi < 1) return hipErrorInvalidValue;
+    if (d.ksplit > 1 && d.epi != EPI_STORE) return hipErrorInvalidValue;
+    // 16-byte vector loads: contiguous extents, leading dims and strides in multiples of 4
+    // a K-contiguous operand is read 4 k at a time; an MN-contiguous one row by row
+    if ((d.a_kcontig || d.b_kcontig) && (d.K % 4)) return hipErrorInvalidValue;
+    if ((d.lda % 4) || (d.ldb % 4)) return hipErrorInvalidValue;
+    if (!d.a_kcontig && (d.M % 4)) return hipErrorInvalidValue;
+    if (!d.b_kcontig && (d.N % 4)) return hipErrorInvalidValue;
+    if ((d.sAo % 4) || (d.sAi % 4) || (d.sBo % 4) || (d.sBi % 4)) return hipErrorInvalidValue;
+    if (!aligned16(d.A) || !aligned16(d.B)) return hipErrorInvalidValue;
+    if ((d.epi == EPI_RESID || d.epi == EPI_GELU_BWD) && !d.aux) return hipErrorInvalidValue;
+    if (d.epi == EPI_GELU && !d.C2) return hipErrorInvalidValue;
+
+    GemmArgs a{};
+    a.A = d.A; a.B = d.B; a.C = d.C; a.C2 = d.C2; a.bias = d.bias; a.aux = d.aux;
+    a.lda = d.lda; a.ldb = d.ldb; a.ldc = d.ldc; a.ldaux = d.ldaux;
+    a.sAo = d.sAo; a.sAi = d.sAi; a.sBo = d.sBo; a.sBi = d.sBi; a.sCo = d.sCo; a.sCi = d.sCi;
+    a.sCs = d.sCs;
+    a.alpha = d.alpha;
+    a.M = d.M; a.N = d.N; a.K = d.K;
+    a.epi = d.epi; a.causal = d.causal;
+    a.nbi = d.nbi; a.ksplit = d.ksplit;
+    int kc = (d.K + d.ksplit - 1) / d.ksplit;
+    a.kchunk = (kc + GEMM_BK - 1) / GEMM_BK * GEMM_BK;
+    if (a.kchunk == 0) a.kchunk = GEMM_BK;
+
+    int tile = d.tile;
+    if (tile == 0) {
+        long long batches = (long long)d.nbo * d.nbi * d.ksplit;
+        long long t128 = (long long)((d.M + 127) / 128) * ((d.N + 127) / 128) * batches;
+        long long t64n = (long long)((d.M + 127) / 128) * ((d.N + 63) / 64) * batches;
+        if (d.N <= 64) tile = 2;
+        else if (t128 >= 512) tile = 1;
+        else if (t64n >= 512) tile = 2;
+        else tile = 3;
+    }
+    // causal tiles must fit inside the zero padding written above the diagonal
+    switch (tile) {
+        case 1: return launch_tile<128, 128>(d, a, stream);
+        case 2: return launch_tile<128, 64>(d, a, stream);
+        case 3: return launch_tile<64, 64>(d, a, stream);
+    }
+    return hipErrorInvalidValue;
+}

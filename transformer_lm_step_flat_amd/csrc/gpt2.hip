@@ -1,0 +1,687 @@
+// libgpt2mi: C ABI of the fp32 GPT-2 training step on gfx950 (include/gpt2.h,
+// include/gpt2_kernels.h).  Host side: buffer layout, argument checks, and the
+// ordered launch sequence of forward, backward and AdamW on one HIP stream.
+//
+// The sequence follows the block dataflow of the GeekNews page on the
+// 3000-byte C GPT-2 ("Phần lõi Transformer"): LayerNorm -> qkv linear ->
+// causal attention -> projection + residual -> LayerNorm -> fc linear ->
+// GELU -> projection + residual, then the final LayerNorm and the product
+// with the token-embedding weights; and the QbitAI/InfoQ llm.c articles'
+// scheme of one allocation made up front with every tensor at a fixed offset
+// and a hand-written backward per layer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gpt2.h"
+#include "../../include/gpt2_kernels.h"
+#include "common.h"
+#include "gemm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t ALIGN = 64;  // floats: every tensor offset is a multiple of 256 bytes
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+const char *kParamNames[16] = {"wte",  "wpe",  "ln1w", "ln1b", "qkvw", "qkvb",    "attprojw", "attprojb",
+                               "ln2w", "ln2b", "fcw",  "fcb",  "fcprojw", "fcprojb", "lnfw",  "lnfb"};
+
+enum ActId {
+    A_ENCODED, A_LN1, A_LN1_MEAN, A_LN1_RSTD, A_QKV, A_ATT, A_ATTY, A_RES2, A_LN2, A_LN2_MEAN, A_LN2_RSTD,
+    A_FCH, A_FCH_GELU, A_RES3, A_LNF, A_LNF_MEAN, A_LNF_RSTD, A_LOGITS, A_LOSSES, A_LOSS, NUM_ACTS
+};
+const char *kActNames[NUM_ACTS] = {"encoded", "ln1",      "ln1_mean", "ln1_rstd",  "qkv",      "att",
+                                   "atty",    "residual2", "ln2",     "ln2_mean",  "ln2_rstd", "fch",
+                                   "fch_gelu", "residual3", "lnf",    "lnf_mean",  "lnf_rstd", "logits",
+                                   "losses",  "loss"};
+
+// How a GEMM is launched: tile shape and number of K splits.
+struct Plan {
+    int tile;
+    int ksplit;
+};
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Tile choice: the largest tile that still gives about two workgroups per
+// CU; when even the smallest does not and the caller can take partial
+// products, split K as well.
+Plan plan_gemm(int M, int N, int K, long long batches, bool allow_split) {
+    auto tiles = [&](int bm, int bn) { return ceil_div(M, bm) * ceil_div(N, bn) * batches; };
+    const long long want = 512;
+    Plan p{3, 1};
+    if (N <= 64) {
+        p.tile = tiles(128, 64) >= 256 ? 2 : 3;
+    } else if (tiles(128, 128) >= want) {
+        p.tile = 1;
+    } else if (allow_split && K >= 8192) {
+        p.tile = 1;  // long reductions: keep the large tile and split K
+    } else if (tiles(128, 64) >= want) {
+        p.tile = 2;
+    }
+    if (allow_split) {
+        int bm = p.tile == 3 ? 64 : 128, bn = p.tile == 1 ? 128 : 64;
+        long long t = tiles(bm, bn);
+        if (t < want) {
+            long long ks = ceil_div(want, t);
+            long long kmax = K / 256;
+            if (ks > kmax) ks = kmax;
+            if (ks > 16) ks = 16;
+            if (ks < 1) ks = 1;
+            p.ksplit = (int)ks;
+        }
+    }
+    return p;
+}
+
+struct Layout {
+    int B, T, C, L, NH, V, Vp, maxT, hd;
+    long long BT;
+    size_t poff[16], pcnt[16], nparams;
+    size_t aoff[NUM_ACTS], acnt[NUM_ACTS], nacts;
+    // work buffer
+    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_part, w_splitk, nwork;
+    // int buffer
+    size_t i_tok, i_order, i_err, niwork;
+};
+
+bool config_ok(const gpt2_config *c, int B, int T, std::string *why) {
+    char buf[256];
+    auto fail = [&](const char *m) {
+        if (why) *why = m;
+        return false;
+    };
+    if (!c) return fail("config is NULL");
+    if (c->max_seq_len <= 0 || c->vocab_size <= 0 || c->num_layers <= 0 || c->num_heads <= 0 || c->channels <= 0)
+        return fail("config fields must be positive");
+    if (c->padded_vocab_size < c->vocab_size) return fail("padded_vocab_size < vocab_size");
+    if (c->padded_vocab_size % 4) return fail("padded_vocab_size must be a multiple of 4");
+    if (c->channels % c->num_heads) return fail("channels must be a multiple of num_heads");
+    if (c->channels % 4 || (c->channels / c->num_heads) % 4)
+        return fail("channels and head dimension must be multiples of 4");
+    if (c->channels > 2048) return fail("channels > 2048 is not supported");
+    if (B <= 0 || T <= 0) return fail("B and T must be positive");
+    if (T > c->max_seq_len) return fail("T > max_seq_len");
+    if (T > 1024) return fail("T > 1024 is not supported");
+    if (T % 4) return fail("T must be a multiple of 4");
+    if ((long long)B * T > (1LL << 24)) return fail("B*T too large");
+    snprintf(buf, sizeof buf, "ok");
+    return true;
+}
+
+void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
+    Layout &l = *Lo;
+    l.B = B; l.T = T; l.C = c->channels; l.L = c->num_layers; l.NH = c->num_heads; l.V = c->vocab_size;
+    l.Vp = c->padded_vocab_size; l.maxT = c->max_seq_len; l.hd = l.C / l.NH;
+    l.BT = (long long)B * T;
+    const size_t C = l.C, L = l.L, BT = l.BT, NH = l.NH, TT = (size_t)T * T;
+    size_t n[16] = {(size_t)l.Vp * C, (size_t)l.maxT * C, L * C, L * C, L * 3 * C * C, L * 3 * C, L * C * C, L * C,
+                    L * C, L * C, L * 4 * C * C, L * 4 * C, L * C * 4 * C, L * C, C, C};
+    size_t off = 0;
+    for (int i = 0; i < 16; i++) {
+        l.poff[i] = off;
+        l.pcnt[i] = n[i];
+        off += n[i];
+    }
+    l.nparams = off;
+    size_t a[NUM_ACTS] = {BT * C,      L * BT * C,  L * BT,     L * BT,     L * BT * 3 * C, L * B * NH * TT,
+                          L * BT * C,  L * BT * C,  L * BT * C, L * BT,     L * BT,         L * BT * 4 * C,
+                          L * BT * 4 * C, L * BT * C, BT * C,   BT,         BT,             BT * (size_t)l.Vp,
+                          BT,          1};
+    off = 0;
+    for (int i = 0; i < NUM_ACTS; i++) {
+        l.aoff[i] = off;
+        l.acnt[i] = a[i];
+        off = align_up(off + a[i]);
+    }
+    l.nacts = off;
+
+    off = 0;
+    l.w_dres = off; off = align_up(off + BT * C);
+    l.w_dln = off; off = align_up(off + BT * C);
+    l.w_datty = off; off = align_up(off + BT * C);
+    l.w_dqkv = off; off = align_up(off + BT * 3 * C);
+    l.w_dfch = off; off = align_up(off + BT * 4 * C);
+    l.w_datt = off; off = align_up(off + (size_t)B * NH * TT);
+    size_t part = (size_t)ln_partials((int)BT) * 2 * C;
+    size_t part2 = (size_t)colsum_partials((int)BT) * 4 * C;
+    l.w_part = off; off = align_up(off + (part > part2 ? part : part2));
+    // split-K partial products of the GEMMs that may split (weight gradients, dlnf)
+    size_t sk = 0;
+    auto need = [&](int M, int N, int K) {
+        Plan p = plan_gemm(M, N, K, 1, true);
+        if (p.ksplit > 1 && (size_t)p.ksplit * M * N > sk) sk = (size_t)p.ksplit * M * N;
+    };
+    need((int)(3 * C), (int)C, (int)BT);
+    need((int)C, (int)C, (int)BT);
+    need((int)(4 * C), (int)C, (int)BT);
+    need((int)C, (int)(4 * C), (int)BT);
+    need(l.Vp, (int)C, (int)BT);
+    need((int)BT, (int)C, l.Vp);
+    l.w_splitk = off; off = align_up(off + sk);
+    l.nwork = off;
+    l.i_tok = 0;
+    l.i_order = align_up(BT);
+    l.i_err = l.i_order + align_up(BT);
+    l.niwork = l.i_err + ALIGN;
+}
+
+}  // namespace
+
+struct gpt2_model {
+    Layout lo;
+    gpt2_buffers buf;
+    hipStream_t stream;
+    bool have_targets = false;
+    std::string err;
+};
+
+namespace {
+
+gpt2_status fail(gpt2_model *m, gpt2_status st, const std::string &msg) {
+    if (m) m->err = msg;
+    g_last_error = msg;
+    return st;
+}
+
+#define HIPCK(model, expr)                                                                             \
+    do {                                                                                               \
+        hipError_t e_ = (expr);                                                                        \
+        if (e_ != hipSuccess)                                                                          \
+            return fail(model, GPT2_EDEVICE, std::string(#expr) + ": " + hipGetErrorString(e_));      \
+    } while (0)
+
+// ---------------------------------------------------------------- building blocks
+
+// out[N][OC] = inp[N][K] W^T (+ bias) with an epilogue.
+hipError_t linear_fwd(float *out, const float *inp, const float *W, const float *bias, int N, int K, int OC,
+                      int epi, const float *aux, float *out2, hipStream_t s) {
+    GemmDesc d;
+    d.a_kcontig = true; d.b_kcontig = true;
+    d.M = N; d.N = OC; d.K = K;
+    d.A = inp; d.lda = K; d.B = W; d.ldb = K; d.C = out; d.ldc = OC;
+    d.epi = epi; d.bias = bias; d.aux = aux; d.ldaux = OC; d.C2 = out2;
+    d.tile = plan_gemm(N, OC, K, 1, false).tile;
+    return gemm_launch(d, s);
+}
+
+// dinp[N][K] = dout[N][OC] W[OC][K]  (epilogue EPI_STORE or EPI_GELU_BWD with aux)
+hipError_t linear_bwd_dinp(float *dinp, const float *dout, const float *W, int N, int K, int OC, int epi,
+                           const float *aux, float *splitk, hipStream_t s) {
+    GemmDesc d;
+    d.a_kcontig = true; d.b_kcontig = false;
+    d.M = N; d.N = K; d.K = OC;
+    d.A = dout; d.lda = OC; d.B = W; d.ldb = K; d.C = dinp; d.ldc = K;
+    d.epi = epi; d.aux = aux; d.ldaux = K;
+    Plan p = plan_gemm(N, K, OC, 1, epi == EPI_STORE && splitk != nullptr);
+    d.tile = p.tile;
+    if (p.ksplit > 1) {
+        d.C = splitk; d.ldc = K; d.ksplit = p.ksplit; d.sCs = (long long)N * K;
+        hipError_t e = gemm_launch(d, s);
+        if (e != hipSuccess) return e;
+        return k_sum_partials(dinp, splitk, p.ksplit, (size_t)N * K, false, s);
+    }
+    return gemm_launch(d, s);
+}
+
+// dW[OC][K] += dout[N][OC]^T inp[N][K]
+hipError_t linear_bwd_dw(float *dW, const float *dout, const float *inp, int N, int K, int OC, float *splitk,
+                         hipStream_t s) {
+    GemmDesc d;
+    d.a_kcontig = false; d.b_kcontig = false;
+    d.M = OC; d.N = K; d.K = N;
+    d.A = dout; d.lda = OC; d.B = inp; d.ldb = K; d.C = dW; d.ldc = K;
+    Plan p = plan_gemm(OC, K, N, 1, splitk != nullptr);
+    d.tile = p.tile;
+    if (p.ksplit > 1) {
+        d.epi = EPI_STORE; d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)OC * K;
+        hipError_t e = gemm_launch(d, s);
+        if (e != hipSuccess) return e;
+        return k_sum_partials(dW, splitk, p.ksplit, (size_t)OC * K, true, s);
+    }
+    d.epi = EPI_ACCUM;
+    return gemm_launch(d, s);
+}
+
+// Attention forward over qkv [B][T][3C]: att = softmax(scale Q K^T) (causal), atty = att V.
+hipError_t attention_fwd(float *atty, float *att, const float *qkv, int B, int T, int C, int NH, hipStream_t s) {
+    const int hd = C / NH;
+    const long long C3 = 3LL * C, TT = (long long)T * T;
+    GemmDesc d;
+    d.a_kcontig = true; d.b_kcontig = true;
+    d.M = T; d.N = T; d.K = hd;
+    d.A = qkv; d.lda = C3; d.B = qkv + C; d.ldb = C3; d.C = att; d.ldc = T;
+    d.alpha = 1.0f / sqrtf((float)hd);
+    d.causal = CAUSAL_SKIP_UPPER;
+    d.nbo = B; d.nbi = NH;
+    d.sAo = T * C3; d.sAi = hd; d.sBo = T * C3; d.sBi = hd; d.sCo = NH * TT; d.sCi = TT;
+    d.tile = plan_gemm(T, T, hd, (long long)B * NH, false).tile;
+    hipError_t e = gemm_launch(d, s);
+    if (e != hipSuccess) return e;
+    e = k_attn_softmax_forward(att, (long long)B * NH * T, T, s);
+    if (e != hipSuccess) return e;
+    GemmDesc y;
+    y.a_kcontig = true; y.b_kcontig = false;
+    y.M = T; y.N = hd; y.K = T;
+    y.A = att; y.lda = T; y.B = qkv + 2 * C; y.ldb = C3; y.C = atty; y.ldc = C;
+    y.causal = CAUSAL_KEND;
+    y.nbo = B; y.nbi = NH;
+    y.sAo = NH * TT; y.sAi = TT; y.sBo = T * C3; y.sBi = hd; y.sCo = (long long)T * C; y.sCi = hd;
+    y.tile = plan_gemm(T, hd, T, (long long)B * NH, false).tile;
+    return gemm_launch(y, s);
+}
+
+// Attention backward: dqkv (overwritten) from datty; dscore is B*NH*T*T scratch.
+hipError_t attention_bwd(float *dqkv, float *dscore, const float *datty, const float *qkv, const float *att, int B,
+                         int T, int C, int NH, hipStream_t s) {
+    const int hd = C / NH;
+    const long long C3 = 3LL * C, TT = (long long)T * T;
+    const float scale = 1.0f / sqrtf((float)hd);
+    const long long nb = (long long)B * NH;
+    // dP = dY V^T on the causal tiles
+    GemmDesc d;
+    d.a_kcontig = true; d.b_kcontig = true;
+    d.M = T; d.N = T; d.K = hd;
+    d.A = datty; d.lda = C; d.B = qkv + 2 * C; d.ldb = C3; d.C = dscore; d.ldc = T;
+    d.causal = CAUSAL_SKIP_UPPER;
+    d.nbo = B; d.nbi = NH;
+    d.sAo = (long long)T * C; d.sAi = hd; d.sBo = T * C3; d.sBi = hd; d.sCo = NH * TT; d.sCi = TT;
+    d.tile = plan_gemm(T, T, hd, nb, false).tile;
+    hipError_t e = gemm_launch(d, s);
+    if (e != hipSuccess) return e;
+    // dS = P (dP - rowsum(P dP)), in place
+    e = k_attn_softmax_backward(dscore, att, nb * T, T, s);
+    if (e != hipSuccess) return e;
+    // dQ = scale dS K
+    GemmDesc q;
+    q.a_kcontig = true; q.b_kcontig = false;
+    q.M = T; q.N = hd; q.K = T;
+    q.A = dscore; q.lda = T; q.B = qkv + C; q.ldb = C3; q.C = dqkv; q.ldc = C3;
+    q.alpha = scale; q.causal = CAUSAL_KEND;
+    q.nbo = B; q.nbi = NH;
+    q.sAo = NH * TT; q.sAi = TT; q.sBo = T * C3; q.sBi = hd; q.sCo = T * C3; q.sCi = hd;
+    q.tile = plan_gemm(T, hd, T, nb, false).tile;
+    e = gemm_launch(q, s);
+    if (e != hipSuccess) return e;
+    // dK = scale dS^T Q
+    GemmDesc k = q;
+    k.a_kcontig = false; k.b_kcontig = false;
+    k.B = qkv; k.C = dqkv + C; k.causal = CAUSAL_KSTART;
+    e = gemm_launch(k, s);
+    if (e != hipSuccess) return e;
+    // dV = P^T dY
+    GemmDesc v = k;
+    v.A = att; v.alpha = 1.0f;
+    v.B = datty; v.ldb = C; v.sBo = (long long)T * C; v.sBi = hd;
+    v.C = dqkv + 2 * C;
+    return gemm_launch(v, s);
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+gpt2_status gpt2_query_sizes(const gpt2_config *cfg, int B, int T, gpt2_sizes *out) {
+    std::string why;
+    if (!config_ok(cfg, B, T, &why)) return fail(nullptr, GPT2_EINVAL, why);
+    if (!out) return fail(nullptr, GPT2_EINVAL, "out is NULL");
+    Layout l;
+    make_layout(cfg, B, T, &l);
+    out->params = l.nparams;
+    out->acts = l.nacts;
+    out->work = l.nwork;
+    out->iwork = l.niwork;
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_layout(const gpt2_config *cfg, int B, int T, int which, int idx, const char **name,
+                        size_t *offset, size_t *count) {
+    std::string why;
+    if (!config_ok(cfg, B, T, &why)) return fail(nullptr, GPT2_EINVAL, why);
+    Layout l;
+    make_layout(cfg, B, T, &l);
+    if (which == GPT2_PARAMS && idx >= 0 && idx < 16) {
+        if (name) *name = kParamNames[idx];
+        if (offset) *offset = l.poff[idx];
+        if (count) *count = l.pcnt[idx];
+        return GPT2_OK;
+    }
+    if (which == GPT2_ACTS && idx >= 0 && idx < NUM_ACTS) {
+        if (name) *name = kActNames[idx];
+        if (offset) *offset = l.aoff[idx];
+        if (count) *count = l.acnt[idx];
+        return GPT2_OK;
+    }
+    return fail(nullptr, GPT2_EINVAL, "layout index out of range");
+}
+
+gpt2_status gpt2_build(const gpt2_config *cfg, int B, int T, const gpt2_buffers *dev,
+                       const float *init_params_host, void *hip_stream, gpt2_model **out) {
+    std::string why;
+    if (!out) return fail(nullptr, GPT2_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!config_ok(cfg, B, T, &why)) return fail(nullptr, GPT2_EINVAL, why);
+    if (!dev || !dev->params || !dev->grads || !dev->adam_m || !dev->adam_v || !dev->acts || !dev->work ||
+        !dev->iwork)
+        return fail(nullptr, GPT2_EINVAL, "a device buffer is NULL");
+    const void *ptrs[7] = {dev->params, dev->grads, dev->adam_m, dev->adam_v, dev->acts, dev->work, dev->iwork};
+    for (const void *p : ptrs)
+        if ((uintptr_t)p & 255) return fail(nullptr, GPT2_EINVAL, "device buffers must be 256-byte aligned");
+    gpt2_model *m = new gpt2_model();
+    make_layout(cfg, B, T, &m->lo);
+    m->buf = *dev;
+    m->stream = (hipStream_t)hip_stream;
+    const size_t np = m->lo.nparams;
+    hipError_t e = hipSuccess;
+    if (init_params_host) {
+        e = hipMemcpyAsync(dev->params, init_params_host, np * sizeof(float), hipMemcpyHostToDevice, m->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+    }
+    if (e == hipSuccess) e = k_fill(dev->grads, np, 0.0f, m->stream);
+    if (e == hipSuccess) e = k_fill(dev->adam_m, np, 0.0f, m->stream);
+    if (e == hipSuccess) e = k_fill(dev->adam_v, np, 0.0f, m->stream);
+    if (e == hipSuccess) e = k_fill_i32(dev->iwork, m->lo.niwork, 0, m->stream);
+    if (e != hipSuccess) {
+        std::string msg = std::string("gpt2_build: ") + hipGetErrorString(e);
+        delete m;
+        return fail(nullptr, GPT2_EDEVICE, msg);
+    }
+    *out = m;
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *targets, float *mean_loss) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    if (!inputs) return fail(m, GPT2_EINVAL, "inputs is NULL");
+    if (mean_loss && !targets) return fail(m, GPT2_EINVAL, "mean_loss needs targets");
+    const Layout &l = m->lo;
+    const int B = l.B, T = l.T, C = l.C, NH = l.NH, BT = (int)l.BT;
+    const size_t BTC = (size_t)BT * C;
+    hipStream_t s = m->stream;
+    float *P = m->buf.params, *A = m->buf.acts;
+    int32_t *order = m->buf.iwork + l.i_order, *err = m->buf.iwork + l.i_err;
+    int32_t *tok = m->buf.iwork + l.i_tok;
+    m->have_targets = false;
+
+    // keep this batch's ids for the embedding backward
+    HIPCK(m, hipMemcpyAsync(tok, inputs, sizeof(int32_t) * BT, hipMemcpyDeviceToDevice, s));
+    inputs = tok;
+    HIPCK(m, k_token_prep(inputs, targets, order, err, BT, l.V, s));
+    HIPCK(m, k_encoder_forward(A + l.aoff[A_ENCODED], inputs, P + l.poff[0], P + l.poff[1], B, T, C, l.V, s));
+    for (int li = 0; li < l.L; li++) {
+        const float *res = li == 0 ? A + l.aoff[A_ENCODED] : A + l.aoff[A_RES3] + (li - 1) * BTC;
+        float *ln1 = A + l.aoff[A_LN1] + li * BTC;
+        float *ln1m = A + l.aoff[A_LN1_MEAN] + (size_t)li * BT, *ln1r = A + l.aoff[A_LN1_RSTD] + (size_t)li * BT;
+        float *qkv = A + l.aoff[A_QKV] + li * 3 * BTC;
+        float *att = A + l.aoff[A_ATT] + (size_t)li * B * NH * T * T;
+        float *atty = A + l.aoff[A_ATTY] + li * BTC;
+        float *res2 = A + l.aoff[A_RES2] + li * BTC;
+        float *ln2 = A + l.aoff[A_LN2] + li * BTC;
+        float *ln2m = A + l.aoff[A_LN2_MEAN] + (size_t)li * BT, *ln2r = A + l.aoff[A_LN2_RSTD] + (size_t)li * BT;
+        float *fch = A + l.aoff[A_FCH] + li * 4 * BTC, *fchg = A + l.aoff[A_FCH_GELU] + li * 4 * BTC;
+        float *res3 = A + l.aoff[A_RES3] + li * BTC;
+        const size_t c = C;
+        HIPCK(m, k_layernorm_forward(ln1, ln1m, ln1r, res, P + l.poff[2] + li * c, P + l.poff[3] + li * c, BT, C, s));
+        HIPCK(m, linear_fwd(qkv, ln1, P + l.poff[4] + li * 3 * c * c, P + l.poff[5] + li * 3 * c, BT, C, 3 * C,
+                            EPI_STORE, nullptr, nullptr, s));
+        HIPCK(m, attention_fwd(atty, att, qkv, B, T, C, NH, s));
+        HIPCK(m, linear_fwd(res2, atty, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, BT, C, C, EPI_RESID,
+                            res, nullptr, s));
+        HIPCK(m, k_layernorm_forward(ln2, ln2m, ln2r, res2, P + l.poff[8] + li * c, P + l.poff[9] + li * c, BT, C, s));
+        HIPCK(m, linear_fwd(fch, ln2, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, BT, C, 4 * C,
+                            EPI_GELU, nullptr, fchg, s));
+        HIPCK(m, linear_fwd(res3, fchg, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, BT, 4 * C, C,
+                            EPI_RESID, res2, nullptr, s));
+    }
+    const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
+    float *lnf = A + l.aoff[A_LNF], *logits = A + l.aoff[A_LOGITS];
+    HIPCK(m, k_layernorm_forward(lnf, A + l.aoff[A_LNF_MEAN], A + l.aoff[A_LNF_RSTD], last, P + l.poff[14],
+                                 P + l.poff[15], BT, C, s));
+    HIPCK(m, linear_fwd(logits, lnf, P + l.poff[0], nullptr, BT, C, l.Vp, EPI_STORE, nullptr, nullptr, s));
+    if (targets) {
+        HIPCK(m, k_crossentropy(logits, A + l.aoff[A_LOSSES], targets, BT, l.V, l.Vp, 1.0f / BT, s));
+        HIPCK(m, k_mean(A + l.aoff[A_LOSS], A + l.aoff[A_LOSSES], BT, s));
+        m->have_targets = true;
+    }
+    if (mean_loss) {
+        float h_loss = 0.f;
+        int32_t h_err = 0;
+        HIPCK(m, hipMemcpyAsync(&h_loss, A + l.aoff[A_LOSS], sizeof(float), hipMemcpyDeviceToHost, s));
+        HIPCK(m, hipMemcpyAsync(&h_err, err, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+        HIPCK(m, hipStreamSynchronize(s));
+        *mean_loss = h_loss;
+        if (h_err) {
+            HIPCK(m, k_fill_i32(err, 1, 0, s));
+            return fail(m, GPT2_ERANGE, h_err & 1 ? "an input id is outside [0, vocab_size)"
+                                                  : "a target id is outside [0, vocab_size)");
+        }
+    }
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_zero_grad(gpt2_model *m) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    HIPCK(m, k_fill(m->buf.grads, m->lo.nparams, 0.0f, m->stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_backward(gpt2_model *m) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    if (!m->have_targets) return fail(m, GPT2_ESTATE, "gpt2_backward needs a preceding gpt2_forward with targets");
+    const Layout &l = m->lo;
+    const int B = l.B, T = l.T, C = l.C, NH = l.NH, BT = (int)l.BT;
+    const size_t BTC = (size_t)BT * C, c = C;
+    hipStream_t s = m->stream;
+    float *P = m->buf.params, *G = m->buf.grads, *A = m->buf.acts, *W = m->buf.work;
+    float *dres = W + l.w_dres, *dln = W + l.w_dln, *datty = W + l.w_datty, *dqkv = W + l.w_dqkv;
+    float *dfch = W + l.w_dfch, *dscore = W + l.w_datt, *part = W + l.w_part, *splitk = W + l.w_splitk;
+    const float *dlogits = A + l.aoff[A_LOGITS], *lnf = A + l.aoff[A_LNF];
+
+    // head: dlnf = dlogits wte, dwte += dlogits^T lnf
+    HIPCK(m, linear_bwd_dinp(dln, dlogits, P + l.poff[0], BT, C, l.Vp, EPI_STORE, nullptr, splitk, s));
+    HIPCK(m, linear_bwd_dw(G + l.poff[0], dlogits, lnf, BT, C, l.Vp, splitk, s));
+    const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
+    HIPCK(m, k_layernorm_backward(dres, G + l.poff[14], G + l.poff[15], part, dln, last, P + l.poff[14],
+                                  A + l.aoff[A_LNF_MEAN], A + l.aoff[A_LNF_RSTD], BT, C, false, s));
+    for (int li = l.L - 1; li >= 0; li--) {
+        const float *res = li == 0 ? A + l.aoff[A_ENCODED] : A + l.aoff[A_RES3] + (li - 1) * BTC;
+        const float *ln1 = A + l.aoff[A_LN1] + li * BTC;
+        const float *ln1m = A + l.aoff[A_LN1_MEAN] + (size_t)li * BT, *ln1r = A + l.aoff[A_LN1_RSTD] + (size_t)li * BT;
+        const float *qkv = A + l.aoff[A_QKV] + li * 3 * BTC;
+        const float *att = A + l.aoff[A_ATT] + (size_t)li * B * NH * T * T;
+        const float *atty = A + l.aoff[A_ATTY] + li * BTC;
+        const float *res2 = A + l.aoff[A_RES2] + li * BTC;
+        const float *ln2 = A + l.aoff[A_LN2] + li * BTC;
+        const float *ln2m = A + l.aoff[A_LN2_MEAN] + (size_t)li * BT, *ln2r = A + l.aoff[A_LN2_RSTD] + (size_t)li * BT;
+        const float *fch = A + l.aoff[A_FCH] + li * 4 * BTC, *fchg = A + l.aoff[A_FCH_GELU] + li * 4 * BTC;
+        const float *qkvw = P + l.poff[4] + li * 3 * c * c, *aw = P + l.poff[6] + li * c * c;
+        const float *fw = P + l.poff[10] + li * 4 * c * c, *pw = P + l.poff[12] + li * 4 * c * c;
+
+        // fcproj: dout = dres (gradient of residual3)
+        HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, dres, fchg, BT, 4 * C, C, splitk, s));
+        HIPCK(m, k_colsum_accumulate(G + l.poff[13] + li * c, part, dres, BT, C, C, s));
+        HIPCK(m, linear_bwd_dinp(dfch, dres, pw, BT, 4 * C, C, EPI_GELU_BWD, fch, nullptr, s));
+        // fc
+        HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, dfch, ln2, BT, C, 4 * C, splitk, s));
+        HIPCK(m, k_colsum_accumulate(G + l.poff[11] + li * 4 * c, part, dfch, BT, 4 * C, 4 * C, s));
+        HIPCK(m, linear_bwd_dinp(dln, dfch, fw, BT, C, 4 * C, EPI_STORE, nullptr, nullptr, s));
+        // ln2: dres becomes the gradient of residual2
+        HIPCK(m, k_layernorm_backward(dres, G + l.poff[8] + li * c, G + l.poff[9] + li * c, part, dln, res2,
+                                      P + l.poff[8] + li * c, ln2m, ln2r, BT, C, true, s));
+        // attproj: dout = dres
+        HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, dres, atty, BT, C, C, splitk, s));
+        HIPCK(m, k_colsum_accumulate(G + l.poff[7] + li * c, part, dres, BT, C, C, s));
+        HIPCK(m, linear_bwd_dinp(datty, dres, aw, BT, C, C, EPI_STORE, nullptr, nullptr, s));
+        // attention
+        HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
+        // qkv
+        HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, dqkv, ln1, BT, C, 3 * C, splitk, s));
+        HIPCK(m, k_colsum_accumulate(G + l.poff[5] + li * 3 * c, part, dqkv, BT, 3 * C, 3 * C, s));
+        HIPCK(m, linear_bwd_dinp(dln, dqkv, qkvw, BT, C, 3 * C, EPI_STORE, nullptr, nullptr, s));
+        // ln1: dres becomes the gradient of this layer's input
+        HIPCK(m, k_layernorm_backward(dres, G + l.poff[2] + li * c, G + l.poff[3] + li * c, part, dln, res,
+                                      P + l.poff[2] + li * c, ln1m, ln1r, BT, C, true, s));
+    }
+    HIPCK(m, k_encoder_backward(G + l.poff[0], G + l.poff[1], dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
+                                l.V, s));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_update(gpt2_model *m, float lr, float beta1, float beta2, float eps, float weight_decay, int t) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    if (t < 1) return fail(m, GPT2_EINVAL, "t must be >= 1");
+    double c1 = 1.0 - std::pow((double)beta1, t), c2 = 1.0 - std::pow((double)beta2, t);
+    HIPCK(m, k_adamw(m->buf.params, m->buf.grads, m->buf.adam_m, m->buf.adam_v, m->lo.nparams, lr, beta1, beta2,
+                     eps, weight_decay, (float)c1, (float)c2, m->stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_sync(gpt2_model *m) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    int32_t h_err = 0;
+    HIPCK(m, hipMemcpyAsync(&h_err, m->buf.iwork + m->lo.i_err, sizeof(int32_t), hipMemcpyDeviceToHost, m->stream));
+    HIPCK(m, hipStreamSynchronize(m->stream));
+    if (h_err) {
+        HIPCK(m, k_fill_i32(m->buf.iwork + m->lo.i_err, 1, 0, m->stream));
+        return fail(m, GPT2_ERANGE, "an id was outside [0, vocab_size)");
+    }
+    return GPT2_OK;
+}
+
+void gpt2_free(gpt2_model *m) { delete m; }
+
+const char *gpt2_last_error(const gpt2_model *m) { return m ? m->err.c_str() : g_last_error.c_str(); }
+
+// ====================================================================== kernel-level entry points
+
+#define KCK(expr)                                                                                      \
+    do {                                                                                               \
+        hipError_t e_ = (expr);                                                                        \
+        if (e_ == hipErrorInvalidValue) return fail(nullptr, GPT2_EINVAL, std::string(#expr) + ": invalid shape or alignment"); \
+        if (e_ != hipSuccess) return fail(nullptr, GPT2_EDEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+gpt2_status gpt2k_linear_forward(float *out, const float *inp, const float *W, const float *bias, int N, int K,
+                                 int OC, void *stream) {
+    KCK(linear_fwd(out, inp, W, bias, N, K, OC, EPI_STORE, nullptr, nullptr, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+size_t gpt2k_linear_backward_work(int N, int K, int OC) {
+    size_t sk = 0;
+    Plan p1 = plan_gemm(N, K, OC, 1, true), p2 = plan_gemm(OC, K, N, 1, true);
+    if (p1.ksplit > 1) sk = (size_t)p1.ksplit * N * K;
+    if (p2.ksplit > 1 && (size_t)p2.ksplit * OC * K > sk) sk = (size_t)p2.ksplit * OC * K;
+    size_t part = (size_t)colsum_partials(N) * OC;
+    return align_up(sk) + align_up(part);
+}
+
+gpt2_status gpt2k_linear_backward(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
+                                  const float *W, int N, int K, int OC, float *work, void *stream) {
+    hipStream_t s = (hipStream_t)stream;
+    Plan p1 = plan_gemm(N, K, OC, 1, true), p2 = plan_gemm(OC, K, N, 1, true);
+    size_t sk = 0;
+    if (p1.ksplit > 1) sk = (size_t)p1.ksplit * N * K;
+    if (p2.ksplit > 1 && (size_t)p2.ksplit * OC * K > sk) sk = (size_t)p2.ksplit * OC * K;
+    float *splitk = work, *part = work + align_up(sk);
+    if (dinp) KCK(linear_bwd_dinp(dinp, dout, W, N, K, OC, EPI_STORE, nullptr, splitk, s));
+    KCK(linear_bwd_dw(dW, dout, inp, N, K, OC, splitk, s));
+    if (dbias) KCK(k_colsum_accumulate(dbias, part, dout, N, OC, OC, s));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_layernorm_forward(float *out, float *mean, float *rstd, const float *inp, const float *w,
+                                    const float *b, int N, int C, void *stream) {
+    KCK(k_layernorm_forward(out, mean, rstd, inp, w, b, N, C, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+size_t gpt2k_layernorm_backward_work(int N, int C) { return (size_t)ln_partials(N) * 2 * C; }
+
+gpt2_status gpt2k_layernorm_backward(float *dinp, float *dw, float *db, const float *dout, const float *inp,
+                                     const float *w, const float *mean, const float *rstd, int N, int C,
+                                     int accumulate, float *work, void *stream) {
+    KCK(k_layernorm_backward(dinp, dw, db, work, dout, inp, w, mean, rstd, N, C, accumulate != 0,
+                             (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+static bool attn_shape_ok(int B, int T, int C, int NH) {
+    return B > 0 && T > 0 && T <= 1024 && T % 4 == 0 && NH > 0 && C % NH == 0 && (C / NH) % 4 == 0;
+}
+
+gpt2_status gpt2k_attention_forward(float *atty, float *att, const float *qkv, int B, int T, int C, int NH,
+                                    void *stream) {
+    if (!attn_shape_ok(B, T, C, NH)) return fail(nullptr, GPT2_EINVAL, "attention shape not supported");
+    KCK(attention_fwd(atty, att, qkv, B, T, C, NH, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+size_t gpt2k_attention_backward_work(int B, int T, int C, int NH) {
+    (void)C;
+    return (size_t)B * NH * T * T;
+}
+
+gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const float *qkv, const float *att, int B,
+                                     int T, int C, int NH, float *work, void *stream) {
+    if (!attn_shape_ok(B, T, C, NH)) return fail(nullptr, GPT2_EINVAL, "attention shape not supported");
+    KCK(attention_bwd(dqkv, work, datty, qkv, att, B, T, C, NH, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_gelu_forward(float *out, const float *inp, size_t n, void *stream) {
+    KCK(k_gelu_forward(out, inp, n, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_gelu_backward(float *dinp, const float *inp, const float *dout, size_t n, void *stream) {
+    KCK(k_gelu_backward(dinp, inp, dout, n, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_crossentropy(float *logits, float *losses, float *loss, const int32_t *targets, int BT, int V,
+                               int Vp, void *stream) {
+    if (V <= 0 || Vp < V || BT <= 0) return fail(nullptr, GPT2_EINVAL, "bad crossentropy shape");
+    KCK(k_crossentropy(logits, losses, targets, BT, V, Vp, 1.0f / BT, (hipStream_t)stream));
+    KCK(k_mean(loss, losses, BT, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_encoder_forward(float *out, const int32_t *ids, const float *wte, const float *wpe, int B, int T,
+                                  int C, int V, void *stream) {
+    if (C % 4) return fail(nullptr, GPT2_EINVAL, "C must be a multiple of 4");
+    KCK(k_encoder_forward(out, ids, wte, wpe, B, T, C, V, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_token_order(int32_t *order, int32_t *err_flag, const int32_t *ids, const int32_t *targets,
+                              int BT, int V, void *stream) {
+    KCK(k_token_prep(ids, targets, order, err_flag, BT, V, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *ids,
+                                   const int32_t *order, int B, int T, int C, int V, void *stream) {
+    if (C % 4) return fail(nullptr, GPT2_EINVAL, "C must be a multiple of 4");
+    KCK(k_encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float beta1,
+                        float beta2, float eps, float weight_decay, int t, void *stream) {
+    if (t < 1) return fail(nullptr, GPT2_EINVAL, "t must be >= 1");
+    double c1 = 1.0 - std::pow((double)beta1, t), c2 = 1.0 - std::pow((double)beta2, t);
+    KCK(k_adamw(params, grads, m, v, n, lr, beta1, beta2, eps, weight_decay, (float)c1, (float)c2,
+                (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+}  // extern "C"

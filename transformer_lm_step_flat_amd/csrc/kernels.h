@@ -1,0 +1,59 @@
+// Launchers for the non-GEMM kernels of the training step (gfx950).
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+hipError_t k_fill(float *p, size_t n, float v, hipStream_t s);
+hipError_t k_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s);
+
+// Validate ids (err |= 1 for an input, 2 for a target outside [0, V)) and
+// sort the positions by (input id, position): order[rank] = position.
+hipError_t k_token_prep(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int BT, int V,
+                        hipStream_t s);
+
+// out[b][t][:] = wte[inp[b][t]][:] + wpe[t][:]
+hipError_t k_encoder_forward(float *out, const int32_t *inp, const float *wte, const float *wpe, int B, int T,
+                             int C, int V, hipStream_t s);
+// dwte[id][:] += sum of dout rows of that id (positions in ascending order);
+// dwpe[t][:] += sum_b dout[b][t][:]
+hipError_t k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *inp,
+                              const int32_t *order, int B, int T, int C, int V, hipStream_t s);
+
+hipError_t k_layernorm_forward(float *out, float *mean, float *rstd, const float *inp, const float *w,
+                               const float *b, int N, int C, hipStream_t s);
+// dinp (+)= LayerNorm input gradient; the weight/bias gradients go to
+// `partial` ([ln_partials(N)][2C]) and are then added to dw, db.
+int ln_partials(int N);
+hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partial, const float *dout,
+                                const float *inp, const float *w, const float *mean, const float *rstd, int N,
+                                int C, bool accumulate, hipStream_t s);
+
+// db[n] += sum_r src[r][n]  (src is R x N with leading dim ld); uses partial ([colsum_partials(R)][N])
+int colsum_partials(int R);
+hipError_t k_colsum_accumulate(float *db, float *partial, const float *src, int R, int N, long long ld,
+                               hipStream_t s);
+
+// dst[i] (+)= sum_{p < P} src[p * n + i]   (fixed order)
+hipError_t k_sum_partials(float *dst, const float *src, int P, size_t n, bool accumulate, hipStream_t s);
+
+// Causal row softmax in place over rows of T (T <= 1024): nrows = B*NH*T rows,
+// row index t = row % T.  Writes zeros for t < u < round_up(t+1, CAUSAL_PAD).
+hipError_t k_attn_softmax_forward(float *att, long long nrows, int T, hipStream_t s);
+// dS = P * (dP - sum_u P dP), in place over dP; same zero padding.
+hipError_t k_attn_softmax_backward(float *dp, const float *att, long long nrows, int T, hipStream_t s);
+
+// Fused softmax cross-entropy over logits rows of width Vp (first V real):
+// losses[r] = logsumexp - z[target]; logits <- (softmax - onehot) * dscale
+// (0 in the padded columns).
+hipError_t k_crossentropy(float *logits, float *losses, const int32_t *tgt, int BT, int V, int Vp, float dscale,
+                          hipStream_t s);
+// loss[0] = sum(losses) / n  (fixed order)
+hipError_t k_mean(float *loss, const float *losses, int n, hipStream_t s);
+
+// out = gelu(inp); dinp = dout * gelu'(inp)   (n % 4 == 0)
+hipError_t k_gelu_forward(float *out, const float *inp, size_t n, hipStream_t s);
+hipError_t k_gelu_backward(float *dinp, const float *inp, const float *dout, size_t n, hipStream_t s);
+
+hipError_t k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float b1, float b2,
+                   float eps, float wd, float c1, float c2, hipStream_t s);

@@ -1,0 +1,591 @@
+// Memory-bound kernels of the training step for gfx950: encoder, LayerNorm,
+// causal softmax, fused cross-entropy, reductions, AdamW.  Row kernels give
+// each row to one 64-lane wavefront and reduce across lanes with shuffles;
+// streaming kernels move 16 bytes per lane per access.  Every reduction runs
+// in a fixed order, so results are bitwise reproducible run to run.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+inline unsigned grid_for(size_t n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
+
+__global__ void fill_kernel(float *p, size_t n, float v) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) p[i] = v;
+}
+
+__global__ void fill_i32_kernel(int32_t *p, size_t n, int32_t v) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) p[i] = v;
+}
+
+__device__ __forceinline__ int clamp_id(int id, int V) { return id < 0 ? 0 : (id >= V ? V - 1 : id); }
+
+// Rank of key (id, position) among all BT keys, by counting smaller keys.
+// Keys are distinct (positions differ), so the ranks are a permutation.
+__global__ void token_prep_kernel(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int BT,
+                                  int V) {
+    __shared__ long long keys[256];
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    long long mykey = 0;
+    if (p < BT) {
+        int id = inp[p];
+        int e = 0;
+        if (id < 0 || id >= V) e |= 1;
+        if (tgt) {
+            int tg = tgt[p];
+            if (tg < 0 || tg >= V) e |= 2;
+        }
+        if (e) atomicOr(err, e);
+        mykey = (long long)clamp_id(id, V) * BT + p;
+    }
+    int rank = 0;
+    for (int c0 = 0; c0 < BT; c0 += 256) {
+        __syncthreads();
+        int q = c0 + threadIdx.x;
+        keys[threadIdx.x] = q < BT ? (long long)clamp_id(inp[q], V) * BT + q : 0x7fffffffffffffffLL;
+        __syncthreads();
+        int lim = min(256, BT - c0);
+        for (int j = 0; j < lim; j++) rank += keys[j] < mykey;
+    }
+    if (p < BT) order[rank] = p;
+}
+
+__global__ void encoder_forward_kernel(float *out, const int32_t *inp, const float *wte, const float *wpe, int T,
+                                       int C, int V, long long total4) {
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total4) return;
+    const int C4 = C / 4;
+    long long bt = i / C4;
+    int c4 = (int)(i - bt * C4);
+    int t = (int)(bt % T);
+    int id = clamp_id(inp[bt], V);
+    floatx4 a = ((const floatx4 *)(wte + (long long)id * C))[c4];
+    floatx4 b = ((const floatx4 *)(wpe + (long long)t * C))[c4];
+    ((floatx4 *)(out + bt * C))[c4] = a + b;
+}
+
+// One block per (sorted index, 1024-column chunk).  The block at the first
+// position of a run of equal ids sums the run's rows (ascending position)
+// and adds them to that id's row of dwte; all other blocks exit.
+__global__ void encoder_backward_wte_kernel(float *dwte, const float *dout, const int32_t *inp,
+                                            const int32_t *order, int BT, int C, int V) {
+    const int i = blockIdx.x;
+    const int id = clamp_id(inp[order[i]], V);
+    if (i > 0 && clamp_id(inp[order[i - 1]], V) == id) return;
+    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+    if (c >= C) return;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = i; j < BT; j++) {
+        int pos = order[j];
+        if (clamp_id(inp[pos], V) != id) break;
+        acc += *(const floatx4 *)(dout + (long long)pos * C + c);
+    }
+    floatx4 *dst = (floatx4 *)(dwte + (long long)id * C + c);
+    *dst = *dst + acc;
+}
+
+__global__ void encoder_backward_wpe_kernel(float *dwpe, const float *dout, int B, int T, int C) {
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int C4 = C / 4;
+    if (i >= (long long)T * C4) return;
+    int t = (int)(i / C4), c4 = (int)(i % C4);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < B; b++) acc += ((const floatx4 *)(dout + ((long long)b * T + t) * C))[c4];
+    floatx4 *dst = (floatx4 *)(dwpe + (long long)t * C) + c4;
+    *dst = *dst + acc;
+}
+
+// LayerNorm forward: one wavefront per row, the row held in registers
+// (NV float4 per lane, C <= 256 * NV).
+template <int NV>
+__global__ __launch_bounds__(256) void layernorm_forward_kernel(float *out, float *mean, float *rstd,
+                                                                const float *inp, const float *w,
+                                                                const float *b, int N, int C) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N) return;
+    const int C4 = C / 4;
+    const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
+    floatx4 v[NV];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        int k = lane + 64 * i;
+        v[i] = k < C4 ? x[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+        sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    }
+    const float m = wave_sum(sum) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        int k = lane + 64 * i;
+        if (k < C4) {
+            floatx4 d = v[i] - m;
+            ss += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+        }
+    }
+    const float rs = rsqrtf(wave_sum(ss) / C + 1e-5f);
+    floatx4 *o = (floatx4 *)(out + (long long)row * C);
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        int k = lane + 64 * i;
+        if (k < C4) {
+            floatx4 g = ((const floatx4 *)w)[k], bb = ((const floatx4 *)b)[k];
+            o[k] = (v[i] - m) * rs * g + bb;
+        }
+    }
+    if (lane == 0) {
+        mean[row] = m;
+        rstd[row] = rs;
+    }
+}
+
+constexpr int LN_BWD_ROWS = 16;  // rows per block (4 per wavefront)
+
+// LayerNorm backward.  Block b handles rows [16b, 16b+16); each wavefront
+// four of them, one at a time.  dx (+)= rstd (g - mean(g) - xhat mean(g xhat))
+// with g = dy * w.  Per-column sums of dy*xhat and dy are kept per lane,
+// combined over the 4 wavefronts in a fixed order and written as the
+// block's partial row [dw(C) | db(C)].
+template <int NV>
+__global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, float *partial, const float *dout,
+                                                                 const float *inp, const float *w,
+                                                                 const float *mean, const float *rstd, int N,
+                                                                 int C, int accumulate) {
+    extern __shared__ float lds[];  // [4][2C]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int C4 = C / 4;
+    floatx4 dwacc[NV], dbacc[NV], wv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        int k = lane + 64 * i;
+        dwacc[i] = dbacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        wv[i] = k < C4 ? ((const floatx4 *)w)[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int rr = 0; rr < LN_BWD_ROWS / 4; rr++) {
+        const int row = blockIdx.x * LN_BWD_ROWS + rr * 4 + wave;
+        if (row >= N) break;
+        const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
+        const floatx4 *dy = (const floatx4 *)(dout + (long long)row * C);
+        const float mu = mean[row], rs = rstd[row];
+        floatx4 xh[NV], g[NV], d[NV];
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            int k = lane + 64 * i;
+            if (k < C4) {
+                xh[i] = (x[k] - mu) * rs;
+                d[i] = dy[k];
+                g[i] = d[i] * wv[i];
+                sg += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
+                floatx4 gx = g[i] * xh[i];
+                sgx += (gx[0] + gx[1]) + (gx[2] + gx[3]);
+                dwacc[i] += d[i] * xh[i];
+                dbacc[i] += d[i];
+            }
+        }
+        const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+        floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            int k = lane + 64 * i;
+            if (k < C4) {
+                floatx4 val = rs * (g[i] - mg - xh[i] * mgx);
+                dx[k] = accumulate ? dx[k] + val : val;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        int k = lane + 64 * i;
+        if (k < C4) {
+            *(floatx4 *)&lds[wave * 2 * C + 4 * k] = dwacc[i];
+            *(floatx4 *)&lds[wave * 2 * C + C + 4 * k] = dbacc[i];
+        }
+    }
+    __syncthreads();
+    float *out = partial + (long long)blockIdx.x * 2 * C;
+    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x)
+        out[c] = ((lds[c] + lds[2 * C + c]) + lds[4 * C + c]) + lds[6 * C + c];
+}
+
+constexpr int COLSUM_ROWS = 128;  // rows per partial
+
+// Partial column sums: block (x, y) sums rows [128y, 128y+128) of 64 columns;
+// wavefront w takes rows w, w+4, ...; the four are combined in fixed order.
+__global__ __launch_bounds__(256) void colsum_partial_kernel(float *partial, const float *src, int R, int N,
+                                                             long long ld) {
+    __shared__ float lds[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.x * 64 + lane;
+    const int r0 = blockIdx.y * COLSUM_ROWS;
+    float acc = 0.f;
+    if (n < N) {
+        int r1 = min(R, r0 + COLSUM_ROWS);
+        for (int r = r0 + wave; r < r1; r += 4) acc += src[(long long)r * ld + n];
+    }
+    lds[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && n < N)
+        partial[(long long)blockIdx.y * N + n] = ((lds[0][lane] + lds[1][lane]) + lds[2][lane]) + lds[3][lane];
+}
+
+// dst[i] (+)= sum_p src[p*ld + i]: 32 columns x 8 partial groups per block;
+// group g sums p = g, g+8, ...; the 8 group sums are added in fixed order.
+__global__ __launch_bounds__(256) void sum_partials_kernel(float *dst, const float *src, int P, size_t n,
+                                                           size_t ld, int accumulate) {
+    __shared__ float lds[8][32];
+    const int col = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const size_t i = (size_t)blockIdx.x * 32 + col;
+    float acc = 0.f;
+    if (i < n)
+        for (int p = g; p < P; p += 8) acc += src[(size_t)p * ld + i];
+    lds[g][col] = acc;
+    __syncthreads();
+    if (g == 0 && i < n) {
+        float s = lds[0][col];
+#pragma unroll
+        for (int k = 1; k < 8; k++) s += lds[k][col];
+        dst[i] = accumulate ? dst[i] + s : s;
+    }
+}
+
+constexpr int SM_NV = 16;  // up to 1024 columns per row in registers
+
+__device__ __forceinline__ int pad_end(int t, int T) {
+    int e = (t / CAUSAL_PAD + 1) * CAUSAL_PAD;
+    return e < T ? e : T;
+}
+
+// Causal softmax of one row per wavefront, in place.
+__global__ __launch_bounds__(256) void attn_softmax_forward_kernel(float *att, long long nrows, int T) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= nrows) return;
+    const int t = (int)(row % T);
+    float *r = att + row * T;
+    float x[SM_NV];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < SM_NV; i++) {
+        int u = lane + 64 * i;
+        x[i] = u <= t ? r[u] : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+    }
+    mx = wave_max(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < SM_NV; i++) {
+        int u = lane + 64 * i;
+        x[i] = u <= t ? __expf(x[i] - mx) : 0.f;
+        sum += x[i];
+    }
+    const float inv = 1.0f / wave_sum(sum);
+    const int e = pad_end(t, T);
+#pragma unroll
+    for (int i = 0; i < SM_NV; i++) {
+        int u = lane + 64 * i;
+        if (u < e) r[u] = x[i] * inv;
+    }
+}
+
+// dS[t][u] = P[t][u] (dP[t][u] - sum_u' P[t][u'] dP[t][u']) for u <= t, in place over dP.
+__global__ __launch_bounds__(256) void attn_softmax_backward_kernel(float *dp, const float *att, long long nrows,
+                                                                    int T) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= nrows) return;
+    const int t = (int)(row % T);
+    float *d = dp + row * T;
+    const float *pr = att + row * T;
+    float pv[SM_NV], dv[SM_NV];
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < SM_NV; i++) {
+        int u = lane + 64 * i;
+        pv[i] = u <= t ? pr[u] : 0.f;
+        dv[i] = u <= t ? d[u] : 0.f;
+        dot += pv[i] * dv[i];
+    }
+    dot = wave_sum(dot);
+    const int e = pad_end(t, T);
+#pragma unroll
+    for (int i = 0; i < SM_NV; i++) {
+        int u = lane + 64 * i;
+        if (u < e) d[u] = pv[i] * (dv[i] - dot);
+    }
+}
+
+__device__ __forceinline__ void online_combine(float &m, float &s, float m2, float s2) {
+    float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+    m = mn;
+}
+
+// Fused softmax cross-entropy, one 256-thread block per row.  Pass 1: running
+// (max, sum of exp) per thread over the V real columns, combined across the
+// block.  Pass 2: overwrite the row with (p - onehot) * dscale.
+__global__ __launch_bounds__(256) void crossentropy_kernel(float *logits, float *losses, const int32_t *tgt,
+                                                           int V, int Vp, float dscale) {
+    __shared__ float sm[4], ss[4];
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float *z = logits + (long long)row * Vp;
+    float m = -INFINITY, s = 0.f;
+    for (int v4 = threadIdx.x; v4 * 4 < V; v4 += 256) {
+        floatx4 x = ((const floatx4 *)z)[v4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            if (v4 * 4 + e < V) {
+                float xe = x[e];
+                if (xe > m) {
+                    s = s * __expf(m - xe) + 1.0f;
+                    m = xe;
+                } else {
+                    s += __expf(xe - m);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
+        online_combine(m, s, m2, s2);
+    }
+    if (lane == 0) {
+        sm[wave] = m;
+        ss[wave] = s;
+    }
+    __syncthreads();
+    m = sm[0];
+    s = ss[0];
+    for (int w = 1; w < 4; w++) online_combine(m, s, sm[w], ss[w]);
+    const float lse = m + __logf(s);
+    const int y = clamp_id(tgt[row], V);
+    if (threadIdx.x == 0) losses[row] = lse - z[y];
+    __syncthreads();  // z[y] is read above before any thread overwrites it
+    for (int v4 = threadIdx.x; v4 * 4 < Vp; v4 += 256) {
+        floatx4 x = ((const floatx4 *)z)[v4];
+        floatx4 o;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            int v = v4 * 4 + e;
+            o[e] = v < V ? (__expf(x[e] - lse) - (v == y ? 1.0f : 0.0f)) * dscale : 0.0f;
+        }
+        ((floatx4 *)z)[v4] = o;
+    }
+}
+
+__global__ __launch_bounds__(256) void mean_kernel(float *loss, const float *losses, int n) {
+    __shared__ float part[256];
+    float acc = 0.f;
+    for (int i = threadIdx.x; i < n; i += 256) acc += losses[i];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = part[0] / n;
+}
+
+__global__ __launch_bounds__(256) void gelu_forward_kernel(floatx4 *out, const floatx4 *inp, size_t n4) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    floatx4 x = inp[i], y;
+#pragma unroll
+    for (int e = 0; e < 4; e++) y[e] = gelu_fwd(x[e]);
+    out[i] = y;
+}
+
+__global__ __launch_bounds__(256) void gelu_backward_kernel(floatx4 *dinp, const floatx4 *inp, const floatx4 *dout,
+                                                            size_t n4) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    floatx4 x = inp[i], d = dout[i], y;
+#pragma unroll
+    for (int e = 0; e < 4; e++) y[e] = d[e] * gelu_grad(x[e]);
+    dinp[i] = y;
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(floatx4 *params, const floatx4 *grads, floatx4 *m, floatx4 *v,
+                                                    size_t n4, float lr, float b1, float b2, float eps, float wd,
+                                                    float inv_c1, float inv_c2) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n4; i += stride) {
+        floatx4 g = grads[i], mm = m[i], vv = v[i], p = params[i];
+        mm = b1 * mm + (1.0f - b1) * g;
+        vv = b2 * vv + (1.0f - b2) * g * g;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float mhat = mm[e] * inv_c1, vhat = vv[e] * inv_c2;
+            p[e] -= lr * (mhat / (sqrtf(vhat) + eps) + wd * p[e]);
+        }
+        m[i] = mm;
+        v[i] = vv;
+        params[i] = p;
+    }
+}
+
+}  // namespace
+
+hipError_t k_fill(float *p, size_t n, float v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    unsigned g = grid_for(n, 256);
+    if (g > 16384) g = 16384;
+    hipLaunchKernelGGL(fill_kernel, dim3(g), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t k_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    unsigned g = grid_for(n, 256);
+    if (g > 16384) g = 16384;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(g), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t k_token_prep(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int BT, int V,
+                        hipStream_t s) {
+    hipLaunchKernelGGL(token_prep_kernel, dim3(grid_for(BT, 256)), dim3(256), 0, s, inp, tgt, order, err, BT, V);
+    return hipGetLastError();
+}
+
+hipError_t k_encoder_forward(float *out, const int32_t *inp, const float *wte, const float *wpe, int B, int T,
+                             int C, int V, hipStream_t s) {
+    long long total4 = (long long)B * T * (C / 4);
+    hipLaunchKernelGGL(encoder_forward_kernel, dim3(grid_for(total4, 256)), dim3(256), 0, s, out, inp, wte, wpe,
+                       T, C, V, total4);
+    return hipGetLastError();
+}
+
+hipError_t k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *inp,
+                              const int32_t *order, int B, int T, int C, int V, hipStream_t s) {
+    const int BT = B * T;
+    hipLaunchKernelGGL(encoder_backward_wte_kernel, dim3(BT, grid_for(C, 1024)), dim3(256), 0, s, dwte, dout, inp,
+                       order, BT, C, V);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(encoder_backward_wpe_kernel, dim3(grid_for((size_t)T * (C / 4), 256)), dim3(256), 0, s,
+                       dwpe, dout, B, T, C);
+    return hipGetLastError();
+}
+
+#define LN_DISPATCH(NVV, KER, ...)                                                            \
+    switch (NVV) {                                                                              \
+        case 1: hipLaunchKernelGGL(KER<1>, __VA_ARGS__); break;                               \
+        case 2: hipLaunchKernelGGL(KER<2>, __VA_ARGS__); break;                               \
+        case 3: hipLaunchKernelGGL(KER<3>, __VA_ARGS__); break;                               \
+        case 4: hipLaunchKernelGGL(KER<4>, __VA_ARGS__); break;                               \
+        case 5: hipLaunchKernelGGL(KER<5>, __VA_ARGS__); break;                               \
+        case 6: hipLaunchKernelGGL(KER<6>, __VA_ARGS__); break;                               \
+        case 7: hipLaunchKernelGGL(KER<7>, __VA_ARGS__); break;                               \
+        case 8: hipLaunchKernelGGL(KER<8>, __VA_ARGS__); break;                               \
+        default: return hipErrorInvalidValue;                                                   \
+    }
+
+hipError_t k_layernorm_forward(float *out, float *mean, float *rstd, const float *inp, const float *w,
+                               const float *b, int N, int C, hipStream_t s) {
+    if (C % 4 || C > 2048) return hipErrorInvalidValue;
+    int nv = (C / 4 + 63) / 64;
+    LN_DISPATCH(nv, layernorm_forward_kernel, dim3(grid_for(N, 4)), dim3(256), 0, s, out, mean, rstd, inp, w, b, N,
+                C);
+    return hipGetLastError();
+}
+
+int ln_partials(int N) { return (N + LN_BWD_ROWS - 1) / LN_BWD_ROWS; }
+
+hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partial, const float *dout,
+                                const float *inp, const float *w, const float *mean, const float *rstd, int N,
+                                int C, bool accumulate, hipStream_t s) {
+    if (C % 4 || C > 2048) return hipErrorInvalidValue;
+    int nv = (C / 4 + 63) / 64;
+    int P = ln_partials(N);
+    size_t lds = (size_t)4 * 2 * C * sizeof(float);
+    LN_DISPATCH(nv, layernorm_backward_kernel, dim3(P), dim3(256), lds, s, dinp, partial, dout, inp, w, mean, rstd,
+                N, C, accumulate ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // partial rows are [dw | db]: sum each half into its own tensor
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(C, 32)), dim3(256), 0, s, dw, (const float *)partial, P,
+                       (size_t)C, (size_t)2 * C, 1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(C, 32)), dim3(256), 0, s, db,
+                       (const float *)(partial + C), P, (size_t)C, (size_t)2 * C, 1);
+    return hipGetLastError();
+}
+
+int colsum_partials(int R) { return (R + COLSUM_ROWS - 1) / COLSUM_ROWS; }
+
+hipError_t k_colsum_accumulate(float *db, float *partial, const float *src, int R, int N, long long ld,
+                               hipStream_t s) {
+    int P = colsum_partials(R);
+    hipLaunchKernelGGL(colsum_partial_kernel, dim3(grid_for(N, 64), P), dim3(256), 0, s, partial, src, R, N, ld);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(N, 32)), dim3(256), 0, s, db, (const float *)partial, P,
+                       (size_t)N, (size_t)N, 1);
+    return hipGetLastError();
+}
+
+hipError_t k_sum_partials(float *dst, const float *src, int P, size_t n, bool accumulate, hipStream_t s) {
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(n, 32)), dim3(256), 0, s, dst, src, P, n, n,
+                       accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t k_attn_softmax_forward(float *att, long long nrows, int T, hipStream_t s) {
+    if (T > 64 * SM_NV) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_softmax_forward_kernel, dim3(grid_for(nrows, 4)), dim3(256), 0, s, att, nrows, T);
+    return hipGetLastError();
+}
+
+hipError_t k_attn_softmax_backward(float *dp, const float *att, long long nrows, int T, hipStream_t s) {
+    if (T > 64 * SM_NV) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_softmax_backward_kernel, dim3(grid_for(nrows, 4)), dim3(256), 0, s, dp, att, nrows, T);
+    return hipGetLastError();
+}
+
+hipError_t k_crossentropy(float *logits, float *losses, const int32_t *tgt, int BT, int V, int Vp, float dscale,
+                          hipStream_t s) {
+    if (Vp % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(crossentropy_kernel, dim3(BT), dim3(256), 0, s, logits, losses, tgt, V, Vp, dscale);
+    return hipGetLastError();
+}
+
+hipError_t k_mean(float *loss, const float *losses, int n, hipStream_t s) {
+    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, loss, losses, n);
+    return hipGetLastError();
+}
+
+hipError_t k_gelu_forward(float *out, const float *inp, size_t n, hipStream_t s) {
+    if (n % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gelu_forward_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, (floatx4 *)out,
+                       (const floatx4 *)inp, n / 4);
+    return hipGetLastError();
+}
+
+hipError_t k_gelu_backward(float *dinp, const float *inp, const float *dout, size_t n, hipStream_t s) {
+    if (n % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gelu_backward_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, (floatx4 *)dinp,
+                       (const floatx4 *)inp, (const floatx4 *)dout, n / 4);
+    return hipGetLastError();
+}
+
+hipError_t k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float b1, float b2,
+                   float eps, float wd, float c1, float c2, hipStream_t s) {
+    if (n % 4) return hipErrorInvalidValue;
+    size_t n4 = n / 4;
+    unsigned g = grid_for(n4, 256);
+    if (g > 8192) g = 8192;
+    hipLaunchKernelGGL(adamw_kernel, dim3(g), dim3(256), 0, s, (floatx4 *)params, (const floatx4 *)grads,
+                       (floatx4 *)m, (floatx4 *)v, n4, lr, b1, b2, eps, wd, 1.0f / c1, 1.0f / c2);
+    return hipGetLastError();
+}

@@ -1,0 +1,318 @@
+"""ctypes binding of ``libgpt2mi.so`` (include/gpt2.h, include/gpt2_kernels.h).
+
+Argument marshalling only: PyTorch provides device memory (``torch.empty``)
+and the current HIP stream; every step of the training path runs in the
+library's HIP kernels.  There is no fallback: if the library is missing or
+no GPU is present, construction raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # noqa: F401  (loads the HIP runtime the library then shares)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
+
+GPT2_OK, GPT2_EINVAL, GPT2_ERANGE, GPT2_ESTATE, GPT2_EDEVICE = 0, -1, -2, -3, -4
+GPT2_PARAMS, GPT2_ACTS = 0, 1
+_STATUS = {0: "GPT2_OK", -1: "GPT2_EINVAL", -2: "GPT2_ERANGE", -3: "GPT2_ESTATE", -4: "GPT2_EDEVICE"}
+
+
+class Gpt2Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("max_seq_len", ctypes.c_int), ("vocab_size", ctypes.c_int), ("padded_vocab_size", ctypes.c_int),
+                ("num_layers", ctypes.c_int), ("num_heads", ctypes.c_int), ("channels", ctypes.c_int)]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("params", ctypes.c_size_t), ("acts", ctypes.c_size_t), ("work", ctypes.c_size_t),
+                ("iwork", ctypes.c_size_t)]
+
+
+class Buffers(ctypes.Structure):
+    _fields_ = [("params", ctypes.c_void_p), ("grads", ctypes.c_void_p), ("adam_m", ctypes.c_void_p),
+                ("adam_v", ctypes.c_void_p), ("acts", ctypes.c_void_p), ("work", ctypes.c_void_p),
+                ("iwork", ctypes.c_void_p)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+
+_SIGS = {
+    "gpt2_query_sizes": [ctypes.POINTER(Config), _I, _I, ctypes.POINTER(Sizes)],
+    "gpt2_layout": [ctypes.POINTER(Config), _I, _I, _I, _I, ctypes.POINTER(ctypes.c_char_p),
+                    ctypes.POINTER(_Z), ctypes.POINTER(_Z)],
+    "gpt2_build": [ctypes.POINTER(Config), _I, _I, ctypes.POINTER(Buffers), _P, _P, ctypes.POINTER(_P)],
+    "gpt2_forward": [_P, _P, _P, ctypes.POINTER(_F)],
+    "gpt2_zero_grad": [_P],
+    "gpt2_backward": [_P],
+    "gpt2_update": [_P, _F, _F, _F, _F, _F, _I],
+    "gpt2_sync": [_P],
+    "gpt2k_linear_forward": [_P, _P, _P, _P, _I, _I, _I, _P],
+    "gpt2k_linear_backward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
+    "gpt2k_layernorm_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _P],
+    "gpt2k_layernorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
+    "gpt2k_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P],
+    "gpt2k_attention_backward": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
+    "gpt2k_gelu_forward": [_P, _P, _Z, _P],
+    "gpt2k_gelu_backward": [_P, _P, _P, _Z, _P],
+    "gpt2k_crossentropy": [_P, _P, _P, _P, _I, _I, _I, _P],
+    "gpt2k_encoder_forward": [_P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "gpt2k_token_order": [_P, _P, _P, _P, _I, _I, _P],
+    "gpt2k_encoder_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "gpt2k_adamw": [_P, _P, _P, _P, _Z, _F, _F, _F, _F, _F, _I, _P],
+}
+_SIZE_FNS = {
+    "gpt2k_linear_backward_work": [_I, _I, _I],
+    "gpt2k_layernorm_backward_work": [_I, _I],
+    "gpt2k_attention_backward_work": [_I, _I, _I, _I],
+}
+
+# every symbol the headers declare
+EXPORTS = sorted(list(_SIGS) + list(_SIZE_FNS) + ["gpt2_free", "gpt2_last_error"])
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m transformer_lm_step_flat_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        for name, args in _SIZE_FNS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = _Z
+        L.gpt2_free.argtypes = [_P]
+        L.gpt2_free.restype = None
+        L.gpt2_last_error.argtypes = [_P]
+        L.gpt2_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, handle=None):
+    if status != GPT2_OK:
+        msg = lib().gpt2_last_error(handle)
+        raise Gpt2Error(status, (msg or b"").decode())
+
+
+def make_config(cfg) -> Config:
+    return Config(cfg["maxT"], cfg["V"], cfg["Vp"], cfg["L"], cfg["NH"], cfg["C"])
+
+
+def query_sizes(cfg, B: int, T: int) -> Sizes:
+    s = Sizes()
+    c = make_config(cfg)
+    _check(lib().gpt2_query_sizes(ctypes.byref(c), B, T, ctypes.byref(s)))
+    return s
+
+
+def layout(cfg, B: int, T: int, which: int):
+    """[(name, offset, count)] of the parameter (GPT2_PARAMS) or activation table."""
+    c = make_config(cfg)
+    out = []
+    i = 0
+    while True:
+        nm, off, cnt = ctypes.c_char_p(), _Z(), _Z()
+        st = lib().gpt2_layout(ctypes.byref(c), B, T, which, i, ctypes.byref(nm), ctypes.byref(off),
+                               ctypes.byref(cnt))
+        if st != GPT2_OK:
+            break
+        out.append((nm.value.decode(), off.value, cnt.value))
+        i += 1
+    return out
+
+
+def pack_params(cfg, tensors: dict, B: int = 1, T: int = 4) -> np.ndarray:
+    """Named host tensors -> one flat float32 array in the library's layout."""
+    lay = layout(cfg, B, T, GPT2_PARAMS)
+    n = lay[-1][1] + lay[-1][2]
+    flat = np.empty(n, dtype=np.float32)
+    for name, off, cnt in lay:
+        a = np.asarray(tensors[name], dtype=np.float32).reshape(-1)
+        if a.size != cnt:
+            raise ValueError(f"{name}: {a.size} values, layout wants {cnt}")
+        flat[off:off + cnt] = a
+    return flat
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Model:
+    """One fp32 GPT-2 at fixed (B, T) over flat device buffers owned here
+    (allocated once with torch.empty) and borrowed by the library."""
+
+    def __init__(self, cfg, B: int, T: int, init_params: np.ndarray | None = None, device: str = "cuda"):
+        if not torch.cuda.is_available():
+            raise RuntimeError("libgpt2mi needs a GPU; none is visible")
+        self.cfg, self.B, self.T = dict(cfg), B, T
+        self.device = torch.device(device)
+        sz = query_sizes(cfg, B, T)
+        self.sizes = sz
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.params = torch.empty(sz.params, **f32)
+        self.grads = torch.empty(sz.params, **f32)
+        self.adam_m = torch.empty(sz.params, **f32)
+        self.adam_v = torch.empty(sz.params, **f32)
+        self.acts = torch.empty(sz.acts, **f32)
+        self.work = torch.empty(max(sz.work, 1), **f32)
+        self.iwork = torch.empty(sz.iwork, dtype=torch.int32, device=self.device)
+        self._bufs = Buffers(*[t.data_ptr() for t in (self.params, self.grads, self.adam_m, self.adam_v, self.acts,
+                                                       self.work, self.iwork)])
+        host = None
+        if init_params is not None:
+            host = np.ascontiguousarray(init_params, dtype=np.float32)
+            if host.size != sz.params:
+                raise ValueError(f"init_params has {host.size} values, the layout has {sz.params}")
+        c = make_config(cfg)
+        h = _P()
+        st = lib().gpt2_build(ctypes.byref(c), B, T, ctypes.byref(self._bufs),
+                              None if host is None else host.ctypes.data, _stream(self.device), ctypes.byref(h))
+        _check(st)
+        self._h = h
+        self.param_layout = {n: (o, k) for n, o, k in layout(cfg, B, T, GPT2_PARAMS)}
+        self.act_layout = {n: (o, k) for n, o, k in layout(cfg, B, T, GPT2_ACTS)}
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().gpt2_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # --- views into the flat buffers
+    def param(self, name):
+        o, k = self.param_layout[name]
+        return self.params[o:o + k]
+
+    def grad(self, name):
+        o, k = self.param_layout[name]
+        return self.grads[o:o + k]
+
+    def act(self, name):
+        o, k = self.act_layout[name]
+        return self.acts[o:o + k]
+
+    # --- the step
+    def forward(self, inputs, targets=None, want_loss: bool = True):
+        """inputs/targets: int32 device tensors of B*T ids.  Returns the mean
+        loss (waits for the GPU) when targets are given and want_loss."""
+        for t in (inputs, targets):
+            if t is not None and (t.dtype != torch.int32 or not t.is_cuda or t.numel() != self.B * self.T
+                                  or not t.is_contiguous()):
+                raise ValueError("ids must be contiguous int32 device tensors of B*T elements")
+        loss = ctypes.c_float()
+        st = lib().gpt2_forward(self._h, _ptr(inputs), _ptr(targets),
+                                ctypes.byref(loss) if (targets is not None and want_loss) else None)
+        _check(st, self._h)
+        return loss.value if (targets is not None and want_loss) else None
+
+    def zero_grad(self):
+        _check(lib().gpt2_zero_grad(self._h), self._h)
+
+    def backward(self):
+        _check(lib().gpt2_backward(self._h), self._h)
+
+    def update(self, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, t=1):
+        _check(lib().gpt2_update(self._h, lr, beta1, beta2, eps, weight_decay, t), self._h)
+
+    def sync(self):
+        _check(lib().gpt2_sync(self._h), self._h)
+
+
+# ---------------------------------------------------------------- kernel-level calls
+
+def _s():
+    return _stream()
+
+
+def linear_forward(out, inp, W, bias, N, K, OC):
+    _check(lib().gpt2k_linear_forward(_ptr(out), _ptr(inp), _ptr(W), _ptr(bias), N, K, OC, _s()))
+
+
+def linear_backward(dinp, dW, dbias, dout, inp, W, N, K, OC):
+    work = torch.empty(max(1, lib().gpt2k_linear_backward_work(N, K, OC)), dtype=torch.float32, device=dout.device)
+    _check(lib().gpt2k_linear_backward(_ptr(dinp), _ptr(dW), _ptr(dbias), _ptr(dout), _ptr(inp), _ptr(W), N, K,
+                                       OC, _ptr(work), _s()))
+    return work
+
+
+def layernorm_forward(out, mean, rstd, inp, w, b, N, C):
+    _check(lib().gpt2k_layernorm_forward(_ptr(out), _ptr(mean), _ptr(rstd), _ptr(inp), _ptr(w), _ptr(b), N, C,
+                                         _s()))
+
+
+def layernorm_backward(dinp, dw, db, dout, inp, w, mean, rstd, N, C, accumulate):
+    work = torch.empty(max(1, lib().gpt2k_layernorm_backward_work(N, C)), dtype=torch.float32, device=dout.device)
+    _check(lib().gpt2k_layernorm_backward(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(inp), _ptr(w),
+                                          _ptr(mean), _ptr(rstd), N, C, int(accumulate), _ptr(work), _s()))
+    return work
+
+
+def attention_forward(atty, att, qkv, B, T, C, NH):
+    _check(lib().gpt2k_attention_forward(_ptr(atty), _ptr(att), _ptr(qkv), B, T, C, NH, _s()))
+
+
+def attention_backward(dqkv, datty, qkv, att, B, T, C, NH):
+    work = torch.empty(max(1, lib().gpt2k_attention_backward_work(B, T, C, NH)), dtype=torch.float32,
+                       device=qkv.device)
+    _check(lib().gpt2k_attention_backward(_ptr(dqkv), _ptr(datty), _ptr(qkv), _ptr(att), B, T, C, NH, _ptr(work),
+                                          _s()))
+    return work
+
+
+def gelu_forward(out, inp):
+    _check(lib().gpt2k_gelu_forward(_ptr(out), _ptr(inp), inp.numel(), _s()))
+
+
+def gelu_backward(dinp, inp, dout):
+    _check(lib().gpt2k_gelu_backward(_ptr(dinp), _ptr(inp), _ptr(dout), inp.numel(), _s()))
+
+
+def crossentropy(logits, losses, loss, targets, BT, V, Vp):
+    _check(lib().gpt2k_crossentropy(_ptr(logits), _ptr(losses), _ptr(loss), _ptr(targets), BT, V, Vp, _s()))
+
+
+def encoder_forward(out, ids, wte, wpe, B, T, C, V):
+    _check(lib().gpt2k_encoder_forward(_ptr(out), _ptr(ids), _ptr(wte), _ptr(wpe), B, T, C, V, _s()))
+
+
+def token_order(order, err, ids, targets, BT, V):
+    _check(lib().gpt2k_token_order(_ptr(order), _ptr(err), _ptr(ids), _ptr(targets), BT, V, _s()))
+
+
+def encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V):
+    _check(lib().gpt2k_encoder_backward(_ptr(dwte), _ptr(dwpe), _ptr(dout), _ptr(ids), _ptr(order), B, T, C, V,
+                                        _s()))
+
+
+def adamw(params, grads, m, v, lr, b1, b2, eps, wd, t):
+    _check(lib().gpt2k_adamw(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), params.numel(), lr, b1, b2, eps, wd, t,
+                             _s()))
