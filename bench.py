@@ -1,23 +1,57 @@
-"""Benchmark: fp32 GPT-2 training step (forward + backward + AdamW) on one MI355X.
+"""Benchmark: one fp32 GPT-2 training step (forward + backward + AdamW) on one MI355X.
 
-python bench.py [--steps K] [--warmup W] [--config 124m] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config 124m] [--gpus 1]
 
-One step = gpt2_forward (ids resident in HBM) + gpt2_zero_grad +
-gpt2_backward + gpt2_update, all enqueued on one HIP stream.  W untimed
-steps, then K timed steps between two device synchronizations.  Prints one
-JSON line.
+A step is gpt2_forward (ids already resident in HBM) + gpt2_zero_grad +
+gpt2_backward + gpt2_update, enqueued on one HIP stream.  W untimed steps,
+then K timed steps between two device synchronizations.  During the timed
+steps every launch is bracketed by HIP events on the step's stream (the
+library's per-launch timing), which gives each kernel's average duration and
+the roofline fraction of the dominant one.  Then the CPU oracle is timed on a
+bounded sample of the same workload.  Prints one JSON line on stdout.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec (fwd+bwd+AdamW) GPT-2 124M B=4 T=1024 fp32; % MFMA/HBM roofline"
+PEAK_MFMA_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, T_sample: int):
+    """The oracle (as it is) on one sequence of T_sample ids of the same
+    workload: one full step, forward + backward + AdamW over all parameters."""
+    import numpy as np
+    import oracle
+    from transformer_lm_step_flat_amd import synth
+    oracle.build(force=False)
+    tensors = synth.init_params(cfg)
+    p = oracle.pack(cfg, tensors)
+    del tensors
+    inp, tgt = synth.batch(cfg, step=0, B=1, T=T_sample)
+    R = oracle.RefModel(cfg, 1, T_sample)
+    g, m, v = np.zeros_like(p), np.zeros_like(p), np.zeros_like(p)
+    t0 = time.perf_counter()
+    R.forward(p, inp, tgt)
+    R.backward(p, g)
+    oracle.adamw(p, g, m, v, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1)
+    dt = time.perf_counter() - t0
+    R.close()
+    return {"value": T_sample / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one full step (forward, backward, AdamW over all {p.size} parameters) of the same model on "
+                      f"1 sequence x {T_sample} ids of the same seeded stream, float64; {dt:.1f} s wall"}
 
 
 def main():
@@ -27,18 +61,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="124m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-events", action="store_true", help="time the steps without per-launch events")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
-              "see the sharding design notes.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the data-parallel path over several "
+              "GPUs is designed but not built; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from transformer_lm_step_flat_amd import gpt2, synth
 
     cfg = synth.config(args.config)
     B, T = cfg["B"], cfg["T"]
+    log(f"building {args.config}: L={cfg['L']} C={cfg['C']} NH={cfg['NH']} V={cfg['V']} B={B} T={T}")
     M = gpt2.Model(cfg, B, T, init_params=gpt2.pack_params(cfg, synth.init_params(cfg), B, T))
     nb = 4
     batches = []
@@ -56,6 +92,10 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+    M.sync()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # timed region: no instrumentation
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -66,8 +106,72 @@ def main():
     loss = float(M.act("loss")[0].item())
     ms = dt_s / args.steps * 1e3
     tok_s = B * T * args.steps / dt_s
+    log(f"timed {args.steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, last loss {loss:.4f}")
+
+    # the same steps again, each launch bracketed by HIP events on the step's stream
+    kernels, roofline, ms_ev, sites = [], None, None, []
+    if not args.no_events:
+        M.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + args.steps + i)
+        torch.cuda.synchronize()
+        ms_ev = (time.perf_counter() - t0) / args.steps * 1e3
+        prof = M.profile_read()
+        M.profile_enable(False)
+        log(f"timed {args.steps} steps with per-launch events: {ms_ev:.2f} ms/step")
+        by_kernel = {}
+        for e in prof:
+            k, _, site = e["name"].partition("|")
+            a = by_kernel.setdefault(k, dict(name=k, launches=0, ms=0.0, flops=0.0, bytes=0.0))
+            for f in ("launches", "ms", "flops", "bytes"):
+                a[f] += e[f]
+            sites.append(dict(e, kernel=k, site=site))
+        tot = sum(e["ms"] for e in by_kernel.values())
+
+        def rate(e):
+            bound = "mfma" if e["flops"] > 0 else "hbm"
+            r = (e["flops"] / e["ms"] * 1e-9) if bound == "mfma" else (e["bytes"] / e["ms"] * 1e-6)
+            return bound, r, (PEAK_MFMA_FP32_TFLOPS if bound == "mfma" else PEAK_HBM_GBS)
+
+        for e in sorted(by_kernel.values(), key=lambda e: -e["ms"]):
+            bound, r, peak = rate(e)
+            kernels.append({"name": e["name"], "launches_per_step": e["launches"] / args.steps,
+                            "ms_per_step": e["ms"] / args.steps, "share": e["ms"] / tot, "bound": bound,
+                            "achieved": r, "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": r / peak})
+        log("per kernel (summed over call sites):")
+        for k in kernels:
+            log(f"  {k['name']:<38s} {k['launches_per_step']:6.1f}/step {k['ms_per_step']:8.3f} ms/step "
+                f"{100 * k['share']:5.1f}%  {k['achieved']:9.1f} {k['unit']} ({100 * k['frac']:.1f}% of peak)")
+        log("per call site:")
+        for e in sorted(sites, key=lambda e: -e["ms"]):
+            bound, r, peak = rate(e)
+            log(f"  {e['site']:<14s} {e['kernel']:<38s} {e['launches'] / args.steps:6.1f}/step "
+                f"{e['ms'] / args.steps:8.3f} ms/step {r:9.1f} {'TFLOP/s' if bound == 'mfma' else 'GB/s'} "
+                f"({100 * r / peak:.1f}%)")
+        d = max(by_kernel.values(), key=lambda e: e["ms"])
+        bound, _, peak = rate(d)
+        per_launch = (d["flops"] if bound == "mfma" else d["bytes"]) / d["launches"]
+        avg_ms = d["ms"] / d["launches"]
+        achieved = per_launch / (avg_ms * 1e-3) / (1e12 if bound == "mfma" else 1e9)
+        all_flops = sum(e["flops"] for e in by_kernel.values()) / args.steps
+        roofline = {"bound": bound, "achieved": achieved, "peak": peak,
+                    "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak, "traffic": None,
+                    "kernel": d["name"], "avg_launch_ms": avg_ms, "launches_per_step": d["launches"] / args.steps,
+                    "algorithmic_per_launch": per_launch,
+                    "step_flops": all_flops,
+                    "step_mfma_frac": all_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP32_TFLOPS}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on a {args.cpu_sample_tokens}-id sample ...")
+        cpu = cpu_baseline(cfg, args.cpu_sample_tokens)
+        log(f"  oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    ids = "Zipf(1.1) ids" if cfg.get("tokens") == "zipf" else "uniform ids"
     out = {
-        "metric": "train tokens/sec (fwd+bwd+AdamW) GPT-2 124M B=4 T=1024 fp32",
+        "metric": METRIC,
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -79,11 +183,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"gpt2 {args.config}: L={cfg['L']} C={cfg['C']} NH={cfg['NH']} "
-                               f"V={cfg['V']} (Vp={cfg['Vp']}) B={B} T={T}, seeded N(0,0.02) init, "
-                               f"Zipf(1.1) ids" if cfg.get("tokens") == "zipf" else "uniform ids",
-                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "config": {"workload": f"GPT-2 {args.config} fp32 training step: L={cfg['L']} C={cfg['C']} NH={cfg['NH']} "
+                               f"V={cfg['V']} (head padded to {cfg['Vp']}), B={B}, T={T}, seeded N(0,0.02) init, "
+                               f"{ids}, AdamW lr 1e-4",
+                   "B": B, "T": T},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
         "last_loss": loss,
+        "ms_per_step_with_events": ms_ev,
+        "kernels": kernels[:16],
     }
     print(json.dumps(out))
 

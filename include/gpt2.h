@@ -148,6 +148,26 @@ gpt2_status gpt2_update(gpt2_model *model, float lr, float beta1, float beta2, f
  * last report, GPT2_EDEVICE on a HIP error. */
 gpt2_status gpt2_sync(gpt2_model *model);
 
+/* Per-launch timing of the step (tracing).  While enabled, every kernel
+ * launch made by gpt2_forward / gpt2_zero_grad / gpt2_backward / gpt2_update
+ * is bracketed by two HIP events on the model's stream.  gpt2_profile_read
+ * waits for the stream, then returns one entry per kernel name (the name a
+ * kernel-trace profiler shows) with the number of launches, the summed
+ * event-to-event time, and the summed algorithmic FLOPs and bytes (the
+ * compulsory operand traffic of each launch; causal products count only the
+ * u <= t triangle); it then clears the records.  *n_entries gets the number
+ * of names; at most max_entries are written.  Enabling creates HIP events
+ * (host-side runtime objects); nothing is allocated during a step. */
+typedef struct {
+    char name[64];
+    long long launches;
+    double ms;
+    double flops;
+    double bytes;
+} gpt2_profile_entry;
+gpt2_status gpt2_profile_enable(gpt2_model *model, int enable);
+gpt2_status gpt2_profile_read(gpt2_model *model, gpt2_profile_entry *out, int max_entries, int *n_entries);
+
 /* Release the handle (not the caller's buffers). */
 void gpt2_free(gpt2_model *model);
 

@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/gpt2.h"
 #include "../../include/gpt2_kernels.h"
@@ -172,6 +173,22 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.niwork = l.i_err + ALIGN;
 }
 
+// When a model's profiler is on, each launch of the step is bracketed by two
+// HIP events on the model's stream and tagged with the kernel's name and its
+// algorithmic FLOPs and bytes (compulsory operand traffic).
+struct ProfRec {
+    const char *name, *site;
+    double flops, bytes;
+    hipEvent_t a, b;
+};
+struct Profiler {
+    bool on = false;
+    hipStream_t stream = nullptr;
+    std::vector<hipEvent_t> pool;
+    size_t used = 0;
+    std::vector<ProfRec> recs;
+};
+
 }  // namespace
 
 struct gpt2_model {
@@ -180,6 +197,7 @@ struct gpt2_model {
     hipStream_t stream;
     bool have_targets = false;
     std::string err;
+    Profiler prof;
 };
 
 namespace {
@@ -197,6 +215,80 @@ gpt2_status fail(gpt2_model *m, gpt2_status st, const std::string &msg) {
             return fail(model, GPT2_EDEVICE, std::string(#expr) + ": " + hipGetErrorString(e_));      \
     } while (0)
 
+#define KRUN(model, name, bytes, call) HIPCK(model, timed(name, 0.0, (double)(bytes), [&]() { return call; }))
+
+// ---------------------------------------------------------------- per-launch timing
+
+thread_local Profiler *g_prof = nullptr;
+
+thread_local const char *g_site = "";  // call site of the launches being made
+
+template <class F>
+hipError_t timed(const char *name, double flops, double bytes, F &&f) {
+    Profiler *p = g_prof;
+    if (!p) return f();
+    while (p->used + 2 > p->pool.size()) {
+        hipEvent_t e;
+        hipError_t er = hipEventCreate(&e);
+        if (er != hipSuccess) return er;
+        p->pool.push_back(e);
+    }
+    hipEvent_t a = p->pool[p->used++], b = p->pool[p->used++];
+    hipError_t e = hipEventRecord(a, p->stream);
+    if (e != hipSuccess) return e;
+    e = f();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, p->stream);
+    p->recs.push_back({name, g_site, flops, bytes, a, b});
+    return e;
+}
+
+// Names the call site of the launches made in its scope (profile entries are
+// reported as "kernel|site").
+struct Site {
+    const char *saved;
+    explicit Site(const char *s) : saved(g_site) { g_site = s; }
+    ~Site() { g_site = saved; }
+};
+
+// Makes a model's profiler the active one for the duration of an API call.
+struct ProfScope {
+    Profiler *saved;
+    explicit ProfScope(gpt2_model *m) : saved(g_prof) { g_prof = m && m->prof.on ? &m->prof : nullptr; }
+    ~ProfScope() { g_prof = saved; }
+};
+
+// The name rocprofv3 shows for the GEMM instantiation a descriptor runs.
+const char *gemm_name(const GemmDesc &d) {
+    static const char *names[3][3] = {
+        {"gemm_kernel<128, 128, true, true>", "gemm_kernel<128, 128, true, false>", "gemm_kernel<128, 128, false, false>"},
+        {"gemm_kernel<128, 64, true, true>", "gemm_kernel<128, 64, true, false>", "gemm_kernel<128, 64, false, false>"},
+        {"gemm_kernel<64, 64, true, true>", "gemm_kernel<64, 64, true, false>", "gemm_kernel<64, 64, false, false>"}};
+    int t = d.tile >= 1 && d.tile <= 3 ? d.tile - 1 : 0;
+    int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
+    return names[t][l];
+}
+
+// Every GEMM of the step goes through here (`site` overrides the caller's).
+hipError_t gemm_run(const GemmDesc &d, hipStream_t s, const char *site = nullptr) {
+    Site site_(site ? site : g_site);
+    const double nb = (double)d.nbo * d.nbi;
+    double flops, bytes;
+    if (d.causal != CAUSAL_NONE) {
+        // only the lower triangle (u <= t) of each T x T score matrix is work
+        const double tri = 0.5 * d.M * (d.M + 1.0);
+        const double inner = d.causal == CAUSAL_SKIP_UPPER ? d.K : d.N;
+        flops = 2.0 * tri * inner * nb;
+        bytes = 4.0 * nb * (tri + 2.0 * d.M * inner);
+    } else {
+        flops = 2.0 * d.M * d.N * d.K * nb;
+        double out = (double)d.M * d.N * (d.ksplit > 1 ? d.ksplit : 1);
+        if (d.epi == EPI_ACCUM || d.epi == EPI_RESID || d.epi == EPI_GELU || d.epi == EPI_GELU_BWD) out *= 2;
+        bytes = 4.0 * nb * ((double)d.M * d.K + (double)d.K * d.N + out);
+    }
+    return timed(gemm_name(d), flops, bytes, [&]() { return gemm_launch(d, s); });
+}
+
 // ---------------------------------------------------------------- building blocks
 
 // out[N][OC] = inp[N][K] W^T (+ bias) with an epilogue.
@@ -208,7 +300,7 @@ hipError_t linear_fwd(float *out, const float *inp, const float *W, const float 
     d.A = inp; d.lda = K; d.B = W; d.ldb = K; d.C = out; d.ldc = OC;
     d.epi = epi; d.bias = bias; d.aux = aux; d.ldaux = OC; d.C2 = out2;
     d.tile = plan_gemm(N, OC, K, 1, false).tile;
-    return gemm_launch(d, s);
+    return gemm_run(d, s);
 }
 
 // dinp[N][K] = dout[N][OC] W[OC][K]  (epilogue EPI_STORE or EPI_GELU_BWD with aux)
@@ -223,11 +315,12 @@ hipError_t linear_bwd_dinp(float *dinp, const float *dout, const float *W, int N
     d.tile = p.tile;
     if (p.ksplit > 1) {
         d.C = splitk; d.ldc = K; d.ksplit = p.ksplit; d.sCs = (long long)N * K;
-        hipError_t e = gemm_launch(d, s);
+        hipError_t e = gemm_run(d, s);
         if (e != hipSuccess) return e;
-        return k_sum_partials(dinp, splitk, p.ksplit, (size_t)N * K, false, s);
+        return timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 1) * N * K,
+                     [&]() { return k_sum_partials(dinp, splitk, p.ksplit, (size_t)N * K, false, s); });
     }
-    return gemm_launch(d, s);
+    return gemm_run(d, s);
 }
 
 // dW[OC][K] += dout[N][OC]^T inp[N][K]
@@ -241,12 +334,13 @@ hipError_t linear_bwd_dw(float *dW, const float *dout, const float *inp, int N, 
     d.tile = p.tile;
     if (p.ksplit > 1) {
         d.epi = EPI_STORE; d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)OC * K;
-        hipError_t e = gemm_launch(d, s);
+        hipError_t e = gemm_run(d, s);
         if (e != hipSuccess) return e;
-        return k_sum_partials(dW, splitk, p.ksplit, (size_t)OC * K, true, s);
+        return timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 2) * OC * K,
+                     [&]() { return k_sum_partials(dW, splitk, p.ksplit, (size_t)OC * K, true, s); });
     }
     d.epi = EPI_ACCUM;
-    return gemm_launch(d, s);
+    return gemm_run(d, s);
 }
 
 // Attention forward over qkv [B][T][3C]: att = softmax(scale Q K^T) (causal), atty = att V.
@@ -262,9 +356,11 @@ hipError_t attention_fwd(float *atty, float *att, const float *qkv, int B, int T
     d.nbo = B; d.nbi = NH;
     d.sAo = T * C3; d.sAi = hd; d.sBo = T * C3; d.sBi = hd; d.sCo = NH * TT; d.sCi = TT;
     d.tile = plan_gemm(T, T, hd, (long long)B * NH, false).tile;
-    hipError_t e = gemm_launch(d, s);
+    hipError_t e = gemm_run(d, s, "attn_qk");
     if (e != hipSuccess) return e;
-    e = k_attn_softmax_forward(att, (long long)B * NH * T, T, s);
+    const double tri = 0.5 * T * (T + 1.0) * B * NH;
+    e = timed("attn_softmax_forward_kernel", 0, 8.0 * tri,
+              [&]() { return k_attn_softmax_forward(att, (long long)B * NH * T, T, s); });
     if (e != hipSuccess) return e;
     GemmDesc y;
     y.a_kcontig = true; y.b_kcontig = false;
@@ -274,7 +370,7 @@ hipError_t attention_fwd(float *atty, float *att, const float *qkv, int B, int T
     y.nbo = B; y.nbi = NH;
     y.sAo = NH * TT; y.sAi = TT; y.sBo = T * C3; y.sBi = hd; y.sCo = (long long)T * C; y.sCi = hd;
     y.tile = plan_gemm(T, hd, T, (long long)B * NH, false).tile;
-    return gemm_launch(y, s);
+    return gemm_run(y, s, "attn_pv");
 }
 
 // Attention backward: dqkv (overwritten) from datty; dscore is B*NH*T*T scratch.
@@ -293,10 +389,12 @@ hipError_t attention_bwd(float *dqkv, float *dscore, const float *datty, const f
     d.nbo = B; d.nbi = NH;
     d.sAo = (long long)T * C; d.sAi = hd; d.sBo = T * C3; d.sBi = hd; d.sCo = NH * TT; d.sCi = TT;
     d.tile = plan_gemm(T, T, hd, nb, false).tile;
-    hipError_t e = gemm_launch(d, s);
+    hipError_t e = gemm_run(d, s, "attn_dp");
     if (e != hipSuccess) return e;
     // dS = P (dP - rowsum(P dP)), in place
-    e = k_attn_softmax_backward(dscore, att, nb * T, T, s);
+    const double tri = 0.5 * T * (T + 1.0) * nb;
+    e = timed("attn_softmax_backward_kernel", 0, 12.0 * tri,
+              [&]() { return k_attn_softmax_backward(dscore, att, nb * T, T, s); });
     if (e != hipSuccess) return e;
     // dQ = scale dS K
     GemmDesc q;
@@ -307,20 +405,20 @@ hipError_t attention_bwd(float *dqkv, float *dscore, const float *datty, const f
     q.nbo = B; q.nbi = NH;
     q.sAo = NH * TT; q.sAi = TT; q.sBo = T * C3; q.sBi = hd; q.sCo = T * C3; q.sCi = hd;
     q.tile = plan_gemm(T, hd, T, nb, false).tile;
-    e = gemm_launch(q, s);
+    e = gemm_run(q, s, "attn_dq");
     if (e != hipSuccess) return e;
     // dK = scale dS^T Q
     GemmDesc k = q;
     k.a_kcontig = false; k.b_kcontig = false;
     k.B = qkv; k.C = dqkv + C; k.causal = CAUSAL_KSTART;
-    e = gemm_launch(k, s);
+    e = gemm_run(k, s, "attn_dk");
     if (e != hipSuccess) return e;
     // dV = P^T dY
     GemmDesc v = k;
     v.A = att; v.alpha = 1.0f;
     v.B = datty; v.ldb = C; v.sBo = (long long)T * C; v.sBi = hd;
     v.C = dqkv + 2 * C;
-    return gemm_launch(v, s);
+    return gemm_run(v, s, "attn_dv");
 }
 
 }  // namespace
@@ -400,6 +498,7 @@ gpt2_status gpt2_build(const gpt2_config *cfg, int B, int T, const gpt2_buffers 
 
 gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *targets, float *mean_loss) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    ProfScope prof_scope(m);
     if (!inputs) return fail(m, GPT2_EINVAL, "inputs is NULL");
     if (mean_loss && !targets) return fail(m, GPT2_EINVAL, "mean_loss needs targets");
     const Layout &l = m->lo;
@@ -414,8 +513,8 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
     // keep this batch's ids for the embedding backward
     HIPCK(m, hipMemcpyAsync(tok, inputs, sizeof(int32_t) * BT, hipMemcpyDeviceToDevice, s));
     inputs = tok;
-    HIPCK(m, k_token_prep(inputs, targets, order, err, BT, l.V, s));
-    HIPCK(m, k_encoder_forward(A + l.aoff[A_ENCODED], inputs, P + l.poff[0], P + l.poff[1], B, T, C, l.V, s));
+    KRUN(m, "token_prep_kernel", 12.0 * BT, k_token_prep(inputs, targets, order, err, BT, l.V, s));
+    KRUN(m, "encoder_forward_kernel", 12.0 * BTC, k_encoder_forward(A + l.aoff[A_ENCODED], inputs, P + l.poff[0], P + l.poff[1], B, T, C, l.V, s));
     for (int li = 0; li < l.L; li++) {
         const float *res = li == 0 ? A + l.aoff[A_ENCODED] : A + l.aoff[A_RES3] + (li - 1) * BTC;
         float *ln1 = A + l.aoff[A_LN1] + li * BTC;
@@ -429,26 +528,44 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
         float *fch = A + l.aoff[A_FCH] + li * 4 * BTC, *fchg = A + l.aoff[A_FCH_GELU] + li * 4 * BTC;
         float *res3 = A + l.aoff[A_RES3] + li * BTC;
         const size_t c = C;
-        HIPCK(m, k_layernorm_forward(ln1, ln1m, ln1r, res, P + l.poff[2] + li * c, P + l.poff[3] + li * c, BT, C, s));
-        HIPCK(m, linear_fwd(qkv, ln1, P + l.poff[4] + li * 3 * c * c, P + l.poff[5] + li * 3 * c, BT, C, 3 * C,
+        KRUN(m, "layernorm_forward_kernel", 8.0 * (BTC + BT), k_layernorm_forward(ln1, ln1m, ln1r, res, P + l.poff[2] + li * c, P + l.poff[3] + li * c, BT, C, s));
+        {
+            Site site_("qkv");
+            HIPCK(m, linear_fwd(qkv, ln1, P + l.poff[4] + li * 3 * c * c, P + l.poff[5] + li * 3 * c, BT, C, 3 * C,
                             EPI_STORE, nullptr, nullptr, s));
-        HIPCK(m, attention_fwd(atty, att, qkv, B, T, C, NH, s));
-        HIPCK(m, linear_fwd(res2, atty, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, BT, C, C, EPI_RESID,
+        }
+        {
+            Site site_("attn_fwd");
+            HIPCK(m, attention_fwd(atty, att, qkv, B, T, C, NH, s));
+        }
+        {
+            Site site_("attproj");
+            HIPCK(m, linear_fwd(res2, atty, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, BT, C, C, EPI_RESID,
                             res, nullptr, s));
-        HIPCK(m, k_layernorm_forward(ln2, ln2m, ln2r, res2, P + l.poff[8] + li * c, P + l.poff[9] + li * c, BT, C, s));
-        HIPCK(m, linear_fwd(fch, ln2, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, BT, C, 4 * C,
+        }
+        KRUN(m, "layernorm_forward_kernel", 8.0 * (BTC + BT), k_layernorm_forward(ln2, ln2m, ln2r, res2, P + l.poff[8] + li * c, P + l.poff[9] + li * c, BT, C, s));
+        {
+            Site site_("fc");
+            HIPCK(m, linear_fwd(fch, ln2, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, BT, C, 4 * C,
                             EPI_GELU, nullptr, fchg, s));
-        HIPCK(m, linear_fwd(res3, fchg, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, BT, 4 * C, C,
+        }
+        {
+            Site site_("fcproj");
+            HIPCK(m, linear_fwd(res3, fchg, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, BT, 4 * C, C,
                             EPI_RESID, res2, nullptr, s));
+        }
     }
     const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
     float *lnf = A + l.aoff[A_LNF], *logits = A + l.aoff[A_LOGITS];
-    HIPCK(m, k_layernorm_forward(lnf, A + l.aoff[A_LNF_MEAN], A + l.aoff[A_LNF_RSTD], last, P + l.poff[14],
+    KRUN(m, "layernorm_forward_kernel", 8.0 * (BTC + BT), k_layernorm_forward(lnf, A + l.aoff[A_LNF_MEAN], A + l.aoff[A_LNF_RSTD], last, P + l.poff[14],
                                  P + l.poff[15], BT, C, s));
-    HIPCK(m, linear_fwd(logits, lnf, P + l.poff[0], nullptr, BT, C, l.Vp, EPI_STORE, nullptr, nullptr, s));
+    {
+        Site site_("head");
+        HIPCK(m, linear_fwd(logits, lnf, P + l.poff[0], nullptr, BT, C, l.Vp, EPI_STORE, nullptr, nullptr, s));
+    }
     if (targets) {
-        HIPCK(m, k_crossentropy(logits, A + l.aoff[A_LOSSES], targets, BT, l.V, l.Vp, 1.0f / BT, s));
-        HIPCK(m, k_mean(A + l.aoff[A_LOSS], A + l.aoff[A_LOSSES], BT, s));
+        KRUN(m, "crossentropy_kernel", 8.0 * BT * l.Vp, k_crossentropy(logits, A + l.aoff[A_LOSSES], targets, BT, l.V, l.Vp, 1.0f / BT, s));
+        KRUN(m, "mean_kernel", 4.0 * BT, k_mean(A + l.aoff[A_LOSS], A + l.aoff[A_LOSSES], BT, s));
         m->have_targets = true;
     }
     if (mean_loss) {
@@ -469,12 +586,14 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
 
 gpt2_status gpt2_zero_grad(gpt2_model *m) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
-    HIPCK(m, k_fill(m->buf.grads, m->lo.nparams, 0.0f, m->stream));
+    ProfScope prof_scope(m);
+    KRUN(m, "fill_kernel", 4.0 * m->lo.nparams, k_fill(m->buf.grads, m->lo.nparams, 0.0f, m->stream));
     return GPT2_OK;
 }
 
 gpt2_status gpt2_backward(gpt2_model *m) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    ProfScope prof_scope(m);
     if (!m->have_targets) return fail(m, GPT2_ESTATE, "gpt2_backward needs a preceding gpt2_forward with targets");
     const Layout &l = m->lo;
     const int B = l.B, T = l.T, C = l.C, NH = l.NH, BT = (int)l.BT;
@@ -486,10 +605,16 @@ gpt2_status gpt2_backward(gpt2_model *m) {
     const float *dlogits = A + l.aoff[A_LOGITS], *lnf = A + l.aoff[A_LNF];
 
     // head: dlnf = dlogits wte, dwte += dlogits^T lnf
-    HIPCK(m, linear_bwd_dinp(dln, dlogits, P + l.poff[0], BT, C, l.Vp, EPI_STORE, nullptr, splitk, s));
-    HIPCK(m, linear_bwd_dw(G + l.poff[0], dlogits, lnf, BT, C, l.Vp, splitk, s));
+    {
+        Site site_("head_dinp");
+        HIPCK(m, linear_bwd_dinp(dln, dlogits, P + l.poff[0], BT, C, l.Vp, EPI_STORE, nullptr, splitk, s));
+    }
+    {
+        Site site_("head_dw");
+        HIPCK(m, linear_bwd_dw(G + l.poff[0], dlogits, lnf, BT, C, l.Vp, splitk, s));
+    }
     const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
-    HIPCK(m, k_layernorm_backward(dres, G + l.poff[14], G + l.poff[15], part, dln, last, P + l.poff[14],
+    KRUN(m, "layernorm_backward_kernel", 12.0 * BTC, k_layernorm_backward(dres, G + l.poff[14], G + l.poff[15], part, dln, last, P + l.poff[14],
                                   A + l.aoff[A_LNF_MEAN], A + l.aoff[A_LNF_RSTD], BT, C, false, s));
     for (int li = l.L - 1; li >= 0; li--) {
         const float *res = li == 0 ? A + l.aoff[A_ENCODED] : A + l.aoff[A_RES3] + (li - 1) * BTC;
@@ -506,40 +631,68 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         const float *fw = P + l.poff[10] + li * 4 * c * c, *pw = P + l.poff[12] + li * 4 * c * c;
 
         // fcproj: dout = dres (gradient of residual3)
-        HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, dres, fchg, BT, 4 * C, C, splitk, s));
-        HIPCK(m, k_colsum_accumulate(G + l.poff[13] + li * c, part, dres, BT, C, C, s));
-        HIPCK(m, linear_bwd_dinp(dfch, dres, pw, BT, 4 * C, C, EPI_GELU_BWD, fch, nullptr, s));
+        {
+            Site site_("fcproj_dw");
+            HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, dres, fchg, BT, 4 * C, C, splitk, s));
+        }
+        KRUN(m, "colsum_partial_kernel", 4.0 * BTC, k_colsum_accumulate(G + l.poff[13] + li * c, part, dres, BT, C, C, s));
+        {
+            Site site_("fcproj_dinp");
+            HIPCK(m, linear_bwd_dinp(dfch, dres, pw, BT, 4 * C, C, EPI_GELU_BWD, fch, nullptr, s));
+        }
         // fc
-        HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, dfch, ln2, BT, C, 4 * C, splitk, s));
-        HIPCK(m, k_colsum_accumulate(G + l.poff[11] + li * 4 * c, part, dfch, BT, 4 * C, 4 * C, s));
-        HIPCK(m, linear_bwd_dinp(dln, dfch, fw, BT, C, 4 * C, EPI_STORE, nullptr, nullptr, s));
+        {
+            Site site_("fc_dw");
+            HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, dfch, ln2, BT, C, 4 * C, splitk, s));
+        }
+        KRUN(m, "colsum_partial_kernel", 16.0 * BTC, k_colsum_accumulate(G + l.poff[11] + li * 4 * c, part, dfch, BT, 4 * C, 4 * C, s));
+        {
+            Site site_("fc_dinp");
+            HIPCK(m, linear_bwd_dinp(dln, dfch, fw, BT, C, 4 * C, EPI_STORE, nullptr, nullptr, s));
+        }
         // ln2: dres becomes the gradient of residual2
-        HIPCK(m, k_layernorm_backward(dres, G + l.poff[8] + li * c, G + l.poff[9] + li * c, part, dln, res2,
+        KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[8] + li * c, G + l.poff[9] + li * c, part, dln, res2,
                                       P + l.poff[8] + li * c, ln2m, ln2r, BT, C, true, s));
         // attproj: dout = dres
-        HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, dres, atty, BT, C, C, splitk, s));
-        HIPCK(m, k_colsum_accumulate(G + l.poff[7] + li * c, part, dres, BT, C, C, s));
-        HIPCK(m, linear_bwd_dinp(datty, dres, aw, BT, C, C, EPI_STORE, nullptr, nullptr, s));
+        {
+            Site site_("attproj_dw");
+            HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, dres, atty, BT, C, C, splitk, s));
+        }
+        KRUN(m, "colsum_partial_kernel", 4.0 * BTC, k_colsum_accumulate(G + l.poff[7] + li * c, part, dres, BT, C, C, s));
+        {
+            Site site_("attproj_dinp");
+            HIPCK(m, linear_bwd_dinp(datty, dres, aw, BT, C, C, EPI_STORE, nullptr, nullptr, s));
+        }
         // attention
-        HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
+        {
+            Site site_("attn_bwd");
+            HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
+        }
         // qkv
-        HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, dqkv, ln1, BT, C, 3 * C, splitk, s));
-        HIPCK(m, k_colsum_accumulate(G + l.poff[5] + li * 3 * c, part, dqkv, BT, 3 * C, 3 * C, s));
-        HIPCK(m, linear_bwd_dinp(dln, dqkv, qkvw, BT, C, 3 * C, EPI_STORE, nullptr, nullptr, s));
+        {
+            Site site_("qkv_dw");
+            HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, dqkv, ln1, BT, C, 3 * C, splitk, s));
+        }
+        KRUN(m, "colsum_partial_kernel", 12.0 * BTC, k_colsum_accumulate(G + l.poff[5] + li * 3 * c, part, dqkv, BT, 3 * C, 3 * C, s));
+        {
+            Site site_("qkv_dinp");
+            HIPCK(m, linear_bwd_dinp(dln, dqkv, qkvw, BT, C, 3 * C, EPI_STORE, nullptr, nullptr, s));
+        }
         // ln1: dres becomes the gradient of this layer's input
-        HIPCK(m, k_layernorm_backward(dres, G + l.poff[2] + li * c, G + l.poff[3] + li * c, part, dln, res,
+        KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[2] + li * c, G + l.poff[3] + li * c, part, dln, res,
                                       P + l.poff[2] + li * c, ln1m, ln1r, BT, C, true, s));
     }
-    HIPCK(m, k_encoder_backward(G + l.poff[0], G + l.poff[1], dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
+    KRUN(m, "encoder_backward_kernel", 12.0 * BTC, k_encoder_backward(G + l.poff[0], G + l.poff[1], dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
                                 l.V, s));
     return GPT2_OK;
 }
 
 gpt2_status gpt2_update(gpt2_model *m, float lr, float beta1, float beta2, float eps, float weight_decay, int t) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    ProfScope prof_scope(m);
     if (t < 1) return fail(m, GPT2_EINVAL, "t must be >= 1");
     double c1 = 1.0 - std::pow((double)beta1, t), c2 = 1.0 - std::pow((double)beta2, t);
-    HIPCK(m, k_adamw(m->buf.params, m->buf.grads, m->buf.adam_m, m->buf.adam_v, m->lo.nparams, lr, beta1, beta2,
+    KRUN(m, "adamw_kernel", 28.0 * m->lo.nparams, k_adamw(m->buf.params, m->buf.grads, m->buf.adam_m, m->buf.adam_v, m->lo.nparams, lr, beta1, beta2,
                      eps, weight_decay, (float)c1, (float)c2, m->stream));
     return GPT2_OK;
 }
@@ -556,7 +709,54 @@ gpt2_status gpt2_sync(gpt2_model *m) {
     return GPT2_OK;
 }
 
-void gpt2_free(gpt2_model *m) { delete m; }
+gpt2_status gpt2_profile_enable(gpt2_model *m, int enable) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    m->prof.on = enable != 0;
+    m->prof.stream = m->stream;
+    // create events up front so that none is created inside a timed region
+    while (m->prof.on && m->prof.pool.size() < 4096) {
+        hipEvent_t e;
+        HIPCK(m, hipEventCreate(&e));
+        m->prof.pool.push_back(e);
+    }
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_profile_read(gpt2_model *m, gpt2_profile_entry *out, int max_entries, int *n_entries) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    HIPCK(m, hipStreamSynchronize(m->stream));
+    std::vector<gpt2_profile_entry> agg;
+    for (const ProfRec &r : m->prof.recs) {
+        float ms = 0.f;
+        HIPCK(m, hipEventElapsedTime(&ms, r.a, r.b));
+        char key[sizeof(gpt2_profile_entry::name)];
+        snprintf(key, sizeof key, "%s|%s", r.name, r.site);
+        gpt2_profile_entry *e = nullptr;
+        for (auto &x : agg)
+            if (strncmp(x.name, key, sizeof x.name) == 0) e = &x;
+        if (!e) {
+            agg.push_back(gpt2_profile_entry{});
+            e = &agg.back();
+            strncpy(e->name, key, sizeof e->name - 1);
+        }
+        e->launches += 1;
+        e->ms += ms;
+        e->flops += r.flops;
+        e->bytes += r.bytes;
+    }
+    m->prof.recs.clear();
+    m->prof.used = 0;
+    int n = (int)agg.size();
+    if (n_entries) *n_entries = n;
+    for (int i = 0; i < n && i < max_entries && out; i++) out[i] = agg[i];
+    return GPT2_OK;
+}
+
+void gpt2_free(gpt2_model *m) {
+    if (!m) return;
+    for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
+    delete m;
+}
 
 const char *gpt2_last_error(const gpt2_model *m) { return m ? m->err.c_str() : g_last_error.c_str(); }
 

@@ -43,6 +43,11 @@ class Buffers(ctypes.Structure):
                 ("iwork", ctypes.c_void_p)]
 
 
+class ProfileEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_longlong), ("ms", ctypes.c_double),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
 _lib = None
 
 _P = ctypes.c_void_p
@@ -60,6 +65,8 @@ _SIGS = {
     "gpt2_backward": [_P],
     "gpt2_update": [_P, _F, _F, _F, _F, _F, _I],
     "gpt2_sync": [_P],
+    "gpt2_profile_enable": [_P, _I],
+    "gpt2_profile_read": [_P, ctypes.POINTER(ProfileEntry), _I, ctypes.POINTER(_I)],
     "gpt2k_linear_forward": [_P, _P, _P, _P, _I, _I, _I, _P],
     "gpt2k_linear_backward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
     "gpt2k_layernorm_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _P],
@@ -245,6 +252,18 @@ class Model:
 
     def sync(self):
         _check(lib().gpt2_sync(self._h), self._h)
+
+    # --- per-launch timing
+    def profile_enable(self, on: bool = True):
+        _check(lib().gpt2_profile_enable(self._h, int(on)), self._h)
+
+    def profile_read(self):
+        """[{name, launches, ms, flops, bytes}] since the last read (waits for the GPU)."""
+        n = ctypes.c_int()
+        buf = (ProfileEntry * 256)()
+        _check(lib().gpt2_profile_read(self._h, buf, 256, ctypes.byref(n)), self._h)
+        return [dict(name=buf[i].name.decode(), launches=buf[i].launches, ms=buf[i].ms, flops=buf[i].flops,
+                     bytes=buf[i].bytes) for i in range(min(n.value, 256))]
 
 
 # ---------------------------------------------------------------- kernel-level calls
