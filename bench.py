@@ -4,10 +4,11 @@
 
 A step is gpt2_forward (ids already resident in HBM) + gpt2_zero_grad +
 gpt2_backward + gpt2_update, enqueued on one HIP stream.  W untimed steps,
-then K timed steps between two device synchronizations.  During the timed
-steps every launch is bracketed by HIP events on the step's stream (the
-library's per-launch timing), which gives each kernel's average duration and
-the roofline fraction of the dominant one.  Then the CPU oracle is timed on a
+then K timed steps between two device synchronizations (`value`).  The same
+number of steps is then run again with every launch bracketed by HIP events
+on the step's stream (the library's per-launch timing): that gives each
+kernel's average duration and the roofline fraction of the dominant kernel
+without perturbing the first timing.  Last, the CPU oracle is timed on a
 bounded sample of the same workload.  Prints one JSON line on stdout.
 """
 from __future__ import annotations
