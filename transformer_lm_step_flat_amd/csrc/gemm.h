@@ -52,6 +52,11 @@ struct GemmDesc {
     // split-K: partial s goes to C + s * sCs (EPI_STORE only)
     int ksplit = 1;
     long long sCs = 0;
+    // Column sums of A (sum over k of A(m, k), m < M), for an MN-contiguous A
+    // (the bias gradient of a weight-gradient GEMM): added into colsum[m], or
+    // with split-K stored to colsum + s * M.  Computed by the workgroups of the
+    // first column of tiles from the A slices already in LDS.
+    float *colsum = nullptr;
     int tile = 0;  // 0 = choose; 1 = 128x128, 2 = 128x64, 3 = 64x64
 };
 

@@ -29,6 +29,7 @@ struct GemmArgs {
     const float *A, *B;
     float *C, *C2;
     const float *bias, *aux;
+    float *colsum;
     long long lda, ldb, ldc, ldaux;
     long long sAo, sAi, sBo, sBi, sCo, sCi, sCs;
     float alpha;
@@ -60,7 +61,7 @@ __device__ __forceinline__ void group_order(int bid, int tiles_m, int tiles_n, i
 }
 
 template <int BM, int BN, bool AK, bool BKC>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
     constexpr int BK = GEMM_BK;
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -103,6 +104,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs p) {
 
     floatx4 ra[A_F4], rb[B_F4];
     const int M = p.M, N = p.N;
+    // column sums of A (only MN-contiguous A, only the first tile column)
+    constexpr int CS_LANES = GEMM_THREADS / BM;
+    const bool do_colsum = !AK && p.colsum != nullptr && tn == 0;
+    float csum = 0.0f;
     const long long lda = p.lda, ldb = p.ldb;
 
     auto gload = [&](int k0) {
@@ -150,6 +155,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs p) {
         lstore();
         __syncthreads();
         if (k0 + BK < kend) gload(k0 + BK);
+        if (!AK && do_colsum) {
+#pragma unroll
+            for (int j = 0; j < BK / CS_LANES; j++) csum += As[(tid / BM + j * CS_LANES) * BM + tid % BM];
+        }
 #pragma unroll
         for (int q = 0; q < BK / 8; q++) {
             floatx4 a[MI], b[NI];
@@ -180,6 +189,22 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int j = 0; j < NI; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    if (!AK && do_colsum) {
+        // combine the CS_LANES partial sums of each column in a fixed order
+        __syncthreads();
+        As[tid] = csum;
+        __syncthreads();
+        if (tid < BM && m0 + tid < M) {
+            float t = As[tid];
+#pragma unroll
+            for (int j = 1; j < CS_LANES; j++) t += As[j * BM + tid];
+            if (p.ksplit > 1)
+                p.colsum[(long long)s * M + m0 + tid] = t;
+            else
+                p.colsum[m0 + tid] += t;
         }
     }
 
@@ -255,7 +280,8 @@ hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
     if (d.epi == EPI_GELU && !d.C2) return hipErrorInvalidValue;
 
     GemmArgs a{};
-    a.A = d.A; a.B = d.B; a.C = d.C; a.C2 = d.C2; a.bias = d.bias; a.aux = d.aux;
+    a.A = d.A; a.B = d.B; a.C = d.C; a.C2 = d.C2; a.bias = d.bias; a.aux = d.aux; a.colsum = d.colsum;
+    if (d.colsum && (d.a_kcontig || d.nbo * d.nbi != 1)) return hipErrorInvalidValue;
     a.lda = d.lda; a.ldb = d.ldb; a.ldc = d.ldc; a.ldaux = d.ldaux;
     a.sAo = d.sAo; a.sAi = d.sAi; a.sBo = d.sBo; a.sBi = d.sBi; a.sCo = d.sCo; a.sCi = d.sCi;
     a.sCs = d.sCs;

@@ -50,35 +50,59 @@ struct Plan {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// Tile choice: the largest tile that still gives about two workgroups per
-// CU; when even the smallest does not and the caller can take partial
-// products, split K as well.
-Plan plan_gemm(int M, int N, int K, long long batches, bool allow_split) {
-    auto tiles = [&](int bm, int bn) { return ceil_div(M, bm) * ceil_div(N, bn) * batches; };
-    const long long want = 512;
-    Plan p{3, 1};
-    if (N <= 64) {
-        p.tile = tiles(128, 64) >= 256 ? 2 : 3;
-    } else if (tiles(128, 128) >= want) {
-        p.tile = 1;
-    } else if (allow_split && K >= 8192) {
-        p.tile = 1;  // long reductions: keep the large tile and split K
-    } else if (tiles(128, 64) >= want) {
-        p.tile = 2;
+// Launch planning.  Work is spread over 256 CUs; a CU holds up to `occ`
+// workgroups of a tile shape at once (register/LDS limited) and reaches full
+// MFMA throughput with two or more resident.  Workgroups are all the same
+// size, so a CU with n of them runs rounds of min(occ, left) at a time, and
+// a round of k costs max(k, 2) tile-times.  The plan with the least
+// predicted time wins; a split of K adds the traffic of writing and summing
+// the partial products.  The per-shape efficiencies are measured values of
+// the kernel on long runs at this occupancy.
+struct TileShape {
+    int bm, bn, occ;
+    double eff;
+};
+const TileShape kTiles[4] = {{0, 0, 0, 0.0}, {128, 128, 3, 0.73}, {128, 64, 4, 0.68}, {64, 64, 6, 0.66}};
+
+double predict_gemm_us(int M, int N, int K, long long batches, int tile, int ks) {
+    const TileShape &t = kTiles[tile];
+    const long long wgs = ceil_div(M, t.bm) * ceil_div(N, t.bn) * batches * ks;
+    double units = 0;
+    if (wgs <= 256LL * t.occ) {
+        // all resident from the start: the CU with the most sets the time
+        long long n = ceil_div(wgs, 256);
+        while (n > 0) {
+            long long k = n < t.occ ? n : t.occ;
+            units += k > 2 ? k : 2;
+            n -= k;
+        }
+    } else {
+        // refilled as slots free up: even spread plus a partial last tile
+        units = wgs / 256.0 + 0.5;
     }
-    if (allow_split) {
-        int bm = p.tile == 3 ? 64 : 128, bn = p.tile == 1 ? 128 : 64;
-        long long t = tiles(bm, bn);
-        if (t < want) {
-            long long ks = ceil_div(want, t);
-            long long kmax = K / 256;
-            if (ks > kmax) ks = kmax;
-            if (ks > 16) ks = 16;
-            if (ks < 1) ks = 1;
-            p.ksplit = (int)ks;
+    const double kc = (double)ceil_div(ceil_div(K, ks), 32) * 32;
+    const double cu_flops_per_us = 157.3e6 / 256.0;
+    double us = units * (2.0 * t.bm * t.bn * kc) / (t.eff * cu_flops_per_us);
+    if (ks > 1) us += 8.0 + (2.0 * ks + 2.0) * M * N * 4.0 / 5.0e6;  // extra launch + partials written, read, summed
+    return us;
+}
+
+Plan plan_gemm(int M, int N, int K, long long batches, bool allow_split) {
+    Plan best{1, 1};
+    double best_us = 1e30;
+    static const int splits[] = {1, 2, 3, 4, 6, 8, 12, 16};
+    for (int tile = 1; tile <= 3; tile++) {
+        if (N <= 64 && tile == 1) continue;
+        for (int ks : splits) {
+            if (ks > 1 && (!allow_split || K / ks < 256)) break;
+            double us = predict_gemm_us(M, N, K, batches, tile, ks);
+            if (us < best_us * 0.98) {
+                best_us = us;
+                best = Plan{tile, ks};
+            }
         }
     }
-    return p;
+    return best;
 }
 
 struct Layout {
@@ -87,7 +111,7 @@ struct Layout {
     size_t poff[16], pcnt[16], nparams;
     size_t aoff[NUM_ACTS], acnt[NUM_ACTS], nacts;
     // work buffer
-    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_part, w_splitk, nwork;
+    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_part, w_splitk, w_dbias, nwork;
     // int buffer
     size_t i_tok, i_order, i_err, niwork;
 };
@@ -150,9 +174,7 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.w_dqkv = off; off = align_up(off + BT * 3 * C);
     l.w_dfch = off; off = align_up(off + BT * 4 * C);
     l.w_datt = off; off = align_up(off + (size_t)B * NH * TT);
-    size_t part = (size_t)ln_partials((int)BT) * 2 * C;
-    size_t part2 = (size_t)colsum_partials((int)BT) * 4 * C;
-    l.w_part = off; off = align_up(off + (part > part2 ? part : part2));
+    l.w_part = off; off = align_up(off + (size_t)ln_partials((int)BT) * 2 * C);
     // split-K partial products of the GEMMs that may split (weight gradients, dlnf)
     size_t sk = 0;
     auto need = [&](int M, int N, int K) {
@@ -166,6 +188,7 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     need(l.Vp, (int)C, (int)BT);
     need((int)BT, (int)C, l.Vp);
     l.w_splitk = off; off = align_up(off + sk);
+    l.w_dbias = off; off = align_up(off + 16 * 4 * C);
     l.nwork = off;
     l.i_tok = 0;
     l.i_order = align_up(BT);
@@ -323,9 +346,11 @@ hipError_t linear_bwd_dinp(float *dinp, const float *dout, const float *W, int N
     return gemm_run(d, s);
 }
 
-// dW[OC][K] += dout[N][OC]^T inp[N][K]
-hipError_t linear_bwd_dw(float *dW, const float *dout, const float *inp, int N, int K, int OC, float *splitk,
-                         hipStream_t s) {
+// dW[OC][K] += dout[N][OC]^T inp[N][K]; dbias[OC] += column sums of dout
+// (dbias may be null).  With split-K the partial products go to `splitk`
+// and the partial bias sums to `dbias_ws` (16 * OC floats).
+hipError_t linear_bwd_dw(float *dW, float *dbias, const float *dout, const float *inp, int N, int K, int OC,
+                         float *splitk, float *dbias_ws, hipStream_t s) {
     GemmDesc d;
     d.a_kcontig = false; d.b_kcontig = false;
     d.M = OC; d.N = K; d.K = N;
@@ -334,12 +359,17 @@ hipError_t linear_bwd_dw(float *dW, const float *dout, const float *inp, int N, 
     d.tile = p.tile;
     if (p.ksplit > 1) {
         d.epi = EPI_STORE; d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)OC * K;
+        d.colsum = dbias ? dbias_ws : nullptr;
         hipError_t e = gemm_run(d, s);
         if (e != hipSuccess) return e;
-        return timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 2) * OC * K,
-                     [&]() { return k_sum_partials(dW, splitk, p.ksplit, (size_t)OC * K, true, s); });
+        e = timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 2) * OC * K,
+                  [&]() { return k_sum_partials(dW, splitk, p.ksplit, (size_t)OC * K, true, s); });
+        if (e != hipSuccess || !dbias) return e;
+        return timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 2) * OC,
+                     [&]() { return k_sum_partials(dbias, dbias_ws, p.ksplit, (size_t)OC, true, s); });
     }
     d.epi = EPI_ACCUM;
+    d.colsum = dbias;
     return gemm_run(d, s);
 }
 
@@ -602,6 +632,7 @@ gpt2_status gpt2_backward(gpt2_model *m) {
     float *P = m->buf.params, *G = m->buf.grads, *A = m->buf.acts, *W = m->buf.work;
     float *dres = W + l.w_dres, *dln = W + l.w_dln, *datty = W + l.w_datty, *dqkv = W + l.w_dqkv;
     float *dfch = W + l.w_dfch, *dscore = W + l.w_datt, *part = W + l.w_part, *splitk = W + l.w_splitk;
+    float *dbias_ws = W + l.w_dbias;
     const float *dlogits = A + l.aoff[A_LOGITS], *lnf = A + l.aoff[A_LNF];
 
     // head: dlnf = dlogits wte, dwte += dlogits^T lnf
@@ -611,7 +642,7 @@ gpt2_status gpt2_backward(gpt2_model *m) {
     }
     {
         Site site_("head_dw");
-        HIPCK(m, linear_bwd_dw(G + l.poff[0], dlogits, lnf, BT, C, l.Vp, splitk, s));
+        HIPCK(m, linear_bwd_dw(G + l.poff[0], nullptr, dlogits, lnf, BT, C, l.Vp, splitk, dbias_ws, s));
     }
     const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
     KRUN(m, "layernorm_backward_kernel", 12.0 * BTC, k_layernorm_backward(dres, G + l.poff[14], G + l.poff[15], part, dln, last, P + l.poff[14],
@@ -633,9 +664,8 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         // fcproj: dout = dres (gradient of residual3)
         {
             Site site_("fcproj_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, dres, fchg, BT, 4 * C, C, splitk, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, G + l.poff[13] + li * c, dres, fchg, BT, 4 * C, C, splitk, dbias_ws, s));
         }
-        KRUN(m, "colsum_partial_kernel", 4.0 * BTC, k_colsum_accumulate(G + l.poff[13] + li * c, part, dres, BT, C, C, s));
         {
             Site site_("fcproj_dinp");
             HIPCK(m, linear_bwd_dinp(dfch, dres, pw, BT, 4 * C, C, EPI_GELU_BWD, fch, nullptr, s));
@@ -643,9 +673,8 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         // fc
         {
             Site site_("fc_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, dfch, ln2, BT, C, 4 * C, splitk, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, G + l.poff[11] + li * 4 * c, dfch, ln2, BT, C, 4 * C, splitk, dbias_ws, s));
         }
-        KRUN(m, "colsum_partial_kernel", 16.0 * BTC, k_colsum_accumulate(G + l.poff[11] + li * 4 * c, part, dfch, BT, 4 * C, 4 * C, s));
         {
             Site site_("fc_dinp");
             HIPCK(m, linear_bwd_dinp(dln, dfch, fw, BT, C, 4 * C, EPI_STORE, nullptr, nullptr, s));
@@ -656,9 +685,8 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         // attproj: dout = dres
         {
             Site site_("attproj_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, dres, atty, BT, C, C, splitk, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, G + l.poff[7] + li * c, dres, atty, BT, C, C, splitk, dbias_ws, s));
         }
-        KRUN(m, "colsum_partial_kernel", 4.0 * BTC, k_colsum_accumulate(G + l.poff[7] + li * c, part, dres, BT, C, C, s));
         {
             Site site_("attproj_dinp");
             HIPCK(m, linear_bwd_dinp(datty, dres, aw, BT, C, C, EPI_STORE, nullptr, nullptr, s));
@@ -671,9 +699,8 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         // qkv
         {
             Site site_("qkv_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, dqkv, ln1, BT, C, 3 * C, splitk, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, G + l.poff[5] + li * 3 * c, dqkv, ln1, BT, C, 3 * C, splitk, dbias_ws, s));
         }
-        KRUN(m, "colsum_partial_kernel", 12.0 * BTC, k_colsum_accumulate(G + l.poff[5] + li * 3 * c, part, dqkv, BT, 3 * C, 3 * C, s));
         {
             Site site_("qkv_dinp");
             HIPCK(m, linear_bwd_dinp(dln, dqkv, qkvw, BT, C, 3 * C, EPI_STORE, nullptr, nullptr, s));
@@ -780,8 +807,7 @@ size_t gpt2k_linear_backward_work(int N, int K, int OC) {
     Plan p1 = plan_gemm(N, K, OC, 1, true), p2 = plan_gemm(OC, K, N, 1, true);
     if (p1.ksplit > 1) sk = (size_t)p1.ksplit * N * K;
     if (p2.ksplit > 1 && (size_t)p2.ksplit * OC * K > sk) sk = (size_t)p2.ksplit * OC * K;
-    size_t part = (size_t)colsum_partials(N) * OC;
-    return align_up(sk) + align_up(part);
+    return align_up(sk) + align_up((size_t)16 * OC);
 }
 
 gpt2_status gpt2k_linear_backward(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
@@ -791,10 +817,9 @@ gpt2_status gpt2k_linear_backward(float *dinp, float *dW, float *dbias, const fl
     size_t sk = 0;
     if (p1.ksplit > 1) sk = (size_t)p1.ksplit * N * K;
     if (p2.ksplit > 1 && (size_t)p2.ksplit * OC * K > sk) sk = (size_t)p2.ksplit * OC * K;
-    float *splitk = work, *part = work + align_up(sk);
+    float *splitk = work, *dbias_ws = work + align_up(sk);
     if (dinp) KCK(linear_bwd_dinp(dinp, dout, W, N, K, OC, EPI_STORE, nullptr, splitk, s));
-    KCK(linear_bwd_dw(dW, dout, inp, N, K, OC, splitk, s));
-    if (dbias) KCK(k_colsum_accumulate(dbias, part, dout, N, OC, OC, s));
+    KCK(linear_bwd_dw(dW, dbias, dout, inp, N, K, OC, splitk, dbias_ws, s));
     return GPT2_OK;
 }
 

@@ -22,20 +22,18 @@ hipError_t k_encoder_backward(float *dwte, float *dwpe, const float *dout, const
 
 hipError_t k_layernorm_forward(float *out, float *mean, float *rstd, const float *inp, const float *w,
                                const float *b, int N, int C, hipStream_t s);
-// dinp (+)= LayerNorm input gradient; the weight/bias gradients go to
-// `partial` ([ln_partials(N)][2C]) and are then added to dw, db.
+// dinp (+)= LayerNorm input gradient; dw, db += weight/bias gradients, summed
+// through `partial` ([ln_partials(N)][2C]) in a fixed order.
 int ln_partials(int N);
 hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partial, const float *dout,
                                 const float *inp, const float *w, const float *mean, const float *rstd, int N,
                                 int C, bool accumulate, hipStream_t s);
 
-// db[n] += sum_r src[r][n]  (src is R x N with leading dim ld); uses partial ([colsum_partials(R)][N])
-int colsum_partials(int R);
-hipError_t k_colsum_accumulate(float *db, float *partial, const float *src, int R, int N, long long ld,
-                               hipStream_t s);
-
-// dst[i] (+)= sum_{p < P} src[p * n + i]   (fixed order)
+// dst[i] (+)= sum_{p < P} src[p * n + i]   (fixed order; n % 4 == 0, 16-byte aligned)
 hipError_t k_sum_partials(float *dst, const float *src, int P, size_t n, bool accumulate, hipStream_t s);
+// the same with partial rows ld apart
+hipError_t k_sum_partials_ld(float *dst, const float *src, int P, size_t n, size_t ld, bool accumulate,
+                             hipStream_t s);
 
 // Causal row softmax in place over rows of T (T <= 1024): nrows = B*NH*T rows,
 // row index t = row % T.  Writes zeros for t < u < round_up(t+1, CAUSAL_PAD).

@@ -144,113 +144,111 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(float *out, floa
     }
 }
 
-constexpr int LN_BWD_ROWS = 16;  // rows per block (4 per wavefront)
-
-// LayerNorm backward.  Block b handles rows [16b, 16b+16); each wavefront
-// four of them, one at a time.  dx (+)= rstd (g - mean(g) - xhat mean(g xhat))
-// with g = dy * w.  Per-column sums of dy*xhat and dy are kept per lane,
-// combined over the 4 wavefronts in a fixed order and written as the
-// block's partial row [dw(C) | db(C)].
+// LayerNorm backward, input gradient: one wavefront per row, as the forward.
+// xhat = (x - mean) rstd, g = dy * w,
+// dx (+)= rstd (g - mean_c(g) - xhat mean_c(g xhat)).
 template <int NV>
-__global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, float *partial, const float *dout,
-                                                                 const float *inp, const float *w,
-                                                                 const float *mean, const float *rstd, int N,
-                                                                 int C, int accumulate) {
-    extern __shared__ float lds[];  // [4][2C]
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, const float *dout, const float *inp,
+                                                                 const float *w, const float *mean,
+                                                                 const float *rstd, int N, int C,
+                                                                 int accumulate) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N) return;
     const int C4 = C / 4;
-    floatx4 dwacc[NV], dbacc[NV], wv[NV];
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-        int k = lane + 64 * i;
-        dwacc[i] = dbacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-        wv[i] = k < C4 ? ((const floatx4 *)w)[k] : floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int rr = 0; rr < LN_BWD_ROWS / 4; rr++) {
-        const int row = blockIdx.x * LN_BWD_ROWS + rr * 4 + wave;
-        if (row >= N) break;
-        const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
-        const floatx4 *dy = (const floatx4 *)(dout + (long long)row * C);
-        const float mu = mean[row], rs = rstd[row];
-        floatx4 xh[NV], g[NV], d[NV];
-        float sg = 0.f, sgx = 0.f;
-#pragma unroll
-        for (int i = 0; i < NV; i++) {
-            int k = lane + 64 * i;
-            if (k < C4) {
-                xh[i] = (x[k] - mu) * rs;
-                d[i] = dy[k];
-                g[i] = d[i] * wv[i];
-                sg += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
-                floatx4 gx = g[i] * xh[i];
-                sgx += (gx[0] + gx[1]) + (gx[2] + gx[3]);
-                dwacc[i] += d[i] * xh[i];
-                dbacc[i] += d[i];
-            }
-        }
-        const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
-        floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
-#pragma unroll
-        for (int i = 0; i < NV; i++) {
-            int k = lane + 64 * i;
-            if (k < C4) {
-                floatx4 val = rs * (g[i] - mg - xh[i] * mgx);
-                dx[k] = accumulate ? dx[k] + val : val;
-            }
-        }
-    }
+    const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
+    const floatx4 *dy = (const floatx4 *)(dout + (long long)row * C);
+    floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
+    const float mu = mean[row], rs = rstd[row];
+    floatx4 xh[NV], g[NV], old[NV];
+    float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; i++) {
         int k = lane + 64 * i;
         if (k < C4) {
-            *(floatx4 *)&lds[wave * 2 * C + 4 * k] = dwacc[i];
-            *(floatx4 *)&lds[wave * 2 * C + C + 4 * k] = dbacc[i];
+            floatx4 xv = x[k], dv = dy[k], wv = ((const floatx4 *)w)[k];
+            old[i] = accumulate ? dx[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+            xh[i] = (xv - mu) * rs;
+            g[i] = dv * wv;
+            floatx4 gx = g[i] * xh[i];
+            sg += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
+            sgx += (gx[0] + gx[1]) + (gx[2] + gx[3]);
         }
     }
-    __syncthreads();
-    float *out = partial + (long long)blockIdx.x * 2 * C;
-    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x)
-        out[c] = ((lds[c] + lds[2 * C + c]) + lds[4 * C + c]) + lds[6 * C + c];
-}
-
-constexpr int COLSUM_ROWS = 128;  // rows per partial
-
-// Partial column sums: block (x, y) sums rows [128y, 128y+128) of 64 columns;
-// wavefront w takes rows w, w+4, ...; the four are combined in fixed order.
-__global__ __launch_bounds__(256) void colsum_partial_kernel(float *partial, const float *src, int R, int N,
-                                                             long long ld) {
-    __shared__ float lds[4][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = blockIdx.x * 64 + lane;
-    const int r0 = blockIdx.y * COLSUM_ROWS;
-    float acc = 0.f;
-    if (n < N) {
-        int r1 = min(R, r0 + COLSUM_ROWS);
-        for (int r = r0 + wave; r < r1; r += 4) acc += src[(long long)r * ld + n];
-    }
-    lds[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0 && n < N)
-        partial[(long long)blockIdx.y * N + n] = ((lds[0][lane] + lds[1][lane]) + lds[2][lane]) + lds[3][lane];
-}
-
-// dst[i] (+)= sum_p src[p*ld + i]: 32 columns x 8 partial groups per block;
-// group g sums p = g, g+8, ...; the 8 group sums are added in fixed order.
-__global__ __launch_bounds__(256) void sum_partials_kernel(float *dst, const float *src, int P, size_t n,
-                                                           size_t ld, int accumulate) {
-    __shared__ float lds[8][32];
-    const int col = threadIdx.x & 31, g = threadIdx.x >> 5;
-    const size_t i = (size_t)blockIdx.x * 32 + col;
-    float acc = 0.f;
-    if (i < n)
-        for (int p = g; p < P; p += 8) acc += src[(size_t)p * ld + i];
-    lds[g][col] = acc;
-    __syncthreads();
-    if (g == 0 && i < n) {
-        float s = lds[0][col];
+    const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
 #pragma unroll
-        for (int k = 1; k < 8; k++) s += lds[k][col];
-        dst[i] = accumulate ? dst[i] + s : s;
+    for (int i = 0; i < NV; i++) {
+        int k = lane + 64 * i;
+        if (k < C4) dx[k] = old[i] + rs * (g[i] - mg - xh[i] * mgx);
+    }
+}
+
+constexpr int COL_CHUNK = 32;  // rows per partial of a column reduction
+
+// LayerNorm backward, parameter gradients: per column c, over a chunk of 32
+// rows, sum dy * xhat and dy.  Block (x, y): 64 float4 columns x 4 row
+// lanes over rows [32y, 32y+32); the four row lanes are combined in a fixed
+// order.  partial[y] = [dw (C) | db (C)].
+__global__ __launch_bounds__(256) void layernorm_param_grad_kernel(float *partial, const float *dout,
+                                                                   const float *inp, const float *mean,
+                                                                   const float *rstd, int N, int C) {
+    __shared__ floatx4 lw[4][64], lb[4][64];
+    const int c4 = blockIdx.x * 64 + (threadIdx.x & 63), rl = threadIdx.x >> 6;
+    const int C4 = C / 4;
+    const int r0 = blockIdx.y * COL_CHUNK, r1 = min(N, r0 + COL_CHUNK);
+    floatx4 sw = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    if (c4 < C4) {
+#pragma unroll 4
+        for (int r = r0 + rl; r < r1; r += 4) {
+            floatx4 d = ((const floatx4 *)(dout + (long long)r * C))[c4];
+            floatx4 xv = ((const floatx4 *)(inp + (long long)r * C))[c4];
+            sw += d * ((xv - mean[r]) * rstd[r]);
+            sb += d;
+        }
+    }
+    lw[rl][threadIdx.x & 63] = sw;
+    lb[rl][threadIdx.x & 63] = sb;
+    __syncthreads();
+    if (rl == 0 && c4 < C4) {
+        const int l = threadIdx.x;
+        floatx4 w = ((lw[0][l] + lw[1][l]) + lw[2][l]) + lw[3][l];
+        floatx4 b = ((lb[0][l] + lb[1][l]) + lb[2][l]) + lb[3][l];
+        ((floatx4 *)(partial + (long long)blockIdx.y * 2 * C))[c4] = w;
+        ((floatx4 *)(partial + (long long)blockIdx.y * 2 * C + C))[c4] = b;
+    }
+}
+
+// dst[i] (+)= sum_{p < P} src[p*ld + i], 4 consecutive i per thread, p in order.
+__global__ __launch_bounds__(256) void sum_partials_kernel(float *dst, const float *src, int P, size_t n4,
+                                                           size_t ld4, int accumulate) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    const floatx4 *s4 = (const floatx4 *)src;
+    floatx4 acc = s4[i];
+    for (int p = 1; p < P; p++) acc += s4[(size_t)p * ld4 + i];
+    floatx4 *d4 = (floatx4 *)dst;
+    d4[i] = accumulate ? d4[i] + acc : acc;
+}
+
+// The same for many partials: 16 float4 columns x 16 partial lanes per block;
+// lane l sums p = l, l+16, ...; the 16 lane sums are added in a fixed order.
+__global__ __launch_bounds__(256) void sum_partials_wide_kernel(float *dst, const float *src, int P, size_t n4,
+                                                                size_t ld4, int accumulate) {
+    __shared__ floatx4 lds[16][16];
+    const int c = threadIdx.x & 15, pl = threadIdx.x >> 4;
+    const size_t i = (size_t)blockIdx.x * 16 + c;
+    const floatx4 *s4 = (const floatx4 *)src;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (i < n4)
+        for (int p = pl; p < P; p += 16) acc += s4[(size_t)p * ld4 + i];
+    lds[pl][c] = acc;
+    __syncthreads();
+    if (pl == 0 && i < n4) {
+        floatx4 t = lds[0][c];
+#pragma unroll
+        for (int k = 1; k < 16; k++) t += lds[k][c];
+        floatx4 *d4 = (floatx4 *)dst;
+        d4[i] = accumulate ? d4[i] + t : t;
     }
 }
 
@@ -499,46 +497,42 @@ hipError_t k_layernorm_forward(float *out, float *mean, float *rstd, const float
     return hipGetLastError();
 }
 
-int ln_partials(int N) { return (N + LN_BWD_ROWS - 1) / LN_BWD_ROWS; }
+int ln_partials(int N) { return (N + COL_CHUNK - 1) / COL_CHUNK; }
 
 hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partial, const float *dout,
                                 const float *inp, const float *w, const float *mean, const float *rstd, int N,
                                 int C, bool accumulate, hipStream_t s) {
     if (C % 4 || C > 2048) return hipErrorInvalidValue;
     int nv = (C / 4 + 63) / 64;
-    int P = ln_partials(N);
-    size_t lds = (size_t)4 * 2 * C * sizeof(float);
-    LN_DISPATCH(nv, layernorm_backward_kernel, dim3(P), dim3(256), lds, s, dinp, partial, dout, inp, w, mean, rstd,
-                N, C, accumulate ? 1 : 0);
+    LN_DISPATCH(nv, layernorm_backward_kernel, dim3(grid_for(N, 4)), dim3(256), 0, s, dinp, dout, inp, w, mean,
+                rstd, N, C, accumulate ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // partial rows are [dw | db]: sum each half into its own tensor
-    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(C, 32)), dim3(256), 0, s, dw, (const float *)partial, P,
-                       (size_t)C, (size_t)2 * C, 1);
+    const int P = ln_partials(N);
+    hipLaunchKernelGGL(layernorm_param_grad_kernel, dim3(grid_for(C / 4, 64), P), dim3(256), 0, s, partial, dout,
+                       inp, mean, rstd, N, C);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(C, 32)), dim3(256), 0, s, db,
-                       (const float *)(partial + C), P, (size_t)C, (size_t)2 * C, 1);
-    return hipGetLastError();
+    // partial rows are [dw | db]: sum each half into its own tensor
+    e = k_sum_partials_ld(dw, partial, P, (size_t)C, (size_t)2 * C, true, s);
+    if (e != hipSuccess) return e;
+    return k_sum_partials_ld(db, partial + C, P, (size_t)C, (size_t)2 * C, true, s);
 }
 
-int colsum_partials(int R) { return (R + COLSUM_ROWS - 1) / COLSUM_ROWS; }
-
-hipError_t k_colsum_accumulate(float *db, float *partial, const float *src, int R, int N, long long ld,
-                               hipStream_t s) {
-    int P = colsum_partials(R);
-    hipLaunchKernelGGL(colsum_partial_kernel, dim3(grid_for(N, 64), P), dim3(256), 0, s, partial, src, R, N, ld);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(N, 32)), dim3(256), 0, s, db, (const float *)partial, P,
-                       (size_t)N, (size_t)N, 1);
+hipError_t k_sum_partials_ld(float *dst, const float *src, int P, size_t n, size_t ld, bool accumulate,
+                             hipStream_t s) {
+    if (n % 4 || ld % 4 || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15) || P < 1) return hipErrorInvalidValue;
+    if (P >= 32)
+        hipLaunchKernelGGL(sum_partials_wide_kernel, dim3(grid_for(n / 4, 16)), dim3(256), 0, s, dst, src, P, n / 4,
+                           ld / 4, accumulate ? 1 : 0);
+    else
+        hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, dst, src, P, n / 4,
+                           ld / 4, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
 hipError_t k_sum_partials(float *dst, const float *src, int P, size_t n, bool accumulate, hipStream_t s) {
-    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(n, 32)), dim3(256), 0, s, dst, src, P, n, n,
-                       accumulate ? 1 : 0);
-    return hipGetLastError();
+    return k_sum_partials_ld(dst, src, P, n, n, accumulate, s);
 }
 
 hipError_t k_attn_softmax_forward(float *att, long long nrows, int T, hipStream_t s) {
