@@ -102,9 +102,11 @@ gpt2_status gpt2_query_sizes(const gpt2_config *cfg, int B, int T, gpt2_sizes *o
  *   qkv[BT][3C] att[B][NH][T][T] atty[BT][C] residual2[BT][C] ln2[BT][C]
  *   ln2_mean[BT] ln2_rstd[BT] fch[BT][4C] fch_gelu[BT][4C] residual3[BT][C]
  *   (each stacked over layers); lnf[BT][C] lnf_mean[BT] lnf_rstd[BT]
- *   logits[BT][Vp] losses[BT] loss[1].
- * att holds the softmax probabilities: row t is meaningful for u <= t and
- * zero for t < u < round_up(t+1, 128).  After a forward with targets,
+ *   logits[BT][Vp] losses[BT] loss[1] lse[L][B][NH][T].
+ * When the head dimension is 16, 32 or 64 attention runs fused: att has 0
+ * elements and lse holds each query's log-sum-exp of its scaled scores.
+ * Otherwise lse has 0 elements and att holds the softmax probabilities: row
+ * t is meaningful for u <= t and zero for t < u < round_up(t+1, 128).  After a forward with targets,
  * logits holds d(mean loss)/d(logits) instead (columns >= V are zero).
  * Returns GPT2_EINVAL for idx out of range; *name, *offset, *count may be
  * NULL.  The returned name is a static string. */

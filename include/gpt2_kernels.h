@@ -44,8 +44,9 @@ gpt2_status gpt2k_layernorm_backward(float *dinp, float *dw, float *db, const fl
                                      const float *w, const float *mean, const float *rstd, int N, int C,
                                      int accumulate, float *work, void *stream);
 
-/* Causal multi-head attention over qkv[B][T][3C] (q | k | v, heads of C/NH):
- * att[B][NH][T][T] = softmax probabilities (zero above the diagonal up to the
+/* Causal multi-head attention over qkv[B][T][3C] (q | k | v, heads of C/NH),
+ * with the score matrices materialised (any head dimension that is a
+ * multiple of 4): att[B][NH][T][T] = softmax probabilities (zero above the diagonal up to the
  * next multiple of 128 columns), atty[B][T][C] = heads concatenated. */
 gpt2_status gpt2k_attention_forward(float *atty, float *att, const float *qkv, int B, int T, int C, int NH,
                                     void *stream);
@@ -54,6 +55,17 @@ gpt2_status gpt2k_attention_forward(float *atty, float *att, const float *qkv, i
 size_t gpt2k_attention_backward_work(int B, int T, int C, int NH);
 gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const float *qkv, const float *att, int B,
                                      int T, int C, int NH, float *work, void *stream);
+
+/* The same attention fused (the path gpt2_forward / gpt2_backward take when
+ * the head dimension is 16, 32 or 64): no T x T matrix is kept.  The forward
+ * writes atty and lse[B][NH][T] (log-sum-exp of each query's scaled scores);
+ * the backward recomputes the probabilities from them and overwrites dqkv;
+ * work holds B*NH*T floats.  GPT2_EINVAL for other head dimensions. */
+gpt2_status gpt2k_flash_attention_forward(float *atty, float *lse, const float *qkv, int B, int T, int C, int NH,
+                                          void *stream);
+gpt2_status gpt2k_flash_attention_backward(float *dqkv, const float *datty, const float *qkv, const float *atty,
+                                           const float *lse, int B, int T, int C, int NH, float *work,
+                                           void *stream);
 
 /* tanh-GELU forward / backward (dinp = dout * gelu'(inp)), n % 4 == 0. */
 gpt2_status gpt2k_gelu_forward(float *out, const float *inp, size_t n, void *stream);

@@ -69,7 +69,13 @@ def test_activation_table_is_aligned_and_disjoint(g):
     cfg = synth.config("small")
     acts = g.layout(cfg, 32, 256, g.GPT2_ACTS)
     names = [a[0] for a in acts]
-    assert names[:3] == ["encoded", "ln1", "ln1_mean"] and names[-3:] == ["logits", "losses", "loss"]
+    assert names[:3] == ["encoded", "ln1", "ln1_mean"] and names[-4:] == ["logits", "losses", "loss", "lse"]
+    sizes = {n: c for n, _, c in acts}
+    # head dim 16: fused attention keeps lse, not the T x T probabilities
+    assert sizes["att"] == 0 and sizes["lse"] == cfg["L"] * 32 * cfg["NH"] * 256
+    cfg12 = synth.config(dict(L=1, C=48, NH=4, T=8, B=2, V=10))
+    sizes12 = {n: c for n, _, c in g.layout(cfg12, 2, 8, g.GPT2_ACTS)}
+    assert sizes12["att"] == 2 * 4 * 8 * 8 and sizes12["lse"] == 0
     end = 0
     for n, o, c in acts:
         assert o % 64 == 0 and o >= end, n

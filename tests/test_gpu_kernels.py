@@ -151,6 +151,49 @@ def test_attention(g, oracle_lib, B, T, C, NH):
         assert rel(gd[:, :, i], rd[:, :, i]) < 1e-4, "qkv"[i]
 
 
+FLASH_SHAPES = [(2, 64, 64, 4), (1, 100, 48, 3), (2, 256, 128, 2), (1, 132, 128, 8), (3, 20, 96, 3),
+                (1, 260, 128, 2), (2, 4, 64, 1)]
+
+
+@pytest.mark.parametrize("B,T,C,NH", FLASH_SHAPES)
+def test_flash_attention(g, oracle_lib, B, T, C, NH):
+    """The fused kernels: output, log-sum-exp and all three input gradients."""
+    import torch
+    rng = np.random.default_rng(B * T + C + 1)
+    qkv = f32(rng, B, T, 3 * C, scale=1.5)
+    atty = torch.empty(B * T * C, device="cuda")
+    lse = torch.empty(B * NH * T, device="cuda")
+    dq = dev(qkv)
+    g.flash_attention_forward(atty, lse, dq, B, T, C, NH)
+    ry, rpre, ratt = oracle_lib.attention_forward(qkv.astype(np.float64).ravel(), B, T, C, NH)
+    assert rel(host(atty), ry) < 1e-5
+    pre = rpre.reshape(B, NH, T, T)
+    low = np.tril(np.ones((T, T), dtype=bool))
+    mx = np.where(low, pre, -np.inf).max(-1)
+    rlse = mx + np.log(np.where(low, np.exp(pre - mx[..., None]), 0.0).sum(-1))
+    assert np.abs(host(lse).reshape(B, NH, T) - rlse).max() < 1e-5 * max(1.0, np.abs(rlse).max())
+    datty = f32(rng, B, T, C)
+    dqkv = torch.full((B * T * 3 * C,), float("nan"), device="cuda")
+    g.flash_attention_backward(dqkv, dev(datty), dq, atty, lse, B, T, C, NH)
+    rdqkv = np.zeros(B * T * 3 * C)
+    oracle_lib.attention_backward(rdqkv, datty.astype(np.float64).ravel(), qkv.astype(np.float64).ravel(), ratt,
+                                  B, T, C, NH)
+    gd = host(dqkv).reshape(B, T, 3, C)
+    rd = rdqkv.reshape(B, T, 3, C)
+    for i in range(3):
+        assert rel(gd[:, :, i], rd[:, :, i]) < 1e-4, "qkv"[i]
+
+
+def test_flash_attention_rejects_other_head_dims(g):
+    import torch
+    B, T, C, NH = 1, 8, 24, 2
+    x = torch.zeros(B * T * 3 * C, device="cuda")
+    with pytest.raises(g.Gpt2Error) as e:
+        g.flash_attention_forward(torch.empty(B * T * C, device="cuda"), torch.empty(B * NH * T, device="cuda"), x,
+                                  B, T, C, NH)
+    assert e.value.status == g.GPT2_EINVAL
+
+
 def test_attention_full_shape_sampled_heads(g, oracle_lib):
     """B=4, T=1024, C=768, 12 heads; the oracle recomputes 2 (b, h) pairs."""
     import torch
@@ -165,8 +208,19 @@ def test_attention_full_shape_sampled_heads(g, oracle_lib):
     datty = f32(rng, B, T, C)
     dqkv = torch.empty(B * T * 3 * C, device="cuda")
     g.attention_backward(dqkv, dev(datty), dq, att, B, T, C, NH)
-    gy = host(atty).reshape(B, T, C)
-    gd = host(dqkv).reshape(B, T, 3, C)
+    # the fused path at the same shape, on the same inputs
+    fy = torch.empty(B * T * C, device="cuda")
+    flse = torch.empty(B * NH * T, device="cuda")
+    g.flash_attention_forward(fy, flse, dq, B, T, C, NH)
+    fd = torch.empty(B * T * 3 * C, device="cuda")
+    g.flash_attention_backward(fd, dev(datty), dq, fy, flse, B, T, C, NH)
+    for gy, gd in [(host(atty).reshape(B, T, C), host(dqkv).reshape(B, T, 3, C)),
+                   (host(fy).reshape(B, T, C), host(fd).reshape(B, T, 3, C))]:
+        check_sampled_heads(oracle_lib, qkv, datty, gy, gd, B, T, C, NH)
+
+
+def check_sampled_heads(oracle_lib, qkv, datty, gy, gd, B, T, C, NH):
+    hd = C // NH
     for b, h in [(0, 0), (3, 11)]:
         sl = slice(h * hd, (h + 1) * hd)
         sub = np.ascontiguousarray(qkv[b:b + 1].reshape(1, T, 3, C)[:, :, :, sl]).astype(np.float64)

@@ -58,6 +58,8 @@ CASES = {
     "degenerate": synth.config(dict(L=2, C=32, NH=2, T=4, B=1, V=11, maxT=4)),
     "small_b4": synth.config("small", B=4),
     "hd64": synth.config(dict(L=2, C=128, NH=2, T=132, B=2, V=300, maxT=132, tokens="zipf")),
+    # head dim 12: attention takes the materialised-score path
+    "hd12": synth.config(dict(L=2, C=48, NH=4, T=40, B=2, V=50, maxT=40)),
 }
 
 

@@ -19,6 +19,7 @@
 
 #include "../../include/gpt2.h"
 #include "../../include/gpt2_kernels.h"
+#include "attention.h"
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -35,12 +36,12 @@ const char *kParamNames[16] = {"wte",  "wpe",  "ln1w", "ln1b", "qkvw", "qkvb",  
 
 enum ActId {
     A_ENCODED, A_LN1, A_LN1_MEAN, A_LN1_RSTD, A_QKV, A_ATT, A_ATTY, A_RES2, A_LN2, A_LN2_MEAN, A_LN2_RSTD,
-    A_FCH, A_FCH_GELU, A_RES3, A_LNF, A_LNF_MEAN, A_LNF_RSTD, A_LOGITS, A_LOSSES, A_LOSS, NUM_ACTS
+    A_FCH, A_FCH_GELU, A_RES3, A_LNF, A_LNF_MEAN, A_LNF_RSTD, A_LOGITS, A_LOSSES, A_LOSS, A_LSE, NUM_ACTS
 };
 const char *kActNames[NUM_ACTS] = {"encoded", "ln1",      "ln1_mean", "ln1_rstd",  "qkv",      "att",
                                    "atty",    "residual2", "ln2",     "ln2_mean",  "ln2_rstd", "fch",
                                    "fch_gelu", "residual3", "lnf",    "lnf_mean",  "lnf_rstd", "logits",
-                                   "losses",  "loss"};
+                                   "losses",  "loss",     "lse"};
 
 // How a GEMM is launched: tile shape and number of K splits.
 struct Plan {
@@ -107,6 +108,7 @@ Plan plan_gemm(int M, int N, int K, long long batches, bool allow_split) {
 
 struct Layout {
     int B, T, C, L, NH, V, Vp, maxT, hd;
+    bool flash;  // fused attention (no T x T matrices kept)
     long long BT;
     size_t poff[16], pcnt[16], nparams;
     size_t aoff[NUM_ACTS], acnt[NUM_ACTS], nacts;
@@ -155,10 +157,12 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
         off += n[i];
     }
     l.nparams = off;
-    size_t a[NUM_ACTS] = {BT * C,      L * BT * C,  L * BT,     L * BT,     L * BT * 3 * C, L * B * NH * TT,
+    l.flash = flash_attention_supported(l.hd);
+    const size_t natt = l.flash ? 0 : L * B * NH * TT, nlse = l.flash ? L * B * NH * (size_t)T : 0;
+    size_t a[NUM_ACTS] = {BT * C,      L * BT * C,  L * BT,     L * BT,     L * BT * 3 * C, natt,
                           L * BT * C,  L * BT * C,  L * BT * C, L * BT,     L * BT,         L * BT * 4 * C,
                           L * BT * 4 * C, L * BT * C, BT * C,   BT,         BT,             BT * (size_t)l.Vp,
-                          BT,          1};
+                          BT,          1,           nlse};
     off = 0;
     for (int i = 0; i < NUM_ACTS; i++) {
         l.aoff[i] = off;
@@ -173,7 +177,7 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.w_datty = off; off = align_up(off + BT * C);
     l.w_dqkv = off; off = align_up(off + BT * 3 * C);
     l.w_dfch = off; off = align_up(off + BT * 4 * C);
-    l.w_datt = off; off = align_up(off + (size_t)B * NH * TT);
+    l.w_datt = off; off = align_up(off + (l.flash ? (size_t)B * NH * T : (size_t)B * NH * TT));
     l.w_part = off; off = align_up(off + (size_t)ln_partials((int)BT) * 2 * C);
     // split-K partial products of the GEMMs that may split (weight gradients, dlnf)
     size_t sk = 0;
@@ -239,6 +243,8 @@ gpt2_status fail(gpt2_model *m, gpt2_status st, const std::string &msg) {
     } while (0)
 
 #define KRUN(model, name, bytes, call) HIPCK(model, timed(name, 0.0, (double)(bytes), [&]() { return call; }))
+#define KRUNF(model, name, flops, bytes, call) \
+    HIPCK(model, timed(name, (double)(flops), (double)(bytes), [&]() { return call; }))
 
 // ---------------------------------------------------------------- per-launch timing
 
@@ -290,6 +296,17 @@ const char *gemm_name(const GemmDesc &d) {
     int t = d.tile >= 1 && d.tile <= 3 ? d.tile - 1 : 0;
     int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
     return names[t][l];
+}
+
+// "kernel<hd>" as a kernel-trace profiler shows the fused attention kernels
+// (static strings: profile records keep the pointer).
+enum { FL_FWD = 0, FL_DQ = 1, FL_DKDV = 2 };
+const char *flash_name(int which, int hd) {
+    static const char *names[3][3] = {
+        {"flash_fwd_kernel<16>", "flash_fwd_kernel<32>", "flash_fwd_kernel<64>"},
+        {"flash_bwd_dq_kernel<16>", "flash_bwd_dq_kernel<32>", "flash_bwd_dq_kernel<64>"},
+        {"flash_bwd_dkdv_kernel<16>", "flash_bwd_dkdv_kernel<32>", "flash_bwd_dkdv_kernel<64>"}};
+    return names[which][hd == 16 ? 0 : (hd == 32 ? 1 : 2)];
 }
 
 // Every GEMM of the step goes through here (`site` overrides the caller's).
@@ -564,7 +581,12 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
             HIPCK(m, linear_fwd(qkv, ln1, P + l.poff[4] + li * 3 * c * c, P + l.poff[5] + li * 3 * c, BT, C, 3 * C,
                             EPI_STORE, nullptr, nullptr, s));
         }
-        {
+        if (l.flash) {
+            float *lse = A + l.aoff[A_LSE] + (size_t)li * B * NH * T;
+            const double tri = 0.5 * T * (T + 1.0) * B * NH;
+            KRUNF(m, flash_name(FL_FWD, l.hd), 4.0 * tri * l.hd, 16.0 * BTC,
+                 flash_attention_forward(atty, lse, qkv, B, T, C, NH, s));
+        } else {
             Site site_("attn_fwd");
             HIPCK(m, attention_fwd(atty, att, qkv, B, T, C, NH, s));
         }
@@ -692,7 +714,14 @@ gpt2_status gpt2_backward(gpt2_model *m) {
             HIPCK(m, linear_bwd_dinp(datty, dres, aw, BT, C, C, EPI_STORE, nullptr, nullptr, s));
         }
         // attention
-        {
+        if (l.flash) {
+            const float *lse = A + l.aoff[A_LSE] + (size_t)li * B * NH * T;
+            const double tri = 0.5 * T * (T + 1.0) * B * NH;
+            KRUNF(m, flash_name(FL_DQ, l.hd), 4.0 * tri * l.hd, 20.0 * BTC,
+                 flash_attention_backward_dq(dqkv, dscore, datty, qkv, atty, lse, B, T, C, NH, s));
+            KRUNF(m, flash_name(FL_DKDV, l.hd), 4.0 * tri * l.hd, 24.0 * BTC,
+                 flash_attention_backward_dkdv(dqkv, dscore, datty, qkv, lse, B, T, C, NH, s));
+        } else {
             Site site_("attn_bwd");
             HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
         }
@@ -859,6 +888,24 @@ gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const floa
                                      int T, int C, int NH, float *work, void *stream) {
     if (!attn_shape_ok(B, T, C, NH)) return fail(nullptr, GPT2_EINVAL, "attention shape not supported");
     KCK(attention_bwd(dqkv, work, datty, qkv, att, B, T, C, NH, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_flash_attention_forward(float *atty, float *lse, const float *qkv, int B, int T, int C, int NH,
+                                          void *stream) {
+    if (!attn_shape_ok(B, T, C, NH) || !flash_attention_supported(C / NH))
+        return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024, T % 4 == 0");
+    KCK(flash_attention_forward(atty, lse, qkv, B, T, C, NH, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_flash_attention_backward(float *dqkv, const float *datty, const float *qkv, const float *atty,
+                                           const float *lse, int B, int T, int C, int NH, float *work,
+                                           void *stream) {
+    if (!attn_shape_ok(B, T, C, NH) || !flash_attention_supported(C / NH))
+        return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024, T % 4 == 0");
+    KCK(flash_attention_backward_dq(dqkv, work, datty, qkv, atty, lse, B, T, C, NH, (hipStream_t)stream));
+    KCK(flash_attention_backward_dkdv(dqkv, work, datty, qkv, lse, B, T, C, NH, (hipStream_t)stream));
     return GPT2_OK;
 }
 

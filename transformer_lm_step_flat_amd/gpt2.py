@@ -73,6 +73,8 @@ _SIGS = {
     "gpt2k_layernorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
     "gpt2k_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P],
     "gpt2k_attention_backward": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
+    "gpt2k_flash_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P],
+    "gpt2k_flash_attention_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
     "gpt2k_gelu_forward": [_P, _P, _Z, _P],
     "gpt2k_gelu_backward": [_P, _P, _P, _Z, _P],
     "gpt2k_crossentropy": [_P, _P, _P, _P, _I, _I, _I, _P],
@@ -304,6 +306,17 @@ def attention_backward(dqkv, datty, qkv, att, B, T, C, NH):
                        device=qkv.device)
     _check(lib().gpt2k_attention_backward(_ptr(dqkv), _ptr(datty), _ptr(qkv), _ptr(att), B, T, C, NH, _ptr(work),
                                           _s()))
+    return work
+
+
+def flash_attention_forward(atty, lse, qkv, B, T, C, NH):
+    _check(lib().gpt2k_flash_attention_forward(_ptr(atty), _ptr(lse), _ptr(qkv), B, T, C, NH, _s()))
+
+
+def flash_attention_backward(dqkv, datty, qkv, atty, lse, B, T, C, NH):
+    work = torch.empty(max(1, B * NH * T), dtype=torch.float32, device=qkv.device)
+    _check(lib().gpt2k_flash_attention_backward(_ptr(dqkv), _ptr(datty), _ptr(qkv), _ptr(atty), _ptr(lse), B, T, C,
+                                                NH, _ptr(work), _s()))
     return work
 
 
