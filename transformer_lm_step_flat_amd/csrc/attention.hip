@@ -72,18 +72,42 @@ struct TileLoader {
 };
 
 // s^T[mb] (keys 32mb.., this lane's query) = X[key][:] . frag   with X a [KB][pitch] LDS tile.
+// The two 32-key halves are independent accumulation chains, interleaved.
 template <int HD>
 __device__ __forceinline__ void keys_times_frag(floatx16 (&s)[2], const float *X, int pitch, const float *frag,
                                                 int l32, int h) {
+    s[0] = zero16();
+    s[1] = zero16();
 #pragma unroll
-    for (int mb = 0; mb < 2; mb++) {
-        s[mb] = zero16();
+    for (int j4 = 0; j4 < HD / 8; j4++) {
+        floatx4 a0 = *(const floatx4 *)&X[l32 * pitch + h * (HD / 2) + 4 * j4];
+        floatx4 a1 = *(const floatx4 *)&X[(32 + l32) * pitch + h * (HD / 2) + 4 * j4];
 #pragma unroll
-        for (int j4 = 0; j4 < HD / 8; j4++) {
-            floatx4 a = *(const floatx4 *)&X[(32 * mb + l32) * pitch + h * (HD / 2) + 4 * j4];
+        for (int e = 0; e < 4; e++) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[e], frag[4 * j4 + e], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[e], frag[4 * j4 + e], s[1], 0, 0, 0);
+        }
+    }
+}
+
+// Both products of the dq kernel at once (four interleaved chains):
+// s^T = K frag_q, dp^T = V frag_do.
+template <int HD>
+__device__ __forceinline__ void keys_times_two_frags(floatx16 (&s)[2], floatx16 (&dp)[2], const float *K,
+                                                     const float *V, int pitch, const float *fq, const float *fdo,
+                                                     int l32, int h) {
+    s[0] = s[1] = dp[0] = dp[1] = zero16();
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], frag[4 * j4 + e], s[mb], 0, 0, 0);
+    for (int j4 = 0; j4 < HD / 8; j4++) {
+        const int c = h * (HD / 2) + 4 * j4;
+        floatx4 k0 = *(const floatx4 *)&K[l32 * pitch + c], k1 = *(const floatx4 *)&K[(32 + l32) * pitch + c];
+        floatx4 v0 = *(const floatx4 *)&V[l32 * pitch + c], v1 = *(const floatx4 *)&V[(32 + l32) * pitch + c];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(k0[e], fq[4 * j4 + e], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(k1[e], fq[4 * j4 + e], s[1], 0, 0, 0);
+            dp[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0[e], fdo[4 * j4 + e], dp[0], 0, 0, 0);
+            dp[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1[e], fdo[4 * j4 + e], dp[1], 0, 0, 0);
         }
     }
 }
@@ -115,13 +139,15 @@ __device__ __forceinline__ void accum_xt_pt_any(floatx16 (&acc)[HeadBlocks<HD>::
         }
 }
 
-// Write a per-wave transposed accumulator (lane: one query row t, registers:
-// head dims) to global rows through LDS so that the stores are row-contiguous.
+// Write a per-wave transposed accumulator (lane: one row, registers: head
+// dims) to `nrows` global rows (row stride rs) through LDS, so that the
+// stores are row-contiguous.  Each lane's values are multiplied by its `mul`.
 // Called by every wavefront of the workgroup (it contains a barrier); each
-// wavefront uses its own LDS region.
+// wavefront passes its own LDS region of 32 x pitch floats.
 template <int HD>
-__device__ __forceinline__ void store_rows_t(float *dst, long long rs, int t0, int T, const floatx16 (&acc)[HeadBlocks<HD>::N],
-                                             float mul, float *lds, int pitch, int lane) {
+__device__ __forceinline__ void store_rows_t(float *dst, long long rs, int nrows,
+                                             const floatx16 (&acc)[HeadBlocks<HD>::N], float mul, float *lds,
+                                             int pitch, int lane) {
     const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int md = 0; md < HeadBlocks<HD>::N; md++)
@@ -131,34 +157,71 @@ __device__ __forceinline__ void store_rows_t(float *dst, long long rs, int t0, i
             if (d < HD) lds[l32 * pitch + d] = acc[md][r] * mul;
         }
     __syncthreads();
-    // row-contiguous write-back: HD/4 float4 per row, 32 rows
     for (int f = lane; f < QW * HD / 4; f += 64) {
         const int row = f / (HD / 4), c4 = f % (HD / 4);
-        if (t0 + row < T) *(floatx4 *)(dst + (long long)(t0 + row) * rs + 4 * c4) = *(const floatx4 *)&lds[row * pitch + 4 * c4];
+        if (row < nrows) *(floatx4 *)(dst + (long long)row * rs + 4 * c4) = *(const floatx4 *)&lds[row * pitch + 4 * c4];
     }
+}
+
+// ------------------------------------------------------------------ work split
+//
+// Long causal rows are split so that no workgroup walks more than a few
+// blocks in sequence.  Forward and dq: a workgroup takes 128 queries and one
+// chunk of at most 256 of the keys they need; dk/dv: 128 keys and one chunk of
+// at most 256 of the queries that see them.  A block whose range fits in one
+// chunk writes its result directly; otherwise each chunk writes a partial
+// (normalised output and log-sum-exp, or a gradient sum) to a workspace and a
+// combine kernel merges the chunks in order.
+
+constexpr int QBLK = QW * NWAVE;  // rows of a workgroup: 128
+constexpr int KCH = 256;          // keys per chunk (forward, dq)
+constexpr int QCH = 256;          // queries per chunk (dk/dv)
+
+__host__ __device__ inline int q_items(int qb, int T) {
+    const int kend = min(T, (qb + 1) * QBLK);
+    return (kend + KCH - 1) / KCH;
+}
+__host__ __device__ inline int k_items(int kb, int T) { return (T - kb * QBLK + QCH - 1) / QCH; }
+
+// block index and chunk of workgroup x; `first` = item index of the block's chunk 0
+template <bool KEYS>
+__device__ __forceinline__ void decode_item(int x, int T, int &blk, int &chunk, int &first) {
+    blk = 0;
+    first = 0;
+    for (;;) {
+        const int n = KEYS ? k_items(blk, T) : q_items(blk, T);
+        if (x < first + n) break;
+        first += n;
+        blk++;
+    }
+    chunk = x - first;
 }
 
 // ------------------------------------------------------------------ forward
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(float *__restrict__ out, float *__restrict__ lse,
+                                                           float *__restrict__ ws, float *__restrict__ wlse,
                                                            const float *__restrict__ qkv, int T, int C, int NH,
-                                                           float scale) {
+                                                           int items, float scale) {
     constexpr int P = HD + 4;
     __shared__ __attribute__((aligned(16))) float Ks[KB * P];
     __shared__ __attribute__((aligned(16))) float Vs[KB * P];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
-    const int nqb = (T + QW * NWAVE - 1) / (QW * NWAVE);
-    const int q0 = (nqb - 1 - blockIdx.x) * QW * NWAVE;  // longest rows first
+    int qb, chunk, first;
+    decode_item<false>(blockIdx.x, T, qb, chunk, first);
+    const int nch = q_items(qb, T);
+    const int q0 = qb * QBLK;
     const int tq0 = q0 + wave * QW, t = tq0 + l32;
     const long long rs = 3LL * C;
-    const float *qb = qkv + (long long)b * T * rs + hd_off;
+    const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
 
     float qf[HD / 2];
 #pragma unroll
     for (int j4 = 0; j4 < HD / 8; j4++) {
-        floatx4 v = t < T ? *(const floatx4 *)(qb + (long long)t * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 v = t < T ? *(const floatx4 *)(qb_ptr + (long long)t * rs + h * (HD / 2) + 4 * j4)
+                          : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; e++) qf[4 * j4 + e] = v[e] * scale;
     }
@@ -167,18 +230,18 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(float *__restrict__ o
     for (int md = 0; md < HeadBlocks<HD>::N; md++) o[md] = zero16();
     float m = -INFINITY, lsum = 0.0f;
 
-    const int kend = min(T, q0 + QW * NWAVE);
+    const int kc0 = chunk * KCH, kc1 = min(min(T, q0 + QBLK), kc0 + KCH);
     TileLoader<HD, KB> lk, lv;
-    lk.load(qb + C, rs, 0, T, tid);
-    lv.load(qb + 2 * C, rs, 0, T, tid);
-    for (int k0 = 0; k0 < kend; k0 += KB) {
+    lk.load(qb_ptr + C, rs, kc0, T, tid);
+    lv.load(qb_ptr + 2 * C, rs, kc0, T, tid);
+    for (int k0 = kc0; k0 < kc1; k0 += KB) {
         __syncthreads();
         lk.store(Ks, P, tid);
         lv.store(Vs, P, tid);
         __syncthreads();
-        if (k0 + KB < kend) {
-            lk.load(qb + C, rs, k0 + KB, T, tid);
-            lv.load(qb + 2 * C, rs, k0 + KB, T, tid);
+        if (k0 + KB < kc1) {
+            lk.load(qb_ptr + C, rs, k0 + KB, T, tid);
+            lv.load(qb_ptr + 2 * C, rs, k0 + KB, T, tid);
         }
         if (k0 > tq0 + QW - 1) continue;  // every key of the block is after this wave's queries
         floatx16 s[2];
@@ -194,13 +257,15 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(float *__restrict__ o
                 mx = fmaxf(mx, v);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-        const float alpha = __expf(m - mx);
+        // a query that sees no key yet keeps m = -inf; exponentiate against 0 then
+        const float mref = mx == -INFINITY ? 0.0f : mx;
+        const float alpha = __expf(m - mref);
         float ps = 0.0f;
 #pragma unroll
         for (int mb = 0; mb < 2; mb++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const float p = __expf(s[mb][r] - mx);
+                const float p = __expf(s[mb][r] - mref);
                 s[mb][r] = p;
                 ps += p;
             }
@@ -213,29 +278,74 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(float *__restrict__ o
     }
     __syncthreads();  // the K/V tiles become per-wave transpose space
     float *tr = (wave < 2 ? Ks : Vs) + (wave & 1) * QW * P;
-    store_rows_t<HD>(out + (long long)b * T * C + hd_off, C, tq0, T, o, 1.0f / lsum, tr, P, lane);
-    if (h == 0 && t < T) lse[(long long)bh * T + t] = m + __logf(lsum);
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    const float lse_t = lsum > 0.0f ? m + __logf(lsum) : -INFINITY;
+    if (nch == 1) {
+        store_rows_t<HD>(out + ((long long)b * T + tq0) * C + hd_off, C, T - tq0, o, inv, tr, P, lane);
+        if (h == 0 && t < T) lse[(long long)bh * T + t] = lse_t;
+    } else {
+        const long long item = (long long)bh * items + first + chunk;
+        store_rows_t<HD>(ws + (item * QBLK + wave * QW) * HD, HD, QW, o, inv, tr, P, lane);
+        if (h == 0) wlse[item * QBLK + wave * QW + l32] = lse_t;
+    }
+}
+
+// Merge the chunk partials of the forward: lse = log sum_c exp(lse_c);
+// out = sum_c exp(lse_c - lse) out_c (chunks in order).  One thread per
+// (row, 4 head dims) of the blocks that were split.
+template <int HD>
+__global__ __launch_bounds__(256) void flash_fwd_merge_kernel(float *__restrict__ out, float *__restrict__ lse,
+                                                              const float *__restrict__ ws,
+                                                              const float *__restrict__ wlse, int T, int C, int NH,
+                                                              int BNH, int items) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int d4 = (int)(i % (HD / 4));
+    const long long r = i / (HD / 4);
+    const int t = (int)(r % T), bh = (int)(r / T);
+    if (bh >= BNH) return;
+    const int qb = t / QBLK, nch = q_items(qb, T);
+    if (nch == 1) return;  // written directly by the forward kernel
+    int first = 0;
+    for (int q = 0; q < qb; q++) first += q_items(q, T);
+    const long long base = (long long)bh * items + first;
+    const int row = t % QBLK;
+    float mx = -INFINITY;
+    for (int c = 0; c < nch; c++) mx = fmaxf(mx, wlse[(base + c) * QBLK + row]);
+    float ssum = 0.0f;
+    for (int c = 0; c < nch; c++) ssum += __expf(wlse[(base + c) * QBLK + row] - mx);
+    const float L = mx + __logf(ssum);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nch; c++) {
+        const float w = __expf(wlse[(base + c) * QBLK + row] - L);
+        acc += w * *(const floatx4 *)(ws + ((base + c) * QBLK + row) * HD + 4 * d4);
+    }
+    const int b = bh / NH, hd_off = (bh % NH) * HD;
+    *(floatx4 *)(out + ((long long)b * T + t) * C + hd_off + 4 * d4) = acc;
+    if (d4 == 0) lse[(long long)bh * T + t] = L;
 }
 
 // ------------------------------------------------------------------ backward: dq and D
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict__ dqkv, float *__restrict__ Dbuf,
+                                                              float *__restrict__ ws,
                                                               const float *__restrict__ dout,
                                                               const float *__restrict__ qkv,
                                                               const float *__restrict__ out,
                                                               const float *__restrict__ lse, int T, int C, int NH,
-                                                              float scale) {
+                                                              int items, float scale) {
     constexpr int P = HD + 4;
     __shared__ __attribute__((aligned(16))) float Ks[KB * P];
     __shared__ __attribute__((aligned(16))) float Vs[KB * P];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
-    const int nqb = (T + QW * NWAVE - 1) / (QW * NWAVE);
-    const int q0 = (nqb - 1 - blockIdx.x) * QW * NWAVE;
+    int qb, chunk, first;
+    decode_item<false>(blockIdx.x, T, qb, chunk, first);
+    const int nch = q_items(qb, T);
+    const int q0 = qb * QBLK;
     const int tq0 = q0 + wave * QW, t = tq0 + l32;
     const long long rs = 3LL * C;
-    const float *qb = qkv + (long long)b * T * rs + hd_off;
+    const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
     const float *dob = dout + (long long)b * T * C + hd_off;
     const float *ob = out + (long long)b * T * C + hd_off;
 
@@ -244,7 +354,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
 #pragma unroll
     for (int j4 = 0; j4 < HD / 8; j4++) {
         const bool ok = t < T;
-        floatx4 q = ok ? *(const floatx4 *)(qb + (long long)t * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 q = ok ? *(const floatx4 *)(qb_ptr + (long long)t * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
         floatx4 d = ok ? *(const floatx4 *)(dob + (long long)t * C + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
         floatx4 o = ok ? *(const floatx4 *)(ob + (long long)t * C + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -256,29 +366,28 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
     }
     const float Dt = dsum + __shfl_xor(dsum, 32, WAVE);
     const float lt = t < T ? lse[(long long)bh * T + t] : 0.0f;
-    if (h == 0 && t < T) Dbuf[(long long)bh * T + t] = Dt;
+    if (chunk == 0 && h == 0 && t < T) Dbuf[(long long)bh * T + t] = Dt;
 
     floatx16 dq[HeadBlocks<HD>::N];
 #pragma unroll
     for (int md = 0; md < HeadBlocks<HD>::N; md++) dq[md] = zero16();
 
-    const int kend = min(T, q0 + QW * NWAVE);
+    const int kc0 = chunk * KCH, kc1 = min(min(T, q0 + QBLK), kc0 + KCH);
     TileLoader<HD, KB> lk, lv;
-    lk.load(qb + C, rs, 0, T, tid);
-    lv.load(qb + 2 * C, rs, 0, T, tid);
-    for (int k0 = 0; k0 < kend; k0 += KB) {
+    lk.load(qb_ptr + C, rs, kc0, T, tid);
+    lv.load(qb_ptr + 2 * C, rs, kc0, T, tid);
+    for (int k0 = kc0; k0 < kc1; k0 += KB) {
         __syncthreads();
         lk.store(Ks, P, tid);
         lv.store(Vs, P, tid);
         __syncthreads();
-        if (k0 + KB < kend) {
-            lk.load(qb + C, rs, k0 + KB, T, tid);
-            lv.load(qb + 2 * C, rs, k0 + KB, T, tid);
+        if (k0 + KB < kc1) {
+            lk.load(qb_ptr + C, rs, k0 + KB, T, tid);
+            lv.load(qb_ptr + 2 * C, rs, k0 + KB, T, tid);
         }
         if (k0 > tq0 + QW - 1) continue;
         floatx16 s[2], dp[2];
-        keys_times_frag<HD>(s, Ks, P, qf, l32, h);
-        keys_times_frag<HD>(dp, Vs, P, dof, l32, h);
+        keys_times_two_frags<HD>(s, dp, Ks, Vs, P, qf, dof, l32, h);
 #pragma unroll
         for (int mb = 0; mb < 2; mb++)
 #pragma unroll
@@ -291,36 +400,44 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
     }
     __syncthreads();
     float *tr = (wave < 2 ? Ks : Vs) + (wave & 1) * QW * P;
-    store_rows_t<HD>(dqkv + (long long)b * T * rs + hd_off, rs, tq0, T, dq, scale, tr, P, lane);
+    if (nch == 1) {
+        store_rows_t<HD>(dqkv + ((long long)b * T + tq0) * rs + hd_off, rs, T - tq0, dq, scale, tr, P, lane);
+    } else {
+        const long long item = (long long)bh * items + first + chunk;
+        store_rows_t<HD>(ws + (item * QBLK + wave * QW) * HD, HD, QW, dq, scale, tr, P, lane);
+    }
 }
 
 // ------------------------------------------------------------------ backward: dk and dv
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv,
+__global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv, float *__restrict__ ws,
                                                                 const float *__restrict__ dout,
                                                                 const float *__restrict__ qkv,
                                                                 const float *__restrict__ lse,
                                                                 const float *__restrict__ Dbuf, int T, int C, int NH,
-                                                                float scale) {
+                                                                int items, float scale) {
     constexpr int P = HD + 4;
     __shared__ __attribute__((aligned(16))) float Qs[TB * P];
     __shared__ __attribute__((aligned(16))) float Os[TB * P];  // dO tile
     __shared__ float Ls[TB], Ds[TB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
-    const int u0w = blockIdx.x * QW * NWAVE;  // first key of the workgroup (earliest keys: most queries)
+    int kb, chunk, first;
+    decode_item<true>(blockIdx.x, T, kb, chunk, first);
+    const int nch = k_items(kb, T);
+    const int u0w = kb * QBLK;
     const int u0 = u0w + wave * QW, u = u0 + l32;
     const long long rs = 3LL * C;
-    const float *qb = qkv + (long long)b * T * rs + hd_off;
+    const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
     const float *dob = dout + (long long)b * T * C + hd_off;
 
     float kf[HD / 2], vf[HD / 2];
 #pragma unroll
     for (int j4 = 0; j4 < HD / 8; j4++) {
         const bool ok = u < T;
-        floatx4 k = ok ? *(const floatx4 *)(qb + C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-        floatx4 v = ok ? *(const floatx4 *)(qb + 2 * C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 k = ok ? *(const floatx4 *)(qb_ptr + C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 v = ok ? *(const floatx4 *)(qb_ptr + 2 * C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             kf[4 * j4 + e] = k[e] * scale;
@@ -331,11 +448,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
 #pragma unroll
     for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) dk[nd] = dv[nd] = zero16();
 
+    const int tc0 = u0w + chunk * QCH, tc1 = min(T, tc0 + QCH);
     TileLoader<HD, TB> lq, lo;
-    const int tstart = u0w - u0w % TB;
-    lq.load(qb, rs, tstart, T, tid);
-    lo.load(dob, C, tstart, T, tid);
-    for (int t0 = tstart; t0 < T; t0 += TB) {
+    lq.load(qb_ptr, rs, tc0, T, tid);
+    lo.load(dob, C, tc0, T, tid);
+    for (int t0 = tc0; t0 < tc1; t0 += TB) {
         __syncthreads();
         lq.store(Qs, P, tid);
         lo.store(Os, P, tid);
@@ -344,12 +461,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             Ds[tid] = t0 + tid < T ? Dbuf[(long long)bh * T + t0 + tid] : 0.0f;
         }
         __syncthreads();
-        if (t0 + TB < T) {
-            lq.load(qb, rs, t0 + TB, T, tid);
+        if (t0 + TB < tc1) {
+            lq.load(qb_ptr, rs, t0 + TB, T, tid);
             lo.load(dob, C, t0 + TB, T, tid);
         }
         if (t0 + TB - 1 < u0) continue;  // every query of the block precedes this wave's keys
-        // s[t][u] (rows: queries, column: this lane's key) and dp[t][u]
         floatx16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int j4 = 0; j4 < HD / 8; j4++) {
@@ -365,10 +481,9 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         for (int r = 0; r < 16; r++) {
             const int tl = row_of(r, h), tt = t0 + tl;
             const float p = (tt < u || tt >= T || u >= T) ? 0.0f : __expf(s[r] - Ls[tl]);
-            s[r] = p;                         // p
-            dp[r] = p * (dp[r] - Ds[tl]);     // ds
+            s[r] = p;                      // p
+            dp[r] = p * (dp[r] - Ds[tl]);  // ds
         }
-        // dv[u][d] += sum_t p[t][u] dO[t][d];  dk[u][d] += sum_t ds[t][u] q[t][d]
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int tl = row_of(r, h);
@@ -382,9 +497,19 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             }
         }
     }
-    // dk, dv: lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
-    float *dkb = dqkv + (long long)b * T * rs + C + hd_off;
-    float *dvb = dqkv + (long long)b * T * rs + 2 * C + hd_off;
+    // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
+    float *dkb, *dvb;
+    long long krs;
+    if (nch == 1) {
+        dkb = dqkv + (long long)b * T * rs + C + hd_off;
+        dvb = dqkv + (long long)b * T * rs + 2 * C + hd_off;
+        krs = rs;
+    } else {
+        const long long item = (long long)bh * items + first + chunk;
+        dkb = ws + item * 2 * QBLK * HD - (long long)u0w * HD;  // rows indexed by the key u
+        dvb = dkb + QBLK * HD;
+        krs = HD;
+    }
 #pragma unroll
     for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
         const int d = 32 * nd + l32;
@@ -393,35 +518,93 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         for (int r = 0; r < 16; r++) {
             const int uu = u0 + row_of(r, h);
             if (uu < T) {
-                dkb[(long long)uu * rs + d] = dk[nd][r] * scale;
-                dvb[(long long)uu * rs + d] = dv[nd][r];
+                dkb[(long long)uu * krs + d] = dk[nd][r] * scale;
+                dvb[(long long)uu * krs + d] = dv[nd][r];
             }
         }
     }
 }
 
+// Sum the chunk partials of dq (KEYS = false: rows are queries, one block
+// per 128 queries) or of dk and dv (KEYS = true) into dqkv, chunks in order.
+template <int HD, bool KEYS>
+__global__ __launch_bounds__(256) void flash_bwd_sum_kernel(float *__restrict__ dqkv, const float *__restrict__ ws,
+                                                            int T, int C, int NH, int BNH, int items) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int d4 = (int)(i % (HD / 4));
+    const long long r = i / (HD / 4);
+    const int t = (int)(r % T), bh = (int)(r / T);
+    if (bh >= BNH) return;
+    const int blk = t / QBLK, nch = KEYS ? k_items(blk, T) : q_items(blk, T);
+    if (nch == 1) return;  // written directly by the chunk kernel
+    int first = 0;
+    for (int q = 0; q < blk; q++) first += KEYS ? k_items(q, T) : q_items(q, T);
+    const long long base = (long long)bh * items + first;
+    const int row = t % QBLK;
+    const long long rs = 3LL * C;
+    const int b = bh / NH, hd_off = (bh % NH) * HD;
+    if (!KEYS) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < nch; c++) acc += *(const floatx4 *)(ws + ((base + c) * QBLK + row) * HD + 4 * d4);
+        *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + hd_off + 4 * d4) = acc;
+    } else {
+        floatx4 ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < nch; c++) {
+            const float *p = ws + (base + c) * 2 * QBLK * HD + (long long)row * HD + 4 * d4;
+            ak += *(const floatx4 *)p;
+            av += *(const floatx4 *)(p + QBLK * HD);
+        }
+        *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + C + hd_off + 4 * d4) = ak;
+        *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + 2 * C + hd_off + 4 * d4) = av;
+    }
+}
+
+int total_items(bool keys, int T) {
+    int n = 0;
+    for (int blk = 0; blk * QBLK < T; blk++) n += keys ? k_items(blk, T) : q_items(blk, T);
+    return n;
+}
+
 template <int HD>
-hipError_t launch_fwd(float *out, float *lse, const float *qkv, int B, int T, int C, int NH, hipStream_t s) {
-    dim3 grid((T + QW * NWAVE - 1) / (QW * NWAVE), B * NH);
-    hipLaunchKernelGGL(flash_fwd_kernel<HD>, grid, dim3(256), 0, s, out, lse, qkv, T, C, NH, 1.0f / sqrtf((float)HD));
+hipError_t launch_fwd(float *out, float *lse, float *ws, const float *qkv, int B, int T, int C, int NH,
+                      hipStream_t s) {
+    const int items = total_items(false, T);
+    float *wlse = ws + (size_t)B * NH * items * QBLK * HD;
+    hipLaunchKernelGGL(flash_fwd_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, out, lse, ws, wlse, qkv, T, C,
+                       NH, items, 1.0f / sqrtf((float)HD));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || items == (T + QBLK - 1) / QBLK) return e;  // nothing was split
+    const long long n = (long long)B * NH * T * (HD / 4);
+    hipLaunchKernelGGL(flash_fwd_merge_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, lse, ws,
+                       wlse, T, C, NH, B * NH, items);
     return hipGetLastError();
 }
 
 template <int HD>
-hipError_t launch_bwd_dq(float *dqkv, float *Dbuf, const float *dout, const float *qkv, const float *out,
+hipError_t launch_bwd_dq(float *dqkv, float *Dbuf, float *ws, const float *dout, const float *qkv, const float *out,
                          const float *lse, int B, int T, int C, int NH, hipStream_t s) {
-    dim3 grid((T + QW * NWAVE - 1) / (QW * NWAVE), B * NH);
-    hipLaunchKernelGGL(flash_bwd_dq_kernel<HD>, grid, dim3(256), 0, s, dqkv, Dbuf, dout, qkv, out, lse, T, C, NH,
-                       1.0f / sqrtf((float)HD));
+    const int items = total_items(false, T);
+    hipLaunchKernelGGL(flash_bwd_dq_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, dqkv, Dbuf, ws, dout, qkv, out,
+                       lse, T, C, NH, items, 1.0f / sqrtf((float)HD));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || items == (T + QBLK - 1) / QBLK) return e;
+    const long long n = (long long)B * NH * T * (HD / 4);
+    hipLaunchKernelGGL((flash_bwd_sum_kernel<HD, false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dqkv,
+                       (const float *)ws, T, C, NH, B * NH, items);
     return hipGetLastError();
 }
 
 template <int HD>
-hipError_t launch_bwd_dkdv(float *dqkv, const float *Dbuf, const float *dout, const float *qkv, const float *lse,
-                           int B, int T, int C, int NH, hipStream_t s) {
-    dim3 grid((T + QW * NWAVE - 1) / (QW * NWAVE), B * NH);
-    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, grid, dim3(256), 0, s, dqkv, dout, qkv, lse, Dbuf, T, C, NH,
-                       1.0f / sqrtf((float)HD));
+hipError_t launch_bwd_dkdv(float *dqkv, float *ws, const float *Dbuf, const float *dout, const float *qkv,
+                           const float *lse, int B, int T, int C, int NH, hipStream_t s) {
+    const int items = total_items(true, T);
+    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, dqkv, ws, dout, qkv, lse,
+                       Dbuf, T, C, NH, items, 1.0f / sqrtf((float)HD));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || items == (T + QBLK - 1) / QBLK) return e;
+    const long long n = (long long)B * NH * T * (HD / 4);
+    hipLaunchKernelGGL((flash_bwd_sum_kernel<HD, true>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dqkv,
+                       (const float *)ws, T, C, NH, B * NH, items);
     return hipGetLastError();
 }
 
@@ -429,34 +612,41 @@ hipError_t launch_bwd_dkdv(float *dqkv, const float *Dbuf, const float *dout, co
 
 bool flash_attention_supported(int hd) { return hd == 16 || hd == 32 || hd == 64; }
 
-hipError_t flash_attention_forward(float *out, float *lse, const float *qkv, int B, int T, int C, int NH,
-                                   hipStream_t s) {
+size_t flash_attention_work(int B, int T, int C, int NH) {
     const int hd = C / NH;
-    switch (hd) {
-        case 16: return launch_fwd<16>(out, lse, qkv, B, T, C, NH, s);
-        case 32: return launch_fwd<32>(out, lse, qkv, B, T, C, NH, s);
-        case 64: return launch_fwd<64>(out, lse, qkv, B, T, C, NH, s);
+    const size_t fq = (size_t)B * NH * total_items(false, T) * QBLK * (hd + 1);
+    const size_t kv = (size_t)B * NH * total_items(true, T) * QBLK * 2 * hd;
+    return fq > kv ? fq : kv;
+}
+
+hipError_t flash_attention_forward(float *out, float *lse, float *ws, const float *qkv, int B, int T, int C, int NH,
+                                   hipStream_t s) {
+    switch (C / NH) {
+        case 16: return launch_fwd<16>(out, lse, ws, qkv, B, T, C, NH, s);
+        case 32: return launch_fwd<32>(out, lse, ws, qkv, B, T, C, NH, s);
+        case 64: return launch_fwd<64>(out, lse, ws, qkv, B, T, C, NH, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t flash_attention_backward_dq(float *dqkv, float *Dbuf, const float *dout, const float *qkv,
+hipError_t flash_attention_backward_dq(float *dqkv, float *Dbuf, float *ws, const float *dout, const float *qkv,
                                        const float *out, const float *lse, int B, int T, int C, int NH,
                                        hipStream_t s) {
     switch (C / NH) {
-        case 16: return launch_bwd_dq<16>(dqkv, Dbuf, dout, qkv, out, lse, B, T, C, NH, s);
-        case 32: return launch_bwd_dq<32>(dqkv, Dbuf, dout, qkv, out, lse, B, T, C, NH, s);
-        case 64: return launch_bwd_dq<64>(dqkv, Dbuf, dout, qkv, out, lse, B, T, C, NH, s);
+        case 16: return launch_bwd_dq<16>(dqkv, Dbuf, ws, dout, qkv, out, lse, B, T, C, NH, s);
+        case 32: return launch_bwd_dq<32>(dqkv, Dbuf, ws, dout, qkv, out, lse, B, T, C, NH, s);
+        case 64: return launch_bwd_dq<64>(dqkv, Dbuf, ws, dout, qkv, out, lse, B, T, C, NH, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t flash_attention_backward_dkdv(float *dqkv, const float *Dbuf, const float *dout, const float *qkv,
-                                         const float *lse, int B, int T, int C, int NH, hipStream_t s) {
+hipError_t flash_attention_backward_dkdv(float *dqkv, float *ws, const float *Dbuf, const float *dout,
+                                         const float *qkv, const float *lse, int B, int T, int C, int NH,
+                                         hipStream_t s) {
     switch (C / NH) {
-        case 16: return launch_bwd_dkdv<16>(dqkv, Dbuf, dout, qkv, lse, B, T, C, NH, s);
-        case 32: return launch_bwd_dkdv<32>(dqkv, Dbuf, dout, qkv, lse, B, T, C, NH, s);
-        case 64: return launch_bwd_dkdv<64>(dqkv, Dbuf, dout, qkv, lse, B, T, C, NH, s);
+        case 16: return launch_bwd_dkdv<16>(dqkv, ws, Dbuf, dout, qkv, lse, B, T, C, NH, s);
+        case 32: return launch_bwd_dkdv<32>(dqkv, ws, Dbuf, dout, qkv, lse, B, T, C, NH, s);
+        case 64: return launch_bwd_dkdv<64>(dqkv, ws, Dbuf, dout, qkv, lse, B, T, C, NH, s);
     }
     return hipErrorInvalidValue;
 }

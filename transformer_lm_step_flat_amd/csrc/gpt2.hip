@@ -113,7 +113,7 @@ struct Layout {
     size_t poff[16], pcnt[16], nparams;
     size_t aoff[NUM_ACTS], acnt[NUM_ACTS], nacts;
     // work buffer
-    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_part, w_splitk, w_dbias, nwork;
+    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_flash, w_part, w_splitk, w_dbias, nwork;
     // int buffer
     size_t i_tok, i_order, i_err, niwork;
 };
@@ -178,6 +178,7 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.w_dqkv = off; off = align_up(off + BT * 3 * C);
     l.w_dfch = off; off = align_up(off + BT * 4 * C);
     l.w_datt = off; off = align_up(off + (l.flash ? (size_t)B * NH * T : (size_t)B * NH * TT));
+    l.w_flash = off; off = align_up(off + (l.flash ? flash_attention_work(B, T, (int)C, (int)NH) : 0));
     l.w_part = off; off = align_up(off + (size_t)ln_partials((int)BT) * 2 * C);
     // split-K partial products of the GEMMs that may split (weight gradients, dlnf)
     size_t sk = 0;
@@ -585,7 +586,7 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
             float *lse = A + l.aoff[A_LSE] + (size_t)li * B * NH * T;
             const double tri = 0.5 * T * (T + 1.0) * B * NH;
             KRUNF(m, flash_name(FL_FWD, l.hd), 4.0 * tri * l.hd, 16.0 * BTC,
-                 flash_attention_forward(atty, lse, qkv, B, T, C, NH, s));
+                 flash_attention_forward(atty, lse, m->buf.work + l.w_flash, qkv, B, T, C, NH, s));
         } else {
             Site site_("attn_fwd");
             HIPCK(m, attention_fwd(atty, att, qkv, B, T, C, NH, s));
@@ -718,9 +719,9 @@ gpt2_status gpt2_backward(gpt2_model *m) {
             const float *lse = A + l.aoff[A_LSE] + (size_t)li * B * NH * T;
             const double tri = 0.5 * T * (T + 1.0) * B * NH;
             KRUNF(m, flash_name(FL_DQ, l.hd), 4.0 * tri * l.hd, 20.0 * BTC,
-                 flash_attention_backward_dq(dqkv, dscore, datty, qkv, atty, lse, B, T, C, NH, s));
+                 flash_attention_backward_dq(dqkv, dscore, W + l.w_flash, datty, qkv, atty, lse, B, T, C, NH, s));
             KRUNF(m, flash_name(FL_DKDV, l.hd), 4.0 * tri * l.hd, 24.0 * BTC,
-                 flash_attention_backward_dkdv(dqkv, dscore, datty, qkv, lse, B, T, C, NH, s));
+                 flash_attention_backward_dkdv(dqkv, W + l.w_flash, dscore, datty, qkv, lse, B, T, C, NH, s));
         } else {
             Site site_("attn_bwd");
             HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
@@ -891,11 +892,17 @@ gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const floa
     return GPT2_OK;
 }
 
+size_t gpt2k_flash_attention_work(int B, int T, int C, int NH) {
+    if (B <= 0 || T <= 0 || NH <= 0 || C % NH) return 0;
+    return align_up((size_t)B * NH * T) + flash_attention_work(B, T, C, NH);
+}
+
 gpt2_status gpt2k_flash_attention_forward(float *atty, float *lse, const float *qkv, int B, int T, int C, int NH,
-                                          void *stream) {
+                                          float *work, void *stream) {
     if (!attn_shape_ok(B, T, C, NH) || !flash_attention_supported(C / NH))
         return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024, T % 4 == 0");
-    KCK(flash_attention_forward(atty, lse, qkv, B, T, C, NH, (hipStream_t)stream));
+    KCK(flash_attention_forward(atty, lse, work + align_up((size_t)B * NH * T), qkv, B, T, C, NH,
+                                (hipStream_t)stream));
     return GPT2_OK;
 }
 
@@ -904,8 +911,9 @@ gpt2_status gpt2k_flash_attention_backward(float *dqkv, const float *datty, cons
                                            void *stream) {
     if (!attn_shape_ok(B, T, C, NH) || !flash_attention_supported(C / NH))
         return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024, T % 4 == 0");
-    KCK(flash_attention_backward_dq(dqkv, work, datty, qkv, atty, lse, B, T, C, NH, (hipStream_t)stream));
-    KCK(flash_attention_backward_dkdv(dqkv, work, datty, qkv, lse, B, T, C, NH, (hipStream_t)stream));
+    float *Dbuf = work, *ws = work + align_up((size_t)B * NH * T);
+    KCK(flash_attention_backward_dq(dqkv, Dbuf, ws, datty, qkv, atty, lse, B, T, C, NH, (hipStream_t)stream));
+    KCK(flash_attention_backward_dkdv(dqkv, ws, Dbuf, datty, qkv, lse, B, T, C, NH, (hipStream_t)stream));
     return GPT2_OK;
 }
 

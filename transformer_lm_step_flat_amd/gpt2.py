@@ -73,7 +73,7 @@ _SIGS = {
     "gpt2k_layernorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
     "gpt2k_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P],
     "gpt2k_attention_backward": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
-    "gpt2k_flash_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P],
+    "gpt2k_flash_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P, _P],
     "gpt2k_flash_attention_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
     "gpt2k_gelu_forward": [_P, _P, _Z, _P],
     "gpt2k_gelu_backward": [_P, _P, _P, _Z, _P],
@@ -87,6 +87,7 @@ _SIZE_FNS = {
     "gpt2k_linear_backward_work": [_I, _I, _I],
     "gpt2k_layernorm_backward_work": [_I, _I],
     "gpt2k_attention_backward_work": [_I, _I, _I, _I],
+    "gpt2k_flash_attention_work": [_I, _I, _I, _I],
 }
 
 # every symbol the headers declare
@@ -309,12 +310,18 @@ def attention_backward(dqkv, datty, qkv, att, B, T, C, NH):
     return work
 
 
+def _flash_work(B, T, C, NH, device):
+    return torch.empty(max(1, lib().gpt2k_flash_attention_work(B, T, C, NH)), dtype=torch.float32, device=device)
+
+
 def flash_attention_forward(atty, lse, qkv, B, T, C, NH):
-    _check(lib().gpt2k_flash_attention_forward(_ptr(atty), _ptr(lse), _ptr(qkv), B, T, C, NH, _s()))
+    work = _flash_work(B, T, C, NH, qkv.device)
+    _check(lib().gpt2k_flash_attention_forward(_ptr(atty), _ptr(lse), _ptr(qkv), B, T, C, NH, _ptr(work), _s()))
+    return work
 
 
 def flash_attention_backward(dqkv, datty, qkv, atty, lse, B, T, C, NH):
-    work = torch.empty(max(1, B * NH * T), dtype=torch.float32, device=qkv.device)
+    work = _flash_work(B, T, C, NH, qkv.device)
     _check(lib().gpt2k_flash_attention_backward(_ptr(dqkv), _ptr(datty), _ptr(qkv), _ptr(atty), _ptr(lse), B, T, C,
                                                 NH, _ptr(work), _s()))
     return work
