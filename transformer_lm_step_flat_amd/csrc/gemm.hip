@@ -104,10 +104,11 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
 
     floatx4 ra[A_F4], rb[B_F4];
     const int M = p.M, N = p.N;
-    // column sums of A (only MN-contiguous A, only the first tile column)
-    constexpr int CS_LANES = GEMM_THREADS / BM;
+    // Column sums of A (only MN-contiguous A, only the first tile column),
+    // accumulated from the A values each thread loads: for an MN-contiguous
+    // A a thread's 16-byte loads always cover the same 4 columns.
     const bool do_colsum = !AK && p.colsum != nullptr && tn == 0;
-    float csum = 0.0f;
+    floatx4 csum = {0.f, 0.f, 0.f, 0.f};
     const long long lda = p.lda, ldb = p.ldb;
 
     auto gload = [&](int k0) {
@@ -135,6 +136,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
         }
     };
     auto lstore = [&]() {
+        if (!AK && do_colsum) {
+#pragma unroll
+            for (int i = 0; i < A_F4; i++) csum += ra[i];
+        }
 #pragma unroll
         for (int i = 0; i < A_F4; i++) {
             int f = tid + GEMM_THREADS * i;
@@ -155,10 +160,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
         lstore();
         __syncthreads();
         if (k0 + BK < kend) gload(k0 + BK);
-        if (!AK && do_colsum) {
-#pragma unroll
-            for (int j = 0; j < BK / CS_LANES; j++) csum += As[(tid / BM + j * CS_LANES) * BM + tid % BM];
-        }
 #pragma unroll
         for (int q = 0; q < BK / 8; q++) {
             floatx4 a[MI], b[NI];
@@ -193,48 +194,61 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
     }
 
     if (!AK && do_colsum) {
-        // combine the CS_LANES partial sums of each column in a fixed order
+        // combine the partial sums of the threads sharing 4 columns, in a fixed order
+        constexpr int CQ = BM / 4, RL = GEMM_THREADS / CQ;
         __syncthreads();
-        As[tid] = csum;
+        *(floatx4 *)&As[4 * tid] = csum;
         __syncthreads();
-        if (tid < BM && m0 + tid < M) {
-            float t = As[tid];
+        if (tid < CQ && m0 + 4 * tid < M) {
+            floatx4 t = *(const floatx4 *)&As[4 * tid];
 #pragma unroll
-            for (int j = 1; j < CS_LANES; j++) t += As[j * BM + tid];
-            if (p.ksplit > 1)
-                p.colsum[(long long)s * M + m0 + tid] = t;
-            else
-                p.colsum[m0 + tid] += t;
+            for (int g = 1; g < RL; g++) t += *(const floatx4 *)&As[4 * (g * CQ + tid)];
+            float *dst = p.ksplit > 1 ? p.colsum + (long long)s * M + m0 + 4 * tid : p.colsum + m0 + 4 * tid;
+#pragma unroll
+            for (int e = 0; e < 4; e++) dst[e] = p.ksplit > 1 ? t[e] : dst[e] + t[e];
         }
     }
 
     // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and
-    // rows 8*(r/4) + 4*(l/32) + r%4 for its registers r = 0..15.
+    // rows 8*(r/4) + 4*(l/32) + r%4 for its registers r = 0..15.  Operands
+    // that live in memory (C for accumulation, the residual or the GELU
+    // input) are loaded for a whole 32 x 32 block before any arithmetic, so
+    // that their latencies overlap.
     const int epi = p.epi;
+    const float *src = epi == EPI_ACCUM ? C : p.aux;
+    const long long lds_ = epi == EPI_ACCUM ? p.ldc : p.ldaux;
+    const bool gather = epi == EPI_ACCUM || epi == EPI_RESID || epi == EPI_GELU_BWD;
 #pragma unroll
     for (int i = 0; i < MI; i++)
 #pragma unroll
         for (int j = 0; j < NI; j++) {
             const int n = n0 + wn * WN + j * 32 + l32;
             if (n >= N) continue;
+            float ext[16];
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                ext[r] = (gather && m < M) ? src[(long long)m * lds_ + n] : 0.0f;
+            }
             const float bn = p.bias ? p.bias[n] : 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
                 if (m >= M) continue;
                 const float v = p.alpha * acc[i][j][r];
+                const float x = ext[r];
                 const long long off = (long long)m * p.ldc + n;
                 switch (epi) {
                     case EPI_STORE: C[off] = v + bn; break;
-                    case EPI_ACCUM: C[off] += v; break;
-                    case EPI_RESID: C[off] = v + bn + p.aux[(long long)m * p.ldaux + n]; break;
+                    case EPI_ACCUM: C[off] = x + v; break;
+                    case EPI_RESID: C[off] = v + bn + x; break;
                     case EPI_GELU: {
                         const float pre = v + bn;
                         C[off] = pre;
                         p.C2[off] = gelu_fwd(pre);
                         break;
                     }
-                    case EPI_GELU_BWD: C[off] = v * gelu_grad(p.aux[(long long)m * p.ldaux + n]); break;
+                    case EPI_GELU_BWD: C[off] = v * gelu_grad(x); break;
                 }
             }
         }
