@@ -68,24 +68,33 @@ __global__ void encoder_forward_kernel(float *out, const int32_t *inp, const flo
     ((floatx4 *)(out + bt * C))[c4] = a + b;
 }
 
-// One block per (sorted index, 1024-column chunk).  The block at the first
-// position of a run of equal ids sums the run's rows (ascending position)
-// and adds them to that id's row of dwte; all other blocks exit.
-__global__ void encoder_backward_wte_kernel(float *dwte, const float *dout, const int32_t *inp,
-                                            const int32_t *order, int BT, int C, int V) {
+// One block per (sorted index, 256-column chunk).  The block at the first
+// position of a run of equal ids sums the run's rows and adds the sum to that
+// id's row of dwte; all other blocks exit.  The run is split over 4 row
+// lanes (lane l takes run entries l, l+4, ...), whose sums are added in a
+// fixed order.
+__global__ __launch_bounds__(256) void encoder_backward_wte_kernel(float *dwte, const float *dout,
+                                                                   const int32_t *inp, const int32_t *order, int BT,
+                                                                   int C, int V) {
+    __shared__ floatx4 part[4][64];
     const int i = blockIdx.x;
     const int id = clamp_id(inp[order[i]], V);
     if (i > 0 && clamp_id(inp[order[i - 1]], V) == id) return;
-    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
-    if (c >= C) return;
+    const int c4 = blockIdx.y * 64 + (threadIdx.x & 63), rl = threadIdx.x >> 6;
+    const bool col_ok = c4 < C / 4;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = i; j < BT; j++) {
-        int pos = order[j];
-        if (clamp_id(inp[pos], V) != id) break;
-        acc += *(const floatx4 *)(dout + (long long)pos * C + c);
+    for (int j = i + rl; j < BT; j += 4) {
+        const int pos = order[j];
+        if (clamp_id(inp[pos], V) != id) break;  // sorted by id: the run has ended
+        if (col_ok) acc += ((const floatx4 *)(dout + (long long)pos * C))[c4];
     }
-    floatx4 *dst = (floatx4 *)(dwte + (long long)id * C + c);
-    *dst = *dst + acc;
+    part[rl][threadIdx.x & 63] = acc;
+    __syncthreads();
+    if (rl == 0 && col_ok) {
+        const int l = threadIdx.x;
+        floatx4 *dst = (floatx4 *)(dwte + (long long)id * C) + c4;
+        *dst = *dst + (((part[0][l] + part[1][l]) + part[2][l]) + part[3][l]);
+    }
 }
 
 __global__ void encoder_backward_wpe_kernel(float *dwpe, const float *dout, int B, int T, int C) {
@@ -144,78 +153,99 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(float *out, floa
     }
 }
 
-// LayerNorm backward, input gradient: one wavefront per row, as the forward.
-// xhat = (x - mean) rstd, g = dy * w,
-// dx (+)= rstd (g - mean_c(g) - xhat mean_c(g xhat)).
+constexpr int COL_CHUNK = 16;  // rows per LayerNorm-backward block (and per partial row)
+
+// LayerNorm backward.  Block b takes rows [16b, 16b+16), wavefront w the
+// rows 16b + w + 4k (k = 0..3), one at a time with the next row's loads
+// issued before the current row's reductions:
+//   xhat = (x - mean) rstd, g = dy * w,
+//   dx (+)= rstd (g - mean_c(g) - xhat mean_c(g xhat)).
+// Per-column sums of dy * xhat and dy are kept per lane, combined over the
+// four wavefronts in a fixed order and written as the block's partial row
+// [dw (C) | db (C)].
 template <int NV>
-__global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, const float *dout, const float *inp,
-                                                                 const float *w, const float *mean,
-                                                                 const float *rstd, int N, int C,
+__global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, float *partial, const float *dout,
+                                                                 const float *inp, const float *w,
+                                                                 const float *mean, const float *rstd, int N, int C,
                                                                  int accumulate) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= N) return;
+    extern __shared__ floatx4 lds4[];  // [4][2C/4]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int C4 = C / 4;
-    const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
-    const floatx4 *dy = (const floatx4 *)(dout + (long long)row * C);
-    floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
-    const float mu = mean[row], rs = rstd[row];
-    floatx4 xh[NV], g[NV], old[NV];
-    float sg = 0.f, sgx = 0.f;
+    floatx4 wv[NV], dwacc[NV], dbacc[NV];
 #pragma unroll
     for (int i = 0; i < NV; i++) {
-        int k = lane + 64 * i;
-        if (k < C4) {
-            floatx4 xv = x[k], dv = dy[k], wv = ((const floatx4 *)w)[k];
-            old[i] = accumulate ? dx[k] : floatx4{0.f, 0.f, 0.f, 0.f};
-            xh[i] = (xv - mu) * rs;
-            g[i] = dv * wv;
-            floatx4 gx = g[i] * xh[i];
+        const int k = lane + 64 * i;
+        wv[i] = k < C4 ? ((const floatx4 *)w)[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+        dwacc[i] = dbacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int r0 = blockIdx.x * COL_CHUNK + wave;
+    floatx4 xn[NV], dn[NV], on[NV];
+    float mun = 0.f, rsn = 0.f;
+    auto fetch = [&](int row) {
+        const bool ok = row < N;
+        const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
+        const floatx4 *dy = (const floatx4 *)(dout + (long long)row * C);
+        const floatx4 *dx = (const floatx4 *)(dinp + (long long)row * C);
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int k = lane + 64 * i;
+            const bool kk = ok && k < C4;
+            xn[i] = kk ? x[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+            dn[i] = kk ? dy[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+            on[i] = (kk && accumulate) ? dx[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        mun = ok ? mean[row] : 0.f;
+        rsn = ok ? rstd[row] : 0.f;
+    };
+    fetch(r0);
+    for (int k = 0; k < COL_CHUNK / 4; k++) {
+        const int row = r0 + 4 * k;
+        if (row >= N) break;
+        floatx4 xc[NV], dc[NV], oc[NV];
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            xc[i] = xn[i];
+            dc[i] = dn[i];
+            oc[i] = on[i];
+        }
+        const float mu = mun, rs = rsn;
+        // prefetch the next row while reducing this one (wide rows: registers
+        // would spill, so they load each row when it is reached)
+        constexpr bool kPrefetch = NV <= 4;
+        if (kPrefetch && k + 1 < COL_CHUNK / 4) fetch(row + 4);
+        floatx4 xh[NV], g[NV];
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            xh[i] = (xc[i] - mu) * rs;
+            g[i] = dc[i] * wv[i];
+            const floatx4 gx = g[i] * xh[i];
             sg += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
             sgx += (gx[0] + gx[1]) + (gx[2] + gx[3]);
+            dwacc[i] += dc[i] * xh[i];
+            dbacc[i] += dc[i];
         }
+        const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+        floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int kk = lane + 64 * i;
+            if (kk < C4) dx[kk] = oc[i] + rs * (g[i] - mg - xh[i] * mgx);
+        }
+        if (!kPrefetch && k + 1 < COL_CHUNK / 4) fetch(row + 4);
     }
-    const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
 #pragma unroll
     for (int i = 0; i < NV; i++) {
-        int k = lane + 64 * i;
-        if (k < C4) dx[k] = old[i] + rs * (g[i] - mg - xh[i] * mgx);
-    }
-}
-
-constexpr int COL_CHUNK = 32;  // rows per partial of a column reduction
-
-// LayerNorm backward, parameter gradients: per column c, over a chunk of 32
-// rows, sum dy * xhat and dy.  Block (x, y): 64 float4 columns x 4 row
-// lanes over rows [32y, 32y+32); the four row lanes are combined in a fixed
-// order.  partial[y] = [dw (C) | db (C)].
-__global__ __launch_bounds__(256) void layernorm_param_grad_kernel(float *partial, const float *dout,
-                                                                   const float *inp, const float *mean,
-                                                                   const float *rstd, int N, int C) {
-    __shared__ floatx4 lw[4][64], lb[4][64];
-    const int c4 = blockIdx.x * 64 + (threadIdx.x & 63), rl = threadIdx.x >> 6;
-    const int C4 = C / 4;
-    const int r0 = blockIdx.y * COL_CHUNK, r1 = min(N, r0 + COL_CHUNK);
-    floatx4 sw = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-    if (c4 < C4) {
-#pragma unroll 4
-        for (int r = r0 + rl; r < r1; r += 4) {
-            floatx4 d = ((const floatx4 *)(dout + (long long)r * C))[c4];
-            floatx4 xv = ((const floatx4 *)(inp + (long long)r * C))[c4];
-            sw += d * ((xv - mean[r]) * rstd[r]);
-            sb += d;
+        const int k = lane + 64 * i;
+        if (k < C4) {
+            lds4[wave * 2 * C4 + k] = dwacc[i];
+            lds4[wave * 2 * C4 + C4 + k] = dbacc[i];
         }
     }
-    lw[rl][threadIdx.x & 63] = sw;
-    lb[rl][threadIdx.x & 63] = sb;
     __syncthreads();
-    if (rl == 0 && c4 < C4) {
-        const int l = threadIdx.x;
-        floatx4 w = ((lw[0][l] + lw[1][l]) + lw[2][l]) + lw[3][l];
-        floatx4 b = ((lb[0][l] + lb[1][l]) + lb[2][l]) + lb[3][l];
-        ((floatx4 *)(partial + (long long)blockIdx.y * 2 * C))[c4] = w;
-        ((floatx4 *)(partial + (long long)blockIdx.y * 2 * C + C))[c4] = b;
-    }
+    floatx4 *out = (floatx4 *)(partial + (long long)blockIdx.x * 2 * C);
+    for (int c = threadIdx.x; c < 2 * C4; c += blockDim.x)
+        out[c] = ((lds4[c] + lds4[2 * C4 + c]) + lds4[4 * C4 + c]) + lds4[6 * C4 + c];
 }
 
 // dst[i] (+)= sum_{p < P} src[p*ld + i], 4 consecutive i per thread, p in order.
@@ -228,6 +258,28 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(float *dst, const flo
     for (int p = 1; p < P; p++) acc += s4[(size_t)p * ld4 + i];
     floatx4 *d4 = (floatx4 *)dst;
     d4[i] = accumulate ? d4[i] + acc : acc;
+}
+
+// dst (n floats) and dst2 (n2 floats) += the column sums of partial rows of
+// n + n2 floats (fixed order): used for the [dw | db] partials of LayerNorm.
+__global__ __launch_bounds__(256) void sum_partials_split_kernel(float *dst, float *dst2, const float *src, int P,
+                                                                 int n4, int n24) {
+    __shared__ floatx4 lds[16][16];
+    const int c = threadIdx.x & 15, pl = threadIdx.x >> 4;
+    const int i = blockIdx.x * 16 + c, ld4 = n4 + n24;
+    const floatx4 *s4 = (const floatx4 *)src;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (i < ld4)
+        for (int p = pl; p < P; p += 16) acc += s4[(size_t)p * ld4 + i];
+    lds[pl][c] = acc;
+    __syncthreads();
+    if (pl == 0 && i < ld4) {
+        floatx4 t = lds[0][c];
+#pragma unroll
+        for (int k = 1; k < 16; k++) t += lds[k][c];
+        floatx4 *d4 = i < n4 ? (floatx4 *)dst + i : (floatx4 *)dst2 + (i - n4);
+        *d4 = *d4 + t;
+    }
 }
 
 // The same for many partials: 16 float4 columns x 16 partial lanes per block;
@@ -414,20 +466,33 @@ __global__ __launch_bounds__(256) void gelu_backward_kernel(floatx4 *dinp, const
 __global__ __launch_bounds__(256) void adamw_kernel(floatx4 *params, const floatx4 *grads, floatx4 *m, floatx4 *v,
                                                     size_t n4, float lr, float b1, float b2, float eps, float wd,
                                                     float inv_c1, float inv_c2) {
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (; i < n4; i += stride) {
-        floatx4 g = grads[i], mm = m[i], vv = v[i], p = params[i];
-        mm = b1 * mm + (1.0f - b1) * g;
-        vv = b2 * vv + (1.0f - b2) * g * g;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    // two 16-byte elements per thread and iteration: more loads in flight
+    for (size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n4; i0 += 2 * stride) {
+        const size_t idx[2] = {i0, i0 + stride};
+        floatx4 g[2], mm[2], vv[2], p[2];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            float mhat = mm[e] * inv_c1, vhat = vv[e] * inv_c2;
-            p[e] -= lr * (mhat / (sqrtf(vhat) + eps) + wd * p[e]);
-        }
-        m[i] = mm;
-        v[i] = vv;
-        params[i] = p;
+        for (int u = 0; u < 2; u++)
+            if (idx[u] < n4) {
+                g[u] = grads[idx[u]];
+                mm[u] = m[idx[u]];
+                vv[u] = v[idx[u]];
+                p[u] = params[idx[u]];
+            }
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+            if (idx[u] < n4) {
+                mm[u] = b1 * mm[u] + (1.0f - b1) * g[u];
+                vv[u] = b2 * vv[u] + (1.0f - b2) * g[u] * g[u];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float mhat = mm[u][e] * inv_c1, vhat = vv[u][e] * inv_c2;
+                    p[u][e] -= lr * (mhat / (sqrtf(vhat) + eps) + wd * p[u][e]);
+                }
+                m[idx[u]] = mm[u];
+                v[idx[u]] = vv[u];
+                params[idx[u]] = p[u];
+            }
     }
 }
 
@@ -466,7 +531,7 @@ hipError_t k_encoder_forward(float *out, const int32_t *inp, const float *wte, c
 hipError_t k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *inp,
                               const int32_t *order, int B, int T, int C, int V, hipStream_t s) {
     const int BT = B * T;
-    hipLaunchKernelGGL(encoder_backward_wte_kernel, dim3(BT, grid_for(C, 1024)), dim3(256), 0, s, dwte, dout, inp,
+    hipLaunchKernelGGL(encoder_backward_wte_kernel, dim3(BT, grid_for(C / 4, 64)), dim3(256), 0, s, dwte, dout, inp,
                        order, BT, C, V);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -504,19 +569,15 @@ hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partia
                                 int C, bool accumulate, hipStream_t s) {
     if (C % 4 || C > 2048) return hipErrorInvalidValue;
     int nv = (C / 4 + 63) / 64;
-    LN_DISPATCH(nv, layernorm_backward_kernel, dim3(grid_for(N, 4)), dim3(256), 0, s, dinp, dout, inp, w, mean,
-                rstd, N, C, accumulate ? 1 : 0);
+    const int P = ln_partials(N);
+    const size_t lds = (size_t)8 * C * sizeof(float);
+    LN_DISPATCH(nv, layernorm_backward_kernel, dim3(P), dim3(256), lds, s, dinp, partial, dout, inp, w, mean, rstd, N,
+                C, accumulate ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int P = ln_partials(N);
-    hipLaunchKernelGGL(layernorm_param_grad_kernel, dim3(grid_for(C / 4, 64), P), dim3(256), 0, s, partial, dout,
-                       inp, mean, rstd, N, C);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // partial rows are [dw | db]: sum each half into its own tensor
-    e = k_sum_partials_ld(dw, partial, P, (size_t)C, (size_t)2 * C, true, s);
-    if (e != hipSuccess) return e;
-    return k_sum_partials_ld(db, partial + C, P, (size_t)C, (size_t)2 * C, true, s);
+    hipLaunchKernelGGL(sum_partials_split_kernel, dim3(grid_for(2 * C / 4, 16)), dim3(256), 0, s, dw, db,
+                       (const float *)partial, P, C / 4, C / 4);
+    return hipGetLastError();
 }
 
 hipError_t k_sum_partials_ld(float *dst, const float *src, int P, size_t n, size_t ld, bool accumulate,
