@@ -3,13 +3,16 @@
     python bench.py [--steps K] [--warmup W] [--config 124m] [--gpus 1]
 
 A step is gpt2_forward (ids already resident in HBM) + gpt2_zero_grad +
-gpt2_backward + gpt2_update, enqueued on one HIP stream.  W untimed steps,
-then K timed steps between two device synchronizations (`value`).  The same
-number of steps is then run again with every launch bracketed by HIP events
-on the step's stream (the library's per-launch timing): that gives each
-kernel's average duration and the roofline fraction of the dominant kernel
-without perturbing the first timing.  Last, the CPU oracle is timed on a
-bounded sample of the same workload.  Prints one JSON line on stdout.
+gpt2_backward + gpt2_update, enqueued on the current HIP stream (the backward
+also runs its weight-gradient products on a second stream of the library).
+W untimed steps, then K timed steps between two device synchronizations
+(`value`).  The same number of steps is then run again on one stream, with
+every launch bracketed by HIP events (the library's per-launch timing): that
+gives each kernel's average duration on its own, and so the roofline
+fraction of the dominant kernel, without perturbing the first timing.  With
+--one-stream every pass keeps to one stream (the command whose kernel trace
+matches those per-launch times).  Last, the CPU oracle is timed on a bounded
+sample of the same workload.  Prints one JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -25,6 +28,48 @@ sys.path.insert(0, ROOT)
 METRIC = "train tokens/sec (fwd+bwd+AdamW) GPT-2 124M B=4 T=1024 fp32; % MFMA/HBM roofline"
 PEAK_MFMA_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) of this script with --copy-calibration; the
+# file records a hash of the sources that decide that kernel's launches, and
+# the figure is reported only while they are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_124m_b4_t1024.json")
+KERNEL_SOURCES = ["gemm.hip", "gemm.h", "attention.hip", "attention.h", "kernels.hip", "kernels.h", "common.h",
+                  "gpt2.hip"]
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "transformer_lm_step_flat_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, config: str):
+    """Bytes per launch of `kernel` from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("config") != config or t.get("sources_sha256") != sources_sha256():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib: int):
+    """A plain elementwise copy of known size (reads and writes mib MiB each),
+    for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 x {mib} MiB read + {mib} MiB written (elementwise mul by 1)")
 
 
 def log(*a):
@@ -63,7 +108,11 @@ def main():
     ap.add_argument("--config", default="124m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time the steps without per-launch events")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run the backward on one stream in every pass (not only the per-launch timing)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain copy of MIB MiB (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the data-parallel path over several "
@@ -83,6 +132,9 @@ def main():
         inp, tgt = synth.batch(cfg, step=i)
         batches.append((torch.from_numpy(inp.ravel()).cuda(), torch.from_numpy(tgt.ravel()).cuda()))
     torch.cuda.synchronize()
+    M.set_concurrency(not args.one_stream)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
 
     def step(i):
         di, dt = batches[i % nb]
@@ -112,6 +164,7 @@ def main():
     # the same steps again, each launch bracketed by HIP events on the step's stream
     kernels, roofline, ms_ev, sites = [], None, None, []
     if not args.no_events:
+        M.set_concurrency(False)  # each launch alone: its time is its own
         M.profile_enable(True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -121,6 +174,7 @@ def main():
         ms_ev = (time.perf_counter() - t0) / args.steps * 1e3
         prof = M.profile_read()
         M.profile_enable(False)
+        M.set_concurrency(not args.one_stream)
         log(f"timed {args.steps} steps with per-launch events: {ms_ev:.2f} ms/step")
         by_kernel = {}
         for e in prof:
@@ -158,7 +212,8 @@ def main():
         achieved = per_launch / (avg_ms * 1e-3) / (1e12 if bound == "mfma" else 1e9)
         all_flops = sum(e["flops"] for e in by_kernel.values()) / args.steps
         roofline = {"bound": bound, "achieved": achieved, "peak": peak,
-                    "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak, "traffic": None,
+                    "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak,
+                    "traffic": measured_traffic(d["name"], args.config),
                     "kernel": d["name"], "avg_launch_ms": avg_ms, "launches_per_step": d["launches"] / args.steps,
                     "algorithmic_per_launch": per_launch,
                     "step_flops": all_flops,
@@ -192,6 +247,7 @@ def main():
         "cpu_baseline": cpu,
         "last_loss": loss,
         "ms_per_step_with_events": ms_ev,
+        "streams": 1 if args.one_stream else 2,
         "kernels": kernels[:16],
     }
     print(json.dumps(out))

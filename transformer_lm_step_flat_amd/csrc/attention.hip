@@ -54,12 +54,13 @@ struct TileLoader {
     __device__ __forceinline__ void load(const float *base, long long rs, int row0, int nrows, int tid) {
 #pragma unroll
         for (int i = 0; i < F4; i++) {
-            int f = tid + 256 * i;
-            int row = f / (HD / 4), c4 = f % (HD / 4);
-            if (f < ROWS * HD / 4 && row0 + row < nrows)
-                r[i] = *(const floatx4 *)(base + (long long)(row0 + row) * rs + 4 * c4);
-            else
-                r[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+            // branch-free: out-of-range threads read row 0 (always valid) and keep zeros
+            const int f = tid + 256 * i;
+            const int row = f / (HD / 4), c4 = f % (HD / 4);
+            const bool ok = f < ROWS * HD / 4 && row0 + row < nrows;
+            const floatx4 v = *(const floatx4 *)(base + (ok ? (long long)(row0 + row) * rs + 4 * c4 : 0));
+            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            r[i] = ok ? v : z;
         }
     }
     __device__ __forceinline__ void store(float *lds, int pitch, int tid) const {
@@ -67,6 +68,19 @@ struct TileLoader {
         for (int i = 0; i < F4; i++) {
             int f = tid + 256 * i;
             if (f < ROWS * HD / 4) *(floatx4 *)&lds[(f / (HD / 4)) * pitch + 4 * (f % (HD / 4))] = r[i];
+        }
+    }
+    // The same tile transposed, [HD][pitch] (row index contiguous), so that
+    // 4 consecutive rows of one column are one 16-byte LDS read.
+    __device__ __forceinline__ void store_t(float *lds, int pitch, int tid) const {
+#pragma unroll
+        for (int i = 0; i < F4; i++) {
+            int f = tid + 256 * i;
+            if (f < ROWS * HD / 4) {
+                const int row = f / (HD / 4), c = 4 * (f % (HD / 4));
+#pragma unroll
+                for (int e = 0; e < 4; e++) lds[(c + e) * pitch + row] = r[i][e];
+            }
         }
     }
 };
@@ -119,24 +133,28 @@ struct HeadBlocks {
 };
 
 // acc^T[md] (head dims 32md.., this lane's query) += X^T P^T over the 64 keys
-// of a block: X is a [KB][pitch] LDS tile, P (this lane's query, 32 keys per
-// mb) is in registers.  For HD = 16 the head-dim block is half used: its
-// other 16 rows get zero A values.
+// of a block: Xt is the block's [HD][KB + 4] transposed LDS tile, P (this
+// lane's query, 32 keys per mb) is in registers.  Register r of P holds key
+// 8(r/4) + 4h + r%4, so the 4 registers 4g..4g+3 take 4 consecutive keys:
+// one 16-byte read feeds 4 MFMAs.  For HD = 16 the head-dim block is half
+// used: its other 16 rows get zero A values.
 template <int HD>
-__device__ __forceinline__ void accum_xt_pt_any(floatx16 (&acc)[HeadBlocks<HD>::N], const float *X, int pitch,
+__device__ __forceinline__ void accum_xt_pt_any(floatx16 (&acc)[HeadBlocks<HD>::N], const float *Xt,
                                                 const floatx16 (&p)[2], int l32, int h) {
+    constexpr int PT = KB + 4;
 #pragma unroll
     for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int u = 32 * mb + row_of(r, h);
+        for (int g = 0; g < 4; g++)
 #pragma unroll
             for (int md = 0; md < HeadBlocks<HD>::N; md++) {
                 const int d = 32 * md + l32;
-                const float a = d < HD ? X[u * pitch + d] : 0.0f;
-                acc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[mb][r], acc[md], 0, 0, 0);
+                const floatx4 a = d < HD ? *(const floatx4 *)&Xt[d * PT + 32 * mb + 8 * g + 4 * h]
+                                         : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    acc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], p[mb][4 * g + i], acc[md], 0, 0, 0);
             }
-        }
 }
 
 // Write a per-wave transposed accumulator (lane: one row, registers: head
@@ -200,13 +218,16 @@ __device__ __forceinline__ void decode_item(int x, int T, int &blk, int &chunk, 
 // ------------------------------------------------------------------ forward
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(float *__restrict__ out, float *__restrict__ lse,
+__global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ out, float *__restrict__ lse,
                                                            float *__restrict__ ws, float *__restrict__ wlse,
                                                            const float *__restrict__ qkv, int T, int C, int NH,
                                                            int items, float scale) {
     constexpr int P = HD + 4;
-    __shared__ __attribute__((aligned(16))) float Ks[KB * P];
-    __shared__ __attribute__((aligned(16))) float Vs[KB * P];
+    constexpr int PT = KB + 4;
+    // K row-major [KB][P]; V transposed [HD][PT]; both reused as transpose space at the end
+    constexpr int KS = KB * P, VS = (HD * PT > QW * NWAVE / 2 * P ? HD * PT : QW * NWAVE / 2 * P);
+    __shared__ __attribute__((aligned(16))) float Ks[KS];
+    __shared__ __attribute__((aligned(16))) float Vs[VS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
     int qb, chunk, first;
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(float *__restrict__ o
     for (int k0 = kc0; k0 < kc1; k0 += KB) {
         __syncthreads();
         lk.store(Ks, P, tid);
-        lv.store(Vs, P, tid);
+        lv.store_t(Vs, PT, tid);
         __syncthreads();
         if (k0 + KB < kc1) {
             lk.load(qb_ptr + C, rs, k0 + KB, T, tid);
@@ -274,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(float *__restrict__ o
         m = mx;
 #pragma unroll
         for (int md = 0; md < HeadBlocks<HD>::N; md++) o[md] *= alpha;
-        accum_xt_pt_any<HD>(o, Vs, P, s, l32, h);
+        accum_xt_pt_any<HD>(o, Vs, s, l32, h);
     }
     __syncthreads();  // the K/V tiles become per-wave transpose space
     float *tr = (wave < 2 ? Ks : Vs) + (wave & 1) * QW * P;
@@ -335,8 +356,10 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
                                                               const float *__restrict__ lse, int T, int C, int NH,
                                                               int items, float scale) {
     constexpr int P = HD + 4;
+    constexpr int PT = KB + 4;
     __shared__ __attribute__((aligned(16))) float Ks[KB * P];
     __shared__ __attribute__((aligned(16))) float Vs[KB * P];
+    __shared__ __attribute__((aligned(16))) float Kt[HD * PT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
     int qb, chunk, first;
@@ -379,6 +402,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
     for (int k0 = kc0; k0 < kc1; k0 += KB) {
         __syncthreads();
         lk.store(Ks, P, tid);
+        lk.store_t(Kt, PT, tid);
         lv.store(Vs, P, tid);
         __syncthreads();
         if (k0 + KB < kc1) {
@@ -396,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
                 const float p = (u > t || u >= T) ? 0.0f : __expf(s[mb][r] - lt);
                 s[mb][r] = p * (dp[mb][r] - Dt);  // ds
             }
-        accum_xt_pt_any<HD>(dq, Ks, P, s, l32, h);
+        accum_xt_pt_any<HD>(dq, Kt, s, l32, h);
     }
     __syncthreads();
     float *tr = (wave < 2 ? Ks : Vs) + (wave & 1) * QW * P;
@@ -418,8 +442,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                                                                 const float *__restrict__ Dbuf, int T, int C, int NH,
                                                                 int items, float scale) {
     constexpr int P = HD + 4;
+    constexpr int PT = TB + 4;
     __shared__ __attribute__((aligned(16))) float Qs[TB * P];
     __shared__ __attribute__((aligned(16))) float Os[TB * P];  // dO tile
+    __shared__ __attribute__((aligned(16))) float Qt[HD * PT];  // the same two, transposed
+    __shared__ __attribute__((aligned(16))) float Ot[HD * PT];
     __shared__ float Ls[TB], Ds[TB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
@@ -456,6 +483,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         __syncthreads();
         lq.store(Qs, P, tid);
         lo.store(Os, P, tid);
+        lq.store_t(Qt, PT, tid);
+        lo.store_t(Ot, PT, tid);
         if (tid < TB) {
             Ls[tid] = t0 + tid < T ? lse[(long long)bh * T + t0 + tid] : 0.0f;
             Ds[tid] = t0 + tid < T ? Dbuf[(long long)bh * T + t0 + tid] : 0.0f;
@@ -484,18 +513,21 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             s[r] = p;                      // p
             dp[r] = p * (dp[r] - Ds[tl]);  // ds
         }
+        // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
+        // the transposed tiles per 4 MFMAs
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int tl = row_of(r, h);
+        for (int g = 0; g < 4; g++)
 #pragma unroll
             for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
                 const int d = 32 * nd + l32;
-                const float ob = d < HD ? Os[tl * P + d] : 0.0f;
-                const float qv = d < HD ? Qs[tl * P + d] : 0.0f;
-                dv[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[r], ob, dv[nd], 0, 0, 0);
-                dk[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(dp[r], qv, dk[nd], 0, 0, 0);
+                const floatx4 ob = d < HD ? *(const floatx4 *)&Ot[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
+                const floatx4 qv = d < HD ? *(const floatx4 *)&Qt[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    dv[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[4 * g + i], ob[i], dv[nd], 0, 0, 0);
+                    dk[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(dp[4 * g + i], qv[i], dk[nd], 0, 0, 0);
+                }
             }
-        }
     }
     // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
     float *dkb, *dvb;

@@ -113,7 +113,7 @@ struct Layout {
     size_t poff[16], pcnt[16], nparams;
     size_t aoff[NUM_ACTS], acnt[NUM_ACTS], nacts;
     // work buffer
-    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_flash, w_part, w_splitk, w_dbias, nwork;
+    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_flash, w_part, w_splitk, w_splitk_dw, w_dbias, nwork;
     // int buffer
     size_t i_tok, i_order, i_err, niwork;
 };
@@ -180,19 +180,22 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.w_datt = off; off = align_up(off + (l.flash ? (size_t)B * NH * T : (size_t)B * NH * TT));
     l.w_flash = off; off = align_up(off + (l.flash ? flash_attention_work(B, T, (int)C, (int)NH) : 0));
     l.w_part = off; off = align_up(off + (size_t)ln_partials((int)BT) * 2 * C);
-    // split-K partial products of the GEMMs that may split (weight gradients, dlnf)
-    size_t sk = 0;
-    auto need = [&](int M, int N, int K) {
+    // split-K partial products of the GEMMs that may split: dlnf (main stream)
+    // and the weight gradients (side stream), in separate regions because the
+    // two streams run concurrently
+    size_t sk = 0, sk_dw = 0;
+    auto need = [&](size_t &acc, int M, int N, int K) {
         Plan p = plan_gemm(M, N, K, 1, true);
-        if (p.ksplit > 1 && (size_t)p.ksplit * M * N > sk) sk = (size_t)p.ksplit * M * N;
+        if (p.ksplit > 1 && (size_t)p.ksplit * M * N > acc) acc = (size_t)p.ksplit * M * N;
     };
-    need((int)(3 * C), (int)C, (int)BT);
-    need((int)C, (int)C, (int)BT);
-    need((int)(4 * C), (int)C, (int)BT);
-    need((int)C, (int)(4 * C), (int)BT);
-    need(l.Vp, (int)C, (int)BT);
-    need((int)BT, (int)C, l.Vp);
+    need(sk_dw, (int)(3 * C), (int)C, (int)BT);
+    need(sk_dw, (int)C, (int)C, (int)BT);
+    need(sk_dw, (int)(4 * C), (int)C, (int)BT);
+    need(sk_dw, (int)C, (int)(4 * C), (int)BT);
+    need(sk_dw, l.Vp, (int)C, (int)BT);
+    need(sk, (int)BT, (int)C, l.Vp);
     l.w_splitk = off; off = align_up(off + sk);
+    l.w_splitk_dw = off; off = align_up(off + sk_dw);
     l.w_dbias = off; off = align_up(off + 16 * 4 * C);
     l.nwork = off;
     l.i_tok = 0;
@@ -223,6 +226,14 @@ struct gpt2_model {
     Layout lo;
     gpt2_buffers buf;
     hipStream_t stream;
+    // The backward runs the weight-gradient GEMMs on a second stream, beside
+    // the input-gradient chain on `stream`; events order the two (ring of
+    // reusable events: a wait is enqueued right after each record).
+    hipStream_t side = nullptr;
+    static constexpr int NEV = 8;
+    hipEvent_t ev[NEV] = {};
+    int ev_next = 0;
+    bool concurrent = true;  // false: the backward keeps to `stream` alone
     bool have_targets = false;
     std::string err;
     Profiler prof;
@@ -253,6 +264,8 @@ thread_local Profiler *g_prof = nullptr;
 
 thread_local const char *g_site = "";  // call site of the launches being made
 
+thread_local hipStream_t g_launch_stream = nullptr;  // stream of the launches being made, if not the model's
+
 template <class F>
 hipError_t timed(const char *name, double flops, double bytes, F &&f) {
     Profiler *p = g_prof;
@@ -264,11 +277,12 @@ hipError_t timed(const char *name, double flops, double bytes, F &&f) {
         p->pool.push_back(e);
     }
     hipEvent_t a = p->pool[p->used++], b = p->pool[p->used++];
-    hipError_t e = hipEventRecord(a, p->stream);
+    hipStream_t ls = g_launch_stream ? g_launch_stream : p->stream;
+    hipError_t e = hipEventRecord(a, ls);
     if (e != hipSuccess) return e;
     e = f();
     if (e != hipSuccess) return e;
-    e = hipEventRecord(b, p->stream);
+    e = hipEventRecord(b, ls);
     p->recs.push_back({name, g_site, flops, bytes, a, b});
     return e;
 }
@@ -279,6 +293,13 @@ struct Site {
     const char *saved;
     explicit Site(const char *s) : saved(g_site) { g_site = s; }
     ~Site() { g_site = saved; }
+};
+
+// Launches in its scope go to stream `s` (for the per-launch timing events).
+struct OnStream {
+    hipStream_t saved;
+    explicit OnStream(hipStream_t s) : saved(g_launch_stream) { g_launch_stream = s; }
+    ~OnStream() { g_launch_stream = saved; }
 };
 
 // Makes a model's profiler the active one for the duration of an API call.
@@ -535,9 +556,12 @@ gpt2_status gpt2_build(const gpt2_config *cfg, int B, int T, const gpt2_buffers 
     if (e == hipSuccess) e = k_fill(dev->adam_m, np, 0.0f, m->stream);
     if (e == hipSuccess) e = k_fill(dev->adam_v, np, 0.0f, m->stream);
     if (e == hipSuccess) e = k_fill_i32(dev->iwork, m->lo.niwork, 0, m->stream);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking);
+    for (int i = 0; i < gpt2_model::NEV && e == hipSuccess; i++)
+        e = hipEventCreateWithFlags(&m->ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
         std::string msg = std::string("gpt2_build: ") + hipGetErrorString(e);
-        delete m;
+        gpt2_free(m);
         return fail(nullptr, GPT2_EDEVICE, msg);
     }
     *out = m;
@@ -644,6 +668,15 @@ gpt2_status gpt2_zero_grad(gpt2_model *m) {
     return GPT2_OK;
 }
 
+// Make `to` wait for the work enqueued so far on `from`.
+hipError_t join(gpt2_model *m, hipStream_t from, hipStream_t to) {
+    if (from == to) return hipSuccess;
+    hipEvent_t e = m->ev[m->ev_next];
+    m->ev_next = (m->ev_next + 1) % gpt2_model::NEV;
+    hipError_t r = hipEventRecord(e, from);
+    return r == hipSuccess ? hipStreamWaitEvent(to, e, 0) : r;
+}
+
 gpt2_status gpt2_backward(gpt2_model *m) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
     ProfScope prof_scope(m);
@@ -651,21 +684,30 @@ gpt2_status gpt2_backward(gpt2_model *m) {
     const Layout &l = m->lo;
     const int B = l.B, T = l.T, C = l.C, NH = l.NH, BT = (int)l.BT;
     const size_t BTC = (size_t)BT * C, c = C;
-    hipStream_t s = m->stream;
+    // Two streams: `s` carries the chain of input gradients (each step needs
+    // the previous one); `s2` the weight gradients, which only read what `s`
+    // produced.  s2 waits (join s -> s2) until its inputs are written; s waits
+    // (join s2 -> s) before it overwrites a buffer that s2 still reads: the
+    // residual gradient dres (updated in place by the LayerNorm backward),
+    // dfch and dqkv (reused by every layer).  s2 runs in order, so one wait
+    // covers everything s2 had enqueued before it.
+    hipStream_t s = m->stream, s2 = m->concurrent ? m->side : m->stream;
     float *P = m->buf.params, *G = m->buf.grads, *A = m->buf.acts, *W = m->buf.work;
     float *dres = W + l.w_dres, *dln = W + l.w_dln, *datty = W + l.w_datty, *dqkv = W + l.w_dqkv;
     float *dfch = W + l.w_dfch, *dscore = W + l.w_datt, *part = W + l.w_part, *splitk = W + l.w_splitk;
-    float *dbias_ws = W + l.w_dbias;
+    float *splitk_dw = W + l.w_splitk_dw, *dbias_ws = W + l.w_dbias;
     const float *dlogits = A + l.aoff[A_LOGITS], *lnf = A + l.aoff[A_LNF];
 
-    // head: dlnf = dlogits wte, dwte += dlogits^T lnf
+    // head: dwte += dlogits^T lnf (s2), dlnf = dlogits wte (s)
+    HIPCK(m, join(m, s, s2));
+    {
+        OnStream on_(s2);
+        Site site_("head_dw");
+        HIPCK(m, linear_bwd_dw(G + l.poff[0], nullptr, dlogits, lnf, BT, C, l.Vp, splitk_dw, dbias_ws, s2));
+    }
     {
         Site site_("head_dinp");
         HIPCK(m, linear_bwd_dinp(dln, dlogits, P + l.poff[0], BT, C, l.Vp, EPI_STORE, nullptr, splitk, s));
-    }
-    {
-        Site site_("head_dw");
-        HIPCK(m, linear_bwd_dw(G + l.poff[0], nullptr, dlogits, lnf, BT, C, l.Vp, splitk, dbias_ws, s));
     }
     const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
     KRUN(m, "layernorm_backward_kernel", 12.0 * BTC, k_layernorm_backward(dres, G + l.poff[14], G + l.poff[15], part, dln, last, P + l.poff[14],
@@ -685,36 +727,51 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         const float *fw = P + l.poff[10] + li * 4 * c * c, *pw = P + l.poff[12] + li * 4 * c * c;
 
         // fcproj: dout = dres (gradient of residual3)
+        HIPCK(m, join(m, s, s2));
         {
+            OnStream on_(s2);
             Site site_("fcproj_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, G + l.poff[13] + li * c, dres, fchg, BT, 4 * C, C, splitk, dbias_ws, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, G + l.poff[13] + li * c, dres, fchg, BT, 4 * C, C, splitk_dw, dbias_ws, s2));
         }
+        // after fcproj_dw: dres may change; the previous layer's qkv_dw is done with dqkv
+        hipEvent_t fcproj_done = m->ev[m->ev_next];
+        m->ev_next = (m->ev_next + 1) % gpt2_model::NEV;
+        if (s2 != s) HIPCK(m, hipEventRecord(fcproj_done, s2));
         {
             Site site_("fcproj_dinp");
             HIPCK(m, linear_bwd_dinp(dfch, dres, pw, BT, 4 * C, C, EPI_GELU_BWD, fch, nullptr, s));
         }
         // fc
+        HIPCK(m, join(m, s, s2));
         {
+            OnStream on_(s2);
             Site site_("fc_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, G + l.poff[11] + li * 4 * c, dfch, ln2, BT, C, 4 * C, splitk, dbias_ws, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, G + l.poff[11] + li * 4 * c, dfch, ln2, BT, C, 4 * C, splitk_dw, dbias_ws, s2));
         }
         {
             Site site_("fc_dinp");
             HIPCK(m, linear_bwd_dinp(dln, dfch, fw, BT, C, 4 * C, EPI_STORE, nullptr, nullptr, s));
         }
         // ln2: dres becomes the gradient of residual2
+        if (s2 != s) HIPCK(m, hipStreamWaitEvent(s, fcproj_done, 0));
         KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[8] + li * c, G + l.poff[9] + li * c, part, dln, res2,
                                       P + l.poff[8] + li * c, ln2m, ln2r, BT, C, true, s));
         // attproj: dout = dres
+        HIPCK(m, join(m, s, s2));
         {
+            OnStream on_(s2);
             Site site_("attproj_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, G + l.poff[7] + li * c, dres, atty, BT, C, C, splitk, dbias_ws, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, G + l.poff[7] + li * c, dres, atty, BT, C, C, splitk_dw, dbias_ws, s2));
         }
+        // after attproj_dw: dres may change; fc_dw is done with dfch
+        hipEvent_t attproj_done = m->ev[m->ev_next];
+        m->ev_next = (m->ev_next + 1) % gpt2_model::NEV;
+        if (s2 != s) HIPCK(m, hipEventRecord(attproj_done, s2));
         {
             Site site_("attproj_dinp");
             HIPCK(m, linear_bwd_dinp(datty, dres, aw, BT, C, C, EPI_STORE, nullptr, nullptr, s));
         }
-        // attention
+        // attention (overwrites dqkv: the previous layer's qkv_dw ran before fcproj_dw)
         if (l.flash) {
             const float *lse = A + l.aoff[A_LSE] + (size_t)li * B * NH * T;
             const double tri = 0.5 * T * (T + 1.0) * B * NH;
@@ -727,18 +784,23 @@ gpt2_status gpt2_backward(gpt2_model *m) {
             HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
         }
         // qkv
+        HIPCK(m, join(m, s, s2));
         {
+            OnStream on_(s2);
             Site site_("qkv_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, G + l.poff[5] + li * 3 * c, dqkv, ln1, BT, C, 3 * C, splitk, dbias_ws, s));
+            HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, G + l.poff[5] + li * 3 * c, dqkv, ln1, BT, C, 3 * C, splitk_dw, dbias_ws, s2));
         }
         {
             Site site_("qkv_dinp");
             HIPCK(m, linear_bwd_dinp(dln, dqkv, qkvw, BT, C, 3 * C, EPI_STORE, nullptr, nullptr, s));
         }
         // ln1: dres becomes the gradient of this layer's input
+        if (s2 != s) HIPCK(m, hipStreamWaitEvent(s, attproj_done, 0));
         KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[2] + li * c, G + l.poff[3] + li * c, part, dln, res,
                                       P + l.poff[2] + li * c, ln1m, ln1r, BT, C, true, s));
     }
+    // all weight gradients (dwte among them) are complete before the embedding backward adds to dwte
+    HIPCK(m, join(m, s2, s));
     KRUN(m, "encoder_backward_kernel", 12.0 * BTC, k_encoder_backward(G + l.poff[0], G + l.poff[1], dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
                                 l.V, s));
     return GPT2_OK;
@@ -763,6 +825,12 @@ gpt2_status gpt2_sync(gpt2_model *m) {
         HIPCK(m, k_fill_i32(m->buf.iwork + m->lo.i_err, 1, 0, m->stream));
         return fail(m, GPT2_ERANGE, "an id was outside [0, vocab_size)");
     }
+    return GPT2_OK;
+}
+
+gpt2_status gpt2_set_concurrency(gpt2_model *m, int enable) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    m->concurrent = enable != 0;
     return GPT2_OK;
 }
 
@@ -812,6 +880,9 @@ gpt2_status gpt2_profile_read(gpt2_model *m, gpt2_profile_entry *out, int max_en
 void gpt2_free(gpt2_model *m) {
     if (!m) return;
     for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : m->ev)
+        if (e) (void)hipEventDestroy(e);
+    if (m->side) (void)hipStreamDestroy(m->side);
     delete m;
 }
 
