@@ -3,16 +3,13 @@
     python bench.py [--steps K] [--warmup W] [--config 124m] [--gpus 1]
 
 A step is gpt2_forward (ids already resident in HBM) + gpt2_zero_grad +
-gpt2_backward + gpt2_update, enqueued on the current HIP stream (the backward
-also runs its weight-gradient products on a second stream of the library).
-W untimed steps, then K timed steps between two device synchronizations
-(`value`).  The same number of steps is then run again on one stream, with
-every launch bracketed by HIP events (the library's per-launch timing): that
-gives each kernel's average duration on its own, and so the roofline
-fraction of the dominant kernel, without perturbing the first timing.  With
---one-stream every pass keeps to one stream (the command whose kernel trace
-matches those per-launch times).  Last, the CPU oracle is timed on a bounded
-sample of the same workload.  Prints one JSON line on stdout.
+gpt2_backward + gpt2_update, enqueued on one HIP stream.  W untimed steps,
+then K timed steps between two device synchronizations (`value`).  The same
+number of steps is then run again with every launch bracketed by HIP events
+on the step's stream (the library's per-launch timing): that gives each
+kernel's average duration and the roofline fraction of the dominant kernel
+without perturbing the first timing.  Last, the CPU oracle is timed on a
+bounded sample of the same workload.  Prints one JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -108,8 +105,6 @@ def main():
     ap.add_argument("--config", default="124m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time the steps without per-launch events")
-    ap.add_argument("--one-stream", action="store_true",
-                    help="run the backward on one stream in every pass (not only the per-launch timing)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of MIB MiB (for scaling HBM byte counters)")
@@ -132,7 +127,6 @@ def main():
         inp, tgt = synth.batch(cfg, step=i)
         batches.append((torch.from_numpy(inp.ravel()).cuda(), torch.from_numpy(tgt.ravel()).cuda()))
     torch.cuda.synchronize()
-    M.set_concurrency(not args.one_stream)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
@@ -164,7 +158,6 @@ def main():
     # the same steps again, each launch bracketed by HIP events on the step's stream
     kernels, roofline, ms_ev, sites = [], None, None, []
     if not args.no_events:
-        M.set_concurrency(False)  # each launch alone: its time is its own
         M.profile_enable(True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -174,7 +167,6 @@ def main():
         ms_ev = (time.perf_counter() - t0) / args.steps * 1e3
         prof = M.profile_read()
         M.profile_enable(False)
-        M.set_concurrency(not args.one_stream)
         log(f"timed {args.steps} steps with per-launch events: {ms_ev:.2f} ms/step")
         by_kernel = {}
         for e in prof:
@@ -247,7 +239,6 @@ def main():
         "cpu_baseline": cpu,
         "last_loss": loss,
         "ms_per_step_with_events": ms_ev,
-        "streams": 1 if args.one_stream else 2,
         "kernels": kernels[:16],
     }
     print(json.dumps(out))

@@ -137,20 +137,8 @@ gpt2_status gpt2_forward(gpt2_model *model, const int32_t *inputs, const int32_t
 gpt2_status gpt2_zero_grad(gpt2_model *model);
 
 /* Backward pass of the mean loss of the last forward-with-targets:
- * grads += d(mean loss)/d(params).  GPT2_ESTATE without such a forward.
- * The weight-gradient products run on a second stream that the handle owns
- * (created by gpt2_build, default priority), concurrently with the chain of
- * input gradients on the model's stream; HIP events order the two.  Before
- * the call returns, the model's stream is made to wait for all of that work,
- * so anything enqueued later on the model's stream (gpt2_update, a copy of
- * grads, a synchronize) sees the complete gradients.  Results are the same,
- * bit for bit, with and without the second stream. */
+ * grads += d(mean loss)/d(params).  GPT2_ESTATE without such a forward. */
 gpt2_status gpt2_backward(gpt2_model *model);
-
-/* enable = 0: gpt2_backward keeps to the model's stream alone (every launch
- * in sequence, as the per-launch timing wants them); 1 (the default): it
- * uses the second stream as described above. */
-gpt2_status gpt2_set_concurrency(gpt2_model *model, int enable);
 
 /* AdamW over all params: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
  * theta -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + weight_decay theta).
@@ -164,10 +152,7 @@ gpt2_status gpt2_sync(gpt2_model *model);
 
 /* Per-launch timing of the step (tracing).  While enabled, every kernel
  * launch made by gpt2_forward / gpt2_zero_grad / gpt2_backward / gpt2_update
- * is bracketed by two HIP events on the stream it is launched on.  With the
- * second stream in use, launches overlap and each one's time includes the
- * sharing of the GPU: disable it (gpt2_set_concurrency) for times of the
- * kernels alone.  gpt2_profile_read
+ * is bracketed by two HIP events on the model's stream.  gpt2_profile_read
  * waits for the stream, then returns one entry per kernel name (the name a
  * kernel-trace profiler shows) with the number of launches, the summed
  * event-to-event time, and the summed algorithmic FLOPs and bytes (the
@@ -176,7 +161,7 @@ gpt2_status gpt2_sync(gpt2_model *model);
  * of names; at most max_entries are written.  Enabling creates HIP events
  * (host-side runtime objects); nothing is allocated during a step. */
 typedef struct {
-    char name[64];
+    char name[128];
     long long launches;
     double ms;
     double flops;

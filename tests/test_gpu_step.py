@@ -168,23 +168,6 @@ def test_backward_accumulates_and_is_deterministic(g):
     M.close()
 
 
-@pytest.mark.parametrize("case", ["hd64", "small_b4"])
-def test_one_and_two_streams_agree_bitwise(g, case):
-    cfg = CASES[case]
-    B, T = cfg["B"], cfg["T"]
-    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, synth.init_params(cfg), B, T))
-    inp, tgt = synth.batch(cfg)
-    M.forward(dev_ids(inp), dev_ids(tgt))
-    grads = []
-    for on in (True, False, True):
-        M.set_concurrency(on)
-        M.zero_grad()
-        M.backward()
-        grads.append(host(M.grads))
-    assert np.array_equal(grads[0], grads[1]) and np.array_equal(grads[0], grads[2])
-    M.close()
-
-
 def test_errors_are_reported(g):
     import torch
     cfg = CASES["tiny"]

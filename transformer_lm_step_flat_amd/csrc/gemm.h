@@ -63,3 +63,9 @@ struct GemmDesc {
 // Validates the descriptor and enqueues the kernel; returns hipErrorInvalidValue
 // for a descriptor the kernel cannot take.
 hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream);
+
+// Two independent products in one launch (they share the GPU as one grid, so
+// the tail of one is filled by the other): d1 a weight gradient (A and B
+// MN-contiguous), d2 an input gradient (A K-contiguous, B MN-contiguous),
+// both with the same nonzero `tile` and no causal mode.
+hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t stream);

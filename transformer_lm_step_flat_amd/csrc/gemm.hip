@@ -60,19 +60,26 @@ __device__ __forceinline__ void group_order(int bid, int tiles_m, int tiles_n, i
     tn = r / gs;
 }
 
+// LDS floats of the two operand tiles
 template <int BM, int BN, bool AK, bool BKC>
-__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
+struct TileLds {
+    static constexpr int KP = GEMM_BK + 4;  // pitch of a K-contiguous LDS tile
+    static constexpr int A = AK ? BM * KP : GEMM_BK * BM;
+    static constexpr int B = BKC ? BN * KP : GEMM_BK * BN;
+};
+
+// One BM x BN output tile: number `t` (after the XCD remap) of the tile
+// grid, batch / split index z, operand tiles staged in As / Bs.
+template <int BM, int BN, bool AK, bool BKC>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &p, int t, int z, float *__restrict__ As,
+                                          float *__restrict__ Bs) {
     constexpr int BK = GEMM_BK;
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int KP = BK + 4;  // pitch of a K-contiguous LDS tile
-    constexpr int A_LDS = AK ? BM * KP : BK * BM;
-    constexpr int B_LDS = BKC ? BN * KP : BK * BN;
+    constexpr int KP = TileLds<BM, BN, AK, BKC>::KP;
     constexpr int A_F4 = BM * BK / 4 / GEMM_THREADS;
     constexpr int B_F4 = BN * BK / 4 / GEMM_THREADS;
     static_assert(A_F4 >= 1 && B_F4 >= 1, "tile too small for 256 threads");
-    __shared__ __attribute__((aligned(16))) float As[A_LDS];
-    __shared__ __attribute__((aligned(16))) float Bs[B_LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -80,8 +87,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
     const int l32 = lane & 31, h = lane >> 5;
 
     int tm, tn;
-    group_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int z = blockIdx.z;
+    group_order(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int s = z % p.ksplit, zb = z / p.ksplit;
     const int zo = zb / p.nbi, zi = zb % p.nbi;
     const float *__restrict__ A = p.A + zo * p.sAo + zi * p.sAi;
@@ -254,12 +260,51 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
         }
 }
 
+template <int BM, int BN, bool AK, bool BKC>
+__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
+    using L = TileLds<BM, BN, AK, BKC>;
+    __shared__ __attribute__((aligned(16))) float As[L::A];
+    __shared__ __attribute__((aligned(16))) float Bs[L::B];
+    gemm_tile<BM, BN, AK, BKC>(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), blockIdx.z, As, Bs);
+}
+
+// Two independent products in one grid of w = w1 + w2 workgroups (w1 of
+// problem 1: its tiles, then its batches / splits; w2 of problem 2).  Both
+// use the same tile shape.  Each XCD gets an eighth of each problem, as one
+// contiguous run of problem 1 followed by one of problem 2, so that the work
+// per XCD is balanced and operand tiles are shared within an XCD's L2.
+template <int BM, int BN, bool AK1, bool BKC1, bool AK2, bool BKC2>
+__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int w1, int w) {
+    using L1 = TileLds<BM, BN, AK1, BKC1>;
+    using L2 = TileLds<BM, BN, AK2, BKC2>;
+    __shared__ __attribute__((aligned(16))) float As[L1::A > L2::A ? L1::A : L2::A];
+    __shared__ __attribute__((aligned(16))) float Bs[L1::B > L2::B ? L1::B : L2::B];
+    const int X = 8;
+    const int x = blockIdx.x % X, j = blockIdx.x / X;  // XCD, and order within it
+    const int q1 = w1 / X, m1 = w1 % X;
+    const int r1 = q1 + (x < m1);                    // problem-1 workgroups of this XCD
+    const int s1 = x * q1 + min(x, m1);              // their first index
+    if (j < r1) {
+        const int g = s1 + j, nt = p1.tiles_m * p1.tiles_n;
+        gemm_tile<BM, BN, AK1, BKC1>(p1, g % nt, g / nt, As, Bs);
+    } else {
+        const int s2 = x * (w / X) + min(x, w % X) - s1;  // workgroups of XCDs before x, less problem 1's
+        const int g = s2 + j - r1, nt = p2.tiles_m * p2.tiles_n;
+        gemm_tile<BM, BN, AK2, BKC2>(p2, g % nt, g / nt, As, Bs);
+    }
+}
+
 template <int BM, int BN>
-hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream) {
-    GemmArgs a = a0;
+void set_tiles(const GemmDesc &d, GemmArgs &a) {
     a.tiles_m = (d.M + BM - 1) / BM;
     a.tiles_n = (d.N + BN - 1) / BN;
     a.group_m = 8;
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream) {
+    GemmArgs a = a0;
+    set_tiles<BM, BN>(d, a);
     long long nb = (long long)d.nbo * d.nbi * d.ksplit;
     if (nb > 65535) return hipErrorInvalidValue;
     dim3 grid(a.tiles_m * a.tiles_n, 1, (unsigned)nb);
@@ -274,11 +319,26 @@ hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream
     return hipGetLastError();
 }
 
+template <int BM, int BN>
+hipError_t launch_pair(const GemmDesc &d1, const GemmArgs &a1_, const GemmDesc &d2, const GemmArgs &a2_,
+                       hipStream_t stream) {
+    GemmArgs a1 = a1_, a2 = a2_;
+    set_tiles<BM, BN>(d1, a1);
+    set_tiles<BM, BN>(d2, a2);
+    const long long w1 = (long long)a1.tiles_m * a1.tiles_n * d1.nbo * d1.nbi * d1.ksplit;
+    const long long w2 = (long long)a2.tiles_m * a2.tiles_n * d2.nbo * d2.nbi * d2.ksplit;
+    if (w1 + w2 > (1LL << 30)) return hipErrorInvalidValue;
+    // the one instantiation used: a weight gradient (both MN-contiguous) beside an input gradient
+    if (d1.a_kcontig || d1.b_kcontig || !d2.a_kcontig || d2.b_kcontig) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, false, false, true, false>), dim3((unsigned)(w1 + w2)),
+                       dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+    return hipGetLastError();
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-}  // namespace
-
-hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
+// Checks a descriptor and fills the kernel arguments (all but the tile grid).
+hipError_t make_args(const GemmDesc &d, GemmArgs &a) {
     if (d.M <= 0 || d.N <= 0 || d.K < 0 || !d.A || !d.B || !d.C) return hipErrorInvalidValue;
     if (d.ksplit < 1 || d.nbo < 1 || d.nbi < 1) return hipErrorInvalidValue;
     if (d.ksplit > 1 && d.epi != EPI_STORE) return hipErrorInvalidValue;
@@ -292,10 +352,10 @@ hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
     if (!aligned16(d.A) || !aligned16(d.B)) return hipErrorInvalidValue;
     if ((d.epi == EPI_RESID || d.epi == EPI_GELU_BWD) && !d.aux) return hipErrorInvalidValue;
     if (d.epi == EPI_GELU && !d.C2) return hipErrorInvalidValue;
-
-    GemmArgs a{};
-    a.A = d.A; a.B = d.B; a.C = d.C; a.C2 = d.C2; a.bias = d.bias; a.aux = d.aux; a.colsum = d.colsum;
     if (d.colsum && (d.a_kcontig || d.nbo * d.nbi != 1)) return hipErrorInvalidValue;
+
+    a = GemmArgs{};
+    a.A = d.A; a.B = d.B; a.C = d.C; a.C2 = d.C2; a.bias = d.bias; a.aux = d.aux; a.colsum = d.colsum;
     a.lda = d.lda; a.ldb = d.ldb; a.ldc = d.ldc; a.ldaux = d.ldaux;
     a.sAo = d.sAo; a.sAi = d.sAi; a.sBo = d.sBo; a.sBi = d.sBi; a.sCo = d.sCo; a.sCi = d.sCi;
     a.sCs = d.sCs;
@@ -306,7 +366,15 @@ hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
     int kc = (d.K + d.ksplit - 1) / d.ksplit;
     a.kchunk = (kc + GEMM_BK - 1) / GEMM_BK * GEMM_BK;
     if (a.kchunk == 0) a.kchunk = GEMM_BK;
+    return hipSuccess;
+}
 
+}  // namespace
+
+hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
+    GemmArgs a;
+    hipError_t e = make_args(d, a);
+    if (e != hipSuccess) return e;
     int tile = d.tile;
     if (tile == 0) {
         long long batches = (long long)d.nbo * d.nbi * d.ksplit;
@@ -317,11 +385,24 @@ hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
         else if (t64n >= 512) tile = 2;
         else tile = 3;
     }
-    // causal tiles must fit inside the zero padding written above the diagonal
     switch (tile) {
         case 1: return launch_tile<128, 128>(d, a, stream);
         case 2: return launch_tile<128, 64>(d, a, stream);
         case 3: return launch_tile<64, 64>(d, a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t stream) {
+    GemmArgs a1, a2;
+    hipError_t e = make_args(d1, a1);
+    if (e == hipSuccess) e = make_args(d2, a2);
+    if (e != hipSuccess) return e;
+    if (d1.tile != d2.tile || d1.causal || d2.causal) return hipErrorInvalidValue;
+    switch (d1.tile) {
+        case 1: return launch_pair<128, 128>(d1, a1, d2, a2, stream);
+        case 2: return launch_pair<128, 64>(d1, a1, d2, a2, stream);
+        case 3: return launch_pair<64, 64>(d1, a1, d2, a2, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -11,10 +11,15 @@
 // and a hand-written backward per layer.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <queue>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/gpt2.h"
@@ -106,6 +111,138 @@ Plan plan_gemm(int M, int N, int K, long long batches, bool allow_split) {
     return best;
 }
 
+// Planning of a weight gradient and an input gradient launched as one grid
+// (gemm_launch_pair).  Workgroups of unequal length share the CUs, so the
+// time is simulated: workgroups are dealt to the 256 CUs in grid order, a
+// CU holds up to `occ` of them and shares its rate among those resident
+// (full rate from two up, half rate with one), and a freed slot takes the
+// next workgroup.  Each workgroup's work is its tile's flops at the tile
+// shape's measured efficiency plus a fixed cost.
+struct WgGroup {
+    long long count;
+    double us;  // one workgroup alone on a CU at full rate
+};
+// fixed cost of a workgroup (first operand loads, epilogue), fitted to
+// measured pair timings at the GPT-2 layer shapes
+const double kWgFixedUs = 2.0;
+
+double simulate_us(int occ, const std::vector<WgGroup> &groups) {
+    const int NCU = 256;
+    struct Cu {
+        double t = 0;            // time of the last update
+        std::vector<double> rem;  // remaining work of the resident workgroups
+        int ver = 0;
+    };
+    std::vector<Cu> cu(NCU);
+    size_t gi = 0;
+    long long left = groups.empty() ? 0 : groups[0].count;
+    auto next_wg = [&](double &w) {
+        while (gi < groups.size() && left == 0) {
+            if (++gi < groups.size()) left = groups[gi].count;
+        }
+        if (gi >= groups.size()) return false;
+        left--;
+        w = groups[gi].us;
+        return true;
+    };
+    auto speed = [](size_t k) { return k >= 2 ? 1.0 / (double)k : 0.5; };
+    typedef std::tuple<double, int, int> Ev;  // completion time, cu, version
+    std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> pq;
+    auto schedule = [&](int c) {
+        Cu &u = cu[c];
+        u.ver++;
+        if (u.rem.empty()) return;
+        double mn = u.rem[0];
+        for (double r : u.rem) mn = r < mn ? r : mn;
+        pq.push(Ev(u.t + mn / speed(u.rem.size()), c, u.ver));
+    };
+    double w;
+    for (int k = 0; k < occ; k++)
+        for (int c = 0; c < NCU; c++)
+            if (next_wg(w)) cu[c].rem.push_back(w);
+    for (int c = 0; c < NCU; c++) schedule(c);
+    double end = 0;
+    while (!pq.empty()) {
+        Ev ev = pq.top();
+        pq.pop();
+        const double t = std::get<0>(ev);
+        const int c = std::get<1>(ev);
+        Cu &u = cu[c];
+        if (std::get<2>(ev) != u.ver) continue;
+        const double done = (t - u.t) * speed(u.rem.size());
+        std::vector<double> keep;
+        for (double r : u.rem)
+            if (r - done > 1e-9) keep.push_back(r - done);
+        u.rem.swap(keep);
+        u.t = t;
+        end = t > end ? t : end;
+        while ((int)u.rem.size() < occ && next_wg(w)) u.rem.push_back(w);
+        schedule(c);
+    }
+    return end;
+}
+
+double split_overhead_us(int ks, long long M, long long N) {
+    return ks > 1 ? 8.0 + (2.0 * ks + 2.0) * M * N * 4.0 / 5.0e6 : 0.0;
+}
+
+struct PairPlan {
+    bool pair;
+    int tile, ks_dw, ks_dinp;
+};
+
+// dW[OC][K] += dout^T inp (reduction over N) beside dinp[N][K] = dout W
+// (reduction over OC); the input gradient may split K only if allowed.  The
+// pair always runs as one grid: measured, that beats two launches (whose
+// ramp-up and drain the model does not see); the model picks the tile shape
+// and the splits.
+PairPlan plan_pair(int N, int K, int OC, bool split_dinp) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, bool>, PairPlan> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto key = std::make_tuple(N, K, OC, split_dinp);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    double best = 1e30;
+    PairPlan bp{true, 1, 1, 1};
+    static const int splits[] = {1, 2, 3, 4, 6, 8, 12, 16};
+    const double cu_flops_per_us = 157.3e6 / 256.0;
+    for (int tile = 1; tile <= 3; tile++) {
+        const TileShape &t = kTiles[tile];
+        if (K <= 64 && tile == 1) continue;
+        for (int kd : splits) {
+            if (kd > 1 && N / kd < 256) break;
+            for (int ki : splits) {
+                if (ki > 1 && (!split_dinp || OC / ki < 256)) break;
+                const double kcd = (double)ceil_div(ceil_div(N, kd), 32) * 32;
+                const double kci = (double)ceil_div(ceil_div(OC, ki), 32) * 32;
+                std::vector<WgGroup> g = {
+                    {ceil_div(OC, t.bm) * ceil_div(K, t.bn) * kd, kWgFixedUs + 2.0 * t.bm * t.bn * kcd / (t.eff * cu_flops_per_us)},
+                    {ceil_div(N, t.bm) * ceil_div(K, t.bn) * ki, kWgFixedUs + 2.0 * t.bm * t.bn * kci / (t.eff * cu_flops_per_us)}};
+                const double us = simulate_us(t.occ, g) + split_overhead_us(kd, OC, K) + split_overhead_us(ki, N, K);
+                if (us < best * 0.98) {
+                    best = us;
+                    bp = PairPlan{true, tile, kd, ki};
+                }
+            }
+        }
+    }
+    cache[key] = bp;
+    return bp;
+}
+
+// Floats of split-K partials a linear layer's backward may need, for the
+// input gradient and the weight gradient (as separate launches or as a pair).
+void bwd_split_need(int N, int K, int OC, bool split_dinp, size_t &sk_dinp, size_t &sk_dw) {
+    const Plan sd = plan_gemm(OC, K, N, 1, true), si = plan_gemm(N, K, OC, 1, split_dinp);
+    const PairPlan pp = plan_pair(N, K, OC, split_dinp);
+    size_t a = si.ksplit > 1 ? (size_t)si.ksplit * N * K : 0, b = sd.ksplit > 1 ? (size_t)sd.ksplit * OC * K : 0;
+    if (pp.pair && pp.ks_dinp > 1) a = std::max(a, (size_t)pp.ks_dinp * N * K);
+    if (pp.pair && pp.ks_dw > 1) b = std::max(b, (size_t)pp.ks_dw * OC * K);
+    sk_dinp = std::max(sk_dinp, a);
+    sk_dw = std::max(sk_dw, b);
+}
+
 struct Layout {
     int B, T, C, L, NH, V, Vp, maxT, hd;
     bool flash;  // fused attention (no T x T matrices kept)
@@ -180,20 +317,15 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.w_datt = off; off = align_up(off + (l.flash ? (size_t)B * NH * T : (size_t)B * NH * TT));
     l.w_flash = off; off = align_up(off + (l.flash ? flash_attention_work(B, T, (int)C, (int)NH) : 0));
     l.w_part = off; off = align_up(off + (size_t)ln_partials((int)BT) * 2 * C);
-    // split-K partial products of the GEMMs that may split: dlnf (main stream)
-    // and the weight gradients (side stream), in separate regions because the
-    // two streams run concurrently
+    // split-K partial products: of the input gradient dlnf (the only one
+    // allowed to split) and of the weight gradients, in separate regions
+    // because a pair of them runs as one grid
     size_t sk = 0, sk_dw = 0;
-    auto need = [&](size_t &acc, int M, int N, int K) {
-        Plan p = plan_gemm(M, N, K, 1, true);
-        if (p.ksplit > 1 && (size_t)p.ksplit * M * N > acc) acc = (size_t)p.ksplit * M * N;
-    };
-    need(sk_dw, (int)(3 * C), (int)C, (int)BT);
-    need(sk_dw, (int)C, (int)C, (int)BT);
-    need(sk_dw, (int)(4 * C), (int)C, (int)BT);
-    need(sk_dw, (int)C, (int)(4 * C), (int)BT);
-    need(sk_dw, l.Vp, (int)C, (int)BT);
-    need(sk, (int)BT, (int)C, l.Vp);
+    bwd_split_need((int)BT, (int)C, (int)(3 * C), false, sk, sk_dw);
+    bwd_split_need((int)BT, (int)C, (int)C, false, sk, sk_dw);
+    bwd_split_need((int)BT, (int)C, (int)(4 * C), false, sk, sk_dw);
+    bwd_split_need((int)BT, (int)(4 * C), (int)C, false, sk, sk_dw);
+    bwd_split_need((int)BT, (int)C, l.Vp, true, sk, sk_dw);
     l.w_splitk = off; off = align_up(off + sk);
     l.w_splitk_dw = off; off = align_up(off + sk_dw);
     l.w_dbias = off; off = align_up(off + 16 * 4 * C);
@@ -226,14 +358,6 @@ struct gpt2_model {
     Layout lo;
     gpt2_buffers buf;
     hipStream_t stream;
-    // The backward runs the weight-gradient GEMMs on a second stream, beside
-    // the input-gradient chain on `stream`; events order the two (ring of
-    // reusable events: a wait is enqueued right after each record).
-    hipStream_t side = nullptr;
-    static constexpr int NEV = 8;
-    hipEvent_t ev[NEV] = {};
-    int ev_next = 0;
-    bool concurrent = true;  // false: the backward keeps to `stream` alone
     bool have_targets = false;
     std::string err;
     Profiler prof;
@@ -264,8 +388,6 @@ thread_local Profiler *g_prof = nullptr;
 
 thread_local const char *g_site = "";  // call site of the launches being made
 
-thread_local hipStream_t g_launch_stream = nullptr;  // stream of the launches being made, if not the model's
-
 template <class F>
 hipError_t timed(const char *name, double flops, double bytes, F &&f) {
     Profiler *p = g_prof;
@@ -277,12 +399,11 @@ hipError_t timed(const char *name, double flops, double bytes, F &&f) {
         p->pool.push_back(e);
     }
     hipEvent_t a = p->pool[p->used++], b = p->pool[p->used++];
-    hipStream_t ls = g_launch_stream ? g_launch_stream : p->stream;
-    hipError_t e = hipEventRecord(a, ls);
+    hipError_t e = hipEventRecord(a, p->stream);
     if (e != hipSuccess) return e;
     e = f();
     if (e != hipSuccess) return e;
-    e = hipEventRecord(b, ls);
+    e = hipEventRecord(b, p->stream);
     p->recs.push_back({name, g_site, flops, bytes, a, b});
     return e;
 }
@@ -295,19 +416,19 @@ struct Site {
     ~Site() { g_site = saved; }
 };
 
-// Launches in its scope go to stream `s` (for the per-launch timing events).
-struct OnStream {
-    hipStream_t saved;
-    explicit OnStream(hipStream_t s) : saved(g_launch_stream) { g_launch_stream = s; }
-    ~OnStream() { g_launch_stream = saved; }
-};
-
 // Makes a model's profiler the active one for the duration of an API call.
 struct ProfScope {
     Profiler *saved;
     explicit ProfScope(gpt2_model *m) : saved(g_prof) { g_prof = m && m->prof.on ? &m->prof : nullptr; }
     ~ProfScope() { g_prof = saved; }
 };
+
+const char *gemm_pair_name(int tile) {
+    static const char *names[3] = {"gemm_pair_kernel<128, 128, false, false, true, false>",
+                                   "gemm_pair_kernel<128, 64, false, false, true, false>",
+                                   "gemm_pair_kernel<64, 64, false, false, true, false>"};
+    return names[tile >= 1 && tile <= 3 ? tile - 1 : 0];
+}
 
 // The name rocprofv3 shows for the GEMM instantiation a descriptor runs.
 const char *gemm_name(const GemmDesc &d) {
@@ -366,23 +487,67 @@ hipError_t linear_fwd(float *out, const float *inp, const float *W, const float 
 }
 
 // dinp[N][K] = dout[N][OC] W[OC][K]  (epilogue EPI_STORE or EPI_GELU_BWD with aux)
-hipError_t linear_bwd_dinp(float *dinp, const float *dout, const float *W, int N, int K, int OC, int epi,
-                           const float *aux, float *splitk, hipStream_t s) {
+// Flops and compulsory bytes of one (unbatched, non-causal) product.
+void gemm_cost(const GemmDesc &d, double &flops, double &bytes) {
+    flops = 2.0 * d.M * d.N * d.K;
+    double out = (double)d.M * d.N * (d.ksplit > 1 ? d.ksplit : 1);
+    if (d.epi == EPI_ACCUM || d.epi == EPI_RESID || d.epi == EPI_GELU || d.epi == EPI_GELU_BWD) out *= 2;
+    bytes = 4.0 * ((double)d.M * d.K + (double)d.K * d.N + out);
+}
+
+// Descriptors of the two products of a linear layer's backward.
+// dinp[N][K] = dout[N][OC] W[OC][K] with epilogue epi (split-K partials to splitk if ks > 1)
+GemmDesc dinp_desc(float *dinp, const float *dout, const float *W, int N, int K, int OC, int epi, const float *aux,
+                   Plan p, float *splitk) {
     GemmDesc d;
     d.a_kcontig = true; d.b_kcontig = false;
     d.M = N; d.N = K; d.K = OC;
     d.A = dout; d.lda = OC; d.B = W; d.ldb = K; d.C = dinp; d.ldc = K;
     d.epi = epi; d.aux = aux; d.ldaux = K;
-    Plan p = plan_gemm(N, K, OC, 1, epi == EPI_STORE && splitk != nullptr);
+    d.tile = p.tile;
+    if (p.ksplit > 1) { d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)N * K; }
+    return d;
+}
+// dW[OC][K] += dout^T inp, dbias += column sums of dout (partials to splitk / dbias_ws if ks > 1)
+GemmDesc dw_desc(float *dW, float *dbias, const float *dout, const float *inp, int N, int K, int OC, Plan p,
+                 float *splitk, float *dbias_ws) {
+    GemmDesc d;
+    d.a_kcontig = false; d.b_kcontig = false;
+    d.M = OC; d.N = K; d.K = N;
+    d.A = dout; d.lda = OC; d.B = inp; d.ldb = K; d.C = dW; d.ldc = K;
     d.tile = p.tile;
     if (p.ksplit > 1) {
-        d.C = splitk; d.ldc = K; d.ksplit = p.ksplit; d.sCs = (long long)N * K;
-        hipError_t e = gemm_run(d, s);
-        if (e != hipSuccess) return e;
-        return timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 1) * N * K,
-                     [&]() { return k_sum_partials(dinp, splitk, p.ksplit, (size_t)N * K, false, s); });
+        d.epi = EPI_STORE; d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)OC * K;
+        d.colsum = dbias ? dbias_ws : nullptr;
+    } else {
+        d.epi = EPI_ACCUM;
+        d.colsum = dbias;
     }
-    return gemm_run(d, s);
+    return d;
+}
+
+hipError_t dinp_finish(float *dinp, const float *splitk, int N, int K, int ks, hipStream_t s) {
+    if (ks <= 1) return hipSuccess;
+    return timed("sum_partials_kernel", 0, 4.0 * (ks + 1) * N * K,
+                 [&]() { return k_sum_partials(dinp, splitk, ks, (size_t)N * K, false, s); });
+}
+hipError_t dw_finish(float *dW, float *dbias, const float *splitk, const float *dbias_ws, int K, int OC, int ks,
+                     hipStream_t s) {
+    if (ks <= 1) return hipSuccess;
+    hipError_t e = timed("sum_partials_kernel", 0, 4.0 * (ks + 2) * OC * K,
+                         [&]() { return k_sum_partials(dW, splitk, ks, (size_t)OC * K, true, s); });
+    if (e != hipSuccess || !dbias) return e;
+    return timed("sum_partials_kernel", 0, 4.0 * (ks + 2) * OC,
+                 [&]() { return k_sum_partials(dbias, dbias_ws, ks, (size_t)OC, true, s); });
+}
+
+// dinp[N][K] = dout[N][OC] W[OC][K] with an epilogue (the input gradient of a
+// linear layer).  Split-K only for EPI_STORE and when splitk is given.
+hipError_t linear_bwd_dinp(float *dinp, const float *dout, const float *W, int N, int K, int OC, int epi,
+                           const float *aux, float *splitk, hipStream_t s) {
+    const Plan p = plan_gemm(N, K, OC, 1, epi == EPI_STORE && splitk != nullptr);
+    hipError_t e = gemm_run(dinp_desc(dinp, dout, W, N, K, OC, epi, aux, p, splitk), s);
+    return e != hipSuccess ? e : dinp_finish(dinp, splitk, N, K, p.ksplit, s);
 }
 
 // dW[OC][K] += dout[N][OC]^T inp[N][K]; dbias[OC] += column sums of dout
@@ -390,26 +555,35 @@ hipError_t linear_bwd_dinp(float *dinp, const float *dout, const float *W, int N
 // and the partial bias sums to `dbias_ws` (16 * OC floats).
 hipError_t linear_bwd_dw(float *dW, float *dbias, const float *dout, const float *inp, int N, int K, int OC,
                          float *splitk, float *dbias_ws, hipStream_t s) {
-    GemmDesc d;
-    d.a_kcontig = false; d.b_kcontig = false;
-    d.M = OC; d.N = K; d.K = N;
-    d.A = dout; d.lda = OC; d.B = inp; d.ldb = K; d.C = dW; d.ldc = K;
-    Plan p = plan_gemm(OC, K, N, 1, splitk != nullptr);
-    d.tile = p.tile;
-    if (p.ksplit > 1) {
-        d.epi = EPI_STORE; d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)OC * K;
-        d.colsum = dbias ? dbias_ws : nullptr;
-        hipError_t e = gemm_run(d, s);
-        if (e != hipSuccess) return e;
-        e = timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 2) * OC * K,
-                  [&]() { return k_sum_partials(dW, splitk, p.ksplit, (size_t)OC * K, true, s); });
-        if (e != hipSuccess || !dbias) return e;
-        return timed("sum_partials_kernel", 0, 4.0 * (p.ksplit + 2) * OC,
-                     [&]() { return k_sum_partials(dbias, dbias_ws, p.ksplit, (size_t)OC, true, s); });
+    const Plan p = plan_gemm(OC, K, N, 1, splitk != nullptr);
+    hipError_t e = gemm_run(dw_desc(dW, dbias, dout, inp, N, K, OC, p, splitk, dbias_ws), s);
+    return e != hipSuccess ? e : dw_finish(dW, dbias, splitk, dbias_ws, K, OC, p.ksplit, s);
+}
+
+// Both gradients of a linear layer out = inp W^T + b given dout: the weight
+// and bias gradients (accumulated) and the input gradient (with epilogue
+// epi; dinp may be null to skip it).  When the planner predicts a gain the
+// two products run as one grid, so that each fills the other's idle CUs.
+// splitk_dinp (may be null: no split of the input gradient) and splitk_dw /
+// dbias_ws are separate regions, both in use at once.
+hipError_t linear_bwd(float *dinp, int epi, const float *aux, float *dW, float *dbias, const float *dout,
+                      const float *inp, const float *W, int N, int K, int OC, float *splitk_dinp, float *splitk_dw,
+                      float *dbias_ws, hipStream_t s) {
+    const bool split_dinp = epi == EPI_STORE && splitk_dinp != nullptr;
+    const PairPlan pp = dinp ? plan_pair(N, K, OC, split_dinp) : PairPlan{false, 0, 1, 1};
+    if (!pp.pair) {
+        hipError_t e = dinp ? linear_bwd_dinp(dinp, dout, W, N, K, OC, epi, aux, splitk_dinp, s) : hipSuccess;
+        return e != hipSuccess ? e : linear_bwd_dw(dW, dbias, dout, inp, N, K, OC, splitk_dw, dbias_ws, s);
     }
-    d.epi = EPI_ACCUM;
-    d.colsum = dbias;
-    return gemm_run(d, s);
+    const GemmDesc dd = dw_desc(dW, dbias, dout, inp, N, K, OC, Plan{pp.tile, pp.ks_dw}, splitk_dw, dbias_ws);
+    const GemmDesc di = dinp_desc(dinp, dout, W, N, K, OC, epi, aux, Plan{pp.tile, pp.ks_dinp}, splitk_dinp);
+    double f1, b1, f2, b2;
+    gemm_cost(dd, f1, b1);
+    gemm_cost(di, f2, b2);
+    hipError_t e = timed(gemm_pair_name(pp.tile), f1 + f2, b1 + b2, [&]() { return gemm_launch_pair(dd, di, s); });
+    if (e == hipSuccess) e = dw_finish(dW, dbias, splitk_dw, dbias_ws, K, OC, pp.ks_dw, s);
+    if (e == hipSuccess) e = dinp_finish(dinp, splitk_dinp, N, K, pp.ks_dinp, s);
+    return e;
 }
 
 // Attention forward over qkv [B][T][3C]: att = softmax(scale Q K^T) (causal), atty = att V.
@@ -556,9 +730,6 @@ gpt2_status gpt2_build(const gpt2_config *cfg, int B, int T, const gpt2_buffers 
     if (e == hipSuccess) e = k_fill(dev->adam_m, np, 0.0f, m->stream);
     if (e == hipSuccess) e = k_fill(dev->adam_v, np, 0.0f, m->stream);
     if (e == hipSuccess) e = k_fill_i32(dev->iwork, m->lo.niwork, 0, m->stream);
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking);
-    for (int i = 0; i < gpt2_model::NEV && e == hipSuccess; i++)
-        e = hipEventCreateWithFlags(&m->ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
         std::string msg = std::string("gpt2_build: ") + hipGetErrorString(e);
         gpt2_free(m);
@@ -668,15 +839,6 @@ gpt2_status gpt2_zero_grad(gpt2_model *m) {
     return GPT2_OK;
 }
 
-// Make `to` wait for the work enqueued so far on `from`.
-hipError_t join(gpt2_model *m, hipStream_t from, hipStream_t to) {
-    if (from == to) return hipSuccess;
-    hipEvent_t e = m->ev[m->ev_next];
-    m->ev_next = (m->ev_next + 1) % gpt2_model::NEV;
-    hipError_t r = hipEventRecord(e, from);
-    return r == hipSuccess ? hipStreamWaitEvent(to, e, 0) : r;
-}
-
 gpt2_status gpt2_backward(gpt2_model *m) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
     ProfScope prof_scope(m);
@@ -684,30 +846,18 @@ gpt2_status gpt2_backward(gpt2_model *m) {
     const Layout &l = m->lo;
     const int B = l.B, T = l.T, C = l.C, NH = l.NH, BT = (int)l.BT;
     const size_t BTC = (size_t)BT * C, c = C;
-    // Two streams: `s` carries the chain of input gradients (each step needs
-    // the previous one); `s2` the weight gradients, which only read what `s`
-    // produced.  s2 waits (join s -> s2) until its inputs are written; s waits
-    // (join s2 -> s) before it overwrites a buffer that s2 still reads: the
-    // residual gradient dres (updated in place by the LayerNorm backward),
-    // dfch and dqkv (reused by every layer).  s2 runs in order, so one wait
-    // covers everything s2 had enqueued before it.
-    hipStream_t s = m->stream, s2 = m->concurrent ? m->side : m->stream;
+    hipStream_t s = m->stream;
     float *P = m->buf.params, *G = m->buf.grads, *A = m->buf.acts, *W = m->buf.work;
     float *dres = W + l.w_dres, *dln = W + l.w_dln, *datty = W + l.w_datty, *dqkv = W + l.w_dqkv;
     float *dfch = W + l.w_dfch, *dscore = W + l.w_datt, *part = W + l.w_part, *splitk = W + l.w_splitk;
     float *splitk_dw = W + l.w_splitk_dw, *dbias_ws = W + l.w_dbias;
     const float *dlogits = A + l.aoff[A_LOGITS], *lnf = A + l.aoff[A_LNF];
 
-    // head: dwte += dlogits^T lnf (s2), dlnf = dlogits wte (s)
-    HIPCK(m, join(m, s, s2));
+    // head: dlnf = dlogits wte, dwte += dlogits^T lnf
     {
-        OnStream on_(s2);
-        Site site_("head_dw");
-        HIPCK(m, linear_bwd_dw(G + l.poff[0], nullptr, dlogits, lnf, BT, C, l.Vp, splitk_dw, dbias_ws, s2));
-    }
-    {
-        Site site_("head_dinp");
-        HIPCK(m, linear_bwd_dinp(dln, dlogits, P + l.poff[0], BT, C, l.Vp, EPI_STORE, nullptr, splitk, s));
+        Site site_("head_bwd");
+        HIPCK(m, linear_bwd(dln, EPI_STORE, nullptr, G + l.poff[0], nullptr, dlogits, lnf, P + l.poff[0], BT, C, l.Vp,
+                            splitk, splitk_dw, dbias_ws, s));
     }
     const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
     KRUN(m, "layernorm_backward_kernel", 12.0 * BTC, k_layernorm_backward(dres, G + l.poff[14], G + l.poff[15], part, dln, last, P + l.poff[14],
@@ -726,52 +876,28 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         const float *qkvw = P + l.poff[4] + li * 3 * c * c, *aw = P + l.poff[6] + li * c * c;
         const float *fw = P + l.poff[10] + li * 4 * c * c, *pw = P + l.poff[12] + li * 4 * c * c;
 
-        // fcproj: dout = dres (gradient of residual3)
-        HIPCK(m, join(m, s, s2));
+        // fcproj: dout = dres (gradient of residual3); dfch through GELU'
         {
-            OnStream on_(s2);
-            Site site_("fcproj_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[12] + li * 4 * c * c, G + l.poff[13] + li * c, dres, fchg, BT, 4 * C, C, splitk_dw, dbias_ws, s2));
-        }
-        // after fcproj_dw: dres may change; the previous layer's qkv_dw is done with dqkv
-        hipEvent_t fcproj_done = m->ev[m->ev_next];
-        m->ev_next = (m->ev_next + 1) % gpt2_model::NEV;
-        if (s2 != s) HIPCK(m, hipEventRecord(fcproj_done, s2));
-        {
-            Site site_("fcproj_dinp");
-            HIPCK(m, linear_bwd_dinp(dfch, dres, pw, BT, 4 * C, C, EPI_GELU_BWD, fch, nullptr, s));
+            Site site_("fcproj_bwd");
+            HIPCK(m, linear_bwd(dfch, EPI_GELU_BWD, fch, G + l.poff[12] + li * 4 * c * c, G + l.poff[13] + li * c, dres,
+                                fchg, pw, BT, 4 * C, C, nullptr, splitk_dw, dbias_ws, s));
         }
         // fc
-        HIPCK(m, join(m, s, s2));
         {
-            OnStream on_(s2);
-            Site site_("fc_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[10] + li * 4 * c * c, G + l.poff[11] + li * 4 * c, dfch, ln2, BT, C, 4 * C, splitk_dw, dbias_ws, s2));
-        }
-        {
-            Site site_("fc_dinp");
-            HIPCK(m, linear_bwd_dinp(dln, dfch, fw, BT, C, 4 * C, EPI_STORE, nullptr, nullptr, s));
+            Site site_("fc_bwd");
+            HIPCK(m, linear_bwd(dln, EPI_STORE, nullptr, G + l.poff[10] + li * 4 * c * c, G + l.poff[11] + li * 4 * c,
+                                dfch, ln2, fw, BT, C, 4 * C, nullptr, splitk_dw, dbias_ws, s));
         }
         // ln2: dres becomes the gradient of residual2
-        if (s2 != s) HIPCK(m, hipStreamWaitEvent(s, fcproj_done, 0));
         KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[8] + li * c, G + l.poff[9] + li * c, part, dln, res2,
                                       P + l.poff[8] + li * c, ln2m, ln2r, BT, C, true, s));
         // attproj: dout = dres
-        HIPCK(m, join(m, s, s2));
         {
-            OnStream on_(s2);
-            Site site_("attproj_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[6] + li * c * c, G + l.poff[7] + li * c, dres, atty, BT, C, C, splitk_dw, dbias_ws, s2));
+            Site site_("attproj_bwd");
+            HIPCK(m, linear_bwd(datty, EPI_STORE, nullptr, G + l.poff[6] + li * c * c, G + l.poff[7] + li * c, dres,
+                                atty, aw, BT, C, C, nullptr, splitk_dw, dbias_ws, s));
         }
-        // after attproj_dw: dres may change; fc_dw is done with dfch
-        hipEvent_t attproj_done = m->ev[m->ev_next];
-        m->ev_next = (m->ev_next + 1) % gpt2_model::NEV;
-        if (s2 != s) HIPCK(m, hipEventRecord(attproj_done, s2));
-        {
-            Site site_("attproj_dinp");
-            HIPCK(m, linear_bwd_dinp(datty, dres, aw, BT, C, C, EPI_STORE, nullptr, nullptr, s));
-        }
-        // attention (overwrites dqkv: the previous layer's qkv_dw ran before fcproj_dw)
+        // attention
         if (l.flash) {
             const float *lse = A + l.aoff[A_LSE] + (size_t)li * B * NH * T;
             const double tri = 0.5 * T * (T + 1.0) * B * NH;
@@ -784,23 +910,15 @@ gpt2_status gpt2_backward(gpt2_model *m) {
             HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
         }
         // qkv
-        HIPCK(m, join(m, s, s2));
         {
-            OnStream on_(s2);
-            Site site_("qkv_dw");
-            HIPCK(m, linear_bwd_dw(G + l.poff[4] + li * 3 * c * c, G + l.poff[5] + li * 3 * c, dqkv, ln1, BT, C, 3 * C, splitk_dw, dbias_ws, s2));
-        }
-        {
-            Site site_("qkv_dinp");
-            HIPCK(m, linear_bwd_dinp(dln, dqkv, qkvw, BT, C, 3 * C, EPI_STORE, nullptr, nullptr, s));
+            Site site_("qkv_bwd");
+            HIPCK(m, linear_bwd(dln, EPI_STORE, nullptr, G + l.poff[4] + li * 3 * c * c, G + l.poff[5] + li * 3 * c, dqkv,
+                                ln1, qkvw, BT, C, 3 * C, nullptr, splitk_dw, dbias_ws, s));
         }
         // ln1: dres becomes the gradient of this layer's input
-        if (s2 != s) HIPCK(m, hipStreamWaitEvent(s, attproj_done, 0));
         KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[2] + li * c, G + l.poff[3] + li * c, part, dln, res,
                                       P + l.poff[2] + li * c, ln1m, ln1r, BT, C, true, s));
     }
-    // all weight gradients (dwte among them) are complete before the embedding backward adds to dwte
-    HIPCK(m, join(m, s2, s));
     KRUN(m, "encoder_backward_kernel", 12.0 * BTC, k_encoder_backward(G + l.poff[0], G + l.poff[1], dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
                                 l.V, s));
     return GPT2_OK;
@@ -825,12 +943,6 @@ gpt2_status gpt2_sync(gpt2_model *m) {
         HIPCK(m, k_fill_i32(m->buf.iwork + m->lo.i_err, 1, 0, m->stream));
         return fail(m, GPT2_ERANGE, "an id was outside [0, vocab_size)");
     }
-    return GPT2_OK;
-}
-
-gpt2_status gpt2_set_concurrency(gpt2_model *m, int enable) {
-    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
-    m->concurrent = enable != 0;
     return GPT2_OK;
 }
 
@@ -880,9 +992,6 @@ gpt2_status gpt2_profile_read(gpt2_model *m, gpt2_profile_entry *out, int max_en
 void gpt2_free(gpt2_model *m) {
     if (!m) return;
     for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
-    for (hipEvent_t e : m->ev)
-        if (e) (void)hipEventDestroy(e);
-    if (m->side) (void)hipStreamDestroy(m->side);
     delete m;
 }
 
@@ -904,23 +1013,18 @@ gpt2_status gpt2k_linear_forward(float *out, const float *inp, const float *W, c
 }
 
 size_t gpt2k_linear_backward_work(int N, int K, int OC) {
-    size_t sk = 0;
-    Plan p1 = plan_gemm(N, K, OC, 1, true), p2 = plan_gemm(OC, K, N, 1, true);
-    if (p1.ksplit > 1) sk = (size_t)p1.ksplit * N * K;
-    if (p2.ksplit > 1 && (size_t)p2.ksplit * OC * K > sk) sk = (size_t)p2.ksplit * OC * K;
-    return align_up(sk) + align_up((size_t)16 * OC);
+    size_t a = 0, b = 0;
+    bwd_split_need(N, K, OC, true, a, b);
+    return align_up(a) + align_up(b) + align_up((size_t)16 * OC);
 }
 
 gpt2_status gpt2k_linear_backward(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
                                   const float *W, int N, int K, int OC, float *work, void *stream) {
     hipStream_t s = (hipStream_t)stream;
-    Plan p1 = plan_gemm(N, K, OC, 1, true), p2 = plan_gemm(OC, K, N, 1, true);
-    size_t sk = 0;
-    if (p1.ksplit > 1) sk = (size_t)p1.ksplit * N * K;
-    if (p2.ksplit > 1 && (size_t)p2.ksplit * OC * K > sk) sk = (size_t)p2.ksplit * OC * K;
-    float *splitk = work, *dbias_ws = work + align_up(sk);
-    if (dinp) KCK(linear_bwd_dinp(dinp, dout, W, N, K, OC, EPI_STORE, nullptr, splitk, s));
-    KCK(linear_bwd_dw(dW, dbias, dout, inp, N, K, OC, splitk, dbias_ws, s));
+    size_t a = 0, b = 0;
+    bwd_split_need(N, K, OC, true, a, b);
+    float *splitk = work, *splitk_dw = work + align_up(a), *dbias_ws = splitk_dw + align_up(b);
+    KCK(linear_bwd(dinp, EPI_STORE, nullptr, dW, dbias, dout, inp, W, N, K, OC, splitk, splitk_dw, dbias_ws, s));
     return GPT2_OK;
 }
 

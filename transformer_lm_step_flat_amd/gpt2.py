@@ -44,7 +44,7 @@ class Buffers(ctypes.Structure):
 
 
 class ProfileEntry(ctypes.Structure):
-    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_longlong), ("ms", ctypes.c_double),
+    _fields_ = [("name", ctypes.c_char * 128), ("launches", ctypes.c_longlong), ("ms", ctypes.c_double),
                 ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
 
 
@@ -65,7 +65,6 @@ _SIGS = {
     "gpt2_backward": [_P],
     "gpt2_update": [_P, _F, _F, _F, _F, _F, _I],
     "gpt2_sync": [_P],
-    "gpt2_set_concurrency": [_P, _I],
     "gpt2_profile_enable": [_P, _I],
     "gpt2_profile_read": [_P, ctypes.POINTER(ProfileEntry), _I, ctypes.POINTER(_I)],
     "gpt2k_linear_forward": [_P, _P, _P, _P, _I, _I, _I, _P],
@@ -258,10 +257,6 @@ class Model:
         _check(lib().gpt2_sync(self._h), self._h)
 
     # --- per-launch timing
-    def set_concurrency(self, on: bool = True):
-        """True (default): the backward runs weight gradients on a second stream."""
-        _check(lib().gpt2_set_concurrency(self._h, int(on)), self._h)
-
     def profile_enable(self, on: bool = True):
         _check(lib().gpt2_profile_enable(self._h, int(on)), self._h)
 
