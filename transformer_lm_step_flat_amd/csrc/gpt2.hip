@@ -486,7 +486,6 @@ hipError_t linear_fwd(float *out, const float *inp, const float *W, const float 
     return gemm_run(d, s);
 }
 
-// dinp[N][K] = dout[N][OC] W[OC][K]  (epilogue EPI_STORE or EPI_GELU_BWD with aux)
 // Flops and compulsory bytes of one (unbatched, non-causal) product.
 void gemm_cost(const GemmDesc &d, double &flops, double &bytes) {
     flops = 2.0 * d.M * d.N * d.K;

@@ -463,36 +463,40 @@ __global__ __launch_bounds__(256) void gelu_backward_kernel(floatx4 *dinp, const
     dinp[i] = y;
 }
 
+// Each workgroup updates one contiguous run of 4 x 256 float4s: every load
+// of the run is issued before any arithmetic, and the four streams are read
+// and written with non-temporal hints (each byte is touched once per step).
+constexpr int ADAMW_U = 4;
 __global__ __launch_bounds__(256) void adamw_kernel(floatx4 *params, const floatx4 *grads, floatx4 *m, floatx4 *v,
                                                     size_t n4, float lr, float b1, float b2, float eps, float wd,
                                                     float inv_c1, float inv_c2) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    // two 16-byte elements per thread and iteration: more loads in flight
-    for (size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n4; i0 += 2 * stride) {
-        const size_t idx[2] = {i0, i0 + stride};
-        floatx4 g[2], mm[2], vv[2], p[2];
+    const size_t base = (size_t)blockIdx.x * 256 * ADAMW_U + threadIdx.x;
+    floatx4 g[ADAMW_U], mm[ADAMW_U], vv[ADAMW_U], p[ADAMW_U];
 #pragma unroll
-        for (int u = 0; u < 2; u++)
-            if (idx[u] < n4) {
-                g[u] = grads[idx[u]];
-                mm[u] = m[idx[u]];
-                vv[u] = v[idx[u]];
-                p[u] = params[idx[u]];
+    for (int u = 0; u < ADAMW_U; u++) {
+        const size_t i = base + (size_t)u * 256;
+        if (i < n4) {
+            g[u] = __builtin_nontemporal_load(grads + i);
+            mm[u] = __builtin_nontemporal_load(m + i);
+            vv[u] = __builtin_nontemporal_load(v + i);
+            p[u] = __builtin_nontemporal_load(params + i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < ADAMW_U; u++) {
+        const size_t i = base + (size_t)u * 256;
+        if (i < n4) {
+            mm[u] = b1 * mm[u] + (1.0f - b1) * g[u];
+            vv[u] = b2 * vv[u] + (1.0f - b2) * g[u] * g[u];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float mhat = mm[u][e] * inv_c1, vhat = vv[u][e] * inv_c2;
+                p[u][e] -= lr * (mhat / (sqrtf(vhat) + eps) + wd * p[u][e]);
             }
-#pragma unroll
-        for (int u = 0; u < 2; u++)
-            if (idx[u] < n4) {
-                mm[u] = b1 * mm[u] + (1.0f - b1) * g[u];
-                vv[u] = b2 * vv[u] + (1.0f - b2) * g[u] * g[u];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float mhat = mm[u][e] * inv_c1, vhat = vv[u][e] * inv_c2;
-                    p[u][e] -= lr * (mhat / (sqrtf(vhat) + eps) + wd * p[u][e]);
-                }
-                m[idx[u]] = mm[u];
-                v[idx[u]] = vv[u];
-                params[idx[u]] = p[u];
-            }
+            __builtin_nontemporal_store(mm[u], m + i);
+            __builtin_nontemporal_store(vv[u], v + i);
+            __builtin_nontemporal_store(p[u], params + i);
+        }
     }
 }
 
@@ -638,9 +642,10 @@ hipError_t k_adamw(float *params, const float *grads, float *m, float *v, size_t
                    float eps, float wd, float c1, float c2, hipStream_t s) {
     if (n % 4) return hipErrorInvalidValue;
     size_t n4 = n / 4;
-    unsigned g = grid_for(n4, 256);
-    if (g > 8192) g = 8192;
-    hipLaunchKernelGGL(adamw_kernel, dim3(g), dim3(256), 0, s, (floatx4 *)params, (const floatx4 *)grads,
+    if (n4 == 0) return hipSuccess;
+    const size_t g = (n4 + 256 * ADAMW_U - 1) / (256 * ADAMW_U);
+    if (g > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)g), dim3(256), 0, s, (floatx4 *)params, (const floatx4 *)grads,
                        (floatx4 *)m, (floatx4 *)v, n4, lr, b1, b2, eps, wd, 1.0f / c1, 1.0f / c2);
     return hipGetLastError();
 }
