@@ -97,6 +97,104 @@ def cpu_baseline(cfg, T_sample: int):
                       f"1 sequence x {T_sample} ids of the same seeded stream, float64; {dt:.1f} s wall"}
 
 
+def _short_kernel_name(n: str) -> str:
+    n = n.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    i = n.find("(")
+    return n[:i] if i > 0 else n
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, steps: int, copy_mib: int, command: str, config: str):
+    """Summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, each with --copy-calibration): per-kernel HBM bytes per
+    dispatch scaled by what the counters read for the plain copy of known
+    size, and per-kernel durations from the dispatch timestamps (counter
+    collection serialises dispatches, so each is a kernel alone).  Writes
+    the Markdown summary to stdout and the dominant kernel's bytes per
+    launch to TRAFFIC_FILE."""
+    import collections
+    import csv
+
+    def load(path, counter):
+        per = collections.defaultdict(list)
+        dur = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _short_kernel_name(r["Kernel_Name"])
+            per[k].append(float(r["Counter_Value"]))
+            dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
+        return per, dur
+
+    fetch, dur = load(fetch_csv, "FETCH_SIZE")
+    write, _ = load(write_csv, "WRITE_SIZE")
+    # the copy: the elementwise kernel with the largest write (the fill of its source writes but does not read)
+    copy_kib = copy_mib * 1024.0
+    cands = [k for k in write if "elementwise" in k]
+    ck = max(cands, key=lambda k: max(fetch.get(k, [0])))
+    f_scale = copy_kib / max(fetch[ck])
+    w_scale = copy_kib / max(write[ck])
+    lib_kernels = [k for k in dur if "elementwise" not in k and "rocclr" not in k]
+    tot = {k: sum(dur[k]) for k in lib_kernels}
+    dom = max(tot, key=tot.get)
+    rows = []
+    for k in sorted(lib_kernels, key=lambda k: -tot[k]):
+        n = len(dur[k])
+        fb = sum(fetch[k]) / n * 1024 * f_scale
+        wb = sum(write.get(k, [0])) / max(1, len(write.get(k, []))) * 1024 * w_scale
+        rows.append((k, n, sum(dur[k]) / n, fb, wb))
+    print(f"# HBM traffic and kernel durations under counter collection: {config}\n")
+    print(f"Command (each pass its own run): `{command}`\n")
+    print(f"Copy calibration: {copy_mib} MiB read and written by `{ck}`; FETCH_SIZE reads "
+          f"{max(fetch[ck]):.0f} KiB (scale {f_scale:.3f}), WRITE_SIZE {max(write[ck]):.0f} KiB (scale {w_scale:.3f}).\n")
+    print("| kernel | dispatches | avg ms | HBM read MB / dispatch | HBM write MB / dispatch |")
+    print("|---|---:|---:|---:|---:|")
+    for k, n, ms, fb, wb in rows:
+        print(f"| `{k}` | {n} | {ms:.4f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    k, n, ms, fb, wb = next(r for r in rows if r[0] == dom)
+    out = {"kernel": dom, "config": config, "sources_sha256": sources_sha256(), "dispatches": n,
+           "hbm_read_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
+           "hbm_bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
+           "command": command}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"\nDominant kernel `{dom}`: {(fb + wb) / 1e6:.1f} MB of HBM traffic per launch "
+          f"(read {fb / 1e6:.1f}, write {wb / 1e6:.1f}); written to {os.path.relpath(TRAFFIC_FILE, ROOT)}.")
+
+
+def sq_summary(sq_csv: str, command: str, config: str):
+    """Summarise a rocprofv3 --pmc run with SQ_BUSY_CYCLES, SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_MFMA, SQ_WAVES and GRBM_GUI_ACTIVE: per kernel, the share of busy
+    cycles in which the SIMDs' matrix units were busy and the shader clock.
+    MI355X counts: SQ_BUSY_CYCLES summed over 32 shader engines,
+    SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs, GRBM_GUI_ACTIVE over 8 XCDs."""
+    import collections
+    import csv
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(dict)
+    for r in csv.DictReader(open(sq_csv)):
+        k = _short_kernel_name(r["Kernel_Name"])
+        disp[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+    print(f"# Matrix-unit busy share and clock under counter collection: {config}\n")
+    print(f"Command: `{command}`\n")
+    print("| kernel | dispatches | avg ms | clock GHz | MFMA busy / busy cycles | MFMA instr / dispatch |")
+    print("|---|---:|---:|---:|---:|---:|")
+    rows = []
+    for k, c in acc.items():
+        n = len(disp[k])
+        secs = sum(disp[k].values())
+        if c.get("SQ_BUSY_CYCLES", 0) <= 0 or secs <= 0:
+            continue
+        busy = c["SQ_BUSY_CYCLES"] / 32
+        rows.append((secs, k, n, secs / n * 1e3, c["GRBM_GUI_ACTIVE"] / 8 / secs / 1e9,
+                     c["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / busy, c["SQ_INSTS_MFMA"] / n))
+    for _, k, n, ms, ghz, fr, mi in sorted(rows, reverse=True):
+        if mi > 0:
+            print(f"| `{k}` | {n} | {ms:.4f} | {ghz:.2f} | {100 * fr:.1f}% | {mi:.3g} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +206,18 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of MIB MiB (for scaling HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs of this script and exit")
+    ap.add_argument("--pmc-command", default="", help="the profiled command, quoted in the summary")
+    ap.add_argument("--sq-summary", metavar="SQ_CSV", help="summarise a rocprofv3 --pmc run of SQ counters and exit")
     args = ap.parse_args()
+    if args.sq_summary:
+        sq_summary(args.sq_summary, args.pmc_command, args.config)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.steps, args.copy_calibration or 1024,
+                    args.pmc_command, args.config)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the data-parallel path over several "
               "GPUs is designed but not built; run with --gpus 1.", file=sys.stderr)
