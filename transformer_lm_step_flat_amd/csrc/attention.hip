@@ -45,6 +45,12 @@ __device__ __forceinline__ floatx16 zero16() {
 
 __device__ __forceinline__ int row_of(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Scores are kept in base 2: q (or k) is pre-multiplied by scale * log2(e),
+// so that exp(scale q.k - lse) = 2^(s2 - lse * log2(e)) is one v_exp_f32.
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Load `rows` rows of HD floats (row stride `rs` floats, rows >= nvalid are
 // zero) into registers: thread tid owns float4 number tid + 256*i.
 template <int HD, int ROWS>
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
         floatx4 v = t < T ? *(const floatx4 *)(qb_ptr + (long long)t * rs + h * (HD / 2) + 4 * j4)
                           : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; e++) qf[4 * j4 + e] = v[e] * scale;
+        for (int e = 0; e < 4; e++) qf[4 * j4 + e] = v[e] * (scale * LOG2E);
     }
     floatx16 o[HeadBlocks<HD>::N];
 #pragma unroll
@@ -268,25 +274,32 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
         floatx16 s[2];
         keys_times_frag<HD>(s, Ks, P, qf, l32, h);
         float mx = m;
+        if (k0 + KB - 1 > tq0 || k0 + KB > T) {  // the block crosses the diagonal or the end: mask
 #pragma unroll
-        for (int mb = 0; mb < 2; mb++)
+            for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int u = k0 + 32 * mb + row_of(r, h);
-                const float v = (u > t || u >= T) ? -INFINITY : s[mb][r];
-                s[mb][r] = v;
-                mx = fmaxf(mx, v);
-            }
+                for (int r = 0; r < 16; r++) {
+                    const int u = k0 + 32 * mb + row_of(r, h);
+                    const float v = (u > t || u >= T) ? -INFINITY : s[mb][r];
+                    s[mb][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[mb][r]);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
         // a query that sees no key yet keeps m = -inf; exponentiate against 0 then
         const float mref = mx == -INFINITY ? 0.0f : mx;
-        const float alpha = __expf(m - mref);
+        const float alpha = exp2_fast(m - mref);
         float ps = 0.0f;
 #pragma unroll
         for (int mb = 0; mb < 2; mb++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const float p = __expf(s[mb][r] - mref);
+                const float p = exp2_fast(s[mb][r] - mref);
                 s[mb][r] = p;
                 ps += p;
             }
@@ -300,7 +313,7 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
     __syncthreads();  // the K/V tiles become per-wave transpose space
     float *tr = (wave < 2 ? Ks : Vs) + (wave & 1) * QW * P;
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    const float lse_t = lsum > 0.0f ? m + __logf(lsum) : -INFINITY;
+    const float lse_t = lsum > 0.0f ? (m + __log2f(lsum)) * LN2 : -INFINITY;
     if (nch == 1) {
         store_rows_t<HD>(out + ((long long)b * T + tq0) * C + hd_off, C, T - tq0, o, inv, tr, P, lane);
         if (h == 0 && t < T) lse[(long long)bh * T + t] = lse_t;
@@ -382,13 +395,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
         floatx4 o = ok ? *(const floatx4 *)(ob + (long long)t * C + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            qf[4 * j4 + e] = q[e] * scale;
+            qf[4 * j4 + e] = q[e] * (scale * LOG2E);
             dof[4 * j4 + e] = d[e];
             dsum += d[e] * o[e];
         }
     }
     const float Dt = dsum + __shfl_xor(dsum, 32, WAVE);
-    const float lt = t < T ? lse[(long long)bh * T + t] : 0.0f;
+    const float lt = t < T ? lse[(long long)bh * T + t] * LOG2E : 0.0f;
     if (chunk == 0 && h == 0 && t < T) Dbuf[(long long)bh * T + t] = Dt;
 
     floatx16 dq[HeadBlocks<HD>::N];
@@ -415,11 +428,20 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict_
 #pragma unroll
         for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int u = k0 + 32 * mb + row_of(r, h);
-                const float p = (u > t || u >= T) ? 0.0f : __expf(s[mb][r] - lt);
-                s[mb][r] = p * (dp[mb][r] - Dt);  // ds
-            }
+            for (int r = 0; r < 16; r++) s[mb][r] = exp2_fast(s[mb][r] - lt);  // p
+        if (k0 + KB - 1 > tq0 || k0 + KB > T) {  // the block crosses the diagonal or the end: mask
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int u = k0 + 32 * mb + row_of(r, h);
+                    if (u > t || u >= T) s[mb][r] = 0.0f;
+                }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) s[mb][r] *= dp[mb][r] - Dt;  // ds
         accum_xt_pt_any<HD>(dq, Kt, s, l32, h);
     }
     __syncthreads();
@@ -467,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         floatx4 v = ok ? *(const floatx4 *)(qb_ptr + 2 * C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            kf[4 * j4 + e] = k[e] * scale;
+            kf[4 * j4 + e] = k[e] * (scale * LOG2E);
             vf[4 * j4 + e] = v[e];
         }
     }
@@ -486,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         lq.store_t(Qt, PT, tid);
         lo.store_t(Ot, PT, tid);
         if (tid < TB) {
-            Ls[tid] = t0 + tid < T ? lse[(long long)bh * T + t0 + tid] : 0.0f;
+            Ls[tid] = t0 + tid < T ? lse[(long long)bh * T + t0 + tid] * LOG2E : 0.0f;
             Ds[tid] = t0 + tid < T ? Dbuf[(long long)bh * T + t0 + tid] : 0.0f;
         }
         __syncthreads();
@@ -506,12 +528,22 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                 dp = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[e], vf[4 * j4 + e], dp, 0, 0, 0);
             }
         }
+        if (t0 < u0 + QW - 1 || t0 + TB > T || u0 + QW > T) {  // crosses the diagonal or an end: mask
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int tl = row_of(r, h), tt = t0 + tl;
-            const float p = (tt < u || tt >= T || u >= T) ? 0.0f : __expf(s[r] - Ls[tl]);
-            s[r] = p;                      // p
-            dp[r] = p * (dp[r] - Ds[tl]);  // ds
+            for (int r = 0; r < 16; r++) {
+                const int tl = row_of(r, h), tt = t0 + tl;
+                const float p = (tt < u || tt >= T || u >= T) ? 0.0f : exp2_fast(s[r] - Ls[tl]);
+                s[r] = p;                      // p
+                dp[r] = p * (dp[r] - Ds[tl]);  // ds
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int tl = row_of(r, h);
+                const float p = exp2_fast(s[r] - Ls[tl]);
+                s[r] = p;
+                dp[r] = p * (dp[r] - Ds[tl]);
+            }
         }
         // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
         // the transposed tiles per 4 MFMAs
