@@ -811,7 +811,7 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
         HIPCK(m, linear_fwd(logits, lnf, P + l.poff[0], nullptr, BT, C, l.Vp, EPI_STORE, nullptr, nullptr, s));
     }
     if (targets) {
-        KRUN(m, "crossentropy_kernel", 8.0 * BT * l.Vp, k_crossentropy(logits, A + l.aoff[A_LOSSES], targets, BT, l.V, l.Vp, 1.0f / BT, s));
+        KRUN(m, k_crossentropy_name(l.Vp), 8.0 * BT * l.Vp, k_crossentropy(logits, A + l.aoff[A_LOSSES], targets, BT, l.V, l.Vp, 1.0f / BT, s));
         KRUN(m, "mean_kernel", 4.0 * BT, k_mean(A + l.aoff[A_LOSS], A + l.aoff[A_LOSSES], BT, s));
         m->have_targets = true;
     }

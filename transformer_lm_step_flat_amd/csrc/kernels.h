@@ -46,6 +46,8 @@ hipError_t k_attn_softmax_backward(float *dp, const float *att, long long nrows,
 // (0 in the padded columns).
 hipError_t k_crossentropy(float *logits, float *losses, const int32_t *tgt, int BT, int V, int Vp, float dscale,
                           hipStream_t s);
+// Name of the kernel k_crossentropy launches for this padded vocabulary.
+const char *k_crossentropy_name(int Vp);
 // loss[0] = sum(losses) / n  (fixed order)
 hipError_t k_mean(float *loss, const float *losses, int n, hipStream_t s);
 

@@ -262,15 +262,29 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(float *dst, const flo
 
 // dst (n floats) and dst2 (n2 floats) += the column sums of partial rows of
 // n + n2 floats (fixed order): used for the [dw | db] partials of LayerNorm.
+// sum of src[p * ld] over p = p0, p0 + 16, ... < P, added in that order; the
+// loads are issued eight at a time so that their latencies overlap.
+__device__ __forceinline__ floatx4 sum_rows_strided(const floatx4 *src, int p0, int P, size_t ld) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    int p = p0;
+    for (; p + 16 * 7 < P; p += 16 * 8) {
+        floatx4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = src[(size_t)(p + 16 * u) * ld];
+#pragma unroll
+        for (int u = 0; u < 8; u++) acc += v[u];
+    }
+    for (; p < P; p += 16) acc += src[(size_t)p * ld];
+    return acc;
+}
+
 __global__ __launch_bounds__(256) void sum_partials_split_kernel(float *dst, float *dst2, const float *src, int P,
                                                                  int n4, int n24) {
     __shared__ floatx4 lds[16][16];
     const int c = threadIdx.x & 15, pl = threadIdx.x >> 4;
     const int i = blockIdx.x * 16 + c, ld4 = n4 + n24;
     const floatx4 *s4 = (const floatx4 *)src;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (i < ld4)
-        for (int p = pl; p < P; p += 16) acc += s4[(size_t)p * ld4 + i];
+    const floatx4 acc = i < ld4 ? sum_rows_strided(s4 + i, pl, P, (size_t)ld4) : floatx4{0.f, 0.f, 0.f, 0.f};
     lds[pl][c] = acc;
     __syncthreads();
     if (pl == 0 && i < ld4) {
@@ -290,9 +304,7 @@ __global__ __launch_bounds__(256) void sum_partials_wide_kernel(float *dst, cons
     const int c = threadIdx.x & 15, pl = threadIdx.x >> 4;
     const size_t i = (size_t)blockIdx.x * 16 + c;
     const floatx4 *s4 = (const floatx4 *)src;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (i < n4)
-        for (int p = pl; p < P; p += 16) acc += s4[(size_t)p * ld4 + i];
+    const floatx4 acc = i < n4 ? sum_rows_strided(s4 + i, pl, P, ld4) : floatx4{0.f, 0.f, 0.f, 0.f};
     lds[pl][c] = acc;
     __syncthreads();
     if (pl == 0 && i < n4) {
@@ -428,6 +440,79 @@ __global__ __launch_bounds__(256) void crossentropy_kernel(float *logits, float 
             o[e] = v < V ? (__expf(x[e] - lse) - (v == y ? 1.0f : 0.0f)) * dscale : 0.0f;
         }
         ((floatx4 *)z)[v4] = o;
+    }
+}
+
+// The same with the whole row held in registers, for Vp <= 4 * 1024 * NV4:
+// one 1024-thread workgroup per row, thread i holding float4s i + 1024 j.
+// The row is read once and written once (no second read pass).  Max and sum
+// are reduced over the block in a fixed order.
+template <int NV4>
+__global__ __launch_bounds__(1024) void crossentropy_reg_kernel(float *logits, float *losses, const int32_t *tgt,
+                                                                int V, int Vp, float dscale) {
+    __shared__ float red[16];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    floatx4 *z = (floatx4 *)(logits + (long long)row * Vp);
+    const int n4 = Vp / 4;
+    const int y = clamp_id(tgt[row], V);
+    floatx4 x[NV4];
+#pragma unroll
+    for (int j = 0; j < NV4; j++) {
+        const int i = tid + 1024 * j;
+        x[j] = i < n4 ? z[i] : floatx4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    // the thread holding the target's logit keeps it (other threads overwrite
+    // the row in memory before that thread writes the loss)
+    const int yown = (y >> 2) % 1024, yj = (y >> 2) / 1024, ye = y & 3;
+    float zy = 0.0f;
+    if (tid == yown) {
+#pragma unroll
+        for (int j = 0; j < NV4; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) zy = (j == yj && e == ye) ? x[j][e] : zy;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NV4; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int v = 4 * (tid + 1024 * j) + e;
+            if (v >= V) x[j][e] = -INFINITY;  // padded columns take no part
+            m = fmaxf(m, x[j][e]);
+        }
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < 16; w++) m = fmaxf(m, red[w]);
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV4; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) sum += __expf(x[j][e] - m);
+    sum = wave_sum(sum);
+    __syncthreads();  // every wave has read red[] for the max
+    if (lane == 0) red[wave] = sum;
+    __syncthreads();
+    sum = red[0];
+#pragma unroll
+    for (int w = 1; w < 16; w++) sum += red[w];
+    const float lse = m + __logf(sum);
+    if (tid == yown) losses[row] = lse - zy;
+#pragma unroll
+    for (int j = 0; j < NV4; j++) {
+        const int i = tid + 1024 * j;
+        if (i < n4) {
+            floatx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int v = 4 * i + e;
+                o[e] = (__expf(x[j][e] - lse) - (v == y ? 1.0f : 0.0f)) * dscale;  // 0 for padded columns
+            }
+            z[i] = o;
+        }
     }
 }
 
@@ -615,8 +700,24 @@ hipError_t k_attn_softmax_backward(float *dp, const float *att, long long nrows,
 hipError_t k_crossentropy(float *logits, float *losses, const int32_t *tgt, int BT, int V, int Vp, float dscale,
                           hipStream_t s) {
     if (Vp % 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(crossentropy_kernel, dim3(BT), dim3(256), 0, s, logits, losses, tgt, V, Vp, dscale);
+    const int n4 = Vp / 4;
+    if (n4 <= 1024)
+        hipLaunchKernelGGL(crossentropy_reg_kernel<1>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale);
+    else if (n4 <= 4 * 1024)
+        hipLaunchKernelGGL(crossentropy_reg_kernel<4>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale);
+    else if (n4 <= 13 * 1024)
+        hipLaunchKernelGGL(crossentropy_reg_kernel<13>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale);
+    else
+        hipLaunchKernelGGL(crossentropy_kernel, dim3(BT), dim3(256), 0, s, logits, losses, tgt, V, Vp, dscale);
     return hipGetLastError();
+}
+
+const char *k_crossentropy_name(int Vp) {
+    const int n4 = Vp / 4;
+    if (n4 <= 1024) return "crossentropy_reg_kernel<1>";
+    if (n4 <= 4 * 1024) return "crossentropy_reg_kernel<4>";
+    if (n4 <= 13 * 1024) return "crossentropy_reg_kernel<13>";
+    return "crossentropy_kernel";
 }
 
 hipError_t k_mean(float *loss, const float *losses, int n, hipStream_t s) {
