@@ -57,12 +57,14 @@ gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const floa
                                      int T, int C, int NH, float *work, void *stream);
 
 /* The same attention fused (the path gpt2_forward / gpt2_backward take when
- * the head dimension is 16, 32 or 64): no T x T matrix is kept.  The forward
- * writes atty and lse[B][NH][T] (log-sum-exp of each query's scaled scores);
- * the backward recomputes the probabilities from them and overwrites dqkv.
- * Rows longer than one work chunk are split over workgroups and merged in a
- * fixed order through `work` (gpt2k_flash_attention_work floats; the same
- * size serves both calls).  GPT2_EINVAL for other head dimensions. */
+ * the head dimension is 16, 32 or 64): the forward keeps no T x T matrix; it
+ * writes atty and lse[B][NH][T] (log-sum-exp of each query's scaled scores).
+ * The backward recomputes the probabilities from them, computes dk and dv,
+ * stores ds = p (dp - D) for every causal (t, u) in `work`, and finishes dq
+ * as a causal GEMM over ds; it overwrites dqkv.  Rows longer than one work
+ * chunk are split over workgroups and merged in a fixed order through `work`
+ * (gpt2k_flash_attention_work floats, B*NH*T*T of them for ds; the same size
+ * serves both calls).  GPT2_EINVAL for other head dimensions. */
 size_t gpt2k_flash_attention_work(int B, int T, int C, int NH);
 gpt2_status gpt2k_flash_attention_forward(float *atty, float *lse, const float *qkv, int B, int T, int C, int NH,
                                           float *work, void *stream);

@@ -14,12 +14,15 @@ size_t flash_attention_work(int B, int T, int C, int NH);
 hipError_t flash_attention_forward(float *out, float *lse, float *ws, const float *qkv, int B, int T, int C, int NH,
                                    hipStream_t s);
 
-// Backward, in two calls: first dq (the q block of dqkv, overwritten) and
-// Dbuf[B][NH][T] = rowwise dout . out; then dk and dv (the k and v blocks of
-// dqkv, overwritten), which reads Dbuf.
-hipError_t flash_attention_backward_dq(float *dqkv, float *Dbuf, float *ws, const float *dout, const float *qkv,
-                                       const float *out, const float *lse, int B, int T, int C, int NH,
-                                       hipStream_t s);
-hipError_t flash_attention_backward_dkdv(float *dqkv, float *ws, const float *Dbuf, const float *dout,
-                                         const float *qkv, const float *lse, int B, int T, int C, int NH,
+// Backward, first part: Dbuf[B][NH][T] = rowwise dout . out; dk and dv (the
+// k and v blocks of dqkv, overwritten); and ds = p (dp - D) of every causal
+// (t, u) into the workspace (flash_attention_ds), zero above the diagonal
+// within each diagonal 128 x 128 tile.  The caller finishes with the
+// product dq = ds K / sqrt(hd) (a causal GEMM that reads ds up to the end of
+// each 128-row tile).
+hipError_t flash_attention_backward_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dout, const float *qkv,
+                                         const float *out, const float *lse, int B, int T, int C, int NH,
                                          hipStream_t s);
+
+// The [B][NH][T][T] ds matrices inside the workspace.
+const float *flash_attention_ds(const float *ws);

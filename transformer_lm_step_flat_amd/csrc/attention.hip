@@ -15,13 +15,15 @@
 // MFMA layout (v_mfma_f32_32x32x2_f32, lane l, half h = l / 32): the A
 // operand is A[m = l % 32][k = slot h], B is B[k = slot h][n = l % 32], and
 // the 32x32 result holds column l % 32, rows 8(r/4) + 4h + r%4 in register r.
-// The forward and the dq kernel compute s^T = K Q^T so that a lane owns one
-// query (a result column) and 32 keys (its rows): the softmax statistics are
-// then per lane (plus its partner lane l ^ 32), and the probabilities sit
-// exactly where o^T += V^T p^T needs them as its B operand.  The dk/dv kernel
-// computes s = Q K^T so that a lane owns one key, and p / ds are in place as
-// the A operand of dv += p^T dO and dk += ds^T Q.  Reductions over the head
-// dimension use the k-split trick of the GEMM kernel: lane half h walks
+// The forward computes s^T = K Q^T so that a lane owns one query (a result
+// column) and 32 keys (its rows): the softmax statistics are then per lane
+// (plus its partner lane l ^ 32), and the probabilities sit exactly where
+// o^T += V^T p^T needs them as its B operand.  The backward kernel computes
+// s = Q K^T so that a lane owns one key, and p / ds are in place as the A
+// operand of dv += p^T dO and dk += ds^T Q; it also stores ds (coalesced: a
+// register holds one query's 32 consecutive keys across the lanes), and dq =
+// scale ds K is then a causal GEMM over the stored ds.  Reductions over the
+// head dimension use the k-split trick of the GEMM kernel: lane half h walks
 // d = h*HD/2 + j.
 //
 // Every output element is written by exactly one lane, with sums in a fixed
@@ -33,7 +35,7 @@ namespace {
 
 constexpr int QW = 32;     // queries (or keys) per wavefront
 constexpr int NWAVE = 4;   // wavefronts per workgroup
-constexpr int KB = 64;     // keys per block in the forward and dq kernels
+constexpr int KB = 64;     // keys per block in the forward kernel
 constexpr int TB = 32;     // queries per block in the dk/dv kernel
 
 __device__ __forceinline__ floatx16 zero16() {
@@ -110,28 +112,6 @@ __device__ __forceinline__ void keys_times_frag(floatx16 (&s)[2], const float *X
     }
 }
 
-// Both products of the dq kernel at once (four interleaved chains):
-// s^T = K frag_q, dp^T = V frag_do.
-template <int HD>
-__device__ __forceinline__ void keys_times_two_frags(floatx16 (&s)[2], floatx16 (&dp)[2], const float *K,
-                                                     const float *V, int pitch, const float *fq, const float *fdo,
-                                                     int l32, int h) {
-    s[0] = s[1] = dp[0] = dp[1] = zero16();
-#pragma unroll
-    for (int j4 = 0; j4 < HD / 8; j4++) {
-        const int c = h * (HD / 2) + 4 * j4;
-        floatx4 k0 = *(const floatx4 *)&K[l32 * pitch + c], k1 = *(const floatx4 *)&K[(32 + l32) * pitch + c];
-        floatx4 v0 = *(const floatx4 *)&V[l32 * pitch + c], v1 = *(const floatx4 *)&V[(32 + l32) * pitch + c];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(k0[e], fq[4 * j4 + e], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(k1[e], fq[4 * j4 + e], s[1], 0, 0, 0);
-            dp[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0[e], fdo[4 * j4 + e], dp[0], 0, 0, 0);
-            dp[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1[e], fdo[4 * j4 + e], dp[1], 0, 0, 0);
-        }
-    }
-}
-
 // HD = 16 has a single half-filled 32-row block for the head dimension.
 template <int HD>
 struct HeadBlocks {
@@ -190,7 +170,7 @@ __device__ __forceinline__ void store_rows_t(float *dst, long long rs, int nrows
 // ------------------------------------------------------------------ work split
 //
 // Long causal rows are split so that no workgroup walks more than a few
-// blocks in sequence.  Forward and dq: a workgroup takes 128 queries and one
+// blocks in sequence.  Forward: a workgroup takes 128 queries and one
 // chunk of at most 256 of the keys they need; dk/dv: 128 keys and one chunk of
 // at most 256 of the queries that see them.  A block whose range fits in one
 // chunk writes its result directly; otherwise each chunk writes a partial
@@ -198,7 +178,7 @@ __device__ __forceinline__ void store_rows_t(float *dst, long long rs, int nrows
 // combine kernel merges the chunks in order.
 
 constexpr int QBLK = QW * NWAVE;  // rows of a workgroup: 128
-constexpr int KCH = 256;          // keys per chunk (forward, dq)
+constexpr int KCH = 256;          // keys per chunk (forward)
 constexpr int QCH = 256;          // queries per chunk (dk/dv)
 
 __host__ __device__ inline int q_items(int qb, int T) {
@@ -358,106 +338,11 @@ __global__ __launch_bounds__(256) void flash_fwd_merge_kernel(float *__restrict_
     if (d4 == 0) lse[(long long)bh * T + t] = L;
 }
 
-// ------------------------------------------------------------------ backward: dq and D
-
-template <int HD>
-__global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(float *__restrict__ dqkv, float *__restrict__ Dbuf,
-                                                              float *__restrict__ ws,
-                                                              const float *__restrict__ dout,
-                                                              const float *__restrict__ qkv,
-                                                              const float *__restrict__ out,
-                                                              const float *__restrict__ lse, int T, int C, int NH,
-                                                              int items, float scale) {
-    constexpr int P = HD + 4;
-    constexpr int PT = KB + 4;
-    __shared__ __attribute__((aligned(16))) float Ks[KB * P];
-    __shared__ __attribute__((aligned(16))) float Vs[KB * P];
-    __shared__ __attribute__((aligned(16))) float Kt[HD * PT];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
-    const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
-    int qb, chunk, first;
-    decode_item<false>(blockIdx.x, T, qb, chunk, first);
-    const int nch = q_items(qb, T);
-    const int q0 = qb * QBLK;
-    const int tq0 = q0 + wave * QW, t = tq0 + l32;
-    const long long rs = 3LL * C;
-    const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
-    const float *dob = dout + (long long)b * T * C + hd_off;
-    const float *ob = out + (long long)b * T * C + hd_off;
-
-    float qf[HD / 2], dof[HD / 2];
-    float dsum = 0.0f;
-#pragma unroll
-    for (int j4 = 0; j4 < HD / 8; j4++) {
-        const bool ok = t < T;
-        floatx4 q = ok ? *(const floatx4 *)(qb_ptr + (long long)t * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-        floatx4 d = ok ? *(const floatx4 *)(dob + (long long)t * C + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-        floatx4 o = ok ? *(const floatx4 *)(ob + (long long)t * C + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            qf[4 * j4 + e] = q[e] * (scale * LOG2E);
-            dof[4 * j4 + e] = d[e];
-            dsum += d[e] * o[e];
-        }
-    }
-    const float Dt = dsum + __shfl_xor(dsum, 32, WAVE);
-    const float lt = t < T ? lse[(long long)bh * T + t] * LOG2E : 0.0f;
-    if (chunk == 0 && h == 0 && t < T) Dbuf[(long long)bh * T + t] = Dt;
-
-    floatx16 dq[HeadBlocks<HD>::N];
-#pragma unroll
-    for (int md = 0; md < HeadBlocks<HD>::N; md++) dq[md] = zero16();
-
-    const int kc0 = chunk * KCH, kc1 = min(min(T, q0 + QBLK), kc0 + KCH);
-    TileLoader<HD, KB> lk, lv;
-    lk.load(qb_ptr + C, rs, kc0, T, tid);
-    lv.load(qb_ptr + 2 * C, rs, kc0, T, tid);
-    for (int k0 = kc0; k0 < kc1; k0 += KB) {
-        __syncthreads();
-        lk.store(Ks, P, tid);
-        lk.store_t(Kt, PT, tid);
-        lv.store(Vs, P, tid);
-        __syncthreads();
-        if (k0 + KB < kc1) {
-            lk.load(qb_ptr + C, rs, k0 + KB, T, tid);
-            lv.load(qb_ptr + 2 * C, rs, k0 + KB, T, tid);
-        }
-        if (k0 > tq0 + QW - 1) continue;
-        floatx16 s[2], dp[2];
-        keys_times_two_frags<HD>(s, dp, Ks, Vs, P, qf, dof, l32, h);
-#pragma unroll
-        for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) s[mb][r] = exp2_fast(s[mb][r] - lt);  // p
-        if (k0 + KB - 1 > tq0 || k0 + KB > T) {  // the block crosses the diagonal or the end: mask
-#pragma unroll
-            for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int u = k0 + 32 * mb + row_of(r, h);
-                    if (u > t || u >= T) s[mb][r] = 0.0f;
-                }
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) s[mb][r] *= dp[mb][r] - Dt;  // ds
-        accum_xt_pt_any<HD>(dq, Kt, s, l32, h);
-    }
-    __syncthreads();
-    float *tr = (wave < 2 ? Ks : Vs) + (wave & 1) * QW * P;
-    if (nch == 1) {
-        store_rows_t<HD>(dqkv + ((long long)b * T + tq0) * rs + hd_off, rs, T - tq0, dq, scale, tr, P, lane);
-    } else {
-        const long long item = (long long)bh * items + first + chunk;
-        store_rows_t<HD>(ws + (item * QBLK + wave * QW) * HD, HD, QW, dq, scale, tr, P, lane);
-    }
-}
-
 // ------------------------------------------------------------------ backward: dk and dv
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv, float *__restrict__ ws,
+                                                                float *__restrict__ dsout,
                                                                 const float *__restrict__ dout,
                                                                 const float *__restrict__ qkv,
                                                                 const float *__restrict__ lse,
@@ -516,7 +401,17 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             lq.load(qb_ptr, rs, t0 + TB, T, tid);
             lo.load(dob, C, t0 + TB, T, tid);
         }
-        if (t0 + TB - 1 < u0) continue;  // every query of the block precedes this wave's keys
+        if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
+            if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
+                float *dsb = dsout + (long long)bh * T * T;
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int tt = t0 + row_of(r, h);
+                    if (tt < T && u < T) dsb[(long long)tt * T + u] = 0.0f;
+                }
+            }
+            continue;
+        }
         floatx16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int j4 = 0; j4 < HD / 8; j4++) {
@@ -543,6 +438,14 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                 const float p = exp2_fast(s[r] - Ls[tl]);
                 s[r] = p;
                 dp[r] = p * (dp[r] - Ds[tl]);
+            }
+        }
+        {  // ds[t][u] for the dq product (a row of 32 keys per register: coalesced)
+            float *dsb = dsout + (long long)bh * T * T;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int tt = t0 + row_of(r, h);
+                if (tt < T && u < T) dsb[(long long)tt * T + u] = dp[r];
             }
         }
         // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
@@ -589,9 +492,31 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
     }
 }
 
-// Sum the chunk partials of dq (KEYS = false: rows are queries, one block
-// per 128 queries) or of dk and dv (KEYS = true) into dqkv, chunks in order.
-template <int HD, bool KEYS>
+// D[bh][t] = dO_t . O_t over the head's HD dims, one thread per (b, t, head):
+// consecutive threads take consecutive heads of a row.
+template <int HD>
+__global__ __launch_bounds__(256) void flash_bwd_D_kernel(float *__restrict__ Dbuf, const float *__restrict__ dout,
+                                                          const float *__restrict__ out, int T, int C, int NH,
+                                                          long long rows) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * NH) return;
+    const long long bt = i / NH;
+    const int hh = (int)(i % NH);
+    const floatx4 *a = (const floatx4 *)(dout + bt * C + hh * HD);
+    const floatx4 *o = (const floatx4 *)(out + bt * C + hh * HD);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < HD / 4; j++) {
+        const floatx4 x = a[j], y = o[j];
+        acc += (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
+    }
+    const long long b = bt / T, t = bt % T;
+    Dbuf[(b * NH + hh) * T + t] = acc;
+}
+
+// Sum the chunk partials of dk and dv into dqkv, chunks in order.  One
+// thread per (key row, 4 head dims) of the key blocks that were split.
+template <int HD>
 __global__ __launch_bounds__(256) void flash_bwd_sum_kernel(float *__restrict__ dqkv, const float *__restrict__ ws,
                                                             int T, int C, int NH, int BNH, int items) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -599,29 +524,26 @@ __global__ __launch_bounds__(256) void flash_bwd_sum_kernel(float *__restrict__ 
     const long long r = i / (HD / 4);
     const int t = (int)(r % T), bh = (int)(r / T);
     if (bh >= BNH) return;
-    const int blk = t / QBLK, nch = KEYS ? k_items(blk, T) : q_items(blk, T);
+    const int blk = t / QBLK, nch = k_items(blk, T);
     if (nch == 1) return;  // written directly by the chunk kernel
     int first = 0;
-    for (int q = 0; q < blk; q++) first += KEYS ? k_items(q, T) : q_items(q, T);
+    for (int q = 0; q < blk; q++) first += k_items(q, T);
     const long long base = (long long)bh * items + first;
     const int row = t % QBLK;
     const long long rs = 3LL * C;
     const int b = bh / NH, hd_off = (bh % NH) * HD;
-    if (!KEYS) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < nch; c++) acc += *(const floatx4 *)(ws + ((base + c) * QBLK + row) * HD + 4 * d4);
-        *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + hd_off + 4 * d4) = acc;
-    } else {
-        floatx4 ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < nch; c++) {
-            const float *p = ws + (base + c) * 2 * QBLK * HD + (long long)row * HD + 4 * d4;
-            ak += *(const floatx4 *)p;
-            av += *(const floatx4 *)(p + QBLK * HD);
-        }
-        *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + C + hd_off + 4 * d4) = ak;
-        *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + 2 * C + hd_off + 4 * d4) = av;
+    floatx4 ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nch; c++) {
+        const float *p = ws + (base + c) * 2 * QBLK * HD + (long long)row * HD + 4 * d4;
+        ak += *(const floatx4 *)p;
+        av += *(const floatx4 *)(p + QBLK * HD);
     }
+    *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + C + hd_off + 4 * d4) = ak;
+    *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + 2 * C + hd_off + 4 * d4) = av;
 }
+
+// floats of the ds matrices at the start of the backward workspace (256-byte aligned)
+size_t ds_floats(int B, int T, int NH) { return ((size_t)B * NH * T * T + 63) / 64 * 64; }
 
 int total_items(bool keys, int T) {
     int n = 0;
@@ -645,30 +567,22 @@ hipError_t launch_fwd(float *out, float *lse, float *ws, const float *qkv, int B
 }
 
 template <int HD>
-hipError_t launch_bwd_dq(float *dqkv, float *Dbuf, float *ws, const float *dout, const float *qkv, const float *out,
-                         const float *lse, int B, int T, int C, int NH, hipStream_t s) {
-    const int items = total_items(false, T);
-    hipLaunchKernelGGL(flash_bwd_dq_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, dqkv, Dbuf, ws, dout, qkv, out,
-                       lse, T, C, NH, items, 1.0f / sqrtf((float)HD));
+hipError_t launch_bwd_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dout, const float *qkv,
+                           const float *out, const float *lse, int B, int T, int C, int NH, hipStream_t s) {
+    const long long rows = (long long)B * T;
+    hipLaunchKernelGGL(flash_bwd_D_kernel<HD>, dim3((unsigned)((rows * NH + 255) / 256)), dim3(256), 0, s, Dbuf, dout,
+                       out, T, C, NH, rows);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || items == (T + QBLK - 1) / QBLK) return e;
-    const long long n = (long long)B * NH * T * (HD / 4);
-    hipLaunchKernelGGL((flash_bwd_sum_kernel<HD, false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dqkv,
-                       (const float *)ws, T, C, NH, B * NH, items);
-    return hipGetLastError();
-}
-
-template <int HD>
-hipError_t launch_bwd_dkdv(float *dqkv, float *ws, const float *Dbuf, const float *dout, const float *qkv,
-                           const float *lse, int B, int T, int C, int NH, hipStream_t s) {
+    if (e != hipSuccess) return e;
     const int items = total_items(true, T);
-    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, dqkv, ws, dout, qkv, lse,
-                       Dbuf, T, C, NH, items, 1.0f / sqrtf((float)HD));
-    hipError_t e = hipGetLastError();
+    float *ds = ws, *kvws = ws + ds_floats(B, T, NH);
+    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, dqkv, kvws, ds, dout, qkv,
+                       lse, (const float *)Dbuf, T, C, NH, items, 1.0f / sqrtf((float)HD));
+    e = hipGetLastError();
     if (e != hipSuccess || items == (T + QBLK - 1) / QBLK) return e;
     const long long n = (long long)B * NH * T * (HD / 4);
-    hipLaunchKernelGGL((flash_bwd_sum_kernel<HD, true>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dqkv,
-                       (const float *)ws, T, C, NH, B * NH, items);
+    hipLaunchKernelGGL((flash_bwd_sum_kernel<HD>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dqkv,
+                       (const float *)kvws, T, C, NH, B * NH, items);
     return hipGetLastError();
 }
 
@@ -679,9 +593,11 @@ bool flash_attention_supported(int hd) { return hd == 16 || hd == 32 || hd == 64
 size_t flash_attention_work(int B, int T, int C, int NH) {
     const int hd = C / NH;
     const size_t fq = (size_t)B * NH * total_items(false, T) * QBLK * (hd + 1);
-    const size_t kv = (size_t)B * NH * total_items(true, T) * QBLK * 2 * hd;
+    const size_t kv = ds_floats(B, T, NH) + (size_t)B * NH * total_items(true, T) * QBLK * 2 * hd;
     return fq > kv ? fq : kv;
 }
+
+const float *flash_attention_ds(const float *ws) { return ws; }
 
 hipError_t flash_attention_forward(float *out, float *lse, float *ws, const float *qkv, int B, int T, int C, int NH,
                                    hipStream_t s) {
@@ -693,24 +609,13 @@ hipError_t flash_attention_forward(float *out, float *lse, float *ws, const floa
     return hipErrorInvalidValue;
 }
 
-hipError_t flash_attention_backward_dq(float *dqkv, float *Dbuf, float *ws, const float *dout, const float *qkv,
-                                       const float *out, const float *lse, int B, int T, int C, int NH,
-                                       hipStream_t s) {
-    switch (C / NH) {
-        case 16: return launch_bwd_dq<16>(dqkv, Dbuf, ws, dout, qkv, out, lse, B, T, C, NH, s);
-        case 32: return launch_bwd_dq<32>(dqkv, Dbuf, ws, dout, qkv, out, lse, B, T, C, NH, s);
-        case 64: return launch_bwd_dq<64>(dqkv, Dbuf, ws, dout, qkv, out, lse, B, T, C, NH, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-hipError_t flash_attention_backward_dkdv(float *dqkv, float *ws, const float *Dbuf, const float *dout,
-                                         const float *qkv, const float *lse, int B, int T, int C, int NH,
+hipError_t flash_attention_backward_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dout, const float *qkv,
+                                         const float *out, const float *lse, int B, int T, int C, int NH,
                                          hipStream_t s) {
     switch (C / NH) {
-        case 16: return launch_bwd_dkdv<16>(dqkv, ws, Dbuf, dout, qkv, lse, B, T, C, NH, s);
-        case 32: return launch_bwd_dkdv<32>(dqkv, ws, Dbuf, dout, qkv, lse, B, T, C, NH, s);
-        case 64: return launch_bwd_dkdv<64>(dqkv, ws, Dbuf, dout, qkv, lse, B, T, C, NH, s);
+        case 16: return launch_bwd_dkdv<16>(dqkv, ws, Dbuf, dout, qkv, out, lse, B, T, C, NH, s);
+        case 32: return launch_bwd_dkdv<32>(dqkv, ws, Dbuf, dout, qkv, out, lse, B, T, C, NH, s);
+        case 64: return launch_bwd_dkdv<64>(dqkv, ws, Dbuf, dout, qkv, out, lse, B, T, C, NH, s);
     }
     return hipErrorInvalidValue;
 }

@@ -68,10 +68,10 @@ struct TileLds {
     static constexpr int B = BKC ? BN * KP : GEMM_BK * BN;
 };
 
-// One BM x BN output tile: number `t` (after the XCD remap) of the tile
-// grid, batch / split index z, operand tiles staged in As / Bs.
+// One BM x BN output tile (row tile tm, column tile tn), batch / split
+// index z, operand tiles staged in As / Bs.
 template <int BM, int BN, bool AK, bool BKC>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &p, int t, int z, float *__restrict__ As,
+__device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int z, float *__restrict__ As,
                                           float *__restrict__ Bs) {
     constexpr int BK = GEMM_BK;
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -86,8 +86,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int t, int z, float
     const int wm = wave & 1, wn = wave >> 1;
     const int l32 = lane & 31, h = lane >> 5;
 
-    int tm, tn;
-    group_order(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int s = z % p.ksplit, zb = z / p.ksplit;
     const int zo = zb / p.nbi, zi = zb % p.nbi;
     const float *__restrict__ A = p.A + zo * p.sAo + zi * p.sAi;
@@ -265,7 +263,25 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
     using L = TileLds<BM, BN, AK, BKC>;
     __shared__ __attribute__((aligned(16))) float As[L::A];
     __shared__ __attribute__((aligned(16))) float Bs[L::B];
-    gemm_tile<BM, BN, AK, BKC>(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), blockIdx.z, As, Bs);
+    int tm, tn;
+    group_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    gemm_tile<BM, BN, AK, BKC>(p, tm, tn, blockIdx.z, As, Bs);
+}
+
+// Causal products whose K range grows (KEND) or shrinks (KSTART) with the row
+// tile: a workgroup takes row tiles i and tiles_m - 1 - i of one column, whose
+// K ranges add up to the same length for every workgroup.
+template <int BM, int BN, bool AK, bool BKC>
+__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_fold_kernel(GemmArgs p) {
+    using L = TileLds<BM, BN, AK, BKC>;
+    __shared__ __attribute__((aligned(16))) float As[L::A];
+    __shared__ __attribute__((aligned(16))) float Bs[L::B];
+    const int half = (p.tiles_m + 1) / 2;
+    const int t = xcd_remap(blockIdx.x, half * p.tiles_n);
+    const int tn = t / half, i = t % half, j = p.tiles_m - 1 - i;
+    const int npass = i == j ? 1 : 2;
+    for (int pass = 0; pass < npass; pass++)
+        gemm_tile<BM, BN, AK, BKC>(p, pass == 0 ? j : i, tn, blockIdx.z, As, Bs);
 }
 
 // Two independent products in one grid of w = w1 + w2 workgroups (w1 of
@@ -286,11 +302,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_pair_kernel(GemmArgs p1,
     const int s1 = x * q1 + min(x, m1);              // their first index
     if (j < r1) {
         const int g = s1 + j, nt = p1.tiles_m * p1.tiles_n;
-        gemm_tile<BM, BN, AK1, BKC1>(p1, g % nt, g / nt, As, Bs);
+        int tm, tn;
+        group_order(g % nt, p1.tiles_m, p1.tiles_n, p1.group_m, tm, tn);
+        gemm_tile<BM, BN, AK1, BKC1>(p1, tm, tn, g / nt, As, Bs);
     } else {
         const int s2 = x * (w / X) + min(x, w % X) - s1;  // workgroups of XCDs before x, less problem 1's
         const int g = s2 + j - r1, nt = p2.tiles_m * p2.tiles_n;
-        gemm_tile<BM, BN, AK2, BKC2>(p2, g % nt, g / nt, As, Bs);
+        int tm, tn;
+        group_order(g % nt, p2.tiles_m, p2.tiles_n, p2.group_m, tm, tn);
+        gemm_tile<BM, BN, AK2, BKC2>(p2, tm, tn, g / nt, As, Bs);
     }
 }
 
@@ -307,6 +327,16 @@ hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream
     set_tiles<BM, BN>(d, a);
     long long nb = (long long)d.nbo * d.nbi * d.ksplit;
     if (nb > 65535) return hipErrorInvalidValue;
+    if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && a.tiles_m > 1) {
+        dim3 g((a.tiles_m + 1) / 2 * a.tiles_n, 1, (unsigned)nb);
+        if (d.a_kcontig && !d.b_kcontig)
+            hipLaunchKernelGGL((gemm_fold_kernel<BM, BN, true, false>), g, dim3(GEMM_THREADS), 0, stream, a);
+        else if (!d.a_kcontig && !d.b_kcontig)
+            hipLaunchKernelGGL((gemm_fold_kernel<BM, BN, false, false>), g, dim3(GEMM_THREADS), 0, stream, a);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     dim3 grid(a.tiles_m * a.tiles_n, 1, (unsigned)nb);
     if (d.a_kcontig && d.b_kcontig)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true>), grid, dim3(GEMM_THREADS), 0, stream, a);

@@ -436,18 +436,24 @@ const char *gemm_name(const GemmDesc &d) {
         {"gemm_kernel<128, 128, true, true>", "gemm_kernel<128, 128, true, false>", "gemm_kernel<128, 128, false, false>"},
         {"gemm_kernel<128, 64, true, true>", "gemm_kernel<128, 64, true, false>", "gemm_kernel<128, 64, false, false>"},
         {"gemm_kernel<64, 64, true, true>", "gemm_kernel<64, 64, true, false>", "gemm_kernel<64, 64, false, false>"}};
+    static const char *fold_names[3][3] = {
+        {"", "gemm_fold_kernel<128, 128, true, false>", "gemm_fold_kernel<128, 128, false, false>"},
+        {"", "gemm_fold_kernel<128, 64, true, false>", "gemm_fold_kernel<128, 64, false, false>"},
+        {"", "gemm_fold_kernel<64, 64, true, false>", "gemm_fold_kernel<64, 64, false, false>"}};
+    static const int bm[3] = {128, 128, 64};
     int t = d.tile >= 1 && d.tile <= 3 ? d.tile - 1 : 0;
     int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
+    // causal products with a growing or shrinking K range run with folded row tiles
+    if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];
     return names[t][l];
 }
 
 // "kernel<hd>" as a kernel-trace profiler shows the fused attention kernels
 // (static strings: profile records keep the pointer).
-enum { FL_FWD = 0, FL_DQ = 1, FL_DKDV = 2 };
+enum { FL_FWD = 0, FL_DKDV = 1 };
 const char *flash_name(int which, int hd) {
-    static const char *names[3][3] = {
+    static const char *names[2][3] = {
         {"flash_fwd_kernel<16>", "flash_fwd_kernel<32>", "flash_fwd_kernel<64>"},
-        {"flash_bwd_dq_kernel<16>", "flash_bwd_dq_kernel<32>", "flash_bwd_dq_kernel<64>"},
         {"flash_bwd_dkdv_kernel<16>", "flash_bwd_dkdv_kernel<32>", "flash_bwd_dkdv_kernel<64>"}};
     return names[which][hd == 16 ? 0 : (hd == 32 ? 1 : 2)];
 }
@@ -661,6 +667,30 @@ hipError_t attention_bwd(float *dqkv, float *dscore, const float *datty, const f
     v.B = datty; v.ldb = C; v.sBo = (long long)T * C; v.sBi = hd;
     v.C = dqkv + 2 * C;
     return gemm_run(v, s, "attn_dv");
+}
+
+// Fused attention backward: D, dk, dv and ds in the attention kernels, then
+// dq = scale ds K as a causal GEMM over the ds matrices.
+hipError_t flash_backward(float *dqkv, float *Dbuf, float *ws, const float *datty, const float *qkv,
+                          const float *atty, const float *lse, int B, int T, int C, int NH, hipStream_t s) {
+    const int hd = C / NH;
+    const double tri = 0.5 * T * (T + 1.0) * B * NH;
+    const size_t BTC = (size_t)B * T * C;
+    // counted: dp, dv, dk (the recomputed s is not)
+    hipError_t e = timed(flash_name(FL_DKDV, hd), 6.0 * tri * hd, 24.0 * BTC + 4.0 * tri, [&]() {
+        return flash_attention_backward_dkdv(dqkv, ws, Dbuf, datty, qkv, atty, lse, B, T, C, NH, s);
+    });
+    if (e != hipSuccess) return e;
+    const long long C3 = 3LL * C, TT = (long long)T * T;
+    GemmDesc q;
+    q.a_kcontig = true; q.b_kcontig = false;
+    q.M = T; q.N = hd; q.K = T;
+    q.A = flash_attention_ds(ws); q.lda = T; q.B = qkv + C; q.ldb = C3; q.C = dqkv; q.ldc = C3;
+    q.alpha = 1.0f / sqrtf((float)hd); q.causal = CAUSAL_KEND;
+    q.nbo = B; q.nbi = NH;
+    q.sAo = NH * TT; q.sAi = TT; q.sBo = T * C3; q.sBi = hd; q.sCo = T * C3; q.sCi = hd;
+    q.tile = plan_gemm(T, hd, T, (long long)B * NH, false).tile;
+    return gemm_run(q, s, "attn_dq");
 }
 
 }  // namespace
@@ -899,11 +929,7 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         // attention
         if (l.flash) {
             const float *lse = A + l.aoff[A_LSE] + (size_t)li * B * NH * T;
-            const double tri = 0.5 * T * (T + 1.0) * B * NH;
-            KRUNF(m, flash_name(FL_DQ, l.hd), 4.0 * tri * l.hd, 20.0 * BTC,
-                 flash_attention_backward_dq(dqkv, dscore, W + l.w_flash, datty, qkv, atty, lse, B, T, C, NH, s));
-            KRUNF(m, flash_name(FL_DKDV, l.hd), 4.0 * tri * l.hd, 24.0 * BTC,
-                 flash_attention_backward_dkdv(dqkv, W + l.w_flash, dscore, datty, qkv, lse, B, T, C, NH, s));
+            HIPCK(m, flash_backward(dqkv, dscore, W + l.w_flash, datty, qkv, atty, lse, B, T, C, NH, s));
         } else {
             Site site_("attn_bwd");
             HIPCK(m, attention_bwd(dqkv, dscore, datty, qkv, att, B, T, C, NH, s));
@@ -1086,8 +1112,7 @@ gpt2_status gpt2k_flash_attention_backward(float *dqkv, const float *datty, cons
     if (!attn_shape_ok(B, T, C, NH) || !flash_attention_supported(C / NH))
         return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024, T % 4 == 0");
     float *Dbuf = work, *ws = work + align_up((size_t)B * NH * T);
-    KCK(flash_attention_backward_dq(dqkv, Dbuf, ws, datty, qkv, atty, lse, B, T, C, NH, (hipStream_t)stream));
-    KCK(flash_attention_backward_dkdv(dqkv, ws, Dbuf, datty, qkv, lse, B, T, C, NH, (hipStream_t)stream));
+    KCK(flash_backward(dqkv, Dbuf, ws, datty, qkv, atty, lse, B, T, C, NH, (hipStream_t)stream));
     return GPT2_OK;
 }
 
