@@ -316,7 +316,8 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.w_dfch = off; off = align_up(off + BT * 4 * C);
     l.w_datt = off; off = align_up(off + (l.flash ? (size_t)B * NH * T : (size_t)B * NH * TT));
     l.w_flash = off; off = align_up(off + (l.flash ? flash_attention_work(B, T, (int)C, (int)NH) : 0));
-    l.w_part = off; off = align_up(off + (size_t)ln_partials((int)BT) * 2 * C);
+    // LayerNorm parameter partials of all 2L + 1 LayerNorms (summed once at the end)
+    l.w_part = off; off = align_up(off + (2 * L + 1) * (size_t)ln_partials((int)BT) * 2 * C);
     // split-K partial products: of the input gradient dlnf (the only one
     // allowed to split) and of the weight gradients, in separate regions
     // because a pair of them runs as one grid
@@ -539,11 +540,12 @@ hipError_t dinp_finish(float *dinp, const float *splitk, int N, int K, int ks, h
 hipError_t dw_finish(float *dW, float *dbias, const float *splitk, const float *dbias_ws, int K, int OC, int ks,
                      hipStream_t s) {
     if (ks <= 1) return hipSuccess;
-    hipError_t e = timed("sum_partials_kernel", 0, 4.0 * (ks + 2) * OC * K,
-                         [&]() { return k_sum_partials(dW, splitk, ks, (size_t)OC * K, true, s); });
-    if (e != hipSuccess || !dbias) return e;
-    return timed("sum_partials_kernel", 0, 4.0 * (ks + 2) * OC,
-                 [&]() { return k_sum_partials(dbias, dbias_ws, ks, (size_t)OC, true, s); });
+    if (!dbias)
+        return timed("sum_partials_kernel", 0, 4.0 * (ks + 2) * OC * K,
+                     [&]() { return k_sum_partials(dW, splitk, ks, (size_t)OC * K, true, s); });
+    return timed("sum_partials2_kernel", 0, 4.0 * (ks + 2) * ((double)OC * K + OC), [&]() {
+        return k_sum_partials2(dW, splitk, (size_t)OC * K, dbias, dbias_ws, (size_t)OC, ks, true, s);
+    });
 }
 
 // dinp[N][K] = dout[N][OC] W[OC][K] with an epilogue (the input gradient of a
@@ -889,7 +891,8 @@ gpt2_status gpt2_backward(gpt2_model *m) {
                             splitk, splitk_dw, dbias_ws, s));
     }
     const float *last = A + l.aoff[A_RES3] + (size_t)(l.L - 1) * BTC;
-    KRUN(m, "layernorm_backward_kernel", 12.0 * BTC, k_layernorm_backward(dres, G + l.poff[14], G + l.poff[15], part, dln, last, P + l.poff[14],
+    const size_t pslot = (size_t)ln_partials(BT) * 2 * C;  // floats of one LayerNorm's partials
+    KRUN(m, "layernorm_backward_kernel", 12.0 * BTC, k_layernorm_backward(dres, nullptr, nullptr, part + 2 * l.L * pslot, dln, last, P + l.poff[14],
                                   A + l.aoff[A_LNF_MEAN], A + l.aoff[A_LNF_RSTD], BT, C, false, s));
     for (int li = l.L - 1; li >= 0; li--) {
         const float *res = li == 0 ? A + l.aoff[A_ENCODED] : A + l.aoff[A_RES3] + (li - 1) * BTC;
@@ -918,7 +921,7 @@ gpt2_status gpt2_backward(gpt2_model *m) {
                                 dfch, ln2, fw, BT, C, 4 * C, nullptr, splitk_dw, dbias_ws, s));
         }
         // ln2: dres becomes the gradient of residual2
-        KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[8] + li * c, G + l.poff[9] + li * c, part, dln, res2,
+        KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, nullptr, nullptr, part + (l.L + li) * pslot, dln, res2,
                                       P + l.poff[8] + li * c, ln2m, ln2r, BT, C, true, s));
         // attproj: dout = dres
         {
@@ -941,9 +944,13 @@ gpt2_status gpt2_backward(gpt2_model *m) {
                                 ln1, qkvw, BT, C, 3 * C, nullptr, splitk_dw, dbias_ws, s));
         }
         // ln1: dres becomes the gradient of this layer's input
-        KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, G + l.poff[2] + li * c, G + l.poff[3] + li * c, part, dln, res,
+        KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, nullptr, nullptr, part + li * pslot, dln, res,
                                       P + l.poff[2] + li * c, ln1m, ln1r, BT, C, true, s));
     }
+    // gamma / beta gradients of every LayerNorm from their partials, one launch
+    KRUN(m, "ln_param_sums_kernel", 4.0 * (2 * l.L + 1) * (pslot + 4.0 * C),
+         k_ln_param_sums(G + l.poff[2], G + l.poff[3], G + l.poff[8], G + l.poff[9], G + l.poff[14], G + l.poff[15], l.L,
+                         part, BT, C, s));
     KRUN(m, "encoder_backward_kernel", 12.0 * BTC, k_encoder_backward(G + l.poff[0], G + l.poff[1], dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
                                 l.V, s));
     return GPT2_OK;

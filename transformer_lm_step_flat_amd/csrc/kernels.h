@@ -28,9 +28,18 @@ int ln_partials(int N);
 hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partial, const float *dout,
                                 const float *inp, const float *w, const float *mean, const float *rstd, int N,
                                 int C, bool accumulate, hipStream_t s);
+// With dw == NULL the row kernel only writes its partial rows [dw | db] (P x
+// 2C floats at `partial`); k_ln_param_sums then adds the partials of all
+// 2L + 1 LayerNorms of a backward pass (slot order: ln1 of each layer, ln2 of
+// each layer, the final one; P x 2C floats per slot) into their gradients.
+hipError_t k_ln_param_sums(float *w1, float *b1, float *w2, float *b2, float *w3, float *b3, int L,
+                           const float *partial, int N, int C, hipStream_t s);
 
 // dst[i] (+)= sum_{p < P} src[p * n + i]   (fixed order; n % 4 == 0, 16-byte aligned)
 hipError_t k_sum_partials(float *dst, const float *src, int P, size_t n, bool accumulate, hipStream_t s);
+// Two such sums (regions of n1 and n2 floats, partial strides n1 and n2) in one launch.
+hipError_t k_sum_partials2(float *dst1, const float *src1, size_t n1, float *dst2, const float *src2, size_t n2, int P,
+                          bool accumulate, hipStream_t s);
 // the same with partial rows ld apart
 hipError_t k_sum_partials_ld(float *dst, const float *src, int P, size_t n, size_t ld, bool accumulate,
                              hipStream_t s);

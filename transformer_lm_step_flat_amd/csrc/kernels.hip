@@ -260,6 +260,36 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(float *dst, const flo
     d4[i] = accumulate ? d4[i] + acc : acc;
 }
 
+// Two split-K sums in one launch: dst1[i] (+)= sum_p src1[p*n1 + i] for the
+// first n1 (float4) threads, the same for region 2 after them; p in order,
+// the loads of up to 8 partials issued before the adds.
+__global__ __launch_bounds__(256) void sum_partials2_kernel(floatx4 *dst1, const floatx4 *src1, size_t n1,
+                                                            floatx4 *dst2, const floatx4 *src2, size_t n2, int P,
+                                                            int accumulate) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    floatx4 *dst = dst1;
+    const floatx4 *src = src1;
+    size_t ld = n1;
+    if (i >= n1) {
+        i -= n1;
+        if (i >= n2) return;
+        dst = dst2;
+        src = src2;
+        ld = n2;
+    }
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    int p = 0;
+    for (; p + 8 <= P; p += 8) {
+        floatx4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = src[(size_t)(p + u) * ld + i];
+#pragma unroll
+        for (int u = 0; u < 8; u++) acc += v[u];
+    }
+    for (; p < P; p++) acc += src[(size_t)p * ld + i];
+    dst[i] = accumulate ? dst[i] + acc : acc;
+}
+
 // dst (n floats) and dst2 (n2 floats) += the column sums of partial rows of
 // n + n2 floats (fixed order): used for the [dw | db] partials of LayerNorm.
 // sum of src[p * ld] over p = p0, p0 + 16, ... < P, added in that order; the
@@ -292,6 +322,31 @@ __global__ __launch_bounds__(256) void sum_partials_split_kernel(float *dst, flo
 #pragma unroll
         for (int k = 1; k < 16; k++) t += lds[k][c];
         floatx4 *d4 = i < n4 ? (floatx4 *)dst + i : (floatx4 *)dst2 + (i - n4);
+        *d4 = *d4 + t;
+    }
+}
+
+// The LayerNorm parameter sums of a whole backward pass in one launch: slot
+// y = blockIdx.y holds P partial rows [dw | db] of one LayerNorm; slots
+// [0, L) are the ln1 of each layer, [L, 2L) the ln2, 2L the final one, each
+// added into its (w, b) gradient at stride C within its group.
+__global__ __launch_bounds__(256) void ln_param_sums_kernel(float *w1, float *b1, float *w2, float *b2, float *w3,
+                                                            float *b3, int L, const float *partial, int P, int C) {
+    __shared__ floatx4 lds[16][16];
+    const int y = blockIdx.y;
+    const int c = threadIdx.x & 15, pl = threadIdx.x >> 4;
+    const int C4 = C / 4, i = blockIdx.x * 16 + c, ld4 = 2 * C4;
+    const floatx4 *s4 = (const floatx4 *)(partial + (size_t)y * P * 2 * C);
+    const floatx4 acc = i < ld4 ? sum_rows_strided(s4 + i, pl, P, (size_t)ld4) : floatx4{0.f, 0.f, 0.f, 0.f};
+    lds[pl][c] = acc;
+    __syncthreads();
+    if (pl == 0 && i < ld4) {
+        floatx4 t = lds[0][c];
+#pragma unroll
+        for (int k = 1; k < 16; k++) t += lds[k][c];
+        float *w = y < L ? w1 + (size_t)y * C : (y < 2 * L ? w2 + (size_t)(y - L) * C : w3);
+        float *b = y < L ? b1 + (size_t)y * C : (y < 2 * L ? b2 + (size_t)(y - L) * C : b3);
+        floatx4 *d4 = i < C4 ? (floatx4 *)w + i : (floatx4 *)b + (i - C4);
         *d4 = *d4 + t;
     }
 }
@@ -653,6 +708,14 @@ hipError_t k_layernorm_forward(float *out, float *mean, float *rstd, const float
 
 int ln_partials(int N) { return (N + COL_CHUNK - 1) / COL_CHUNK; }
 
+hipError_t k_ln_param_sums(float *w1, float *b1, float *w2, float *b2, float *w3, float *b3, int L,
+                           const float *partial, int N, int C, hipStream_t s) {
+    if (C % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ln_param_sums_kernel, dim3(grid_for(2 * C / 4, 16), 2 * L + 1), dim3(256), 0, s, w1, b1, w2, b2,
+                       w3, b3, L, partial, ln_partials(N), C);
+    return hipGetLastError();
+}
+
 hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partial, const float *dout,
                                 const float *inp, const float *w, const float *mean, const float *rstd, int N,
                                 int C, bool accumulate, hipStream_t s) {
@@ -663,7 +726,7 @@ hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partia
     LN_DISPATCH(nv, layernorm_backward_kernel, dim3(P), dim3(256), lds, s, dinp, partial, dout, inp, w, mean, rstd, N,
                 C, accumulate ? 1 : 0);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !dw) return e;  // no dw: the caller sums the partials later
     hipLaunchKernelGGL(sum_partials_split_kernel, dim3(grid_for(2 * C / 4, 16)), dim3(256), 0, s, dw, db,
                        (const float *)partial, P, C / 4, C / 4);
     return hipGetLastError();
@@ -678,6 +741,19 @@ hipError_t k_sum_partials_ld(float *dst, const float *src, int P, size_t n, size
     else
         hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, dst, src, P, n / 4,
                            ld / 4, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t k_sum_partials2(float *dst1, const float *src1, size_t n1, float *dst2, const float *src2, size_t n2, int P,
+                          bool accumulate, hipStream_t s) {
+    if (n1 % 4 || n2 % 4 || P < 1) return hipErrorInvalidValue;
+    const uintptr_t al = (uintptr_t)dst1 | (uintptr_t)src1 | (uintptr_t)dst2 | (uintptr_t)src2;
+    if (al & 15) return hipErrorInvalidValue;
+    const size_t n = (n1 + n2) / 4;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(sum_partials2_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (floatx4 *)dst1,
+                       (const floatx4 *)src1, n1 / 4, (floatx4 *)dst2, (const floatx4 *)src2, n2 / 4, P,
+                       accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
