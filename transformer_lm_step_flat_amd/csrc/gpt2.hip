@@ -243,6 +243,17 @@ void bwd_split_need(int N, int K, int OC, bool split_dinp, size_t &sk_dinp, size
     sk_dw = std::max(sk_dw, b);
 }
 
+// The K split linear_bwd uses for the weight gradient (with an input gradient
+// beside it, whose own split is allowed or not).
+int dw_ksplit(int N, int K, int OC, bool split_dinp) {
+    const PairPlan pp = plan_pair(N, K, OC, split_dinp);
+    return pp.pair ? pp.ks_dw : plan_gemm(OC, K, N, 1, true).ksplit;
+}
+
+// The four weight-gradient sites of a layer: (in, out) features and the
+// parameter tensors of the weight and the bias.
+enum { SITE_QKV = 0, SITE_ATTPROJ = 1, SITE_FC = 2, SITE_FCPROJ = 3, NSITES = 4 };
+
 struct Layout {
     int B, T, C, L, NH, V, Vp, maxT, hd;
     bool flash;  // fused attention (no T x T matrices kept)
@@ -251,6 +262,10 @@ struct Layout {
     size_t aoff[NUM_ACTS], acnt[NUM_ACTS], nacts;
     // work buffer
     size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_flash, w_part, w_splitk, w_splitk_dw, w_dbias, nwork;
+    // per-layer split-K partials of each site's weight / bias gradient, summed
+    // for all layers at the end of the backward (ks 1: none)
+    int site_ks[NSITES];
+    size_t w_site_dw[NSITES], w_site_db[NSITES];
     // int buffer
     size_t i_tok, i_order, i_err, niwork;
 };
@@ -329,6 +344,17 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     bwd_split_need((int)BT, (int)C, l.Vp, true, sk, sk_dw);
     l.w_splitk = off; off = align_up(off + sk);
     l.w_splitk_dw = off; off = align_up(off + sk_dw);
+    {
+        const int sin[NSITES] = {(int)C, (int)C, (int)C, (int)(4 * C)};
+        const int sout[NSITES] = {(int)(3 * C), (int)C, (int)(4 * C), (int)C};
+        for (int j = 0; j < NSITES; j++) {
+            const int ks = dw_ksplit((int)BT, sin[j], sout[j], false);
+            l.site_ks[j] = ks;
+            const size_t kk = ks > 1 ? (size_t)ks : 0;
+            l.w_site_dw[j] = off; off = align_up(off + L * kk * sout[j] * sin[j]);
+            l.w_site_db[j] = off; off = align_up(off + L * kk * sout[j]);
+        }
+    }
     l.w_dbias = off; off = align_up(off + 16 * 4 * C);
     l.nwork = off;
     l.i_tok = 0;
@@ -561,10 +587,10 @@ hipError_t linear_bwd_dinp(float *dinp, const float *dout, const float *W, int N
 // (dbias may be null).  With split-K the partial products go to `splitk`
 // and the partial bias sums to `dbias_ws` (16 * OC floats).
 hipError_t linear_bwd_dw(float *dW, float *dbias, const float *dout, const float *inp, int N, int K, int OC,
-                         float *splitk, float *dbias_ws, hipStream_t s) {
+                         float *splitk, float *dbias_ws, hipStream_t s, bool defer_sum = false) {
     const Plan p = plan_gemm(OC, K, N, 1, splitk != nullptr);
     hipError_t e = gemm_run(dw_desc(dW, dbias, dout, inp, N, K, OC, p, splitk, dbias_ws), s);
-    return e != hipSuccess ? e : dw_finish(dW, dbias, splitk, dbias_ws, K, OC, p.ksplit, s);
+    return e != hipSuccess || defer_sum ? e : dw_finish(dW, dbias, splitk, dbias_ws, K, OC, p.ksplit, s);
 }
 
 // Both gradients of a linear layer out = inp W^T + b given dout: the weight
@@ -575,12 +601,13 @@ hipError_t linear_bwd_dw(float *dW, float *dbias, const float *dout, const float
 // dbias_ws are separate regions, both in use at once.
 hipError_t linear_bwd(float *dinp, int epi, const float *aux, float *dW, float *dbias, const float *dout,
                       const float *inp, const float *W, int N, int K, int OC, float *splitk_dinp, float *splitk_dw,
-                      float *dbias_ws, hipStream_t s) {
+                      float *dbias_ws, hipStream_t s, bool defer_dw_sum = false) {
     const bool split_dinp = epi == EPI_STORE && splitk_dinp != nullptr;
     const PairPlan pp = dinp ? plan_pair(N, K, OC, split_dinp) : PairPlan{false, 0, 1, 1};
     if (!pp.pair) {
         hipError_t e = dinp ? linear_bwd_dinp(dinp, dout, W, N, K, OC, epi, aux, splitk_dinp, s) : hipSuccess;
-        return e != hipSuccess ? e : linear_bwd_dw(dW, dbias, dout, inp, N, K, OC, splitk_dw, dbias_ws, s);
+        return e != hipSuccess ? e
+                               : linear_bwd_dw(dW, dbias, dout, inp, N, K, OC, splitk_dw, dbias_ws, s, defer_dw_sum);
     }
     const GemmDesc dd = dw_desc(dW, dbias, dout, inp, N, K, OC, Plan{pp.tile, pp.ks_dw}, splitk_dw, dbias_ws);
     const GemmDesc di = dinp_desc(dinp, dout, W, N, K, OC, epi, aux, Plan{pp.tile, pp.ks_dinp}, splitk_dinp);
@@ -588,7 +615,7 @@ hipError_t linear_bwd(float *dinp, int epi, const float *aux, float *dW, float *
     gemm_cost(dd, f1, b1);
     gemm_cost(di, f2, b2);
     hipError_t e = timed(gemm_pair_name(pp.tile), f1 + f2, b1 + b2, [&]() { return gemm_launch_pair(dd, di, s); });
-    if (e == hipSuccess) e = dw_finish(dW, dbias, splitk_dw, dbias_ws, K, OC, pp.ks_dw, s);
+    if (e == hipSuccess && !defer_dw_sum) e = dw_finish(dW, dbias, splitk_dw, dbias_ws, K, OC, pp.ks_dw, s);
     if (e == hipSuccess) e = dinp_finish(dinp, splitk_dinp, N, K, pp.ks_dinp, s);
     return e;
 }
@@ -883,6 +910,14 @@ gpt2_status gpt2_backward(gpt2_model *m) {
     float *dfch = W + l.w_dfch, *dscore = W + l.w_datt, *part = W + l.w_part, *splitk = W + l.w_splitk;
     float *splitk_dw = W + l.w_splitk_dw, *dbias_ws = W + l.w_dbias;
     const float *dlogits = A + l.aoff[A_LOGITS], *lnf = A + l.aoff[A_LNF];
+    // per-site split-K partials of layer li (their sums for all layers come at the end)
+    const int s_in[NSITES] = {C, C, C, 4 * C}, s_out[NSITES] = {3 * C, C, 4 * C, C};
+    auto site_dw = [&](int j, int li) {
+        return l.site_ks[j] > 1 ? W + l.w_site_dw[j] + (size_t)li * l.site_ks[j] * s_out[j] * s_in[j] : splitk_dw;
+    };
+    auto site_db = [&](int j, int li) {
+        return l.site_ks[j] > 1 ? W + l.w_site_db[j] + (size_t)li * l.site_ks[j] * s_out[j] : dbias_ws;
+    };
 
     // head: dlnf = dlogits wte, dwte += dlogits^T lnf
     {
@@ -912,13 +947,14 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         {
             Site site_("fcproj_bwd");
             HIPCK(m, linear_bwd(dfch, EPI_GELU_BWD, fch, G + l.poff[12] + li * 4 * c * c, G + l.poff[13] + li * c, dres,
-                                fchg, pw, BT, 4 * C, C, nullptr, splitk_dw, dbias_ws, s));
+                                fchg, pw, BT, 4 * C, C, nullptr, site_dw(SITE_FCPROJ, li), site_db(SITE_FCPROJ, li), s,
+                                true));
         }
         // fc
         {
             Site site_("fc_bwd");
             HIPCK(m, linear_bwd(dln, EPI_STORE, nullptr, G + l.poff[10] + li * 4 * c * c, G + l.poff[11] + li * 4 * c,
-                                dfch, ln2, fw, BT, C, 4 * C, nullptr, splitk_dw, dbias_ws, s));
+                                dfch, ln2, fw, BT, C, 4 * C, nullptr, site_dw(SITE_FC, li), site_db(SITE_FC, li), s, true));
         }
         // ln2: dres becomes the gradient of residual2
         KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, nullptr, nullptr, part + (l.L + li) * pslot, dln, res2,
@@ -927,7 +963,8 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         {
             Site site_("attproj_bwd");
             HIPCK(m, linear_bwd(datty, EPI_STORE, nullptr, G + l.poff[6] + li * c * c, G + l.poff[7] + li * c, dres,
-                                atty, aw, BT, C, C, nullptr, splitk_dw, dbias_ws, s));
+                                atty, aw, BT, C, C, nullptr, site_dw(SITE_ATTPROJ, li), site_db(SITE_ATTPROJ, li), s,
+                                true));
         }
         // attention
         if (l.flash) {
@@ -941,11 +978,23 @@ gpt2_status gpt2_backward(gpt2_model *m) {
         {
             Site site_("qkv_bwd");
             HIPCK(m, linear_bwd(dln, EPI_STORE, nullptr, G + l.poff[4] + li * 3 * c * c, G + l.poff[5] + li * 3 * c, dqkv,
-                                ln1, qkvw, BT, C, 3 * C, nullptr, splitk_dw, dbias_ws, s));
+                                ln1, qkvw, BT, C, 3 * C, nullptr, site_dw(SITE_QKV, li), site_db(SITE_QKV, li), s, true));
         }
         // ln1: dres becomes the gradient of this layer's input
         KRUN(m, "layernorm_backward_kernel", 16.0 * BTC, k_layernorm_backward(dres, nullptr, nullptr, part + li * pslot, dln, res,
                                       P + l.poff[2] + li * c, ln1m, ln1r, BT, C, true, s));
+    }
+    // weight and bias gradients of the split sites, all layers of a site in one launch
+    {
+        const int pw_[NSITES] = {4, 6, 10, 12};
+        for (int j = 0; j < NSITES; j++) {
+            const int ks = l.site_ks[j];
+            if (ks <= 1) continue;
+            const size_t n1 = (size_t)s_out[j] * s_in[j], n2 = (size_t)s_out[j];
+            KRUN(m, "sum_layers_kernel", 4.0 * (ks + 2) * (double)l.L * (n1 + n2),
+                 k_sum_layers(G + l.poff[pw_[j]], W + l.w_site_dw[j], n1, G + l.poff[pw_[j] + 1], W + l.w_site_db[j], n2,
+                              ks, l.L, s));
+        }
     }
     // gamma / beta gradients of every LayerNorm from their partials, one launch
     KRUN(m, "ln_param_sums_kernel", 4.0 * (2 * l.L + 1) * (pslot + 4.0 * C),

@@ -37,6 +37,10 @@ hipError_t k_ln_param_sums(float *w1, float *b1, float *w2, float *b2, float *w3
 
 // dst[i] (+)= sum_{p < P} src[p * n + i]   (fixed order; n % 4 == 0, 16-byte aligned)
 hipError_t k_sum_partials(float *dst, const float *src, int P, size_t n, bool accumulate, hipStream_t s);
+// For L layers at once: dst1[l*n1 + i] += sum_p src1[(l*P + p)*n1 + i], and
+// the same for region 2 (weight and bias gradients of one site of every layer).
+hipError_t k_sum_layers(float *dst1, const float *src1, size_t n1, float *dst2, const float *src2, size_t n2, int P,
+                       int L, hipStream_t s);
 // Two such sums (regions of n1 and n2 floats, partial strides n1 and n2) in one launch.
 hipError_t k_sum_partials2(float *dst1, const float *src1, size_t n1, float *dst2, const float *src2, size_t n2, int P,
                           bool accumulate, hipStream_t s);

@@ -290,6 +290,43 @@ __global__ __launch_bounds__(256) void sum_partials2_kernel(floatx4 *dst1, const
     dst[i] = accumulate ? dst[i] + acc : acc;
 }
 
+// The split-K sums of one weight-gradient site over all L layers in one
+// launch: for layer l, dst1[l*n1 + i] += sum_p src1[(l*P + p)*n1 + i] and the
+// same for region 2 (n counted in float4s; p in order).
+__global__ __launch_bounds__(256) void sum_layers_kernel(floatx4 *dst1, const floatx4 *src1, size_t n1,
+                                                         floatx4 *dst2, const floatx4 *src2, size_t n2, int P,
+                                                         int L) {
+    const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t per = n1 + n2;
+    if (g >= per * L) return;
+    const size_t l = g / per;
+    size_t i = g % per;
+    floatx4 *dst;
+    const floatx4 *src;
+    size_t ld;
+    if (i < n1) {
+        dst = dst1 + l * n1;
+        src = src1 + l * P * n1;
+        ld = n1;
+    } else {
+        i -= n1;
+        dst = dst2 + l * n2;
+        src = src2 + l * P * n2;
+        ld = n2;
+    }
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    int p = 0;
+    for (; p + 8 <= P; p += 8) {
+        floatx4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = src[(size_t)(p + u) * ld + i];
+#pragma unroll
+        for (int u = 0; u < 8; u++) acc += v[u];
+    }
+    for (; p < P; p++) acc += src[(size_t)p * ld + i];
+    dst[i] = dst[i] + acc;
+}
+
 // dst (n floats) and dst2 (n2 floats) += the column sums of partial rows of
 // n + n2 floats (fixed order): used for the [dw | db] partials of LayerNorm.
 // sum of src[p * ld] over p = p0, p0 + 16, ... < P, added in that order; the
@@ -754,6 +791,17 @@ hipError_t k_sum_partials2(float *dst1, const float *src1, size_t n1, float *dst
     hipLaunchKernelGGL(sum_partials2_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (floatx4 *)dst1,
                        (const floatx4 *)src1, n1 / 4, (floatx4 *)dst2, (const floatx4 *)src2, n2 / 4, P,
                        accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t k_sum_layers(float *dst1, const float *src1, size_t n1, float *dst2, const float *src2, size_t n2, int P,
+                       int L, hipStream_t s) {
+    if (n1 % 4 || n2 % 4 || P < 1 || L < 1) return hipErrorInvalidValue;
+    const uintptr_t al = (uintptr_t)dst1 | (uintptr_t)src1 | (uintptr_t)dst2 | (uintptr_t)src2;
+    if (al & 15) return hipErrorInvalidValue;
+    const size_t n = (n1 + n2) / 4 * L;
+    hipLaunchKernelGGL(sum_layers_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (floatx4 *)dst1,
+                       (const floatx4 *)src1, n1 / 4, (floatx4 *)dst2, (const floatx4 *)src2, n2 / 4, P, L);
     return hipGetLastError();
 }
 
