@@ -83,13 +83,15 @@ gpt2_status gpt2k_crossentropy(float *logits, float *losses, float *loss, const 
 
 /* Encoder: out[B][T][C] = wte[ids] + wpe[t].  Backward: dwte[id] += rows of
  * dout with that id, dwpe[t] += sum over b.  The backward needs the position
- * order computed by gpt2k_token_order (iwork of BT int32s + 1 flag). */
+ * order computed by gpt2k_token_order (iwork of BT int32s + 1 flag) and
+ * gpt2k_encoder_backward_work floats of `work` (segment sums). */
 gpt2_status gpt2k_encoder_forward(float *out, const int32_t *ids, const float *wte, const float *wpe, int B, int T,
                                   int C, int V, void *stream);
 gpt2_status gpt2k_token_order(int32_t *order, int32_t *err_flag, const int32_t *ids, const int32_t *targets,
                               int BT, int V, void *stream);
+size_t gpt2k_encoder_backward_work(int B, int T, int C);
 gpt2_status gpt2k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *ids,
-                                   const int32_t *order, int B, int T, int C, int V, void *stream);
+                                   const int32_t *order, int B, int T, int C, int V, float *work, void *stream);
 
 /* AdamW over n floats (n % 4 == 0), t >= 1; same update as gpt2_update. */
 gpt2_status gpt2k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float beta1,

@@ -278,6 +278,31 @@ def test_crossentropy(g, oracle_lib, BT, V, Vp):
     assert np.all(gd[:, V:] == 0.0)
 
 
+@pytest.mark.parametrize("B,T,C", [(3, 100, 64), (1, 68, 32), (2, 512, 96)])
+def test_encoder_backward_long_runs(g, oracle_lib, B, T, C):
+    """Runs of one id longer than the 64-entry segments of the scatter-add,
+    crossing several segment boundaries, with B*T not a multiple of 64."""
+    import torch
+    V = 50
+    rng = np.random.default_rng(B * T + C)
+    ids = rng.integers(0, V, (B, T)).astype(np.int32)
+    ids[rng.random((B, T)) < 0.7] = 7  # one id takes ~70 % of the positions
+    ids[0, 0], ids[-1, -1] = 0, V - 1
+    dids = dev(ids)
+    order = torch.empty(B * T, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.token_order(order, err, dids, None, B * T, V)
+    dout = f32(rng, B, T, C)
+    dwte0, dwpe0 = f32(rng, V, C), f32(rng, T, C)
+    dwte, dwpe = dev(dwte0), dev(dwpe0)
+    g.encoder_backward(dwte, dwpe, dev(dout), dids, order, B, T, C, V)
+    rw, rp = dwte0.astype(np.float64).ravel(), dwpe0.astype(np.float64).ravel()
+    oracle_lib.encoder_backward(rw, rp, dout.astype(np.float64).ravel(), ids.ravel().astype(np.int32), B, T, C)
+    assert rel(host(dwte).ravel(), rw) < 1e-5
+    assert rel(host(dwpe).ravel(), rp) < 1e-5
+    assert int(err.item()) == 0
+
+
 def test_encoder_and_token_order(g, oracle_lib):
     import torch
     from transformer_lm_step_flat_amd import synth

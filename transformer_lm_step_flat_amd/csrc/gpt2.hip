@@ -1000,7 +1000,8 @@ gpt2_status gpt2_backward(gpt2_model *m) {
     KRUN(m, "ln_param_sums_kernel", 4.0 * (2 * l.L + 1) * (pslot + 4.0 * C),
          k_ln_param_sums(G + l.poff[2], G + l.poff[3], G + l.poff[8], G + l.poff[9], G + l.poff[14], G + l.poff[15], l.L,
                          part, BT, C, s));
-    KRUN(m, "encoder_backward_kernel", 12.0 * BTC, k_encoder_backward(G + l.poff[0], G + l.poff[1], dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
+    // (datty is free by now: it holds the segment sums of the embedding scatter-add)
+    KRUN(m, "encoder_backward_kernel", 16.0 * BTC, k_encoder_backward(G + l.poff[0], G + l.poff[1], datty, dres, m->buf.iwork + l.i_tok, m->buf.iwork + l.i_order, B, T, C,
                                 l.V, s));
     return GPT2_OK;
 }
@@ -1203,10 +1204,12 @@ gpt2_status gpt2k_token_order(int32_t *order, int32_t *err_flag, const int32_t *
     return GPT2_OK;
 }
 
+size_t gpt2k_encoder_backward_work(int B, int T, int C) { return (size_t)B * T * C; }
+
 gpt2_status gpt2k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *ids,
-                                   const int32_t *order, int B, int T, int C, int V, void *stream) {
+                                   const int32_t *order, int B, int T, int C, int V, float *work, void *stream) {
     if (C % 4) return fail(nullptr, GPT2_EINVAL, "C must be a multiple of 4");
-    KCK(k_encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V, (hipStream_t)stream));
+    KCK(k_encoder_backward(dwte, dwpe, work, dout, ids, order, B, T, C, V, (hipStream_t)stream));
     return GPT2_OK;
 }
 

@@ -17,7 +17,8 @@ hipError_t k_encoder_forward(float *out, const int32_t *inp, const float *wte, c
                              int C, int V, hipStream_t s);
 // dwte[id][:] += sum of dout rows of that id (positions in ascending order);
 // dwpe[t][:] += sum_b dout[b][t][:]
-hipError_t k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *inp,
+// part: B*T*C floats of workspace (segment sums).
+hipError_t k_encoder_backward(float *dwte, float *dwpe, float *part, const float *dout, const int32_t *inp,
                               const int32_t *order, int B, int T, int C, int V, hipStream_t s);
 
 hipError_t k_layernorm_forward(float *out, float *mean, float *rstd, const float *inp, const float *w,

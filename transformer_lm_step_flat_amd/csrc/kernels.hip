@@ -68,33 +68,65 @@ __global__ void encoder_forward_kernel(float *out, const int32_t *inp, const flo
     ((floatx4 *)(out + bt * C))[c4] = a + b;
 }
 
-// One block per (sorted index, 256-column chunk).  The block at the first
-// position of a run of equal ids sums the run's rows and adds the sum to that
-// id's row of dwte; all other blocks exit.  The run is split over 4 row
-// lanes (lane l takes run entries l, l+4, ...), whose sums are added in a
-// fixed order.
-__global__ __launch_bounds__(256) void encoder_backward_wte_kernel(float *dwte, const float *dout,
-                                                                   const int32_t *inp, const int32_t *order, int BT,
-                                                                   int C, int V) {
-    __shared__ floatx4 part[4][64];
+// dwte scatter-add in two deterministic phases over the positions sorted by
+// (id, position).  Phase 1: the sorted sequence is cut into chunks of
+// ENC_CHUNK entries; within a chunk each run of equal ids (a segment) is
+// summed in position order and stored at part[first sorted index of the
+// segment].  Phase 2: each run of equal ids adds its segments (its first one
+// and one per chunk boundary inside the run, in order) to the id's row.  No
+// run is walked by one thread, so the cost does not grow with the longest run.
+constexpr int ENC_CHUNK = 64;
+
+__global__ __launch_bounds__(64) void encoder_backward_segments_kernel(floatx4 *part, const float *dout,
+                                                                        const int32_t *inp, const int32_t *order,
+                                                                        int BT, int C, int V) {
+    __shared__ int ids[ENC_CHUNK + 1], pos[ENC_CHUNK];
+    const int base = blockIdx.x * ENC_CHUNK, n = min(ENC_CHUNK, BT - base);
+    const int tid = threadIdx.x;
+    if (tid < n) {
+        const int p = order[base + tid];
+        pos[tid] = p;
+        ids[tid] = clamp_id(inp[p], V);
+    }
+    if (tid == 0) ids[n] = -1;  // closes the last segment
+    __syncthreads();
+    const int C4 = C / 4, c4 = blockIdx.y * 64 + tid;
+    if (c4 >= C4) return;
+    const floatx4 *src = (const floatx4 *)dout + c4;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    int seg = 0;
+    for (int e0 = 0; e0 < n; e0 += 8) {
+        floatx4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = e0 + u < n ? src[(long long)pos[e0 + u] * C4] : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int e = e0 + u;
+            if (e < n) {
+                acc += v[u];
+                if (ids[e + 1] != ids[e]) {
+                    part[(long long)(base + seg) * C4 + c4] = acc;
+                    acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                    seg = e + 1;
+                }
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(64) void encoder_backward_runs_kernel(float *dwte, const floatx4 *part,
+                                                                    const int32_t *inp, const int32_t *order, int BT,
+                                                                    int C, int V) {
     const int i = blockIdx.x;
     const int id = clamp_id(inp[order[i]], V);
-    if (i > 0 && clamp_id(inp[order[i - 1]], V) == id) return;
-    const int c4 = blockIdx.y * 64 + (threadIdx.x & 63), rl = threadIdx.x >> 6;
-    const bool col_ok = c4 < C / 4;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = i + rl; j < BT; j += 4) {
-        const int pos = order[j];
-        if (clamp_id(inp[pos], V) != id) break;  // sorted by id: the run has ended
-        if (col_ok) acc += ((const floatx4 *)(dout + (long long)pos * C))[c4];
-    }
-    part[rl][threadIdx.x & 63] = acc;
-    __syncthreads();
-    if (rl == 0 && col_ok) {
-        const int l = threadIdx.x;
-        floatx4 *dst = (floatx4 *)(dwte + (long long)id * C) + c4;
-        *dst = *dst + (((part[0][l] + part[1][l]) + part[2][l]) + part[3][l]);
-    }
+    if (i > 0 && clamp_id(inp[order[i - 1]], V) == id) return;  // not the first entry of its run
+    const int C4 = C / 4, c4 = blockIdx.y * 64 + threadIdx.x;
+    if (c4 >= C4) return;
+    floatx4 acc = part[(long long)i * C4 + c4];
+    for (int k = (i / ENC_CHUNK + 1) * ENC_CHUNK; k < BT && clamp_id(inp[order[k]], V) == id; k += ENC_CHUNK)
+        acc += part[(long long)k * C4 + c4];
+    floatx4 *dst = (floatx4 *)(dwte + (long long)id * C) + c4;
+    *dst = *dst + acc;
 }
 
 __global__ void encoder_backward_wpe_kernel(float *dwpe, const float *dout, int B, int T, int C) {
@@ -709,12 +741,17 @@ hipError_t k_encoder_forward(float *out, const int32_t *inp, const float *wte, c
     return hipGetLastError();
 }
 
-hipError_t k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *inp,
+hipError_t k_encoder_backward(float *dwte, float *dwpe, float *part, const float *dout, const int32_t *inp,
                               const int32_t *order, int B, int T, int C, int V, hipStream_t s) {
     const int BT = B * T;
-    hipLaunchKernelGGL(encoder_backward_wte_kernel, dim3(BT, grid_for(C / 4, 64)), dim3(256), 0, s, dwte, dout, inp,
-                       order, BT, C, V);
+    if (C % 4 || ((uintptr_t)part & 15)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(encoder_backward_segments_kernel, dim3(grid_for(BT, ENC_CHUNK), grid_for(C / 4, 64)), dim3(64), 0,
+                       s, (floatx4 *)part, dout, inp, order, BT, C, V);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(encoder_backward_runs_kernel, dim3(BT, grid_for(C / 4, 64)), dim3(64), 0, s, dwte,
+                       (const floatx4 *)part, inp, order, BT, C, V);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(encoder_backward_wpe_kernel, dim3(grid_for((size_t)T * (C / 4), 256)), dim3(256), 0, s,
                        dwpe, dout, B, T, C);

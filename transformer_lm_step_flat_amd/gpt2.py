@@ -80,7 +80,7 @@ _SIGS = {
     "gpt2k_crossentropy": [_P, _P, _P, _P, _I, _I, _I, _P],
     "gpt2k_encoder_forward": [_P, _P, _P, _P, _I, _I, _I, _I, _P],
     "gpt2k_token_order": [_P, _P, _P, _P, _I, _I, _P],
-    "gpt2k_encoder_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "gpt2k_encoder_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
     "gpt2k_adamw": [_P, _P, _P, _P, _Z, _F, _F, _F, _F, _F, _I, _P],
 }
 _SIZE_FNS = {
@@ -88,6 +88,7 @@ _SIZE_FNS = {
     "gpt2k_layernorm_backward_work": [_I, _I],
     "gpt2k_attention_backward_work": [_I, _I, _I, _I],
     "gpt2k_flash_attention_work": [_I, _I, _I, _I],
+    "gpt2k_encoder_backward_work": [_I, _I, _I],
 }
 
 # every symbol the headers declare
@@ -348,8 +349,10 @@ def token_order(order, err, ids, targets, BT, V):
 
 
 def encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V):
+    work = torch.empty(max(1, lib().gpt2k_encoder_backward_work(B, T, C)), dtype=torch.float32, device=dout.device)
     _check(lib().gpt2k_encoder_backward(_ptr(dwte), _ptr(dwpe), _ptr(dout), _ptr(ids), _ptr(order), B, T, C, V,
-                                        _s()))
+                                        _ptr(work), _s()))
+    return work
 
 
 def adamw(params, grads, m, v, lr, b1, b2, eps, wd, t):
