@@ -893,7 +893,7 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
 gpt2_status gpt2_zero_grad(gpt2_model *m) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
     ProfScope prof_scope(m);
-    KRUN(m, "fill_kernel", 4.0 * m->lo.nparams, k_fill(m->buf.grads, m->lo.nparams, 0.0f, m->stream));
+    KRUN(m, "fill4_kernel", 4.0 * m->lo.nparams, k_fill(m->buf.grads, m->lo.nparams, 0.0f, m->stream));
     return GPT2_OK;
 }
 

@@ -16,6 +16,16 @@ __global__ void fill_kernel(float *p, size_t n, float v) {
     for (; i < n; i += stride) p[i] = v;
 }
 
+// The same for 16-byte-aligned buffers of n4 float4s: each workgroup stores
+// one contiguous run of 4 x 256 float4s with non-temporal stores.
+__global__ __launch_bounds__(256) void fill4_kernel(floatx4 *p, size_t n4, float v) {
+    const size_t base = (size_t)blockIdx.x * 1024 + threadIdx.x;
+    const floatx4 x = {v, v, v, v};
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+        if (base + (size_t)u * 256 < n4) __builtin_nontemporal_store(x, p + base + (size_t)u * 256);
+}
+
 __global__ void fill_i32_kernel(int32_t *p, size_t n, int32_t v) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -24,34 +34,32 @@ __global__ void fill_i32_kernel(int32_t *p, size_t n, int32_t v) {
 
 __device__ __forceinline__ int clamp_id(int id, int V) { return id < 0 ? 0 : (id >= V ? V - 1 : id); }
 
-// Rank of key (id, position) among all BT keys, by counting smaller keys.
+// Id validation and the position order of the embedding backward: the
+// positions sorted by (id, position).  One wavefront per position p: its
+// rank is the number of positions q with key(q) < key(p), key = id * BT +
+// position, each lane counting every 64th q and the lanes' counts summed.
 // Keys are distinct (positions differ), so the ranks are a permutation.
-__global__ void token_prep_kernel(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int BT,
-                                  int V) {
-    __shared__ long long keys[256];
-    const int p = blockIdx.x * blockDim.x + threadIdx.x;
-    long long mykey = 0;
-    if (p < BT) {
-        int id = inp[p];
+__global__ __launch_bounds__(256) void token_prep_kernel(const int32_t *inp, const int32_t *tgt, int32_t *order,
+                                                         int32_t *err, int BT, int V) {
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= BT) return;
+    const int id = inp[p];
+    const long long mykey = (long long)clamp_id(id, V) * BT + p;
+    int cnt = 0;
+    for (int q = lane; q < BT; q += 64) cnt += (long long)clamp_id(inp[q], V) * BT + q < mykey;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, WAVE);
+    if (lane == 0) {
         int e = 0;
         if (id < 0 || id >= V) e |= 1;
         if (tgt) {
-            int tg = tgt[p];
+            const int tg = tgt[p];
             if (tg < 0 || tg >= V) e |= 2;
         }
         if (e) atomicOr(err, e);
-        mykey = (long long)clamp_id(id, V) * BT + p;
+        order[cnt] = p;
     }
-    int rank = 0;
-    for (int c0 = 0; c0 < BT; c0 += 256) {
-        __syncthreads();
-        int q = c0 + threadIdx.x;
-        keys[threadIdx.x] = q < BT ? (long long)clamp_id(inp[q], V) * BT + q : 0x7fffffffffffffffLL;
-        __syncthreads();
-        int lim = min(256, BT - c0);
-        for (int j = 0; j < lim; j++) rank += keys[j] < mykey;
-    }
-    if (p < BT) order[rank] = p;
 }
 
 __global__ void encoder_forward_kernel(float *out, const int32_t *inp, const float *wte, const float *wpe, int T,
@@ -713,6 +721,11 @@ __global__ __launch_bounds__(256) void adamw_kernel(floatx4 *params, const float
 
 hipError_t k_fill(float *p, size_t n, float v, hipStream_t s) {
     if (n == 0) return hipSuccess;
+    if (n % 4 == 0 && ((uintptr_t)p & 15) == 0 && n / 4 / 1024 < 0x7fffffff) {
+        hipLaunchKernelGGL(fill4_kernel, dim3((unsigned)((n / 4 + 1023) / 1024)), dim3(256), 0, s, (floatx4 *)p, n / 4,
+                           v);
+        return hipGetLastError();
+    }
     unsigned g = grid_for(n, 256);
     if (g > 16384) g = 16384;
     hipLaunchKernelGGL(fill_kernel, dim3(g), dim3(256), 0, s, p, n, v);
@@ -729,7 +742,7 @@ hipError_t k_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s) {
 
 hipError_t k_token_prep(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int BT, int V,
                         hipStream_t s) {
-    hipLaunchKernelGGL(token_prep_kernel, dim3(grid_for(BT, 256)), dim3(256), 0, s, inp, tgt, order, err, BT, V);
+    hipLaunchKernelGGL(token_prep_kernel, dim3(grid_for(BT, 4)), dim3(256), 0, s, inp, tgt, order, err, BT, V);
     return hipGetLastError();
 }
 
