@@ -69,3 +69,8 @@ hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream);
 // MN-contiguous), d2 an input gradient (A K-contiguous, B MN-contiguous),
 // both with the same nonzero `tile` and no causal mode.
 hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t stream);
+
+// The names a kernel-trace profiler shows for the kernels the two calls
+// above run with descriptor d (static strings).
+const char *gemm_kernel_name(const GemmDesc &d);
+const char *gemm_pair_kernel_name(int tile);

@@ -2,15 +2,15 @@
 //
 // One workgroup = 4 wavefronts (2 x 2) computes a BM x BN tile of C; each
 // wavefront owns a (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA blocks with
-// the accumulators held in registers.  The K loop stages BK = 32 slices of A
-// and B through LDS: while the MFMAs consume the current slice, the next one
+// the accumulators held in registers.  The K loop stages BK = 32 or 64 slices
+// of A and B through LDS: while the MFMAs consume the current slice, the next one
 // is already on its way from global memory into registers.
 //
 // K-index assignment inside a slice: v_mfma_f32_32x32x2_f32 takes two k
 // values per instruction, one from each half of the wavefront (lanes 0-31
-// and 32-63).  Lane half h feeds k = h*16 + j for the j-th instruction of the
-// slice, so each lane walks 16 consecutive k: for a K-contiguous operand that
-// is four 16-byte LDS reads per 32 x 32 block per slice.  Any pairing of k to
+// and 32-63).  Lane half h feeds k = h*BK/2 + j for the j-th instruction of
+// the slice, so each lane walks BK/2 consecutive k: for a K-contiguous operand
+// that is BK/8 16-byte LDS reads per 32 x 32 block per slice.  Any pairing of k to
 // instruction slots gives the same sum, so this only changes rounding order.
 //
 // LDS layouts: a K-contiguous operand is kept [mn][k] with a row pitch of
@@ -22,7 +22,6 @@
 
 namespace {
 
-constexpr int GEMM_BK = 32;
 constexpr int GEMM_THREADS = 256;
 
 struct GemmArgs {
@@ -61,22 +60,21 @@ __device__ __forceinline__ void group_order(int bid, int tiles_m, int tiles_n, i
 }
 
 // LDS floats of the two operand tiles
-template <int BM, int BN, bool AK, bool BKC>
+template <int BM, int BN, bool AK, bool BKC, int BK>
 struct TileLds {
-    static constexpr int KP = GEMM_BK + 4;  // pitch of a K-contiguous LDS tile
-    static constexpr int A = AK ? BM * KP : GEMM_BK * BM;
-    static constexpr int B = BKC ? BN * KP : GEMM_BK * BN;
+    static constexpr int KP = BK + 4;  // pitch of a K-contiguous LDS tile
+    static constexpr int A = AK ? BM * KP : BK * BM;
+    static constexpr int B = BKC ? BN * KP : BK * BN;
 };
 
 // One BM x BN output tile (row tile tm, column tile tn), batch / split
 // index z, operand tiles staged in As / Bs.
-template <int BM, int BN, bool AK, bool BKC>
+template <int BM, int BN, bool AK, bool BKC, int BK>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int z, float *__restrict__ As,
                                           float *__restrict__ Bs) {
-    constexpr int BK = GEMM_BK;
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int KP = TileLds<BM, BN, AK, BKC>::KP;
+    constexpr int KP = TileLds<BM, BN, AK, BKC, BK>::KP;
     constexpr int A_F4 = BM * BK / 4 / GEMM_THREADS;
     constexpr int B_F4 = BN * BK / 4 / GEMM_THREADS;
     static_assert(A_F4 >= 1 && B_F4 >= 1, "tile too small for 256 threads");
@@ -258,22 +256,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         }
 }
 
-template <int BM, int BN, bool AK, bool BKC>
-__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs p) {
-    using L = TileLds<BM, BN, AK, BKC>;
+template <int BM, int BN, bool AK, bool BKC, int BK, int LB>
+__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_kernel(GemmArgs p) {
+    using L = TileLds<BM, BN, AK, BKC, BK>;
     __shared__ __attribute__((aligned(16))) float As[L::A];
     __shared__ __attribute__((aligned(16))) float Bs[L::B];
     int tm, tn;
     group_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    gemm_tile<BM, BN, AK, BKC>(p, tm, tn, blockIdx.z, As, Bs);
+    gemm_tile<BM, BN, AK, BKC, BK>(p, tm, tn, blockIdx.z, As, Bs);
 }
 
 // Causal products whose K range grows (KEND) or shrinks (KSTART) with the row
 // tile: a workgroup takes row tiles i and tiles_m - 1 - i of one column, whose
 // K ranges add up to the same length for every workgroup.
-template <int BM, int BN, bool AK, bool BKC>
-__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_fold_kernel(GemmArgs p) {
-    using L = TileLds<BM, BN, AK, BKC>;
+template <int BM, int BN, bool AK, bool BKC, int BK, int LB>
+__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_fold_kernel(GemmArgs p) {
+    using L = TileLds<BM, BN, AK, BKC, BK>;
     __shared__ __attribute__((aligned(16))) float As[L::A];
     __shared__ __attribute__((aligned(16))) float Bs[L::B];
     const int half = (p.tiles_m + 1) / 2;
@@ -281,7 +279,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_fold_kernel(GemmArgs p) 
     const int tn = t / half, i = t % half, j = p.tiles_m - 1 - i;
     const int npass = i == j ? 1 : 2;
     for (int pass = 0; pass < npass; pass++)
-        gemm_tile<BM, BN, AK, BKC>(p, pass == 0 ? j : i, tn, blockIdx.z, As, Bs);
+        gemm_tile<BM, BN, AK, BKC, BK>(p, pass == 0 ? j : i, tn, blockIdx.z, As, Bs);
 }
 
 // Two independent products in one grid of w = w1 + w2 workgroups (w1 of
@@ -289,10 +287,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_fold_kernel(GemmArgs p) 
 // use the same tile shape.  Each XCD gets an eighth of each problem, as one
 // contiguous run of problem 1 followed by one of problem 2, so that the work
 // per XCD is balanced and operand tiles are shared within an XCD's L2.
-template <int BM, int BN, bool AK1, bool BKC1, bool AK2, bool BKC2>
-__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int w1, int w) {
-    using L1 = TileLds<BM, BN, AK1, BKC1>;
-    using L2 = TileLds<BM, BN, AK2, BKC2>;
+template <int BM, int BN, int BK, int LB, bool AK1, bool BKC1, bool AK2, bool BKC2>
+__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int w1, int w) {
+    using L1 = TileLds<BM, BN, AK1, BKC1, BK>;
+    using L2 = TileLds<BM, BN, AK2, BKC2, BK>;
     __shared__ __attribute__((aligned(16))) float As[L1::A > L2::A ? L1::A : L2::A];
     __shared__ __attribute__((aligned(16))) float Bs[L1::B > L2::B ? L1::B : L2::B];
     const int X = 8;
@@ -304,63 +302,66 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_pair_kernel(GemmArgs p1,
         const int g = s1 + j, nt = p1.tiles_m * p1.tiles_n;
         int tm, tn;
         group_order(g % nt, p1.tiles_m, p1.tiles_n, p1.group_m, tm, tn);
-        gemm_tile<BM, BN, AK1, BKC1>(p1, tm, tn, g / nt, As, Bs);
+        gemm_tile<BM, BN, AK1, BKC1, BK>(p1, tm, tn, g / nt, As, Bs);
     } else {
         const int s2 = x * (w / X) + min(x, w % X) - s1;  // workgroups of XCDs before x, less problem 1's
         const int g = s2 + j - r1, nt = p2.tiles_m * p2.tiles_n;
         int tm, tn;
         group_order(g % nt, p2.tiles_m, p2.tiles_n, p2.group_m, tm, tn);
-        gemm_tile<BM, BN, AK2, BKC2>(p2, tm, tn, g / nt, As, Bs);
+        gemm_tile<BM, BN, AK2, BKC2, BK>(p2, tm, tn, g / nt, As, Bs);
     }
 }
 
-template <int BM, int BN>
+// Tile grid and the K range of each split (a whole number of BK slices).
+template <int BM, int BN, int BK>
 void set_tiles(const GemmDesc &d, GemmArgs &a) {
     a.tiles_m = (d.M + BM - 1) / BM;
     a.tiles_n = (d.N + BN - 1) / BN;
     a.group_m = 8;
+    const int kc = (d.K + d.ksplit - 1) / d.ksplit;
+    a.kchunk = kc > 0 ? (kc + BK - 1) / BK * BK : BK;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int LB>
 hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream) {
     GemmArgs a = a0;
-    set_tiles<BM, BN>(d, a);
+    set_tiles<BM, BN, BK>(d, a);
     long long nb = (long long)d.nbo * d.nbi * d.ksplit;
     if (nb > 65535) return hipErrorInvalidValue;
     if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && a.tiles_m > 1) {
         dim3 g((a.tiles_m + 1) / 2 * a.tiles_n, 1, (unsigned)nb);
         if (d.a_kcontig && !d.b_kcontig)
-            hipLaunchKernelGGL((gemm_fold_kernel<BM, BN, true, false>), g, dim3(GEMM_THREADS), 0, stream, a);
+            hipLaunchKernelGGL((gemm_fold_kernel<BM, BN, true, false, BK, LB>), g, dim3(GEMM_THREADS), 0, stream, a);
         else if (!d.a_kcontig && !d.b_kcontig)
-            hipLaunchKernelGGL((gemm_fold_kernel<BM, BN, false, false>), g, dim3(GEMM_THREADS), 0, stream, a);
+            hipLaunchKernelGGL((gemm_fold_kernel<BM, BN, false, false, BK, LB>), g, dim3(GEMM_THREADS), 0, stream, a);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
     }
     dim3 grid(a.tiles_m * a.tiles_n, 1, (unsigned)nb);
     if (d.a_kcontig && d.b_kcontig)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true>), grid, dim3(GEMM_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true, BK, LB>), grid, dim3(GEMM_THREADS), 0, stream, a);
     else if (d.a_kcontig && !d.b_kcontig)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false>), grid, dim3(GEMM_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false, BK, LB>), grid, dim3(GEMM_THREADS), 0, stream, a);
     else if (!d.a_kcontig && !d.b_kcontig)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false>), grid, dim3(GEMM_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false, BK, LB>), grid, dim3(GEMM_THREADS), 0, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int LB>
 hipError_t launch_pair(const GemmDesc &d1, const GemmArgs &a1_, const GemmDesc &d2, const GemmArgs &a2_,
                        hipStream_t stream) {
     GemmArgs a1 = a1_, a2 = a2_;
-    set_tiles<BM, BN>(d1, a1);
-    set_tiles<BM, BN>(d2, a2);
+    set_tiles<BM, BN, BK>(d1, a1);
+    set_tiles<BM, BN, BK>(d2, a2);
     const long long w1 = (long long)a1.tiles_m * a1.tiles_n * d1.nbo * d1.nbi * d1.ksplit;
     const long long w2 = (long long)a2.tiles_m * a2.tiles_n * d2.nbo * d2.nbi * d2.ksplit;
     if (w1 + w2 > (1LL << 30)) return hipErrorInvalidValue;
     // the one instantiation used: a weight gradient (both MN-contiguous) beside an input gradient
     if (d1.a_kcontig || d1.b_kcontig || !d2.a_kcontig || d2.b_kcontig) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, false, false, true, false>), dim3((unsigned)(w1 + w2)),
+    hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false>), dim3((unsigned)(w1 + w2)),
                        dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
     return hipGetLastError();
 }
@@ -393,10 +394,19 @@ hipError_t make_args(const GemmDesc &d, GemmArgs &a) {
     a.M = d.M; a.N = d.N; a.K = d.K;
     a.epi = d.epi; a.causal = d.causal;
     a.nbi = d.nbi; a.ksplit = d.ksplit;
-    int kc = (d.K + d.ksplit - 1) / d.ksplit;
-    a.kchunk = (kc + GEMM_BK - 1) / GEMM_BK * GEMM_BK;
-    if (a.kchunk == 0) a.kchunk = GEMM_BK;
     return hipSuccess;
+}
+
+// The tile shape a descriptor runs with (its own, or one picked by size).
+int resolve_tile(const GemmDesc &d) {
+    if (d.tile != 0) return d.tile;
+    const long long batches = (long long)d.nbo * d.nbi * d.ksplit;
+    const long long t128 = (long long)((d.M + 127) / 128) * ((d.N + 127) / 128) * batches;
+    const long long t64n = (long long)((d.M + 127) / 128) * ((d.N + 63) / 64) * batches;
+    if (d.N <= 64) return 2;
+    if (t128 >= 512) return 1;
+    if (t64n >= 512) return 2;
+    return 3;
 }
 
 }  // namespace
@@ -405,20 +415,10 @@ hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
     GemmArgs a;
     hipError_t e = make_args(d, a);
     if (e != hipSuccess) return e;
-    int tile = d.tile;
-    if (tile == 0) {
-        long long batches = (long long)d.nbo * d.nbi * d.ksplit;
-        long long t128 = (long long)((d.M + 127) / 128) * ((d.N + 127) / 128) * batches;
-        long long t64n = (long long)((d.M + 127) / 128) * ((d.N + 63) / 64) * batches;
-        if (d.N <= 64) tile = 2;
-        else if (t128 >= 512) tile = 1;
-        else if (t64n >= 512) tile = 2;
-        else tile = 3;
-    }
-    switch (tile) {
-        case 1: return launch_tile<128, 128>(d, a, stream);
-        case 2: return launch_tile<128, 64>(d, a, stream);
-        case 3: return launch_tile<64, 64>(d, a, stream);
+    switch (resolve_tile(d)) {
+        case 1: return launch_tile<128, 128, 32, 3>(d, a, stream);
+        case 2: return launch_tile<128, 64, 32, 3>(d, a, stream);
+        case 3: return launch_tile<64, 64, 32, 3>(d, a, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -430,9 +430,38 @@ hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t 
     if (e != hipSuccess) return e;
     if (d1.tile != d2.tile || d1.causal || d2.causal) return hipErrorInvalidValue;
     switch (d1.tile) {
-        case 1: return launch_pair<128, 128>(d1, a1, d2, a2, stream);
-        case 2: return launch_pair<128, 64>(d1, a1, d2, a2, stream);
-        case 3: return launch_pair<64, 64>(d1, a1, d2, a2, stream);
+        case 1: return launch_pair<128, 128, 32, 3>(d1, a1, d2, a2, stream);
+        case 2: return launch_pair<128, 64, 32, 3>(d1, a1, d2, a2, stream);
+        case 3: return launch_pair<64, 64, 32, 3>(d1, a1, d2, a2, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// Keep in step with the instantiations chosen in gemm_launch and gemm_launch_pair.
+const char *gemm_pair_kernel_name(int tile) {
+    static const char *names[3] = {"gemm_pair_kernel<128, 128, 32, 3, false, false, true, false>",
+                                   "gemm_pair_kernel<128, 64, 32, 3, false, false, true, false>",
+                                   "gemm_pair_kernel<64, 64, 32, 3, false, false, true, false>"};
+    return names[tile >= 1 && tile <= 3 ? tile - 1 : 0];
+}
+
+const char *gemm_kernel_name(const GemmDesc &d) {
+    static const char *names[3][3] = {
+        {"gemm_kernel<128, 128, true, true, 32, 3>", "gemm_kernel<128, 128, true, false, 32, 3>",
+         "gemm_kernel<128, 128, false, false, 32, 3>"},
+        {"gemm_kernel<128, 64, true, true, 32, 3>", "gemm_kernel<128, 64, true, false, 32, 3>",
+         "gemm_kernel<128, 64, false, false, 32, 3>"},
+        {"gemm_kernel<64, 64, true, true, 32, 3>", "gemm_kernel<64, 64, true, false, 32, 3>",
+         "gemm_kernel<64, 64, false, false, 32, 3>"}};
+    static const char *fold_names[3][3] = {
+        {"", "gemm_fold_kernel<128, 128, true, false, 32, 3>", "gemm_fold_kernel<128, 128, false, false, 32, 3>"},
+        {"", "gemm_fold_kernel<128, 64, true, false, 32, 3>", "gemm_fold_kernel<128, 64, false, false, 32, 3>"},
+        {"", "gemm_fold_kernel<64, 64, true, false, 32, 3>", "gemm_fold_kernel<64, 64, false, false, 32, 3>"}};
+    static const int bm[3] = {128, 128, 64};
+    const int tile = resolve_tile(d);
+    const int t = tile >= 1 && tile <= 3 ? tile - 1 : 0;
+    const int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
+    // causal products with a growing or shrinking K range run with folded row tiles
+    if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];
+    return names[t][l];
 }

@@ -450,31 +450,6 @@ struct ProfScope {
     ~ProfScope() { g_prof = saved; }
 };
 
-const char *gemm_pair_name(int tile) {
-    static const char *names[3] = {"gemm_pair_kernel<128, 128, false, false, true, false>",
-                                   "gemm_pair_kernel<128, 64, false, false, true, false>",
-                                   "gemm_pair_kernel<64, 64, false, false, true, false>"};
-    return names[tile >= 1 && tile <= 3 ? tile - 1 : 0];
-}
-
-// The name rocprofv3 shows for the GEMM instantiation a descriptor runs.
-const char *gemm_name(const GemmDesc &d) {
-    static const char *names[3][3] = {
-        {"gemm_kernel<128, 128, true, true>", "gemm_kernel<128, 128, true, false>", "gemm_kernel<128, 128, false, false>"},
-        {"gemm_kernel<128, 64, true, true>", "gemm_kernel<128, 64, true, false>", "gemm_kernel<128, 64, false, false>"},
-        {"gemm_kernel<64, 64, true, true>", "gemm_kernel<64, 64, true, false>", "gemm_kernel<64, 64, false, false>"}};
-    static const char *fold_names[3][3] = {
-        {"", "gemm_fold_kernel<128, 128, true, false>", "gemm_fold_kernel<128, 128, false, false>"},
-        {"", "gemm_fold_kernel<128, 64, true, false>", "gemm_fold_kernel<128, 64, false, false>"},
-        {"", "gemm_fold_kernel<64, 64, true, false>", "gemm_fold_kernel<64, 64, false, false>"}};
-    static const int bm[3] = {128, 128, 64};
-    int t = d.tile >= 1 && d.tile <= 3 ? d.tile - 1 : 0;
-    int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
-    // causal products with a growing or shrinking K range run with folded row tiles
-    if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];
-    return names[t][l];
-}
-
 // "kernel<hd>" as a kernel-trace profiler shows the fused attention kernels
 // (static strings: profile records keep the pointer).
 enum { FL_FWD = 0, FL_DKDV = 1 };
@@ -502,7 +477,7 @@ hipError_t gemm_run(const GemmDesc &d, hipStream_t s, const char *site = nullptr
         if (d.epi == EPI_ACCUM || d.epi == EPI_RESID || d.epi == EPI_GELU || d.epi == EPI_GELU_BWD) out *= 2;
         bytes = 4.0 * nb * ((double)d.M * d.K + (double)d.K * d.N + out);
     }
-    return timed(gemm_name(d), flops, bytes, [&]() { return gemm_launch(d, s); });
+    return timed(gemm_kernel_name(d), flops, bytes, [&]() { return gemm_launch(d, s); });
 }
 
 // ---------------------------------------------------------------- building blocks
@@ -614,7 +589,7 @@ hipError_t linear_bwd(float *dinp, int epi, const float *aux, float *dW, float *
     double f1, b1, f2, b2;
     gemm_cost(dd, f1, b1);
     gemm_cost(di, f2, b2);
-    hipError_t e = timed(gemm_pair_name(pp.tile), f1 + f2, b1 + b2, [&]() { return gemm_launch_pair(dd, di, s); });
+    hipError_t e = timed(gemm_pair_kernel_name(pp.tile), f1 + f2, b1 + b2, [&]() { return gemm_launch_pair(dd, di, s); });
     if (e == hipSuccess && !defer_dw_sum) e = dw_finish(dW, dbias, splitk_dw, dbias_ws, K, OC, pp.ks_dw, s);
     if (e == hipSuccess) e = dinp_finish(dinp, splitk_dinp, N, K, pp.ks_dinp, s);
     return e;
