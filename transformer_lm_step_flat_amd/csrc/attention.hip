@@ -54,28 +54,34 @@ constexpr float LN2 = 0.6931471805599453f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Load `rows` rows of HD floats (row stride `rs` floats, rows >= nvalid are
-// zero) into registers: thread tid owns float4 number tid + 256*i.
+// zero) into registers: thread tid owns float4 number tid + 256*i.  The loads
+// are issued unconditionally (a thread out of range reads row 0, which is
+// always valid) and the zeroing is applied when the tile is stored, so that
+// nothing waits for the loads until then: the next tile is in flight while
+// the current one is consumed.
 template <int HD, int ROWS>
 struct TileLoader {
     static constexpr int F4 = ROWS * HD / 4 / 256 > 0 ? ROWS * HD / 4 / 256 : 1;
     floatx4 r[F4];
+    bool ok[F4];
     __device__ __forceinline__ void load(const float *base, long long rs, int row0, int nrows, int tid) {
 #pragma unroll
         for (int i = 0; i < F4; i++) {
-            // branch-free: out-of-range threads read row 0 (always valid) and keep zeros
             const int f = tid + 256 * i;
             const int row = f / (HD / 4), c4 = f % (HD / 4);
-            const bool ok = f < ROWS * HD / 4 && row0 + row < nrows;
-            const floatx4 v = *(const floatx4 *)(base + (ok ? (long long)(row0 + row) * rs + 4 * c4 : 0));
-            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-            r[i] = ok ? v : z;
+            ok[i] = f < ROWS * HD / 4 && row0 + row < nrows;
+            r[i] = *(const floatx4 *)(base + (ok[i] ? (long long)(row0 + row) * rs + 4 * c4 : 0));
         }
+    }
+    __device__ __forceinline__ floatx4 value(int i) const {
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+        return ok[i] ? r[i] : z;
     }
     __device__ __forceinline__ void store(float *lds, int pitch, int tid) const {
 #pragma unroll
         for (int i = 0; i < F4; i++) {
             int f = tid + 256 * i;
-            if (f < ROWS * HD / 4) *(floatx4 *)&lds[(f / (HD / 4)) * pitch + 4 * (f % (HD / 4))] = r[i];
+            if (f < ROWS * HD / 4) *(floatx4 *)&lds[(f / (HD / 4)) * pitch + 4 * (f % (HD / 4))] = value(i);
         }
     }
     // The same tile transposed, [HD][pitch] (row index contiguous), so that
@@ -86,8 +92,9 @@ struct TileLoader {
             int f = tid + 256 * i;
             if (f < ROWS * HD / 4) {
                 const int row = f / (HD / 4), c = 4 * (f % (HD / 4));
+                const floatx4 v = value(i);
 #pragma unroll
-                for (int e = 0; e < 4; e++) lds[(c + e) * pitch + row] = r[i][e];
+                for (int e = 0; e < 4; e++) lds[(c + e) * pitch + row] = v[e];
             }
         }
     }
@@ -167,38 +174,60 @@ __device__ __forceinline__ void store_rows_t(float *dst, long long rs, int nrows
     }
 }
 
-// ------------------------------------------------------------------ work split
+// ------------------------------------------------------------------ work split (forward)
 //
 // Long causal rows are split so that no workgroup walks more than a few
-// blocks in sequence.  Forward: a workgroup takes 128 queries and one
-// chunk of at most 256 of the keys they need; dk/dv: 128 keys and one chunk of
-// at most 256 of the queries that see them.  A block whose range fits in one
+// blocks in sequence: a forward workgroup takes 128 queries and one chunk of
+// at most KCH of the keys they need.  A query block whose keys fit in one
 // chunk writes its result directly; otherwise each chunk writes a partial
-// (normalised output and log-sum-exp, or a gradient sum) to a workspace and a
-// combine kernel merges the chunks in order.
+// (normalised output and log-sum-exp) to a workspace and a combine kernel
+// merges the chunks in order.  (The dk/dv kernel splits its work differently;
+// see there.)
 
 constexpr int QBLK = QW * NWAVE;  // rows of a workgroup: 128
-constexpr int KCH = 256;          // keys per chunk (forward)
-constexpr int QCH = 256;          // queries per chunk (dk/dv)
+constexpr int KCH = 256;          // keys per chunk
 
 __host__ __device__ inline int q_items(int qb, int T) {
     const int kend = min(T, (qb + 1) * QBLK);
     return (kend + KCH - 1) / KCH;
 }
-__host__ __device__ inline int k_items(int kb, int T) { return (T - kb * QBLK + QCH - 1) / QCH; }
+// chunks of query block qb that hold KCH keys (only the last can hold fewer)
+__host__ __device__ inline int full_chunks(int qb, int T) { return min(T, (qb + 1) * QBLK) / KCH; }
 
-// block index and chunk of workgroup x; `first` = item index of the block's chunk 0
-template <bool KEYS>
-__device__ __forceinline__ void decode_item(int x, int T, int &blk, int &chunk, int &first) {
-    blk = 0;
-    first = 0;
-    for (;;) {
-        const int n = KEYS ? k_items(blk, T) : q_items(blk, T);
-        if (x < first + n) break;
-        first += n;
-        blk++;
+// Work order: workgroup g of the one-dimensional grid takes first the full
+// chunks of every (batch, head) in turn, then the shorter last chunks, so
+// that the short ones fill the end of the launch.  Returns the (batch, head)
+// index, the query block, the chunk and `first` = the item index of the
+// block's chunk 0 (items numbered block by block within a (batch, head)).
+__device__ __forceinline__ int decode_item(int g, int T, int &blk, int &chunk, int &first) {
+    int nfull = 0, items = 0;
+    for (int b = 0; b * QBLK < T; b++) {
+        nfull += full_chunks(b, T);
+        items += q_items(b, T);
     }
-    chunk = x - first;
+    const int npart = items - nfull, BH = gridDim.x / items;
+    int bh, j;
+    const bool full = g < BH * nfull;
+    if (full) {
+        bh = g / nfull;
+        j = g % nfull;
+    } else {
+        bh = (g - BH * nfull) / npart;
+        j = (g - BH * nfull) % npart;
+    }
+    first = 0;
+    for (blk = 0;; blk++) {
+        const int n = q_items(blk, T), f = full_chunks(blk, T);
+        if (full) {
+            if (j < f) { chunk = j; break; }
+            j -= f;
+        } else if (n > f) {
+            if (j == 0) { chunk = n - 1; break; }
+            j--;
+        }
+        first += n;
+    }
+    return bh;
 }
 
 // ------------------------------------------------------------------ forward
@@ -215,9 +244,9 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
     __shared__ __attribute__((aligned(16))) float Ks[KS];
     __shared__ __attribute__((aligned(16))) float Vs[VS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
-    const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
     int qb, chunk, first;
-    decode_item<false>(blockIdx.x, T, qb, chunk, first);
+    const int bh = decode_item(blockIdx.x, T, qb, chunk, first);
+    const int b = bh / NH, hd_off = (bh % NH) * HD;
     const int nch = q_items(qb, T);
     const int q0 = qb * QBLK;
     const int tq0 = q0 + wave * QW, t = tq0 + l32;
@@ -339,6 +368,39 @@ __global__ __launch_bounds__(256) void flash_fwd_merge_kernel(float *__restrict_
 }
 
 // ------------------------------------------------------------------ backward: dk and dv
+//
+// Work split: the (batch, head, key block, query block) iterations are
+// numbered key block by key block (128 keys, then its query blocks of TB
+// from the block's diagonal on), (batch, head) after (batch, head), and the
+// G workgroups (as many as can be resident) take equal contiguous ranges of
+// them, so that all finish together.  A range is walked as segments, one per
+// key block it touches.  A segment that covers all of its key block's query
+// blocks writes dk and dv directly; otherwise it writes a partial sum to one
+// of two slots of its workgroup (slot 0 for the segment that starts the
+// range, slot 1 for the one that ends it), and flash_bwd_sum_kernel adds the
+// partials of each split key block in workgroup order.
+
+__host__ __device__ inline int kq_blocks(int kb, int T) { return (T - kb * QBLK + TB - 1) / TB; }
+// first iteration of key block kb within a (batch, head)
+__host__ __device__ inline int kq_start(int kb, int T) {
+    int n = 0;
+    for (int k = 0; k < kb; k++) n += kq_blocks(k, T);
+    return n;
+}
+// range of workgroup g: [lo(g), lo(g + 1)) with lo(g) = g W / G
+__host__ __device__ inline long long range_lo(long long g, long long W, long long G) { return g * W / G; }
+// the workgroup whose range holds iteration i
+__host__ __device__ inline long long range_of(long long i, long long W, long long G) { return ((i + 1) * G - 1) / W; }
+
+// Logical workgroup of launch slot bid: workgroups are handed to the 8 XCDs
+// round-robin, and each XCD gets one contiguous run of logical indices, so
+// that neighbouring ranges (the same heads) share that XCD's L2.
+__device__ __forceinline__ int xcd_run(int bid, int n) {
+    const int X = 8;
+    const int q = n / X, r = n % X;
+    const int x = bid % X, loc = bid / X;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + loc;
+}
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv, float *__restrict__ ws,
@@ -347,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                                                                 const float *__restrict__ qkv,
                                                                 const float *__restrict__ lse,
                                                                 const float *__restrict__ Dbuf, int T, int C, int NH,
-                                                                int items, float scale) {
+                                                                int BH, float scale) {
     constexpr int P = HD + 4;
     constexpr int PT = TB + 4;
     __shared__ __attribute__((aligned(16))) float Qs[TB * P];
@@ -356,140 +418,157 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
     __shared__ __attribute__((aligned(16))) float Ot[HD * PT];
     __shared__ float Ls[TB], Ds[TB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
-    const int bh = blockIdx.y, b = bh / NH, hd_off = (bh % NH) * HD;
-    int kb, chunk, first;
-    decode_item<true>(blockIdx.x, T, kb, chunk, first);
-    const int nch = k_items(kb, T);
-    const int u0w = kb * QBLK;
-    const int u0 = u0w + wave * QW, u = u0 + l32;
+    const int G = gridDim.x, g = xcd_run(blockIdx.x, G);
+    const int nkb = (T + QBLK - 1) / QBLK, W1 = kq_start(nkb, T);
+    const long long W = (long long)BH * W1;
+    const long long lo_g = range_lo(g, W, G), hi_g = range_lo(g + 1, W, G);
     const long long rs = 3LL * C;
-    const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
-    const float *dob = dout + (long long)b * T * C + hd_off;
+    for (long long it = lo_g; it < hi_g;) {
+        const int bh = (int)(it / W1), rem = (int)(it % W1);
+        int kb = 0;
+        while (kb + 1 < nkb && kq_start(kb + 1, T) <= rem) kb++;
+        const int qfirst = rem - kq_start(kb, T), nq = kq_blocks(kb, T);
+        const int qend = (int)min((long long)nq, qfirst + (hi_g - it));
+        const bool whole = qfirst == 0 && qend == nq;
+        const int slot = 2 * g + (it == lo_g ? 0 : 1);
+        it += qend - qfirst;
+        const int b = bh / NH, hd_off = (bh % NH) * HD;
+        const int u0w = kb * QBLK;
+        const int u0 = u0w + wave * QW, u = u0 + l32;
+        const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
+        const float *dob = dout + (long long)b * T * C + hd_off;
 
-    float kf[HD / 2], vf[HD / 2];
-#pragma unroll
-    for (int j4 = 0; j4 < HD / 8; j4++) {
-        const bool ok = u < T;
-        floatx4 k = ok ? *(const floatx4 *)(qb_ptr + C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-        floatx4 v = ok ? *(const floatx4 *)(qb_ptr + 2 * C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            kf[4 * j4 + e] = k[e] * (scale * LOG2E);
-            vf[4 * j4 + e] = v[e];
+        float kf[HD / 2], vf[HD / 2];
+    #pragma unroll
+        for (int j4 = 0; j4 < HD / 8; j4++) {
+            const bool ok = u < T;
+            floatx4 k = ok ? *(const floatx4 *)(qb_ptr + C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 v = ok ? *(const floatx4 *)(qb_ptr + 2 * C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+            for (int e = 0; e < 4; e++) {
+                kf[4 * j4 + e] = k[e] * (scale * LOG2E);
+                vf[4 * j4 + e] = v[e];
+            }
         }
-    }
-    floatx16 dk[HeadBlocks<HD>::N], dv[HeadBlocks<HD>::N];
-#pragma unroll
-    for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) dk[nd] = dv[nd] = zero16();
+        floatx16 dk[HeadBlocks<HD>::N], dv[HeadBlocks<HD>::N];
+    #pragma unroll
+        for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) dk[nd] = dv[nd] = zero16();
 
-    const int tc0 = u0w + chunk * QCH, tc1 = min(T, tc0 + QCH);
-    TileLoader<HD, TB> lq, lo;
-    lq.load(qb_ptr, rs, tc0, T, tid);
-    lo.load(dob, C, tc0, T, tid);
-    for (int t0 = tc0; t0 < tc1; t0 += TB) {
-        __syncthreads();
-        lq.store(Qs, P, tid);
-        lo.store(Os, P, tid);
-        lq.store_t(Qt, PT, tid);
-        lo.store_t(Ot, PT, tid);
-        if (tid < TB) {
-            Ls[tid] = t0 + tid < T ? lse[(long long)bh * T + t0 + tid] * LOG2E : 0.0f;
-            Ds[tid] = t0 + tid < T ? Dbuf[(long long)bh * T + t0 + tid] : 0.0f;
-        }
-        __syncthreads();
-        if (t0 + TB < tc1) {
-            lq.load(qb_ptr, rs, t0 + TB, T, tid);
-            lo.load(dob, C, t0 + TB, T, tid);
-        }
-        if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
-            if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
+        const int tc0 = u0w + qfirst * TB, tc1 = min(T, u0w + qend * TB);
+        TileLoader<HD, TB> lq, lo;
+        // lse and D of the block's queries (threads tid < TB), loaded with the tiles
+        const float *lse_bh = lse + (long long)bh * T, *D_bh = Dbuf + (long long)bh * T;
+        float lse_next = 0.0f, d_next = 0.0f;
+        bool ld_ok = false;
+        auto load_rows = [&](int t0) {
+            lq.load(qb_ptr, rs, t0, T, tid);
+            lo.load(dob, C, t0, T, tid);
+            ld_ok = tid < TB && t0 + tid < T;
+            lse_next = lse_bh[ld_ok ? t0 + tid : 0];
+            d_next = D_bh[ld_ok ? t0 + tid : 0];
+        };
+        load_rows(tc0);
+        for (int t0 = tc0; t0 < tc1; t0 += TB) {
+            __syncthreads();
+            lq.store(Qs, P, tid);
+            lo.store(Os, P, tid);
+            lq.store_t(Qt, PT, tid);
+            lo.store_t(Ot, PT, tid);
+            if (tid < TB) {
+                Ls[tid] = ld_ok ? lse_next * LOG2E : 0.0f;
+                Ds[tid] = ld_ok ? d_next : 0.0f;
+            }
+            __syncthreads();
+            if (t0 + TB < tc1) load_rows(t0 + TB);
+            if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
+                if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
+                    float *dsb = dsout + (long long)bh * T * T;
+    #pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int tt = t0 + row_of(r, h);
+                        if (tt < T && u < T) dsb[(long long)tt * T + u] = 0.0f;
+                    }
+                }
+                continue;
+            }
+            floatx16 s = zero16(), dp = zero16();
+    #pragma unroll
+            for (int j4 = 0; j4 < HD / 8; j4++) {
+                floatx4 qa = *(const floatx4 *)&Qs[l32 * P + h * (HD / 2) + 4 * j4];
+                floatx4 oa = *(const floatx4 *)&Os[l32 * P + h * (HD / 2) + 4 * j4];
+    #pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], kf[4 * j4 + e], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[e], vf[4 * j4 + e], dp, 0, 0, 0);
+                }
+            }
+            if (t0 < u0 + QW - 1 || t0 + TB > T || u0 + QW > T) {  // crosses the diagonal or an end: mask
+    #pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int tl = row_of(r, h), tt = t0 + tl;
+                    const float p = (tt < u || tt >= T || u >= T) ? 0.0f : exp2_fast(s[r] - Ls[tl]);
+                    s[r] = p;                      // p
+                    dp[r] = p * (dp[r] - Ds[tl]);  // ds
+                }
+            } else {
+    #pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int tl = row_of(r, h);
+                    const float p = exp2_fast(s[r] - Ls[tl]);
+                    s[r] = p;
+                    dp[r] = p * (dp[r] - Ds[tl]);
+                }
+            }
+            {  // ds[t][u] for the dq product (a row of 32 keys per register: coalesced)
                 float *dsb = dsout + (long long)bh * T * T;
-#pragma unroll
+    #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int tt = t0 + row_of(r, h);
-                    if (tt < T && u < T) dsb[(long long)tt * T + u] = 0.0f;
+                    if (tt < T && u < T) dsb[(long long)tt * T + u] = dp[r];
                 }
             }
-            continue;
+            // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
+            // the transposed tiles per 4 MFMAs
+    #pragma unroll
+            for (int g = 0; g < 4; g++)
+    #pragma unroll
+                for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
+                    const int d = 32 * nd + l32;
+                    const floatx4 ob = d < HD ? *(const floatx4 *)&Ot[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
+                    const floatx4 qv = d < HD ? *(const floatx4 *)&Qt[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        dv[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[4 * g + i], ob[i], dv[nd], 0, 0, 0);
+                        dk[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(dp[4 * g + i], qv[i], dk[nd], 0, 0, 0);
+                    }
+                }
         }
-        floatx16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int j4 = 0; j4 < HD / 8; j4++) {
-            floatx4 qa = *(const floatx4 *)&Qs[l32 * P + h * (HD / 2) + 4 * j4];
-            floatx4 oa = *(const floatx4 *)&Os[l32 * P + h * (HD / 2) + 4 * j4];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], kf[4 * j4 + e], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[e], vf[4 * j4 + e], dp, 0, 0, 0);
-            }
-        }
-        if (t0 < u0 + QW - 1 || t0 + TB > T || u0 + QW > T) {  // crosses the diagonal or an end: mask
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int tl = row_of(r, h), tt = t0 + tl;
-                const float p = (tt < u || tt >= T || u >= T) ? 0.0f : exp2_fast(s[r] - Ls[tl]);
-                s[r] = p;                      // p
-                dp[r] = p * (dp[r] - Ds[tl]);  // ds
-            }
+        // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
+        float *dkb, *dvb;
+        long long krs;
+        if (whole) {
+            dkb = dqkv + (long long)b * T * rs + C + hd_off;
+            dvb = dqkv + (long long)b * T * rs + 2 * C + hd_off;
+            krs = rs;
         } else {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int tl = row_of(r, h);
-                const float p = exp2_fast(s[r] - Ls[tl]);
-                s[r] = p;
-                dp[r] = p * (dp[r] - Ds[tl]);
-            }
+            dkb = ws + (long long)slot * 2 * QBLK * HD - (long long)u0w * HD;  // rows indexed by the key u
+            dvb = dkb + QBLK * HD;
+            krs = HD;
         }
-        {  // ds[t][u] for the dq product (a row of 32 keys per register: coalesced)
-            float *dsb = dsout + (long long)bh * T * T;
-#pragma unroll
+    #pragma unroll
+        for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
+            const int d = 32 * nd + l32;
+            if (d >= HD) continue;
+    #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int tt = t0 + row_of(r, h);
-                if (tt < T && u < T) dsb[(long long)tt * T + u] = dp[r];
-            }
-        }
-        // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
-        // the transposed tiles per 4 MFMAs
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-#pragma unroll
-            for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
-                const int d = 32 * nd + l32;
-                const floatx4 ob = d < HD ? *(const floatx4 *)&Ot[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
-                const floatx4 qv = d < HD ? *(const floatx4 *)&Qt[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    dv[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[4 * g + i], ob[i], dv[nd], 0, 0, 0);
-                    dk[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(dp[4 * g + i], qv[i], dk[nd], 0, 0, 0);
+                const int uu = u0 + row_of(r, h);
+                if (uu < T) {
+                    dkb[(long long)uu * krs + d] = dk[nd][r] * scale;
+                    dvb[(long long)uu * krs + d] = dv[nd][r];
                 }
             }
-    }
-    // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
-    float *dkb, *dvb;
-    long long krs;
-    if (nch == 1) {
-        dkb = dqkv + (long long)b * T * rs + C + hd_off;
-        dvb = dqkv + (long long)b * T * rs + 2 * C + hd_off;
-        krs = rs;
-    } else {
-        const long long item = (long long)bh * items + first + chunk;
-        dkb = ws + item * 2 * QBLK * HD - (long long)u0w * HD;  // rows indexed by the key u
-        dvb = dkb + QBLK * HD;
-        krs = HD;
-    }
-#pragma unroll
-    for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
-        const int d = 32 * nd + l32;
-        if (d >= HD) continue;
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int uu = u0 + row_of(r, h);
-            if (uu < T) {
-                dkb[(long long)uu * krs + d] = dk[nd][r] * scale;
-                dvb[(long long)uu * krs + d] = dv[nd][r];
-            }
         }
-    }
+    }  // segments
 }
 
 // D[bh][t] = dO_t . O_t over the head's HD dims, one thread per (b, t, head):
@@ -514,30 +593,32 @@ __global__ __launch_bounds__(256) void flash_bwd_D_kernel(float *__restrict__ Db
     Dbuf[(b * NH + hh) * T + t] = acc;
 }
 
-// Sum the chunk partials of dk and dv into dqkv, chunks in order.  One
-// thread per (key row, 4 head dims) of the key blocks that were split.
+// Sum the partials of dk and dv of the key blocks that were split between
+// workgroups into dqkv, in workgroup order.  One thread per (key row, 4 head
+// dims); rows of key blocks that one workgroup covered are left alone.
 template <int HD>
 __global__ __launch_bounds__(256) void flash_bwd_sum_kernel(float *__restrict__ dqkv, const float *__restrict__ ws,
-                                                            int T, int C, int NH, int BNH, int items) {
+                                                            int T, int C, int NH, int BH, int G) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const int d4 = (int)(i % (HD / 4));
     const long long r = i / (HD / 4);
     const int t = (int)(r % T), bh = (int)(r / T);
-    if (bh >= BNH) return;
-    const int blk = t / QBLK, nch = k_items(blk, T);
-    if (nch == 1) return;  // written directly by the chunk kernel
-    int first = 0;
-    for (int q = 0; q < blk; q++) first += k_items(q, T);
-    const long long base = (long long)bh * items + first;
+    if (bh >= BH) return;
+    const int kb = t / QBLK, nkb = (T + QBLK - 1) / QBLK;
+    const long long W1 = kq_start(nkb, T), W = BH * W1;
+    const long long S = bh * W1 + kq_start(kb, T), E = S + kq_blocks(kb, T);
+    const long long ga = range_of(S, W, G), gb = range_of(E - 1, W, G);
+    if (ga == gb) return;  // written directly
     const int row = t % QBLK;
-    const long long rs = 3LL * C;
-    const int b = bh / NH, hd_off = (bh % NH) * HD;
     floatx4 ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nch; c++) {
-        const float *p = ws + (base + c) * 2 * QBLK * HD + (long long)row * HD + 4 * d4;
+    for (long long g = ga; g <= gb; g++) {
+        const long long slot = 2 * g + (range_lo(g, W, G) >= S ? 0 : 1);
+        const float *p = ws + slot * 2 * QBLK * HD + (long long)row * HD + 4 * d4;
         ak += *(const floatx4 *)p;
         av += *(const floatx4 *)(p + QBLK * HD);
     }
+    const long long rs = 3LL * C;
+    const int b = bh / NH, hd_off = (bh % NH) * HD;
     *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + C + hd_off + 4 * d4) = ak;
     *(floatx4 *)(dqkv + ((long long)b * T + t) * rs + 2 * C + hd_off + 4 * d4) = av;
 }
@@ -545,18 +626,19 @@ __global__ __launch_bounds__(256) void flash_bwd_sum_kernel(float *__restrict__ 
 // floats of the ds matrices at the start of the backward workspace (256-byte aligned)
 size_t ds_floats(int B, int T, int NH) { return ((size_t)B * NH * T * T + 63) / 64 * 64; }
 
-int total_items(bool keys, int T) {
+// forward items (query block chunks) of one (batch, head)
+int total_items(int T) {
     int n = 0;
-    for (int blk = 0; blk * QBLK < T; blk++) n += keys ? k_items(blk, T) : q_items(blk, T);
+    for (int blk = 0; blk * QBLK < T; blk++) n += q_items(blk, T);
     return n;
 }
 
 template <int HD>
 hipError_t launch_fwd(float *out, float *lse, float *ws, const float *qkv, int B, int T, int C, int NH,
                       hipStream_t s) {
-    const int items = total_items(false, T);
+    const int items = total_items(T);
     float *wlse = ws + (size_t)B * NH * items * QBLK * HD;
-    hipLaunchKernelGGL(flash_fwd_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, out, lse, ws, wlse, qkv, T, C,
+    hipLaunchKernelGGL(flash_fwd_kernel<HD>, dim3(items * B * NH), dim3(256), 0, s, out, lse, ws, wlse, qkv, T, C,
                        NH, items, 1.0f / sqrtf((float)HD));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || items == (T + QBLK - 1) / QBLK) return e;  // nothing was split
@@ -564,6 +646,14 @@ hipError_t launch_fwd(float *out, float *lse, float *ws, const float *qkv, int B
     hipLaunchKernelGGL(flash_fwd_merge_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, lse, ws,
                        wlse, T, C, NH, B * NH, items);
     return hipGetLastError();
+}
+
+// Workgroups of the dk/dv kernel: as many as are resident at once (256 CUs,
+// two per CU by its register use), at most one per iteration.
+int dkdv_groups(int B, int T, int NH, int hd) {
+    const long long W = (long long)B * NH * kq_start((T + QBLK - 1) / QBLK, T);
+    const long long cap = 256LL * 2;
+    return (int)(W < cap ? W : cap);
 }
 
 template <int HD>
@@ -574,15 +664,15 @@ hipError_t launch_bwd_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dou
                        out, T, C, NH, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int items = total_items(true, T);
+    const int G = dkdv_groups(B, T, NH, HD);
     float *ds = ws, *kvws = ws + ds_floats(B, T, NH);
-    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, dim3(items, B * NH), dim3(256), 0, s, dqkv, kvws, ds, dout, qkv,
-                       lse, (const float *)Dbuf, T, C, NH, items, 1.0f / sqrtf((float)HD));
+    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, dim3(G), dim3(256), 0, s, dqkv, kvws, ds, dout, qkv, lse,
+                       (const float *)Dbuf, T, C, NH, B * NH, 1.0f / sqrtf((float)HD));
     e = hipGetLastError();
-    if (e != hipSuccess || items == (T + QBLK - 1) / QBLK) return e;
+    if (e != hipSuccess) return e;
     const long long n = (long long)B * NH * T * (HD / 4);
     hipLaunchKernelGGL((flash_bwd_sum_kernel<HD>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dqkv,
-                       (const float *)kvws, T, C, NH, B * NH, items);
+                       (const float *)kvws, T, C, NH, B * NH, G);
     return hipGetLastError();
 }
 
@@ -592,8 +682,8 @@ bool flash_attention_supported(int hd) { return hd == 16 || hd == 32 || hd == 64
 
 size_t flash_attention_work(int B, int T, int C, int NH) {
     const int hd = C / NH;
-    const size_t fq = (size_t)B * NH * total_items(false, T) * QBLK * (hd + 1);
-    const size_t kv = ds_floats(B, T, NH) + (size_t)B * NH * total_items(true, T) * QBLK * 2 * hd;
+    const size_t fq = (size_t)B * NH * total_items(T) * QBLK * (hd + 1);
+    const size_t kv = ds_floats(B, T, NH) + (size_t)2 * dkdv_groups(B, T, NH, hd) * QBLK * 2 * hd;
     return fq > kv ? fq : kv;
 }
 
