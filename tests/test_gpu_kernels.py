@@ -152,7 +152,10 @@ def test_attention(g, oracle_lib, B, T, C, NH):
 
 
 FLASH_SHAPES = [(2, 64, 64, 4), (1, 100, 48, 3), (2, 256, 128, 2), (1, 132, 128, 8), (3, 20, 96, 3),
-                (1, 260, 128, 2), (2, 4, 64, 1), (1, 700, 128, 2), (1, 1024, 64, 1)]
+                (1, 260, 128, 2), (2, 4, 64, 1), (1, 700, 128, 2), (1, 1024, 64, 1),
+                # more dk/dv iterations than resident workgroups: ranges that cross
+                # key blocks and (batch, head) boundaries
+                (2, 520, 768, 12)]
 
 
 @pytest.mark.parametrize("B,T,C,NH", FLASH_SHAPES)
