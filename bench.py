@@ -195,6 +195,33 @@ def sq_summary(sq_csv: str, command: str, config: str):
             print(f"| `{k}` | {n} | {ms:.4f} | {ghz:.2f} | {100 * fr:.1f}% | {mi:.3g} |")
 
 
+def measured_peaks(torch, gpt2, copy_mib=1024, reps=5):
+    """The fp32 matrix-core rate (calibration kernel of back-to-back MFMAs on
+    every CU) and the HBM copy rate (copy_mib MiB read and written) this
+    device reaches, best of `reps` timed launches each."""
+    out = torch.zeros(1, device="cuda")
+    n = copy_mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_mfma, best_copy = 0.0, 0.0
+    gpt2.probe_mfma(out, 200)
+    gpt2.probe_copy(dst, src)
+    for _ in range(reps):
+        e0.record()
+        flops = gpt2.probe_mfma(out, 2000)
+        e1.record()
+        torch.cuda.synchronize()
+        best_mfma = max(best_mfma, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        e0.record()
+        gpt2.probe_copy(dst, src)
+        e1.record()
+        torch.cuda.synchronize()
+        best_copy = max(best_copy, 8.0 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return {"mfma_fp32_tflops": best_mfma, "hbm_copy_gbs": best_copy, "copy_mib": copy_mib}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,18 +278,28 @@ def main():
     M.sync()
     log(f"warmup done ({args.warmup} steps)")
 
-    # timed region: no instrumentation
+    # timed region: no instrumentation but one event between steps on the step's stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    evs[0].record()
     for i in range(args.steps):
         step(args.warmup + i)
+        evs[i + 1].record()
     torch.cuda.synchronize()
     dt_s = time.perf_counter() - t0
     M.sync()
     loss = float(M.act("loss")[0].item())
     ms = dt_s / args.steps * 1e3
     tok_s = B * T * args.steps / dt_s
-    log(f"timed {args.steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, last loss {loss:.4f}")
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    step_ms = {"mean": sum(per_step) / len(per_step), "median": per_step[len(per_step) // 2],
+               "min": per_step[0], "max": per_step[-1]}
+    log(f"timed {args.steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, last loss {loss:.4f} "
+        f"(per step: median {step_ms['median']:.2f}, min {step_ms['min']:.2f}, max {step_ms['max']:.2f} ms)")
+    peaks = measured_peaks(torch, gpt2)
+    log(f"measured on this device: fp32 matrix-core {peaks['mfma_fp32_tflops']:.1f} TFLOP/s, "
+        f"HBM copy {peaks['hbm_copy_gbs']:.0f} GB/s")
 
     # the same steps again, each launch bracketed by HIP events on the step's stream
     kernels, roofline, ms_ev, sites = [], None, None, []
@@ -318,7 +355,9 @@ def main():
                     "kernel": d["name"], "avg_launch_ms": avg_ms, "launches_per_step": d["launches"] / args.steps,
                     "algorithmic_per_launch": per_launch,
                     "step_flops": all_flops,
-                    "step_mfma_frac": all_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP32_TFLOPS}
+                    "step_mfma_frac": all_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP32_TFLOPS,
+                    "frac_of_measured_peak": achieved / (peaks["mfma_fp32_tflops"] if bound == "mfma"
+                                                         else peaks["hbm_copy_gbs"])}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -347,6 +386,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "last_loss": loss,
+        "step_ms": step_ms,
+        "measured_peaks": peaks,
         "ms_per_step_with_events": ms_ev,
         "kernels": kernels[:16],
     }

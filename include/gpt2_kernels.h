@@ -97,6 +97,18 @@ gpt2_status gpt2k_encoder_backward(float *dwte, float *dwpe, const float *dout, 
 gpt2_status gpt2k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float beta1,
                         float beta2, float eps, float weight_decay, int t, void *stream);
 
+/* Calibration of the measurement (not a step of the training path): the
+ * rates this device reaches, reported beside the vendor peaks.
+ * gpt2k_probe_mfma launches one workgroup of 16 wavefronts per CU, each
+ * running iters x 32 fp32 32x32x2 matrix instructions on register operands;
+ * `out` is one device float (never written in practice), *flops (a HOST
+ * double, may be NULL) receives the floating-point work launched; time the
+ * call with events on `stream`.  gpt2k_probe_copy copies n floats
+ * (n % 4 == 0, 16-byte aligned) with streaming loads and stores; a copy of
+ * n floats moves 8n bytes.  GPT2_EINVAL for iters < 1 or a bad size. */
+gpt2_status gpt2k_probe_mfma(float *out, int iters, double *flops, void *stream);
+gpt2_status gpt2k_probe_copy(float *dst, const float *src, size_t n, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -362,3 +362,25 @@ def test_adamw(g, oracle_lib):
     assert rel(host(dv), rv) < 1e-6
     assert rel(host(dp) - p, rp - p) < 1e-5
     assert rel(host(dp), rp) < 1e-6
+
+
+# ---------------------------------------------------------------- calibration kernels of the measurement
+
+def test_probes(g):
+    """The copy probe copies exactly (ragged tail of the last workgroup); the
+    matrix-core probe runs and reports its work; bad sizes are rejected."""
+    import torch
+    rng = np.random.default_rng(11)
+    n = 4 * 1000 + 4 * 257
+    src = f32(rng, n)
+    dst = torch.zeros(n, device="cuda")
+    g.probe_copy(dst, dev(src))
+    assert np.array_equal(host(dst), src)
+    out = torch.zeros(1, device="cuda")
+    flops = g.probe_mfma(out, 3)
+    torch.cuda.synchronize()
+    assert flops > 0 and float(out.item()) == 0.0
+    with pytest.raises(g.Gpt2Error):
+        g.probe_mfma(out, 0)
+    with pytest.raises(g.Gpt2Error):
+        g.probe_copy(dst[:6], dev(src)[:6])

@@ -27,6 +27,7 @@
 #include "attention.h"
 #include "common.h"
 #include "gemm.h"
+#include "probe.h"
 #include "kernels.h"
 
 namespace {
@@ -1194,6 +1195,16 @@ gpt2_status gpt2k_adamw(float *params, const float *grads, float *m, float *v, s
     double c1 = 1.0 - std::pow((double)beta1, t), c2 = 1.0 - std::pow((double)beta2, t);
     KCK(k_adamw(params, grads, m, v, n, lr, beta1, beta2, eps, weight_decay, (float)c1, (float)c2,
                 (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_probe_mfma(float *out, int iters, double *flops, void *stream) {
+    KCK(probe_mfma(out, iters, (hipStream_t)stream, flops));
+    return GPT2_OK;
+}
+
+gpt2_status gpt2k_probe_copy(float *dst, const float *src, size_t n, void *stream) {
+    KCK(probe_copy(dst, src, n, (hipStream_t)stream));
     return GPT2_OK;
 }
 

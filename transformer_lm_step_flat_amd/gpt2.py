@@ -82,6 +82,8 @@ _SIGS = {
     "gpt2k_token_order": [_P, _P, _P, _P, _I, _I, _P],
     "gpt2k_encoder_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
     "gpt2k_adamw": [_P, _P, _P, _P, _Z, _F, _F, _F, _F, _F, _I, _P],
+    "gpt2k_probe_mfma": [_P, _I, ctypes.POINTER(ctypes.c_double), _P],
+    "gpt2k_probe_copy": [_P, _P, _Z, _P],
 }
 _SIZE_FNS = {
     "gpt2k_linear_backward_work": [_I, _I, _I],
@@ -358,3 +360,14 @@ def encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V):
 def adamw(params, grads, m, v, lr, b1, b2, eps, wd, t):
     _check(lib().gpt2k_adamw(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), params.numel(), lr, b1, b2, eps, wd, t,
                              _s()))
+
+
+def probe_mfma(out, iters):
+    """Launch the matrix-core calibration kernel; returns the FLOPs it does."""
+    flops = ctypes.c_double(0.0)
+    _check(lib().gpt2k_probe_mfma(_ptr(out), iters, ctypes.byref(flops), _s()))
+    return flops.value
+
+
+def probe_copy(dst, src):
+    _check(lib().gpt2k_probe_copy(_ptr(dst), _ptr(src), src.numel(), _s()))
