@@ -439,19 +439,19 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         const float *dob = dout + (long long)b * T * C + hd_off;
 
         float kf[HD / 2], vf[HD / 2];
-    #pragma unroll
+#pragma unroll
         for (int j4 = 0; j4 < HD / 8; j4++) {
             const bool ok = u < T;
             floatx4 k = ok ? *(const floatx4 *)(qb_ptr + C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
             floatx4 v = ok ? *(const floatx4 *)(qb_ptr + 2 * C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; e++) {
                 kf[4 * j4 + e] = k[e] * (scale * LOG2E);
                 vf[4 * j4 + e] = v[e];
             }
         }
         floatx16 dk[HeadBlocks<HD>::N], dv[HeadBlocks<HD>::N];
-    #pragma unroll
+#pragma unroll
         for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) dk[nd] = dv[nd] = zero16();
 
         const int tc0 = u0w + qfirst * TB, tc1 = min(T, u0w + qend * TB);
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
                 if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
                     float *dsb = dsout + (long long)bh * T * T;
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; r++) {
                         const int tt = t0 + row_of(r, h);
                         if (tt < T && u < T) dsb[(long long)tt * T + u] = 0.0f;
@@ -492,18 +492,18 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                 continue;
             }
             floatx16 s = zero16(), dp = zero16();
-    #pragma unroll
+#pragma unroll
             for (int j4 = 0; j4 < HD / 8; j4++) {
                 floatx4 qa = *(const floatx4 *)&Qs[l32 * P + h * (HD / 2) + 4 * j4];
                 floatx4 oa = *(const floatx4 *)&Os[l32 * P + h * (HD / 2) + 4 * j4];
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; e++) {
                     s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], kf[4 * j4 + e], s, 0, 0, 0);
                     dp = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[e], vf[4 * j4 + e], dp, 0, 0, 0);
                 }
             }
             if (t0 < u0 + QW - 1 || t0 + TB > T || u0 + QW > T) {  // crosses the diagonal or an end: mask
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int tl = row_of(r, h), tt = t0 + tl;
                     const float p = (tt < u || tt >= T || u >= T) ? 0.0f : exp2_fast(s[r] - Ls[tl]);
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                     dp[r] = p * (dp[r] - Ds[tl]);  // ds
                 }
             } else {
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int tl = row_of(r, h);
                     const float p = exp2_fast(s[r] - Ls[tl]);
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             }
             {  // ds[t][u] for the dq product (a row of 32 keys per register: coalesced)
                 float *dsb = dsout + (long long)bh * T * T;
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int tt = t0 + row_of(r, h);
                     if (tt < T && u < T) dsb[(long long)tt * T + u] = dp[r];
@@ -529,14 +529,14 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             }
             // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
             // the transposed tiles per 4 MFMAs
-    #pragma unroll
+#pragma unroll
             for (int g = 0; g < 4; g++)
-    #pragma unroll
+#pragma unroll
                 for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
                     const int d = 32 * nd + l32;
                     const floatx4 ob = d < HD ? *(const floatx4 *)&Ot[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
                     const floatx4 qv = d < HD ? *(const floatx4 *)&Qt[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; i++) {
                         dv[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[4 * g + i], ob[i], dv[nd], 0, 0, 0);
                         dk[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(dp[4 * g + i], qv[i], dk[nd], 0, 0, 0);
@@ -555,11 +555,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             dvb = dkb + QBLK * HD;
             krs = HD;
         }
-    #pragma unroll
+#pragma unroll
         for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
             const int d = 32 * nd + l32;
             if (d >= HD) continue;
-    #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int uu = u0 + row_of(r, h);
                 if (uu < T) {

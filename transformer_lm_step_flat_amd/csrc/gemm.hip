@@ -162,6 +162,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         lstore();
         __syncthreads();
         if (k0 + BK < kend) gload(k0 + BK);
+        // Raised wave priority while this slice's MFMAs issue: the sequencer
+        // then prefers the wavefronts feeding the matrix unit over those of
+        // other workgroups that are storing their next slice to LDS or
+        // waiting at a barrier (measured: -1.2 % step time).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int q = 0; q < BK / 8; q++) {
             floatx4 a[MI], b[NI];
@@ -193,6 +198,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
                     for (int j = 0; j < NI; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     if (!AK && do_colsum) {
