@@ -10,8 +10,8 @@ oracle can compute on their own:
   (dlnf = dlogits wte, dwte += dlogits^T lnf) on sampled rows; the other
   backward kernels are checked at full shapes in test_gpu_kernels.py.
 - properties of the whole step at full size: gradients finite, padded wte
-  rows untouched, bitwise reproducible, and one AdamW step lowers the loss of
-  the same batch.
+  rows untouched, bitwise reproducible, and one small AdamW step lowers the
+  loss of the same batch by what the gradients predict to first order.
 """
 import math
 
@@ -19,6 +19,8 @@ import numpy as np
 import pytest
 
 from transformer_lm_step_flat_amd import synth
+
+from .step_checks import check_first_order_step
 
 pytestmark = pytest.mark.gpu
 
@@ -124,7 +126,5 @@ def test_full_step_properties(full):
     M.backward()
     torch.cuda.synchronize()
     assert bool(torch.equal(M.grads, g1))
-    # one AdamW step on the same batch lowers its loss
-    M.update(lr=1e-4, t=1)
-    loss2 = M.forward(full["di"], full["dt"])
-    assert loss2 < full["loss"] - 1e-3, (loss2, full["loss"])
+    # one small AdamW step lowers the loss by what the gradients predict
+    check_first_order_step(M, full["di"], full["dt"], full["loss"])
