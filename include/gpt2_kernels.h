@@ -61,8 +61,10 @@ gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const floa
  * writes atty and lse[B][NH][T] (log-sum-exp of each query's scaled scores).
  * The backward recomputes the probabilities from them, computes dk and dv,
  * stores ds = p (dp - D) for every causal (t, u) in `work`, and finishes dq
- * as a causal GEMM over ds; it overwrites dqkv.  Rows longer than one work
- * chunk are split over workgroups and merged in a fixed order through `work`
+ * as a causal GEMM over ds; it overwrites dqkv.  Long causal rows are split
+ * over workgroups (forward: chunks of at most 256 keys; dk/dv: equal ranges of
+ * the (key block, query block) iterations over the resident workgroups) and
+ * their partial results merged in a fixed order through `work`
  * (gpt2k_flash_attention_work floats, B*NH*T*T of them for ds; the same size
  * serves both calls).  GPT2_EINVAL for other head dimensions. */
 size_t gpt2k_flash_attention_work(int B, int T, int C, int NH);

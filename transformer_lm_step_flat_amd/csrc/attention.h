@@ -5,8 +5,9 @@
 
 bool flash_attention_supported(int hd);
 
-// Floats of workspace the three calls below need (chunk partials of rows
-// longer than one chunk).
+// Floats of workspace the calls below need: the forward's partial results of
+// query blocks split between workgroups; for the backward the ds matrices and
+// the dk/dv partials of key blocks split between workgroups.
 size_t flash_attention_work(int B, int T, int C, int NH);
 
 // out[B][T][C] = softmax(q k^T / sqrt(hd), causal) v per head;
