@@ -57,7 +57,7 @@ struct GemmDesc {
     // with split-K stored to colsum + s * M.  Computed by the workgroups of the
     // first column of tiles from the A slices already in LDS.
     float *colsum = nullptr;
-    int tile = 0;  // 0 = choose; 1 = 128x128, 2 = 128x64, 3 = 64x64
+    int tile = 0;  // 0 = choose; 1 = 128x128, 2 = 128x64, 3 = 64x64, 4 = 64x192 (not paired)
 };
 
 // Validates the descriptor and enqueues the kernel; returns hipErrorInvalidValue

@@ -425,6 +425,7 @@ hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
         case 1: return launch_tile<128, 128, 32, 3>(d, a, stream);
         case 2: return launch_tile<128, 64, 32, 3>(d, a, stream);
         case 3: return launch_tile<64, 64, 32, 3>(d, a, stream);
+        case 4: return launch_tile<64, 192, 32, 3>(d, a, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -452,20 +453,23 @@ const char *gemm_pair_kernel_name(int tile) {
 }
 
 const char *gemm_kernel_name(const GemmDesc &d) {
-    static const char *names[3][3] = {
+    static const char *names[4][3] = {
         {"gemm_kernel<128, 128, true, true, 32, 3>", "gemm_kernel<128, 128, true, false, 32, 3>",
          "gemm_kernel<128, 128, false, false, 32, 3>"},
         {"gemm_kernel<128, 64, true, true, 32, 3>", "gemm_kernel<128, 64, true, false, 32, 3>",
          "gemm_kernel<128, 64, false, false, 32, 3>"},
         {"gemm_kernel<64, 64, true, true, 32, 3>", "gemm_kernel<64, 64, true, false, 32, 3>",
-         "gemm_kernel<64, 64, false, false, 32, 3>"}};
-    static const char *fold_names[3][3] = {
+         "gemm_kernel<64, 64, false, false, 32, 3>"},
+        {"gemm_kernel<64, 192, true, true, 32, 3>", "gemm_kernel<64, 192, true, false, 32, 3>",
+         "gemm_kernel<64, 192, false, false, 32, 3>"}};
+    static const char *fold_names[4][3] = {
         {"", "gemm_fold_kernel<128, 128, true, false, 32, 3>", "gemm_fold_kernel<128, 128, false, false, 32, 3>"},
         {"", "gemm_fold_kernel<128, 64, true, false, 32, 3>", "gemm_fold_kernel<128, 64, false, false, 32, 3>"},
-        {"", "gemm_fold_kernel<64, 64, true, false, 32, 3>", "gemm_fold_kernel<64, 64, false, false, 32, 3>"}};
-    static const int bm[3] = {128, 128, 64};
+        {"", "gemm_fold_kernel<64, 64, true, false, 32, 3>", "gemm_fold_kernel<64, 64, false, false, 32, 3>"},
+        {"", "gemm_fold_kernel<64, 192, true, false, 32, 3>", "gemm_fold_kernel<64, 192, false, false, 32, 3>"}};
+    static const int bm[4] = {128, 128, 64, 64};
     const int tile = resolve_tile(d);
-    const int t = tile >= 1 && tile <= 3 ? tile - 1 : 0;
+    const int t = tile >= 1 && tile <= 4 ? tile - 1 : 0;
     const int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
     // causal products with a growing or shrinking K range run with folded row tiles
     if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];

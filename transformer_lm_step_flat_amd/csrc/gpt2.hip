@@ -69,7 +69,8 @@ struct TileShape {
     int bm, bn, occ;
     double eff;
 };
-const TileShape kTiles[4] = {{0, 0, 0, 0.0}, {128, 128, 3, 0.73}, {128, 64, 4, 0.68}, {64, 64, 6, 0.66}};
+const TileShape kTiles[5] = {
+    {0, 0, 0, 0.0}, {128, 128, 3, 0.73}, {128, 64, 4, 0.68}, {64, 64, 6, 0.66}, {64, 192, 3, 0.70}};
 
 double predict_gemm_us(int M, int N, int K, long long batches, int tile, int ks) {
     const TileShape &t = kTiles[tile];
@@ -98,8 +99,8 @@ Plan plan_gemm(int M, int N, int K, long long batches, bool allow_split) {
     Plan best{1, 1};
     double best_us = 1e30;
     static const int splits[] = {1, 2, 3, 4, 6, 8, 12, 16};
-    for (int tile = 1; tile <= 3; tile++) {
-        if (N <= 64 && tile == 1) continue;
+    for (int tile = 1; tile <= 4; tile++) {
+        if (N <= 64 && (tile == 1 || tile == 4)) continue;
         for (int ks : splits) {
             if (ks > 1 && (!allow_split || K / ks < 256)) break;
             double us = predict_gemm_us(M, N, K, batches, tile, ks);
