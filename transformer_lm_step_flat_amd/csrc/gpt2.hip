@@ -75,18 +75,15 @@ const TileShape kTiles[5] = {
 double predict_gemm_us(int M, int N, int K, long long batches, int tile, int ks) {
     const TileShape &t = kTiles[tile];
     const long long wgs = ceil_div(M, t.bm) * ceil_div(N, t.bn) * batches * ks;
+    // equal workgroups run in rounds of up to occ per CU: the CU with the
+    // most sets the time, a round of k costing max(k, 2) tile-times (a short
+    // last round costs nearly a full one)
     double units = 0;
-    if (wgs <= 256LL * t.occ) {
-        // all resident from the start: the CU with the most sets the time
-        long long n = ceil_div(wgs, 256);
-        while (n > 0) {
-            long long k = n < t.occ ? n : t.occ;
-            units += k > 2 ? k : 2;
-            n -= k;
-        }
-    } else {
-        // refilled as slots free up: even spread plus a partial last tile
-        units = wgs / 256.0 + 0.5;
+    long long n = ceil_div(wgs, 256);
+    while (n > 0) {
+        long long k = n < t.occ ? n : t.occ;
+        units += k > 2 ? k : 2;
+        n -= k;
     }
     const double kc = (double)ceil_div(ceil_div(K, ks), 32) * 32;
     const double cu_flops_per_us = 157.3e6 / 256.0;
