@@ -27,3 +27,8 @@ hipError_t flash_attention_backward_dkdv(float *dqkv, float *ws, float *Dbuf, co
 
 // The [B][NH][T][T] ds matrices inside the workspace.
 const float *flash_attention_ds(const float *ws);
+
+// B*T*C floats of the workspace free once flash_attention_backward_dkdv has
+// returned (its dk/dv partials are summed by then): room for the partial sums
+// of the dq product.
+float *flash_attention_dq_partial(float *ws, int B, int T, int NH);

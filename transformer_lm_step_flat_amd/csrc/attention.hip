@@ -683,11 +683,15 @@ bool flash_attention_supported(int hd) { return hd == 16 || hd == 32 || hd == 64
 size_t flash_attention_work(int B, int T, int C, int NH) {
     const int hd = C / NH;
     const size_t fq = (size_t)B * NH * total_items(T) * QBLK * (hd + 1);
-    const size_t kv = ds_floats(B, T, NH) + (size_t)2 * dkdv_groups(B, T, NH, hd) * QBLK * 2 * hd;
+    // after ds: the dk/dv partials, later reused for the partial sums of dq
+    const size_t kvp = (size_t)2 * dkdv_groups(B, T, NH, hd) * QBLK * 2 * hd, dqp = (size_t)B * T * C;
+    const size_t kv = ds_floats(B, T, NH) + (kvp > dqp ? kvp : dqp);
     return fq > kv ? fq : kv;
 }
 
 const float *flash_attention_ds(const float *ws) { return ws; }
+
+float *flash_attention_dq_partial(float *ws, int B, int T, int NH) { return ws + ds_floats(B, T, NH); }
 
 hipError_t flash_attention_forward(float *out, float *lse, float *ws, const float *qkv, int B, int T, int C, int NH,
                                    hipStream_t s) {

@@ -57,6 +57,11 @@ struct GemmDesc {
     // with split-K stored to colsum + s * M.  Computed by the workgroups of the
     // first column of tiles from the A slices already in LDS.
     float *colsum = nullptr;
+    // CAUSAL_KEND, EPI_STORE, no bias, ksplit 1: run each folded pair of row
+    // tiles as two workgroups, the second one's partial sums of the upper row
+    // tiles going to part ([nbo*nbi][M][N] floats) and added into C by a
+    // second kernel.
+    float *part = nullptr;
     int tile = 0;  // 0 = choose; 1 = 128x128, 2 = 128x64, 3 = 64x64, 4 = 64x192 (not paired)
 };
 

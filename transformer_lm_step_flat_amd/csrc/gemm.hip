@@ -68,10 +68,11 @@ struct TileLds {
 };
 
 // One BM x BN output tile (row tile tm, column tile tn), batch / split
-// index z, operand tiles staged in As / Bs.
+// index z, operand tiles staged in As / Bs.  kr0 >= 0 replaces the tile's K
+// range by [kr0, kr1).
 template <int BM, int BN, bool AK, bool BKC, int BK>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int z, float *__restrict__ As,
-                                          float *__restrict__ Bs) {
+                                          float *__restrict__ Bs, int kr0 = -1, int kr1 = 0) {
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int KP = TileLds<BM, BN, AK, BKC, BK>::KP;
@@ -95,6 +96,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
     int kbeg = s * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
     if (p.causal == CAUSAL_KEND) kend = min(kend, m0 + BM);
     if (p.causal == CAUSAL_KSTART) kbeg = max(kbeg, m0);
+    if (kr0 >= 0) {
+        kbeg = kr0;
+        kend = kr1;
+    }
 
     floatx16 acc[MI][NI];
 #pragma unroll
@@ -288,6 +293,53 @@ __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_fold_kernel(GemmArgs p)
         gemm_tile<BM, BN, AK, BKC, BK>(p, pass == 0 ? j : i, tn, blockIdx.z, As, Bs);
 }
 
+// The folded causal product (KEND) with twice the workgroups: the pair of
+// row tiles (i, j = tiles_m - 1 - i) has kj + ki k values in all (one tile if
+// i == j); workgroup s = 0 takes the first half of row tile j's range into C,
+// s = 1 the rest of j's range into pp (a compact copy of C's layout: the
+// partial sums) and all of row tile i into C.  fold_split_sum_kernel then
+// adds the partials into the row tiles j >= tiles_m / 2.  Same result as one
+// workgroup per pair up to the order of two partial sums; twice the
+// workgroups for products with few row tiles.
+template <int BM, int BN, bool AK, bool BKC, int BK, int LB>
+__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_fold_split_kernel(GemmArgs p, GemmArgs pp) {
+    using L = TileLds<BM, BN, AK, BKC, BK>;
+    __shared__ __attribute__((aligned(16))) float As[L::A];
+    __shared__ __attribute__((aligned(16))) float Bs[L::B];
+    const int half = (p.tiles_m + 1) / 2;
+    const int t = xcd_remap(blockIdx.x, 2 * half * p.tiles_n);
+    const int s = t & 1, u = t >> 1;
+    const int tn = u / half, i = u % half, j = p.tiles_m - 1 - i;
+    const int kj = min(p.K, (j + 1) * BM), ki = min(p.K, (i + 1) * BM);
+    const int tot = i == j ? kj : kj + ki;
+    const int hk = min(kj, (tot / 2 + BK - 1) / BK * BK);
+    if (s == 0) {
+        gemm_tile<BM, BN, AK, BKC, BK>(p, j, tn, blockIdx.z, As, Bs, 0, hk);
+    } else {
+        gemm_tile<BM, BN, AK, BKC, BK>(pp, j, tn, blockIdx.z, As, Bs, hk, kj);
+        if (i != j) gemm_tile<BM, BN, AK, BKC, BK>(p, i, tn, blockIdx.z, As, Bs, 0, ki);
+    }
+}
+
+// C(z, m, n) += part[z][m][n] for the rows m >= m0 of every batch z; one
+// thread per 4 columns.
+__global__ __launch_bounds__(256) void fold_split_sum_kernel(float *C, long long ldc, long long sCo, long long sCi,
+                                                             int nbi, const float *part, int M, int N, int m0,
+                                                             long long n4) {
+    const long long f = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (f >= n4) return;
+    const int N4 = N / 4, R = M - m0;
+    const int c4 = (int)(f % N4);
+    const long long r = f / N4;
+    const int m = m0 + (int)(r % R);
+    const int z = (int)(r / R);
+    const int zo = z / nbi, zi = z % nbi;
+    float *c = C + zo * sCo + zi * sCi + (long long)m * ldc + 4 * c4;
+    const floatx4 a = *(const floatx4 *)c;
+    const floatx4 b = *(const floatx4 *)(part + ((long long)z * M + m) * N + 4 * c4);
+    *(floatx4 *)c = a + b;
+}
+
 // Two independent products in one grid of w = w1 + w2 workgroups (w1 of
 // problem 1: its tiles, then its batches / splits; w2 of problem 2).  Both
 // use the same tile shape.  Each XCD gets an eighth of each problem, as one
@@ -334,6 +386,27 @@ hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream
     set_tiles<BM, BN, BK>(d, a);
     long long nb = (long long)d.nbo * d.nbi * d.ksplit;
     if (nb > 65535) return hipErrorInvalidValue;
+    if (d.part && d.causal == CAUSAL_KEND && a.tiles_m > 1) {
+        const int half = (a.tiles_m + 1) / 2;
+        GemmArgs pp = a;
+        pp.C = d.part;
+        pp.ldc = d.N;
+        pp.sCi = (long long)d.M * d.N;
+        pp.sCo = pp.sCi * d.nbi;
+        dim3 g(2 * half * a.tiles_n, 1, (unsigned)nb);
+        if (d.a_kcontig && !d.b_kcontig)
+            hipLaunchKernelGGL((gemm_fold_split_kernel<BM, BN, true, false, BK, LB>), g, dim3(GEMM_THREADS), 0, stream,
+                               a, pp);
+        else
+            return hipErrorInvalidValue;
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int m0 = a.tiles_m / 2 * BM;
+        const long long n4 = nb * (long long)(d.M - m0) * (d.N / 4);
+        hipLaunchKernelGGL(fold_split_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, d.C, d.ldc,
+                           d.sCo, d.sCi, d.nbi, (const float *)d.part, d.M, d.N, m0, n4);
+        return hipGetLastError();
+    }
     if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && a.tiles_m > 1) {
         dim3 g((a.tiles_m + 1) / 2 * a.tiles_n, 1, (unsigned)nb);
         if (d.a_kcontig && !d.b_kcontig)
@@ -390,6 +463,9 @@ hipError_t make_args(const GemmDesc &d, GemmArgs &a) {
     if ((d.epi == EPI_RESID || d.epi == EPI_GELU_BWD) && !d.aux) return hipErrorInvalidValue;
     if (d.epi == EPI_GELU && !d.C2) return hipErrorInvalidValue;
     if (d.colsum && (d.a_kcontig || d.nbo * d.nbi != 1)) return hipErrorInvalidValue;
+    if (d.part && (d.causal != CAUSAL_KEND || d.epi != EPI_STORE || d.ksplit != 1 || d.bias || d.colsum ||
+                   d.N % 4 || d.ldc % 4 || d.sCo % 4 || d.sCi % 4 || ((uintptr_t)d.C & 15) || ((uintptr_t)d.part & 15)))
+        return hipErrorInvalidValue;
 
     a = GemmArgs{};
     a.A = d.A; a.B = d.B; a.C = d.C; a.C2 = d.C2; a.bias = d.bias; a.aux = d.aux; a.colsum = d.colsum;
@@ -471,7 +547,12 @@ const char *gemm_kernel_name(const GemmDesc &d) {
     const int tile = resolve_tile(d);
     const int t = tile >= 1 && tile <= 4 ? tile - 1 : 0;
     const int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
+    static const char *split_names[4] = {"gemm_fold_split_kernel<128, 128, true, false, 32, 3>",
+                                         "gemm_fold_split_kernel<128, 64, true, false, 32, 3>",
+                                         "gemm_fold_split_kernel<64, 64, true, false, 32, 3>",
+                                         "gemm_fold_split_kernel<64, 192, true, false, 32, 3>"};
     // causal products with a growing or shrinking K range run with folded row tiles
+    if (d.part && d.causal == CAUSAL_KEND && d.M > bm[t] && l == 1) return split_names[t];
     if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];
     return names[t][l];
 }

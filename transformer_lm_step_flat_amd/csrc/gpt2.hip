@@ -693,6 +693,8 @@ hipError_t flash_backward(float *dqkv, float *Dbuf, float *ws, const float *datt
     q.nbo = B; q.nbi = NH;
     q.sAo = NH * TT; q.sAi = TT; q.sBo = T * C3; q.sBi = hd; q.sCo = T * C3; q.sCi = hd;
     q.tile = plan_gemm(T, hd, T, (long long)B * NH, false).tile;
+    // each folded pair of row tiles as two workgroups: few row tiles per head
+    q.part = flash_attention_dq_partial(ws, B, T, NH);
     return gemm_run(q, s, "attn_dq");
 }
 
