@@ -219,34 +219,39 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, fl
         dwacc[i] = dbacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     const int r0 = blockIdx.x * COL_CHUNK + wave;
-    floatx4 xn[NV], dn[NV], on[NV];
+    floatx4 xn[NV], dn[NV], on[NV] = {};
     float mun = 0.f, rsn = 0.f;
+    // The loads read only valid addresses (a row past the end is never used,
+    // lanes past the row end read its last float4) and the zeros of lanes
+    // past the row end are applied when the row is used, so the next row's
+    // loads stay in flight while the current row is reduced.
     auto fetch = [&](int row) {
-        const bool ok = row < N;
-        const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
-        const floatx4 *dy = (const floatx4 *)(dout + (long long)row * C);
-        const floatx4 *dx = (const floatx4 *)(dinp + (long long)row * C);
+        const int rr = row < N ? row : N - 1;
+        const floatx4 *x = (const floatx4 *)(inp + (long long)rr * C);
+        const floatx4 *dy = (const floatx4 *)(dout + (long long)rr * C);
+        const floatx4 *dx = (const floatx4 *)(dinp + (long long)rr * C);
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int k = lane + 64 * i;
-            const bool kk = ok && k < C4;
-            xn[i] = kk ? x[k] : floatx4{0.f, 0.f, 0.f, 0.f};
-            dn[i] = kk ? dy[k] : floatx4{0.f, 0.f, 0.f, 0.f};
-            on[i] = (kk && accumulate) ? dx[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+            const int k = lane + 64 * i, kc = k < C4 ? k : C4 - 1;
+            xn[i] = x[kc];
+            dn[i] = dy[kc];
+            if (accumulate) on[i] = dx[kc];
         }
-        mun = ok ? mean[row] : 0.f;
-        rsn = ok ? rstd[row] : 0.f;
+        mun = mean[rr];
+        rsn = rstd[rr];
     };
     fetch(r0);
     for (int k = 0; k < COL_CHUNK / 4; k++) {
         const int row = r0 + 4 * k;
         if (row >= N) break;
         floatx4 xc[NV], dc[NV], oc[NV];
+        const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            xc[i] = xn[i];
-            dc[i] = dn[i];
-            oc[i] = on[i];
+            const bool kk = lane + 64 * i < C4;
+            xc[i] = kk ? xn[i] : z4;
+            dc[i] = kk ? dn[i] : z4;
+            oc[i] = (kk && accumulate) ? on[i] : z4;
         }
         const float mu = mun, rs = rsn;
         // prefetch the next row while reducing this one (wide rows: registers
