@@ -266,12 +266,13 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
-    def step(i):
+    def step(i, want_loss=False):
         di, dt = batches[i % nb]
-        M.forward(di, dt, want_loss=False)
+        loss = M.forward(di, dt, want_loss=want_loss)
         M.zero_grad()
         M.backward()
         M.update(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, t=i + 1)
+        return loss
 
     for i in range(args.warmup):
         step(i)
@@ -302,13 +303,14 @@ def main():
         f"HBM copy {peaks['hbm_copy_gbs']:.0f} GB/s")
 
     # the same steps again, each launch bracketed by HIP events on the step's stream
-    kernels, roofline, ms_ev, sites = [], None, None, []
+    kernels, roofline, ms_ev, sites, losses = [], None, None, [], []
     if not args.no_events:
         M.profile_enable(True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(args.warmup + args.steps + i)
+            # the loss of each step (read back, so this pass also waits once per step)
+            losses.append(step(args.warmup + args.steps + i, want_loss=True))
         torch.cuda.synchronize()
         ms_ev = (time.perf_counter() - t0) / args.steps * 1e3
         prof = M.profile_read()
@@ -386,6 +388,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "last_loss": loss,
+        "losses_of_event_pass": losses,
         "step_ms": step_ms,
         "measured_peaks": peaks,
         "ms_per_step_with_events": ms_ev,
