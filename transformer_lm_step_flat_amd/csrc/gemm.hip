@@ -118,7 +118,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
     floatx4 csum = {0.f, 0.f, 0.f, 0.f};
     const long long lda = p.lda, ldb = p.ldb;
 
+    // A tile inside M x N whose slice lies inside [kbeg, kend) loads without
+    // bounds tests: no predication, no zeroing of the load targets.  Vector
+    // ALU and global-memory instructions do not issue on a SIMD while another
+    // wavefront there keeps its matrix unit busy, so every such instruction
+    // saved shortens the K loop (measured: -1.5 % step time).
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
     auto gload = [&](int k0) {
+        if (interior && k0 + BK <= kend) {
+#pragma unroll
+            for (int i = 0; i < A_F4; i++) {
+                const int f = tid + GEMM_THREADS * i;
+                const int gm = AK ? m0 + f / (BK / 4) : m0 + 4 * (f % (BM / 4));
+                const int gk = AK ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BM / 4);
+                ra[i] = *(const floatx4 *)(AK ? A + gm * lda + gk : A + gk * lda + gm);
+            }
+#pragma unroll
+            for (int i = 0; i < B_F4; i++) {
+                const int f = tid + GEMM_THREADS * i;
+                const int gn = BKC ? n0 + f / (BK / 4) : n0 + 4 * (f % (BN / 4));
+                const int gk = BKC ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BN / 4);
+                rb[i] = *(const floatx4 *)(BKC ? B + gn * ldb + gk : B + gk * ldb + gn);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < A_F4; i++) {
             int f = tid + GEMM_THREADS * i;
@@ -170,7 +193,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         // Raised wave priority while this slice's MFMAs issue: the sequencer
         // then prefers the wavefronts feeding the matrix unit over those of
         // other workgroups that are storing their next slice to LDS or
-        // waiting at a barrier (measured: -1.2 % step time).
+        // waiting at a barrier (measured: without it the step takes 3 %
+        // longer; raising the load phase's priority instead costs 3 to 4 %).
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int q = 0; q < BK / 8; q++) {
