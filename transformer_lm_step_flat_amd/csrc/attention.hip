@@ -417,6 +417,9 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
     __shared__ __attribute__((aligned(16))) float Qt[HD * PT];  // the same two, transposed
     __shared__ __attribute__((aligned(16))) float Ot[HD * PT];
     __shared__ float Ls[TB], Ds[TB];
+    // per wavefront, its 32 x 32 block of ds on the way to memory (row pitch PP)
+    constexpr int PP = QW + 4;
+    __shared__ __attribute__((aligned(16))) float Ps[NWAVE * QW * PP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int G = gridDim.x, g = xcd_run(blockIdx.x, G);
     const int nkb = (T + QBLK - 1) / QBLK, W1 = kq_start(nkb, T);
@@ -480,14 +483,24 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             }
             __syncthreads();
             if (t0 + TB < tc1) load_rows(t0 + TB);
+            const bool edge = t0 + TB > T || u0 + QW > T;
+            // This wave's 32 x 32 block of ds leaves as 16-byte stores: lane l takes
+            // row l / 2, columns 8 i + 4 (l % 2) .. + 3 for i = 0..3 (one base address,
+            // constant offsets).  T % 4 == 0 and u0 % 32 == 0, so a group of 4
+            // columns lies wholly inside or outside [0, T).
+            const int drow = lane >> 1, dcol = 4 * (lane & 1);
+            float *const dsw = dsout + ((long long)bh * T + t0 + drow) * T + u0 + dcol;
+            const bool row_ok = t0 + drow < T;
             if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
                 if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
-                    float *dsb = dsout + (long long)bh * T * T;
+                    // (a zero the compiler cannot see as a constant: it would keep a
+                    // zero vector in registers through the whole loop otherwise)
+                    float zf;
+                    asm volatile("v_mov_b32 %0, 0" : "=v"(zf));
+                    const floatx4 z = {zf, zf, zf, zf};
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int tt = t0 + row_of(r, h);
-                        if (tt < T && u < T) dsb[(long long)tt * T + u] = 0.0f;
-                    }
+                    for (int i = 0; i < 4; i++)
+                        if (!edge || (row_ok && u0 + dcol + 8 * i < T)) *(floatx4 *)(dsw + 8 * i) = z;
                 }
                 continue;
             }
@@ -502,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                     dp = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[e], vf[4 * j4 + e], dp, 0, 0, 0);
                 }
             }
-            if (t0 < u0 + QW - 1 || t0 + TB > T || u0 + QW > T) {  // crosses the diagonal or an end: mask
+            if (t0 < u0 + QW - 1 || edge) {  // crosses the diagonal or an end: mask
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int tl = row_of(r, h), tt = t0 + tl;
@@ -519,13 +532,14 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                     dp[r] = p * (dp[r] - Ds[tl]);
                 }
             }
-            {  // ds[t][u] for the dq product (a row of 32 keys per register: coalesced)
-                float *dsb = dsout + (long long)bh * T * T;
+            // ds[t][u] for the dq product goes through this wave's LDS patch (read
+            // back as rows after the MFMAs below, when their operands are free).
+            // The index is the lane's base plus a constant per register, so that
+            // the constant becomes the instruction's offset.
+            {
+                const int pl = (wave * QW + 4 * h) * PP + l32;
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int tt = t0 + row_of(r, h);
-                    if (tt < T && u < T) dsb[(long long)tt * T + u] = dp[r];
-                }
+                for (int r = 0; r < 16; r++) Ps[pl + (8 * (r >> 2) + (r & 3)) * PP] = dp[r];
             }
             // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
             // the transposed tiles per 4 MFMAs
@@ -542,6 +556,22 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                         dk[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(dp[4 * g + i], qv[i], dk[nd], 0, 0, 0);
                     }
                 }
+            {
+                // the patch is this wavefront's alone: order its LDS writes before the reads
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const int pr = (wave * QW + drow) * PP + dcol;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const floatx4 v = *(const floatx4 *)&Ps[pr + 8 * i];
+                    if (!edge || (row_ok && u0 + dcol + 8 * i < T)) *(floatx4 *)(dsw + 8 * i) = v;
+                }
+                // and the reads before the next iteration's writes
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
         }
         // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
         float *dkb, *dvb;
