@@ -78,4 +78,7 @@ hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t 
 // The names a kernel-trace profiler shows for the kernels the two calls
 // above run with descriptor d (static strings).
 const char *gemm_kernel_name(const GemmDesc &d);
-const char *gemm_pair_kernel_name(int tile);
+const char *gemm_pair_kernel_name(int tile, bool full);
+// Whether gemm_launch_pair runs the pair (weight gradient dw, input gradient
+// di) with the kernel for whole tiles and whole K slices.
+bool gemm_pair_full(const GemmDesc &dw, const GemmDesc &di, int tile);

@@ -69,8 +69,10 @@ struct TileLds {
 
 // One BM x BN output tile (row tile tm, column tile tn), batch / split
 // index z, operand tiles staged in As / Bs.  kr0 >= 0 replaces the tile's K
-// range by [kr0, kr1).
-template <int BM, int BN, bool AK, bool BKC, int BK>
+// range by [kr0, kr1).  FULL: the launch guarantees that every tile lies
+// inside M x N and every K range is a whole number of BK slices (no bounds
+// tests anywhere in the K loop).
+template <int BM, int BN, bool AK, bool BKC, int BK, bool FULL = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int z, float *__restrict__ As,
                                           float *__restrict__ Bs, int kr0 = -1, int kr1 = 0) {
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -184,50 +186,156 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         }
     };
 
-    if (kbeg < kend) gload(kbeg);
-    for (int k0 = kbeg; k0 < kend; k0 += BK) {
-        __syncthreads();
-        lstore();
-        __syncthreads();
-        if (k0 + BK < kend) gload(k0 + BK);
-        // Raised wave priority while this slice's MFMAs issue: the sequencer
-        // then prefers the wavefronts feeding the matrix unit over those of
-        // other workgroups that are storing their next slice to LDS or
-        // waiting at a barrier (measured: without it the step takes 3 %
-        // longer; raising the load phase's priority instead costs 3 to 4 %).
-        __builtin_amdgcn_s_setprio(1);
+    if constexpr (FULL) {
+        // Full-slice loads.  Where GEMM_THREADS is a multiple of the float4s per
+        // row of the staged layout (BK / 4 for a K-contiguous operand, BM / 4 or
+        // BN / 4 otherwise), thread tid's float4 number i (f = tid + 256 i) sits at
+        // a per-thread address plus an offset common to the workgroup, so one
+        // pointer per operand and thread serves every load.
+        constexpr bool kEvenA = GEMM_THREADS % (AK ? BK / 4 : BM / 4) == 0;
+        constexpr bool kEvenB = GEMM_THREADS % (BKC ? BK / 4 : BN / 4) == 0;
+        const float *const pa = AK ? A + (long long)(m0 + tid / (BK / 4)) * lda + 4 * (tid % (BK / 4))
+                                   : A + (long long)(tid / (BM / 4)) * lda + m0 + 4 * (tid % (BM / 4));
+        const float *const pb = BKC ? B + (long long)(n0 + tid / (BK / 4)) * ldb + 4 * (tid % (BK / 4))
+                                    : B + (long long)(tid / (BN / 4)) * ldb + n0 + 4 * (tid % (BN / 4));
+        auto gload_full = [&](int k0) {
 #pragma unroll
-        for (int q = 0; q < BK / 8; q++) {
-            floatx4 a[MI], b[NI];
-#pragma unroll
-            for (int i = 0; i < MI; i++) {
-                const int mm = wm * WM + i * 32 + l32;
-                if (AK) {
-                    a[i] = *(const floatx4 *)&As[mm * KP + h * (BK / 2) + 4 * q];
+            for (int i = 0; i < A_F4; i++) {
+                if constexpr (kEvenA) {
+                    const long long off = AK ? (long long)(GEMM_THREADS / (BK / 4)) * i * lda + k0
+                                             : ((long long)(GEMM_THREADS / (BM / 4)) * i + k0) * lda;
+                    ra[i] = *(const floatx4 *)(pa + off);
                 } else {
-#pragma unroll
-                    for (int e = 0; e < 4; e++) a[i][e] = As[(h * (BK / 2) + 4 * q + e) * BM + mm];
+                    const int f = tid + GEMM_THREADS * i;
+                    const int gm = AK ? m0 + f / (BK / 4) : m0 + 4 * (f % (BM / 4));
+                    const int gk = AK ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BM / 4);
+                    ra[i] = *(const floatx4 *)(AK ? A + gm * lda + gk : A + gk * lda + gm);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < NI; j++) {
-                const int nn = wn * WN + j * 32 + l32;
-                if (BKC) {
-                    b[j] = *(const floatx4 *)&Bs[nn * KP + h * (BK / 2) + 4 * q];
+            for (int i = 0; i < B_F4; i++) {
+                if constexpr (kEvenB) {
+                    const long long off = BKC ? (long long)(GEMM_THREADS / (BK / 4)) * i * ldb + k0
+                                              : ((long long)(GEMM_THREADS / (BN / 4)) * i + k0) * ldb;
+                    rb[i] = *(const floatx4 *)(pb + off);
                 } else {
-#pragma unroll
-                    for (int e = 0; e < 4; e++) b[j][e] = Bs[(h * (BK / 2) + 4 * q + e) * BN + nn];
+                    const int f = tid + GEMM_THREADS * i;
+                    const int gn = BKC ? n0 + f / (BK / 4) : n0 + 4 * (f % (BN / 4));
+                    const int gk = BKC ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BN / 4);
+                    rb[i] = *(const floatx4 *)(BKC ? B + gn * ldb + gk : B + gk * ldb + gn);
                 }
             }
+        };
+        // one slice's MFMAs (the wave priority is raised around them, as in
+        // the general loop below)
+        auto mfma_slice = [&]() {
 #pragma unroll
-            for (int e = 0; e < 4; e++)
+            for (int q = 0; q < BK / 8; q++) {
+                floatx4 a[MI], b[NI];
 #pragma unroll
-                for (int i = 0; i < MI; i++)
+                for (int i = 0; i < MI; i++) {
+                    const int mm = wm * WM + i * 32 + l32;
+                    if (AK) {
+                        a[i] = *(const floatx4 *)&As[mm * KP + h * (BK / 2) + 4 * q];
+                    } else {
 #pragma unroll
-                    for (int j = 0; j < NI; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+                        for (int e = 0; e < 4; e++) a[i][e] = As[(h * (BK / 2) + 4 * q + e) * BM + mm];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NI; j++) {
+                    const int nn = wn * WN + j * 32 + l32;
+                    if (BKC) {
+                        b[j] = *(const floatx4 *)&Bs[nn * KP + h * (BK / 2) + 4 * q];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++) b[j][e] = Bs[(h * (BK / 2) + 4 * q + e) * BN + nn];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+#pragma unroll
+                    for (int i = 0; i < MI; i++)
+#pragma unroll
+                        for (int j = 0; j < NI; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+            }
+        };
+
+        // Every slice is full: a branch-free loop, the last slice peeled off.
+        // The next slice's loads are placed one after each of the first
+        // MFMAs, so that they issue while this wavefront's own MFMAs run
+        // instead of waiting behind those of other workgroups.
+        int k0 = kbeg;
+        if (kbeg < kend) gload_full(kbeg);
+        for (; k0 + BK < kend; k0 += BK) {
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            __builtin_amdgcn_s_setprio(1);
+            gload_full(k0 + BK);
+            mfma_slice();
+#pragma unroll
+            for (int i = 0; i < A_F4 + B_F4; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+            }
+            __builtin_amdgcn_s_setprio(0);
         }
-        __builtin_amdgcn_s_setprio(0);
+        if (k0 < kend) {
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            __builtin_amdgcn_s_setprio(1);
+            mfma_slice();
+            __builtin_amdgcn_s_setprio(0);
+        }
+    } else {
+        if (kbeg < kend) gload(kbeg);
+        for (int k0 = kbeg; k0 < kend; k0 += BK) {
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            if (k0 + BK < kend) gload(k0 + BK);
+            // Raised wave priority while this slice's MFMAs issue: the sequencer
+            // then prefers the wavefronts feeding the matrix unit over those of
+            // other workgroups that are storing their next slice to LDS or
+            // waiting at a barrier (measured: without it the step takes 3 %
+            // longer; raising the load phase's priority instead costs 3 to 4 %).
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int q = 0; q < BK / 8; q++) {
+                floatx4 a[MI], b[NI];
+#pragma unroll
+                for (int i = 0; i < MI; i++) {
+                    const int mm = wm * WM + i * 32 + l32;
+                    if (AK) {
+                        a[i] = *(const floatx4 *)&As[mm * KP + h * (BK / 2) + 4 * q];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++) a[i][e] = As[(h * (BK / 2) + 4 * q + e) * BM + mm];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NI; j++) {
+                    const int nn = wn * WN + j * 32 + l32;
+                    if (BKC) {
+                        b[j] = *(const floatx4 *)&Bs[nn * KP + h * (BK / 2) + 4 * q];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++) b[j][e] = Bs[(h * (BK / 2) + 4 * q + e) * BN + nn];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+#pragma unroll
+                    for (int i = 0; i < MI; i++)
+#pragma unroll
+                        for (int j = 0; j < NI; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+        }
     }
 
     if (!AK && do_colsum) {
@@ -291,14 +399,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         }
 }
 
-template <int BM, int BN, bool AK, bool BKC, int BK, int LB>
+template <int BM, int BN, bool AK, bool BKC, int BK, int LB, bool FULL>
 __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_kernel(GemmArgs p) {
     using L = TileLds<BM, BN, AK, BKC, BK>;
     __shared__ __attribute__((aligned(16))) float As[L::A];
     __shared__ __attribute__((aligned(16))) float Bs[L::B];
     int tm, tn;
     group_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    gemm_tile<BM, BN, AK, BKC, BK>(p, tm, tn, blockIdx.z, As, Bs);
+    gemm_tile<BM, BN, AK, BKC, BK, FULL>(p, tm, tn, blockIdx.z, As, Bs);
 }
 
 // Causal products whose K range grows (KEND) or shrinks (KSTART) with the row
@@ -369,7 +477,7 @@ __global__ __launch_bounds__(256) void fold_split_sum_kernel(float *C, long long
 // use the same tile shape.  Each XCD gets an eighth of each problem, as one
 // contiguous run of problem 1 followed by one of problem 2, so that the work
 // per XCD is balanced and operand tiles are shared within an XCD's L2.
-template <int BM, int BN, int BK, int LB, bool AK1, bool BKC1, bool AK2, bool BKC2>
+template <int BM, int BN, int BK, int LB, bool AK1, bool BKC1, bool AK2, bool BKC2, bool FULL>
 __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int w1, int w) {
     using L1 = TileLds<BM, BN, AK1, BKC1, BK>;
     using L2 = TileLds<BM, BN, AK2, BKC2, BK>;
@@ -384,13 +492,13 @@ __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_pair_kernel(GemmArgs p1
         const int g = s1 + j, nt = p1.tiles_m * p1.tiles_n;
         int tm, tn;
         group_order(g % nt, p1.tiles_m, p1.tiles_n, p1.group_m, tm, tn);
-        gemm_tile<BM, BN, AK1, BKC1, BK>(p1, tm, tn, g / nt, As, Bs);
+        gemm_tile<BM, BN, AK1, BKC1, BK, FULL>(p1, tm, tn, g / nt, As, Bs);
     } else {
         const int s2 = x * (w / X) + min(x, w % X) - s1;  // workgroups of XCDs before x, less problem 1's
         const int g = s2 + j - r1, nt = p2.tiles_m * p2.tiles_n;
         int tm, tn;
         group_order(g % nt, p2.tiles_m, p2.tiles_n, p2.group_m, tm, tn);
-        gemm_tile<BM, BN, AK2, BKC2, BK>(p2, tm, tn, g / nt, As, Bs);
+        gemm_tile<BM, BN, AK2, BKC2, BK, FULL>(p2, tm, tn, g / nt, As, Bs);
     }
 }
 
@@ -402,6 +510,21 @@ void set_tiles(const GemmDesc &d, GemmArgs &a) {
     a.group_m = 8;
     const int kc = (d.K + d.ksplit - 1) / d.ksplit;
     a.kchunk = kc > 0 ? (kc + BK - 1) / BK * BK : BK;
+}
+
+// Whether every tile of d lies inside M x N and every K range (one per
+// split) is a whole number of BK slices: the launch may then use the
+// kernels without bounds tests.  Causal products are excluded.
+bool gemm_full(const GemmDesc &d, int bm, int bn, int bk) {
+    return d.causal == 0 && d.M % bm == 0 && d.N % bn == 0 && d.K % bk == 0;
+}
+
+template <int BM, int BN, bool AKV, bool BKV, int BK, int LB>
+void launch_gemm_kernel(bool full, dim3 grid, hipStream_t stream, const GemmArgs &a) {
+    if (full)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, AKV, BKV, BK, LB, true>), grid, dim3(GEMM_THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, AKV, BKV, BK, LB, false>), grid, dim3(GEMM_THREADS), 0, stream, a);
 }
 
 template <int BM, int BN, int BK, int LB>
@@ -442,15 +565,24 @@ hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream
         return hipGetLastError();
     }
     dim3 grid(a.tiles_m * a.tiles_n, 1, (unsigned)nb);
+    const bool full = gemm_full(d, BM, BN, BK);
     if (d.a_kcontig && d.b_kcontig)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true, BK, LB>), grid, dim3(GEMM_THREADS), 0, stream, a);
+        launch_gemm_kernel<BM, BN, true, true, BK, LB>(full, grid, stream, a);
     else if (d.a_kcontig && !d.b_kcontig)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false, BK, LB>), grid, dim3(GEMM_THREADS), 0, stream, a);
+        launch_gemm_kernel<BM, BN, true, false, BK, LB>(full, grid, stream, a);
     else if (!d.a_kcontig && !d.b_kcontig)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false, BK, LB>), grid, dim3(GEMM_THREADS), 0, stream, a);
+        launch_gemm_kernel<BM, BN, false, false, BK, LB>(full, grid, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+// The paired kernel for whole tiles is used for the 128 x 128 and 64 x 64
+// shapes; at 128 x 64 it measured slower than the general one (fc and
+// attproj backward: +7 % and +42 %), so that shape keeps the general kernel.
+template <int BM, int BN>
+constexpr bool pair_full_shape() {
+    return !(BM == 128 && BN == 64);
 }
 
 template <int BM, int BN, int BK, int LB>
@@ -464,8 +596,12 @@ hipError_t launch_pair(const GemmDesc &d1, const GemmArgs &a1_, const GemmDesc &
     if (w1 + w2 > (1LL << 30)) return hipErrorInvalidValue;
     // the one instantiation used: a weight gradient (both MN-contiguous) beside an input gradient
     if (d1.a_kcontig || d1.b_kcontig || !d2.a_kcontig || d2.b_kcontig) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false>), dim3((unsigned)(w1 + w2)),
-                       dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+    if (pair_full_shape<BM, BN>() && gemm_full(d1, BM, BN, BK) && gemm_full(d2, BM, BN, BK))
+        hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false, true>),
+                           dim3((unsigned)(w1 + w2)), dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+    else
+        hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false, false>),
+                           dim3((unsigned)(w1 + w2)), dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
     return hipGetLastError();
 }
 
@@ -545,29 +681,44 @@ hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t 
 }
 
 // Keep in step with the instantiations chosen in gemm_launch and gemm_launch_pair.
-const char *gemm_pair_kernel_name(int tile) {
-    static const char *names[3] = {"gemm_pair_kernel<128, 128, 32, 3, false, false, true, false>",
-                                   "gemm_pair_kernel<128, 64, 32, 3, false, false, true, false>",
-                                   "gemm_pair_kernel<64, 64, 32, 3, false, false, true, false>"};
-    return names[tile >= 1 && tile <= 3 ? tile - 1 : 0];
+const char *gemm_pair_kernel_name(int tile, bool full) {
+    static const char *names[3][2] = {
+        {"gemm_pair_kernel<128, 128, 32, 3, false, false, true, false, false>",
+         "gemm_pair_kernel<128, 128, 32, 3, false, false, true, false, true>"},
+        {"gemm_pair_kernel<128, 64, 32, 3, false, false, true, false, false>",
+         "gemm_pair_kernel<128, 64, 32, 3, false, false, true, false, true>"},
+        {"gemm_pair_kernel<64, 64, 32, 3, false, false, true, false, false>",
+         "gemm_pair_kernel<64, 64, 32, 3, false, false, true, false, true>"}};
+    return names[tile >= 1 && tile <= 3 ? tile - 1 : 0][full ? 1 : 0];
+}
+
+bool gemm_pair_full(const GemmDesc &dw, const GemmDesc &di, int tile) {
+    static const int bm[3] = {128, 128, 64}, bn[3] = {128, 64, 64};
+    const int t = tile >= 1 && tile <= 3 ? tile - 1 : 0;
+    return (t == 0 ? pair_full_shape<128, 128>() : t == 1 ? pair_full_shape<128, 64>() : pair_full_shape<64, 64>()) &&
+           gemm_full(dw, bm[t], bn[t], 32) && gemm_full(di, bm[t], bn[t], 32);
 }
 
 const char *gemm_kernel_name(const GemmDesc &d) {
-    static const char *names[4][3] = {
-        {"gemm_kernel<128, 128, true, true, 32, 3>", "gemm_kernel<128, 128, true, false, 32, 3>",
-         "gemm_kernel<128, 128, false, false, 32, 3>"},
-        {"gemm_kernel<128, 64, true, true, 32, 3>", "gemm_kernel<128, 64, true, false, 32, 3>",
-         "gemm_kernel<128, 64, false, false, 32, 3>"},
-        {"gemm_kernel<64, 64, true, true, 32, 3>", "gemm_kernel<64, 64, true, false, 32, 3>",
-         "gemm_kernel<64, 64, false, false, 32, 3>"},
-        {"gemm_kernel<64, 192, true, true, 32, 3>", "gemm_kernel<64, 192, true, false, 32, 3>",
-         "gemm_kernel<64, 192, false, false, 32, 3>"}};
+    static const char *names[4][3][2] = {
+        {{"gemm_kernel<128, 128, true, true, 32, 3, false>", "gemm_kernel<128, 128, true, true, 32, 3, true>"},
+         {"gemm_kernel<128, 128, true, false, 32, 3, false>", "gemm_kernel<128, 128, true, false, 32, 3, true>"},
+         {"gemm_kernel<128, 128, false, false, 32, 3, false>", "gemm_kernel<128, 128, false, false, 32, 3, true>"}},
+        {{"gemm_kernel<128, 64, true, true, 32, 3, false>", "gemm_kernel<128, 64, true, true, 32, 3, true>"},
+         {"gemm_kernel<128, 64, true, false, 32, 3, false>", "gemm_kernel<128, 64, true, false, 32, 3, true>"},
+         {"gemm_kernel<128, 64, false, false, 32, 3, false>", "gemm_kernel<128, 64, false, false, 32, 3, true>"}},
+        {{"gemm_kernel<64, 64, true, true, 32, 3, false>", "gemm_kernel<64, 64, true, true, 32, 3, true>"},
+         {"gemm_kernel<64, 64, true, false, 32, 3, false>", "gemm_kernel<64, 64, true, false, 32, 3, true>"},
+         {"gemm_kernel<64, 64, false, false, 32, 3, false>", "gemm_kernel<64, 64, false, false, 32, 3, true>"}},
+        {{"gemm_kernel<64, 192, true, true, 32, 3, false>", "gemm_kernel<64, 192, true, true, 32, 3, true>"},
+         {"gemm_kernel<64, 192, true, false, 32, 3, false>", "gemm_kernel<64, 192, true, false, 32, 3, true>"},
+         {"gemm_kernel<64, 192, false, false, 32, 3, false>", "gemm_kernel<64, 192, false, false, 32, 3, true>"}}};
     static const char *fold_names[4][3] = {
         {"", "gemm_fold_kernel<128, 128, true, false, 32, 3>", "gemm_fold_kernel<128, 128, false, false, 32, 3>"},
         {"", "gemm_fold_kernel<128, 64, true, false, 32, 3>", "gemm_fold_kernel<128, 64, false, false, 32, 3>"},
         {"", "gemm_fold_kernel<64, 64, true, false, 32, 3>", "gemm_fold_kernel<64, 64, false, false, 32, 3>"},
         {"", "gemm_fold_kernel<64, 192, true, false, 32, 3>", "gemm_fold_kernel<64, 192, false, false, 32, 3>"}};
-    static const int bm[4] = {128, 128, 64, 64};
+    static const int bm[4] = {128, 128, 64, 64}, bn[4] = {128, 64, 64, 192};
     const int tile = resolve_tile(d);
     const int t = tile >= 1 && tile <= 4 ? tile - 1 : 0;
     const int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
@@ -578,5 +729,5 @@ const char *gemm_kernel_name(const GemmDesc &d) {
     // causal products with a growing or shrinking K range run with folded row tiles
     if (d.part && d.causal == CAUSAL_KEND && d.M > bm[t] && l == 1) return split_names[t];
     if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];
-    return names[t][l];
+    return names[t][l][gemm_full(d, bm[t], bn[t], 32) ? 1 : 0];
 }

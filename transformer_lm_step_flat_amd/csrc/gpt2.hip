@@ -588,7 +588,8 @@ hipError_t linear_bwd(float *dinp, int epi, const float *aux, float *dW, float *
     double f1, b1, f2, b2;
     gemm_cost(dd, f1, b1);
     gemm_cost(di, f2, b2);
-    hipError_t e = timed(gemm_pair_kernel_name(pp.tile), f1 + f2, b1 + b2, [&]() { return gemm_launch_pair(dd, di, s); });
+    hipError_t e = timed(gemm_pair_kernel_name(pp.tile, gemm_pair_full(dd, di, pp.tile)), f1 + f2, b1 + b2,
+                         [&]() { return gemm_launch_pair(dd, di, s); });
     if (e == hipSuccess && !defer_dw_sum) e = dw_finish(dW, dbias, splitk_dw, dbias_ws, K, OC, pp.ks_dw, s);
     if (e == hipSuccess) e = dinp_finish(dinp, splitk_dinp, N, K, pp.ks_dinp, s);
     return e;
