@@ -411,12 +411,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                                                                 const float *__restrict__ Dbuf, int T, int C, int NH,
                                                                 int BH, float scale) {
     constexpr int P = HD + 4;
-    constexpr int PT = TB + 4;
-    __shared__ __attribute__((aligned(16))) float Qs[TB * P];
-    __shared__ __attribute__((aligned(16))) float Os[TB * P];  // dO tile
-    __shared__ __attribute__((aligned(16))) float Qt[HD * PT];  // the same two, transposed
-    __shared__ __attribute__((aligned(16))) float Ot[HD * PT];
-    __shared__ float Ls[TB], Ds[TB];
+    // Q and dO tiles of TB queries, row-major, two buffers: the next block's
+    // tiles are stored into the other buffer at the end of an iteration, so
+    // one barrier per iteration suffices
+    __shared__ __attribute__((aligned(16))) float Qs[2 * TB * P];
+    __shared__ __attribute__((aligned(16))) float Os[2 * TB * P];
+    __shared__ float Ls[2 * TB], Ds[2 * TB];
     // per wavefront, its 32 x 32 block of ds on the way to memory (row pitch PP)
     constexpr int PP = QW + 4;
     __shared__ __attribute__((aligned(16))) float Ps[NWAVE * QW * PP];
@@ -470,19 +470,26 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             lse_next = lse_bh[ld_ok ? t0 + tid : 0];
             d_next = D_bh[ld_ok ? t0 + tid : 0];
         };
-        load_rows(tc0);
-        for (int t0 = tc0; t0 < tc1; t0 += TB) {
-            __syncthreads();
-            lq.store(Qs, P, tid);
-            lo.store(Os, P, tid);
-            lq.store_t(Qt, PT, tid);
-            lo.store_t(Ot, PT, tid);
+        auto store_rows = [&](int buf) {
+            lq.store(Qs + buf * TB * P, P, tid);
+            lo.store(Os + buf * TB * P, P, tid);
             if (tid < TB) {
-                Ls[tid] = ld_ok ? lse_next * LOG2E : 0.0f;
-                Ds[tid] = ld_ok ? d_next : 0.0f;
+                Ls[buf * TB + tid] = ld_ok ? lse_next * LOG2E : 0.0f;
+                Ds[buf * TB + tid] = ld_ok ? d_next : 0.0f;
             }
-            __syncthreads();
-            if (t0 + TB < tc1) load_rows(t0 + TB);
+        };
+        // every wavefront is past the previous segment's last barrier: both buffers are free
+        load_rows(tc0);
+        store_rows(0);
+        __syncthreads();
+        int cur = 0;
+        for (int t0 = tc0; t0 < tc1; t0 += TB, cur ^= 1) {
+            const bool more = t0 + TB < tc1;
+            if (more) load_rows(t0 + TB);
+            const float *const Qc = Qs + cur * TB * P;
+            const float *const Oc = Os + cur * TB * P;
+            const float *const Lc = Ls + cur * TB;
+            const float *const Dc = Ds + cur * TB;
             const bool edge = t0 + TB > T || u0 + QW > T;
             // This wave's 32 x 32 block of ds leaves as 16-byte stores: lane l takes
             // row l / 2, columns 8 i + 4 (l % 2) .. + 3 for i = 0..3 (one base address,
@@ -502,13 +509,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                     for (int i = 0; i < 4; i++)
                         if (!edge || (row_ok && u0 + dcol + 8 * i < T)) *(floatx4 *)(dsw + 8 * i) = z;
                 }
-                continue;
-            }
+            } else {
             floatx16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int j4 = 0; j4 < HD / 8; j4++) {
-                floatx4 qa = *(const floatx4 *)&Qs[l32 * P + h * (HD / 2) + 4 * j4];
-                floatx4 oa = *(const floatx4 *)&Os[l32 * P + h * (HD / 2) + 4 * j4];
+                floatx4 qa = *(const floatx4 *)&Qc[l32 * P + h * (HD / 2) + 4 * j4];
+                floatx4 oa = *(const floatx4 *)&Oc[l32 * P + h * (HD / 2) + 4 * j4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], kf[4 * j4 + e], s, 0, 0, 0);
@@ -519,17 +525,17 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int tl = row_of(r, h), tt = t0 + tl;
-                    const float p = (tt < u || tt >= T || u >= T) ? 0.0f : exp2_fast(s[r] - Ls[tl]);
+                    const float p = (tt < u || tt >= T || u >= T) ? 0.0f : exp2_fast(s[r] - Lc[tl]);
                     s[r] = p;                      // p
-                    dp[r] = p * (dp[r] - Ds[tl]);  // ds
+                    dp[r] = p * (dp[r] - Dc[tl]);  // ds
                 }
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int tl = row_of(r, h);
-                    const float p = exp2_fast(s[r] - Ls[tl]);
+                    const float p = exp2_fast(s[r] - Lc[tl]);
                     s[r] = p;
-                    dp[r] = p * (dp[r] - Ds[tl]);
+                    dp[r] = p * (dp[r] - Dc[tl]);
                 }
             }
             // ds[t][u] for the dq product goes through this wave's LDS patch (read
@@ -541,15 +547,22 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
 #pragma unroll
                 for (int r = 0; r < 16; r++) Ps[pl + (8 * (r >> 2) + (r & 3)) * PP] = dp[r];
             }
-            // registers 4g..4g+3 hold queries 8g + 4h + 0..3: one 16-byte read of
-            // the transposed tiles per 4 MFMAs
+            // registers 4g..4g+3 hold queries 8g + 4h + 0..3; the B operands are
+            // the rows of those queries at this lane's head dim: four 4-byte LDS
+            // reads per 4 MFMAs (LDS reads issue beside the MFMAs of other
+            // wavefronts, so no transposed copy of the tiles is kept)
+            const int bq = 4 * h * P + l32;
 #pragma unroll
             for (int g = 0; g < 4; g++)
 #pragma unroll
                 for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
                     const int d = 32 * nd + l32;
-                    const floatx4 ob = d < HD ? *(const floatx4 *)&Ot[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
-                    const floatx4 qv = d < HD ? *(const floatx4 *)&Qt[d * PT + 8 * g + 4 * h] : floatx4{0.f, 0.f, 0.f, 0.f};
+                    floatx4 ob, qv;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        ob[i] = d < HD ? Oc[bq + (8 * g + i) * P + 32 * nd] : 0.0f;
+                        qv[i] = d < HD ? Qc[bq + (8 * g + i) * P + 32 * nd] : 0.0f;
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         dv[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[4 * g + i], ob[i], dv[nd], 0, 0, 0);
@@ -572,6 +585,11 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
+            }  // keys after some queries of the block
+            // the next block's tiles into the other buffer (last read in the
+            // previous iteration, before its barrier), then one barrier
+            if (more) store_rows(cur ^ 1);
+            __syncthreads();
         }
         // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
         float *dkb, *dvb;
