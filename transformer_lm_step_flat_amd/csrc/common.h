@@ -26,20 +26,23 @@ __device__ __forceinline__ float wave_max(float v) {
 #define GELU_K 0.7978845608028654f
 #define GELU_A 0.044715f
 
-// tanh(u) = 1 - 2 / (exp(2u) + 1): saturates to +-1 through exp's overflow
+// With r = 1 / (exp(2u) + 1), tanh u = 1 - 2r, so 0.5 (1 + tanh u) = 1 - r and
+// 1 - tanh^2 u = 4 r (1 - r).  r saturates to 0 or 1 through exp's overflow
 // and underflow; its absolute error (a few 1e-7) is what matters here.
-__device__ __forceinline__ float tanh_fast(float u) { return 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f); }
-
-__device__ __forceinline__ float gelu_fwd(float x) {
-    float u = GELU_K * (x + GELU_A * x * x * x);
-    return 0.5f * x * (1.0f + tanh_fast(u));
+__device__ __forceinline__ float gelu_r(float x, float x2) {
+    const float u = GELU_K * x * (1.0f + GELU_A * x2);
+    return 1.0f / (__expf(2.0f * u) + 1.0f);
 }
 
+// gelu(x) = x (1 - r)
+__device__ __forceinline__ float gelu_fwd(float x) { return x * (1.0f - gelu_r(x, x * x)); }
+
 // d gelu / dx = 0.5 (1 + tanh u) + 0.5 x (1 - tanh^2 u) k (1 + 3 a x^2)
+//             = (1 - r) (1 + 2 x r k (1 + 3 a x^2))
 __device__ __forceinline__ float gelu_grad(float x) {
-    float u = GELU_K * (x + GELU_A * x * x * x);
-    float th = tanh_fast(u);
-    return 0.5f * (1.0f + th) + 0.5f * x * (1.0f - th * th) * GELU_K * (1.0f + 3.0f * GELU_A * x * x);
+    const float x2 = x * x;
+    const float r = gelu_r(x, x2);
+    return (1.0f - r) * (1.0f + 2.0f * x * r * (GELU_K + 3.0f * GELU_A * GELU_K * x2));
 }
 
 // Rows of the softmax probabilities (and of their gradient) are written as

@@ -159,12 +159,21 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(float *out, floa
     if (row >= N) return;
     const int C4 = C / 4;
     const floatx4 *x = (const floatx4 *)(inp + (long long)row * C);
-    floatx4 v[NV];
+    floatx4 v[NV], g[NV], bb[NV];
+    // the row and the affine parameters are all requested before the first
+    // reduction, so that only one memory latency sits on the row's path
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        const int k = lane + 64 * i;
+        const int kc = k < C4 ? k : C4 - 1;
+        v[i] = x[kc];
+        g[i] = ((const floatx4 *)w)[kc];
+        bb[i] = ((const floatx4 *)b)[kc];
+    }
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; i++) {
-        int k = lane + 64 * i;
-        v[i] = k < C4 ? x[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+        if (lane + 64 * i >= C4) v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
         sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
     }
     const float m = wave_sum(sum) / C;
@@ -182,10 +191,7 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(float *out, floa
 #pragma unroll
     for (int i = 0; i < NV; i++) {
         int k = lane + 64 * i;
-        if (k < C4) {
-            floatx4 g = ((const floatx4 *)w)[k], bb = ((const floatx4 *)b)[k];
-            o[k] = (v[i] - m) * rs * g + bb;
-        }
+        if (k < C4) o[k] = (v[i] - m) * rs * g[i] + bb[i];
     }
     if (lane == 0) {
         mean[row] = m;
