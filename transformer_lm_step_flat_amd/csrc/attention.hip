@@ -426,66 +426,90 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
     const long long W = (long long)BH * W1;
     const long long lo_g = range_lo(g, W, G), hi_g = range_lo(g + 1, W, G);
     const long long rs = 3LL * C;
-    for (long long it = lo_g; it < hi_g;) {
-        const int bh = (int)(it / W1), rem = (int)(it % W1);
-        int kb = 0;
-        while (kb + 1 < nkb && kq_start(kb + 1, T) <= rem) kb++;
-        const int qfirst = rem - kq_start(kb, T), nq = kq_blocks(kb, T);
-        const int qend = (int)min((long long)nq, qfirst + (hi_g - it));
-        const bool whole = qfirst == 0 && qend == nq;
+    TileLoader<HD, TB> lq, lo;
+    // lse and D of a block's queries (threads tid < TB), loaded with its tiles
+    float lse_next = 0.0f, d_next = 0.0f;
+    bool ld_ok = false;
+    auto load_rows = [&](int bh, int t0) {
+        const int b = bh / NH, hd_off = (bh % NH) * HD;
+        lq.load(qkv + (long long)b * T * rs + hd_off, rs, t0, T, tid);
+        lo.load(dout + (long long)b * T * C + hd_off, C, t0, T, tid);
+        ld_ok = tid < TB && t0 + tid < T;
+        lse_next = lse[(long long)bh * T + (ld_ok ? t0 + tid : 0)];
+        d_next = Dbuf[(long long)bh * T + (ld_ok ? t0 + tid : 0)];
+    };
+    auto store_rows = [&](int buf) {
+        lq.store(Qs + buf * TB * P, P, tid);
+        lo.store(Os + buf * TB * P, P, tid);
+        if (tid < TB) {
+            Ls[buf * TB + tid] = ld_ok ? lse_next * LOG2E : 0.0f;
+            Ds[buf * TB + tid] = ld_ok ? d_next : 0.0f;
+        }
+    };
+    // The segment that starts at iteration `it`: (batch, head), key block and
+    // its query blocks [qfirst, qend).
+    struct Seg {
+        int bh, kb, qfirst, qend;
+    };
+    auto seg_at = [&](long long it) {
+        Seg sg;
+        sg.bh = (int)(it / W1);
+        const int rem = (int)(it % W1);
+        sg.kb = 0;
+        while (sg.kb + 1 < nkb && kq_start(sg.kb + 1, T) <= rem) sg.kb++;
+        sg.qfirst = rem - kq_start(sg.kb, T);
+        sg.qend = (int)min((long long)kq_blocks(sg.kb, T), sg.qfirst + (hi_g - it));
+        return sg;
+    };
+    // A segment's K and V rows (this lane's key, half the head dims per lane
+    // half; a key past T reads row T - 1 and is zeroed when the segment
+    // starts) and its first Q / dO tile are requested before the previous
+    // segment's dk and dv are stored, so that their latency overlaps those stores.
+    float kf[HD / 2], vf[HD / 2];
+    auto request = [&](const Seg &sg) {
+        const int b = sg.bh / NH, hd_off = (sg.bh % NH) * HD;
+        const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
+        const int uk = sg.kb * QBLK + wave * QW + l32, uc = uk < T ? uk : T - 1;
+#pragma unroll
+        for (int j4 = 0; j4 < HD / 8; j4++) {
+            const floatx4 k = *(const floatx4 *)(qb_ptr + C + (long long)uc * rs + h * (HD / 2) + 4 * j4);
+            const floatx4 v = *(const floatx4 *)(qb_ptr + 2 * C + (long long)uc * rs + h * (HD / 2) + 4 * j4);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                kf[4 * j4 + e] = k[e];
+                vf[4 * j4 + e] = v[e];
+            }
+        }
+        load_rows(sg.bh, sg.kb * QBLK + sg.qfirst * TB);
+    };
+    long long it = lo_g;
+    Seg sg = seg_at(it);
+    request(sg);
+    for (;;) {
+        const int bh = sg.bh, kb = sg.kb, qfirst = sg.qfirst, qend = sg.qend;
+        const bool whole = qfirst == 0 && qend == kq_blocks(kb, T);
         const int slot = 2 * g + (it == lo_g ? 0 : 1);
-        it += qend - qfirst;
         const int b = bh / NH, hd_off = (bh % NH) * HD;
         const int u0w = kb * QBLK;
         const int u0 = u0w + wave * QW, u = u0 + l32;
-        const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
-        const float *dob = dout + (long long)b * T * C + hd_off;
-
-        float kf[HD / 2], vf[HD / 2];
+        // K pre-multiplied by scale log2(e); keys past T contribute nothing
 #pragma unroll
-        for (int j4 = 0; j4 < HD / 8; j4++) {
-            const bool ok = u < T;
-            floatx4 k = ok ? *(const floatx4 *)(qb_ptr + C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-            floatx4 v = ok ? *(const floatx4 *)(qb_ptr + 2 * C + (long long)u * rs + h * (HD / 2) + 4 * j4) : floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                kf[4 * j4 + e] = k[e] * (scale * LOG2E);
-                vf[4 * j4 + e] = v[e];
-            }
+        for (int i = 0; i < HD / 2; i++) {
+            kf[i] = u < T ? kf[i] * (scale * LOG2E) : 0.0f;
+            vf[i] = u < T ? vf[i] : 0.0f;
         }
         floatx16 dk[HeadBlocks<HD>::N], dv[HeadBlocks<HD>::N];
 #pragma unroll
         for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) dk[nd] = dv[nd] = zero16();
 
         const int tc0 = u0w + qfirst * TB, tc1 = min(T, u0w + qend * TB);
-        TileLoader<HD, TB> lq, lo;
-        // lse and D of the block's queries (threads tid < TB), loaded with the tiles
-        const float *lse_bh = lse + (long long)bh * T, *D_bh = Dbuf + (long long)bh * T;
-        float lse_next = 0.0f, d_next = 0.0f;
-        bool ld_ok = false;
-        auto load_rows = [&](int t0) {
-            lq.load(qb_ptr, rs, t0, T, tid);
-            lo.load(dob, C, t0, T, tid);
-            ld_ok = tid < TB && t0 + tid < T;
-            lse_next = lse_bh[ld_ok ? t0 + tid : 0];
-            d_next = D_bh[ld_ok ? t0 + tid : 0];
-        };
-        auto store_rows = [&](int buf) {
-            lq.store(Qs + buf * TB * P, P, tid);
-            lo.store(Os + buf * TB * P, P, tid);
-            if (tid < TB) {
-                Ls[buf * TB + tid] = ld_ok ? lse_next * LOG2E : 0.0f;
-                Ds[buf * TB + tid] = ld_ok ? d_next : 0.0f;
-            }
-        };
         // every wavefront is past the previous segment's last barrier: both buffers are free
-        load_rows(tc0);
         store_rows(0);
         __syncthreads();
         int cur = 0;
         for (int t0 = tc0; t0 < tc1; t0 += TB, cur ^= 1) {
             const bool more = t0 + TB < tc1;
-            if (more) load_rows(t0 + TB);
+            if (more) load_rows(bh, t0 + TB);
             const float *const Qc = Qs + cur * TB * P;
             const float *const Oc = Os + cur * TB * P;
             const float *const Lc = Ls + cur * TB;
@@ -591,6 +615,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             if (more) store_rows(cur ^ 1);
             __syncthreads();
         }
+        // the next segment's operands go out before this one's results
+        const long long nxt = it + (qend - qfirst);
+        if (nxt < hi_g) {
+            sg = seg_at(nxt);
+            request(sg);
+        }
         // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
         float *dkb, *dvb;
         long long krs;
@@ -616,6 +646,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
                 }
             }
         }
+        if (nxt >= hi_g) break;
+        it = nxt;
     }  // segments
 }
 
