@@ -20,11 +20,11 @@
 // (plus its partner lane l ^ 32), and the probabilities sit exactly where
 // o^T += V^T p^T needs them as its B operand.  The backward kernel computes
 // s = Q K^T so that a lane owns one key, and p / ds are in place as the A
-// operand of dv += p^T dO and dk += ds^T Q; it also stores ds (coalesced: a
-// register holds one query's 32 consecutive keys across the lanes), and dq =
-// scale ds K is then a causal GEMM over the stored ds.  Reductions over the
-// head dimension use the k-split trick of the GEMM kernel: lane half h walks
-// d = h*HD/2 + j.
+// operand of dv += p^T dO and dk += ds^T Q; it also stores ds (each
+// wavefront's 32 x 32 block through a small LDS patch, as 16-byte row
+// pieces), and dq = scale ds K is then a causal GEMM over the stored ds.
+// Reductions over the head dimension use the k-split trick of the GEMM
+// kernel: lane half h walks d = h*HD/2 + j.
 //
 // Every output element is written by exactly one lane, with sums in a fixed
 // order: results are bitwise reproducible.
