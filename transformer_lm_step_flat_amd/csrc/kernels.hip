@@ -201,21 +201,21 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(float *out, floa
 
 constexpr int COL_CHUNK = 16;  // rows per LayerNorm-backward block (and per partial row)
 
-// LayerNorm backward.  Block b takes rows [16b, 16b+16), wavefront w the
-// rows 16b + w + 4k (k = 0..3), one at a time with the next row's loads
-// issued before the current row's reductions:
+// LayerNorm backward.  Block b takes rows [16b, 16b+16) with nw = 4 or 8
+// wavefronts (blockDim.x / 64), wavefront w the rows 16b + w + nw k, one at a
+// time with the next row's loads issued before the current row's reductions:
 //   xhat = (x - mean) rstd, g = dy * w,
 //   dx (+)= rstd (g - mean_c(g) - xhat mean_c(g xhat)).
 // Per-column sums of dy * xhat and dy are kept per lane, combined over the
-// four wavefronts in a fixed order and written as the block's partial row
+// wavefronts in a fixed order and written as the block's partial row
 // [dw (C) | db (C)].
 template <int NV>
-__global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, float *partial, const float *dout,
+__global__ __launch_bounds__(512) void layernorm_backward_kernel(float *dinp, float *partial, const float *dout,
                                                                  const float *inp, const float *w,
                                                                  const float *mean, const float *rstd, int N, int C,
                                                                  int accumulate) {
-    extern __shared__ floatx4 lds4[];  // [4][2C/4]
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    extern __shared__ floatx4 lds4[];  // [nw][2C/4]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int C4 = C / 4;
     floatx4 wv[NV], dwacc[NV], dbacc[NV];
 #pragma unroll
@@ -247,8 +247,8 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, fl
         rsn = rstd[rr];
     };
     fetch(r0);
-    for (int k = 0; k < COL_CHUNK / 4; k++) {
-        const int row = r0 + 4 * k;
+    for (int k = 0; k < COL_CHUNK / nw; k++) {
+        const int row = r0 + nw * k;
         if (row >= N) break;
         floatx4 xc[NV], dc[NV], oc[NV];
         const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, fl
         // prefetch the next row while reducing this one (wide rows: registers
         // would spill, so they load each row when it is reached)
         constexpr bool kPrefetch = NV <= 4;
-        if (kPrefetch && k + 1 < COL_CHUNK / 4) fetch(row + 4);
+        if (kPrefetch && k + 1 < COL_CHUNK / nw) fetch(row + nw);
         floatx4 xh[NV], g[NV];
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, fl
             const int kk = lane + 64 * i;
             if (kk < C4) dx[kk] = oc[i] + rs * (g[i] - mg - xh[i] * mgx);
         }
-        if (!kPrefetch && k + 1 < COL_CHUNK / 4) fetch(row + 4);
+        if (!kPrefetch && k + 1 < COL_CHUNK / nw) fetch(row + nw);
     }
 #pragma unroll
     for (int i = 0; i < NV; i++) {
@@ -295,8 +295,11 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(float *dinp, fl
     }
     __syncthreads();
     floatx4 *out = (floatx4 *)(partial + (long long)blockIdx.x * 2 * C);
-    for (int c = threadIdx.x; c < 2 * C4; c += blockDim.x)
-        out[c] = ((lds4[c] + lds4[2 * C4 + c]) + lds4[4 * C4 + c]) + lds4[6 * C4 + c];
+    for (int c = threadIdx.x; c < 2 * C4; c += blockDim.x) {
+        floatx4 t = lds4[c];
+        for (int q = 1; q < nw; q++) t += lds4[q * 2 * C4 + c];
+        out[c] = t;
+    }
 }
 
 // dst[i] (+)= sum_{p < P} src[p*ld + i], 4 consecutive i per thread, p in order.
@@ -820,9 +823,12 @@ hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partia
     if (C % 4 || C > 2048) return hipErrorInvalidValue;
     int nv = (C / 4 + 63) / 64;
     const int P = ln_partials(N);
-    const size_t lds = (size_t)8 * C * sizeof(float);
-    LN_DISPATCH(nv, layernorm_backward_kernel, dim3(P), dim3(256), lds, s, dinp, partial, dout, inp, w, mean, rstd, N,
-                C, accumulate ? 1 : 0);
+    // eight wavefronts per block where their column sums fit in 64 KB of LDS
+    // (twice the rows in flight per CU), else four
+    const int nw = (size_t)8 * 2 * C * sizeof(float) <= 65536 ? 8 : 4;
+    const size_t lds = (size_t)nw * 2 * C * sizeof(float);
+    LN_DISPATCH(nv, layernorm_backward_kernel, dim3(P), dim3(64 * nw), lds, s, dinp, partial, dout, inp, w, mean,
+                rstd, N, C, accumulate ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !dw) return e;  // no dw: the caller sums the partials later
     hipLaunchKernelGGL(sum_partials_split_kernel, dim3(grid_for(2 * C / 4, 16)), dim3(256), 0, s, dw, db,
