@@ -31,7 +31,8 @@ __device__ __forceinline__ float wave_max(float v) {
 // and underflow; its absolute error (a few 1e-7) is what matters here.
 __device__ __forceinline__ float gelu_r(float x, float x2) {
     const float u = GELU_K * x * (1.0f + GELU_A * x2);
-    return 1.0f / (__expf(2.0f * u) + 1.0f);
+    // the hardware reciprocal (about 1 ulp): exp(2u) + 1 >= 1, and 1 / inf = 0
+    return __builtin_amdgcn_rcpf(__expf(2.0f * u) + 1.0f);
 }
 
 // gelu(x) = x (1 - r)

@@ -24,6 +24,12 @@ namespace {
 
 constexpr int GEMM_THREADS = 256;
 
+// An epilogue mode as a type, so that one epilogue body serves every mode
+template <int V>
+struct EpiTag {
+    static constexpr int value = V;
+};
+
 struct GemmArgs {
     const float *A, *B;
     float *C, *C2;
@@ -363,44 +369,59 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
     // that live in memory (C for accumulation, the residual or the GELU
     // input) are loaded for a whole 32 x 32 block before any arithmetic, so
     // that their latencies overlap.
-    const int epi = p.epi;
-    const float *src = epi == EPI_ACCUM ? C : p.aux;
-    const long long lds_ = epi == EPI_ACCUM ? p.ldc : p.ldaux;
-    const bool gather = epi == EPI_ACCUM || epi == EPI_RESID || epi == EPI_GELU_BWD;
+    // The mode is dispatched once, outside the element loops; each mode's loop
+    // has no per-element branching on it.  Whole tiles (FULL) skip the bounds
+    // tests, and a row's address is the block's row base plus a multiple of ldc.
+    auto epilogue = [&](auto tag) {
+        constexpr int EPI = decltype(tag)::value;
+        constexpr bool gather = EPI == EPI_ACCUM || EPI == EPI_RESID || EPI == EPI_GELU_BWD;
+        const float *src = EPI == EPI_ACCUM ? C : p.aux;
+        const long long lds_ = EPI == EPI_ACCUM ? p.ldc : p.ldaux;
+        const long long ldc = p.ldc;
 #pragma unroll
-    for (int i = 0; i < MI; i++)
+        for (int i = 0; i < MI; i++)
 #pragma unroll
-        for (int j = 0; j < NI; j++) {
-            const int n = n0 + wn * WN + j * 32 + l32;
-            if (n >= N) continue;
-            float ext[16];
+            for (int j = 0; j < NI; j++) {
+                const int n = n0 + wn * WN + j * 32 + l32;
+                if (!FULL && n >= N) continue;
+                const int mb = m0 + wm * WM + i * 32 + h * 4;  // row of register 0
+                float ext[16];
+                if constexpr (gather) {
+                    const float *sb = src + (long long)mb * lds_ + n;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                ext[r] = (gather && m < M) ? src[(long long)m * lds_ + n] : 0.0f;
-            }
-            const float bn = p.bias ? p.bias[n] : 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                if (m >= M) continue;
-                const float v = p.alpha * acc[i][j][r];
-                const float x = ext[r];
-                const long long off = (long long)m * p.ldc + n;
-                switch (epi) {
-                    case EPI_STORE: C[off] = v + bn; break;
-                    case EPI_ACCUM: C[off] = x + v; break;
-                    case EPI_RESID: C[off] = v + bn + x; break;
-                    case EPI_GELU: {
-                        const float pre = v + bn;
-                        C[off] = pre;
-                        p.C2[off] = gelu_fwd(pre);
-                        break;
+                    for (int r = 0; r < 16; r++) {
+                        const int dr = (r >> 2) * 8 + (r & 3);
+                        ext[r] = (FULL || mb + dr < M) ? sb[dr * lds_] : 0.0f;
                     }
-                    case EPI_GELU_BWD: C[off] = v * gelu_grad(x); break;
+                }
+                const float bn = p.bias ? p.bias[n] : 0.0f;
+                float *cb = C + (long long)mb * ldc + n;
+                float *c2b = EPI == EPI_GELU ? p.C2 + (long long)mb * ldc + n : nullptr;
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int dr = (r >> 2) * 8 + (r & 3);
+                    if (!FULL && mb + dr >= M) continue;
+                    const float v = p.alpha * acc[i][j][r];
+                    const long long off = dr * ldc;
+                    if constexpr (EPI == EPI_STORE) cb[off] = v + bn;
+                    if constexpr (EPI == EPI_ACCUM) cb[off] = ext[r] + v;
+                    if constexpr (EPI == EPI_RESID) cb[off] = v + bn + ext[r];
+                    if constexpr (EPI == EPI_GELU) {
+                        const float pre = v + bn;
+                        cb[off] = pre;
+                        c2b[off] = gelu_fwd(pre);
+                    }
+                    if constexpr (EPI == EPI_GELU_BWD) cb[off] = v * gelu_grad(ext[r]);
                 }
             }
-        }
+    };
+    switch (p.epi) {
+        case EPI_STORE: epilogue(EpiTag<EPI_STORE>{}); break;
+        case EPI_ACCUM: epilogue(EpiTag<EPI_ACCUM>{}); break;
+        case EPI_RESID: epilogue(EpiTag<EPI_RESID>{}); break;
+        case EPI_GELU: epilogue(EpiTag<EPI_GELU>{}); break;
+        case EPI_GELU_BWD: epilogue(EpiTag<EPI_GELU_BWD>{}); break;
+    }
 }
 
 template <int BM, int BN, bool AK, bool BKC, int BK, int LB, bool FULL>
