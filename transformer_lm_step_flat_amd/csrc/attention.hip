@@ -299,7 +299,10 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
 #pragma unroll
                 for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[mb][r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        {
+            const float2 hp = half_pair(mx);  // lanes i and i + 32 hold other keys of one query
+            mx = fmaxf(hp.x, hp.y);
+        }
         // a query that sees no key yet keeps m = -inf; exponentiate against 0 then
         const float mref = mx == -INFINITY ? 0.0f : mx;
         const float alpha = exp2_fast(m - mref);
@@ -312,7 +315,10 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
                 s[mb][r] = p;
                 ps += p;
             }
-        ps += __shfl_xor(ps, 32, WAVE);
+        {
+            const float2 hp = half_pair(ps);
+            ps = hp.x + hp.y;
+        }
         lsum = lsum * alpha + ps;
         m = mx;
 #pragma unroll

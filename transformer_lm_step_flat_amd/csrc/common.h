@@ -8,18 +8,50 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 #define WAVE 64
 
-// Sum over the 64 lanes of a wavefront; every lane gets the total.  The
-// butterfly order is fixed, so the result is deterministic.
+// Lane exchanges inside rows of 16 lanes (DPP): 0xB1 swaps neighbours
+// (lane ^ 1), 0x4E swaps pairs (lane ^ 2), 0x141 reverses each half-row of 8
+// lanes, 0x140 reverses each row of 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront, which must all be active; every lane
+// gets the same total.  Each step adds a lane's value to that of a partner
+// holding the complementary partial sum (neighbour, pair, mirrored quad,
+// mirrored half-row), so after four steps every lane of a row of 16 holds
+// the row's sum, bit for bit; the four row sums are then read as scalars
+// and added in a fixed order.  No LDS round trips; deterministic.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-    return v;
+    v += dpp_move<0xB1>(v);
+    v += dpp_move<0x4E>(v);
+    v += dpp_move<0x141>(v);
+    v += dpp_move<0x140>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-    return v;
+    v = fmaxf(v, dpp_move<0xB1>(v));
+    v = fmaxf(v, dpp_move<0x4E>(v));
+    v = fmaxf(v, dpp_move<0x141>(v));
+    v = fmaxf(v, dpp_move<0x140>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The values of lanes i mod 32 and i mod 32 + 32, in every lane i: one
+// v_permlane32_swap exchanges the two halves of the wavefront in the VALU,
+// without the LDS round trip of a general lane shuffle.
+__device__ __forceinline__ float2 half_pair(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // tanh-approximate GELU, 0.5 x (1 + tanh(k (x + 0.044715 x^3))), k = sqrt(2/pi).
