@@ -31,6 +31,9 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
 # file records a hash of the sources that decide that kernel's launches, and
 # the figure is reported only while they are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_124m_b4_t1024.json")
+# Per-kernel launch durations from a rocprofv3 --kernel-trace --stats run of
+# this script (no counters, so the kernels run as in an ordinary step).
+KTRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_gpt2_124m_b4_t1024.json")
 KERNEL_SOURCES = ["gemm.hip", "gemm.h", "attention.hip", "attention.h", "kernels.hip", "kernels.h", "common.h",
                   "gpt2.hip"]
 
@@ -54,6 +57,39 @@ def measured_traffic(kernel: str, config: str):
     if t.get("kernel") != kernel or t.get("config") != config or t.get("sources_sha256") != sources_sha256():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def traced_duration(kernel: str, config: str):
+    """Average launch duration (ms) of `kernel` in the committed kernel-trace
+    summary, or None when it is missing or its sources have changed since."""
+    try:
+        with open(KTRACE_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("config") != config or t.get("sources_sha256") != sources_sha256():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k["avg_ms"]
+
+
+def host_cpu():
+    """CPU model, online CPUs and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"cpu_model": model, "nproc_online": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
 
 
 def copy_calibration(mib: int):
@@ -92,9 +128,10 @@ def cpu_baseline(cfg, T_sample: int):
     oracle.adamw(p, g, m, v, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1)
     dt = time.perf_counter() - t0
     R.close()
-    return {"value": T_sample / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"one full step (forward, backward, AdamW over all {p.size} parameters) of the same model on "
-                      f"1 sequence x {T_sample} ids of the same seeded stream, float64; {dt:.1f} s wall"}
+    return dict({"value": T_sample / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+                 "sample": f"one full step (forward, backward, AdamW over all {p.size} parameters) of the same model "
+                           f"on 1 sequence x {T_sample} ids of the same seeded stream, float64; {dt:.1f} s wall"},
+                **host_cpu())
 
 
 def _short_kernel_name(n: str) -> str:
@@ -161,6 +198,31 @@ def pmc_summary(fetch_csv: str, write_csv: str, steps: int, copy_mib: int, comma
         json.dump(out, fh, indent=1)
     print(f"\nDominant kernel `{dom}`: {(fb + wb) / 1e6:.1f} MB of HBM traffic per launch "
           f"(read {fb / 1e6:.1f}, write {wb / 1e6:.1f}); written to {os.path.relpath(TRAFFIC_FILE, ROOT)}.")
+
+
+def kt_summary(stats_csv: str, command: str, config: str):
+    """Summarise a rocprofv3 --kernel-trace --stats run of this script
+    (its kernel_stats.csv): per kernel, launches and average duration.
+    Writes Markdown to stdout and the per-kernel averages to KTRACE_FILE."""
+    import csv
+    rows = []
+    for r in csv.DictReader(open(stats_csv)):
+        name = _short_kernel_name(r["Name"])
+        rows.append((name, int(r["Calls"]), float(r["TotalDurationNs"]) * 1e-6, float(r["AverageNs"]) * 1e-6,
+                     float(r["MinNs"]) * 1e-6, float(r["MaxNs"]) * 1e-6))
+    rows.sort(key=lambda x: -x[2])
+    print(f"# Kernel durations from a kernel trace (no counters): {config}\n")
+    print(f"Command: `{command}`\n")
+    print("| kernel | launches | total ms | avg ms | min ms | max ms |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, n, tot, avg, mn, mx in rows:
+        print(f"| `{name}` | {n} | {tot:.3f} | {avg:.4f} | {mn:.4f} | {mx:.4f} |")
+    out = {"config": config, "sources_sha256": sources_sha256(), "command": command,
+           "kernels": {name: {"launches": n, "avg_ms": avg, "min_ms": mn, "max_ms": mx}
+                       for name, n, tot, avg, mn, mx in rows}}
+    with open(KTRACE_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"\nPer-kernel averages written to {os.path.relpath(KTRACE_FILE, ROOT)}.")
 
 
 def sq_summary(sq_csv: str, command: str, config: str):
@@ -237,7 +299,12 @@ def main():
                     help="summarise two rocprofv3 --pmc runs of this script and exit")
     ap.add_argument("--pmc-command", default="", help="the profiled command, quoted in the summary")
     ap.add_argument("--sq-summary", metavar="SQ_CSV", help="summarise a rocprofv3 --pmc run of SQ counters and exit")
+    ap.add_argument("--kt-summary", metavar="STATS_CSV",
+                    help="summarise a rocprofv3 --kernel-trace --stats run (kernel_stats.csv) and exit")
     args = ap.parse_args()
+    if args.kt_summary:
+        kt_summary(args.kt_summary, args.pmc_command, args.config)
+        return
     if args.sq_summary:
         sq_summary(args.sq_summary, args.pmc_command, args.config)
         return
@@ -351,11 +418,19 @@ def main():
         avg_ms = d["ms"] / d["launches"]
         achieved = per_launch / (avg_ms * 1e-3) / (1e12 if bound == "mfma" else 1e9)
         all_flops = sum(e["flops"] for e in by_kernel.values()) / args.steps
+        alg_bytes = d["bytes"] / d["launches"]
+        traffic = measured_traffic(d["name"], args.config)
+        traced_ms = traced_duration(d["name"], args.config)
         roofline = {"bound": bound, "achieved": achieved, "peak": peak,
                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak,
-                    "traffic": measured_traffic(d["name"], args.config),
+                    "traffic": traffic,
                     "kernel": d["name"], "avg_launch_ms": avg_ms, "launches_per_step": d["launches"] / args.steps,
                     "algorithmic_per_launch": per_launch,
+                    "algorithmic_bytes_per_launch": alg_bytes,
+                    "traffic_over_algorithmic_bytes": None if traffic is None else traffic / alg_bytes,
+                    "kernel_trace_avg_launch_ms": traced_ms,
+                    "frac_by_kernel_trace": None if traced_ms is None else
+                    per_launch / (traced_ms * 1e-3) / (1e12 if bound == "mfma" else 1e9) / peak,
                     "step_flops": all_flops,
                     "step_mfma_frac": all_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP32_TFLOPS,
                     "frac_of_measured_peak": achieved / (peaks["mfma_fp32_tflops"] if bound == "mfma"

@@ -85,11 +85,16 @@ typedef struct gpt2_model gpt2_model; /* opaque handle */
 /* Which table gpt2_layout reads. */
 enum { GPT2_PARAMS = 0, GPT2_ACTS = 1 };
 
-/* Buffer sizes for (cfg, B, T).  Host only; B >= 1, 1 <= T <= max_seq_len. */
+/* Buffer sizes for (cfg, B, T): the constant footprint allocated once up
+ * front (QbitAI llm.c article, "手動實現每個層前向/反向傳播": every tensor a fixed
+ * offset into memory allocated at the start).  Host only; B >= 1,
+ * 1 <= T <= max_seq_len. */
 gpt2_status gpt2_query_sizes(const gpt2_config *cfg, int B, int T, gpt2_sizes *out);
 
-/* Entry idx of a layout table (host only).  GPT2_PARAMS has 16 entries, in
- * this order, each stacked over layers where it is per layer:
+/* Entry idx of a layout table (host only).  The tensor order is explicit (the
+ * GeekNews page, "Nạp trọng số", on a flat fp32 weight file whose tensors
+ * must be placed in a stated order).  GPT2_PARAMS has 16 entries, in this
+ * order, each stacked over layers where it is per layer:
  *   wte[Vp][C] wpe[maxT][C] ln1w[L][C] ln1b[L][C] qkvw[L][3C][C] qkvb[L][3C]
  *   attprojw[L][C][C] attprojb[L][C] ln2w[L][C] ln2b[L][C] fcw[L][4C][C]
  *   fcb[L][4C] fcprojw[L][C][4C] fcprojb[L][C] lnfw[C] lnfb[C]
@@ -113,41 +118,62 @@ gpt2_status gpt2_query_sizes(const gpt2_config *cfg, int B, int T, gpt2_sizes *o
 gpt2_status gpt2_layout(const gpt2_config *cfg, int B, int T, int which, int idx,
                         const char **name, size_t *offset, size_t *count);
 
-/* Create a handle over caller buffers for fixed (B, T).  If init_params_host
- * is non-NULL it is copied (params floats, host memory) into dev->params;
- * otherwise dev->params is left as is.  grads, adam_m and adam_v are set to
+/* Create a handle over caller buffers for fixed (B, T) (the one allocation
+ * made at the start, QbitAI llm.c article, "手動實現每個層前向/反向傳播").  If
+ * init_params_host is non-NULL it is copied (params floats, host memory) into
+ * dev->params; otherwise dev->params is left as is.  grads, adam_m and adam_v are set to
  * zero.  hip_stream is a hipStream_t (NULL = the null stream).  The buffers
  * must hold at least the counts of gpt2_query_sizes. */
 gpt2_status gpt2_build(const gpt2_config *cfg, int B, int T, const gpt2_buffers *dev,
                        const float *init_params_host, void *hip_stream, gpt2_model **out);
 
-/* Forward pass over one batch.  inputs and targets are DEVICE pointers to
- * B*T int32 token ids, row-major [B][T], already resident in HBM (targets
- * may be NULL: logits only).  With targets, the per-position losses, their
- * mean, and d(mean loss)/d(logits) (in place of the logits) are produced,
- * which enables gpt2_backward.  If mean_loss is non-NULL the call waits for
- * the stream and stores the mean loss (host float); it then also reports
- * GPT2_ERANGE if any id was outside [0, V).  Ids are checked on the device:
- * out-of-range ids are clamped for memory safety and raise a flag that the
- * next waiting call (this one with mean_loss, or gpt2_sync) reports. */
+/* Forward pass over one batch (the forward half of the loop in the QbitAI
+ * llm.c article, "手動實現每個層前向/反向傳播"; the layer order of the GeekNews
+ * page, "Phần lõi Transformer"; int32 token streams as in the InfoQ article's
+ * walkthrough).  inputs and targets are DEVICE pointers to B*T int32 token
+ * ids, row-major [B][T], already resident in HBM (targets may be NULL:
+ * logits only); they are copied into the model's own buffer, so the caller
+ * may reuse them once the call's work has run.  With targets, the
+ * per-position losses, their mean, and d(mean loss)/d(logits) (in place of
+ * the logits) are produced, which enables gpt2_backward.
+ *
+ * Ids are checked on the device, not on the host (no synchronization).  An id
+ * outside [0, V) sets the model's error flag; for memory safety it is then
+ * read as the nearest valid id.  While the flag is set the step changes no
+ * trainable state: the loss gradient of every batch is written as zeros
+ * (losses as NaN), so gpt2_backward adds exact zeros to grads, and
+ * gpt2_update leaves params, adam_m and adam_v untouched.  The flag stays set
+ * until a waiting call reports it: this call when mean_loss is non-NULL
+ * (then it waits for the stream, stores the mean loss in the host float
+ * *mean_loss and returns GPT2_ERANGE), or gpt2_sync.  After such a report the
+ * batch may not be back-propagated (gpt2_backward returns GPT2_ESTATE until
+ * the next forward with targets). */
 gpt2_status gpt2_forward(gpt2_model *model, const int32_t *inputs, const int32_t *targets,
                          float *mean_loss);
 
-/* grads = 0 over the whole parameter buffer. */
+/* grads = 0 over the whole parameter buffer (the gradients are accumulated
+ * by gpt2_backward, so the caller clears them once per step). */
 gpt2_status gpt2_zero_grad(gpt2_model *model);
 
-/* Backward pass of the mean loss of the last forward-with-targets:
- * grads += d(mean loss)/d(params).  GPT2_ESTATE without such a forward. */
+/* Backward pass of the mean loss of the last forward-with-targets, layer by
+ * layer in reverse (the hand-written backward of each layer in the QbitAI
+ * llm.c article, "手動實現每個層前向/反向傳播"): grads += d(mean loss)/d(params).
+ * GPT2_ESTATE without such a forward. */
 gpt2_status gpt2_backward(gpt2_model *model);
 
-/* AdamW over all params: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+/* The parameter update that closes the loop (Adam at lr 1e-4 in the InfoQ
+ * article's walkthrough; AdamW with decoupled weight decay here, identical to
+ * Adam at weight_decay 0), one pass over the flat buffers:
+ * m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
  * theta -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + weight_decay theta).
- * t is the 1-based step count (GPT2_EINVAL if t < 1). */
+ * t is the 1-based step count (GPT2_EINVAL if t < 1).  Skipped on the device
+ * while the error flag of gpt2_forward is set. */
 gpt2_status gpt2_update(gpt2_model *model, float lr, float beta1, float beta2, float eps,
                         float weight_decay, int t);
 
 /* Wait for the stream; GPT2_ERANGE if an out-of-range id was seen since the
- * last report, GPT2_EDEVICE on a HIP error. */
+ * last report (the flag is then cleared, and gpt2_backward needs a new
+ * forward with targets), GPT2_EDEVICE on a HIP error. */
 gpt2_status gpt2_sync(gpt2_model *model);
 
 /* Per-launch timing of the step (tracing).  While enabled, every kernel

@@ -198,6 +198,63 @@ def test_errors_are_reported(g):
     M.close()
 
 
+def test_bad_id_changes_no_trainable_state(g):
+    """forward (no loss read-back) on a batch with one out-of-range id, then
+    backward, update and sync: sync reports GPT2_ERANGE and grads, params,
+    m and v are bit-identical to before; backward then needs a new forward."""
+    import torch
+    cfg = CASES["tiny"]
+    B, T = cfg["B"], cfg["T"]
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, synth.init_params(cfg), B, T))
+    inp, tgt = synth.batch(cfg)
+    # one good step first, so that grads, m and v are nonzero
+    M.forward(dev_ids(inp), dev_ids(tgt), want_loss=False)
+    M.zero_grad()
+    M.backward()
+    M.update(lr=1e-4, t=1)
+    M.sync()
+    before = [t.clone() for t in (M.grads, M.params, M.adam_m, M.adam_v)]
+    assert float(before[2].abs().max()) > 0 and float(before[0].abs().max()) > 0
+    for bad_where in ("input", "target"):
+        bi, bt = inp.copy(), tgt.copy()
+        if bad_where == "input":
+            bi[2, 9] = cfg["V"] + 3
+        else:
+            bt[0, T - 1] = -1
+        M.forward(dev_ids(bi), dev_ids(bt), want_loss=False)
+        M.backward()  # no zero_grad: grads accumulate, and must not move
+        M.update(lr=1e-4, t=2)
+        with pytest.raises(g.Gpt2Error) as e:
+            M.sync()
+        assert e.value.status == g.GPT2_ERANGE
+        torch.cuda.synchronize()
+        for name, a, b in zip(("grads", "params", "adam_m", "adam_v"), before,
+                              (M.grads, M.params, M.adam_m, M.adam_v)):
+            assert torch.equal(a, b), (bad_where, name)
+        # the reported batch may not be back-propagated
+        with pytest.raises(g.Gpt2Error) as e:
+            M.backward()
+        assert e.value.status == g.GPT2_ESTATE
+    # the mean-loss path reports at once and also refuses the backward
+    bi = inp.copy()
+    bi[0, 0] = -5
+    with pytest.raises(g.Gpt2Error) as e:
+        M.forward(dev_ids(bi), dev_ids(tgt))
+    assert e.value.status == g.GPT2_ERANGE
+    with pytest.raises(g.Gpt2Error) as e:
+        M.backward()
+    assert e.value.status == g.GPT2_ESTATE
+    # a good batch afterwards trains as usual
+    loss = M.forward(dev_ids(inp), dev_ids(tgt))
+    assert math.isfinite(loss)
+    M.zero_grad()
+    M.backward()
+    M.update(lr=1e-4, t=2)
+    M.sync()
+    assert not torch.equal(before[1], M.params)
+    M.close()
+
+
 def test_zero_embeddings_give_ln_v(g):
     """wte = 0 makes every logit 0: loss = ln V exactly and dlogits = (1/V - onehot)/BT."""
     cfg = CASES["tiny"]

@@ -847,7 +847,7 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
         HIPCK(m, linear_fwd(logits, lnf, P + l.poff[0], nullptr, BT, C, l.Vp, EPI_STORE, nullptr, nullptr, s));
     }
     if (targets) {
-        KRUN(m, k_crossentropy_name(l.Vp), 8.0 * BT * l.Vp, k_crossentropy(logits, A + l.aoff[A_LOSSES], targets, BT, l.V, l.Vp, 1.0f / BT, s));
+        KRUN(m, k_crossentropy_name(l.Vp), 8.0 * BT * l.Vp, k_crossentropy(logits, A + l.aoff[A_LOSSES], targets, BT, l.V, l.Vp, 1.0f / BT, err, s));
         KRUN(m, "mean_kernel", 4.0 * BT, k_mean(A + l.aoff[A_LOSS], A + l.aoff[A_LOSSES], BT, s));
         m->have_targets = true;
     }
@@ -860,6 +860,7 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
         *mean_loss = h_loss;
         if (h_err) {
             HIPCK(m, k_fill_i32(err, 1, 0, s));
+            m->have_targets = false;  // this batch's loss gradient is zero and may not be used
             return fail(m, GPT2_ERANGE, h_err & 1 ? "an input id is outside [0, vocab_size)"
                                                   : "a target id is outside [0, vocab_size)");
         }
@@ -989,7 +990,7 @@ gpt2_status gpt2_update(gpt2_model *m, float lr, float beta1, float beta2, float
     if (t < 1) return fail(m, GPT2_EINVAL, "t must be >= 1");
     double c1 = 1.0 - std::pow((double)beta1, t), c2 = 1.0 - std::pow((double)beta2, t);
     KRUN(m, "adamw_kernel", 28.0 * m->lo.nparams, k_adamw(m->buf.params, m->buf.grads, m->buf.adam_m, m->buf.adam_v, m->lo.nparams, lr, beta1, beta2,
-                     eps, weight_decay, (float)c1, (float)c2, m->stream));
+                     eps, weight_decay, (float)c1, (float)c2, m->buf.iwork + m->lo.i_err, m->stream));
     return GPT2_OK;
 }
 
@@ -1000,6 +1001,7 @@ gpt2_status gpt2_sync(gpt2_model *m) {
     HIPCK(m, hipStreamSynchronize(m->stream));
     if (h_err) {
         HIPCK(m, k_fill_i32(m->buf.iwork + m->lo.i_err, 1, 0, m->stream));
+        m->have_targets = false;
         return fail(m, GPT2_ERANGE, "an id was outside [0, vocab_size)");
     }
     return GPT2_OK;
@@ -1163,7 +1165,7 @@ gpt2_status gpt2k_gelu_backward(float *dinp, const float *inp, const float *dout
 gpt2_status gpt2k_crossentropy(float *logits, float *losses, float *loss, const int32_t *targets, int BT, int V,
                                int Vp, void *stream) {
     if (V <= 0 || Vp < V || BT <= 0) return fail(nullptr, GPT2_EINVAL, "bad crossentropy shape");
-    KCK(k_crossentropy(logits, losses, targets, BT, V, Vp, 1.0f / BT, (hipStream_t)stream));
+    KCK(k_crossentropy(logits, losses, targets, BT, V, Vp, 1.0f / BT, nullptr, (hipStream_t)stream));
     KCK(k_mean(loss, losses, BT, (hipStream_t)stream));
     return GPT2_OK;
 }
@@ -1194,7 +1196,7 @@ gpt2_status gpt2k_adamw(float *params, const float *grads, float *m, float *v, s
                         float beta2, float eps, float weight_decay, int t, void *stream) {
     if (t < 1) return fail(nullptr, GPT2_EINVAL, "t must be >= 1");
     double c1 = 1.0 - std::pow((double)beta1, t), c2 = 1.0 - std::pow((double)beta2, t);
-    KCK(k_adamw(params, grads, m, v, n, lr, beta1, beta2, eps, weight_decay, (float)c1, (float)c2,
+    KCK(k_adamw(params, grads, m, v, n, lr, beta1, beta2, eps, weight_decay, (float)c1, (float)c2, nullptr,
                 (hipStream_t)stream));
     return GPT2_OK;
 }

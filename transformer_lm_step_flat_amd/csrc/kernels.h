@@ -57,9 +57,12 @@ hipError_t k_attn_softmax_backward(float *dp, const float *att, long long nrows,
 
 // Fused softmax cross-entropy over logits rows of width Vp (first V real):
 // losses[r] = logsumexp - z[target]; logits <- (softmax - onehot) * dscale
-// (0 in the padded columns).
+// (0 in the padded columns).  If gate is non-null and *gate != 0 (an id of
+// the batch was out of range), every row of the loss gradient is written as
+// zeros and every loss as NaN instead, so that a backward over it adds
+// nothing to the gradients.
 hipError_t k_crossentropy(float *logits, float *losses, const int32_t *tgt, int BT, int V, int Vp, float dscale,
-                          hipStream_t s);
+                          const int32_t *gate, hipStream_t s);
 // Name of the kernel k_crossentropy launches for this padded vocabulary.
 const char *k_crossentropy_name(int Vp);
 // loss[0] = sum(losses) / n  (fixed order)
@@ -69,5 +72,7 @@ hipError_t k_mean(float *loss, const float *losses, int n, hipStream_t s);
 hipError_t k_gelu_forward(float *out, const float *inp, size_t n, hipStream_t s);
 hipError_t k_gelu_backward(float *dinp, const float *inp, const float *dout, size_t n, hipStream_t s);
 
+// AdamW over n floats; if gate is non-null and *gate != 0 nothing is read or
+// written (the update of a batch with an out-of-range id is skipped).
 hipError_t k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float b1, float b2,
-                   float eps, float wd, float c1, float c2, hipStream_t s);
+                   float eps, float wd, float c1, float c2, const int32_t *gate, hipStream_t s);

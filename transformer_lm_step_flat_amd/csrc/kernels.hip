@@ -539,11 +539,16 @@ __device__ __forceinline__ void online_combine(float &m, float &s, float m2, flo
 // (max, sum of exp) per thread over the V real columns, combined across the
 // block.  Pass 2: overwrite the row with (p - onehot) * dscale.
 __global__ __launch_bounds__(256) void crossentropy_kernel(float *logits, float *losses, const int32_t *tgt,
-                                                           int V, int Vp, float dscale) {
+                                                           int V, int Vp, float dscale, const int32_t *gate) {
     __shared__ float sm[4], ss[4];
     const int row = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float *z = logits + (long long)row * Vp;
+    if (gate && *gate) {  // a bad id in the batch: zero loss gradient
+        for (int v4 = threadIdx.x; v4 * 4 < Vp; v4 += 256) ((floatx4 *)z)[v4] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (threadIdx.x == 0) losses[row] = __builtin_nanf("");
+        return;
+    }
     float m = -INFINITY, s = 0.f;
     for (int v4 = threadIdx.x; v4 * 4 < V; v4 += 256) {
         floatx4 x = ((const floatx4 *)z)[v4];
@@ -595,12 +600,17 @@ __global__ __launch_bounds__(256) void crossentropy_kernel(float *logits, float 
 // are reduced over the block in a fixed order.
 template <int NV4>
 __global__ __launch_bounds__(1024) void crossentropy_reg_kernel(float *logits, float *losses, const int32_t *tgt,
-                                                                int V, int Vp, float dscale) {
+                                                                int V, int Vp, float dscale, const int32_t *gate) {
     __shared__ float red[16];
     const int row = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     floatx4 *z = (floatx4 *)(logits + (long long)row * Vp);
     const int n4 = Vp / 4;
+    if (gate && *gate) {  // a bad id in the batch: zero loss gradient
+        for (int i = tid; i < n4; i += 1024) z[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (tid == 0) losses[row] = __builtin_nanf("");
+        return;
+    }
     const int y = clamp_id(tgt[row], V);
     floatx4 x[NV4];
 #pragma unroll
@@ -700,7 +710,8 @@ __global__ __launch_bounds__(256) void gelu_backward_kernel(floatx4 *dinp, const
 constexpr int ADAMW_U = 4;
 __global__ __launch_bounds__(256) void adamw_kernel(floatx4 *params, const floatx4 *grads, floatx4 *m, floatx4 *v,
                                                     size_t n4, float lr, float b1, float b2, float eps, float wd,
-                                                    float inv_c1, float inv_c2) {
+                                                    float inv_c1, float inv_c2, const int32_t *gate) {
+    if (gate && *gate) return;  // the batch had an out-of-range id: no update
     const size_t base = (size_t)blockIdx.x * 256 * ADAMW_U + threadIdx.x;
     floatx4 g[ADAMW_U], mm[ADAMW_U], vv[ADAMW_U], p[ADAMW_U];
 #pragma unroll
@@ -889,17 +900,17 @@ hipError_t k_attn_softmax_backward(float *dp, const float *att, long long nrows,
 }
 
 hipError_t k_crossentropy(float *logits, float *losses, const int32_t *tgt, int BT, int V, int Vp, float dscale,
-                          hipStream_t s) {
+                          const int32_t *gate, hipStream_t s) {
     if (Vp % 4) return hipErrorInvalidValue;
     const int n4 = Vp / 4;
     if (n4 <= 1024)
-        hipLaunchKernelGGL(crossentropy_reg_kernel<1>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale);
+        hipLaunchKernelGGL(crossentropy_reg_kernel<1>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale, gate);
     else if (n4 <= 4 * 1024)
-        hipLaunchKernelGGL(crossentropy_reg_kernel<4>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale);
+        hipLaunchKernelGGL(crossentropy_reg_kernel<4>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale, gate);
     else if (n4 <= 13 * 1024)
-        hipLaunchKernelGGL(crossentropy_reg_kernel<13>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale);
+        hipLaunchKernelGGL(crossentropy_reg_kernel<13>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale, gate);
     else
-        hipLaunchKernelGGL(crossentropy_kernel, dim3(BT), dim3(256), 0, s, logits, losses, tgt, V, Vp, dscale);
+        hipLaunchKernelGGL(crossentropy_kernel, dim3(BT), dim3(256), 0, s, logits, losses, tgt, V, Vp, dscale, gate);
     return hipGetLastError();
 }
 
@@ -931,13 +942,13 @@ hipError_t k_gelu_backward(float *dinp, const float *inp, const float *dout, siz
 }
 
 hipError_t k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float b1, float b2,
-                   float eps, float wd, float c1, float c2, hipStream_t s) {
+                   float eps, float wd, float c1, float c2, const int32_t *gate, hipStream_t s) {
     if (n % 4) return hipErrorInvalidValue;
     size_t n4 = n / 4;
     if (n4 == 0) return hipSuccess;
     const size_t g = (n4 + 256 * ADAMW_U - 1) / (256 * ADAMW_U);
     if (g > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)g), dim3(256), 0, s, (floatx4 *)params, (const floatx4 *)grads,
-                       (floatx4 *)m, (floatx4 *)v, n4, lr, b1, b2, eps, wd, 1.0f / c1, 1.0f / c2);
+                       (floatx4 *)m, (floatx4 *)v, n4, lr, b1, b2, eps, wd, 1.0f / c1, 1.0f / c2, gate);
     return hipGetLastError();
 }
