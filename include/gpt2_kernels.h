@@ -99,6 +99,25 @@ gpt2_status gpt2k_encoder_backward(float *dwte, float *dwpe, const float *dout, 
 gpt2_status gpt2k_adamw(float *params, const float *grads, float *m, float *v, size_t n, float lr, float beta1,
                         float beta2, float eps, float weight_decay, int t, void *stream);
 
+/* LayerNorm backward that allocates nothing, for callers that cannot call
+ * hipMalloc or be handed a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, kernels
+ * and results as gpt2k_layernorm_backward with dw and db given, but the
+ * partial column sums of dw and db live in a static device array of
+ * GPT2K_NOALLOC_SCRATCH_FLOATS floats (8 MiB) that each GPU holds from the
+ * first call on it until the process ends.  Limit: ceil(N / 16) * 2 * C must
+ * not exceed that size (e.g. N <= 21840 rows at C = 768, N <= 8192 at
+ * C = 2048); larger shapes get GPT2_EINVAL with a message before anything is
+ * launched, as do a NULL dw or db.  Every call on one GPU uses that GPU's same array and leaves its last
+ * contents there (each partial row is written before it is read, so nothing
+ * needs clearing); calls that overlap on one GPU (different streams, or other
+ * threads) race on it and must be serialised by the caller.  Calls on one
+ * stream are ordered and safe.  No device memory is allocated or freed. */
+#define GPT2K_NOALLOC_SCRATCH_FLOATS ((size_t)1 << 21)
+gpt2_status gpt2k_layernorm_backward_noalloc(float *dinp, float *dw, float *db, const float *dout, const float *inp,
+                                             const float *w, const float *mean, const float *rstd, int N, int C,
+                                             int accumulate, void *stream);
+
 /* Calibration of the measurement (not a step of the training path): the
  * rates this device reaches, reported beside the vendor peaks.
  * gpt2k_probe_mfma launches one workgroup of 16 wavefronts per CU, each

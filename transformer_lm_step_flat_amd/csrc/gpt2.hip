@@ -29,6 +29,7 @@
 #include "gemm.h"
 #include "probe.h"
 #include "kernels.h"
+#include "status.h"
 
 namespace {
 
@@ -396,6 +397,12 @@ gpt2_status fail(gpt2_model *m, gpt2_status st, const std::string &msg) {
     g_last_error = msg;
     return st;
 }
+
+}  // namespace
+
+void set_last_error(const std::string &msg) { g_last_error = msg; }
+
+namespace {
 
 #define HIPCK(model, expr)                                                                             \
     do {                                                                                               \

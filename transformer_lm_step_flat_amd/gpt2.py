@@ -71,6 +71,7 @@ _SIGS = {
     "gpt2k_linear_backward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
     "gpt2k_layernorm_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _P],
     "gpt2k_layernorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
+    "gpt2k_layernorm_backward_noalloc": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "gpt2k_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P],
     "gpt2k_attention_backward": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
     "gpt2k_flash_attention_forward": [_P, _P, _P, _I, _I, _I, _I, _P, _P],
@@ -299,6 +300,16 @@ def layernorm_backward(dinp, dw, db, dout, inp, w, mean, rstd, N, C, accumulate)
     _check(lib().gpt2k_layernorm_backward(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(inp), _ptr(w),
                                           _ptr(mean), _ptr(rstd), N, C, int(accumulate), _ptr(work), _s()))
     return work
+
+
+def layernorm_backward_noalloc(dinp, dw, db, dout, inp, w, mean, rstd, N, C, accumulate):
+    """The same as layernorm_backward, with the library's static scratch (no allocation)."""
+    for name, t, n in (("dinp", dinp, N * C), ("dw", dw, C), ("db", db, C), ("dout", dout, N * C),
+                       ("inp", inp, N * C), ("w", w, C), ("mean", mean, N), ("rstd", rstd, N)):
+        if t.numel() < n:
+            raise ValueError(f"{name} holds {t.numel()} elements, the call touches {n}")
+    _check(lib().gpt2k_layernorm_backward_noalloc(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(inp), _ptr(w),
+                                                  _ptr(mean), _ptr(rstd), N, C, int(accumulate), _s()))
 
 
 def attention_forward(atty, att, qkv, B, T, C, NH):
