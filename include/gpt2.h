@@ -45,7 +45,8 @@ typedef enum {
     GPT2_EINVAL = -1,  /* bad argument, shape or configuration                 */
     GPT2_ERANGE = -2,  /* a token or target outside [0, vocab_size)            */
     GPT2_ESTATE = -3,  /* call out of order (e.g. backward before forward)     */
-    GPT2_EDEVICE = -4  /* a HIP runtime call or kernel launch failed           */
+    GPT2_EDEVICE = -4, /* a HIP runtime call or kernel launch failed           */
+    GPT2_EIO = -5      /* a file could not be read or written, or is damaged   */
 } gpt2_status;
 
 /* Model shape.  padded_vocab_size >= vocab_size is the row count of wte and
@@ -195,6 +196,29 @@ typedef struct {
 } gpt2_profile_entry;
 gpt2_status gpt2_profile_enable(gpt2_model *model, int enable);
 gpt2_status gpt2_profile_read(gpt2_model *model, gpt2_profile_entry *out, int max_entries, int *n_entries);
+
+/* Checkpoints of the training state (the femtoGPT page, "使用方法": training
+ * may stop and resume at any time from its saved state; the GeekNews page,
+ * "Nạp trọng số": a flat fp32 weight file, read in an explicitly stated
+ * tensor order).  The file holds a header (magic, version, the six config
+ * fields, the step count t, the 16-entry parameter table of gpt2_layout with
+ * names, offsets and counts, and a 64-bit checksum of the payload) followed
+ * by params, adam_m and adam_v as raw little-endian fp32, in that order.
+ * Gradients and activations are not saved (gradients are cleared every
+ * step).  Both calls wait for the model's stream and copy through a 16 MiB
+ * host staging buffer; no device memory is allocated.
+ *
+ * gpt2_save_checkpoint writes `path` (through `path`.tmp, renamed when
+ * complete, so a failed save leaves any older file in place).  t >= 0 is the
+ * number of optimizer steps taken (the next gpt2_update passes t + 1).
+ * gpt2_load_checkpoint reads a file written for the same config (any B, T),
+ * verifies its header, size and checksum before copying anything, then
+ * overwrites params, adam_m and adam_v and stores the saved step count in
+ * *t (may be NULL).  A mismatched config or tensor table is GPT2_EINVAL, an
+ * unreadable, truncated or corrupted file GPT2_EIO; in both cases the model
+ * is unchanged.  After a load, gpt2_backward needs a new forward. */
+gpt2_status gpt2_save_checkpoint(gpt2_model *model, const char *path, int t);
+gpt2_status gpt2_load_checkpoint(gpt2_model *model, const char *path, int *t);
 
 /* Release the handle (not the caller's buffers). */
 void gpt2_free(gpt2_model *model);

@@ -16,13 +16,16 @@ LIB = os.path.join(HERE, "libgpt2mi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["gpt2.hip", "gemm.hip", "kernels.hip", "attention.hip", "probe.hip", "noalloc.hip"]
+SOURCES = ["gpt2.hip", "gemm.hip", "kernels.hip", "attention.hip", "probe.hip", "noalloc.hip", "checkpoint.cpp"]
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):  # host-only C++ (no device code)
+        cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; anything else is shown
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
@@ -36,7 +39,7 @@ def _compile(src: str, obj: str) -> None:
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         list(ex.map(lambda a: _compile(*a), zip(SOURCES, objs)))
     tmp = LIB + ".tmp"

@@ -25,6 +25,7 @@
 #include "../../include/gpt2.h"
 #include "../../include/gpt2_kernels.h"
 #include "attention.h"
+#include "checkpoint.h"
 #include "common.h"
 #include "gemm.h"
 #include "probe.h"
@@ -1012,6 +1013,67 @@ gpt2_status gpt2_sync(gpt2_model *m) {
         return fail(m, GPT2_ERANGE, "an id was outside [0, vocab_size)");
     }
     return GPT2_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- checkpoints
+// (file format in checkpoint.h; here the copies between the device and the
+// host staging buffer)
+namespace {
+
+CkModel ck_model(const Layout &l) {
+    CkModel c;
+    const int32_t cfg[6] = {l.maxT, l.V, l.Vp, l.L, l.NH, l.C};
+    memcpy(c.cfg, cfg, sizeof cfg);
+    c.nparams = (int64_t)l.nparams;
+    for (int i = 0; i < 16; i++) {
+        c.names[i] = kParamNames[i];
+        c.offset[i] = (int64_t)l.poff[i];
+        c.count[i] = (int64_t)l.pcnt[i];
+    }
+    return c;
+}
+
+gpt2_status ck_status(gpt2_model *m, int code, const std::string &msg, hipError_t e) {
+    if (code == CK_OK) return GPT2_OK;
+    if (code == CK_ECOPY) return fail(m, GPT2_EDEVICE, msg + ": " + hipGetErrorString(e));
+    return fail(m, code == CK_EINVAL ? GPT2_EINVAL : GPT2_EIO, msg);
+}
+
+}  // namespace
+
+extern "C" {
+
+gpt2_status gpt2_save_checkpoint(gpt2_model *m, const char *path, int t) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    HIPCK(m, hipStreamSynchronize(m->stream));  // the state on the device is complete
+    const float *src[3] = {m->buf.params, m->buf.adam_m, m->buf.adam_v};
+    hipError_t e = hipSuccess;
+    auto fetch = [&](int a, size_t first, size_t count, float *dst) {
+        e = hipMemcpyAsync(dst, src[a] + first, count * sizeof(float), hipMemcpyDeviceToHost, m->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+        return e == hipSuccess ? 0 : 1;
+    };
+    std::string msg;
+    const int code = ck_save(path, ck_model(m->lo), t, fetch, &msg);
+    return ck_status(m, code, msg, e);
+}
+
+gpt2_status gpt2_load_checkpoint(gpt2_model *m, const char *path, int *t) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    HIPCK(m, hipStreamSynchronize(m->stream));
+    float *dst[3] = {m->buf.params, m->buf.adam_m, m->buf.adam_v};
+    hipError_t e = hipSuccess;
+    auto store = [&](int a, size_t first, size_t count, const float *src) {
+        e = hipMemcpyAsync(dst[a] + first, src, count * sizeof(float), hipMemcpyHostToDevice, m->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+        return e == hipSuccess ? 0 : 1;
+    };
+    std::string msg;
+    const int code = ck_load(path, ck_model(m->lo), t, store, &msg);
+    if (code == CK_OK || code == CK_ECOPY) m->have_targets = false;  // activations belong to the old parameters
+    return ck_status(m, code, msg, e);
 }
 
 gpt2_status gpt2_profile_enable(gpt2_model *m, int enable) {

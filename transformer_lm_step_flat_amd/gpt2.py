@@ -16,9 +16,10 @@ import torch  # noqa: F401  (loads the HIP runtime the library then shares)
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
 
-GPT2_OK, GPT2_EINVAL, GPT2_ERANGE, GPT2_ESTATE, GPT2_EDEVICE = 0, -1, -2, -3, -4
+GPT2_OK, GPT2_EINVAL, GPT2_ERANGE, GPT2_ESTATE, GPT2_EDEVICE, GPT2_EIO = 0, -1, -2, -3, -4, -5
 GPT2_PARAMS, GPT2_ACTS = 0, 1
-_STATUS = {0: "GPT2_OK", -1: "GPT2_EINVAL", -2: "GPT2_ERANGE", -3: "GPT2_ESTATE", -4: "GPT2_EDEVICE"}
+_STATUS = {0: "GPT2_OK", -1: "GPT2_EINVAL", -2: "GPT2_ERANGE", -3: "GPT2_ESTATE", -4: "GPT2_EDEVICE",
+           -5: "GPT2_EIO"}
 
 
 class Gpt2Error(RuntimeError):
@@ -65,6 +66,8 @@ _SIGS = {
     "gpt2_backward": [_P],
     "gpt2_update": [_P, _F, _F, _F, _F, _F, _I],
     "gpt2_sync": [_P],
+    "gpt2_save_checkpoint": [_P, ctypes.c_char_p, _I],
+    "gpt2_load_checkpoint": [_P, ctypes.c_char_p, ctypes.POINTER(_I)],
     "gpt2_profile_enable": [_P, _I],
     "gpt2_profile_read": [_P, ctypes.POINTER(ProfileEntry), _I, ctypes.POINTER(_I)],
     "gpt2k_linear_forward": [_P, _P, _P, _P, _I, _I, _I, _P],
@@ -260,6 +263,17 @@ class Model:
     def sync(self):
         _check(lib().gpt2_sync(self._h), self._h)
 
+    # --- checkpoints
+    def save(self, path: str, t: int):
+        """Write params, m, v and the step count t (optimizer steps taken) to path."""
+        _check(lib().gpt2_save_checkpoint(self._h, os.fsencode(path), t), self._h)
+
+    def load(self, path: str) -> int:
+        """Read a checkpoint of the same config into params, m, v; returns its step count."""
+        t = _I()
+        _check(lib().gpt2_load_checkpoint(self._h, os.fsencode(path), ctypes.byref(t)), self._h)
+        return t.value
+
     # --- per-launch timing
     def profile_enable(self, on: bool = True):
         _check(lib().gpt2_profile_enable(self._h, int(on)), self._h)
@@ -274,16 +288,35 @@ class Model:
 
 
 # ---------------------------------------------------------------- kernel-level calls
+#
+# Each wrapper checks, before the call, that every tensor holds at least the
+# elements the kernels will touch for the given sizes (the C ABI takes raw
+# device pointers and cannot), so a size mistake raises here instead of
+# reaching the GPU as an out-of-bounds access.
 
 def _s():
     return _stream()
 
 
+def _need(**tensors):
+    """tensors: name=(tensor or None, element count it must hold)."""
+    for name, (t, n) in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.numel() < n:
+            raise ValueError(f"{name} holds {t.numel()} elements, the call touches {n}")
+
+
 def linear_forward(out, inp, W, bias, N, K, OC):
+    _need(out=(out, N * OC), inp=(inp, N * K), W=(W, OC * K), bias=(bias, OC))
     _check(lib().gpt2k_linear_forward(_ptr(out), _ptr(inp), _ptr(W), _ptr(bias), N, K, OC, _s()))
 
 
 def linear_backward(dinp, dW, dbias, dout, inp, W, N, K, OC):
+    _need(dinp=(dinp, N * K), dW=(dW, OC * K), dbias=(dbias, OC), dout=(dout, N * OC), inp=(inp, N * K),
+          W=(W, OC * K))
     work = torch.empty(max(1, lib().gpt2k_linear_backward_work(N, K, OC)), dtype=torch.float32, device=dout.device)
     _check(lib().gpt2k_linear_backward(_ptr(dinp), _ptr(dW), _ptr(dbias), _ptr(dout), _ptr(inp), _ptr(W), N, K,
                                        OC, _ptr(work), _s()))
@@ -291,11 +324,18 @@ def linear_backward(dinp, dW, dbias, dout, inp, W, N, K, OC):
 
 
 def layernorm_forward(out, mean, rstd, inp, w, b, N, C):
+    _need(out=(out, N * C), mean=(mean, N), rstd=(rstd, N), inp=(inp, N * C), w=(w, C), b=(b, C))
     _check(lib().gpt2k_layernorm_forward(_ptr(out), _ptr(mean), _ptr(rstd), _ptr(inp), _ptr(w), _ptr(b), N, C,
                                          _s()))
 
 
+def _ln_bwd_need(dinp, dw, db, dout, inp, w, mean, rstd, N, C):
+    _need(dinp=(dinp, N * C), dw=(dw, C), db=(db, C), dout=(dout, N * C), inp=(inp, N * C), w=(w, C),
+          mean=(mean, N), rstd=(rstd, N))
+
+
 def layernorm_backward(dinp, dw, db, dout, inp, w, mean, rstd, N, C, accumulate):
+    _ln_bwd_need(dinp, dw, db, dout, inp, w, mean, rstd, N, C)
     work = torch.empty(max(1, lib().gpt2k_layernorm_backward_work(N, C)), dtype=torch.float32, device=dout.device)
     _check(lib().gpt2k_layernorm_backward(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(inp), _ptr(w),
                                           _ptr(mean), _ptr(rstd), N, C, int(accumulate), _ptr(work), _s()))
@@ -304,19 +344,18 @@ def layernorm_backward(dinp, dw, db, dout, inp, w, mean, rstd, N, C, accumulate)
 
 def layernorm_backward_noalloc(dinp, dw, db, dout, inp, w, mean, rstd, N, C, accumulate):
     """The same as layernorm_backward, with the library's static scratch (no allocation)."""
-    for name, t, n in (("dinp", dinp, N * C), ("dw", dw, C), ("db", db, C), ("dout", dout, N * C),
-                       ("inp", inp, N * C), ("w", w, C), ("mean", mean, N), ("rstd", rstd, N)):
-        if t.numel() < n:
-            raise ValueError(f"{name} holds {t.numel()} elements, the call touches {n}")
+    _ln_bwd_need(dinp, dw, db, dout, inp, w, mean, rstd, N, C)
     _check(lib().gpt2k_layernorm_backward_noalloc(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(inp), _ptr(w),
                                                   _ptr(mean), _ptr(rstd), N, C, int(accumulate), _s()))
 
 
 def attention_forward(atty, att, qkv, B, T, C, NH):
+    _need(atty=(atty, B * T * C), att=(att, B * NH * T * T), qkv=(qkv, B * T * 3 * C))
     _check(lib().gpt2k_attention_forward(_ptr(atty), _ptr(att), _ptr(qkv), B, T, C, NH, _s()))
 
 
 def attention_backward(dqkv, datty, qkv, att, B, T, C, NH):
+    _need(dqkv=(dqkv, B * T * 3 * C), datty=(datty, B * T * C), qkv=(qkv, B * T * 3 * C), att=(att, B * NH * T * T))
     work = torch.empty(max(1, lib().gpt2k_attention_backward_work(B, T, C, NH)), dtype=torch.float32,
                        device=qkv.device)
     _check(lib().gpt2k_attention_backward(_ptr(dqkv), _ptr(datty), _ptr(qkv), _ptr(att), B, T, C, NH, _ptr(work),
@@ -329,12 +368,15 @@ def _flash_work(B, T, C, NH, device):
 
 
 def flash_attention_forward(atty, lse, qkv, B, T, C, NH):
+    _need(atty=(atty, B * T * C), lse=(lse, B * NH * T), qkv=(qkv, B * T * 3 * C))
     work = _flash_work(B, T, C, NH, qkv.device)
     _check(lib().gpt2k_flash_attention_forward(_ptr(atty), _ptr(lse), _ptr(qkv), B, T, C, NH, _ptr(work), _s()))
     return work
 
 
 def flash_attention_backward(dqkv, datty, qkv, atty, lse, B, T, C, NH):
+    _need(dqkv=(dqkv, B * T * 3 * C), datty=(datty, B * T * C), qkv=(qkv, B * T * 3 * C), atty=(atty, B * T * C),
+          lse=(lse, B * NH * T))
     work = _flash_work(B, T, C, NH, qkv.device)
     _check(lib().gpt2k_flash_attention_backward(_ptr(dqkv), _ptr(datty), _ptr(qkv), _ptr(atty), _ptr(lse), B, T, C,
                                                 NH, _ptr(work), _s()))
@@ -342,26 +384,32 @@ def flash_attention_backward(dqkv, datty, qkv, atty, lse, B, T, C, NH):
 
 
 def gelu_forward(out, inp):
+    _need(out=(out, inp.numel()))
     _check(lib().gpt2k_gelu_forward(_ptr(out), _ptr(inp), inp.numel(), _s()))
 
 
 def gelu_backward(dinp, inp, dout):
+    _need(dinp=(dinp, inp.numel()), dout=(dout, inp.numel()))
     _check(lib().gpt2k_gelu_backward(_ptr(dinp), _ptr(inp), _ptr(dout), inp.numel(), _s()))
 
 
 def crossentropy(logits, losses, loss, targets, BT, V, Vp):
+    _need(logits=(logits, BT * Vp), losses=(losses, BT), loss=(loss, 1), targets=(targets, BT))
     _check(lib().gpt2k_crossentropy(_ptr(logits), _ptr(losses), _ptr(loss), _ptr(targets), BT, V, Vp, _s()))
 
 
 def encoder_forward(out, ids, wte, wpe, B, T, C, V):
+    _need(out=(out, B * T * C), ids=(ids, B * T), wte=(wte, V * C), wpe=(wpe, T * C))
     _check(lib().gpt2k_encoder_forward(_ptr(out), _ptr(ids), _ptr(wte), _ptr(wpe), B, T, C, V, _s()))
 
 
 def token_order(order, err, ids, targets, BT, V):
+    _need(order=(order, BT), err=(err, 1), ids=(ids, BT), targets=(targets, BT))
     _check(lib().gpt2k_token_order(_ptr(order), _ptr(err), _ptr(ids), _ptr(targets), BT, V, _s()))
 
 
 def encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V):
+    _need(dwte=(dwte, V * C), dwpe=(dwpe, T * C), dout=(dout, B * T * C), ids=(ids, B * T), order=(order, B * T))
     work = torch.empty(max(1, lib().gpt2k_encoder_backward_work(B, T, C)), dtype=torch.float32, device=dout.device)
     _check(lib().gpt2k_encoder_backward(_ptr(dwte), _ptr(dwpe), _ptr(dout), _ptr(ids), _ptr(order), B, T, C, V,
                                         _ptr(work), _s()))
@@ -369,16 +417,19 @@ def encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V):
 
 
 def adamw(params, grads, m, v, lr, b1, b2, eps, wd, t):
-    _check(lib().gpt2k_adamw(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), params.numel(), lr, b1, b2, eps, wd, t,
-                             _s()))
+    n = params.numel()
+    _need(grads=(grads, n), m=(m, n), v=(v, n))
+    _check(lib().gpt2k_adamw(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, lr, b1, b2, eps, wd, t, _s()))
 
 
 def probe_mfma(out, iters):
     """Launch the matrix-core calibration kernel; returns the FLOPs it does."""
+    _need(out=(out, 1))
     flops = ctypes.c_double(0.0)
     _check(lib().gpt2k_probe_mfma(_ptr(out), iters, ctypes.byref(flops), _s()))
     return flops.value
 
 
 def probe_copy(dst, src):
+    _need(dst=(dst, src.numel()))
     _check(lib().gpt2k_probe_copy(_ptr(dst), _ptr(src), src.numel(), _s()))
