@@ -24,7 +24,7 @@ def g():
 
 def header_functions():
     names = set()
-    for h in ("gpt2.h", "gpt2_kernels.h"):
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
         txt = open(os.path.join(ROOT, "include", h)).read()
         txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
         for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(gpt2k?_[a-z0-9_]+)\s*\(", txt, re.M):

@@ -28,6 +28,7 @@
 //
 // Every output element is written by exactly one lane, with sums in a fixed
 // order: results are bitwise reproducible.
+#include "audit.h"
 #include "attention.h"
 #include "common.h"
 
@@ -724,6 +725,24 @@ hipError_t launch_fwd(float *out, float *lse, float *ws, const float *qkv, int B
                       hipStream_t s) {
     const int items = total_items(T);
     float *wlse = ws + (size_t)B * NH * items * QBLK * HD;
+    if (AuditSink *au = audit_sink()) {
+        // item < B NH items: rows item * QBLK .. + QBLK of HD in ws, one lse each in wlse
+        const long long BTC = (long long)B * T * C, BHT = (long long)B * NH * T;
+        const long long nws = (long long)B * NH * items * QBLK;
+        const char *k = HD == 16 ? "flash_fwd_kernel<16>" : HD == 32 ? "flash_fwd_kernel<32>" : "flash_fwd_kernel<64>";
+        audit(au, k, "qkv", qkv, 3 * BTC, false);
+        audit(au, k, "out", out, BTC, true);
+        audit(au, k, "lse", lse, BHT, true);
+        audit(au, k, "ws", ws, nws * HD, true);
+        audit(au, k, "wlse", wlse, nws, true);
+        if (items != (T + QBLK - 1) / QBLK) {
+            audit(au, "flash_fwd_merge_kernel", "ws", ws, nws * HD, false);
+            audit(au, "flash_fwd_merge_kernel", "wlse", wlse, nws, false);
+            audit(au, "flash_fwd_merge_kernel", "out", out, BTC, true);
+            audit(au, "flash_fwd_merge_kernel", "lse", lse, BHT, true);
+        }
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(flash_fwd_kernel<HD>, dim3(items * B * NH), dim3(256), 0, s, out, lse, ws, wlse, qkv, T, C,
                        NH, items, 1.0f / sqrtf((float)HD));
     hipError_t e = hipGetLastError();
@@ -746,6 +765,26 @@ template <int HD>
 hipError_t launch_bwd_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dout, const float *qkv,
                            const float *out, const float *lse, int B, int T, int C, int NH, hipStream_t s) {
     const long long rows = (long long)B * T;
+    if (AuditSink *au = audit_sink()) {
+        // G workgroups, two partial slots of 2 QBLK HD floats each; ds of every (b, h) T x T
+        const long long BTC = (long long)B * T * C, BHT = (long long)B * NH * T;
+        const long long G = dkdv_groups(B, T, NH, HD);
+        const char *k = HD == 16 ? "flash_bwd_dkdv_kernel<16>" : HD == 32 ? "flash_bwd_dkdv_kernel<32>"
+                                                                          : "flash_bwd_dkdv_kernel<64>";
+        audit(au, "flash_bwd_D_kernel", "Dbuf", Dbuf, BHT, true);
+        audit(au, "flash_bwd_D_kernel", "dout", dout, BTC, false);
+        audit(au, "flash_bwd_D_kernel", "out", out, BTC, false);
+        audit(au, k, "dqkv", dqkv, 3 * BTC, true);
+        audit(au, k, "kvws", ws + ds_floats(B, T, NH), 2 * G * 2 * QBLK * HD, true);
+        audit(au, k, "ds", ws, BHT * T, true);
+        audit(au, k, "dout", dout, BTC, false);
+        audit(au, k, "qkv", qkv, 3 * BTC, false);
+        audit(au, k, "lse", lse, BHT, false);
+        audit(au, k, "Dbuf", Dbuf, BHT, false);
+        audit(au, "flash_bwd_sum_kernel", "kvws", ws + ds_floats(B, T, NH), 2 * G * 2 * QBLK * HD, false);
+        audit(au, "flash_bwd_sum_kernel", "dqkv", dqkv, 3 * BTC, true);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(flash_bwd_D_kernel<HD>, dim3((unsigned)((rows * NH + 255) / 256)), dim3(256), 0, s, Dbuf, dout,
                        out, T, C, NH, rows);
     hipError_t e = hipGetLastError();

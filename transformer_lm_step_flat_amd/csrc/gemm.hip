@@ -18,6 +18,7 @@
 // an MN-contiguous operand is kept [k][mn] and read one float per lane along
 // mn (32 consecutive words per half-wave).
 #include "common.h"
+#include "audit.h"
 #include "gemm.h"
 
 namespace {
@@ -678,10 +679,40 @@ int resolve_tile(const GemmDesc &d) {
 
 }  // namespace
 
+// The elements a launch for descriptor d may touch, from the operand
+// layouts: A(m, k) and B(k, n) over m < M, k < K, n < N in every batch
+// (zo < nbo, zi < nbi at strides s?o, s?i), C(m, n) in every batch and split
+// (s < ksplit at stride sCs), and the epilogue operands.
+static void audit_gemm(AuditSink *au, const char *kernel, const GemmDesc &d) {
+    const long long bo = d.nbo - 1, bi = d.nbi - 1, M = d.M, N = d.N, K = d.K;
+    if (K > 0) {
+        const long long a = (d.a_kcontig ? (M - 1) * d.lda + K : (K - 1) * d.lda + M) + bo * d.sAo + bi * d.sAi;
+        const long long b = (d.b_kcontig ? (N - 1) * d.ldb + K : (K - 1) * d.ldb + N) + bo * d.sBo + bi * d.sBi;
+        audit(au, kernel, "A", d.A, a, false);
+        audit(au, kernel, "B", d.B, b, false);
+    }
+    const long long c = (M - 1) * d.ldc + N + bo * d.sCo + bi * d.sCi + (long long)(d.ksplit - 1) * d.sCs;
+    audit(au, kernel, "C", d.C, c, true);
+    if (d.epi == EPI_GELU) audit(au, kernel, "C2", d.C2, c, true);
+    if (d.epi == EPI_RESID || d.epi == EPI_GELU_BWD) audit(au, kernel, "aux", d.aux, (M - 1) * d.ldaux + N, false);
+    audit(au, kernel, "bias", d.bias, N, false);
+    audit(au, kernel, "colsum", d.colsum, (long long)d.ksplit * M, true);
+    if (d.part && d.causal == CAUSAL_KEND) {
+        // partial sums of the upper row tiles, [nbo * nbi][M][N], added into C by a second kernel
+        audit(au, kernel, "part", d.part, (long long)d.nbo * d.nbi * M * N, true);
+        audit(au, "fold_split_sum_kernel", "part", d.part, (long long)d.nbo * d.nbi * M * N, false);
+        audit(au, "fold_split_sum_kernel", "C", d.C, c, true);
+    }
+}
+
 hipError_t gemm_launch(const GemmDesc &d, hipStream_t stream) {
     GemmArgs a;
     hipError_t e = make_args(d, a);
     if (e != hipSuccess) return e;
+    if (AuditSink *au = audit_sink()) {
+        audit_gemm(au, gemm_kernel_name(d), d);
+        return hipSuccess;
+    }
     switch (resolve_tile(d)) {
         case 1: return launch_tile<128, 128, 32, 3>(d, a, stream);
         case 2: return launch_tile<128, 64, 32, 3>(d, a, stream);
@@ -697,6 +728,12 @@ hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t 
     if (e == hipSuccess) e = make_args(d2, a2);
     if (e != hipSuccess) return e;
     if (d1.tile != d2.tile || d1.causal || d2.causal) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        const char *k = gemm_pair_kernel_name(d1.tile, gemm_pair_full(d1, d2, d1.tile));
+        audit_gemm(au, k, d1);
+        audit_gemm(au, k, d2);
+        return hipSuccess;
+    }
     switch (d1.tile) {
         case 1: return launch_pair<128, 128, 32, 3>(d1, a1, d2, a2, stream);
         case 2: return launch_pair<128, 64, 32, 3>(d1, a1, d2, a2, stream);

@@ -24,7 +24,9 @@
 
 #include "../../include/gpt2.h"
 #include "../../include/gpt2_kernels.h"
+#include "../../include/gpt2_audit.h"
 #include "attention.h"
+#include "audit.h"
 #include "checkpoint.h"
 #include "common.h"
 #include "gemm.h"
@@ -269,6 +271,15 @@ struct Layout {
     size_t w_site_dw[NSITES], w_site_db[NSITES];
     // int buffer
     size_t i_tok, i_order, i_err, niwork;
+    // the work regions with their exact float counts (offsets are padded to
+    // 64 floats), each cut into `parts` equal slices (per layer or per slot)
+    struct WRegion {
+        const char *name;
+        size_t off, cnt;
+        int parts;
+    };
+    WRegion wreg[24];
+    int nwreg;
 };
 
 bool config_ok(const gpt2_config *c, int B, int T, std::string *why) {
@@ -325,15 +336,22 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.nacts = off;
 
     off = 0;
-    l.w_dres = off; off = align_up(off + BT * C);
-    l.w_dln = off; off = align_up(off + BT * C);
-    l.w_datty = off; off = align_up(off + BT * C);
-    l.w_dqkv = off; off = align_up(off + BT * 3 * C);
-    l.w_dfch = off; off = align_up(off + BT * 4 * C);
-    l.w_datt = off; off = align_up(off + (l.flash ? (size_t)B * NH * T : (size_t)B * NH * TT));
-    l.w_flash = off; off = align_up(off + (l.flash ? flash_attention_work(B, T, (int)C, (int)NH) : 0));
+    l.nwreg = 0;
+    auto add_w = [&](const char *name, size_t cnt, int parts) {
+        l.wreg[l.nwreg++] = Layout::WRegion{name, off, cnt, parts};
+        const size_t at = off;
+        off = align_up(off + cnt);
+        return at;
+    };
+    l.w_dres = add_w("dres", BT * C, 1);
+    l.w_dln = add_w("dln", BT * C, 1);
+    l.w_datty = add_w("datty", BT * C, 1);
+    l.w_dqkv = add_w("dqkv", BT * 3 * C, 1);
+    l.w_dfch = add_w("dfch", BT * 4 * C, 1);
+    l.w_datt = add_w("datt", l.flash ? (size_t)B * NH * T : (size_t)B * NH * TT, 1);
+    l.w_flash = add_w("flash_ws", l.flash ? flash_attention_work(B, T, (int)C, (int)NH) : 0, 1);
     // LayerNorm parameter partials of all 2L + 1 LayerNorms (summed once at the end)
-    l.w_part = off; off = align_up(off + (2 * L + 1) * (size_t)ln_partials((int)BT) * 2 * C);
+    l.w_part = add_w("ln_partials", (2 * L + 1) * (size_t)ln_partials((int)BT) * 2 * C, (int)(2 * L + 1));
     // split-K partial products: of the input gradient dlnf (the only one
     // allowed to split) and of the weight gradients, in separate regions
     // because a pair of them runs as one grid
@@ -343,20 +361,22 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     bwd_split_need((int)BT, (int)C, (int)(4 * C), false, sk, sk_dw);
     bwd_split_need((int)BT, (int)(4 * C), (int)C, false, sk, sk_dw);
     bwd_split_need((int)BT, (int)C, l.Vp, true, sk, sk_dw);
-    l.w_splitk = off; off = align_up(off + sk);
-    l.w_splitk_dw = off; off = align_up(off + sk_dw);
+    l.w_splitk = add_w("splitk", sk, 1);
+    l.w_splitk_dw = add_w("splitk_dw", sk_dw, 1);
     {
+        static const char *dw_names[NSITES] = {"site_dw_qkv", "site_dw_attproj", "site_dw_fc", "site_dw_fcproj"};
+        static const char *db_names[NSITES] = {"site_db_qkv", "site_db_attproj", "site_db_fc", "site_db_fcproj"};
         const int sin[NSITES] = {(int)C, (int)C, (int)C, (int)(4 * C)};
         const int sout[NSITES] = {(int)(3 * C), (int)C, (int)(4 * C), (int)C};
         for (int j = 0; j < NSITES; j++) {
             const int ks = dw_ksplit((int)BT, sin[j], sout[j], false);
             l.site_ks[j] = ks;
             const size_t kk = ks > 1 ? (size_t)ks : 0;
-            l.w_site_dw[j] = off; off = align_up(off + L * kk * sout[j] * sin[j]);
-            l.w_site_db[j] = off; off = align_up(off + L * kk * sout[j]);
+            l.w_site_dw[j] = add_w(dw_names[j], L * kk * sout[j] * sin[j], (int)L);
+            l.w_site_db[j] = add_w(db_names[j], L * kk * sout[j], (int)L);
         }
     }
-    l.w_dbias = off; off = align_up(off + 16 * 4 * C);
+    l.w_dbias = add_w("dbias_ws", 16 * 4 * C, 1);
     l.nwork = off;
     l.i_tok = 0;
     l.i_order = align_up(BT);
@@ -488,6 +508,16 @@ hipError_t gemm_run(const GemmDesc &d, hipStream_t s, const char *site = nullptr
 }
 
 // ---------------------------------------------------------------- building blocks
+
+// Device-to-device copy of n ids (declared, not made, during a launch audit).
+hipError_t copy_ids(int32_t *dst, const int32_t *src, int n, hipStream_t s) {
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "copy_ids", "src", src, n, false);
+        audit(au, "copy_ids", "dst", dst, n, true);
+        return hipSuccess;
+    }
+    return hipMemcpyAsync(dst, src, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, s);
+}
 
 // out[N][OC] = inp[N][K] W^T (+ bias) with an epilogue.
 hipError_t linear_fwd(float *out, const float *inp, const float *W, const float *bias, int N, int K, int OC,
@@ -797,7 +827,7 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
     m->have_targets = false;
 
     // keep this batch's ids for the embedding backward
-    HIPCK(m, hipMemcpyAsync(tok, inputs, sizeof(int32_t) * BT, hipMemcpyDeviceToDevice, s));
+    HIPCK(m, copy_ids(tok, inputs, BT, s));
     inputs = tok;
     KRUN(m, "token_prep_kernel", 12.0 * BT, k_token_prep(inputs, targets, order, err, BT, l.V, s));
     KRUN(m, "encoder_forward_kernel", 12.0 * BTC, k_encoder_forward(A + l.aoff[A_ENCODED], inputs, P + l.poff[0], P + l.poff[1], B, T, C, l.V, s));
@@ -1277,6 +1307,130 @@ gpt2_status gpt2k_probe_mfma(float *out, int iters, double *flops, void *stream)
 
 gpt2_status gpt2k_probe_copy(float *dst, const float *src, size_t n, void *stream) {
     KCK(probe_copy(dst, src, n, (hipStream_t)stream));
+    return GPT2_OK;
+}
+
+}  // extern "C"
+
+// ====================================================================== launch audit replay
+
+namespace {
+
+// Named element ranges of the caller's buffers (disjoint), and the check of
+// every declared access against them: an access must stay inside the range
+// it starts in, cover a run of adjacent ranges exactly (a launch over a whole
+// stacked tensor or a whole parameter buffer), or cover one whole caller
+// buffer exactly (a clear of it at build time).
+class LayoutChecker : public AuditSink {
+   public:
+    struct Region {
+        uintptr_t lo, hi;
+        std::string name;
+    };
+    std::vector<Region> regs;
+    std::vector<std::pair<uintptr_t, uintptr_t>> buffers;  // whole caller buffers
+    long long nranges = 0;
+    std::vector<std::string> violations;
+
+    void add(uintptr_t base, size_t first, size_t count, int parts, const std::string &name) {
+        if (!count) return;
+        const size_t each = count / (size_t)parts;
+        for (int p = 0; p < parts; p++) {
+            const size_t c = p + 1 < parts ? each : count - each * (parts - 1);
+            const uintptr_t lo = base + (first + (size_t)p * each) * 4;
+            regs.push_back(Region{lo, lo + c * 4, parts > 1 ? name + "[" + std::to_string(p) + "]" : name});
+        }
+    }
+    void seal() {
+        std::sort(regs.begin(), regs.end(), [](const Region &a, const Region &b) { return a.lo < b.lo; });
+    }
+    void shrink(const std::string &name, size_t floats) {
+        for (Region &r : regs)
+            if (r.name == name) r.hi -= std::min<uintptr_t>(r.hi - r.lo, floats * 4);
+    }
+    void range(const char *kernel, const char *operand, const void *p, size_t bytes, bool write) override {
+        nranges++;
+        const uintptr_t lo = (uintptr_t)p, hi = lo + bytes;
+        for (const auto &b : buffers)
+            if (lo == b.first && hi == b.second) return;
+        auto it = std::upper_bound(regs.begin(), regs.end(), lo,
+                                   [](uintptr_t x, const Region &r) { return x < r.lo; });
+        std::string what;
+        if (it == regs.begin() || lo >= (it - 1)->hi) {
+            what = "starts outside every tensor";
+        } else {
+            auto r = it - 1;
+            if (hi <= r->hi) return;
+            if (lo == r->lo) {  // a run of whole adjacent ranges?
+                auto q = r;
+                while (q->hi < hi && q + 1 != regs.end() && (q + 1)->lo == q->hi) ++q;
+                if (q->hi == hi) return;
+            }
+            what = "runs past the end of " + r->name + " by " + std::to_string((long long)(hi - r->hi)) + " bytes";
+        }
+        if (violations.size() < 64)
+            violations.push_back(std::string(kernel) + " " + operand + (write ? " (write)" : " (read)") + ": " + what);
+        else if (violations.size() == 64)
+            violations.push_back("...");
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+gpt2_status gpt2_audit_step(const gpt2_config *cfg, int B, int T, const char *shrink_region, size_t shrink_floats,
+                            char *report, size_t report_len, long long *n_ranges, long long *n_violations) {
+    std::string why;
+    if (!config_ok(cfg, B, T, &why)) return fail(nullptr, GPT2_EINVAL, why);
+    if (audit_sink()) return fail(nullptr, GPT2_ESTATE, "a launch audit is already running on this thread");
+    Layout l;
+    make_layout(cfg, B, T, &l);
+    // stand-in base addresses, far apart; never dereferenced
+    auto base = [](int b) { return (uintptr_t)(b + 1) << 40; };
+    LayoutChecker ck;
+    static const char *bufnames[4] = {"params:", "grads:", "adam_m:", "adam_v:"};
+    for (int b = 0; b < 4; b++)
+        for (int i = 0; i < 16; i++)
+            ck.add(base(b), l.poff[i], l.pcnt[i], (i >= 2 && i <= 13) ? l.L : 1, std::string(bufnames[b]) + kParamNames[i]);
+    static const bool per_layer[NUM_ACTS] = {false, true, true, true, true, true, true, true, true, true, true,
+                                             true,  true, true, false, false, false, false, false, false, true};
+    for (int i = 0; i < NUM_ACTS; i++)
+        ck.add(base(4), l.aoff[i], l.acnt[i], per_layer[i] ? l.L : 1, std::string("acts:") + kActNames[i]);
+    for (int i = 0; i < l.nwreg; i++)
+        ck.add(base(5), l.wreg[i].off, l.wreg[i].cnt, l.wreg[i].parts, std::string("work:") + l.wreg[i].name);
+    ck.add(base(6), l.i_tok, (size_t)l.BT, 1, "iwork:ids");
+    ck.add(base(6), l.i_order, (size_t)l.BT, 1, "iwork:order");
+    ck.add(base(6), l.i_err, 1, 1, "iwork:err");
+    ck.add(base(7), 0, (size_t)l.BT, 1, "caller:inputs");
+    ck.add(base(8), 0, (size_t)l.BT, 1, "caller:targets");
+    const size_t buf_floats[7] = {l.nparams, l.nparams, l.nparams, l.nparams, l.nacts, l.nwork, l.niwork};
+    for (int b = 0; b < 7; b++) ck.buffers.push_back({base(b), base(b) + buf_floats[b] * 4});
+    ck.seal();
+    if (shrink_region && *shrink_region) ck.shrink(shrink_region, shrink_floats);
+
+    gpt2_buffers dev{(float *)base(0), (float *)base(1), (float *)base(2), (float *)base(3),
+                     (float *)base(4), (float *)base(5), (int32_t *)base(6)};
+    set_audit_sink(&ck);
+    gpt2_model *m = nullptr;
+    gpt2_status st = gpt2_build(cfg, B, T, &dev, nullptr, nullptr, &m);
+    const int32_t *inp = (const int32_t *)base(7), *tgt = (const int32_t *)base(8);
+    if (st == GPT2_OK) st = gpt2_forward(m, inp, nullptr, nullptr);
+    if (st == GPT2_OK) st = gpt2_forward(m, inp, tgt, nullptr);
+    if (st == GPT2_OK) st = gpt2_zero_grad(m);
+    if (st == GPT2_OK) st = gpt2_backward(m);
+    if (st == GPT2_OK) st = gpt2_update(m, 1e-4f, 0.9f, 0.999f, 1e-8f, 0.0f, 1);
+    set_audit_sink(nullptr);
+    const std::string err = m ? m->err : g_last_error;
+    gpt2_free(m);
+    if (st != GPT2_OK) return fail(nullptr, st, "replay stopped: " + err);
+    if (n_ranges) *n_ranges = ck.nranges;
+    if (n_violations) *n_violations = (long long)ck.violations.size();
+    if (report && report_len) {
+        std::string txt;
+        for (const std::string &v : ck.violations) txt += v + "\n";
+        snprintf(report, report_len, "%s", txt.c_str());
+    }
     return GPT2_OK;
 }
 

@@ -3,6 +3,7 @@
 // each row to one 64-lane wavefront and reduce across lanes with shuffles;
 // streaming kernels move 16 bytes per lane per access.  Every reduction runs
 // in a fixed order, so results are bitwise reproducible run to run.
+#include "audit.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -746,6 +747,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(floatx4 *params, const float
 
 hipError_t k_fill(float *p, size_t n, float v, hipStream_t s) {
     if (n == 0) return hipSuccess;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "fill_kernel", "p", p, (long long)n, true);
+        return hipSuccess;
+    }
     if (n % 4 == 0 && ((uintptr_t)p & 15) == 0 && n / 4 / 1024 < 0x7fffffff) {
         hipLaunchKernelGGL(fill4_kernel, dim3((unsigned)((n / 4 + 1023) / 1024)), dim3(256), 0, s, (floatx4 *)p, n / 4,
                            v);
@@ -759,6 +764,10 @@ hipError_t k_fill(float *p, size_t n, float v, hipStream_t s) {
 
 hipError_t k_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s) {
     if (n == 0) return hipSuccess;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "fill_i32_kernel", "p", p, (long long)n, true);
+        return hipSuccess;
+    }
     unsigned g = grid_for(n, 256);
     if (g > 16384) g = 16384;
     hipLaunchKernelGGL(fill_i32_kernel, dim3(g), dim3(256), 0, s, p, n, v);
@@ -767,6 +776,14 @@ hipError_t k_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s) {
 
 hipError_t k_token_prep(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int BT, int V,
                         hipStream_t s) {
+    if (AuditSink *au = audit_sink()) {
+        // every position reads all ids; its rank (an index < BT) receives it
+        audit(au, "token_prep_kernel", "inp", inp, BT, false);
+        audit(au, "token_prep_kernel", "tgt", tgt, BT, false);
+        audit(au, "token_prep_kernel", "order", order, BT, true);
+        audit(au, "token_prep_kernel", "err", err, 1, true);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(token_prep_kernel, dim3(grid_for(BT, 4)), dim3(256), 0, s, inp, tgt, order, err, BT, V);
     return hipGetLastError();
 }
@@ -774,6 +791,14 @@ hipError_t k_token_prep(const int32_t *inp, const int32_t *tgt, int32_t *order, 
 hipError_t k_encoder_forward(float *out, const int32_t *inp, const float *wte, const float *wpe, int B, int T,
                              int C, int V, hipStream_t s) {
     long long total4 = (long long)B * T * (C / 4);
+    if (AuditSink *au = audit_sink()) {
+        // ids are clamped to [0, V): wte rows < V; positions t < T
+        audit(au, "encoder_forward_kernel", "out", out, (long long)B * T * C, true);
+        audit(au, "encoder_forward_kernel", "inp", inp, (long long)B * T, false);
+        audit(au, "encoder_forward_kernel", "wte", wte, (long long)V * C, false);
+        audit(au, "encoder_forward_kernel", "wpe", wpe, (long long)T * C, false);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(encoder_forward_kernel, dim3(grid_for(total4, 256)), dim3(256), 0, s, out, inp, wte, wpe,
                        T, C, V, total4);
     return hipGetLastError();
@@ -783,6 +808,22 @@ hipError_t k_encoder_backward(float *dwte, float *dwpe, float *part, const float
                               const int32_t *order, int B, int T, int C, int V, hipStream_t s) {
     const int BT = B * T;
     if (C % 4 || ((uintptr_t)part & 15)) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        // segment sums at sorted index < BT; positions and ids < BT; rows of
+        // dwte at clamped ids < V; rows of dwpe at t < T
+        const long long BTC = (long long)BT * C;
+        audit(au, "encoder_backward_segments_kernel", "part", part, BTC, true);
+        audit(au, "encoder_backward_segments_kernel", "dout", dout, BTC, false);
+        audit(au, "encoder_backward_segments_kernel", "inp", inp, BT, false);
+        audit(au, "encoder_backward_segments_kernel", "order", order, BT, false);
+        audit(au, "encoder_backward_runs_kernel", "dwte", dwte, (long long)V * C, true);
+        audit(au, "encoder_backward_runs_kernel", "part", part, BTC, false);
+        audit(au, "encoder_backward_runs_kernel", "inp", inp, BT, false);
+        audit(au, "encoder_backward_runs_kernel", "order", order, BT, false);
+        audit(au, "encoder_backward_wpe_kernel", "dwpe", dwpe, (long long)T * C, true);
+        audit(au, "encoder_backward_wpe_kernel", "dout", dout, BTC, false);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(encoder_backward_segments_kernel, dim3(grid_for(BT, ENC_CHUNK), grid_for(C / 4, 64)), dim3(64), 0,
                        s, (floatx4 *)part, dout, inp, order, BT, C, V);
     hipError_t e = hipGetLastError();
@@ -813,6 +854,17 @@ hipError_t k_layernorm_forward(float *out, float *mean, float *rstd, const float
                                const float *b, int N, int C, hipStream_t s) {
     if (C % 4 || C > 2048) return hipErrorInvalidValue;
     int nv = (C / 4 + 63) / 64;
+    if (nv < 1 || nv > 8) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        const long long NC = (long long)N * C;
+        audit(au, "layernorm_forward_kernel", "out", out, NC, true);
+        audit(au, "layernorm_forward_kernel", "mean", mean, N, true);
+        audit(au, "layernorm_forward_kernel", "rstd", rstd, N, true);
+        audit(au, "layernorm_forward_kernel", "inp", inp, NC, false);
+        audit(au, "layernorm_forward_kernel", "w", w, C, false);
+        audit(au, "layernorm_forward_kernel", "b", b, C, false);
+        return hipSuccess;
+    }
     LN_DISPATCH(nv, layernorm_forward_kernel, dim3(grid_for(N, 4)), dim3(256), 0, s, out, mean, rstd, inp, w, b, N,
                 C);
     return hipGetLastError();
@@ -823,6 +875,18 @@ int ln_partials(int N) { return (N + COL_CHUNK - 1) / COL_CHUNK; }
 hipError_t k_ln_param_sums(float *w1, float *b1, float *w2, float *b2, float *w3, float *b3, int L,
                            const float *partial, int N, int C, hipStream_t s) {
     if (C % 4) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        // 2L + 1 slots of P partial rows of 2C; per layer groups of C
+        const long long P = ln_partials(N);
+        audit(au, "ln_param_sums_kernel", "partial", partial, (2LL * L + 1) * P * 2 * C, false);
+        audit(au, "ln_param_sums_kernel", "w1", w1, (long long)L * C, true);
+        audit(au, "ln_param_sums_kernel", "b1", b1, (long long)L * C, true);
+        audit(au, "ln_param_sums_kernel", "w2", w2, (long long)L * C, true);
+        audit(au, "ln_param_sums_kernel", "b2", b2, (long long)L * C, true);
+        audit(au, "ln_param_sums_kernel", "w3", w3, C, true);
+        audit(au, "ln_param_sums_kernel", "b3", b3, C, true);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(ln_param_sums_kernel, dim3(grid_for(2 * C / 4, 16), 2 * L + 1), dim3(256), 0, s, w1, b1, w2, b2,
                        w3, b3, L, partial, ln_partials(N), C);
     return hipGetLastError();
@@ -838,6 +902,24 @@ hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partia
     // (twice the rows in flight per CU), else four
     const int nw = (size_t)8 * 2 * C * sizeof(float) <= 65536 ? 8 : 4;
     const size_t lds = (size_t)nw * 2 * C * sizeof(float);
+    if (nv < 1 || nv > 8) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        // rows are clamped to N - 1; block x writes partial row x (P rows of 2C)
+        const long long NC = (long long)N * C;
+        audit(au, "layernorm_backward_kernel", "dinp", dinp, NC, true);
+        audit(au, "layernorm_backward_kernel", "partial", partial, (long long)P * 2 * C, true);
+        audit(au, "layernorm_backward_kernel", "dout", dout, NC, false);
+        audit(au, "layernorm_backward_kernel", "inp", inp, NC, false);
+        audit(au, "layernorm_backward_kernel", "w", w, C, false);
+        audit(au, "layernorm_backward_kernel", "mean", mean, N, false);
+        audit(au, "layernorm_backward_kernel", "rstd", rstd, N, false);
+        if (dw) {
+            audit(au, "sum_partials_split_kernel", "partial", partial, (long long)P * 2 * C, false);
+            audit(au, "sum_partials_split_kernel", "dw", dw, C, true);
+            audit(au, "sum_partials_split_kernel", "db", db, C, true);
+        }
+        return hipSuccess;
+    }
     LN_DISPATCH(nv, layernorm_backward_kernel, dim3(P), dim3(64 * nw), lds, s, dinp, partial, dout, inp, w, mean,
                 rstd, N, C, accumulate ? 1 : 0);
     hipError_t e = hipGetLastError();
@@ -850,6 +932,12 @@ hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partia
 hipError_t k_sum_partials_ld(float *dst, const float *src, int P, size_t n, size_t ld, bool accumulate,
                              hipStream_t s) {
     if (n % 4 || ld % 4 || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15) || P < 1) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        // src[p * ld + i], p < P, i < n
+        audit(au, "sum_partials_kernel", "src", src, (long long)(P - 1) * (long long)ld + (long long)n, false);
+        audit(au, "sum_partials_kernel", "dst", dst, (long long)n, true);
+        return hipSuccess;
+    }
     if (P >= 32)
         hipLaunchKernelGGL(sum_partials_wide_kernel, dim3(grid_for(n / 4, 16)), dim3(256), 0, s, dst, src, P, n / 4,
                            ld / 4, accumulate ? 1 : 0);
@@ -866,6 +954,13 @@ hipError_t k_sum_partials2(float *dst1, const float *src1, size_t n1, float *dst
     if (al & 15) return hipErrorInvalidValue;
     const size_t n = (n1 + n2) / 4;
     if (n == 0) return hipSuccess;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "sum_partials2_kernel", "src1", src1, (long long)P * (long long)n1, false);
+        audit(au, "sum_partials2_kernel", "dst1", dst1, (long long)n1, true);
+        audit(au, "sum_partials2_kernel", "src2", src2, (long long)P * (long long)n2, false);
+        audit(au, "sum_partials2_kernel", "dst2", dst2, (long long)n2, true);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(sum_partials2_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (floatx4 *)dst1,
                        (const floatx4 *)src1, n1 / 4, (floatx4 *)dst2, (const floatx4 *)src2, n2 / 4, P,
                        accumulate ? 1 : 0);
@@ -878,6 +973,14 @@ hipError_t k_sum_layers(float *dst1, const float *src1, size_t n1, float *dst2, 
     const uintptr_t al = (uintptr_t)dst1 | (uintptr_t)src1 | (uintptr_t)dst2 | (uintptr_t)src2;
     if (al & 15) return hipErrorInvalidValue;
     const size_t n = (n1 + n2) / 4 * L;
+    if (AuditSink *au = audit_sink()) {
+        // layer l: dst + l n, src + l P n (P partials of n)
+        audit(au, "sum_layers_kernel", "src1", src1, (long long)L * P * (long long)n1, false);
+        audit(au, "sum_layers_kernel", "dst1", dst1, (long long)L * (long long)n1, true);
+        audit(au, "sum_layers_kernel", "src2", src2, (long long)L * P * (long long)n2, false);
+        audit(au, "sum_layers_kernel", "dst2", dst2, (long long)L * (long long)n2, true);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(sum_layers_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (floatx4 *)dst1,
                        (const floatx4 *)src1, n1 / 4, (floatx4 *)dst2, (const floatx4 *)src2, n2 / 4, P, L);
     return hipGetLastError();
@@ -889,12 +992,21 @@ hipError_t k_sum_partials(float *dst, const float *src, int P, size_t n, bool ac
 
 hipError_t k_attn_softmax_forward(float *att, long long nrows, int T, hipStream_t s) {
     if (T > 64 * SM_NV) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "attn_softmax_forward_kernel", "att", att, nrows * T, true);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(attn_softmax_forward_kernel, dim3(grid_for(nrows, 4)), dim3(256), 0, s, att, nrows, T);
     return hipGetLastError();
 }
 
 hipError_t k_attn_softmax_backward(float *dp, const float *att, long long nrows, int T, hipStream_t s) {
     if (T > 64 * SM_NV) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "attn_softmax_backward_kernel", "dp", dp, nrows * T, true);
+        audit(au, "attn_softmax_backward_kernel", "att", att, nrows * T, false);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(attn_softmax_backward_kernel, dim3(grid_for(nrows, 4)), dim3(256), 0, s, dp, att, nrows, T);
     return hipGetLastError();
 }
@@ -903,6 +1015,14 @@ hipError_t k_crossentropy(float *logits, float *losses, const int32_t *tgt, int 
                           const int32_t *gate, hipStream_t s) {
     if (Vp % 4) return hipErrorInvalidValue;
     const int n4 = Vp / 4;
+    if (AuditSink *au = audit_sink()) {
+        const char *k = k_crossentropy_name(Vp);
+        audit(au, k, "logits", logits, (long long)BT * Vp, true);
+        audit(au, k, "losses", losses, BT, true);
+        audit(au, k, "tgt", tgt, BT, false);
+        audit(au, k, "gate", gate, 1, false);
+        return hipSuccess;
+    }
     if (n4 <= 1024)
         hipLaunchKernelGGL(crossentropy_reg_kernel<1>, dim3(BT), dim3(1024), 0, s, logits, losses, tgt, V, Vp, dscale, gate);
     else if (n4 <= 4 * 1024)
@@ -923,12 +1043,22 @@ const char *k_crossentropy_name(int Vp) {
 }
 
 hipError_t k_mean(float *loss, const float *losses, int n, hipStream_t s) {
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "mean_kernel", "losses", losses, n, false);
+        audit(au, "mean_kernel", "loss", loss, 1, true);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, loss, losses, n);
     return hipGetLastError();
 }
 
 hipError_t k_gelu_forward(float *out, const float *inp, size_t n, hipStream_t s) {
     if (n % 4) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "gelu_forward_kernel", "out", out, (long long)n, true);
+        audit(au, "gelu_forward_kernel", "inp", inp, (long long)n, false);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(gelu_forward_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, (floatx4 *)out,
                        (const floatx4 *)inp, n / 4);
     return hipGetLastError();
@@ -936,6 +1066,12 @@ hipError_t k_gelu_forward(float *out, const float *inp, size_t n, hipStream_t s)
 
 hipError_t k_gelu_backward(float *dinp, const float *inp, const float *dout, size_t n, hipStream_t s) {
     if (n % 4) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "gelu_backward_kernel", "dinp", dinp, (long long)n, true);
+        audit(au, "gelu_backward_kernel", "inp", inp, (long long)n, false);
+        audit(au, "gelu_backward_kernel", "dout", dout, (long long)n, false);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(gelu_backward_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, (floatx4 *)dinp,
                        (const floatx4 *)inp, (const floatx4 *)dout, n / 4);
     return hipGetLastError();
@@ -948,6 +1084,14 @@ hipError_t k_adamw(float *params, const float *grads, float *m, float *v, size_t
     if (n4 == 0) return hipSuccess;
     const size_t g = (n4 + 256 * ADAMW_U - 1) / (256 * ADAMW_U);
     if (g > 0x7fffffff) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "adamw_kernel", "params", params, (long long)n, true);
+        audit(au, "adamw_kernel", "grads", grads, (long long)n, false);
+        audit(au, "adamw_kernel", "m", m, (long long)n, true);
+        audit(au, "adamw_kernel", "v", v, (long long)n, true);
+        audit(au, "adamw_kernel", "gate", gate, 1, false);
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)g), dim3(256), 0, s, (floatx4 *)params, (const floatx4 *)grads,
                        (floatx4 *)m, (floatx4 *)v, n4, lr, b1, b2, eps, wd, 1.0f / c1, 1.0f / c2, gate);
     return hipGetLastError();

@@ -1,4 +1,5 @@
-"""ctypes binding of ``libgpt2mi.so`` (include/gpt2.h, include/gpt2_kernels.h).
+"""ctypes binding of ``libgpt2mi.so`` (include/gpt2.h, include/gpt2_kernels.h,
+include/gpt2_audit.h).
 
 Argument marshalling only: PyTorch provides device memory (``torch.empty``)
 and the current HIP stream; every step of the training path runs in the
@@ -67,6 +68,8 @@ _SIGS = {
     "gpt2_update": [_P, _F, _F, _F, _F, _F, _I],
     "gpt2_sync": [_P],
     "gpt2_save_checkpoint": [_P, ctypes.c_char_p, _I],
+    "gpt2_audit_step": [ctypes.POINTER(Config), _I, _I, ctypes.c_char_p, _Z, ctypes.c_char_p, _Z,
+                        ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_longlong)],
     "gpt2_load_checkpoint": [_P, ctypes.c_char_p, ctypes.POINTER(_I)],
     "gpt2_profile_enable": [_P, _I],
     "gpt2_profile_read": [_P, ctypes.POINTER(ProfileEntry), _I, ctypes.POINTER(_I)],
@@ -176,6 +179,17 @@ def _ptr(t) -> int:
 
 def _stream(device=None) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def audit_step(cfg, B: int, T: int, shrink: str | None = None, shrink_floats: int = 0):
+    """Host-only replay of one training step's launches against the layout
+    (no GPU): (ranges declared, ranges outside their tensor, report text)."""
+    c = make_config(cfg)
+    buf = ctypes.create_string_buffer(1 << 16)
+    nr, nv = ctypes.c_longlong(), ctypes.c_longlong()
+    _check(lib().gpt2_audit_step(ctypes.byref(c), B, T, shrink.encode() if shrink else None, shrink_floats, buf,
+                                 len(buf), ctypes.byref(nr), ctypes.byref(nv)))
+    return nr.value, nv.value, buf.value.decode()
 
 
 class Model:
