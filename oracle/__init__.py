@@ -66,6 +66,10 @@ def lib():
         L.ref_act_count.restype = _i64
         L.ref_act_count.argtypes = [ctypes.c_void_p, ctypes.c_char_p]
         L.ref_num_threads.restype = ctypes.c_int
+        L.ref_decode_step.restype = ctypes.c_int
+        L.ref_decode_step.argtypes = [ctypes.c_void_p, _dp, _ip, ctypes.c_int, _dp, _ip]
+        L.ref_sample.restype = ctypes.c_int
+        L.ref_sample.argtypes = [_dp, ctypes.c_int, ctypes.c_double]
         for name, args in {
             "ref_encoder_forward": [_dp, _ip, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int],
             "ref_encoder_backward": [_dp, _dp, _dp, _ip, ctypes.c_int, ctypes.c_int, ctypes.c_int],
@@ -178,6 +182,16 @@ class RefModel:
         if lib().ref_backward(self._h, _d(params), _d(grads)) != 0:
             raise RuntimeError("oracle backward needs a forward with targets first")
 
+    def decode_step(self, params: np.ndarray, tokens: np.ndarray, pos: int, coins: np.ndarray | None = None):
+        """Row (b, pos) of every sequence through the model with the cached
+        keys and values of the earlier positions; returns the next ids."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        nxt = np.empty(self.B, dtype=np.int32)
+        c = None if coins is None else np.ascontiguousarray(coins, dtype=np.float64).reshape(-1)
+        if lib().ref_decode_step(self._h, _d(params), _i(tokens), pos, _d(c), _i(nxt)) != 0:
+            raise ValueError("oracle decode: bad position or token")
+        return nxt
+
     def get(self, name: str, grad: bool = False) -> np.ndarray:
         n = lib().ref_act_count(self._h, name.encode())
         if n < 0:
@@ -261,6 +275,12 @@ def crossentropy_softmax_backward(probs, targets, N, V, ld):
     d = np.empty(N * ld)
     lib().ref_crossentropy_softmax_backward(_d(d), _d(probs), _i(targets), N, V, ld)
     return d
+
+
+def sample(z: np.ndarray, coin: float = -1.0) -> int:
+    """The oracle's next-token choice from one row of logits (coin < 0: argmax)."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    return lib().ref_sample(_d(z), z.size, coin)
 
 
 def adamw(params, grads, m, v, lr, b1, b2, eps, wd, t):

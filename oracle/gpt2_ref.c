@@ -43,7 +43,9 @@
  * = ln V for all-zero logits; softmax rows summing to one; LayerNorm output
  * statistics; attention and GELU closed forms; AdamW's first-step closed form;
  * and library routines (torch float64 layer_norm / gelu / attention /
- * cross_entropy) for the forward definitions.
+ * cross_entropy) for the forward definitions; the decoding step against
+ * this file's own full forward (the logits of a decoded position equal the
+ * forward's at that position) and its sampler against a cumulative-sum search.
  */
 #include <math.h>
 #include <stdint.h>
@@ -700,6 +702,111 @@ int ref_backward(ref_model *M, const double *params, double *grads) {
     }
     ref_encoder_backward(PAR(M, grads, 0), PAR(M, grads, 1), GACT(M, A_ENCODED), M->inputs, B, T,
                          C);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* decoding with a key/value cache                                          */
+/* ------------------------------------------------------------------------ */
+
+/* The next token from one row of logits z[0..V-1] (GeekNews, "Cách KV caching
+ * hoạt động": generation picks one token per step; the InfoQ article's run
+ * prints the sampled token ids).  coin < 0: the most probable token (the
+ * lowest index among equal maxima).  Otherwise, with p = softmax(z) (max
+ * subtracted), the first v whose cumulative probability p_0 + ... + p_v
+ * exceeds coin; coin is a uniform draw in [0, 1) supplied by the caller. */
+int ref_sample(const double *z, int V, double coin) {
+    int best = 0;
+    for (int v = 1; v < V; v++)
+        if (z[v] > z[best]) best = v;
+    if (coin < 0.0) return best;
+    double sum = 0.0;
+    for (int v = 0; v < V; v++) sum += exp(z[v] - z[best]);
+    double cum = 0.0;
+    for (int v = 0; v < V; v++) {
+        cum += exp(z[v] - z[best]) / sum;
+        if (cum > coin) return v;
+    }
+    return V - 1;
+}
+
+/* One decoding step (GeekNews, "Cách KV caching hoạt động": the keys and
+ * values of the tokens already processed are kept, so a new token needs only
+ * its own row through every layer; "Phép nhân ma trận nhanh": only the new
+ * rows of a product are multiplied).  For each sequence b, tokens[b] is the
+ * token at position pos (0 <= pos < T); rows (b, u < pos) of the saved qkv
+ * activations must hold the keys and values of the earlier positions, from
+ * ref_forward over them or from earlier decode steps.  Row (b, pos) goes
+ * through the same layers as in ref_forward (encoder, then per layer LN ->
+ * qkv -> attention over u <= pos -> projection + residual -> LN -> fc ->
+ * GELU -> projection + residual, final LN, tied head over v < V).  It writes
+ * row (b, pos) of every layer's qkv (the cache) and of the logits, and
+ * next[b] = ref_sample(logits row, coins ? coins[b] : -1).  Returns 0, or -1
+ * for a bad position or token. */
+int ref_decode_step(ref_model *M, const double *params, const int *tokens, int pos, const double *coins,
+                    int *next) {
+    int B = M->B, T = M->T, C = M->s.C, L = M->s.L, NH = M->s.NH, V = M->s.V;
+    if (pos < 0 || pos >= T) return -1;
+    for (int b = 0; b < B; b++)
+        if (tokens[b] < 0 || tokens[b] >= V) return -1;
+    int hd = C / NH;
+    i64 BT = (i64)B * T, BTC = BT * C, C3 = 3 * (i64)C;
+    double scale = 1.0 / sqrt((double)hd);
+    double *x = malloc(sizeof(double) * C), *ln = malloc(sizeof(double) * C);
+    double *atty = malloc(sizeof(double) * C), *tmp = malloc(sizeof(double) * C);
+    double *h = malloc(sizeof(double) * 4 * C), *g = malloc(sizeof(double) * 4 * C);
+    double *s = malloc(sizeof(double) * (pos + 1)), mean, rstd;
+    for (int b = 0; b < B; b++) {
+        i64 row = (i64)b * T + pos;
+        ref_encoder_forward(x, &tokens[b], PAR(M, params, 0), PAR(M, params, 1) + (i64)pos * C, 1, 1, C);
+        for (int l = 0; l < L; l++) {
+            double *qkv = ACT(M, A_QKV) + l * 3 * BTC; /* this layer's cache */
+            ref_layernorm_forward(ln, &mean, &rstd, x, PAR(M, params, 2) + (i64)l * C,
+                                  PAR(M, params, 3) + (i64)l * C, 1, C);
+            ref_matmul_forward(qkv + row * C3, ln, PAR(M, params, 4) + (i64)l * 3 * C * C,
+                               PAR(M, params, 5) + (i64)l * 3 * C, 1, C, 3 * C);
+            /* the new query against the cached keys u <= pos, per head */
+            for (int hh = 0; hh < NH; hh++) {
+                const double *q = qkv + row * C3 + (i64)hh * hd;
+                double mx = -INFINITY;
+                for (int u = 0; u <= pos; u++) {
+                    const double *k = qkv + ((i64)b * T + u) * C3 + C + (i64)hh * hd;
+                    double d = 0.0;
+                    for (int e = 0; e < hd; e++) d += q[e] * k[e];
+                    s[u] = d * scale;
+                    if (s[u] > mx) mx = s[u];
+                }
+                double sum = 0.0;
+                for (int u = 0; u <= pos; u++) {
+                    s[u] = exp(s[u] - mx);
+                    sum += s[u];
+                }
+                for (int e = 0; e < hd; e++) {
+                    double y = 0.0;
+                    for (int u = 0; u <= pos; u++)
+                        y += s[u] / sum * qkv[((i64)b * T + u) * C3 + 2 * C + (i64)hh * hd + e];
+                    atty[(i64)hh * hd + e] = y;
+                }
+            }
+            ref_matmul_forward(tmp, atty, PAR(M, params, 6) + (i64)l * C * C, PAR(M, params, 7) + (i64)l * C, 1,
+                               C, C);
+            ref_residual_forward(x, x, tmp, C);
+            ref_layernorm_forward(ln, &mean, &rstd, x, PAR(M, params, 8) + (i64)l * C,
+                                  PAR(M, params, 9) + (i64)l * C, 1, C);
+            ref_matmul_forward(h, ln, PAR(M, params, 10) + (i64)l * 4 * C * C, PAR(M, params, 11) + (i64)l * 4 * C,
+                               1, C, 4 * C);
+            ref_gelu_forward(g, h, 4 * C);
+            ref_matmul_forward(tmp, g, PAR(M, params, 12) + (i64)l * 4 * C * C, PAR(M, params, 13) + (i64)l * C, 1,
+                               4 * C, C);
+            ref_residual_forward(x, x, tmp, C);
+        }
+        ref_layernorm_forward(ln, &mean, &rstd, x, PAR(M, params, 14), PAR(M, params, 15), 1, C);
+        double *z = ACT(M, A_LOGITS) + row * V;
+        ref_matmul_forward(z, ln, PAR(M, params, 0), NULL, 1, C, V);
+        next[b] = ref_sample(z, V, coins ? coins[b] : -1.0);
+    }
+    free(x); free(ln); free(atty); free(tmp); free(h); free(g); free(s);
+    M->have_targets = 0; /* the saved activations no longer describe one forward */
     return 0;
 }
 

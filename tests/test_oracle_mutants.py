@@ -45,6 +45,11 @@ MUTANTS = [
     ("adamw_eps_inside_sqrt", "mhat / (sqrt(vhat) + eps) + wd * params[i]", "mhat / sqrt(vhat + eps) + wd * params[i]", 0),
     ("param_count_head_bias", "n[15] = C;               /* lnfb", "n[15] = C + 1;           /* lnfb", 0),
     ("act_set_drops_probs", "n[A_PROBS] = BT * s->V;", "n[A_PROBS] = 0;", 0),
+    ("decode_cache_excludes_new_key", "for (int u = 0; u <= pos; u++) {\n                    const double *k",
+     "for (int u = 0; u < pos + (pos == 0); u++) {\n                    const double *k", 0),
+    ("decode_wrong_position_embedding", "PAR(M, params, 1) + (i64)pos * C, 1, 1, C);", "PAR(M, params, 1), 1, 1, C);",
+     0),
+    ("sampler_cdf_not_normalised", "cum += exp(z[v] - z[best]) / sum;", "cum += exp(z[v] - z[best]);", 0),
 ]
 
 CHECK = r"""
@@ -64,6 +69,9 @@ checks = [
     lambda: P.test_attention_special_cases(oracle),
     lambda: P.test_gelu_limits_and_exact_gelu_bound(oracle),
     lambda: P.test_encoder_backward_all_tokens_equal(oracle),
+    lambda: P.test_decode_from_scratch_reproduces_the_full_forward(oracle, 0),
+    lambda: P.test_decode_from_scratch_reproduces_the_full_forward(oracle, 1),
+    lambda: P.test_sampler_is_argmax_or_the_cumulative_search(oracle),
 ]
 failed = 0
 for c in checks:

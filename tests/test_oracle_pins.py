@@ -364,3 +364,65 @@ def test_result_independent_of_thread_count(oracle_lib):
         outs.append(r.stdout.split())
     assert outs[0][:2] == outs[1][:2]
     assert outs[0][2] == "1" and outs[1][2] == "3"
+
+
+# ---------------------------------------------------------------- decoding with a key/value cache
+
+DECODE_CFGS = [
+    dict(L=2, C=64, NH=4, T=12, B=2, V=65, maxT=16),  # padded vocabulary, head dim 16
+    dict(L=1, C=48, NH=3, T=7, B=3, V=36, Vp=36, maxT=9),  # ragged
+]
+
+
+@pytest.mark.parametrize("cfgi", range(len(DECODE_CFGS)))
+def test_decode_from_scratch_reproduces_the_full_forward(oracle_lib, cfgi):
+    """Decoding position by position from an empty cache (no forward at all)
+    gives, at each position n, the full forward's logits at n, and leaves the
+    forward's keys and values in the cache (the KV-cache passage of the
+    GeekNews page: a new token only needs its own row)."""
+    cfg = synth.config(DECODE_CFGS[cfgi])
+    B, T, V = cfg["B"], cfg["T"], cfg["V"]
+    p = oracle_lib.pack(cfg, synth.init_params(cfg, std=0.3))
+    inp, _ = synth.batch(cfg)
+    R = oracle_lib.RefModel(cfg, B, T)
+    R.forward(p, inp)
+    full = R.get("logits").reshape(B, T, V)
+    qkv_full = R.get("qkv")
+    D = oracle_lib.RefModel(cfg, B, T)
+    for n in range(T):
+        nxt = D.decode_step(p, inp[:, n], n)
+        z = D.get("logits").reshape(B, T, V)[:, n]
+        assert np.abs(z - full[:, n]).max() <= 1e-12 * np.abs(full[:, n]).max(), n
+        assert list(nxt) == [int(np.argmax(full[b, n])) for b in range(B)]
+    assert np.abs(D.get("qkv") - qkv_full).max() <= 1e-12 * np.abs(qkv_full).max()
+    with pytest.raises(ValueError):
+        D.decode_step(p, inp[:, 0], T)
+    bad = inp[:, 0].copy()
+    bad[0] = V
+    with pytest.raises(ValueError):
+        D.decode_step(p, bad, 0)
+    R.close()
+    D.close()
+
+
+def test_sampler_is_argmax_or_the_cumulative_search(oracle_lib):
+    rng = np.random.default_rng(5)
+    for V in (1, 2, 7, 65, 1000):
+        for _ in range(20):
+            z = rng.standard_normal(V) * rng.uniform(0.1, 5.0)
+            assert oracle_lib.sample(z) == int(np.argmax(z))
+            pz = np.exp(z - z.max())
+            pz /= pz.sum()
+            cdf = np.cumsum(pz)
+            for coin in list(rng.uniform(0, 1, 5)) + [0.0]:
+                # the first v whose cumulative probability exceeds the coin
+                expect = min(int(np.searchsorted(cdf, coin, side="right")), V - 1)
+                if abs(cdf[min(expect, V - 1)] - coin) > 1e-12 and (expect == 0 or abs(cdf[expect - 1] - coin) > 1e-12):
+                    assert oracle_lib.sample(z, coin) == expect, (V, coin)
+    # ties: the lowest index
+    assert oracle_lib.sample(np.array([1.0, 3.0, 3.0, 0.0])) == 1
+    # one dominant logit: every coin picks it
+    z = np.full(50, -40.0)
+    z[17] = 40.0
+    assert all(oracle_lib.sample(z, c) == 17 for c in (1e-20, 0.3, 0.999999))
+    assert oracle_lib.sample(z, 0.0) == 0  # coin 0: the first token of nonzero probability
