@@ -172,6 +172,31 @@ gpt2_status gpt2_backward(gpt2_model *model);
 gpt2_status gpt2_update(gpt2_model *model, float lr, float beta1, float beta2, float eps,
                         float weight_decay, int t);
 
+/* One autoregressive decoding step with the key/value cache held in the
+ * model's own activation buffer (the GeekNews page, "Cách KV caching hoạt
+ * động": the keys and values of the tokens already processed are kept and
+ * only the new token's row is computed; "Phép nhân ma trận nhanh": only the
+ * new rows of each product are multiplied; the InfoQ article's run prints the
+ * ids sampled after training).
+ *
+ * tokens: DEVICE int32[B], the token at position pos of each of the B
+ * sequences (0 <= pos < T).  Rows (b, u < pos) of every layer's qkv
+ * activations must hold the keys and values of the earlier positions: from
+ * gpt2_forward over ids whose first pos positions are the prompt (a prefill;
+ * the later positions are not read), or from earlier decode steps.  The call
+ * computes row (b, pos) through every layer, writes its q | k | v into each
+ * layer's qkv rows (extending the cache) and its logits into row (b, pos) of
+ * the logits activation, and stores the next token of each sequence in
+ * next (DEVICE int32[B]): the most probable token (lowest id among equal
+ * maxima) when coins is NULL, otherwise, with p the softmax of the logits
+ * over v < V, the first v whose cumulative probability exceeds coins[b]
+ * (DEVICE float[B] of uniform draws in [0, 1) chosen by the caller).
+ * Asynchronous; ids outside [0, V) raise the model's error flag (reported by
+ * gpt2_sync) and are read as the nearest valid id.  Only activation rows
+ * (b, pos) and the work buffer are written, so a following gpt2_backward needs
+ * a new forward with targets (GPT2_ESTATE otherwise). */
+gpt2_status gpt2_decode_step(gpt2_model *model, const int32_t *tokens, int pos, const float *coins, int32_t *next);
+
 /* Wait for the stream; GPT2_ERANGE if an out-of-range id was seen since the
  * last report (the flag is then cleared, and gpt2_backward needs a new
  * forward with targets), GPT2_EDEVICE on a HIP error. */

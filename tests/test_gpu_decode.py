@@ -1,0 +1,195 @@
+"""Forward-only evaluation and decoding with the key/value cache
+(gpt2_decode_step) against the oracle.
+
+- decoding from an empty cache, position by position, and decoding after a
+  prefill by gpt2_forward: each decoded position's logits match the oracle's
+  full forward at that position (per row, 1e-4 of the row's largest
+  magnitude) and the cache rows (qkv) match the forward's;
+- the chosen ids: argmax is checked exactly against the GPU's own fp32
+  logits and against the oracle wherever the oracle's top two logits are
+  more than the logit tolerance apart; sampling with given uniform draws
+  against the oracle's choice from the same draws, except where a draw lies
+  within 1e-4 of a boundary of the oracle's cumulative distribution (then the
+  GPU's id must be one of the two ids at that boundary);
+- at the GPT-2 124M shape (B=4, T=1024): a 512-token prefill, then 8 decode
+  steps, against the oracle's forward over the first 520 ids of each
+  sequence;
+- evaluation loss: forward passes over held-out batches against the oracle.
+"""
+import numpy as np
+import pytest
+
+from transformer_lm_step_flat_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_LOGITS = 1e-4
+
+CASES = {
+    "tiny": synth.config("tiny"),
+    "ragged": synth.config(dict(L=1, C=48, NH=3, T=20, B=3, V=36, Vp=36, maxT=24)),
+    "hd64": synth.config(dict(L=2, C=128, NH=2, T=132, B=2, V=300, maxT=132, tokens="zipf")),
+    "hd12": synth.config(dict(L=2, C=48, NH=4, T=40, B=2, V=50, maxT=40)),
+}
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from transformer_lm_step_flat_amd import gpt2
+    gpt2.lib()
+    return gpt2
+
+
+def dev(a, dtype=np.int32):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype).ravel()).cuda()
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def rows_close(z, zr):
+    return float((np.abs(z - zr).max(-1) / np.abs(zr).max(-1)).max())
+
+
+def check_argmax(nxt, z_gpu, z_ref):
+    for b in range(z_ref.shape[0]):
+        assert nxt[b] == int(np.argmax(z_gpu[b].astype(np.float32))), b
+        top = np.sort(z_ref[b])[-2:]
+        if top[1] - top[0] > TOL_LOGITS * np.abs(z_ref[b]).max():
+            assert nxt[b] == int(np.argmax(z_ref[b])), b
+
+
+def check_sampled(nxt, z_ref, coins):
+    for b in range(z_ref.shape[0]):
+        p = np.exp(z_ref[b] - z_ref[b].max())
+        cdf = np.cumsum(p / p.sum())
+        want = min(int(np.searchsorted(cdf, coins[b], side="right")), len(cdf) - 1)
+        if nxt[b] != want:
+            # only a draw at a boundary of the distribution may go either way
+            lo = min(nxt[b], want)
+            assert abs(nxt[b] - want) == 1 and abs(cdf[lo] - coins[b]) <= 1e-4, (b, nxt[b], want)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_decode_matches_full_forward(g, oracle_lib, case):
+    import torch
+    cfg = CASES[case]
+    B, T, V, Vp = cfg["B"], cfg["T"], cfg["V"], cfg["Vp"]
+    tensors = synth.init_params(cfg, std=0.3)  # larger weights: peaked softmaxes, distinct argmaxes
+    inp, _ = synth.batch(cfg)
+    R = oracle_lib.RefModel(cfg, B, T)
+    p = oracle_lib.pack(cfg, tensors)
+    R.forward(p, inp)
+    zfull = R.get("logits").reshape(B, T, V)
+    qkv_ref = R.get("qkv")
+    R.close()
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, tensors, B, T))
+    rng = np.random.default_rng(3)
+    coins = rng.uniform(0, 1, (T, B)).astype(np.float32)
+    # from an empty cache: every position decoded (argmax at even positions, sampled at odd)
+    for pos in range(T):
+        c = dev(coins[pos], np.float32) if pos % 2 else None
+        nxt = M.decode_step(dev(inp[:, pos]), pos, c).cpu().numpy()
+        z = host(M.act("logits")).reshape(B, T, Vp)[:, pos, :V]
+        assert rows_close(z, zfull[:, pos]) <= TOL_LOGITS, pos
+        if pos % 2:
+            check_sampled(nxt, zfull[:, pos], coins[pos].astype(np.float64))
+        else:
+            check_argmax(nxt, z, zfull[:, pos])
+    qkv = host(M.act("qkv"))
+    assert np.abs(qkv - qkv_ref).max() <= 1e-4 * np.abs(qkv_ref).max()
+    # after a prefill of the first half by the forward
+    P = T // 2
+    junk = inp.copy()
+    junk[:, P:] = (junk[:, P:] + 7) % V  # positions >= P are never read by the decode
+    M.forward(dev(junk), None)
+    for pos in range(P, T):
+        nxt = M.decode_step(dev(inp[:, pos]), pos).cpu().numpy()
+        z = host(M.act("logits")).reshape(B, T, Vp)[:, pos, :V]
+        assert rows_close(z, zfull[:, pos]) <= TOL_LOGITS, pos
+        check_argmax(nxt, z, zfull[:, pos])
+    # a decode step leaves no batch to back-propagate
+    with pytest.raises(g.Gpt2Error) as e:
+        M.backward()
+    assert e.value.status == g.GPT2_ESTATE
+    with pytest.raises(g.Gpt2Error) as e:
+        M.decode_step(dev(inp[:, 0]), T)
+    assert e.value.status == g.GPT2_EINVAL
+    M.close()
+
+
+def test_greedy_generation_follows_the_oracle(g, oracle_lib):
+    """Generate 24 ids greedily from a 4-id prompt.  Both sides are fed the
+    GPU's ids; at every step the GPU's choice is the oracle's argmax, or, at
+    a near tie, a logit within the tolerance of the oracle's maximum."""
+    cfg = CASES["tiny"]
+    B, T, V = cfg["B"], cfg["T"], cfg["V"]
+    tensors = synth.init_params(cfg, std=0.3)
+    prompt, _ = synth.batch(cfg)
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, tensors, B, T))
+    R = oracle_lib.RefModel(cfg, B, T)
+    p = oracle_lib.pack(cfg, tensors)
+    tok = prompt[:, 0].copy()
+    same = 0
+    for pos in range(28):
+        ng = M.decode_step(dev(tok), pos).cpu().numpy()
+        nr = R.decode_step(p, tok, pos)
+        z = R.get("logits").reshape(B, T, V)[:, pos]
+        for b in range(B):
+            if ng[b] == nr[b]:
+                same += 1
+            else:
+                assert z[b, nr[b]] - z[b, ng[b]] <= TOL_LOGITS * np.abs(z[b]).max(), (pos, b)
+        tok = prompt[:, pos + 1].copy() if pos + 1 < 4 else ng.astype(np.int32)
+    print(f"{same} of {28 * B} greedy choices identical to the oracle's", flush=True)
+    assert same >= 28 * B - 2
+    M.close()
+    R.close()
+
+
+@pytest.mark.timeout(600)
+def test_decode_at_124m_after_a_prefill(g, oracle_lib):
+    cfg = synth.config("124m")
+    B, T, V, Vp = cfg["B"], cfg["T"], cfg["V"], cfg["Vp"]
+    P, S = 512, 8
+    tensors = synth.init_params(cfg)
+    inp, _ = synth.batch(cfg)
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, tensors, B, T))
+    M.forward(dev(inp), None)  # prefill (positions >= P are overwritten or never read)
+    zs, nexts = [], []
+    for pos in range(P, P + S):
+        nexts.append(M.decode_step(dev(inp[:, pos]), pos).cpu().numpy())
+        zs.append(M.act("logits").view(B, T, Vp)[:, pos, :V].cpu().numpy().astype(np.float64))
+    M.close()
+    p = oracle_lib.pack(cfg, tensors)
+    R = oracle_lib.RefModel(cfg, 1, P + S)
+    for b in range(B):
+        R.forward(p, inp[b:b + 1, :P + S])
+        zr = R.get("logits").reshape(P + S, V)[P:]
+        for i in range(S):
+            assert rows_close(zs[i][b:b + 1], zr[i:i + 1]) <= TOL_LOGITS, (b, i)
+            check_argmax(nexts[i][b:b + 1], zs[i][b:b + 1], zr[i:i + 1])
+        print(f"sequence {b}: {S} decoded positions match", flush=True)
+    R.close()
+
+
+def test_eval_loss_over_held_out_batches(g, oracle_lib):
+    cfg = synth.config("small", B=4)
+    B, T = cfg["B"], cfg["T"]
+    tensors = synth.init_params(cfg)
+    M = g.Model(cfg, B, T, init_params=g.pack_params(cfg, tensors, B, T))
+    held_out = [synth.batch(cfg, step=1000 + i) for i in range(3)]
+    loss = M.eval_loss([(dev(i), dev(t)) for i, t in held_out])
+    R = oracle_lib.RefModel(cfg, B, T)
+    p = oracle_lib.pack(cfg, tensors)
+    ref = sum(R.forward(p, i, t) for i, t in held_out) / len(held_out)
+    assert abs(loss - ref) <= 1e-5 * ref, (loss, ref)
+    M.close()
+    R.close()

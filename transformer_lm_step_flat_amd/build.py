@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libgpt2mi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["gpt2.hip", "gemm.hip", "kernels.hip", "attention.hip", "probe.hip", "noalloc.hip", "checkpoint.cpp", "audit.cpp"]
+SOURCES = ["gpt2.hip", "gemm.hip", "kernels.hip", "attention.hip", "probe.hip", "noalloc.hip", "decode.hip", "checkpoint.cpp", "audit.cpp"]
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -1,0 +1,22 @@
+// Launchers of the decoding-step kernels (gfx950); each enqueues on `s` and
+// returns hipGetLastError() (hipErrorInvalidValue for shapes it cannot take).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// out[r][o] = epi(x[r] . W[o] + bias[o]) for r < R, o < OC; x rows ldx apart
+// (K floats used), out rows ldo apart, W [OC][K] (out x in).  epi 0: store;
+// 1: + aux[r][o] (aux rows ldaux apart; out may equal aux); 2: GELU.
+hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ldx, const float *W, const float *bias,
+                         const float *aux, long long ldaux, int R, int K, int OC, int epi, hipStream_t s);
+const char *k_rows_linear_name(int OC);
+
+// atty[b][:] = causal attention of query row (b, pos) over key/value rows
+// (b, u <= pos) of qkv [B][T][3C] (q | k | v, heads of C / NH).
+hipError_t k_decode_attention(float *atty, const float *qkv, int pos, int B, int T, int C, int NH, hipStream_t s);
+
+// next[b] from logits row b (ld floats apart, first V columns): argmax when
+// coins is NULL, else the first v whose cumulative probability exceeds
+// coins[b].
+hipError_t k_sample(int32_t *next, const float *logits, long long ld, int B, int V, const float *coins,
+                    hipStream_t s);

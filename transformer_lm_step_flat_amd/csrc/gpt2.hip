@@ -29,6 +29,7 @@
 #include "audit.h"
 #include "checkpoint.h"
 #include "common.h"
+#include "decode.h"
 #include "gemm.h"
 #include "probe.h"
 #include "kernels.h"
@@ -264,13 +265,14 @@ struct Layout {
     size_t poff[16], pcnt[16], nparams;
     size_t aoff[NUM_ACTS], acnt[NUM_ACTS], nacts;
     // work buffer
-    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_flash, w_part, w_splitk, w_splitk_dw, w_dbias, nwork;
+    size_t w_dres, w_dln, w_datty, w_dqkv, w_dfch, w_datt, w_flash, w_part, w_splitk, w_splitk_dw, w_dbias, w_dec,
+        nwork;
     // per-layer split-K partials of each site's weight / bias gradient, summed
     // for all layers at the end of the backward (ks 1: none)
     int site_ks[NSITES];
     size_t w_site_dw[NSITES], w_site_db[NSITES];
     // int buffer
-    size_t i_tok, i_order, i_err, niwork;
+    size_t i_tok, i_order, i_err, i_dec, niwork;
     // the work regions with their exact float counts (offsets are padded to
     // 64 floats), each cut into `parts` equal slices (per layer or per slot)
     struct WRegion {
@@ -377,11 +379,15 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
         }
     }
     l.w_dbias = add_w("dbias_ws", 16 * 4 * C, 1);
+    // one decoding step's rows: residual x, LayerNorm output, attention
+    // output [B][C] each, MLP hidden [B][4C], row mean and rstd [B] each
+    l.w_dec = add_w("decode", (size_t)B * 7 * C + 2 * (size_t)B, 1);
     l.nwork = off;
     l.i_tok = 0;
     l.i_order = align_up(BT);
     l.i_err = l.i_order + align_up(BT);
-    l.niwork = l.i_err + ALIGN;
+    l.i_dec = l.i_err + ALIGN;  // the decoding step's token order (unused beyond the id check)
+    l.niwork = l.i_dec + align_up((size_t)B);
 }
 
 // When a model's profiler is on, each launch of the step is bracketed by two
@@ -1032,6 +1038,49 @@ gpt2_status gpt2_update(gpt2_model *m, float lr, float beta1, float beta2, float
     return GPT2_OK;
 }
 
+gpt2_status gpt2_decode_step(gpt2_model *m, const int32_t *tokens, int pos, const float *coins, int32_t *next) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    ProfScope prof_scope(m);
+    if (!tokens || !next) return fail(m, GPT2_EINVAL, "tokens and next are required");
+    const Layout &l = m->lo;
+    if (pos < 0 || pos >= l.T) return fail(m, GPT2_EINVAL, "pos must be in [0, T)");
+    const int B = l.B, T = l.T, C = l.C, NH = l.NH;
+    const size_t BTC = (size_t)l.BT * C, c = C;
+    hipStream_t s = m->stream;
+    float *P = m->buf.params, *A = m->buf.acts;
+    float *x = m->buf.work + l.w_dec, *ln = x + (size_t)B * C, *att = ln + (size_t)B * C, *h = att + (size_t)B * C;
+    float *mean = h + (size_t)4 * B * C, *rstd = mean + B;
+    int32_t *err = m->buf.iwork + l.i_err;
+    m->have_targets = false;  // rows of the saved activations are overwritten
+    const double w = 4.0 * B;  // bytes per float of one row per sequence
+    KRUN(m, "token_prep_kernel", 12.0 * B, k_token_prep(tokens, nullptr, m->buf.iwork + l.i_dec, err, B, l.V, s));
+    KRUN(m, "encoder_forward_kernel", 3.0 * w * C, k_encoder_forward(x, tokens, P + l.poff[0], P + l.poff[1] + (size_t)pos * C, B, 1, C, l.V, s));
+    for (int li = 0; li < l.L; li++) {
+        float *qkv = A + l.aoff[A_QKV] + li * 3 * BTC;  // this layer's cache: rows (b, u) of q | k | v
+        KRUN(m, "layernorm_forward_kernel", 2.0 * w * C, k_layernorm_forward(ln, mean, rstd, x, P + l.poff[2] + li * c, P + l.poff[3] + li * c, B, C, s));
+        KRUNF(m, k_rows_linear_name(3 * C), 2.0 * B * C * 3 * C, 4.0 * 3 * C * C + w * 4 * C,
+              k_rows_linear(qkv + (size_t)pos * 3 * C, (long long)T * 3 * C, ln, C, P + l.poff[4] + li * 3 * c * c,
+                            P + l.poff[5] + li * 3 * c, nullptr, 0, B, C, 3 * C, 0, s));
+        KRUNF(m, "decode_attention_kernel", 4.0 * B * C * (pos + 1.0), w * C * 2 * (pos + 1.0) + 2 * w * C,
+              k_decode_attention(att, qkv, pos, B, T, C, NH, s));
+        KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * C, 4.0 * C * C + 3 * w * C,
+              k_rows_linear(x, C, att, C, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, x, C, B, C, C, 1, s));
+        KRUN(m, "layernorm_forward_kernel", 2.0 * w * C, k_layernorm_forward(ln, mean, rstd, x, P + l.poff[8] + li * c, P + l.poff[9] + li * c, B, C, s));
+        KRUNF(m, k_rows_linear_name(4 * C), 2.0 * B * C * 4 * C, 4.0 * 4 * C * C + w * 5 * C,
+              k_rows_linear(h, 4 * C, ln, C, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, nullptr, 0, B,
+                            C, 4 * C, 2, s));
+        KRUNF(m, k_rows_linear_name(C), 2.0 * B * 4 * C * C, 4.0 * 4 * C * C + w * 6 * C,
+              k_rows_linear(x, C, h, 4 * C, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, x, C, B, 4 * C, C,
+                            1, s));
+    }
+    float *logits = A + l.aoff[A_LOGITS] + (size_t)pos * l.Vp;  // row (b, pos) at b T Vp
+    KRUN(m, "layernorm_forward_kernel", 2.0 * w * C, k_layernorm_forward(ln, mean, rstd, x, P + l.poff[14], P + l.poff[15], B, C, s));
+    KRUNF(m, k_rows_linear_name(l.Vp), 2.0 * B * C * l.Vp, 4.0 * (double)l.Vp * C + w * (C + l.Vp),
+          k_rows_linear(logits, (long long)T * l.Vp, ln, C, P + l.poff[0], nullptr, nullptr, 0, B, C, l.Vp, 0, s));
+    KRUN(m, "sample_kernel", w * l.V, k_sample(next, logits, (long long)T * l.Vp, B, l.V, coins, s));
+    return GPT2_OK;
+}
+
 gpt2_status gpt2_sync(gpt2_model *m) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
     int32_t h_err = 0;
@@ -1402,8 +1451,12 @@ gpt2_status gpt2_audit_step(const gpt2_config *cfg, int B, int T, const char *sh
     ck.add(base(6), l.i_tok, (size_t)l.BT, 1, "iwork:ids");
     ck.add(base(6), l.i_order, (size_t)l.BT, 1, "iwork:order");
     ck.add(base(6), l.i_err, 1, 1, "iwork:err");
+    ck.add(base(6), l.i_dec, (size_t)l.B, 1, "iwork:decode_order");
     ck.add(base(7), 0, (size_t)l.BT, 1, "caller:inputs");
     ck.add(base(8), 0, (size_t)l.BT, 1, "caller:targets");
+    ck.add(base(9), 0, (size_t)l.B, 1, "caller:decode_tokens");
+    ck.add(base(10), 0, (size_t)l.B, 1, "caller:coins");
+    ck.add(base(11), 0, (size_t)l.B, 1, "caller:next");
     const size_t buf_floats[7] = {l.nparams, l.nparams, l.nparams, l.nparams, l.nacts, l.nwork, l.niwork};
     for (int b = 0; b < 7; b++) ck.buffers.push_back({base(b), base(b) + buf_floats[b] * 4});
     ck.seal();
@@ -1420,6 +1473,11 @@ gpt2_status gpt2_audit_step(const gpt2_config *cfg, int B, int T, const char *sh
     if (st == GPT2_OK) st = gpt2_zero_grad(m);
     if (st == GPT2_OK) st = gpt2_backward(m);
     if (st == GPT2_OK) st = gpt2_update(m, 1e-4f, 0.9f, 0.999f, 1e-8f, 0.0f, 1);
+    const int32_t *dtok = (const int32_t *)base(9);
+    const float *coins = (const float *)base(10);
+    int32_t *dnext = (int32_t *)base(11);
+    for (int pos : {0, T / 2, T - 1})
+        if (st == GPT2_OK) st = gpt2_decode_step(m, dtok, pos, pos == 0 ? nullptr : coins, dnext);
     set_audit_sink(nullptr);
     const std::string err = m ? m->err : g_last_error;
     gpt2_free(m);

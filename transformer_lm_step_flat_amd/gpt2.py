@@ -67,6 +67,7 @@ _SIGS = {
     "gpt2_backward": [_P],
     "gpt2_update": [_P, _F, _F, _F, _F, _F, _I],
     "gpt2_sync": [_P],
+    "gpt2_decode_step": [_P, _P, _I, _P, _P],
     "gpt2_save_checkpoint": [_P, ctypes.c_char_p, _I],
     "gpt2_audit_step": [ctypes.POINTER(Config), _I, _I, ctypes.c_char_p, _Z, ctypes.c_char_p, _Z,
                         ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_longlong)],
@@ -276,6 +277,24 @@ class Model:
 
     def sync(self):
         _check(lib().gpt2_sync(self._h), self._h)
+
+    # --- evaluation and decoding
+    def eval_loss(self, batches) -> float:
+        """Mean of the mean losses of (inputs, targets) device batches: forward
+        passes only (the pages' validation loss)."""
+        losses = [self.forward(i, t) for i, t in batches]
+        return sum(losses) / len(losses)
+
+    def decode_step(self, tokens, pos: int, coins=None, next_ids=None):
+        """Row pos of every sequence through the model with the cached keys and
+        values of positions < pos; returns the device int32[B] next ids."""
+        for t, dt in ((tokens, torch.int32), (coins, torch.float32)):
+            if t is not None and (t.dtype != dt or not t.is_cuda or t.numel() != self.B or not t.is_contiguous()):
+                raise ValueError("tokens (int32) and coins (float32) must be contiguous device tensors of B elements")
+        if next_ids is None:
+            next_ids = torch.empty(self.B, dtype=torch.int32, device=self.device)
+        _check(lib().gpt2_decode_step(self._h, _ptr(tokens), pos, _ptr(coins), _ptr(next_ids)), self._h)
+        return next_ids
 
     # --- checkpoints
     def save(self, path: str, t: int):
