@@ -284,6 +284,51 @@ def measured_peaks(torch, gpt2, copy_mib=1024, reps=5):
     return {"mfma_fp32_tflops": best_mfma, "hbm_copy_gbs": best_copy, "copy_mib": copy_mib}
 
 
+def decode_bench(torch, M, di, B, T, prefill, steps):
+    """Greedy decoding with the key/value cache: a forward over the batch as
+    the prefill, then `steps` decode steps from position `prefill`, each
+    step's ids feeding the next (no host round trip).  Returns tokens/s and
+    the per-kernel HBM rates of a second, event-bracketed pass."""
+    M.forward(di, None)
+    first = di.view(B, T)[:, prefill].contiguous()
+    bufs = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(2)]
+
+    def run():
+        tok = first
+        for i in range(steps):
+            tok = M.decode_step(tok, prefill + i, None, bufs[i % 2])
+
+    run()  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    M.profile_enable(True)
+    run()
+    prof = M.profile_read()
+    M.profile_enable(False)
+    by = {}
+    for e in prof:
+        k = e["name"].partition("|")[0]
+        a = by.setdefault(k, dict(name=k, launches=0, ms=0.0, bytes=0.0))
+        for f in ("launches", "ms", "bytes"):
+            a[f] += e[f]
+    step_bytes = sum(e["bytes"] for e in by.values()) / steps
+    ev_ms = sum(e["ms"] for e in by.values()) / steps
+    kernels = sorted(({"name": e["name"], "launches_per_step": e["launches"] / steps,
+                       "ms_per_step": e["ms"] / steps, "GBs": e["bytes"] / e["ms"] * 1e-6,
+                       "frac_hbm": e["bytes"] / e["ms"] * 1e-6 / PEAK_HBM_GBS} for e in by.values()),
+                     key=lambda k: -k["ms_per_step"])
+    return {"tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms, "B": B, "prefill": prefill,
+            "steps": steps, "sampling": "greedy",
+            "algorithmic_bytes_per_step": step_bytes,
+            "achieved_GBs": step_bytes / (ms * 1e-3) / 1e9, "frac_hbm": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "kernel_ms_per_step_with_events": ev_ms, "kernels": kernels[:8]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +338,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time the steps without per-launch events")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--decode-steps", type=int, default=64, help="greedy decode steps timed after the training steps")
+    ap.add_argument("--decode-prefill", type=int, default=512)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of MIB MiB (for scaling HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -436,6 +483,15 @@ def main():
                     "frac_of_measured_peak": achieved / (peaks["mfma_fp32_tflops"] if bound == "mfma"
                                                          else peaks["hbm_copy_gbs"])}
 
+    decode = None
+    if args.decode_steps > 0 and args.decode_prefill + args.decode_steps <= T:
+        decode = decode_bench(torch, M, batches[0][0], B, T, args.decode_prefill, args.decode_steps)
+        log(f"decode: {decode['tokens_per_s']:.0f} tokens/s ({decode['ms_per_step']:.3f} ms per step of {B} tokens, "
+            f"{decode['achieved_GBs']:.0f} GB/s of algorithmic traffic, {100 * decode['frac_hbm']:.1f}% of HBM peak)")
+        for k in decode["kernels"]:
+            log(f"  {k['name']:<34s} {k['launches_per_step']:5.1f}/step {k['ms_per_step']:7.4f} ms/step "
+                f"{k['GBs']:7.0f} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on a {args.cpu_sample_tokens}-id sample ...")
@@ -468,6 +524,7 @@ def main():
         "measured_peaks": peaks,
         "ms_per_step_with_events": ms_ev,
         "kernels": kernels[:16],
+        "decode": decode,
     }
     print(json.dumps(out))
 

@@ -4,16 +4,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// out[r][o] = epi(x[r] . W[o] + bias[o]) for r < R, o < OC; x rows ldx apart
-// (K floats used), out rows ldo apart, W [OC][K] (out x in).  epi 0: store;
-// 1: + aux[r][o] (aux rows ldaux apart; out may equal aux); 2: GELU.
+// out[r][o] = epi(xin[r] . W[o] + bias[o]) for r < R, o < OC; x rows ldx
+// apart (K floats used), out rows ldo apart, W [OC][K] (out x in).  xin = x,
+// or LayerNorm(x) with gains lnw and shifts lnb [K] when lnw is non-null
+// (K <= 2048).  epi 0: store; 1: + aux[r][o] (aux rows ldaux apart; out may
+// equal aux; not with LayerNorm); 2: GELU.
 hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ldx, const float *W, const float *bias,
-                         const float *aux, long long ldaux, int R, int K, int OC, int epi, hipStream_t s);
+                         const float *aux, long long ldaux, const float *lnw, const float *lnb, int R, int K, int OC,
+                         int epi, hipStream_t s);
 const char *k_rows_linear_name(int OC);
 
 // atty[b][:] = causal attention of query row (b, pos) over key/value rows
-// (b, u <= pos) of qkv [B][T][3C] (q | k | v, heads of C / NH).
-hipError_t k_decode_attention(float *atty, const float *qkv, int pos, int B, int T, int C, int NH, hipStream_t s);
+// (b, u <= pos) of qkv [B][T][3C] (q | k | v, heads of C / NH), the keys
+// split into chunks whose partial results go through ws
+// (decode_attention_work floats) and are merged in chunk order.
+size_t decode_attention_work(int B, int T, int C, int NH);
+hipError_t k_decode_attention(float *atty, float *ws, const float *qkv, int pos, int B, int T, int C, int NH,
+                              hipStream_t s);
 
 // next[b] from logits row b (ld floats apart, first V columns): argmax when
 // coins is NULL, else the first v whose cumulative probability exceeds

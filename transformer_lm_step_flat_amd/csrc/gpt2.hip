@@ -379,9 +379,9 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
         }
     }
     l.w_dbias = add_w("dbias_ws", 16 * 4 * C, 1);
-    // one decoding step's rows: residual x, LayerNorm output, attention
-    // output [B][C] each, MLP hidden [B][4C], row mean and rstd [B] each
-    l.w_dec = add_w("decode", (size_t)B * 7 * C + 2 * (size_t)B, 1);
+    // one decoding step's rows: residual x and attention output [B][C] each,
+    // MLP hidden [B][4C], then the attention's per-chunk partials
+    l.w_dec = add_w("decode", (size_t)B * 6 * C + decode_attention_work(B, T, (int)C, (int)NH), 1);
     l.nwork = off;
     l.i_tok = 0;
     l.i_order = align_up(BT);
@@ -1048,35 +1048,37 @@ gpt2_status gpt2_decode_step(gpt2_model *m, const int32_t *tokens, int pos, cons
     const size_t BTC = (size_t)l.BT * C, c = C;
     hipStream_t s = m->stream;
     float *P = m->buf.params, *A = m->buf.acts;
-    float *x = m->buf.work + l.w_dec, *ln = x + (size_t)B * C, *att = ln + (size_t)B * C, *h = att + (size_t)B * C;
-    float *mean = h + (size_t)4 * B * C, *rstd = mean + B;
+    float *x = m->buf.work + l.w_dec, *att = x + (size_t)B * C, *h = att + (size_t)B * C;
+    float *aws = h + (size_t)4 * B * C;
     int32_t *err = m->buf.iwork + l.i_err;
     m->have_targets = false;  // rows of the saved activations are overwritten
     const double w = 4.0 * B;  // bytes per float of one row per sequence
+    const double nkeys = pos + 1.0;
     KRUN(m, "token_prep_kernel", 12.0 * B, k_token_prep(tokens, nullptr, m->buf.iwork + l.i_dec, err, B, l.V, s));
     KRUN(m, "encoder_forward_kernel", 3.0 * w * C, k_encoder_forward(x, tokens, P + l.poff[0], P + l.poff[1] + (size_t)pos * C, B, 1, C, l.V, s));
     for (int li = 0; li < l.L; li++) {
         float *qkv = A + l.aoff[A_QKV] + li * 3 * BTC;  // this layer's cache: rows (b, u) of q | k | v
-        KRUN(m, "layernorm_forward_kernel", 2.0 * w * C, k_layernorm_forward(ln, mean, rstd, x, P + l.poff[2] + li * c, P + l.poff[3] + li * c, B, C, s));
+        // qkv of the new rows from LayerNorm(x) (fused)
         KRUNF(m, k_rows_linear_name(3 * C), 2.0 * B * C * 3 * C, 4.0 * 3 * C * C + w * 4 * C,
-              k_rows_linear(qkv + (size_t)pos * 3 * C, (long long)T * 3 * C, ln, C, P + l.poff[4] + li * 3 * c * c,
-                            P + l.poff[5] + li * 3 * c, nullptr, 0, B, C, 3 * C, 0, s));
-        KRUNF(m, "decode_attention_kernel", 4.0 * B * C * (pos + 1.0), w * C * 2 * (pos + 1.0) + 2 * w * C,
-              k_decode_attention(att, qkv, pos, B, T, C, NH, s));
+              k_rows_linear(qkv + (size_t)pos * 3 * C, (long long)T * 3 * C, x, C, P + l.poff[4] + li * 3 * c * c,
+                            P + l.poff[5] + li * 3 * c, nullptr, 0, P + l.poff[2] + li * c, P + l.poff[3] + li * c, B, C,
+                            3 * C, 0, s));
+        KRUNF(m, "decode_attn_partial_kernel", 4.0 * B * C * nkeys, w * C * 2 * nkeys + 2 * w * C,
+              k_decode_attention(att, aws, qkv, pos, B, T, C, NH, s));
         KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * C, 4.0 * C * C + 3 * w * C,
-              k_rows_linear(x, C, att, C, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, x, C, B, C, C, 1, s));
-        KRUN(m, "layernorm_forward_kernel", 2.0 * w * C, k_layernorm_forward(ln, mean, rstd, x, P + l.poff[8] + li * c, P + l.poff[9] + li * c, B, C, s));
+              k_rows_linear(x, C, att, C, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, x, C, nullptr, nullptr, B,
+                            C, C, 1, s));
         KRUNF(m, k_rows_linear_name(4 * C), 2.0 * B * C * 4 * C, 4.0 * 4 * C * C + w * 5 * C,
-              k_rows_linear(h, 4 * C, ln, C, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, nullptr, 0, B,
-                            C, 4 * C, 2, s));
+              k_rows_linear(h, 4 * C, x, C, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, nullptr, 0,
+                            P + l.poff[8] + li * c, P + l.poff[9] + li * c, B, C, 4 * C, 2, s));
         KRUNF(m, k_rows_linear_name(C), 2.0 * B * 4 * C * C, 4.0 * 4 * C * C + w * 6 * C,
-              k_rows_linear(x, C, h, 4 * C, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, x, C, B, 4 * C, C,
-                            1, s));
+              k_rows_linear(x, C, h, 4 * C, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, x, C, nullptr,
+                            nullptr, B, 4 * C, C, 1, s));
     }
     float *logits = A + l.aoff[A_LOGITS] + (size_t)pos * l.Vp;  // row (b, pos) at b T Vp
-    KRUN(m, "layernorm_forward_kernel", 2.0 * w * C, k_layernorm_forward(ln, mean, rstd, x, P + l.poff[14], P + l.poff[15], B, C, s));
     KRUNF(m, k_rows_linear_name(l.Vp), 2.0 * B * C * l.Vp, 4.0 * (double)l.Vp * C + w * (C + l.Vp),
-          k_rows_linear(logits, (long long)T * l.Vp, ln, C, P + l.poff[0], nullptr, nullptr, 0, B, C, l.Vp, 0, s));
+          k_rows_linear(logits, (long long)T * l.Vp, x, C, P + l.poff[0], nullptr, nullptr, 0, P + l.poff[14],
+                        P + l.poff[15], B, C, l.Vp, 0, s));
     KRUN(m, "sample_kernel", w * l.V, k_sample(next, logits, (long long)T * l.Vp, B, l.V, coins, s));
     return GPT2_OK;
 }
