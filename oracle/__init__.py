@@ -68,6 +68,10 @@ def lib():
         L.ref_num_threads.restype = ctypes.c_int
         L.ref_decode_step.restype = ctypes.c_int
         L.ref_decode_step.argtypes = [ctypes.c_void_p, _dp, _ip, ctypes.c_int, _dp, _ip]
+        L.ref_round_bf16.restype = ctypes.c_double
+        L.ref_round_bf16.argtypes = [ctypes.c_double]
+        L.ref_set_bf16_products.restype = None
+        L.ref_set_bf16_products.argtypes = [ctypes.c_int]
         L.ref_sample.restype = ctypes.c_int
         L.ref_sample.argtypes = [_dp, ctypes.c_int, ctypes.c_double]
         for name, args in {
@@ -275,6 +279,24 @@ def crossentropy_softmax_backward(probs, targets, N, V, ld):
     d = np.empty(N * ld)
     lib().ref_crossentropy_softmax_backward(_d(d), _d(probs), _i(targets), N, V, ld)
     return d
+
+
+def round_bf16(x: float) -> float:
+    """x rounded to bfloat16 (8 significant bits, ties to even), as a float."""
+    return lib().ref_round_bf16(float(x))
+
+
+class bf16_products:
+    """Within this context the oracle's linear-layer products (forward and
+    backward, the head included) use bfloat16 roundings of their operands."""
+
+    def __enter__(self):
+        lib().ref_set_bf16_products(1)
+        return self
+
+    def __exit__(self, *exc):
+        lib().ref_set_bf16_products(0)
+        return False
 
 
 def sample(z: np.ndarray, coin: float = -1.0) -> int:

@@ -261,11 +261,49 @@ void ref_layernorm_backward(double *dinp, double *dw, double *db, const double *
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* reduced-precision products                                                */
+/* ------------------------------------------------------------------------ */
+
+/* The QbitAI llm.c article ("手動實現每個層前向/反向傳播") names lower precision
+ * (fp16 and below) as the next step for the trainer.  Reading taken here: in
+ * that mode the operands of every linear-layer product (the qkv, projection,
+ * MLP and head matmuls, forward and backward) are rounded to bfloat16 -- 8
+ * significant bits, the exponent range of fp32 -- and the products are
+ * accumulated at full precision; everything else (attention, LayerNorm,
+ * softmax, GELU, bias sums, AdamW and the stored parameters) stays as it is. */
+
+/* x rounded to the nearest value with 8 significant bits, ties to even. */
+double ref_round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    double m = frexp(x, &e);           /* x = m 2^e, 0.5 <= |m| < 1 */
+    double r = rint(ldexp(m, 8));      /* 8 significant bits; rint rounds ties to even */
+    return ldexp(r, e - 8);
+}
+
+static int ref_bf16_products = 0;
+
+/* 0: products of the operands as given; 1: of their bfloat16 roundings. */
+void ref_set_bf16_products(int on) { ref_bf16_products = on != 0; }
+
+/* a copy of n operand values, rounded when the bfloat16 mode is on (NULL
+ * when it is off: use the operand itself) */
+static double *bf16_operand(const double *a, i64 n) {
+    if (!ref_bf16_products) return NULL;
+    double *c = malloc(sizeof(double) * (size_t)n);
+    for (i64 i = 0; i < n; i++) c[i] = ref_round_bf16(a[i]);
+    return c;
+}
+
 /* Linear: out[r][o] = bias[o] + sum_i inp[r][i] * W[o][i]  (W is OC x K,
  * row o holds the input weights of output o; bias may be NULL) -- GeekNews,
  * "Triển khai các lớp mạng nơ-ron": matmul, then the bias on every row. */
 void ref_matmul_forward(double *out, const double *inp, const double *W, const double *bias,
                         int N, int K, int OC) {
+    double *ri = bf16_operand(inp, (i64)N * K), *rw = bf16_operand(W, (i64)OC * K);
+    if (ri) inp = ri;
+    if (rw) W = rw;
 #pragma omp parallel for schedule(static)
     for (int r = 0; r < N; r++) {
         const double *x = inp + (i64)r * K;
@@ -276,6 +314,8 @@ void ref_matmul_forward(double *out, const double *inp, const double *W, const d
             out[(i64)r * OC + o] = (bias ? bias[o] : 0.0) + acc;
         }
     }
+    free(ri);
+    free(rw);
 }
 
 /* Linear backward:
@@ -286,12 +326,17 @@ void ref_matmul_forward(double *out, const double *inp, const double *W, const d
  * the innermost index is contiguous in memory, which does not change any sum. */
 void ref_matmul_backward(double *dinp, double *dW, double *db, const double *dout,
                          const double *inp, const double *W, int N, int K, int OC) {
+    /* operands of the two products (rounded in the bfloat16 mode); the bias
+     * sum is no product and takes dout as given */
+    double *rd = bf16_operand(dout, (i64)N * OC), *ri = bf16_operand(inp, (i64)N * K);
+    double *rw = bf16_operand(W, (i64)OC * K);
+    const double *pd = rd ? rd : dout, *pi = ri ? ri : inp, *pw = rw ? rw : W;
 #pragma omp parallel for schedule(static)
     for (int r = 0; r < N; r++) {
         double *dx = dinp + (i64)r * K;
         for (int o = 0; o < OC; o++) {
-            double d = dout[(i64)r * OC + o];
-            const double *wr = W + (i64)o * K;
+            double d = pd[(i64)r * OC + o];
+            const double *wr = pw + (i64)o * K;
             for (int i = 0; i < K; i++) dx[i] += d * wr[i];
         }
     }
@@ -300,13 +345,16 @@ void ref_matmul_backward(double *dinp, double *dW, double *db, const double *dou
         double *gw = dW + (i64)o * K;
         double sb = 0.0;
         for (int r = 0; r < N; r++) {
-            double d = dout[(i64)r * OC + o];
-            const double *x = inp + (i64)r * K;
+            double d = pd[(i64)r * OC + o];
+            const double *x = pi + (i64)r * K;
             for (int i = 0; i < K; i++) gw[i] += d * x[i];
-            sb += d;
+            sb += dout[(i64)r * OC + o];
         }
         if (db) db[o] += sb;
     }
+    free(rd);
+    free(ri);
+    free(rw);
 }
 
 /* Causal multi-head self-attention over qkv rows [q | k | v] (each C wide;

@@ -50,6 +50,9 @@ MUTANTS = [
     ("decode_wrong_position_embedding", "PAR(M, params, 1) + (i64)pos * C, 1, 1, C);", "PAR(M, params, 1), 1, 1, C);",
      0),
     ("sampler_cdf_not_normalised", "cum += exp(z[v] - z[best]) / sum;", "cum += exp(z[v] - z[best]);", 0),
+    ("bf16_seven_bits", "double r = rint(ldexp(m, 8));", "double r = rint(ldexp(m, 7));", 0),
+    ("bf16_bias_sum_rounded", "sb += dout[(i64)r * OC + o];", "sb += d;", 0),
+    ("bf16_weight_not_rounded", "if (rw) W = rw;", "(void)rw;", 0),
 ]
 
 CHECK = r"""
@@ -72,6 +75,8 @@ checks = [
     lambda: P.test_decode_from_scratch_reproduces_the_full_forward(oracle, 0),
     lambda: P.test_decode_from_scratch_reproduces_the_full_forward(oracle, 1),
     lambda: P.test_sampler_is_argmax_or_the_cumulative_search(oracle),
+    lambda: P.test_bf16_rounding_matches_closed_forms_and_torch(oracle),
+    lambda: P.test_bf16_products_round_the_operands_only(oracle),
 ]
 failed = 0
 for c in checks:

@@ -426,3 +426,49 @@ def test_sampler_is_argmax_or_the_cumulative_search(oracle_lib):
     z[17] = 40.0
     assert all(oracle_lib.sample(z, c) == 17 for c in (1e-20, 0.3, 0.999999))
     assert oracle_lib.sample(z, 0.0) == 0  # coin 0: the first token of nonzero probability
+
+
+# ---------------------------------------------------------------- bfloat16 products
+
+def test_bf16_rounding_matches_closed_forms_and_torch(oracle_lib):
+    import torch
+    r = oracle_lib.round_bf16
+    assert r(1.0) == 1.0 and r(-2.75) == -2.75 and r(0.0) == 0.0
+    assert r(1 + 2 ** -8) == 1.0               # a tie goes to the even neighbour
+    assert r(1 + 3 * 2 ** -8) == 1 + 2 ** -6   # and here up, to the even one
+    assert r(1 + 2 ** -8 + 2 ** -20) == 1 + 2 ** -7
+    assert r(1 / 3) == 0.333984375
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ties = (np.arange(1, 200, dtype=np.float32) * 2 ** -8 + 1).astype(np.float32)
+    for v in (x, ties, -ties):
+        want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+        got = np.array([r(float(a)) for a in v])
+        assert np.array_equal(got, want)
+
+
+def _bf16(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_products_round_the_operands_only(oracle_lib):
+    """In the bfloat16 mode a linear layer multiplies the roundings of its
+    operands at full precision; the bias and the bias gradient are untouched."""
+    rng = np.random.default_rng(9)
+    N, K, OC = 7, 33, 5
+    x = rng.standard_normal((N, K)).astype(np.float32).astype(np.float64)
+    W = rng.standard_normal((OC, K)).astype(np.float32).astype(np.float64)
+    b = rng.standard_normal(OC).astype(np.float32).astype(np.float64)
+    dout = rng.standard_normal((N, OC)).astype(np.float32).astype(np.float64)
+    with oracle_lib.bf16_products():
+        out = oracle_lib.matmul_forward(x.ravel(), W.ravel(), b, N, K, OC).reshape(N, OC)
+        dx, dW, db = np.zeros(N * K), np.zeros(OC * K), np.zeros(OC)
+        oracle_lib.matmul_backward(dx, dW, db, dout.ravel(), x.ravel(), W.ravel(), N, K, OC)
+    assert np.abs(out - (_bf16(x) @ _bf16(W).T + b)).max() < 1e-12
+    assert np.abs(dx.reshape(N, K) - _bf16(dout) @ _bf16(W)).max() < 1e-12
+    assert np.abs(dW.reshape(OC, K) - _bf16(dout).T @ _bf16(x)).max() < 1e-12
+    assert np.abs(db - dout.sum(0)).max() < 1e-12
+    # and the mode is off again outside the context
+    out2 = oracle_lib.matmul_forward(x.ravel(), W.ravel(), b, N, K, OC).reshape(N, OC)
+    assert np.abs(out2 - (x @ W.T + b)).max() < 1e-12
