@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "train tokens/sec (fwd+bwd+AdamW) GPT-2 124M B=4 T=1024 fp32; % MFMA/HBM roofline"
 PEAK_MFMA_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE) of this script with --copy-calibration; the
@@ -329,6 +330,43 @@ def decode_bench(torch, M, di, B, T, prefill, steps):
             "kernel_ms_per_step_with_events": ev_ms, "kernels": kernels[:8]}
 
 
+def bf16_bench(torch, gpt2, M, step, first, steps, warmup, B, T):
+    """The same training step with bfloat16 linear-layer products (fp32
+    master weights, gradients, moments and activations): tokens/s and the
+    dominant kernel's rate against the dense bf16 matrix peak."""
+    M.set_matmul_precision(gpt2.GPT2_BF16)
+    for i in range(warmup):
+        step(first + i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        step(first + warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    M.profile_enable(True)
+    for i in range(steps):
+        step(first + warmup + steps + i)
+    prof = M.profile_read()
+    M.profile_enable(False)
+    M.set_matmul_precision(gpt2.GPT2_FP32)
+    by = {}
+    for e in prof:
+        k = e["name"].partition("|")[0]
+        a = by.setdefault(k, dict(name=k, launches=0, ms=0.0, flops=0.0))
+        for f in ("launches", "ms", "flops"):
+            a[f] += e[f]
+    bf = [e for e in by.values() if "bf16" in e["name"]]
+    d = max(bf, key=lambda e: e["ms"])
+    achieved = d["flops"] / d["ms"] * 1e-9
+    return {"tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms, "steps": steps,
+            "bf16_gemm_ms_per_step": sum(e["ms"] for e in bf) / steps,
+            "dominant": {"kernel": d["name"], "launches_per_step": d["launches"] / steps,
+                         "avg_launch_ms": d["ms"] / d["launches"], "achieved_tflops": achieved,
+                         "peak_tflops": PEAK_MFMA_BF16_TFLOPS, "frac": achieved / PEAK_MFMA_BF16_TFLOPS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +378,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--decode-steps", type=int, default=64, help="greedy decode steps timed after the training steps")
     ap.add_argument("--decode-prefill", type=int, default=512)
+    ap.add_argument("--bf16-steps", type=int, default=10, help="steps timed with bfloat16 linear-layer products")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of MIB MiB (for scaling HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -492,6 +531,13 @@ def main():
             log(f"  {k['name']:<34s} {k['launches_per_step']:5.1f}/step {k['ms_per_step']:7.4f} ms/step "
                 f"{k['GBs']:7.0f} GB/s")
 
+    bf16 = None
+    if args.bf16_steps > 0:
+        bf16 = bf16_bench(torch, gpt2, M, step, 2 * args.steps + args.warmup, args.bf16_steps, 2, B, T)
+        log(f"bf16 products: {bf16['tokens_per_s']:.0f} tokens/s ({bf16['ms_per_step']:.2f} ms/step; bf16 GEMMs "
+            f"{bf16['bf16_gemm_ms_per_step']:.2f} ms/step with events; {bf16['dominant']['kernel']} at "
+            f"{bf16['dominant']['achieved_tflops']:.0f} TFLOP/s, {100 * bf16['dominant']['frac']:.1f}% of the bf16 peak)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on a {args.cpu_sample_tokens}-id sample ...")
@@ -525,6 +571,7 @@ def main():
         "ms_per_step_with_events": ms_ev,
         "kernels": kernels[:16],
         "decode": decode,
+        "bf16_products": bf16,
     }
     print(json.dumps(out))
 

@@ -83,6 +83,9 @@ typedef struct {
 
 typedef struct gpt2_model gpt2_model; /* opaque handle */
 
+/* Precision of the linear-layer products (gpt2_set_matmul_precision). */
+enum { GPT2_FP32 = 0, GPT2_BF16 = 1 };
+
 /* Which table gpt2_layout reads. */
 enum { GPT2_PARAMS = 0, GPT2_ACTS = 1 };
 
@@ -196,6 +199,18 @@ gpt2_status gpt2_update(gpt2_model *model, float lr, float beta1, float beta2, f
  * (b, pos) and the work buffer are written, so a following gpt2_backward needs
  * a new forward with targets (GPT2_ESTATE otherwise). */
 gpt2_status gpt2_decode_step(gpt2_model *model, const int32_t *tokens, int pos, const float *coins, int32_t *next);
+
+/* Precision of the linear-layer products of gpt2_forward and gpt2_backward
+ * (the QbitAI llm.c article, "手動實現每個層前向/反向傳播", names fp16 and lower
+ * precision as the trainer's next step).  GPT2_FP32 (the default): fp32
+ * products.  GPT2_BF16: the operands of every linear-layer product -- qkv,
+ * attention projection, MLP and the tied head, forward and backward -- are
+ * rounded to bfloat16 (to nearest even) on their way to the matrix unit and
+ * accumulated in fp32; everything stored stays fp32: parameters (the master
+ * weights), gradients, AdamW moments and activations.  Attention, LayerNorm,
+ * softmax, GELU, bias gradients and AdamW are fp32 in both modes.  Takes
+ * effect for the calls enqueued after it; GPT2_EINVAL for other values. */
+gpt2_status gpt2_set_matmul_precision(gpt2_model *model, int precision);
 
 /* Wait for the stream; GPT2_ERANGE if an out-of-range id was seen since the
  * last report (the flag is then cleared, and gpt2_backward needs a new

@@ -5,8 +5,9 @@
  * gpt2_audit_step lays out the buffers for (cfg, B, T) at stand-in
  * addresses (never dereferenced) and runs gpt2_build, a logits-only
  * gpt2_forward, gpt2_forward with targets, gpt2_zero_grad, gpt2_backward,
- * gpt2_update and three gpt2_decode_step calls (first, middle and last
- * position) with the launch audit on: every launcher declares the element
+ * gpt2_update, three gpt2_decode_step calls (first, middle and last
+ * position) and a forward and backward with bfloat16 products, with the
+ * launch audit on: every launcher declares the element
  * ranges its kernels would read or write (from the kernels' index formulas,
  * grids and leading dimensions) instead of launching, and each range is
  * checked against the named tensors of the layout (the 16 parameter tensors

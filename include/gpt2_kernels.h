@@ -29,11 +29,22 @@ extern "C" {
 gpt2_status gpt2k_linear_forward(float *out, const float *inp, const float *W, const float *bias, int N, int K,
                                  int OC, void *stream);
 
+/* The same with the precision of the products given: GPT2_FP32, or GPT2_BF16
+ * (operands rounded to bfloat16 for the matrix unit, fp32 accumulation; see
+ * gpt2_set_matmul_precision). */
+gpt2_status gpt2k_linear_forward_prec(float *out, const float *inp, const float *W, const float *bias, int N, int K,
+                                      int OC, int precision, void *stream);
+
 /* Linear layer backward: dinp[N][K] = dout W (overwritten; may be NULL to skip),
  * dW[OC][K] += dout^T inp, dbias[OC] += column sums of dout (may be NULL). */
 size_t gpt2k_linear_backward_work(int N, int K, int OC);
 gpt2_status gpt2k_linear_backward(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
                                   const float *W, int N, int K, int OC, float *work, void *stream);
+/* The same with the precision of the two products given (the bias gradient,
+ * a plain column sum of dout, is fp32 in both). */
+gpt2_status gpt2k_linear_backward_prec(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
+                                       const float *W, int N, int K, int OC, float *work, int precision,
+                                       void *stream);
 
 /* LayerNorm over rows of C (mean, biased variance, eps 1e-5, affine). */
 gpt2_status gpt2k_layernorm_forward(float *out, float *mean, float *rstd, const float *inp, const float *w,

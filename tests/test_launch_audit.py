@@ -40,7 +40,7 @@ def test_every_access_stays_inside_its_tensor(g, name):
 SHRINK = {
     "124m": ["work:dres", "work:dqkv", "work:flash_ws", "work:splitk", "work:splitk_dw", "work:ln_partials[24]",
              "work:site_dw_fc[11]", "acts:qkv[0]", "acts:logits", "acts:lse[11]", "grads:wte", "grads:lnfb",
-             "iwork:order", "caller:targets", "work:decode", "iwork:decode_order", "caller:next",
+             "iwork:order", "caller:targets", "work:decode", "iwork:decode_pos", "caller:next",
              "caller:coins"],
     "xl": ["work:flash_ws", "work:dfch", "acts:fch_gelu[47]", "grads:fcprojw[47]"],
     "hd12": ["work:datt", "acts:att[1]"],

@@ -37,13 +37,15 @@ __device__ __forceinline__ void block_sums(float (&v)[RCH], float (*red)[RCH], i
 // lnb) over the K = C columns of each row, computed here (two passes over
 // the row held in registers, biased variance, eps 1e-5), so the LayerNorm
 // needs no launch of its own.  epi: 0 store, 1 add aux[r][o] (residual; out
-// may be aux), 2 GELU.
+// may be aux), 2 GELU.  With pos_ptr, out is first moved by *pos_ptr rows of
+// pos_stride floats (the position being decoded, read on the device).
 template <int NC, int EPI, bool LN>
 __global__ __launch_bounds__(256) void rows_linear_kernel(float *out, long long ldo, const float *x, long long ldx,
                                                           const float *W, const float *bias, const float *aux,
                                                           long long ldaux, const float *lnw, const float *lnb, int R,
-                                                          int K, int OC) {
+                                                          int K, int OC, const int *pos_ptr, long long pos_stride) {
     __shared__ float red[4][RCH];
+    if (pos_ptr) out += (long long)(*pos_ptr) * pos_stride;  // the decoded position's rows
     __shared__ float acc_red[4][NC * RCH];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int o0 = blockIdx.x * NC;
@@ -146,13 +148,15 @@ __global__ __launch_bounds__(256) void rows_linear_kernel(float *out, long long 
 // Thread t works on key t / 4 of the chunk, a quarter of the head dims each.
 constexpr int DKCH = 64;
 
-__global__ __launch_bounds__(256) void decode_attn_partial_kernel(float *ws, const float *qkv, int pos, int T, int C,
-                                                                  int NH, float scale) {
+__global__ __launch_bounds__(256) void decode_attn_partial_kernel(float *ws, const float *qkv, const int *pos_ptr, int T,
+                                                                  int C, int NH, float scale) {
     __shared__ float sc[DKCH];
     __shared__ floatx4 part[256];
     __shared__ float ml[2];
+    const int pos = *pos_ptr;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bh = blockIdx.x, chunk = blockIdx.y, nchunk = gridDim.y;
+    const int bh = blockIdx.x, chunk = blockIdx.y, nchunk = gridDim.y;  // chunks of the whole T
+    if (chunk * DKCH > pos) return;  // past the decoded position: no keys (the whole workgroup)
     const int b = bh / NH, h = bh % NH, hd = C / NH, H4 = hd / 4;
     const int u0 = chunk * DKCH, n = min(DKCH, pos + 1 - u0);
     const long long C3 = 3LL * C;
@@ -204,11 +208,13 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(float *ws, con
 }
 
 // atty[b][h hd + d] = sum_c exp(m_c - M) y_c[d] / sum_c exp(m_c - M) l_c over
-// the chunks c of (b, h) = blockIdx.x, in chunk order.
-__global__ __launch_bounds__(64) void decode_attn_combine_kernel(float *atty, const float *ws, int nchunk, int C,
-                                                                 int NH) {
+// the chunks c <= pos / DKCH of (b, h) = blockIdx.x, in chunk order (nmax
+// partial slots per (b, h)).
+__global__ __launch_bounds__(64) void decode_attn_combine_kernel(float *atty, const float *ws, const int *pos_ptr,
+                                                                 int nmax, int C, int NH) {
     const int bh = blockIdx.x, b = bh / NH, h = bh % NH, hd = C / NH;
-    const float *p = ws + (long long)bh * nchunk * (hd + 4);
+    const int nchunk = *pos_ptr / DKCH + 1;
+    const float *p = ws + (long long)bh * nmax * (hd + 4);
     float M = -INFINITY;
     for (int c = 0; c < nchunk; c++) M = fmaxf(M, p[(long long)c * (hd + 4) + hd]);
     float L = 0.0f;
@@ -227,7 +233,8 @@ __global__ __launch_bounds__(64) void decode_attn_combine_kernel(float *atty, co
 // order; the crossing chunk is walked again; V - 1 if rounding leaves no
 // crossing).  One workgroup of 1024 threads per row.
 __global__ __launch_bounds__(1024) void sample_kernel(int32_t *next, const float *logits, long long ld, int V,
-                                                      const float *coins) {
+                                                      const float *coins, const int *pos_ptr, long long pos_stride) {
+    if (pos_ptr) logits += (long long)(*pos_ptr) * pos_stride;
     __shared__ float sv[1024];
     __shared__ int si[1024];
     __shared__ int best;
@@ -290,11 +297,53 @@ __global__ __launch_bounds__(1024) void sample_kernel(int32_t *next, const float
     if (tid == 0) next[b] = best < V ? best : V - 1;
 }
 
+// x[b][:] = wte[id][:] + wpe[pos][:] for the token id of each sequence b at
+// the decoded position pos = *pos_ptr; an id outside [0, V) is read as the
+// nearest valid one and sets bit 1 of *err.  One workgroup per sequence.
+__global__ __launch_bounds__(256) void decode_embed_kernel(float *x, const int32_t *tokens, const float *wte,
+                                                           const float *wpe, const int *pos_ptr, int32_t *err, int C,
+                                                           int V) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int raw = tokens[b], id = raw < 0 ? 0 : (raw >= V ? V - 1 : raw);
+    if (tid == 0 && (raw < 0 || raw >= V)) atomicOr(err, 1);
+    const floatx4 *we = (const floatx4 *)(wte + (long long)id * C);
+    const floatx4 *pe = (const floatx4 *)(wpe + (long long)(*pos_ptr) * C);
+    for (int c4 = tid; c4 < C / 4; c4 += 256) ((floatx4 *)(x + (long long)b * C))[c4] = we[c4] + pe[c4];
+}
+
+__global__ void set_int_kernel(int *p, int v) { *p = v; }
+
 }  // namespace
+
+hipError_t k_set_int(int *p, int v, hipStream_t s) {
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "set_int_kernel", "p", p, 1, true);
+        return hipSuccess;
+    }
+    hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, s, p, v);
+    return hipGetLastError();
+}
+
+hipError_t k_decode_embed(float *x, const int32_t *tokens, const float *wte, const float *wpe, const int *pos_ptr,
+                          int32_t *err, int B, int C, int V, int T, hipStream_t s) {
+    if (B <= 0 || C % 4 || V <= 0) return hipErrorInvalidValue;
+    if (AuditSink *au = audit_sink()) {
+        audit(au, "decode_embed_kernel", "x", x, (long long)B * C, true);
+        audit(au, "decode_embed_kernel", "tokens", tokens, B, false);
+        audit(au, "decode_embed_kernel", "wte", wte, (long long)V * C, false);
+        audit(au, "decode_embed_kernel", "wpe", wpe, (long long)T * C, false);  // rows pos < T
+        audit(au, "decode_embed_kernel", "pos", pos_ptr, 1, false);
+        audit(au, "decode_embed_kernel", "err", err, 1, true);
+        return hipSuccess;
+    }
+    hipLaunchKernelGGL(decode_embed_kernel, dim3((unsigned)B), dim3(256), 0, s, x, tokens, wte, wpe, pos_ptr, err, C,
+                       V);
+    return hipGetLastError();
+}
 
 hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ldx, const float *W, const float *bias,
                          const float *aux, long long ldaux, const float *lnw, const float *lnb, int R, int K, int OC,
-                         int epi, hipStream_t s) {
+                         int epi, const int *pos_ptr, long long pos_stride, int pos_max, hipStream_t s) {
     if (R <= 0 || K <= 0 || OC <= 0 || K % 4 || ldx % 4 || ((uintptr_t)x & 15) || ((uintptr_t)W & 15))
         return hipErrorInvalidValue;
     if (epi < 0 || epi > 2 || (epi == 1 && !aux)) return hipErrorInvalidValue;
@@ -303,7 +352,9 @@ hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ld
     const int nc = OC >= 2048 ? 4 : 2;
     if (AuditSink *au = audit_sink()) {
         const char *k = k_rows_linear_name(OC);
-        audit(au, k, "out", out, (long long)(R - 1) * ldo + OC, true);
+        // every position pos <= pos_max the launch may be replayed with
+        audit(au, k, "out", out, (long long)(R - 1) * ldo + OC + (pos_ptr ? (long long)pos_max * pos_stride : 0), true);
+        audit(au, k, "pos", pos_ptr, 1, false);
         audit(au, k, "x", x, (long long)(R - 1) * ldx + K, false);
         audit(au, k, "W", W, (long long)OC * K, false);
         audit(au, k, "bias", bias, OC, false);
@@ -315,7 +366,7 @@ hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ld
     dim3 grid((unsigned)((OC + nc - 1) / nc), (unsigned)((R + RCH - 1) / RCH));
 #define RL_LAUNCH(NC, E, L)                                                                                     \
     hipLaunchKernelGGL((rows_linear_kernel<NC, E, L>), grid, dim3(256), 0, s, out, ldo, x, ldx, W, bias, aux, ldaux, \
-                       lnw, lnb, R, K, OC)
+                       lnw, lnb, R, K, OC, pos_ptr, pos_stride)
     if (nc == 4) {
         if (ln) {
             if (epi == 0) RL_LAUNCH(4, 0, true);
@@ -347,38 +398,42 @@ size_t decode_attention_work(int B, int T, int C, int NH) {
     return (size_t)B * NH * ((T + DKCH - 1) / DKCH) * (C / NH + 4);
 }
 
-hipError_t k_decode_attention(float *atty, float *ws, const float *qkv, int pos, int B, int T, int C, int NH,
-                              hipStream_t s) {
-    if (B <= 0 || NH <= 0 || C % NH || (C / NH) % 4 || C / NH > 1024 || T > 1024 || pos < 0 || pos >= T)
+hipError_t k_decode_attention(float *atty, float *ws, const float *qkv, const int *pos_ptr, int B, int T, int C,
+                              int NH, hipStream_t s) {
+    if (B <= 0 || NH <= 0 || C % NH || (C / NH) % 4 || C / NH > 1024 || T > 1024 || T <= 0)
         return hipErrorInvalidValue;
-    const int nchunk = (pos + DKCH) / DKCH, hd = C / NH;
+    const int nmax = (T + DKCH - 1) / DKCH, hd = C / NH;
     if (AuditSink *au = audit_sink()) {
-        // rows b T + u, u <= pos, of each sequence's q | k | v; one partial per (b, h, chunk)
-        const long long C3 = 3LL * C, np = (long long)B * NH * nchunk * (hd + 4);
-        audit(au, "decode_attn_partial_kernel", "qkv", qkv, ((long long)(B - 1) * T + pos) * C3 + C3, false);
+        // rows b T + u, u <= pos < T, of each sequence's q | k | v; nmax partial slots per (b, h)
+        const long long C3 = 3LL * C, np = (long long)B * NH * nmax * (hd + 4);
+        audit(au, "decode_attn_partial_kernel", "qkv", qkv, (long long)B * T * C3, false);
+        audit(au, "decode_attn_partial_kernel", "pos", pos_ptr, 1, false);
         audit(au, "decode_attn_partial_kernel", "ws", ws, np, true);
         audit(au, "decode_attn_combine_kernel", "ws", ws, np, false);
         audit(au, "decode_attn_combine_kernel", "atty", atty, (long long)B * C, true);
         return hipSuccess;
     }
-    hipLaunchKernelGGL(decode_attn_partial_kernel, dim3((unsigned)(B * NH), (unsigned)nchunk), dim3(256), 0, s, ws,
-                       qkv, pos, T, C, NH, 1.0f / sqrtf((float)hd));
+    hipLaunchKernelGGL(decode_attn_partial_kernel, dim3((unsigned)(B * NH), (unsigned)nmax), dim3(256), 0, s, ws, qkv,
+                       pos_ptr, T, C, NH, 1.0f / sqrtf((float)hd));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_attn_combine_kernel, dim3((unsigned)(B * NH)), dim3(64), 0, s, atty, (const float *)ws,
-                       nchunk, C, NH);
+                       pos_ptr, nmax, C, NH);
     return hipGetLastError();
 }
 
 hipError_t k_sample(int32_t *next, const float *logits, long long ld, int B, int V, const float *coins,
-                    hipStream_t s) {
+                    const int *pos_ptr, long long pos_stride, int pos_max, hipStream_t s) {
     if (B <= 0 || V <= 0 || ld < V) return hipErrorInvalidValue;
     if (AuditSink *au = audit_sink()) {
-        audit(au, "sample_kernel", "logits", logits, (long long)(B - 1) * ld + V, false);
+        audit(au, "sample_kernel", "logits", logits,
+              (long long)(B - 1) * ld + V + (pos_ptr ? (long long)pos_max * pos_stride : 0), false);
+        audit(au, "sample_kernel", "pos", pos_ptr, 1, false);
         audit(au, "sample_kernel", "coins", coins, B, false);
         audit(au, "sample_kernel", "next", next, B, true);
         return hipSuccess;
     }
-    hipLaunchKernelGGL(sample_kernel, dim3((unsigned)B), dim3(1024), 0, s, next, logits, ld, V, coins);
+    hipLaunchKernelGGL(sample_kernel, dim3((unsigned)B), dim3(1024), 0, s, next, logits, ld, V, coins, pos_ptr,
+                       pos_stride);
     return hipGetLastError();
 }

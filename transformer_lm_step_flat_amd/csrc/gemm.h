@@ -63,6 +63,10 @@ struct GemmDesc {
     // second kernel.
     float *part = nullptr;
     int tile = 0;  // 0 = choose; 1 = 128x128, 2 = 128x64, 3 = 64x64, 4 = 64x192 (not paired)
+    // 0: fp32 products; 1: operands rounded to bfloat16 (to nearest even) for
+    // the matrix unit, accumulation and everything in memory fp32 (not with
+    // causal modes)
+    int prec = 0;
 };
 
 // Validates the descriptor and enqueues the kernel; returns hipErrorInvalidValue
@@ -78,7 +82,7 @@ hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t 
 // The names a kernel-trace profiler shows for the kernels the two calls
 // above run with descriptor d (static strings).
 const char *gemm_kernel_name(const GemmDesc &d);
-const char *gemm_pair_kernel_name(int tile, bool full);
+const char *gemm_pair_kernel_name(int tile, bool full, int prec);
 // Whether gemm_launch_pair runs the pair (weight gradient dw, input gradient
 // di) with the kernel for whole tiles and whole K slices.
 bool gemm_pair_full(const GemmDesc &dw, const GemmDesc &di, int tile);

@@ -25,6 +25,16 @@ namespace {
 
 constexpr int GEMM_THREADS = 256;
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Two 4-float fragments (8 consecutive k) rounded to bfloat16, to nearest
+// even (v_cvt_pk_bf16_f32), as one operand of v_mfma_f32_32x32x16_bf16.
+__device__ __forceinline__ bf16x8 to_bf16x8(const floatx4 &lo, const floatx4 &hi) {
+    const bf16x8 r = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                      (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+    return r;
+}
+
 // An epilogue mode as a type, so that one epilogue body serves every mode
 template <int V>
 struct EpiTag {
@@ -78,8 +88,11 @@ struct TileLds {
 // index z, operand tiles staged in As / Bs.  kr0 >= 0 replaces the tile's K
 // range by [kr0, kr1).  FULL: the launch guarantees that every tile lies
 // inside M x N and every K range is a whole number of BK slices (no bounds
-// tests anywhere in the K loop).
-template <int BM, int BN, bool AK, bool BKC, int BK, bool FULL = false>
+// tests anywhere in the K loop).  PREC 0: fp32 products
+// (v_mfma_f32_32x32x2_f32); PREC 1: the operands are rounded to bfloat16 as
+// they leave LDS and multiplied with v_mfma_f32_32x32x16_bf16 (fp32
+// accumulation; memory, LDS and epilogue stay fp32).
+template <int BM, int BN, bool AK, bool BKC, int BK, bool FULL = false, int PREC = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int z, float *__restrict__ As,
                                           float *__restrict__ Bs, int kr0 = -1, int kr1 = 0) {
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -193,6 +206,68 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         }
     };
 
+    // The fragment of 4 consecutive k (h * BK / 2 + 4 q ..) of row block i of
+    // A and column block j of B that this lane feeds to the matrix unit.
+    auto frag_a = [&](int i, int q) {
+        const int mm = wm * WM + i * 32 + l32;
+        floatx4 a;
+        if (AK) {
+            a = *(const floatx4 *)&As[mm * KP + h * (BK / 2) + 4 * q];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++) a[e] = As[(h * (BK / 2) + 4 * q + e) * BM + mm];
+        }
+        return a;
+    };
+    auto frag_b = [&](int j, int q) {
+        const int nn = wn * WN + j * 32 + l32;
+        floatx4 b;
+        if (BKC) {
+            b = *(const floatx4 *)&Bs[nn * KP + h * (BK / 2) + 4 * q];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++) b[e] = Bs[(h * (BK / 2) + 4 * q + e) * BN + nn];
+        }
+        return b;
+    };
+    // The MFMAs of the slice in LDS.  fp32: one 32x32x2 per k pair (lane half
+    // h giving one k of the pair); bf16: one 32x32x16 per 8 consecutive k of
+    // each lane half (fragments q and q + 1).
+    auto slice_mfma = [&]() {
+        if constexpr (PREC == 0) {
+#pragma unroll
+            for (int q = 0; q < BK / 8; q++) {
+                floatx4 a[MI], b[NI];
+#pragma unroll
+                for (int i = 0; i < MI; i++) a[i] = frag_a(i, q);
+#pragma unroll
+                for (int j = 0; j < NI; j++) b[j] = frag_b(j, q);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+#pragma unroll
+                    for (int i = 0; i < MI; i++)
+#pragma unroll
+                        for (int j = 0; j < NI; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+            }
+        } else {
+            static_assert(BK % 16 == 0, "bf16 slices take 8 k per lane half");
+#pragma unroll
+            for (int q2 = 0; q2 < BK / 16; q2++) {
+                bf16x8 a[MI], b[NI];
+#pragma unroll
+                for (int i = 0; i < MI; i++) a[i] = to_bf16x8(frag_a(i, 2 * q2), frag_a(i, 2 * q2 + 1));
+#pragma unroll
+                for (int j = 0; j < NI; j++) b[j] = to_bf16x8(frag_b(j, 2 * q2), frag_b(j, 2 * q2 + 1));
+#pragma unroll
+                for (int i = 0; i < MI; i++)
+#pragma unroll
+                    for (int j = 0; j < NI; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
     if constexpr (FULL) {
         // Full-slice loads.  Where GEMM_THREADS is a multiple of the float4s per
         // row of the staged layout (BK / 4 for a K-contiguous operand, BM / 4 or
@@ -239,39 +314,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         };
         // one slice's MFMAs (the wave priority is raised around them, as in
         // the general loop below)
-        auto mfma_slice = [&]() {
-#pragma unroll
-            for (int q = 0; q < BK / 8; q++) {
-                floatx4 a[MI], b[NI];
-#pragma unroll
-                for (int i = 0; i < MI; i++) {
-                    const int mm = wm * WM + i * 32 + l32;
-                    if (AK) {
-                        a[i] = *(const floatx4 *)&As[mm * KP + h * (BK / 2) + 4 * q];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; e++) a[i][e] = As[(h * (BK / 2) + 4 * q + e) * BM + mm];
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < NI; j++) {
-                    const int nn = wn * WN + j * 32 + l32;
-                    if (BKC) {
-                        b[j] = *(const floatx4 *)&Bs[nn * KP + h * (BK / 2) + 4 * q];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; e++) b[j][e] = Bs[(h * (BK / 2) + 4 * q + e) * BN + nn];
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-#pragma unroll
-                    for (int i = 0; i < MI; i++)
-#pragma unroll
-                        for (int j = 0; j < NI; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
-            }
-        };
+        auto mfma_slice = [&]() { slice_mfma(); };
 
         // Every slice is full: a branch-free loop, the last slice peeled off.
         // The next slice's loads are placed one after each of the first
@@ -286,8 +329,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
             __builtin_amdgcn_s_setprio(1);
             gload_full(k0 + BK);
             mfma_slice();
+            constexpr int NMFMA = MI * NI * (PREC == 0 ? BK / 2 : BK / 16);
+            constexpr int NPAIR = NMFMA < A_F4 + B_F4 ? NMFMA : A_F4 + B_F4;
 #pragma unroll
-            for (int i = 0; i < A_F4 + B_F4; i++) {
+            for (int i = 0; i < NPAIR; i++) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
             }
@@ -314,37 +359,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
             // waiting at a barrier (measured: without it the step takes 3 %
             // longer; raising the load phase's priority instead costs 3 to 4 %).
             __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int q = 0; q < BK / 8; q++) {
-                floatx4 a[MI], b[NI];
-#pragma unroll
-                for (int i = 0; i < MI; i++) {
-                    const int mm = wm * WM + i * 32 + l32;
-                    if (AK) {
-                        a[i] = *(const floatx4 *)&As[mm * KP + h * (BK / 2) + 4 * q];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; e++) a[i][e] = As[(h * (BK / 2) + 4 * q + e) * BM + mm];
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < NI; j++) {
-                    const int nn = wn * WN + j * 32 + l32;
-                    if (BKC) {
-                        b[j] = *(const floatx4 *)&Bs[nn * KP + h * (BK / 2) + 4 * q];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; e++) b[j][e] = Bs[(h * (BK / 2) + 4 * q + e) * BN + nn];
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-#pragma unroll
-                    for (int i = 0; i < MI; i++)
-#pragma unroll
-                        for (int j = 0; j < NI; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
-            }
+            slice_mfma();
             __builtin_amdgcn_s_setprio(0);
         }
     }
@@ -435,6 +450,17 @@ __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_kernel(GemmArgs p) {
     gemm_tile<BM, BN, AK, BKC, BK, FULL>(p, tm, tn, blockIdx.z, As, Bs);
 }
 
+// The same with bfloat16 products (PREC 1 of gemm_tile).
+template <int BM, int BN, bool AK, bool BKC, int BK, int LB, bool FULL>
+__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_bf16_kernel(GemmArgs p) {
+    using L = TileLds<BM, BN, AK, BKC, BK>;
+    __shared__ __attribute__((aligned(16))) float As[L::A];
+    __shared__ __attribute__((aligned(16))) float Bs[L::B];
+    int tm, tn;
+    group_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    gemm_tile<BM, BN, AK, BKC, BK, FULL, 1>(p, tm, tn, blockIdx.z, As, Bs);
+}
+
 // Causal products whose K range grows (KEND) or shrinks (KSTART) with the row
 // tile: a workgroup takes row tiles i and tiles_m - 1 - i of one column, whose
 // K ranges add up to the same length for every workgroup.
@@ -503,8 +529,8 @@ __global__ __launch_bounds__(256) void fold_split_sum_kernel(float *C, long long
 // use the same tile shape.  Each XCD gets an eighth of each problem, as one
 // contiguous run of problem 1 followed by one of problem 2, so that the work
 // per XCD is balanced and operand tiles are shared within an XCD's L2.
-template <int BM, int BN, int BK, int LB, bool AK1, bool BKC1, bool AK2, bool BKC2, bool FULL>
-__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int w1, int w) {
+template <int BM, int BN, int BK, bool AK1, bool BKC1, bool AK2, bool BKC2, bool FULL, int PREC>
+__device__ __forceinline__ void pair_body(const GemmArgs &p1, const GemmArgs &p2, int w1, int w) {
     using L1 = TileLds<BM, BN, AK1, BKC1, BK>;
     using L2 = TileLds<BM, BN, AK2, BKC2, BK>;
     __shared__ __attribute__((aligned(16))) float As[L1::A > L2::A ? L1::A : L2::A];
@@ -518,14 +544,25 @@ __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_pair_kernel(GemmArgs p1
         const int g = s1 + j, nt = p1.tiles_m * p1.tiles_n;
         int tm, tn;
         group_order(g % nt, p1.tiles_m, p1.tiles_n, p1.group_m, tm, tn);
-        gemm_tile<BM, BN, AK1, BKC1, BK, FULL>(p1, tm, tn, g / nt, As, Bs);
+        gemm_tile<BM, BN, AK1, BKC1, BK, FULL, PREC>(p1, tm, tn, g / nt, As, Bs);
     } else {
         const int s2 = x * (w / X) + min(x, w % X) - s1;  // workgroups of XCDs before x, less problem 1's
         const int g = s2 + j - r1, nt = p2.tiles_m * p2.tiles_n;
         int tm, tn;
         group_order(g % nt, p2.tiles_m, p2.tiles_n, p2.group_m, tm, tn);
-        gemm_tile<BM, BN, AK2, BKC2, BK, FULL>(p2, tm, tn, g / nt, As, Bs);
+        gemm_tile<BM, BN, AK2, BKC2, BK, FULL, PREC>(p2, tm, tn, g / nt, As, Bs);
     }
+}
+
+template <int BM, int BN, int BK, int LB, bool AK1, bool BKC1, bool AK2, bool BKC2, bool FULL>
+__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int w1, int w) {
+    pair_body<BM, BN, BK, AK1, BKC1, AK2, BKC2, FULL, 0>(p1, p2, w1, w);
+}
+
+// The same with bfloat16 products.
+template <int BM, int BN, int BK, int LB, bool AK1, bool BKC1, bool AK2, bool BKC2, bool FULL>
+__global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_pair_bf16_kernel(GemmArgs p1, GemmArgs p2, int w1, int w) {
+    pair_body<BM, BN, BK, AK1, BKC1, AK2, BKC2, FULL, 1>(p1, p2, w1, w);
 }
 
 // Tile grid and the K range of each split (a whole number of BK slices).
@@ -546,11 +583,20 @@ bool gemm_full(const GemmDesc &d, int bm, int bn, int bk) {
 }
 
 template <int BM, int BN, bool AKV, bool BKV, int BK, int LB>
-void launch_gemm_kernel(bool full, dim3 grid, hipStream_t stream, const GemmArgs &a) {
-    if (full)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, AKV, BKV, BK, LB, true>), grid, dim3(GEMM_THREADS), 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, AKV, BKV, BK, LB, false>), grid, dim3(GEMM_THREADS), 0, stream, a);
+void launch_gemm_kernel(bool full, int prec, dim3 grid, hipStream_t stream, const GemmArgs &a) {
+    if (prec == 0) {
+        if (full)
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, AKV, BKV, BK, LB, true>), grid, dim3(GEMM_THREADS), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, AKV, BKV, BK, LB, false>), grid, dim3(GEMM_THREADS), 0, stream, a);
+    } else {
+        if (full)
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AKV, BKV, BK, LB, true>), grid, dim3(GEMM_THREADS), 0, stream,
+                               a);
+        else
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AKV, BKV, BK, LB, false>), grid, dim3(GEMM_THREADS), 0, stream,
+                               a);
+    }
 }
 
 template <int BM, int BN, int BK, int LB>
@@ -593,11 +639,11 @@ hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream
     dim3 grid(a.tiles_m * a.tiles_n, 1, (unsigned)nb);
     const bool full = gemm_full(d, BM, BN, BK);
     if (d.a_kcontig && d.b_kcontig)
-        launch_gemm_kernel<BM, BN, true, true, BK, LB>(full, grid, stream, a);
+        launch_gemm_kernel<BM, BN, true, true, BK, LB>(full, d.prec, grid, stream, a);
     else if (d.a_kcontig && !d.b_kcontig)
-        launch_gemm_kernel<BM, BN, true, false, BK, LB>(full, grid, stream, a);
+        launch_gemm_kernel<BM, BN, true, false, BK, LB>(full, d.prec, grid, stream, a);
     else if (!d.a_kcontig && !d.b_kcontig)
-        launch_gemm_kernel<BM, BN, false, false, BK, LB>(full, grid, stream, a);
+        launch_gemm_kernel<BM, BN, false, false, BK, LB>(full, d.prec, grid, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -622,12 +668,23 @@ hipError_t launch_pair(const GemmDesc &d1, const GemmArgs &a1_, const GemmDesc &
     if (w1 + w2 > (1LL << 30)) return hipErrorInvalidValue;
     // the one instantiation used: a weight gradient (both MN-contiguous) beside an input gradient
     if (d1.a_kcontig || d1.b_kcontig || !d2.a_kcontig || d2.b_kcontig) return hipErrorInvalidValue;
-    if (pair_full_shape<BM, BN>() && gemm_full(d1, BM, BN, BK) && gemm_full(d2, BM, BN, BK))
-        hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false, true>),
-                           dim3((unsigned)(w1 + w2)), dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
-    else
-        hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false, false>),
-                           dim3((unsigned)(w1 + w2)), dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+    const bool full = pair_full_shape<BM, BN>() && gemm_full(d1, BM, BN, BK) && gemm_full(d2, BM, BN, BK);
+    const dim3 grid((unsigned)(w1 + w2));
+    if (d1.prec == 0) {
+        if (full)
+            hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false, true>), grid,
+                               dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+        else
+            hipLaunchKernelGGL((gemm_pair_kernel<BM, BN, BK, LB, false, false, true, false, false>), grid,
+                               dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+    } else {
+        if (full)
+            hipLaunchKernelGGL((gemm_pair_bf16_kernel<BM, BN, BK, LB, false, false, true, false, true>), grid,
+                               dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+        else
+            hipLaunchKernelGGL((gemm_pair_bf16_kernel<BM, BN, BK, LB, false, false, true, false, false>), grid,
+                               dim3(GEMM_THREADS), 0, stream, a1, a2, (int)w1, (int)(w1 + w2));
+    }
     return hipGetLastError();
 }
 
@@ -637,6 +694,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 hipError_t make_args(const GemmDesc &d, GemmArgs &a) {
     if (d.M <= 0 || d.N <= 0 || d.K < 0 || !d.A || !d.B || !d.C) return hipErrorInvalidValue;
     if (d.ksplit < 1 || d.nbo < 1 || d.nbi < 1) return hipErrorInvalidValue;
+    if (d.prec < 0 || d.prec > 1 || (d.prec == 1 && (d.causal != CAUSAL_NONE || d.part))) return hipErrorInvalidValue;
     if (d.ksplit > 1 && d.epi != EPI_STORE) return hipErrorInvalidValue;
     // 16-byte vector loads: contiguous extents, leading dims and strides in multiples of 4
     // a K-contiguous operand is read 4 k at a time; an MN-contiguous one row by row
@@ -727,9 +785,9 @@ hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t 
     hipError_t e = make_args(d1, a1);
     if (e == hipSuccess) e = make_args(d2, a2);
     if (e != hipSuccess) return e;
-    if (d1.tile != d2.tile || d1.causal || d2.causal) return hipErrorInvalidValue;
+    if (d1.tile != d2.tile || d1.causal || d2.causal || d1.prec != d2.prec) return hipErrorInvalidValue;
     if (AuditSink *au = audit_sink()) {
-        const char *k = gemm_pair_kernel_name(d1.tile, gemm_pair_full(d1, d2, d1.tile));
+        const char *k = gemm_pair_kernel_name(d1.tile, gemm_pair_full(d1, d2, d1.tile), d1.prec);
         audit_gemm(au, k, d1);
         audit_gemm(au, k, d2);
         return hipSuccess;
@@ -743,7 +801,15 @@ hipError_t gemm_launch_pair(const GemmDesc &d1, const GemmDesc &d2, hipStream_t 
 }
 
 // Keep in step with the instantiations chosen in gemm_launch and gemm_launch_pair.
-const char *gemm_pair_kernel_name(int tile, bool full) {
+const char *gemm_pair_kernel_name(int tile, bool full, int prec) {
+    static const char *bf16_names[3][2] = {
+        {"gemm_pair_bf16_kernel<128, 128, 32, 3, false, false, true, false, false>",
+         "gemm_pair_bf16_kernel<128, 128, 32, 3, false, false, true, false, true>"},
+        {"gemm_pair_bf16_kernel<128, 64, 32, 3, false, false, true, false, false>",
+         "gemm_pair_bf16_kernel<128, 64, 32, 3, false, false, true, false, true>"},
+        {"gemm_pair_bf16_kernel<64, 64, 32, 3, false, false, true, false, false>",
+         "gemm_pair_bf16_kernel<64, 64, 32, 3, false, false, true, false, true>"}};
+    if (prec) return bf16_names[tile >= 1 && tile <= 3 ? tile - 1 : 0][full ? 1 : 0];
     static const char *names[3][2] = {
         {"gemm_pair_kernel<128, 128, 32, 3, false, false, true, false, false>",
          "gemm_pair_kernel<128, 128, 32, 3, false, false, true, false, true>"},
@@ -788,6 +854,22 @@ const char *gemm_kernel_name(const GemmDesc &d) {
                                          "gemm_fold_split_kernel<128, 64, true, false, 32, 3>",
                                          "gemm_fold_split_kernel<64, 64, true, false, 32, 3>",
                                          "gemm_fold_split_kernel<64, 192, true, false, 32, 3>"};
+    static const char *bf16_names[4][3][2] = {
+        {{"gemm_bf16_kernel<128, 128, true, true, 32, 3, false>", "gemm_bf16_kernel<128, 128, true, true, 32, 3, true>"},
+         {"gemm_bf16_kernel<128, 128, true, false, 32, 3, false>", "gemm_bf16_kernel<128, 128, true, false, 32, 3, true>"},
+         {"gemm_bf16_kernel<128, 128, false, false, 32, 3, false>",
+          "gemm_bf16_kernel<128, 128, false, false, 32, 3, true>"}},
+        {{"gemm_bf16_kernel<128, 64, true, true, 32, 3, false>", "gemm_bf16_kernel<128, 64, true, true, 32, 3, true>"},
+         {"gemm_bf16_kernel<128, 64, true, false, 32, 3, false>", "gemm_bf16_kernel<128, 64, true, false, 32, 3, true>"},
+         {"gemm_bf16_kernel<128, 64, false, false, 32, 3, false>", "gemm_bf16_kernel<128, 64, false, false, 32, 3, true>"}},
+        {{"gemm_bf16_kernel<64, 64, true, true, 32, 3, false>", "gemm_bf16_kernel<64, 64, true, true, 32, 3, true>"},
+         {"gemm_bf16_kernel<64, 64, true, false, 32, 3, false>", "gemm_bf16_kernel<64, 64, true, false, 32, 3, true>"},
+         {"gemm_bf16_kernel<64, 64, false, false, 32, 3, false>", "gemm_bf16_kernel<64, 64, false, false, 32, 3, true>"}},
+        {{"gemm_bf16_kernel<64, 192, true, true, 32, 3, false>", "gemm_bf16_kernel<64, 192, true, true, 32, 3, true>"},
+         {"gemm_bf16_kernel<64, 192, true, false, 32, 3, false>", "gemm_bf16_kernel<64, 192, true, false, 32, 3, true>"},
+         {"gemm_bf16_kernel<64, 192, false, false, 32, 3, false>",
+          "gemm_bf16_kernel<64, 192, false, false, 32, 3, true>"}}};
+    if (d.prec) return bf16_names[t][l][gemm_full(d, bm[t], bn[t], 32) ? 1 : 0];
     // causal products with a growing or shrinking K range run with folded row tiles
     if (d.part && d.causal == CAUSAL_KEND && d.M > bm[t] && l == 1) return split_names[t];
     if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];

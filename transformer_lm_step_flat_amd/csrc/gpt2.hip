@@ -386,8 +386,8 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.i_tok = 0;
     l.i_order = align_up(BT);
     l.i_err = l.i_order + align_up(BT);
-    l.i_dec = l.i_err + ALIGN;  // the decoding step's token order (unused beyond the id check)
-    l.niwork = l.i_dec + align_up((size_t)B);
+    l.i_dec = l.i_err + ALIGN;  // the position a decoding step works on (read on the device)
+    l.niwork = l.i_dec + ALIGN;
 }
 
 // When a model's profiler is on, each launch of the step is bracketed by two
@@ -412,7 +412,18 @@ struct gpt2_model {
     Layout lo;
     gpt2_buffers buf;
     hipStream_t stream;
+    int mm_prec = GPT2_FP32;  // precision of the linear-layer products
     bool have_targets = false;
+    // captured decoding steps, one per (tokens, coins, next) of the caller
+    struct DecodeGraph {
+        const int32_t *tokens;
+        const float *coins;
+        int32_t *next;
+        hipGraphExec_t exec;
+    };
+    std::vector<DecodeGraph> decode_graphs;
+    hipStream_t capture_stream = nullptr;
+    bool graphs_ok = true;
     std::string err;
     Profiler prof;
 };
@@ -476,6 +487,15 @@ struct Site {
     ~Site() { g_site = saved; }
 };
 
+// Precision of the linear-layer products being launched (GPT2_FP32 or
+// GPT2_BF16); attention products are always fp32.
+thread_local int g_prec = GPT2_FP32;
+struct PrecScope {
+    int saved;
+    explicit PrecScope(int prec) : saved(g_prec) { g_prec = prec; }
+    ~PrecScope() { g_prec = saved; }
+};
+
 // Makes a model's profiler the active one for the duration of an API call.
 struct ProfScope {
     Profiler *saved;
@@ -534,6 +554,7 @@ hipError_t linear_fwd(float *out, const float *inp, const float *W, const float 
     d.A = inp; d.lda = K; d.B = W; d.ldb = K; d.C = out; d.ldc = OC;
     d.epi = epi; d.bias = bias; d.aux = aux; d.ldaux = OC; d.C2 = out2;
     d.tile = plan_gemm(N, OC, K, 1, false).tile;
+    d.prec = g_prec;
     return gemm_run(d, s);
 }
 
@@ -555,6 +576,7 @@ GemmDesc dinp_desc(float *dinp, const float *dout, const float *W, int N, int K,
     d.A = dout; d.lda = OC; d.B = W; d.ldb = K; d.C = dinp; d.ldc = K;
     d.epi = epi; d.aux = aux; d.ldaux = K;
     d.tile = p.tile;
+    d.prec = g_prec;
     if (p.ksplit > 1) { d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)N * K; }
     return d;
 }
@@ -566,6 +588,7 @@ GemmDesc dw_desc(float *dW, float *dbias, const float *dout, const float *inp, i
     d.M = OC; d.N = K; d.K = N;
     d.A = dout; d.lda = OC; d.B = inp; d.ldb = K; d.C = dW; d.ldc = K;
     d.tile = p.tile;
+    d.prec = g_prec;
     if (p.ksplit > 1) {
         d.epi = EPI_STORE; d.C = splitk; d.ksplit = p.ksplit; d.sCs = (long long)OC * K;
         d.colsum = dbias ? dbias_ws : nullptr;
@@ -632,7 +655,7 @@ hipError_t linear_bwd(float *dinp, int epi, const float *aux, float *dW, float *
     double f1, b1, f2, b2;
     gemm_cost(dd, f1, b1);
     gemm_cost(di, f2, b2);
-    hipError_t e = timed(gemm_pair_kernel_name(pp.tile, gemm_pair_full(dd, di, pp.tile)), f1 + f2, b1 + b2,
+    hipError_t e = timed(gemm_pair_kernel_name(pp.tile, gemm_pair_full(dd, di, pp.tile), dd.prec), f1 + f2, b1 + b2,
                          [&]() { return gemm_launch_pair(dd, di, s); });
     if (e == hipSuccess && !defer_dw_sum) e = dw_finish(dW, dbias, splitk_dw, dbias_ws, K, OC, pp.ks_dw, s);
     if (e == hipSuccess) e = dinp_finish(dinp, splitk_dinp, N, K, pp.ks_dinp, s);
@@ -821,6 +844,7 @@ gpt2_status gpt2_build(const gpt2_config *cfg, int B, int T, const gpt2_buffers 
 gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *targets, float *mean_loss) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
     ProfScope prof_scope(m);
+    PrecScope prec_scope(m->mm_prec);
     if (!inputs) return fail(m, GPT2_EINVAL, "inputs is NULL");
     if (mean_loss && !targets) return fail(m, GPT2_EINVAL, "mean_loss needs targets");
     const Layout &l = m->lo;
@@ -922,6 +946,7 @@ gpt2_status gpt2_zero_grad(gpt2_model *m) {
 gpt2_status gpt2_backward(gpt2_model *m) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
     ProfScope prof_scope(m);
+    PrecScope prec_scope(m->mm_prec);
     if (!m->have_targets) return fail(m, GPT2_ESTATE, "gpt2_backward needs a preceding gpt2_forward with targets");
     const Layout &l = m->lo;
     const int B = l.B, T = l.T, C = l.C, NH = l.NH, BT = (int)l.BT;
@@ -1038,48 +1063,108 @@ gpt2_status gpt2_update(gpt2_model *m, float lr, float beta1, float beta2, float
     return GPT2_OK;
 }
 
+namespace {
+
+// The launches of one decoding step on stream s, for the position in the
+// model's device int (set before, by gpt2_decode_step).
+gpt2_status decode_launches(gpt2_model *m, hipStream_t s, const int32_t *tokens, const float *coins, int32_t *next) {
+    const Layout &l = m->lo;
+    const int B = l.B, T = l.T, C = l.C, NH = l.NH;
+    const size_t BTC = (size_t)l.BT * C, c = C;
+    float *P = m->buf.params, *A = m->buf.acts;
+    float *x = m->buf.work + l.w_dec, *att = x + (size_t)B * C, *h = att + (size_t)B * C;
+    float *aws = h + (size_t)4 * B * C;
+    int32_t *err = m->buf.iwork + l.i_err;
+    const int *dpos = m->buf.iwork + l.i_dec;
+    const double w = 4.0 * B;  // bytes per float of one row per sequence
+    KRUN(m, "decode_embed_kernel", 3.0 * w * C, k_decode_embed(x, tokens, P + l.poff[0], P + l.poff[1], dpos, err, B, C, l.V, T, s));
+    for (int li = 0; li < l.L; li++) {
+        float *qkv = A + l.aoff[A_QKV] + li * 3 * BTC;  // this layer's cache: rows (b, u) of q | k | v
+        // the new rows' q | k | v from LayerNorm(x) (computed inside), at row (b, pos)
+        KRUNF(m, k_rows_linear_name(3 * C), 2.0 * B * C * 3 * C, 4.0 * 3 * C * C + w * 4 * C,
+              k_rows_linear(qkv, (long long)T * 3 * C, x, C, P + l.poff[4] + li * 3 * c * c, P + l.poff[5] + li * 3 * c,
+                            nullptr, 0, P + l.poff[2] + li * c, P + l.poff[3] + li * c, B, C, 3 * C, 0, dpos, 3 * C,
+                            T - 1, s));
+        KRUN(m, "decode_attn_partial_kernel", w * C * 2 * T,
+             k_decode_attention(att, aws, qkv, dpos, B, T, C, NH, s));
+        KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * C, 4.0 * C * C + 3 * w * C,
+              k_rows_linear(x, C, att, C, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, x, C, nullptr, nullptr, B,
+                            C, C, 1, nullptr, 0, 0, s));
+        KRUNF(m, k_rows_linear_name(4 * C), 2.0 * B * C * 4 * C, 4.0 * 4 * C * C + w * 5 * C,
+              k_rows_linear(h, 4 * C, x, C, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, nullptr, 0,
+                            P + l.poff[8] + li * c, P + l.poff[9] + li * c, B, C, 4 * C, 2, nullptr, 0, 0, s));
+        KRUNF(m, k_rows_linear_name(C), 2.0 * B * 4 * C * C, 4.0 * 4 * C * C + w * 6 * C,
+              k_rows_linear(x, C, h, 4 * C, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, x, C, nullptr,
+                            nullptr, B, 4 * C, C, 1, nullptr, 0, 0, s));
+    }
+    float *logits = A + l.aoff[A_LOGITS];  // row (b, pos) at (b T + pos) Vp
+    KRUNF(m, k_rows_linear_name(l.Vp), 2.0 * B * C * l.Vp, 4.0 * (double)l.Vp * C + w * (C + l.Vp),
+          k_rows_linear(logits, (long long)T * l.Vp, x, C, P + l.poff[0], nullptr, nullptr, 0, P + l.poff[14],
+                        P + l.poff[15], B, C, l.Vp, 0, dpos, l.Vp, T - 1, s));
+    KRUN(m, "sample_kernel", w * l.V, k_sample(next, logits, (long long)T * l.Vp, B, l.V, coins, dpos, l.Vp, T - 1, s));
+    return GPT2_OK;
+}
+
+// The decoding step for (tokens, coins, next) captured into a graph on a
+// stream of the model's own (the launches only record device pointers, and
+// the position is read from the device), or null if capture failed.
+hipGraphExec_t decode_graph(gpt2_model *m, const int32_t *tokens, const float *coins, int32_t *next) {
+    for (const auto &g : m->decode_graphs)
+        if (g.tokens == tokens && g.coins == coins && g.next == next) return g.exec;
+    if (!m->graphs_ok) return nullptr;
+    if (m->decode_graphs.size() >= 8) {  // a few argument sets are in use at a time
+        for (auto &g : m->decode_graphs) (void)hipGraphExecDestroy(g.exec);
+        m->decode_graphs.clear();
+    }
+    if (!m->capture_stream && hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking) != hipSuccess) {
+        m->capture_stream = nullptr;
+        m->graphs_ok = false;
+        return nullptr;
+    }
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    bool ok = hipStreamBeginCapture(m->capture_stream, hipStreamCaptureModeThreadLocal) == hipSuccess;
+    if (ok) {
+        const gpt2_status st = decode_launches(m, m->capture_stream, tokens, coins, next);
+        ok = hipStreamEndCapture(m->capture_stream, &graph) == hipSuccess && st == GPT2_OK && graph;
+    }
+    if (ok) ok = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
+    if (graph) (void)hipGraphDestroy(graph);
+    if (!ok) {
+        (void)hipGetLastError();
+        m->graphs_ok = false;  // direct launches from now on
+        return nullptr;
+    }
+    m->decode_graphs.push_back({tokens, coins, next, exec});
+    return exec;
+}
+
+}  // namespace
+
 gpt2_status gpt2_decode_step(gpt2_model *m, const int32_t *tokens, int pos, const float *coins, int32_t *next) {
     if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
     ProfScope prof_scope(m);
     if (!tokens || !next) return fail(m, GPT2_EINVAL, "tokens and next are required");
     const Layout &l = m->lo;
     if (pos < 0 || pos >= l.T) return fail(m, GPT2_EINVAL, "pos must be in [0, T)");
-    const int B = l.B, T = l.T, C = l.C, NH = l.NH;
-    const size_t BTC = (size_t)l.BT * C, c = C;
     hipStream_t s = m->stream;
-    float *P = m->buf.params, *A = m->buf.acts;
-    float *x = m->buf.work + l.w_dec, *att = x + (size_t)B * C, *h = att + (size_t)B * C;
-    float *aws = h + (size_t)4 * B * C;
-    int32_t *err = m->buf.iwork + l.i_err;
     m->have_targets = false;  // rows of the saved activations are overwritten
-    const double w = 4.0 * B;  // bytes per float of one row per sequence
-    const double nkeys = pos + 1.0;
-    KRUN(m, "token_prep_kernel", 12.0 * B, k_token_prep(tokens, nullptr, m->buf.iwork + l.i_dec, err, B, l.V, s));
-    KRUN(m, "encoder_forward_kernel", 3.0 * w * C, k_encoder_forward(x, tokens, P + l.poff[0], P + l.poff[1] + (size_t)pos * C, B, 1, C, l.V, s));
-    for (int li = 0; li < l.L; li++) {
-        float *qkv = A + l.aoff[A_QKV] + li * 3 * BTC;  // this layer's cache: rows (b, u) of q | k | v
-        // qkv of the new rows from LayerNorm(x) (fused)
-        KRUNF(m, k_rows_linear_name(3 * C), 2.0 * B * C * 3 * C, 4.0 * 3 * C * C + w * 4 * C,
-              k_rows_linear(qkv + (size_t)pos * 3 * C, (long long)T * 3 * C, x, C, P + l.poff[4] + li * 3 * c * c,
-                            P + l.poff[5] + li * 3 * c, nullptr, 0, P + l.poff[2] + li * c, P + l.poff[3] + li * c, B, C,
-                            3 * C, 0, s));
-        KRUNF(m, "decode_attn_partial_kernel", 4.0 * B * C * nkeys, w * C * 2 * nkeys + 2 * w * C,
-              k_decode_attention(att, aws, qkv, pos, B, T, C, NH, s));
-        KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * C, 4.0 * C * C + 3 * w * C,
-              k_rows_linear(x, C, att, C, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, x, C, nullptr, nullptr, B,
-                            C, C, 1, s));
-        KRUNF(m, k_rows_linear_name(4 * C), 2.0 * B * C * 4 * C, 4.0 * 4 * C * C + w * 5 * C,
-              k_rows_linear(h, 4 * C, x, C, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, nullptr, 0,
-                            P + l.poff[8] + li * c, P + l.poff[9] + li * c, B, C, 4 * C, 2, s));
-        KRUNF(m, k_rows_linear_name(C), 2.0 * B * 4 * C * C, 4.0 * 4 * C * C + w * 6 * C,
-              k_rows_linear(x, C, h, 4 * C, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, x, C, nullptr,
-                            nullptr, B, 4 * C, C, 1, s));
+    // the position, for every kernel of the step (its own launch, so that a
+    // captured step serves every position)
+    KRUN(m, "set_int_kernel", 4.0, k_set_int(m->buf.iwork + l.i_dec, pos, s));
+    if (!m->prof.on && !audit_sink()) {
+        if (hipGraphExec_t exec = decode_graph(m, tokens, coins, next)) {
+            HIPCK(m, hipGraphLaunch(exec, s));
+            return GPT2_OK;
+        }
     }
-    float *logits = A + l.aoff[A_LOGITS] + (size_t)pos * l.Vp;  // row (b, pos) at b T Vp
-    KRUNF(m, k_rows_linear_name(l.Vp), 2.0 * B * C * l.Vp, 4.0 * (double)l.Vp * C + w * (C + l.Vp),
-          k_rows_linear(logits, (long long)T * l.Vp, x, C, P + l.poff[0], nullptr, nullptr, 0, P + l.poff[14],
-                        P + l.poff[15], B, C, l.Vp, 0, s));
-    KRUN(m, "sample_kernel", w * l.V, k_sample(next, logits, (long long)T * l.Vp, B, l.V, coins, s));
+    return decode_launches(m, s, tokens, coins, next);
+}
+
+gpt2_status gpt2_set_matmul_precision(gpt2_model *m, int precision) {
+    if (!m) return fail(nullptr, GPT2_EINVAL, "model is NULL");
+    if (precision != GPT2_FP32 && precision != GPT2_BF16) return fail(m, GPT2_EINVAL, "unknown precision");
+    m->mm_prec = precision;
     return GPT2_OK;
 }
 
@@ -1202,6 +1287,8 @@ gpt2_status gpt2_profile_read(gpt2_model *m, gpt2_profile_entry *out, int max_en
 
 void gpt2_free(gpt2_model *m) {
     if (!m) return;
+    for (auto &g : m->decode_graphs) (void)hipGraphExecDestroy(g.exec);
+    if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
     for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
     delete m;
 }
@@ -1219,6 +1306,13 @@ const char *gpt2_last_error(const gpt2_model *m) { return m ? m->err.c_str() : g
 
 gpt2_status gpt2k_linear_forward(float *out, const float *inp, const float *W, const float *bias, int N, int K,
                                  int OC, void *stream) {
+    return gpt2k_linear_forward_prec(out, inp, W, bias, N, K, OC, GPT2_FP32, stream);
+}
+
+gpt2_status gpt2k_linear_forward_prec(float *out, const float *inp, const float *W, const float *bias, int N, int K,
+                                      int OC, int precision, void *stream) {
+    if (precision != GPT2_FP32 && precision != GPT2_BF16) return fail(nullptr, GPT2_EINVAL, "unknown precision");
+    PrecScope prec_scope(precision);
     KCK(linear_fwd(out, inp, W, bias, N, K, OC, EPI_STORE, nullptr, nullptr, (hipStream_t)stream));
     return GPT2_OK;
 }
@@ -1231,6 +1325,14 @@ size_t gpt2k_linear_backward_work(int N, int K, int OC) {
 
 gpt2_status gpt2k_linear_backward(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
                                   const float *W, int N, int K, int OC, float *work, void *stream) {
+    return gpt2k_linear_backward_prec(dinp, dW, dbias, dout, inp, W, N, K, OC, work, GPT2_FP32, stream);
+}
+
+gpt2_status gpt2k_linear_backward_prec(float *dinp, float *dW, float *dbias, const float *dout, const float *inp,
+                                       const float *W, int N, int K, int OC, float *work, int precision,
+                                       void *stream) {
+    if (precision != GPT2_FP32 && precision != GPT2_BF16) return fail(nullptr, GPT2_EINVAL, "unknown precision");
+    PrecScope prec_scope(precision);
     hipStream_t s = (hipStream_t)stream;
     size_t a = 0, b = 0;
     bwd_split_need(N, K, OC, true, a, b);
@@ -1453,7 +1555,7 @@ gpt2_status gpt2_audit_step(const gpt2_config *cfg, int B, int T, const char *sh
     ck.add(base(6), l.i_tok, (size_t)l.BT, 1, "iwork:ids");
     ck.add(base(6), l.i_order, (size_t)l.BT, 1, "iwork:order");
     ck.add(base(6), l.i_err, 1, 1, "iwork:err");
-    ck.add(base(6), l.i_dec, (size_t)l.B, 1, "iwork:decode_order");
+    ck.add(base(6), l.i_dec, 1, 1, "iwork:decode_pos");
     ck.add(base(7), 0, (size_t)l.BT, 1, "caller:inputs");
     ck.add(base(8), 0, (size_t)l.BT, 1, "caller:targets");
     ck.add(base(9), 0, (size_t)l.B, 1, "caller:decode_tokens");
@@ -1480,6 +1582,10 @@ gpt2_status gpt2_audit_step(const gpt2_config *cfg, int B, int T, const char *sh
     int32_t *dnext = (int32_t *)base(11);
     for (int pos : {0, T / 2, T - 1})
         if (st == GPT2_OK) st = gpt2_decode_step(m, dtok, pos, pos == 0 ? nullptr : coins, dnext);
+    // and a step with bfloat16 products
+    if (st == GPT2_OK) st = gpt2_set_matmul_precision(m, GPT2_BF16);
+    if (st == GPT2_OK) st = gpt2_forward(m, inp, tgt, nullptr);
+    if (st == GPT2_OK) st = gpt2_backward(m);
     set_audit_sink(nullptr);
     const std::string err = m ? m->err : g_last_error;
     gpt2_free(m);

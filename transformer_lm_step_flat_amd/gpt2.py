@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ERANGE, GPT2_ESTATE, GPT2_EDEVICE, GPT2_EIO = 0, -1, -2, -3, -4, -5
 GPT2_PARAMS, GPT2_ACTS = 0, 1
+GPT2_FP32, GPT2_BF16 = 0, 1
 _STATUS = {0: "GPT2_OK", -1: "GPT2_EINVAL", -2: "GPT2_ERANGE", -3: "GPT2_ESTATE", -4: "GPT2_EDEVICE",
            -5: "GPT2_EIO"}
 
@@ -67,6 +68,7 @@ _SIGS = {
     "gpt2_backward": [_P],
     "gpt2_update": [_P, _F, _F, _F, _F, _F, _I],
     "gpt2_sync": [_P],
+    "gpt2_set_matmul_precision": [_P, _I],
     "gpt2_decode_step": [_P, _P, _I, _P, _P],
     "gpt2_save_checkpoint": [_P, ctypes.c_char_p, _I],
     "gpt2_audit_step": [ctypes.POINTER(Config), _I, _I, ctypes.c_char_p, _Z, ctypes.c_char_p, _Z,
@@ -76,6 +78,8 @@ _SIGS = {
     "gpt2_profile_read": [_P, ctypes.POINTER(ProfileEntry), _I, ctypes.POINTER(_I)],
     "gpt2k_linear_forward": [_P, _P, _P, _P, _I, _I, _I, _P],
     "gpt2k_linear_backward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
+    "gpt2k_linear_forward_prec": [_P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "gpt2k_linear_backward_prec": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P],
     "gpt2k_layernorm_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _P],
     "gpt2k_layernorm_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
     "gpt2k_layernorm_backward_noalloc": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -278,6 +282,10 @@ class Model:
     def sync(self):
         _check(lib().gpt2_sync(self._h), self._h)
 
+    def set_matmul_precision(self, precision: int):
+        """GPT2_FP32 or GPT2_BF16 for the linear-layer products of later calls."""
+        _check(lib().gpt2_set_matmul_precision(self._h, precision), self._h)
+
     # --- evaluation and decoding
     def eval_loss(self, batches) -> float:
         """Mean of the mean losses of (inputs, targets) device batches: forward
@@ -342,17 +350,17 @@ def _need(**tensors):
             raise ValueError(f"{name} holds {t.numel()} elements, the call touches {n}")
 
 
-def linear_forward(out, inp, W, bias, N, K, OC):
+def linear_forward(out, inp, W, bias, N, K, OC, precision=GPT2_FP32):
     _need(out=(out, N * OC), inp=(inp, N * K), W=(W, OC * K), bias=(bias, OC))
-    _check(lib().gpt2k_linear_forward(_ptr(out), _ptr(inp), _ptr(W), _ptr(bias), N, K, OC, _s()))
+    _check(lib().gpt2k_linear_forward_prec(_ptr(out), _ptr(inp), _ptr(W), _ptr(bias), N, K, OC, precision, _s()))
 
 
-def linear_backward(dinp, dW, dbias, dout, inp, W, N, K, OC):
+def linear_backward(dinp, dW, dbias, dout, inp, W, N, K, OC, precision=GPT2_FP32):
     _need(dinp=(dinp, N * K), dW=(dW, OC * K), dbias=(dbias, OC), dout=(dout, N * OC), inp=(inp, N * K),
           W=(W, OC * K))
     work = torch.empty(max(1, lib().gpt2k_linear_backward_work(N, K, OC)), dtype=torch.float32, device=dout.device)
-    _check(lib().gpt2k_linear_backward(_ptr(dinp), _ptr(dW), _ptr(dbias), _ptr(dout), _ptr(inp), _ptr(W), N, K,
-                                       OC, _ptr(work), _s()))
+    _check(lib().gpt2k_linear_backward_prec(_ptr(dinp), _ptr(dW), _ptr(dbias), _ptr(dout), _ptr(inp), _ptr(W), N,
+                                            K, OC, _ptr(work), precision, _s()))
     return work
 
 
