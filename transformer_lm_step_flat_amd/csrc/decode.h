@@ -6,15 +6,16 @@
 
 // out[r][o] = epi(xin[r] . W[o] + bias[o]) for r < R, o < OC; x rows ldx
 // apart (K floats used), out rows ldo apart, W [OC][K] (out x in).  xin = x,
-// or LayerNorm(x) with gains lnw and shifts lnb [K] when lnw is non-null
-// (K <= 2048).  epi 0: store; 1: + aux[r][o] (aux rows ldaux apart; out may
-// equal aux; not with LayerNorm); 2: GELU.
+// or LayerNorm(x) with gains lnw and shifts lnb [K] when lnw is non-null.
+// epi 0: store; 1: + aux[r][o] (aux rows ldaux apart; out may equal aux; not
+// with LayerNorm); 2: GELU.  x, W, lnw and lnb 16-byte aligned, K and ldx
+// multiples of 4.
 // With pos_ptr (device int, may be NULL) out is first moved by *pos_ptr rows
 // of pos_stride floats; pos_max bounds *pos_ptr (for the launch audit).
 hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ldx, const float *W, const float *bias,
                          const float *aux, long long ldaux, const float *lnw, const float *lnb, int R, int K, int OC,
                          int epi, const int *pos_ptr, long long pos_stride, int pos_max, hipStream_t s);
-const char *k_rows_linear_name(int OC);
+const char *k_rows_linear_name(int K);  // the variant k_rows_linear runs for this K
 
 // atty[b][:] = causal attention of query row (b, pos) over key/value rows
 // (b, u <= pos) of qkv [B][T][3C] (q | k | v, heads of C / NH), pos =

@@ -11,133 +11,155 @@
 
 namespace {
 
-constexpr int RCH = 8;  // rows per workgroup of the row products
-constexpr int KPT = 2;  // float4s per thread of a LayerNorm-ed row (C <= 2048)
+constexpr int RR = 4;  // rows of the row products per wave (grid.y covers the rest)
+constexpr int NO = 4;  // outputs per wave
+constexpr int JC = 4;  // float4s per lane per pass over K (a pass covers 1024 columns)
 
-// Sum of v over the 256 threads of a workgroup for RCH values at once;
-// red is [4][RCH] of LDS.  Fixed order: wavefront sums, then wave 0..3.
-__device__ __forceinline__ void block_sums(float (&v)[RCH], float (*red)[RCH], int nr) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int r = 0; r < RCH; r++)
-        if (r < nr) {
-            const float t = wave_sum(v[r]);
-            if (lane == 0) red[wave][r] = t;
-        }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RCH; r++) v[r] = (red[0][r] + red[1][r]) + (red[2][r] + red[3][r]);
-    __syncthreads();
+__device__ __forceinline__ float dot4(const floatx4 &a, const floatx4 &b) {
+    return (a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3]);
 }
 
 // out[r][o] = epi(xin[r] . W[o] + bias[o]) for the R rows (R small) and all
-// OC outputs; a workgroup owns NC consecutive outputs and its 256 threads
-// stride over K four floats at a time, so the whole weight matrix is read
-// once per launch with 16-byte loads.  LN: xin = LayerNorm(x) with (lnw,
-// lnb) over the K = C columns of each row, computed here (two passes over
-// the row held in registers, biased variance, eps 1e-5), so the LayerNorm
-// needs no launch of its own.  epi: 0 store, 1 add aux[r][o] (residual; out
-// may be aux), 2 GELU.  With pos_ptr, out is first moved by *pos_ptr rows of
-// pos_stride floats (the position being decoded, read on the device).
-template <int NC, int EPI, bool LN>
-__global__ __launch_bounds__(256) void rows_linear_kernel(float *out, long long ldo, const float *x, long long ldx,
-                                                          const float *W, const float *bias, const float *aux,
-                                                          long long ldaux, const float *lnw, const float *lnb, int R,
-                                                          int K, int OC, const int *pos_ptr, long long pos_stride) {
-    __shared__ float red[4][RCH];
+// OC outputs.  Each wave owns NO consecutive outputs and RR rows and keeps
+// their dot products in registers: its lanes stride over K four floats at a
+// time (16-byte loads; the weight matrix is read once per launch for each
+// RR rows), and a wave reduction ends each dot product.  WS = 1: a workgroup
+// is one wave doing all of K (K <= 1024).  WS = 4: the workgroup's four
+// waves share the outputs and take a quarter of K each; their sums are added
+// in wave order through LDS.  Every load a wave needs (weights, rows,
+// LayerNorm gains, bias and residual) is issued before the arithmetic that
+// waits on any of them.
+// LN: xin = LayerNorm(x) with (lnw, lnb) over the K = C columns of each row,
+// computed by each wave for its own rows (two passes, biased variance, eps
+// 1e-5), so the LayerNorm needs no launch of its own.  epi: 0 store, 1 add
+// aux[r][o] (residual; out may be aux), 2 GELU.  With pos_ptr, out is first
+// moved by *pos_ptr rows of pos_stride floats (the position being decoded,
+// read on the device).
+template <int EPI, bool LN, int WS>
+__global__ __launch_bounds__(64 * WS, 2) void rows_linear_kernel(float *out, long long ldo, const float *x, long long ldx,
+                                                             const float *W, const float *bias, const float *aux,
+                                                             long long ldaux, const float *lnw, const float *lnb, int R,
+                                                             int K, int OC, const int *pos_ptr, long long pos_stride) {
+    __shared__ float red[WS][NO * RR];
     if (pos_ptr) out += (long long)(*pos_ptr) * pos_stride;  // the decoded position's rows
-    __shared__ float acc_red[4][NC * RCH];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int o0 = blockIdx.x * NC;
-    const int r0 = blockIdx.y * RCH, nr = min(RCH, R - r0);
-    const int K4 = K / 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int o0 = blockIdx.x * NO, r0 = blockIdx.y * RR, nr = min(RR, R - r0);
+    const int K4 = K >> 2, KS = (K4 + WS - 1) / WS;
+    const int ks = wave * KS, ke = min(K4, ks + KS);
     const floatx4 *W4 = (const floatx4 *)W;
     const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-    float acc[NC][RCH];
-#pragma unroll
-    for (int c = 0; c < NC; c++)
-#pragma unroll
-        for (int r = 0; r < RCH; r++) acc[c][r] = 0.0f;
-    if constexpr (LN) {
-        floatx4 xr[RCH][KPT];
-        float sm[RCH];
-#pragma unroll
-        for (int r = 0; r < RCH; r++) {
-            sm[r] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < KPT; j++) {
-                const int k4 = tid + 256 * j;
-                xr[r][j] = (r < nr && k4 < K4) ? *(const floatx4 *)(x + (long long)(r0 + r) * ldx + 4 * k4) : z4;
-                sm[r] += (xr[r][j][0] + xr[r][j][1]) + (xr[r][j][2] + xr[r][j][3]);
-            }
-        }
-        block_sums(sm, red, nr);
-        float mean[RCH], var[RCH];
-#pragma unroll
-        for (int r = 0; r < RCH; r++) {
-            mean[r] = sm[r] / K;
-            var[r] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < KPT; j++)
-                if (tid + 256 * j < K4) {
-                    const floatx4 d = xr[r][j] - mean[r];
-                    var[r] += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
-                }
-        }
-        block_sums(var, red, nr);
-#pragma unroll
-        for (int j = 0; j < KPT; j++) {
-            const int k4 = tid + 256 * j;
-            if (k4 < K4) {
-                const floatx4 g = ((const floatx4 *)lnw)[k4], bb = ((const floatx4 *)lnb)[k4];
-                floatx4 w[NC];
-#pragma unroll
-                for (int c = 0; c < NC; c++) w[c] = o0 + c < OC ? W4[(long long)(o0 + c) * K4 + k4] : z4;
-#pragma unroll
-                for (int r = 0; r < RCH; r++) {
-                    const float rs = 1.0f / sqrtf(var[r] / K + 1e-5f);
-                    const floatx4 xv = (xr[r][j] - mean[r]) * rs * g + bb;
-#pragma unroll
-                    for (int c = 0; c < NC; c++)
-                        acc[c][r] += (w[c][0] * xv[0] + w[c][1] * xv[1]) + (w[c][2] * xv[2] + w[c][3] * xv[3]);
-                }
-            }
-        }
-    } else {
-        for (int k4 = tid; k4 < K4; k4 += 256) {
-            floatx4 w[NC];
-#pragma unroll
-            for (int c = 0; c < NC; c++) w[c] = o0 + c < OC ? W4[(long long)(o0 + c) * K4 + k4] : z4;
-#pragma unroll
-            for (int r = 0; r < RCH; r++) {
-                if (r < nr) {
-                    const floatx4 xv = *(const floatx4 *)(x + (long long)(r0 + r) * ldx + 4 * k4);
-#pragma unroll
-                    for (int c = 0; c < NC; c++)
-                        acc[c][r] += (w[c][0] * xv[0] + w[c][1] * xv[1]) + (w[c][2] * xv[2] + w[c][3] * xv[3]);
-                }
-            }
-        }
+    // lane i < NO RR of wave 0 finishes output o0 + i / RR of row r0 + i % RR
+    const int eo = o0 + lane / RR, er = lane % RR;
+    const bool ep = wave == 0 && lane < NO * RR && eo < OC && er < nr;
+    float eb = 0.0f, ea = 0.0f;
+    if (ep) {
+        if (bias) eb = bias[eo];
+        if (EPI == 1) ea = aux[(long long)(r0 + er) * ldaux + eo];
     }
+    floatx4 w[JC][NO], xv[JC][RR], g[JC], bb[JC];
+    auto load = [&](int kb) {
 #pragma unroll
-    for (int c = 0; c < NC; c++)
+        for (int j = 0; j < JC; j++) {
+            const int k4 = kb + lane + 64 * j;
+            const bool ok = k4 < ke;
 #pragma unroll
-        for (int r = 0; r < RCH; r++)
-            if (r < nr) {
-                const float t = wave_sum(acc[c][r]);
-                if (lane == 0) acc_red[wave][c * RCH + r] = t;
+            for (int c = 0; c < NO; c++) w[j][c] = ok && o0 + c < OC ? W4[(long long)(o0 + c) * K4 + k4] : z4;
+#pragma unroll
+            for (int r = 0; r < RR; r++)
+                xv[j][r] = ok && r < nr ? *(const floatx4 *)(x + (long long)(r0 + r) * ldx + 4 * k4) : z4;
+            if constexpr (LN) {
+                g[j] = ok ? ((const floatx4 *)lnw)[k4] : z4;
+                bb[j] = ok ? ((const floatx4 *)lnb)[k4] : z4;
             }
-    __syncthreads();
-    if (tid < NC * RCH) {
-        const int c = tid / RCH, r = tid % RCH, o = o0 + c;
-        if (r < nr && o < OC) {
-            const long long rr = r0 + r;
-            float y = (acc_red[0][tid] + acc_red[1][tid]) + (acc_red[2][tid] + acc_red[3][tid]);
-            y += bias ? bias[o] : 0.0f;
-            if (EPI == 1) y += aux[rr * ldaux + o];
-            if (EPI == 2) y = gelu_fwd(y);
-            out[rr * ldo + o] = y;
         }
+    };
+    load(ks);
+    float mean[RR], rs[RR];
+    if constexpr (LN) {
+        // WS = 1: the registers hold the whole rows; WS = 4: each wave reads
+        // the whole rows for the statistics (cache hits after the first)
+        float s[RR], v[RR];
+#pragma unroll
+        for (int r = 0; r < RR; r++) s[r] = v[r] = 0.0f;
+        if constexpr (WS == 1) {
+#pragma unroll
+            for (int j = 0; j < JC; j++)
+#pragma unroll
+                for (int r = 0; r < RR; r++) s[r] += (xv[j][r][0] + xv[j][r][1]) + (xv[j][r][2] + xv[j][r][3]);
+        } else {
+            for (int k4 = lane; k4 < K4; k4 += 64)
+#pragma unroll
+                for (int r = 0; r < RR; r++)
+                    if (r < nr) {
+                        const floatx4 t = *(const floatx4 *)(x + (long long)(r0 + r) * ldx + 4 * k4);
+                        s[r] += (t[0] + t[1]) + (t[2] + t[3]);
+                    }
+        }
+#pragma unroll
+        for (int r = 0; r < RR; r++) mean[r] = wave_sum(s[r]) / K;
+        if constexpr (WS == 1) {
+#pragma unroll
+            for (int j = 0; j < JC; j++)
+                if (lane + 64 * j < K4)
+#pragma unroll
+                    for (int r = 0; r < RR; r++) {
+                        const floatx4 d = xv[j][r] - mean[r];
+                        v[r] += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+                    }
+        } else {
+            for (int k4 = lane; k4 < K4; k4 += 64)
+#pragma unroll
+                for (int r = 0; r < RR; r++)
+                    if (r < nr) {
+                        const floatx4 d = *(const floatx4 *)(x + (long long)(r0 + r) * ldx + 4 * k4) - mean[r];
+                        v[r] += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+                    }
+        }
+#pragma unroll
+        for (int r = 0; r < RR; r++) rs[r] = 1.0f / sqrtf(wave_sum(v[r]) / K + 1e-5f);
+    }
+    float acc[NO][RR];
+#pragma unroll
+    for (int c = 0; c < NO; c++)
+#pragma unroll
+        for (int r = 0; r < RR; r++) acc[c][r] = 0.0f;
+    for (int kb = ks; kb < ke; kb += 64 * JC) {
+        if (kb != ks) load(kb);
+        if constexpr (LN) {
+#pragma unroll
+            for (int j = 0; j < JC; j++)
+#pragma unroll
+                for (int r = 0; r < RR; r++) xv[j][r] = (xv[j][r] - mean[r]) * rs[r] * g[j] + bb[j];
+        }
+        // columns past the end have zero weights, so their products vanish
+#pragma unroll
+        for (int j = 0; j < JC; j++)
+#pragma unroll
+            for (int r = 0; r < RR; r++)
+#pragma unroll
+                for (int c = 0; c < NO; c++) acc[c][r] += dot4(w[j][c], xv[j][r]);
+    }
+    float y = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NO; c++)
+#pragma unroll
+        for (int r = 0; r < RR; r++) {
+            const float t = wave_sum(acc[c][r]);
+            if (lane == c * RR + r) y = t;
+        }
+    if constexpr (WS > 1) {
+        if (lane < NO * RR) red[wave][lane] = y;
+        __syncthreads();
+        if (wave != 0 || lane >= NO * RR) return;
+        y = red[0][lane];
+#pragma unroll
+        for (int q = 1; q < WS; q++) y += red[q][lane];
+    }
+    if (ep) {
+        y += eb;
+        if (EPI == 1) y += ea;
+        if (EPI == 2) y = gelu_fwd(y);
+        out[(long long)(r0 + er) * ldo + eo] = y;
     }
 }
 
@@ -145,8 +167,10 @@ __global__ __launch_bounds__(256) void rows_linear_kernel(float *out, long long 
 // of one chunk of DKCH positions (blockIdx.y): scores, their max m, the
 // exponentials' sum l and the weighted sum y of the chunk's values, written
 // as a partial [y (hd) | m | l] at stride hd + 4 for the combine kernel.
-// Thread t works on key t / 4 of the chunk, a quarter of the head dims each.
+// Thread t scores key t / 4 of the chunk over a quarter of the head dims;
+// the value rows are loaded together with the keys.
 constexpr int DKCH = 64;
+constexpr int VPRE = 4;  // value rows per thread loaded ahead (all of them when hd <= 64)
 
 __global__ __launch_bounds__(256) void decode_attn_partial_kernel(float *ws, const float *qkv, const int *pos_ptr, int T,
                                                                   int C, int NH, float scale) {
@@ -162,15 +186,21 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(float *ws, con
     const long long C3 = 3LL * C;
     const float *rows = qkv + (long long)b * T * C3 + (long long)h * hd;
     const floatx4 *q4 = (const floatx4 *)(rows + (long long)pos * C3);
+    const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // thread (g, d4) sums keys g, g + ng, ... of the chunk at dims 4 d4 .. 4 d4 + 3
+    const int ng = 256 / H4, g = tid / H4, d4 = tid % H4;
+    floatx4 vr[VPRE];
+#pragma unroll
+    for (int i = 0; i < VPRE; i++) {
+        const int j = g + ng * i;
+        vr[i] = g < ng && j < n ? ((const floatx4 *)(rows + (long long)(u0 + j) * C3 + 2 * C))[d4] : z4;
+    }
     {
         const int j = tid >> 2, qq = tid & 3;
         float s = 0.0f;
         if (j < n) {
             const floatx4 *k4 = (const floatx4 *)(rows + (long long)(u0 + j) * C3 + C);
-            for (int d = qq; d < H4; d += 4) {
-                const floatx4 a = q4[d], k = k4[d];
-                s += (a[0] * k[0] + a[1] * k[1]) + (a[2] * k[2] + a[3] * k[3]);
-            }
+            for (int d = qq; d < H4; d += 4) s += dot4(q4[d], k4[d]);
         }
         s += dpp_move<0xB1>(s);  // the four quarters of the key's dot product
         s += dpp_move<0x4E>(s);
@@ -189,10 +219,16 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(float *ws, con
         }
     }
     __syncthreads();
-    const int ng = 256 / H4, g = tid / H4, d4 = tid % H4;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (g < ng)
-        for (int j = g; j < n; j += ng) acc += sc[j] * ((const floatx4 *)(rows + (long long)(u0 + j) * C3 + 2 * C))[d4];
+    floatx4 acc = z4;
+    if (g < ng) {
+#pragma unroll
+        for (int i = 0; i < VPRE; i++) {
+            const int j = g + ng * i;
+            if (j < n) acc += sc[j] * vr[i];
+        }
+        for (int j = g + ng * VPRE; j < n; j += ng)
+            acc += sc[j] * ((const floatx4 *)(rows + (long long)(u0 + j) * C3 + 2 * C))[d4];
+    }
     part[tid] = acc;
     __syncthreads();
     float *dst = ws + ((long long)bh * nchunk + chunk) * (hd + 4);
@@ -209,19 +245,25 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(float *ws, con
 
 // atty[b][h hd + d] = sum_c exp(m_c - M) y_c[d] / sum_c exp(m_c - M) l_c over
 // the chunks c <= pos / DKCH of (b, h) = blockIdx.x, in chunk order (nmax
-// partial slots per (b, h)).
+// partial slots per (b, h)).  The chunks' m and l are read once, all at a
+// time, into LDS.
 __global__ __launch_bounds__(64) void decode_attn_combine_kernel(float *atty, const float *ws, const int *pos_ptr,
                                                                  int nmax, int C, int NH) {
-    const int bh = blockIdx.x, b = bh / NH, h = bh % NH, hd = C / NH;
-    const int nchunk = *pos_ptr / DKCH + 1;
+    __shared__ float sw[64];
+    const int bh = blockIdx.x, b = bh / NH, h = bh % NH, hd = C / NH, lane = threadIdx.x;
+    const int nchunk = *pos_ptr / DKCH + 1;  // <= nmax <= 16
     const float *p = ws + (long long)bh * nmax * (hd + 4);
-    float M = -INFINITY;
-    for (int c = 0; c < nchunk; c++) M = fmaxf(M, p[(long long)c * (hd + 4) + hd]);
+    const float mc = lane < nchunk ? p[(long long)lane * (hd + 4) + hd] : -INFINITY;
+    const float lc = lane < nchunk ? p[(long long)lane * (hd + 4) + hd + 1] : 0.0f;
+    const float M = wave_max(mc);
+    const float e = lane < nchunk ? __expf(mc - M) : 0.0f;
+    sw[lane] = e;
     float L = 0.0f;
-    for (int c = 0; c < nchunk; c++) L += __expf(p[(long long)c * (hd + 4) + hd] - M) * p[(long long)c * (hd + 4) + hd + 1];
-    for (int d = threadIdx.x; d < hd; d += 64) {
+    for (int c = 0; c < nchunk; c++) L += __shfl(e, c) * __shfl(lc, c);
+    __syncthreads();
+    for (int d = lane; d < hd; d += 64) {
         float y = 0.0f;
-        for (int c = 0; c < nchunk; c++) y += __expf(p[(long long)c * (hd + 4) + hd] - M) * p[(long long)c * (hd + 4) + d];
+        for (int c = 0; c < nchunk; c++) y += sw[c] * p[(long long)c * (hd + 4) + d];
         atty[(long long)b * C + (long long)h * hd + d] = y / L;
     }
 }
@@ -241,35 +283,75 @@ __global__ __launch_bounds__(1024) void sample_kernel(int32_t *next, const float
     const int b = blockIdx.x, tid = threadIdx.x;
     const float *z = logits + (long long)b * ld;
     const int chunk = (V + 1023) / 1024, c0 = min(tid * chunk, V), c1 = min(c0 + chunk, V);
-    // max and its lowest index: coalesced strided reads, then (value, index)
-    // pairs reduced over the block
+    // max and its lowest index: each thread visits its indices in increasing
+    // order (16-byte loads, four in flight, when the row is aligned), then
+    // (value, index) pairs are reduced over the wavefront and the 16 waves
     float m = -INFINITY;
     int mi = V;
-    for (int v = tid; v < V; v += 1024)
+    int vs = 0;  // first index left to the scalar loop
+    if (((uintptr_t)z & 15) == 0) {
+        const int V4 = V / 4;
+        const floatx4 *z4 = (const floatx4 *)z;
+        for (int v4 = tid; v4 < V4; v4 += 4096) {
+            floatx4 t[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int i = v4 + 1024 * u;
+                t[u] = i < V4 ? z4[i] : (floatx4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    if (t[u][e] > m) {
+                        m = t[u][e];
+                        mi = 4 * (v4 + 1024 * u) + e;
+                    }
+        }
+        vs = 4 * V4;
+    }
+    for (int v = vs + tid; v < V; v += 1024)
         if (z[v] > m) {
             m = z[v];
             mi = v;
         }
-    sv[tid] = m;
-    si[tid] = mi;
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(m, off);
+        const int oi = __shfl_xor(mi, off);
+        if (ov > m || (ov == m && oi < mi)) {
+            m = ov;
+            mi = oi;
+        }
+    }
+    if ((tid & 63) == 0) {
+        sv[tid >> 6] = m;
+        si[tid >> 6] = mi;
+    }
     __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
-        if (tid < s) {
-            const int o = tid + s;
-            if (sv[o] > sv[tid] || (sv[o] == sv[tid] && si[o] < si[tid])) {
-                sv[tid] = sv[o];
-                si[tid] = si[o];
+    if (tid < 64) {
+        m = tid < 16 ? sv[tid] : -INFINITY;
+        mi = tid < 16 ? si[tid] : V;
+        for (int off = 8; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(m, off);
+            const int oi = __shfl_xor(mi, off);
+            if (ov > m || (ov == m && oi < mi)) {
+                m = ov;
+                mi = oi;
             }
         }
-        __syncthreads();
+        if (tid == 0) {
+            best = mi < V ? mi : 0;  // a row with no finite maximum gives id 0
+            sv[1023] = m;
+        }
     }
-    const float zmax = sv[0];
-    const int amax = si[0];
+    __syncthreads();
+    const float zmax = sv[1023];
+    const int amax = best;
     if (!coins) {
         if (tid == 0) next[b] = amax;
         return;
     }
-    __syncthreads();  // every thread has read sv[0] and si[0]
+    __syncthreads();  // every thread has read the maximum from sv[1023]
     float cs = 0.0f;
     for (int v = c0; v < c1; v++) cs += __expf(z[v] - zmax);
     sv[tid] = cs;
@@ -348,10 +430,10 @@ hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ld
         return hipErrorInvalidValue;
     if (epi < 0 || epi > 2 || (epi == 1 && !aux)) return hipErrorInvalidValue;
     const bool ln = lnw != nullptr;
-    if (ln && (!lnb || K > 4 * 256 * KPT)) return hipErrorInvalidValue;
-    const int nc = OC >= 2048 ? 4 : 2;
+    if (ln && (!lnb || epi == 1 || ((uintptr_t)lnw & 15) || ((uintptr_t)lnb & 15))) return hipErrorInvalidValue;
+    const bool split = K > 1024;  // four waves per output group, a quarter of K each
     if (AuditSink *au = audit_sink()) {
-        const char *k = k_rows_linear_name(OC);
+        const char *k = k_rows_linear_name(K);
         // every position pos <= pos_max the launch may be replayed with
         audit(au, k, "out", out, (long long)(R - 1) * ldo + OC + (pos_ptr ? (long long)pos_max * pos_stride : 0), true);
         audit(au, k, "pos", pos_ptr, 1, false);
@@ -363,36 +445,34 @@ hipError_t k_rows_linear(float *out, long long ldo, const float *x, long long ld
         audit(au, k, "lnb", lnb, ln ? K : 0, false);
         return hipSuccess;
     }
-    dim3 grid((unsigned)((OC + nc - 1) / nc), (unsigned)((R + RCH - 1) / RCH));
-#define RL_LAUNCH(NC, E, L)                                                                                     \
-    hipLaunchKernelGGL((rows_linear_kernel<NC, E, L>), grid, dim3(256), 0, s, out, ldo, x, ldx, W, bias, aux, ldaux, \
-                       lnw, lnb, R, K, OC, pos_ptr, pos_stride)
-    if (nc == 4) {
+    const dim3 grid((unsigned)((OC + NO - 1) / NO), (unsigned)((R + RR - 1) / RR));
+#define RL_LAUNCH(E, L, WS)                                                                                        \
+    hipLaunchKernelGGL((rows_linear_kernel<E, L, WS>), grid, dim3(64 * WS), 0, s, out, ldo, x, ldx, W, bias, aux, \
+                       ldaux, lnw, lnb, R, K, OC, pos_ptr, pos_stride)
+    if (split) {
         if (ln) {
-            if (epi == 0) RL_LAUNCH(4, 0, true);
-            else if (epi == 2) RL_LAUNCH(4, 2, true);
-            else return hipErrorInvalidValue;
+            if (epi == 0) RL_LAUNCH(0, true, 4);
+            else RL_LAUNCH(2, true, 4);
         } else {
-            if (epi == 0) RL_LAUNCH(4, 0, false);
-            else if (epi == 1) RL_LAUNCH(4, 1, false);
-            else RL_LAUNCH(4, 2, false);
+            if (epi == 0) RL_LAUNCH(0, false, 4);
+            else if (epi == 1) RL_LAUNCH(1, false, 4);
+            else RL_LAUNCH(2, false, 4);
         }
     } else {
         if (ln) {
-            if (epi == 0) RL_LAUNCH(2, 0, true);
-            else if (epi == 2) RL_LAUNCH(2, 2, true);
-            else return hipErrorInvalidValue;
+            if (epi == 0) RL_LAUNCH(0, true, 1);
+            else RL_LAUNCH(2, true, 1);
         } else {
-            if (epi == 0) RL_LAUNCH(2, 0, false);
-            else if (epi == 1) RL_LAUNCH(2, 1, false);
-            else RL_LAUNCH(2, 2, false);
+            if (epi == 0) RL_LAUNCH(0, false, 1);
+            else if (epi == 1) RL_LAUNCH(1, false, 1);
+            else RL_LAUNCH(2, false, 1);
         }
     }
 #undef RL_LAUNCH
     return hipGetLastError();
 }
 
-const char *k_rows_linear_name(int OC) { return OC >= 2048 ? "rows_linear_kernel<4>" : "rows_linear_kernel<2>"; }
+const char *k_rows_linear_name(int K) { return K > 1024 ? "rows_linear_kernel<4>" : "rows_linear_kernel<1>"; }
 
 size_t decode_attention_work(int B, int T, int C, int NH) {
     return (size_t)B * NH * ((T + DKCH - 1) / DKCH) * (C / NH + 4);

@@ -1081,7 +1081,7 @@ gpt2_status decode_launches(gpt2_model *m, hipStream_t s, const int32_t *tokens,
     for (int li = 0; li < l.L; li++) {
         float *qkv = A + l.aoff[A_QKV] + li * 3 * BTC;  // this layer's cache: rows (b, u) of q | k | v
         // the new rows' q | k | v from LayerNorm(x) (computed inside), at row (b, pos)
-        KRUNF(m, k_rows_linear_name(3 * C), 2.0 * B * C * 3 * C, 4.0 * 3 * C * C + w * 4 * C,
+        KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * 3 * C, 4.0 * 3 * C * C + w * 4 * C,
               k_rows_linear(qkv, (long long)T * 3 * C, x, C, P + l.poff[4] + li * 3 * c * c, P + l.poff[5] + li * 3 * c,
                             nullptr, 0, P + l.poff[2] + li * c, P + l.poff[3] + li * c, B, C, 3 * C, 0, dpos, 3 * C,
                             T - 1, s));
@@ -1090,15 +1090,15 @@ gpt2_status decode_launches(gpt2_model *m, hipStream_t s, const int32_t *tokens,
         KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * C, 4.0 * C * C + 3 * w * C,
               k_rows_linear(x, C, att, C, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, x, C, nullptr, nullptr, B,
                             C, C, 1, nullptr, 0, 0, s));
-        KRUNF(m, k_rows_linear_name(4 * C), 2.0 * B * C * 4 * C, 4.0 * 4 * C * C + w * 5 * C,
+        KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * 4 * C, 4.0 * 4 * C * C + w * 5 * C,
               k_rows_linear(h, 4 * C, x, C, P + l.poff[10] + li * 4 * c * c, P + l.poff[11] + li * 4 * c, nullptr, 0,
                             P + l.poff[8] + li * c, P + l.poff[9] + li * c, B, C, 4 * C, 2, nullptr, 0, 0, s));
-        KRUNF(m, k_rows_linear_name(C), 2.0 * B * 4 * C * C, 4.0 * 4 * C * C + w * 6 * C,
+        KRUNF(m, k_rows_linear_name(4 * C), 2.0 * B * 4 * C * C, 4.0 * 4 * C * C + w * 6 * C,
               k_rows_linear(x, C, h, 4 * C, P + l.poff[12] + li * 4 * c * c, P + l.poff[13] + li * c, x, C, nullptr,
                             nullptr, B, 4 * C, C, 1, nullptr, 0, 0, s));
     }
     float *logits = A + l.aoff[A_LOGITS];  // row (b, pos) at (b T + pos) Vp
-    KRUNF(m, k_rows_linear_name(l.Vp), 2.0 * B * C * l.Vp, 4.0 * (double)l.Vp * C + w * (C + l.Vp),
+    KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * l.Vp, 4.0 * (double)l.Vp * C + w * (C + l.Vp),
           k_rows_linear(logits, (long long)T * l.Vp, x, C, P + l.poff[0], nullptr, nullptr, 0, P + l.poff[14],
                         P + l.poff[15], B, C, l.Vp, 0, dpos, l.Vp, T - 1, s));
     KRUN(m, "sample_kernel", w * l.V, k_sample(next, logits, (long long)T * l.Vp, B, l.V, coins, dpos, l.Vp, T - 1, s));
