@@ -96,12 +96,16 @@ gpt2_status gpt2k_crossentropy(float *logits, float *losses, float *loss, const 
 
 /* Encoder: out[B][T][C] = wte[ids] + wpe[t].  Backward: dwte[id] += rows of
  * dout with that id, dwpe[t] += sum over b.  The backward needs the position
- * order computed by gpt2k_token_order (iwork of BT int32s + 1 flag) and
- * gpt2k_encoder_backward_work floats of `work` (segment sums). */
+ * order computed by gpt2k_token_order (order: BT int32s, the positions
+ * sorted by (id, position); err_flag |= 1 for an id, 2 for a target outside
+ * [0, V); work: gpt2k_token_order_work(BT) int32s, 8-byte aligned, may be
+ * NULL when that is 0) and gpt2k_encoder_backward_work floats of `work`
+ * (segment sums). */
 gpt2_status gpt2k_encoder_forward(float *out, const int32_t *ids, const float *wte, const float *wpe, int B, int T,
                                   int C, int V, void *stream);
+size_t gpt2k_token_order_work(int BT);
 gpt2_status gpt2k_token_order(int32_t *order, int32_t *err_flag, const int32_t *ids, const int32_t *targets,
-                              int BT, int V, void *stream);
+                              int BT, int V, int32_t *work, void *stream);
 size_t gpt2k_encoder_backward_work(int B, int T, int C);
 gpt2_status gpt2k_encoder_backward(float *dwte, float *dwpe, const float *dout, const int32_t *ids,
                                    const int32_t *order, int B, int T, int C, int V, float *work, void *stream);

@@ -348,6 +348,38 @@ def test_encoder_and_token_order(g, oracle_lib):
     assert int(err.item()) & 1
 
 
+@pytest.mark.parametrize("BT,V,ids", [(1, 7, "zipf"), (3, 50257, "zipf"), (1000, 50257, "zipf"),
+                                      (4096, 50257, "zipf"), (8191, 50257, "zipf"), (8192, 50257, "zipf"),
+                                      (8193, 50257, "zipf"), (16384, 50257, "zipf"), (16384, 50257, "one"),
+                                      (16384, 2000000, "uniform"), (33000, 50257, "zipf")])
+def test_token_order_sizes(g, BT, V, ids):
+    """The position order of the embedding backward on both sides of the
+    switch from the counting kernel to chunk sort + binary search (8192
+    positions), with ragged last chunks, Zipf ids with long runs of repeats,
+    a single repeated id and ids spread over a large vocabulary, against
+    numpy's stable sort by id."""
+    import torch
+    rng = np.random.default_rng(BT)
+    if ids == "zipf":
+        a = np.minimum(rng.zipf(1.1, BT) - 1, V - 1)
+    elif ids == "one":
+        a = np.full(BT, 17)
+    else:
+        a = rng.integers(0, V, BT)
+    a = a.astype(np.int32)
+    order = torch.empty(BT, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.token_order(order, err, dev(a), None, BT, V)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), np.argsort(a, kind="stable"))
+    assert int(err.item()) == 0
+    bad = a.copy()
+    bad[BT // 2] = V
+    g.token_order(order, err, dev(bad), None, BT, V)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+
+
 def test_adamw(g, oracle_lib):
     import torch
     rng = np.random.default_rng(2)

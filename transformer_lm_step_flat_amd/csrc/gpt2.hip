@@ -289,7 +289,7 @@ struct Layout {
     int site_ks[NSITES];
     size_t w_site_dw[NSITES], w_site_db[NSITES];
     // int buffer
-    size_t i_tok, i_order, i_err, i_dec, niwork;
+    size_t i_tok, i_order, i_sort, i_err, i_dec, niwork;
     // the work regions with their exact float counts (offsets are padded to
     // 64 floats), each cut into `parts` equal slices (per layer or per slot)
     struct WRegion {
@@ -402,7 +402,8 @@ void make_layout(const gpt2_config *c, int B, int T, Layout *Lo) {
     l.nwork = off;
     l.i_tok = 0;
     l.i_order = align_up(BT);
-    l.i_err = l.i_order + align_up(BT);
+    l.i_sort = l.i_order + align_up(BT);  // the token order's sorted chunks (8-byte keys), at large BT
+    l.i_err = l.i_sort + align_up(k_token_prep_work((int)BT));
     l.i_dec = l.i_err + ALIGN;  // the position a decoding step works on (read on the device)
     l.niwork = l.i_dec + ALIGN;
 }
@@ -876,7 +877,7 @@ gpt2_status gpt2_forward(gpt2_model *m, const int32_t *inputs, const int32_t *ta
     // keep this batch's ids for the embedding backward
     HIPCK(m, copy_ids(tok, inputs, BT, s));
     inputs = tok;
-    KRUN(m, "token_prep_kernel", 12.0 * BT, k_token_prep(inputs, targets, order, err, BT, l.V, s));
+    KRUN(m, k_token_prep_name(BT), 12.0 * BT, k_token_prep(inputs, targets, order, err, m->buf.iwork + l.i_sort, BT, l.V, s));
     KRUN(m, "encoder_forward_kernel", 12.0 * BTC, k_encoder_forward(A + l.aoff[A_ENCODED], inputs, P + l.poff[0], P + l.poff[1], B, T, C, l.V, s));
     for (int li = 0; li < l.L; li++) {
         const float *res = li == 0 ? A + l.aoff[A_ENCODED] : A + l.aoff[A_RES3] + (li - 1) * BTC;
@@ -1446,9 +1447,13 @@ gpt2_status gpt2k_encoder_forward(float *out, const int32_t *ids, const float *w
     return GPT2_OK;
 }
 
+size_t gpt2k_token_order_work(int BT) { return BT > 0 ? k_token_prep_work(BT) : 0; }
+
 gpt2_status gpt2k_token_order(int32_t *order, int32_t *err_flag, const int32_t *ids, const int32_t *targets,
-                              int BT, int V, void *stream) {
-    KCK(k_token_prep(ids, targets, order, err_flag, BT, V, (hipStream_t)stream));
+                              int BT, int V, int32_t *work, void *stream) {
+    if (BT <= 0 || V <= 0) return fail(nullptr, GPT2_EINVAL, "BT and V must be positive");
+    if (k_token_prep_work(BT) && !work) return fail(nullptr, GPT2_EINVAL, "work is required at this BT");
+    KCK(k_token_prep(ids, targets, order, err_flag, work, BT, V, (hipStream_t)stream));
     return GPT2_OK;
 }
 
@@ -1571,6 +1576,7 @@ gpt2_status gpt2_audit_step(const gpt2_config *cfg, int B, int T, const char *sh
         ck.add(base(5), l.wreg[i].off, l.wreg[i].cnt, l.wreg[i].parts, std::string("work:") + l.wreg[i].name);
     ck.add(base(6), l.i_tok, (size_t)l.BT, 1, "iwork:ids");
     ck.add(base(6), l.i_order, (size_t)l.BT, 1, "iwork:order");
+    if (k_token_prep_work((int)l.BT)) ck.add(base(6), l.i_sort, k_token_prep_work((int)l.BT), 1, "iwork:sort");
     ck.add(base(6), l.i_err, 1, 1, "iwork:err");
     ck.add(base(6), l.i_dec, 1, 1, "iwork:decode_pos");
     ck.add(base(7), 0, (size_t)l.BT, 1, "caller:inputs");

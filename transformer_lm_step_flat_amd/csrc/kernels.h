@@ -8,9 +8,15 @@ hipError_t k_fill(float *p, size_t n, float v, hipStream_t s);
 hipError_t k_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s);
 
 // Validate ids (err |= 1 for an input, 2 for a target outside [0, V)) and
-// sort the positions by (input id, position): order[rank] = position.
-hipError_t k_token_prep(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int BT, int V,
-                        hipStream_t s);
+// sort the positions by (input id, position): order[rank] = position.  Below
+// 8192 positions every position counts the keys below its own (O(BT^2)
+// work, one launch); from there chunks of 1024 keys are sorted and each
+// position's rank is found by binary search in every chunk (O(BT log BT)),
+// with k_token_prep_work(BT) int32s of 8-byte-aligned workspace.
+size_t k_token_prep_work(int BT);
+hipError_t k_token_prep(const int32_t *inp, const int32_t *tgt, int32_t *order, int32_t *err, int32_t *work, int BT,
+                        int V, hipStream_t s);
+const char *k_token_prep_name(int BT);  // the kernel that gives the order
 
 // out[b][t][:] = wte[inp[b][t]][:] + wpe[t][:]
 hipError_t k_encoder_forward(float *out, const int32_t *inp, const float *wte, const float *wpe, int B, int T,

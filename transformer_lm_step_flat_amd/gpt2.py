@@ -91,13 +91,14 @@ _SIGS = {
     "gpt2k_gelu_backward": [_P, _P, _P, _Z, _P],
     "gpt2k_crossentropy": [_P, _P, _P, _P, _I, _I, _I, _P],
     "gpt2k_encoder_forward": [_P, _P, _P, _P, _I, _I, _I, _I, _P],
-    "gpt2k_token_order": [_P, _P, _P, _P, _I, _I, _P],
+    "gpt2k_token_order": [_P, _P, _P, _P, _I, _I, _P, _P],
     "gpt2k_encoder_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
     "gpt2k_adamw": [_P, _P, _P, _P, _Z, _F, _F, _F, _F, _F, _I, _P],
     "gpt2k_probe_mfma": [_P, _I, ctypes.POINTER(ctypes.c_double), _P],
     "gpt2k_probe_copy": [_P, _P, _Z, _P],
 }
 _SIZE_FNS = {
+    "gpt2k_token_order_work": [_I],
     "gpt2k_linear_backward_work": [_I, _I, _I],
     "gpt2k_layernorm_backward_work": [_I, _I],
     "gpt2k_attention_backward_work": [_I, _I, _I, _I],
@@ -446,7 +447,9 @@ def encoder_forward(out, ids, wte, wpe, B, T, C, V):
 
 def token_order(order, err, ids, targets, BT, V):
     _need(order=(order, BT), err=(err, 1), ids=(ids, BT), targets=(targets, BT))
-    _check(lib().gpt2k_token_order(_ptr(order), _ptr(err), _ptr(ids), _ptr(targets), BT, V, _s()))
+    nw = lib().gpt2k_token_order_work(BT)
+    work = torch.empty(nw, dtype=torch.int32, device=ids.device) if nw else None
+    _check(lib().gpt2k_token_order(_ptr(order), _ptr(err), _ptr(ids), _ptr(targets), BT, V, _ptr(work), _s()))
 
 
 def encoder_backward(dwte, dwpe, dout, ids, order, B, T, C, V):
