@@ -367,6 +367,56 @@ def bf16_bench(torch, gpt2, M, step, first, steps, warmup, B, T):
                          "peak_tflops": PEAK_MFMA_BF16_TFLOPS, "frac": achieved / PEAK_MFMA_BF16_TFLOPS}}
 
 
+def ln_sweep(C=768, rows=(4096, 16384), reps=50):
+    """The LayerNorm kernels on their own: `reps` back-to-back launches of
+    the library's forward and backward (accumulating; its kernel and the
+    column sums of dw and db) at N rows of C, replayed from a graph and timed
+    with events around the replay, against the 8 TB/s HBM peak.  Bytes
+    are the algorithmic ones: forward reads x and writes y (8 N C) plus the
+    row statistics; backward reads dy, x and the dx it accumulates into and
+    writes dx (16 N C)."""
+    import torch
+    from transformer_lm_step_flat_amd import gpt2
+    gpt2.lib()
+    print(f"LayerNorm kernels alone, C = {C}: {reps} launches back to back, replayed from a captured graph, "
+          f"HIP events around the replay:")
+    print("| rows N | forward us | forward GB/s | % of 8 TB/s | backward us | backward GB/s | % of 8 TB/s |")
+    print("|---:|---:|---:|---:|---:|---:|---:|")
+    for N in rows:
+        g = torch.Generator(device="cuda").manual_seed(N)
+        x = torch.randn(N * C, device="cuda", generator=g)
+        dy = torch.randn(N * C, device="cuda", generator=g)
+        w = torch.randn(C, device="cuda", generator=g)
+        b = torch.randn(C, device="cuda", generator=g)
+        y, dx = torch.empty_like(x), torch.zeros_like(x)
+        mu, rs = torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+        dw, db = torch.zeros(C, device="cuda"), torch.zeros(C, device="cuda")
+
+        def timed(fn):
+            # the launches are captured in a graph and replayed, so that the
+            # host's per-call cost (argument checks, ctypes) does not pace them
+            fn()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(reps):
+                    fn()
+            gr.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e3
+
+        tf = timed(lambda: gpt2.layernorm_forward(y, mu, rs, x, w, b, N, C))
+        tb = timed(lambda: gpt2.layernorm_backward(dx, dw, db, dy, x, w, mu, rs, N, C, True))
+        bf, bb = 8.0 * N * C + 8.0 * N, 16.0 * N * C + 8.0 * N
+        print(f"| {N} | {tf:.2f} | {bf / tf * 1e-3:.0f} | {bf / tf * 1e-3 / PEAK_HBM_GBS * 100:.1f} | {tb:.2f} | "
+              f"{bb / tb * 1e-3:.0f} | {bb / tb * 1e-3 / PEAK_HBM_GBS * 100:.1f} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,7 +437,11 @@ def main():
     ap.add_argument("--sq-summary", metavar="SQ_CSV", help="summarise a rocprofv3 --pmc run of SQ counters and exit")
     ap.add_argument("--kt-summary", metavar="STATS_CSV",
                     help="summarise a rocprofv3 --kernel-trace --stats run (kernel_stats.csv) and exit")
+    ap.add_argument("--ln-sweep", action="store_true", help="time the LayerNorm kernels alone and exit")
     args = ap.parse_args()
+    if args.ln_sweep:
+        ln_sweep()
+        return
     if args.kt_summary:
         kt_summary(args.kt_summary, args.pmc_command, args.config)
         return
