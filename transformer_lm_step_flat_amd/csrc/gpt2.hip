@@ -1085,7 +1085,11 @@ namespace {
 
 // The launches of one decoding step on stream s, for the position in the
 // model's device int (set before, by gpt2_decode_step).
-gpt2_status decode_launches(gpt2_model *m, hipStream_t s, const int32_t *tokens, const float *coins, int32_t *next) {
+// pos: the position decoded, for the byte counts of per-launch profiling
+// only (the kernels read it from the device, so that a captured step serves
+// every position).
+gpt2_status decode_launches(gpt2_model *m, hipStream_t s, const int32_t *tokens, const float *coins, int32_t *next,
+                            int pos) {
     const Layout &l = m->lo;
     const int B = l.B, T = l.T, C = l.C, NH = l.NH;
     const size_t BTC = (size_t)l.BT * C, c = C;
@@ -1103,7 +1107,7 @@ gpt2_status decode_launches(gpt2_model *m, hipStream_t s, const int32_t *tokens,
               k_rows_linear(qkv, (long long)T * 3 * C, x, C, P + l.poff[4] + li * 3 * c * c, P + l.poff[5] + li * 3 * c,
                             nullptr, 0, P + l.poff[2] + li * c, P + l.poff[3] + li * c, B, C, 3 * C, 0, dpos, 3 * C,
                             T - 1, s));
-        KRUN(m, "decode_attn_partial_kernel", w * C * 2 * T,
+        KRUN(m, "decode_attn_partial_kernel", w * C * 2.0 * (pos + 1),  // k and v rows u <= pos
              k_decode_attention(att, aws, qkv, dpos, B, T, C, NH, s));
         KRUNF(m, k_rows_linear_name(C), 2.0 * B * C * C, 4.0 * C * C + 3 * w * C,
               k_rows_linear(x, C, att, C, P + l.poff[6] + li * c * c, P + l.poff[7] + li * c, x, C, nullptr, nullptr, B,
@@ -1143,7 +1147,7 @@ hipGraphExec_t decode_graph(gpt2_model *m, const int32_t *tokens, const float *c
     hipGraphExec_t exec = nullptr;
     bool ok = hipStreamBeginCapture(m->capture_stream, hipStreamCaptureModeThreadLocal) == hipSuccess;
     if (ok) {
-        const gpt2_status st = decode_launches(m, m->capture_stream, tokens, coins, next);
+        const gpt2_status st = decode_launches(m, m->capture_stream, tokens, coins, next, m->lo.T - 1);
         ok = hipStreamEndCapture(m->capture_stream, &graph) == hipSuccess && st == GPT2_OK && graph;
     }
     if (ok) ok = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
@@ -1176,7 +1180,7 @@ gpt2_status gpt2_decode_step(gpt2_model *m, const int32_t *tokens, int pos, cons
             return GPT2_OK;
         }
     }
-    return decode_launches(m, s, tokens, coins, next);
+    return decode_launches(m, s, tokens, coins, next, pos);
 }
 
 gpt2_status gpt2_set_matmul_precision(gpt2_model *m, int precision) {
