@@ -92,7 +92,8 @@ enum { GPT2_PARAMS = 0, GPT2_ACTS = 1 };
 /* Buffer sizes for (cfg, B, T): the constant footprint allocated once up
  * front (QbitAI llm.c article, "手動實現每個層前向/反向傳播": every tensor a fixed
  * offset into memory allocated at the start).  Host only; B >= 1,
- * 1 <= T <= max_seq_len. */
+ * 1 <= T <= min(max_seq_len, 1024), T a multiple of 4 unless the head
+ * dimension is 16, 32 or 64. */
 gpt2_status gpt2_query_sizes(const gpt2_config *cfg, int B, int T, gpt2_sizes *out);
 
 /* Entry idx of a layout table (host only).  The tensor order is explicit (the

@@ -57,7 +57,7 @@ gpt2_status gpt2k_layernorm_backward(float *dinp, float *dw, float *db, const fl
 
 /* Causal multi-head attention over qkv[B][T][3C] (q | k | v, heads of C/NH),
  * with the score matrices materialised (any head dimension that is a
- * multiple of 4): att[B][NH][T][T] = softmax probabilities (zero above the diagonal up to the
+ * multiple of 4; T a multiple of 4): att[B][NH][T][T] = softmax probabilities (zero above the diagonal up to the
  * next multiple of 128 columns), atty[B][T][C] = heads concatenated. */
 gpt2_status gpt2k_attention_forward(float *atty, float *att, const float *qkv, int B, int T, int C, int NH,
                                     void *stream);
@@ -76,8 +76,9 @@ gpt2_status gpt2k_attention_backward(float *dqkv, const float *datty, const floa
  * over workgroups (forward: chunks of at most 256 keys; dk/dv: equal ranges of
  * the (key block, query block) iterations over the resident workgroups) and
  * their partial results merged in a fixed order through `work`
- * (gpt2k_flash_attention_work floats, B*NH*T*T of them for ds; the same size
- * serves both calls).  GPT2_EINVAL for other head dimensions. */
+ * (gpt2k_flash_attention_work floats, B*NH*T*Tp of them for ds, Tp = T
+ * rounded up to a multiple of 4; the same size serves both calls).  Any
+ * 1 <= T <= 1024.  GPT2_EINVAL for other head dimensions. */
 size_t gpt2k_flash_attention_work(int B, int T, int C, int NH);
 gpt2_status gpt2k_flash_attention_forward(float *atty, float *lse, const float *qkv, int B, int T, int C, int NH,
                                           float *work, void *stream);

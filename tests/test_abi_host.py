@@ -84,7 +84,7 @@ def test_activation_table_is_aligned_and_disjoint(g):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(C=66), dict(NH=5), dict(Vp=999), dict(T=300), dict(T=62), dict(C=4096, NH=64), dict(L=0)])
+    dict(C=66), dict(NH=5), dict(Vp=999), dict(T=300), dict(T=62, C=48, NH=4), dict(C=4096, NH=64), dict(L=0)])
 def test_invalid_shapes_are_rejected(g, bad):
     cfg = synth.config("small")
     cfg.update(bad)
@@ -93,6 +93,16 @@ def test_invalid_shapes_are_rejected(g, bad):
         g.query_sizes(cfg, 2, T)
     assert e.value.status == g.GPT2_EINVAL
     assert g.lib().gpt2_last_error(None)
+
+
+@pytest.mark.parametrize("T", [1, 7, 62])
+def test_any_T_with_fused_attention_head_dims(g, T):
+    """T need not be a multiple of 4 when the head dimension (16 here) takes
+    the fused attention; the score-gradient rows are then padded."""
+    cfg = synth.config("small")
+    cfg.update(T=T)
+    s = g.query_sizes(cfg, 2, T)
+    assert s.work > 0 and s.acts > 0
 
 
 def test_xl_state_fits_in_hbm(g):

@@ -60,6 +60,12 @@ CASES = {
     "hd64": synth.config(dict(L=2, C=128, NH=2, T=132, B=2, V=300, maxT=132, tokens="zipf")),
     # head dim 12: attention takes the materialised-score path
     "hd12": synth.config(dict(L=2, C=48, NH=4, T=40, B=2, V=50, maxT=40)),
+    # T not a multiple of 4 (the fused attention pads its score-gradient rows):
+    # one position (attention returns each head's value row), seven, and 130
+    # (a 128-query block and a ragged one, head dim 64)
+    "T1": synth.config(dict(L=2, C=32, NH=2, T=1, B=3, V=11, maxT=1)),
+    "T7": synth.config(dict(L=2, C=64, NH=4, T=7, B=2, V=50, maxT=8)),
+    "T130_hd64": synth.config(dict(L=2, C=128, NH=2, T=130, B=2, V=300, maxT=130, tokens="zipf")),
 }
 
 

@@ -18,6 +18,10 @@ WORKLOADS = {
     "hd12": synth.config(dict(L=2, C=48, NH=4, T=40, B=2, V=50, maxT=40)),
     "hd64_T132": synth.config(dict(L=2, C=128, NH=2, T=132, B=2, V=300, maxT=132)),
     "one_position": synth.config(dict(L=2, C=32, NH=2, T=4, B=1, V=11, maxT=4)),
+    # T not a multiple of 4 (fused attention only): padded score-gradient rows
+    "T1": synth.config(dict(L=2, C=32, NH=2, T=1, B=3, V=11, maxT=1)),
+    "T7": synth.config(dict(L=2, C=64, NH=4, T=7, B=2, V=50, maxT=8)),
+    "T130_hd64": synth.config(dict(L=2, C=128, NH=2, T=130, B=2, V=300, maxT=130)),
 }
 
 

@@ -433,6 +433,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
     const long long W = (long long)BH * W1;
     const long long lo_g = range_lo(g, W, G), hi_g = range_lo(g + 1, W, G);
     const long long rs = 3LL * C;
+    const int Tp = (T + 3) & ~3;  // ds row pitch
     TileLoader<HD, TB> lq, lo;
     // lse and D of a block's queries (threads tid < TB), loaded with its tiles
     float lse_next = 0.0f, d_next = 0.0f;
@@ -524,10 +525,12 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             const bool edge = t0 + TB > T || u0 + QW > T;
             // This wave's 32 x 32 block of ds leaves as 16-byte stores: lane l takes
             // row l / 2, columns 8 i + 4 (l % 2) .. + 3 for i = 0..3 (one base address,
-            // constant offsets).  T % 4 == 0 and u0 % 32 == 0, so a group of 4
-            // columns lies wholly inside or outside [0, T).
+            // constant offsets).  ds rows are Tp = T rounded up to a multiple of 4
+            // floats apart and u0 % 32 == 0, so a group of 4 columns that starts
+            // below T ends inside its row; columns T..Tp - 1 get the zeros of the
+            // keys past T.
             const int drow = lane >> 1, dcol = 4 * (lane & 1);
-            float *const dsw = dsout + ((long long)bh * T + t0 + drow) * T + u0 + dcol;
+            float *const dsw = dsout + ((long long)bh * T + t0 + drow) * Tp + u0 + dcol;
             const bool row_ok = t0 + drow < T;
             if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
                 if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
@@ -711,7 +714,8 @@ __global__ __launch_bounds__(256) void flash_bwd_sum_kernel(float *__restrict__ 
 }
 
 // floats of the ds matrices at the start of the backward workspace (256-byte aligned)
-size_t ds_floats(int B, int T, int NH) { return ((size_t)B * NH * T * T + 63) / 64 * 64; }
+// (rows of (T + 3) / 4 * 4 floats: 16-byte stores and loads along a row)
+size_t ds_floats(int B, int T, int NH) { return ((size_t)B * NH * T * ((T + 3) / 4 * 4) + 63) / 64 * 64; }
 
 // forward items (query block chunks) of one (batch, head)
 int total_items(int T) {
@@ -776,7 +780,7 @@ hipError_t launch_bwd_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dou
         audit(au, "flash_bwd_D_kernel", "out", out, BTC, false);
         audit(au, k, "dqkv", dqkv, 3 * BTC, true);
         audit(au, k, "kvws", ws + ds_floats(B, T, NH), 2 * G * 2 * QBLK * HD, true);
-        audit(au, k, "ds", ws, BHT * T, true);
+        audit(au, k, "ds", ws, BHT * ((T + 3) / 4 * 4), true);
         audit(au, k, "dout", dout, BTC, false);
         audit(au, k, "qkv", qkv, 3 * BTC, false);
         audit(au, k, "lse", lse, BHT, false);

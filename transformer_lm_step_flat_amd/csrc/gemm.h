@@ -32,6 +32,9 @@ enum GemmCausal {
 
 struct GemmDesc {
     bool a_kcontig = true, b_kcontig = true;
+    // a K-contiguous A whose rows continue, zero, to the next multiple of 4
+    // (lda at least that): K need not be a multiple of 4
+    bool a_kpad = false;
     int M = 0, N = 0, K = 0;
     const float *A = nullptr;
     long long lda = 0;

@@ -698,7 +698,8 @@ hipError_t make_args(const GemmDesc &d, GemmArgs &a) {
     if (d.ksplit > 1 && d.epi != EPI_STORE) return hipErrorInvalidValue;
     // 16-byte vector loads: contiguous extents, leading dims and strides in multiples of 4
     // a K-contiguous operand is read 4 k at a time; an MN-contiguous one row by row
-    if ((d.a_kcontig || d.b_kcontig) && (d.K % 4)) return hipErrorInvalidValue;
+    if (((d.a_kcontig && !d.a_kpad) || d.b_kcontig) && (d.K % 4)) return hipErrorInvalidValue;
+    if (d.a_kpad && (!d.a_kcontig || d.lda < (d.K + 3) / 4 * 4)) return hipErrorInvalidValue;
     if ((d.lda % 4) || (d.ldb % 4)) return hipErrorInvalidValue;
     if (!d.a_kcontig && (d.M % 4)) return hipErrorInvalidValue;
     if (!d.b_kcontig && (d.N % 4)) return hipErrorInvalidValue;
@@ -744,7 +745,9 @@ int resolve_tile(const GemmDesc &d) {
 static void audit_gemm(AuditSink *au, const char *kernel, const GemmDesc &d) {
     const long long bo = d.nbo - 1, bi = d.nbi - 1, M = d.M, N = d.N, K = d.K;
     if (K > 0) {
-        const long long a = (d.a_kcontig ? (M - 1) * d.lda + K : (K - 1) * d.lda + M) + bo * d.sAo + bi * d.sAi;
+        // a K-contiguous A is read 4 k at a time: up to K rounded up to 4 in each row
+        const long long ka = d.a_kpad ? (K + 3) / 4 * 4 : K;
+        const long long a = (d.a_kcontig ? (M - 1) * d.lda + ka : (K - 1) * d.lda + M) + bo * d.sAo + bi * d.sAi;
         const long long b = (d.b_kcontig ? (N - 1) * d.ldb + K : (K - 1) * d.ldb + N) + bo * d.sBo + bi * d.sBi;
         audit(au, kernel, "A", d.A, a, false);
         audit(au, kernel, "B", d.B, b, false);

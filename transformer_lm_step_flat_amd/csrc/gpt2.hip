@@ -319,7 +319,10 @@ bool config_ok(const gpt2_config *c, int B, int T, std::string *why) {
     if (B <= 0 || T <= 0) return fail("B and T must be positive");
     if (T > c->max_seq_len) return fail("T > max_seq_len");
     if (T > 1024) return fail("T > 1024 is not supported");
-    if (T % 4) return fail("T must be a multiple of 4");
+    // the materialised attention (head dims without the fused kernels) keeps
+    // T x T matrices read 16 bytes at a time along T
+    if (T % 4 && !flash_attention_supported(c->channels / c->num_heads))
+        return fail("T must be a multiple of 4 for head dims other than 16, 32 and 64");
     if ((long long)B * T > (1LL << 24)) return fail("B*T too large");
     snprintf(buf, sizeof buf, "ok");
     return true;
@@ -770,11 +773,12 @@ hipError_t flash_backward(float *dqkv, float *Dbuf, float *ws, const float *datt
         return flash_attention_backward_dkdv(dqkv, ws, Dbuf, datty, qkv, atty, lse, B, T, C, NH, s);
     });
     if (e != hipSuccess) return e;
-    const long long C3 = 3LL * C, TT = (long long)T * T;
+    // ds rows are Tp floats apart, zero past T
+    const long long C3 = 3LL * C, Tp = (T + 3) / 4 * 4, TT = (long long)T * Tp;
     GemmDesc q;
-    q.a_kcontig = true; q.b_kcontig = false;
+    q.a_kcontig = true; q.b_kcontig = false; q.a_kpad = true;
     q.M = T; q.N = hd; q.K = T;
-    q.A = flash_attention_ds(ws); q.lda = T; q.B = qkv + C; q.ldb = C3; q.C = dqkv; q.ldc = C3;
+    q.A = flash_attention_ds(ws); q.lda = Tp; q.B = qkv + C; q.ldb = C3; q.C = dqkv; q.ldc = C3;
     q.alpha = 1.0f / sqrtf((float)hd); q.causal = CAUSAL_KEND;
     q.nbo = B; q.nbi = NH;
     q.sAo = NH * TT; q.sAi = TT; q.sBo = T * C3; q.sBi = hd; q.sCo = T * C3; q.sCi = hd;
@@ -1382,6 +1386,10 @@ gpt2_status gpt2k_layernorm_backward(float *dinp, float *dw, float *db, const fl
 static bool attn_shape_ok(int B, int T, int C, int NH) {
     return B > 0 && T > 0 && T <= 1024 && T % 4 == 0 && NH > 0 && C % NH == 0 && (C / NH) % 4 == 0;
 }
+// the fused kernels take any T (their T x T workspace rows are padded to a multiple of 4)
+static bool flash_shape_ok(int B, int T, int C, int NH) {
+    return B > 0 && T > 0 && T <= 1024 && NH > 0 && C % NH == 0 && flash_attention_supported(C / NH);
+}
 
 gpt2_status gpt2k_attention_forward(float *atty, float *att, const float *qkv, int B, int T, int C, int NH,
                                     void *stream) {
@@ -1409,8 +1417,8 @@ size_t gpt2k_flash_attention_work(int B, int T, int C, int NH) {
 
 gpt2_status gpt2k_flash_attention_forward(float *atty, float *lse, const float *qkv, int B, int T, int C, int NH,
                                           float *work, void *stream) {
-    if (!attn_shape_ok(B, T, C, NH) || !flash_attention_supported(C / NH))
-        return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024, T % 4 == 0");
+    if (!flash_shape_ok(B, T, C, NH))
+        return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024");
     KCK(flash_attention_forward(atty, lse, work + align_up((size_t)B * NH * T), qkv, B, T, C, NH,
                                 (hipStream_t)stream));
     return GPT2_OK;
@@ -1419,8 +1427,8 @@ gpt2_status gpt2k_flash_attention_forward(float *atty, float *lse, const float *
 gpt2_status gpt2k_flash_attention_backward(float *dqkv, const float *datty, const float *qkv, const float *atty,
                                            const float *lse, int B, int T, int C, int NH, float *work,
                                            void *stream) {
-    if (!attn_shape_ok(B, T, C, NH) || !flash_attention_supported(C / NH))
-        return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024, T % 4 == 0");
+    if (!flash_shape_ok(B, T, C, NH))
+        return fail(nullptr, GPT2_EINVAL, "fused attention supports head dims 16, 32, 64 and T <= 1024");
     float *Dbuf = work, *ws = work + align_up((size_t)B * NH * T);
     KCK(flash_backward(dqkv, Dbuf, ws, datty, qkv, atty, lse, B, T, C, NH, (hipStream_t)stream));
     return GPT2_OK;
