@@ -30,6 +30,7 @@ CASES = {
     "ragged": synth.config(dict(L=1, C=48, NH=3, T=20, B=3, V=36, Vp=36, maxT=24)),
     "hd64": synth.config(dict(L=2, C=128, NH=2, T=132, B=2, V=300, maxT=132, tokens="zipf")),
     "hd12": synth.config(dict(L=2, C=48, NH=4, T=40, B=2, V=50, maxT=40)),
+    "T7": synth.config(dict(L=2, C=64, NH=4, T=7, B=2, V=50, maxT=8)),
 }
 
 
