@@ -3,8 +3,9 @@
 // positions being read from the rows the forward (or earlier steps) left in
 // the qkv activations (the GeekNews page on the 3000-byte C GPT-2, "Cách KV
 // caching hoạt động" and "Phép nhân ma trận nhanh": keep the cache, multiply
-// only the new rows).  All of it is bound by HBM: the weights are read once
-// per step, the cache once per layer.
+// only the new rows).  All of it is memory-bound (the weights are read once
+// per step, the cache once per layer); at a few rows per step most launches
+// are short enough that their fixed cost is a large part of their time.
 #include "audit.h"
 #include "common.h"
 #include "decode.h"
