@@ -85,18 +85,36 @@ struct TileLoader {
             if (f < ROWS * HD / 4) *(floatx4 *)&lds[(f / (HD / 4)) * pitch + 4 * (f % (HD / 4))] = value(i);
         }
     }
-    // The same tile transposed, [HD][pitch] (row index contiguous), so that
-    // 4 consecutive rows of one column are one 16-byte LDS read.
+};
+
+// A 64-row tile that is stored transposed, [HD][pitch] (row index
+// contiguous), so that 4 consecutive rows of one column are one 16-byte LDS
+// read.  Thread tid loads row 16 wave + lane % 16, column groups 4 i +
+// lane / 16 (i < HD / 16): the 64 lanes of one transposed store then write
+// 16 rows of 4 columns, each of 32 banks twice (with 4 rows of 16 column
+// groups per store, as in the row-major order, one bank takes 8 lanes).
+// A row past nrows reads row 0 (always valid) and is zeroed when stored.
+template <int HD>
+struct TileLoaderT {
+    static constexpr int F4 = HD / 16;
+    floatx4 r[F4];
+    bool ok;
+    __device__ __forceinline__ void load(const float *base, long long rs, int row0, int nrows, int tid) {
+        const int row = 16 * (tid >> 6) + (tid & 15), c0 = (tid >> 4) & 3;
+        ok = row0 + row < nrows;
+        // a 32-bit offset from the workgroup's base (rows < 1024, rs <= 6144): one register
+        const int off = (ok ? (row0 + row) * (int)rs : 0) + 4 * c0;
+#pragma unroll
+        for (int i = 0; i < F4; i++) r[i] = *(const floatx4 *)(base + off + 16 * i);
+    }
     __device__ __forceinline__ void store_t(float *lds, int pitch, int tid) const {
+        const int row = 16 * (tid >> 6) + (tid & 15), c0 = (tid >> 4) & 3;
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < F4; i++) {
-            int f = tid + 256 * i;
-            if (f < ROWS * HD / 4) {
-                const int row = f / (HD / 4), c = 4 * (f % (HD / 4));
-                const floatx4 v = value(i);
+            const floatx4 v = ok ? r[i] : z;
 #pragma unroll
-                for (int e = 0; e < 4; e++) lds[(c + e) * pitch + row] = v[e];
-            }
+            for (int e = 0; e < 4; e++) lds[(4 * (4 * i + c0) + e) * pitch + row] = v[e];
         }
     }
 };
@@ -268,7 +286,9 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
     float m = -INFINITY, lsum = 0.0f;
 
     const int kc0 = chunk * KCH, kc1 = min(min(T, q0 + QBLK), kc0 + KCH);
-    TileLoader<HD, KB> lk, lv;
+    static_assert(KB == 64, "the transposed V tile has 64 rows");
+    TileLoader<HD, KB> lk;
+    TileLoaderT<HD> lv;
     lk.load(qb_ptr + C, rs, kc0, T, tid);
     lv.load(qb_ptr + 2 * C, rs, kc0, T, tid);
     for (int k0 = kc0; k0 < kc1; k0 += KB) {
