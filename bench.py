@@ -417,6 +417,15 @@ def ln_sweep(C=768, rows=(4096, 16384), reps=50):
               f"{bb / tb * 1e-3:.0f} | {bb / tb * 1e-3 / PEAK_HBM_GBS * 100:.1f} |", flush=True)
 
 
+def step_roofline_ms(sites, steps):
+    """The step's roofline time in ms: each call site's launches at the slower
+    of their matrix bound (FLOPs / fp32 matrix peak) and their HBM bound
+    (algorithmic bytes / HBM peak), summed.  Launches at one call site share a
+    shape, so the bound of their sums is the sum of their bounds."""
+    return sum(max(e["flops"] / (PEAK_MFMA_FP32_TFLOPS * 1e9), e["bytes"] / (PEAK_HBM_GBS * 1e6))
+               for e in sites) / steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -558,6 +567,7 @@ def main():
         avg_ms = d["ms"] / d["launches"]
         achieved = per_launch / (avg_ms * 1e-3) / (1e12 if bound == "mfma" else 1e9)
         all_flops = sum(e["flops"] for e in by_kernel.values()) / args.steps
+        roof_ms = step_roofline_ms(sites, args.steps)
         alg_bytes = d["bytes"] / d["launches"]
         traffic = measured_traffic(d["name"], args.config)
         traced_ms = traced_duration(d["name"], args.config)
@@ -573,8 +583,11 @@ def main():
                     per_launch / (traced_ms * 1e-3) / (1e12 if bound == "mfma" else 1e9) / peak,
                     "step_flops": all_flops,
                     "step_mfma_frac": all_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP32_TFLOPS,
+                    "step_roofline_ms": roof_ms, "step_roofline_frac": roof_ms / ms,
                     "frac_of_measured_peak": achieved / (peaks["mfma_fp32_tflops"] if bound == "mfma"
                                                          else peaks["hbm_copy_gbs"])}
+        log(f"step roofline: {roof_ms:.2f} ms (each call site at max(FLOPs / matrix peak, bytes / HBM peak)), "
+            f"{100 * roof_ms / ms:.1f}% of the measured {ms:.2f} ms/step")
 
     decode = None
     if args.decode_steps > 0 and args.decode_prefill + args.decode_steps <= T:

@@ -79,3 +79,12 @@ def test_trace_summary_averages_and_gates_on_sources(bench, tmp_path, capsys):
     assert bench.traced_duration(PAIR, "xl") is None
     bench.sources_sha256 = lambda: "f" * 64
     assert bench.traced_duration(PAIR, "124m") is None
+
+
+def test_step_roofline_takes_each_site_at_its_slower_bound(bench):
+    ms_flops, ms_bytes = 157.3e9, 8e9  # one ms at the fp32 matrix peak, one ms at the HBM peak
+    sites = [dict(flops=2 * ms_flops, bytes=0.1 * ms_bytes),
+             dict(flops=0.0, bytes=3 * ms_bytes),
+             dict(flops=ms_flops, bytes=ms_bytes)]
+    assert bench.step_roofline_ms(sites, 1) == pytest.approx(2.0 + 3.0 + 1.0)
+    assert bench.step_roofline_ms(sites, 2) == pytest.approx(3.0)
