@@ -18,13 +18,12 @@
 // The forward computes s^T = K Q^T so that a lane owns one query (a result
 // column) and 32 keys (its rows): the softmax statistics are then per lane
 // (plus its partner lane l ^ 32), and the probabilities sit exactly where
-// o^T += V^T p^T needs them as its B operand.  The backward kernel computes
-// s = Q K^T so that a lane owns one key, and p / ds are in place as the A
-// operand of dv += p^T dO and dk += ds^T Q; it also stores ds (each
-// wavefront's 32 x 32 block through a small LDS patch, as 16-byte row
-// pieces), and dq = scale ds K is then a causal GEMM over the stored ds.
-// Reductions over the head dimension use the k-split trick of the GEMM
-// kernel: lane half h walks d = h*HD/2 + j.
+// o^T += V^T p^T needs them as its B operand (reductions over the head
+// dimension use the k-split trick of the GEMM kernel: lane half h walks
+// d = h*HD/2 + j).  The backward kernel uses v_mfma_f32_16x16x4_f32 and
+// computes s = Q K^T so that a lane owns one key (a result column), and p /
+// ds are in place as the A operand of dv += p^T dO and dk += ds^T Q; it also
+// stores ds, and dq = scale ds K is then a causal GEMM over the stored ds.
 //
 // Every output element is written by exactly one lane, with sums in a fixed
 // order: results are bitwise reproducible.
@@ -55,20 +54,20 @@ constexpr float LN2 = 0.6931471805599453f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Load `rows` rows of HD floats (row stride `rs` floats, rows >= nvalid are
-// zero) into registers: thread tid owns float4 number tid + 256*i.  The loads
+// zero) into registers: thread tid of NT owns float4 number tid + NT*i.  The loads
 // are issued unconditionally (a thread out of range reads row 0, which is
 // always valid) and the zeroing is applied when the tile is stored, so that
 // nothing waits for the loads until then: the next tile is in flight while
 // the current one is consumed.
-template <int HD, int ROWS>
+template <int HD, int ROWS, int NT = 256>
 struct TileLoader {
-    static constexpr int F4 = ROWS * HD / 4 / 256 > 0 ? ROWS * HD / 4 / 256 : 1;
+    static constexpr int F4 = ROWS * HD / 4 / NT > 0 ? ROWS * HD / 4 / NT : 1;
     floatx4 r[F4];
     bool ok[F4];
     __device__ __forceinline__ void load(const float *base, long long rs, int row0, int nrows, int tid) {
 #pragma unroll
         for (int i = 0; i < F4; i++) {
-            const int f = tid + 256 * i;
+            const int f = tid + NT * i;
             const int row = f / (HD / 4), c4 = f % (HD / 4);
             ok[i] = f < ROWS * HD / 4 && row0 + row < nrows;
             r[i] = *(const floatx4 *)(base + (ok[i] ? (long long)(row0 + row) * rs + 4 * c4 : 0));
@@ -81,7 +80,7 @@ struct TileLoader {
     __device__ __forceinline__ void store(float *lds, int pitch, int tid) const {
 #pragma unroll
         for (int i = 0; i < F4; i++) {
-            int f = tid + 256 * i;
+            int f = tid + NT * i;
             if (f < ROWS * HD / 4) *(floatx4 *)&lds[(f / (HD / 4)) * pitch + 4 * (f % (HD / 4))] = value(i);
         }
     }
@@ -429,51 +428,101 @@ __device__ __forceinline__ int xcd_run(int bid, int n) {
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + loc;
 }
 
+// The dk/dv kernel works with v_mfma_f32_16x16x4_f32 (A[i = l % 16][k = l / 16],
+// B[k = l / 16][j = l % 16], result rows 4 (l / 16) + r, column l % 16 in
+// register r): a wavefront owns KW = 16 keys (result columns of s = Q K^T),
+// eight wavefronts the 128 keys of a key block, so that its persistent state
+// (the keys' k and v rows and their dk, dv sums) is a quarter of what a 32-key
+// wavefront holds and four wavefronts fit on each SIMD.  The Q and dO tiles
+// go from memory straight into LDS (global_load_lds_dwordx4: lane L of a
+// load writes the 16 bytes at the load's LDS base + 16 L), so that a tile in
+// flight holds no registers.
+constexpr int KW = 16;                // keys per wavefront
+constexpr int NWB = QBLK / KW;        // wavefronts per workgroup: 8
+constexpr int BWD_THREADS = 64 * NWB;  // 512
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int HD>
-__global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv, float *__restrict__ ws,
-                                                                float *__restrict__ dsout,
-                                                                const float *__restrict__ dout,
-                                                                const float *__restrict__ qkv,
-                                                                const float *__restrict__ lse,
-                                                                const float *__restrict__ Dbuf, int T, int C, int NH,
-                                                                int BH, float scale) {
-    constexpr int P = HD + 4;
-    // Q and dO tiles of TB queries, row-major, two buffers: the next block's
-    // tiles are stored into the other buffer at the end of an iteration, so
-    // one barrier per iteration suffices
-    __shared__ __attribute__((aligned(16))) float Qs[2 * TB * P];
-    __shared__ __attribute__((aligned(16))) float Os[2 * TB * P];
-    __shared__ float Ls[2 * TB], Ds[2 * TB];
-    // per wavefront, its 32 x 32 block of ds on the way to memory (row pitch PP)
-    constexpr int PP = QW + 4;
-    __shared__ __attribute__((aligned(16))) float Ps[NWAVE * QW * PP];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
+__global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv,
+                                                                        float *__restrict__ ws,
+                                                                        float *__restrict__ dsout,
+                                                                        const float *__restrict__ dout,
+                                                                        const float *__restrict__ qkv,
+                                                                        const float *__restrict__ lse,
+                                                                        const float *__restrict__ Dbuf, int T, int C,
+                                                                        int NH, int BH, float scale) {
+    constexpr int KS = HD / 4;   // k steps of the s and dp products: lane group c takes head dims KS c ..
+    constexpr int NB = HD / 16;  // 16-column blocks of dk and dv: column j of block nb is head dim NB j + nb
+    constexpr int CH = HD / 4;        // 16-byte chunks per tile row
+    constexpr int PC = CH + 1;        // chunks per LDS row: one of padding
+    constexpr int P = 4 * PC;         // LDS row pitch in floats
+    constexpr int NI = (TB * PC + 63) / 64;  // 64-lane loads per tile
+    constexpr int TS = 64 * NI * 4;   // floats per tile buffer (the last load's tail is slack)
+    // Q and dO tiles of TB queries (rows of HD floats, P apart, so that the
+    // reads below meet every bank evenly), and [lse of the TB queries | their
+    // D]; two buffers, in separate arrays: the next block's tiles are loaded
+    // into one while the other is read, and one barrier per block suffices
+    // (one array: every LDS read is a per-lane base plus a constant offset)
+    // The key block's k rows (QBLK rows, P apart): one 64-lane load per 64 chunk positions.
+    constexpr int NKI = (QBLK * PC + 63) / 64;
+    constexpr int KT = 64 * NKI * 4;
+    // buffer b: Q at 2 TS b, dO at 2 TS b + TS, [lse | D] at 4 TS + 2 TB b; the
+    // k rows at 4 TS + 4 TB
+    __shared__ __attribute__((aligned(16))) float sm[4 * TS + 4 * TB + KT];
+    float *const Kt = sm + 4 * TS + 4 * TB;
+    // (the wavefront index as a scalar: everything derived from it stays in scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane >> 4, j = lane & 15;
     const int G = gridDim.x, g = xcd_run(blockIdx.x, G);
     const int nkb = (T + QBLK - 1) / QBLK, W1 = kq_start(nkb, T);
     const long long W = (long long)BH * W1;
     const long long lo_g = range_lo(g, W, G), hi_g = range_lo(g + 1, W, G);
     const long long rs = 3LL * C;
     const int Tp = (T + 3) & ~3;  // ds row pitch
-    TileLoader<HD, TB> lq, lo;
-    // lse and D of a block's queries (threads tid < TB), loaded with its tiles
-    float lse_next = 0.0f, d_next = 0.0f;
-    bool ld_ok = false;
-    auto load_rows = [&](int bh, int t0) {
+    // Loads of the tiles of the block of queries t0 .. t0 + TB - 1 into buffer
+    // BUF: load I < NI of the Q tile (I >= NI: of the dO tile) fills chunk
+    // positions 64 I .. 64 I + 63 of its buffer (row p / PC, chunk p % PC) and
+    // is made by wavefront I % NWB; the lse and D values by the last
+    // wavefront.  A padding chunk or a position past the tile reads a valid
+    // chunk of the tile's rows and is never read back; a row past T reads row
+    // T - 1: the probabilities of such rows are masked to zero, so that their
+    // values never reach a result.  Offsets are 32-bit from the (batch, head)
+    // bases (a batch's rows span fewer than 2^31 floats).
+    auto issue = [&](int buf, int bh, int t0) {
+        float *const Qd = sm + 2 * TS * buf, *const Od = Qd + TS, *const Ld = sm + 4 * TS + 2 * TB * buf;
         const int b = bh / NH, hd_off = (bh % NH) * HD;
-        lq.load(qkv + (long long)b * T * rs + hd_off, rs, t0, T, tid);
-        lo.load(dout + (long long)b * T * C + hd_off, C, t0, T, tid);
-        ld_ok = tid < TB && t0 + tid < T;
-        lse_next = lse[(long long)bh * T + (ld_ok ? t0 + tid : 0)];
-        d_next = Dbuf[(long long)bh * T + (ld_ok ? t0 + tid : 0)];
-    };
-    auto store_rows = [&](int buf) {
-        lq.store(Qs + buf * TB * P, P, tid);
-        lo.store(Os + buf * TB * P, P, tid);
-        if (tid < TB) {
-            Ls[buf * TB + tid] = ld_ok ? lse_next * LOG2E : 0.0f;
-            Ds[buf * TB + tid] = ld_ok ? d_next : 0.0f;
+        // scalar bases and 32-bit per-lane byte offsets: no per-lane pointers held across the loop
+        const char *const qbase = (const char *)(qkv + (long long)b * T * rs + hd_off);
+        const char *const obase = (const char *)(dout + (long long)b * T * C + hd_off);
+        // the lane's positions are formed here on every call (an opaque copy of the
+        // lane index): hoisted out of the loop they would be held, or spilled, throughout
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int I0 = 0; I0 < 2 * NI; I0 += NWB) {
+            const int I = I0 + wave;
+            const int inst = I < NI ? I : I - NI;
+            const int p = 64 * inst + ln, t = min(p / PC, TB - 1), k = min(p % PC, CH - 1);
+            const int tg = min(t0 + t, T - 1);
+            if (I < NI) {
+                const unsigned off = (unsigned)(tg * (int)rs + 4 * k) * 4u;
+                __builtin_amdgcn_global_load_lds(qbase + off, (lds_void *)(Qd + 256 * inst), 16, 0, 0);
+            } else if (I < 2 * NI) {
+                const unsigned off = (unsigned)(tg * C + 4 * k) * 4u;
+                __builtin_amdgcn_global_load_lds(obase + off, (lds_void *)(Od + 256 * inst), 16, 0, 0);
+            }
+        }
+        if (wave == NWB - 1) {
+            const unsigned off = (unsigned)(min(t0 + (ln & 31), T - 1)) * 4u;
+            const char *const lbase = (const char *)(lse + (long long)bh * T);
+            const char *const dbase = (const char *)(Dbuf + (long long)bh * T);
+            if (ln < 32) __builtin_amdgcn_global_load_lds(lbase + off, (lds_void *)Ld, 4, 0, 0);
+            else __builtin_amdgcn_global_load_lds(dbase + off, (lds_void *)Ld, 4, 0, 0);
         }
     };
+    // this wavefront's tile loads have landed (other wavefronts': after the barrier that follows)
+    auto loads_done = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
     // The segment that starts at iteration `it`: (batch, head), key block and
     // its query blocks [qfirst, qend).
     struct Seg {
@@ -489,26 +538,34 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         sg.qend = (int)min((long long)kq_blocks(sg.kb, T), sg.qfirst + (hi_g - it));
         return sg;
     };
-    // A segment's K and V rows (this lane's key, half the head dims per lane
-    // half; a key past T reads row T - 1 and is zeroed when the segment
-    // starts) and its first Q / dO tile are requested before the previous
+    // A segment's k and v rows (this lane's key j, head dims KS c ..; a key
+    // past T reads row T - 1 and is zeroed when the segment starts) and its
+    // first Q / dO tiles (into buffer 0) are requested before the previous
     // segment's dk and dv are stored, so that their latency overlaps those stores.
-    float kf[HD / 2], vf[HD / 2];
+    // (the k rows go to LDS, the v rows to registers: both in registers would
+    // not leave room for four wavefronts per SIMD)
+    float vf[KS];
     auto request = [&](const Seg &sg) {
         const int b = sg.bh / NH, hd_off = (sg.bh % NH) * HD;
         const float *qb_ptr = qkv + (long long)b * T * rs + hd_off;
-        const int uk = sg.kb * QBLK + wave * QW + l32, uc = uk < T ? uk : T - 1;
+        const int uk = sg.kb * QBLK + wave * KW + j, uc = uk < T ? uk : T - 1;
 #pragma unroll
-        for (int j4 = 0; j4 < HD / 8; j4++) {
-            const floatx4 k = *(const floatx4 *)(qb_ptr + C + (long long)uc * rs + h * (HD / 2) + 4 * j4);
-            const floatx4 v = *(const floatx4 *)(qb_ptr + 2 * C + (long long)uc * rs + h * (HD / 2) + 4 * j4);
+        for (int m = 0; m < KS / 4; m++) {
+            const floatx4 v = *(const floatx4 *)(qb_ptr + 2 * C + (long long)uc * rs + KS * c + 4 * m);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                kf[4 * j4 + e] = k[e];
-                vf[4 * j4 + e] = v[e];
-            }
+            for (int e = 0; e < 4; e++) vf[4 * m + e] = v[e];
         }
-        load_rows(sg.bh, sg.kb * QBLK + sg.qfirst * TB);
+        // the key block's k rows: row p / PC, chunk p % PC of position p (a padding
+        // chunk reads a valid chunk; a row past T reads row T - 1: its scores are masked)
+        const char *const kbase = (const char *)(qb_ptr + C);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        for (int I = wave; I < NKI; I += NWB) {
+            const int p = 64 * I + ln, t = p / PC, k = min(p % PC, CH - 1);
+            const unsigned off = (unsigned)(min(sg.kb * QBLK + t, T - 1) * (int)rs + 4 * k) * 4u;
+            __builtin_amdgcn_global_load_lds(kbase + off, (lds_void *)(Kt + 256 * I), 16, 0, 0);
+        }
+        issue(0, sg.bh, sg.kb * QBLK + sg.qfirst * TB);
     };
     long long it = lo_g;
     Seg sg = seg_at(it);
@@ -519,130 +576,121 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
         const int slot = 2 * g + (it == lo_g ? 0 : 1);
         const int b = bh / NH, hd_off = (bh % NH) * HD;
         const int u0w = kb * QBLK;
-        const int u0 = u0w + wave * QW, u = u0 + l32;
-        // K pre-multiplied by scale log2(e); keys past T contribute nothing
+        const int u0 = u0w + wave * KW, u = u0 + j;
+        // keys past T contribute nothing
 #pragma unroll
-        for (int i = 0; i < HD / 2; i++) {
-            kf[i] = u < T ? kf[i] * (scale * LOG2E) : 0.0f;
-            vf[i] = u < T ? vf[i] : 0.0f;
-        }
-        floatx16 dk[HeadBlocks<HD>::N], dv[HeadBlocks<HD>::N];
+        for (int i = 0; i < KS; i++) vf[i] = u < T ? vf[i] : 0.0f;
+        const float sl2e = scale * LOG2E;  // scores in base 2
+        floatx4 dk[NB], dv[NB];
 #pragma unroll
-        for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) dk[nd] = dv[nd] = zero16();
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) dk[nb][r] = dv[nb][r] = 0.0f;
 
         const int tc0 = u0w + qfirst * TB, tc1 = min(T, u0w + qend * TB);
-        // every wavefront is past the previous segment's last barrier: both buffers are free
-        store_rows(0);
+        // ds[t][u] of register r of half qh: query t0 + 16 qh + 4 c + r, key u;
+        // a 32-bit offset from the head's ds matrix (T Tp < 2^31).  Rows are Tp
+        // floats apart; columns T .. Tp - 1 take the zeros of the keys past T,
+        // and nothing is written at or past Tp or at rows past T.
+        float *const dsh = dsout + (long long)bh * T * Tp;
+        const bool col_ok = u < Tp;
+        // the segment's first tiles (buffer 0) were requested with its k and v rows
+        loads_done();
         __syncthreads();
+        // blocks of TB queries, each from buffer cur (its tiles were requested
+        // before); the next block's tiles go into the other buffer meanwhile
         int cur = 0;
         for (int t0 = tc0; t0 < tc1; t0 += TB, cur ^= 1) {
-            const bool more = t0 + TB < tc1;
-            if (more) load_rows(bh, t0 + TB);
-            const float *const Qc = Qs + cur * TB * P;
-            const float *const Oc = Os + cur * TB * P;
-            const float *const Lc = Ls + cur * TB;
-            const float *const Dc = Ds + cur * TB;
-            const bool edge = t0 + TB > T || u0 + QW > T;
-            // This wave's 32 x 32 block of ds leaves as 16-byte stores: lane l takes
-            // row l / 2, columns 8 i + 4 (l % 2) .. + 3 for i = 0..3 (one base address,
-            // constant offsets).  ds rows are Tp = T rounded up to a multiple of 4
-            // floats apart and u0 % 32 == 0, so a group of 4 columns that starts
-            // below T ends inside its row; columns T..Tp - 1 get the zeros of the
-            // keys past T.
-            const int drow = lane >> 1, dcol = 4 * (lane & 1);
-            float *const dsw = dsout + ((long long)bh * T + t0 + drow) * Tp + u0 + dcol;
-            const bool row_ok = t0 + drow < T;
+            const float *const Qc = sm + 2 * TS * cur, *const Oc = Qc + TS, *const Lc = sm + 4 * TS + 2 * TB * cur;
+            if (t0 + TB < tc1) issue(cur ^ 1, bh, t0 + TB);
+            const bool edge = t0 + TB > T || u0 + KW > T;
+            // (opaque to the compiler: the store addresses are formed from it in
+            // each block instead of being kept as sixteen induction pointers)
+            unsigned dso = (unsigned)((t0 + 4 * c) * Tp + u);
+            asm volatile("" : "+v"(dso));
             if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
                 if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
-                    // (a zero the compiler cannot see as a constant: it would keep a
-                    // zero vector in registers through the whole loop otherwise)
-                    float zf;
-                    asm volatile("v_mov_b32 %0, 0" : "=v"(zf));
-                    const floatx4 z = {zf, zf, zf, zf};
 #pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        if (!edge || (row_ok && u0 + dcol + 8 * i < T)) *(floatx4 *)(dsw + 8 * i) = z;
+                    for (int qh = 0; qh < 2; qh++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            if (!edge || (col_ok && t0 + 16 * qh + 4 * c + r < T))
+                                dsh[dso + (unsigned)((16 * qh + r) * Tp)] = 0.0f;
                 }
             } else {
-            floatx16 s = zero16(), dp = zero16();
+                // The two 16-query halves of the block, one after the other (so that
+                // one half's s and dp are live at a time).
+                const bool mask = t0 < u0 + KW - 1 || edge;  // crosses the diagonal or an end
 #pragma unroll
-            for (int j4 = 0; j4 < HD / 8; j4++) {
-                floatx4 qa = *(const floatx4 *)&Qc[l32 * P + h * (HD / 2) + 4 * j4];
-                floatx4 oa = *(const floatx4 *)&Oc[l32 * P + h * (HD / 2) + 4 * j4];
+                for (int qh = 0; qh < 2; qh++) {
+                    // s = Q K^T and dp = dO V^T: two accumulation chains
+                    floatx4 sv = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], kf[4 * j4 + e], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[e], vf[4 * j4 + e], dp, 0, 0, 0);
-                }
-            }
-            if (t0 < u0 + QW - 1 || edge) {  // crosses the diagonal or an end: mask
+                    for (int m = 0; m < KS / 4; m++) {
+                        const int off = (16 * qh + j) * P + KS * c + 4 * m;
+                        const floatx4 qa = *(const floatx4 *)&Qc[off], oa = *(const floatx4 *)&Oc[off];
+                        const floatx4 ka = *(const floatx4 *)&Kt[(wave * KW + j) * P + KS * c + 4 * m];
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int tl = row_of(r, h), tt = t0 + tl;
-                    const float p = (tt < u || tt >= T || u >= T) ? 0.0f : exp2_fast(s[r] - Lc[tl]);
-                    s[r] = p;                      // p
-                    dp[r] = p * (dp[r] - Dc[tl]);  // ds
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int tl = row_of(r, h);
-                    const float p = exp2_fast(s[r] - Lc[tl]);
-                    s[r] = p;
-                    dp[r] = p * (dp[r] - Dc[tl]);
-                }
-            }
-            // ds[t][u] for the dq product goes through this wave's LDS patch (read
-            // back as rows after the MFMAs below, when their operands are free).
-            // The index is the lane's base plus a constant per register, so that
-            // the constant becomes the instruction's offset.
-            {
-                const int pl = (wave * QW + 4 * h) * PP + l32;
-#pragma unroll
-                for (int r = 0; r < 16; r++) Ps[pl + (8 * (r >> 2) + (r & 3)) * PP] = dp[r];
-            }
-            // registers 4g..4g+3 hold queries 8g + 4h + 0..3; the B operands are
-            // the rows of those queries at this lane's head dim: four 4-byte LDS
-            // reads per 4 MFMAs (LDS reads issue beside the MFMAs of other
-            // wavefronts, so no transposed copy of the tiles is kept)
-            const int bq = 4 * h * P + l32;
-#pragma unroll
-            for (int g = 0; g < 4; g++)
-#pragma unroll
-                for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
-                    const int d = 32 * nd + l32;
-                    floatx4 ob, qv;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        ob[i] = d < HD ? Oc[bq + (8 * g + i) * P + 32 * nd] : 0.0f;
-                        qv[i] = d < HD ? Qc[bq + (8 * g + i) * P + 32 * nd] : 0.0f;
+                        for (int e = 0; e < 4; e++) {
+                            sv = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e], ka[e], sv, 0, 0, 0);
+                            dpv = __builtin_amdgcn_mfma_f32_16x16x4f32(oa[e], vf[4 * m + e], dpv, 0, 0, 0);
+                        }
                     }
+                    // p = 2^(s - lse log2 e) and ds = p (dp - D), in place; the four
+                    // queries of a lane's registers are consecutive: one 16-byte read each
+                    const floatx4 L4 = *(const floatx4 *)&Lc[16 * qh + 4 * c];
+                    const floatx4 D4 = *(const floatx4 *)&Lc[TB + 16 * qh + 4 * c];
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        dv[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[4 * g + i], ob[i], dv[nd], 0, 0, 0);
-                        dk[nd] = __builtin_amdgcn_mfma_f32_32x32x2f32(dp[4 * g + i], qv[i], dk[nd], 0, 0, 0);
+                    for (int r = 0; r < 4; r++) {
+                        const int tt = t0 + 16 * qh + 4 * c + r;
+                        // masked entries take 2^-inf = 0 (a select of the argument, so
+                        // that the exponential is not put under a branch)
+                        // (bitwise operators: no short-circuit branches)
+                        const bool off = mask & ((tt < u) | (tt >= T) | (u >= T));
+                        const float x = off ? -INFINITY : sv[r] * sl2e - L4[r] * LOG2E;
+                        const float p = exp2_fast(x);
+                        sv[r] = p;
+                        dpv[r] = p * (dpv[r] - D4[r]);
+                    }
+                    if (!edge) {
+#pragma unroll
+                        for (int r = 0; r < 4; r++) dsh[dso + (unsigned)((16 * qh + r) * Tp)] = dpv[r];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            if (col_ok && t0 + 16 * qh + 4 * c + r < T) dsh[dso + (unsigned)((16 * qh + r) * Tp)] = dpv[r];
+                    }
+                    // dv[u][d] += sum_t p[t][u] dO[t][d], dk[u][d] += sum_t ds[t][u] Q[t][d]:
+                    // register r is the A operand for the queries 16 qh + 4 c' + r
+                    // (c' = 0..3, one per lane group); the B operands are those
+                    // queries' rows at head dims NB j .. NB j + NB - 1
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int off = (16 * qh + 4 * c + r) * P + NB * j;
+                        float ob[NB], qv[NB];
+                        if constexpr (NB == 4) {
+                            const floatx4 o4 = *(const floatx4 *)&Oc[off], q4 = *(const floatx4 *)&Qc[off];
+#pragma unroll
+                            for (int nb = 0; nb < 4; nb++) {
+                                ob[nb] = o4[nb];
+                                qv[nb] = q4[nb];
+                            }
+                        } else {
+#pragma unroll
+                            for (int nb = 0; nb < NB; nb++) {
+                                ob[nb] = Oc[off + nb];
+                                qv[nb] = Qc[off + nb];
+                            }
+                        }
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb++) {
+                            dv[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv[r], ob[nb], dv[nb], 0, 0, 0);
+                            dk[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(dpv[r], qv[nb], dk[nb], 0, 0, 0);
+                        }
                     }
                 }
-            {
-                // the patch is this wavefront's alone: order its LDS writes before the reads
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const int pr = (wave * QW + drow) * PP + dcol;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const floatx4 v = *(const floatx4 *)&Ps[pr + 8 * i];
-                    if (!edge || (row_ok && u0 + dcol + 8 * i < T)) *(floatx4 *)(dsw + 8 * i) = v;
-                }
-                // and the reads before the next iteration's writes
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            }
             }  // keys after some queries of the block
-            // the next block's tiles into the other buffer (last read in the
-            // previous iteration, before its barrier), then one barrier
-            if (more) store_rows(cur ^ 1);
+            loads_done();
             __syncthreads();
         }
         // the next segment's operands go out before this one's results
@@ -651,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             sg = seg_at(nxt);
             request(sg);
         }
-        // lane holds head dim 32nd + l32 of keys u0 + row_of(r, h): row-contiguous across lanes
+        // register r of block nb: key u0 + 4 c + r, head dim NB j + nb
         float *dkb, *dvb;
         long long krs;
         if (whole) {
@@ -664,15 +712,19 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(float *__restric
             krs = HD;
         }
 #pragma unroll
-        for (int nd = 0; nd < HeadBlocks<HD>::N; nd++) {
-            const int d = 32 * nd + l32;
-            if (d >= HD) continue;
+        for (int r = 0; r < 4; r++) {
+            const int uu = u0 + 4 * c + r;
+            if (uu < T) {
+                float *const pk = dkb + (long long)uu * krs + NB * j, *const pv = dvb + (long long)uu * krs + NB * j;
+                if constexpr (NB == 4) {
+                    *(floatx4 *)pk = floatx4{dk[0][r], dk[1][r], dk[2][r], dk[3][r]} * scale;
+                    *(floatx4 *)pv = floatx4{dv[0][r], dv[1][r], dv[2][r], dv[3][r]};
+                } else {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int uu = u0 + row_of(r, h);
-                if (uu < T) {
-                    dkb[(long long)uu * krs + d] = dk[nd][r] * scale;
-                    dvb[(long long)uu * krs + d] = dv[nd][r];
+                    for (int nb = 0; nb < NB; nb++) {
+                        pk[nb] = dk[nb][r] * scale;
+                        pv[nb] = dv[nb][r];
+                    }
                 }
             }
         }
@@ -815,7 +867,7 @@ hipError_t launch_bwd_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dou
     if (e != hipSuccess) return e;
     const int G = dkdv_groups(B, T, NH, HD);
     float *ds = ws, *kvws = ws + ds_floats(B, T, NH);
-    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, dim3(G), dim3(256), 0, s, dqkv, kvws, ds, dout, qkv, lse,
+    hipLaunchKernelGGL(flash_bwd_dkdv_kernel<HD>, dim3(G), dim3(BWD_THREADS), 0, s, dqkv, kvws, ds, dout, qkv, lse,
                        (const float *)Dbuf, T, C, NH, B * NH, 1.0f / sqrtf((float)HD));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
