@@ -188,7 +188,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         }
     };
     auto lstore = [&]() {
-        if (!AK && do_colsum) {
+        // (a scalar condition: the sums are skipped, not computed and discarded,
+        // by the tiles that do not keep them)
+        if (!AK && __builtin_amdgcn_readfirstlane((int)do_colsum)) {
 #pragma unroll
             for (int i = 0; i < A_F4; i++) csum += ra[i];
         }
@@ -280,17 +282,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         // the other way round).
         constexpr bool kEvenA = !BKC && GEMM_THREADS % (AK ? BK / 4 : BM / 4) == 0;
         constexpr bool kEvenB = !BKC && GEMM_THREADS % (BN / 4) == 0;
-        const float *const pa = AK ? A + (long long)(m0 + tid / (BK / 4)) * lda + 4 * (tid % (BK / 4))
-                                   : A + (long long)(tid / (BM / 4)) * lda + m0 + 4 * (tid % (BM / 4));
-        const float *const pb = BKC ? B + (long long)(n0 + tid / (BK / 4)) * ldb + 4 * (tid % (BK / 4))
-                                    : B + (long long)(tid / (BN / 4)) * ldb + n0 + 4 * (tid % (BN / 4));
+        // The per-thread part of that address is a 32-bit byte offset (the same
+        // for every slice and load), the rest a scalar base (tile origin, slice
+        // and load index): the loads then take no vector instructions for their
+        // addresses, which would take issue cycles from the matrix unit.
+        const unsigned va = (unsigned)(4 * (AK ? (long long)(tid / (BK / 4)) * lda + 4 * (tid % (BK / 4))
+                                               : (long long)(tid / (BM / 4)) * lda + 4 * (tid % (BM / 4))));
+        const unsigned vb = (unsigned)(4 * (BKC ? (long long)(tid / (BK / 4)) * ldb + 4 * (tid % (BK / 4))
+                                                : (long long)(tid / (BN / 4)) * ldb + 4 * (tid % (BN / 4))));
+        const char *const a0 = (const char *)(AK ? A + (long long)m0 * lda : A + m0);
+        const char *const b0 = (const char *)(BKC ? B + (long long)n0 * ldb : B + n0);
+        // (buffer loads: a resource per slice whose base is the slice origin, a
+        // scalar offset per load, the thread's offset; all offsets stay small)
         auto gload_full = [&](int k0) {
+            const auto ar = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a0 + 4 * (AK ? (long long)k0 : (long long)k0 * lda)), (short)0, -1, 0x00020000);
+            const auto br = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(b0 + 4 * (BKC ? (long long)k0 : (long long)k0 * ldb)), (short)0, -1, 0x00020000);
 #pragma unroll
             for (int i = 0; i < A_F4; i++) {
                 if constexpr (kEvenA) {
-                    const long long off = AK ? (long long)(GEMM_THREADS / (BK / 4)) * i * lda + k0
-                                             : ((long long)(GEMM_THREADS / (BM / 4)) * i + k0) * lda;
-                    ra[i] = *(const floatx4 *)(pa + off);
+                    const int so = (int)(4 * (long long)(GEMM_THREADS / (AK ? BK / 4 : BM / 4)) * i * lda);
+                    ra[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ar, va, so, 0));
                 } else {
                     const int f = tid + GEMM_THREADS * i;
                     const int gm = AK ? m0 + f / (BK / 4) : m0 + 4 * (f % (BM / 4));
@@ -301,9 +314,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
 #pragma unroll
             for (int i = 0; i < B_F4; i++) {
                 if constexpr (kEvenB) {
-                    const long long off = BKC ? (long long)(GEMM_THREADS / (BK / 4)) * i * ldb + k0
-                                              : ((long long)(GEMM_THREADS / (BN / 4)) * i + k0) * ldb;
-                    rb[i] = *(const floatx4 *)(pb + off);
+                    const int so = (int)(4 * (long long)(GEMM_THREADS / (BKC ? BK / 4 : BN / 4)) * i * ldb);
+                    rb[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(br, vb, so, 0));
                 } else {
                     const int f = tid + GEMM_THREADS * i;
                     const int gn = BKC ? n0 + f / (BK / 4) : n0 + 4 * (f % (BN / 4));
@@ -654,7 +666,7 @@ hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream
 // attproj backward: +7 % and +42 %), so that shape keeps the general kernel.
 template <int BM, int BN>
 constexpr bool pair_full_shape() {
-    return !(BM == 128 && BN == 64);
+    return true;
 }
 
 template <int BM, int BN, int BK, int LB>
