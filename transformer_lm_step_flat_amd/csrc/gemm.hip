@@ -140,6 +140,60 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
     floatx4 csum = {0.f, 0.f, 0.f, 0.f};
     const long long lda = p.lda, ldb = p.ldb;
 
+    // Whole-slice loads of a tile inside M x N.  Where GEMM_THREADS is a
+    // multiple of the float4s per row of the staged layout (BK / 4 for a
+    // K-contiguous operand, BM / 4 or BN / 4 otherwise), thread tid's float4
+    // number i (f = tid + 256 i) sits at
+    // a per-thread address plus an offset common to the workgroup, so one
+    // pointer per operand and thread can serve every load.  That form is
+    // used when B is MN-contiguous (the weight- and input-gradient products);
+    // with both operands K-contiguous (the forward products) an address per
+    // load measured faster (fc forward -3 %; the gradient pairs +1 to 8 %
+    // the other way round).
+    constexpr bool kEvenA = !BKC && GEMM_THREADS % (AK ? BK / 4 : BM / 4) == 0;
+    constexpr bool kEvenB = !BKC && GEMM_THREADS % (BN / 4) == 0;
+    // The per-thread part of that address is a 32-bit byte offset (the same
+    // for every slice and load), the rest a scalar base (tile origin, slice
+    // and load index): the loads then take no vector instructions for their
+    // addresses, which would take issue cycles from the matrix unit.
+    const unsigned va = (unsigned)(4 * (AK ? (long long)(tid / (BK / 4)) * lda + 4 * (tid % (BK / 4))
+                                           : (long long)(tid / (BM / 4)) * lda + 4 * (tid % (BM / 4))));
+    const unsigned vb = (unsigned)(4 * (BKC ? (long long)(tid / (BK / 4)) * ldb + 4 * (tid % (BK / 4))
+                                            : (long long)(tid / (BN / 4)) * ldb + 4 * (tid % (BN / 4))));
+    const char *const a0 = (const char *)(AK ? A + (long long)m0 * lda : A + m0);
+    const char *const b0 = (const char *)(BKC ? B + (long long)n0 * ldb : B + n0);
+    // (buffer loads: a resource per slice whose base is the slice origin, a
+    // scalar offset per load, the thread's offset; all offsets stay small)
+    auto fast_load = [&](int k0) {
+        const auto ar = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a0 + 4 * (AK ? (long long)k0 : (long long)k0 * lda)), (short)0, -1, 0x00020000);
+        const auto br = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(b0 + 4 * (BKC ? (long long)k0 : (long long)k0 * ldb)), (short)0, -1, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < A_F4; i++) {
+            if constexpr (kEvenA) {
+                const int so = (int)(4 * (long long)(GEMM_THREADS / (AK ? BK / 4 : BM / 4)) * i * lda);
+                ra[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ar, va, so, 0));
+            } else {
+                const int f = tid + GEMM_THREADS * i;
+                const int gm = AK ? m0 + f / (BK / 4) : m0 + 4 * (f % (BM / 4));
+                const int gk = AK ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BM / 4);
+                ra[i] = *(const floatx4 *)(AK ? A + gm * lda + gk : A + gk * lda + gm);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_F4; i++) {
+            if constexpr (kEvenB) {
+                const int so = (int)(4 * (long long)(GEMM_THREADS / (BKC ? BK / 4 : BN / 4)) * i * ldb);
+                rb[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(br, vb, so, 0));
+            } else {
+                const int f = tid + GEMM_THREADS * i;
+                const int gn = BKC ? n0 + f / (BK / 4) : n0 + 4 * (f % (BN / 4));
+                const int gk = BKC ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BN / 4);
+                rb[i] = *(const floatx4 *)(BKC ? B + gn * ldb + gk : B + gk * ldb + gn);
+            }
+        }
+    };
     // A tile inside M x N whose slice lies inside [kbeg, kend) loads without
     // bounds tests: no predication, no zeroing of the load targets.  Vector
     // ALU and global-memory instructions do not issue on a SIMD while another
@@ -148,20 +202,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
     const bool interior = m0 + BM <= M && n0 + BN <= N;
     auto gload = [&](int k0) {
         if (interior && k0 + BK <= kend) {
-#pragma unroll
-            for (int i = 0; i < A_F4; i++) {
-                const int f = tid + GEMM_THREADS * i;
-                const int gm = AK ? m0 + f / (BK / 4) : m0 + 4 * (f % (BM / 4));
-                const int gk = AK ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BM / 4);
-                ra[i] = *(const floatx4 *)(AK ? A + gm * lda + gk : A + gk * lda + gm);
-            }
-#pragma unroll
-            for (int i = 0; i < B_F4; i++) {
-                const int f = tid + GEMM_THREADS * i;
-                const int gn = BKC ? n0 + f / (BK / 4) : n0 + 4 * (f % (BN / 4));
-                const int gk = BKC ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BN / 4);
-                rb[i] = *(const floatx4 *)(BKC ? B + gn * ldb + gk : B + gk * ldb + gn);
-            }
+            fast_load(k0);
             return;
         }
 #pragma unroll
@@ -271,59 +312,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
     };
 
     if constexpr (FULL) {
-        // Full-slice loads.  Where GEMM_THREADS is a multiple of the float4s per
-        // row of the staged layout (BK / 4 for a K-contiguous operand, BM / 4 or
-        // BN / 4 otherwise), thread tid's float4 number i (f = tid + 256 i) sits at
-        // a per-thread address plus an offset common to the workgroup, so one
-        // pointer per operand and thread can serve every load.  That form is
-        // used when B is MN-contiguous (the weight- and input-gradient products);
-        // with both operands K-contiguous (the forward products) an address per
-        // load measured faster (fc forward -3 %; the gradient pairs +1 to 8 %
-        // the other way round).
-        constexpr bool kEvenA = !BKC && GEMM_THREADS % (AK ? BK / 4 : BM / 4) == 0;
-        constexpr bool kEvenB = !BKC && GEMM_THREADS % (BN / 4) == 0;
-        // The per-thread part of that address is a 32-bit byte offset (the same
-        // for every slice and load), the rest a scalar base (tile origin, slice
-        // and load index): the loads then take no vector instructions for their
-        // addresses, which would take issue cycles from the matrix unit.
-        const unsigned va = (unsigned)(4 * (AK ? (long long)(tid / (BK / 4)) * lda + 4 * (tid % (BK / 4))
-                                               : (long long)(tid / (BM / 4)) * lda + 4 * (tid % (BM / 4))));
-        const unsigned vb = (unsigned)(4 * (BKC ? (long long)(tid / (BK / 4)) * ldb + 4 * (tid % (BK / 4))
-                                                : (long long)(tid / (BN / 4)) * ldb + 4 * (tid % (BN / 4))));
-        const char *const a0 = (const char *)(AK ? A + (long long)m0 * lda : A + m0);
-        const char *const b0 = (const char *)(BKC ? B + (long long)n0 * ldb : B + n0);
-        // (buffer loads: a resource per slice whose base is the slice origin, a
-        // scalar offset per load, the thread's offset; all offsets stay small)
-        auto gload_full = [&](int k0) {
-            const auto ar = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(a0 + 4 * (AK ? (long long)k0 : (long long)k0 * lda)), (short)0, -1, 0x00020000);
-            const auto br = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(b0 + 4 * (BKC ? (long long)k0 : (long long)k0 * ldb)), (short)0, -1, 0x00020000);
-#pragma unroll
-            for (int i = 0; i < A_F4; i++) {
-                if constexpr (kEvenA) {
-                    const int so = (int)(4 * (long long)(GEMM_THREADS / (AK ? BK / 4 : BM / 4)) * i * lda);
-                    ra[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ar, va, so, 0));
-                } else {
-                    const int f = tid + GEMM_THREADS * i;
-                    const int gm = AK ? m0 + f / (BK / 4) : m0 + 4 * (f % (BM / 4));
-                    const int gk = AK ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BM / 4);
-                    ra[i] = *(const floatx4 *)(AK ? A + gm * lda + gk : A + gk * lda + gm);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < B_F4; i++) {
-                if constexpr (kEvenB) {
-                    const int so = (int)(4 * (long long)(GEMM_THREADS / (BKC ? BK / 4 : BN / 4)) * i * ldb);
-                    rb[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(br, vb, so, 0));
-                } else {
-                    const int f = tid + GEMM_THREADS * i;
-                    const int gn = BKC ? n0 + f / (BK / 4) : n0 + 4 * (f % (BN / 4));
-                    const int gk = BKC ? k0 + 4 * (f % (BK / 4)) : k0 + f / (BN / 4);
-                    rb[i] = *(const floatx4 *)(BKC ? B + gn * ldb + gk : B + gk * ldb + gn);
-                }
-            }
-        };
         // one slice's MFMAs (the wave priority is raised around them, as in
         // the general loop below)
         auto mfma_slice = [&]() { slice_mfma(); };
@@ -333,13 +321,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tm, int tn, int
         // MFMAs, so that they issue while this wavefront's own MFMAs run
         // instead of waiting behind those of other workgroups.
         int k0 = kbeg;
-        if (kbeg < kend) gload_full(kbeg);
+        if (kbeg < kend) fast_load(kbeg);
         for (; k0 + BK < kend; k0 += BK) {
             __syncthreads();
             lstore();
             __syncthreads();
             __builtin_amdgcn_s_setprio(1);
-            gload_full(k0 + BK);
+            fast_load(k0 + BK);
             mfma_slice();
             constexpr int NMFMA = MI * NI * (PREC == 0 ? BK / 2 : BK / 16);
             constexpr int NPAIR = NMFMA < A_F4 + B_F4 ? NMFMA : A_F4 + B_F4;
