@@ -443,15 +443,14 @@ constexpr int BWD_THREADS = 64 * NWB;  // 512
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// (the body is a device function: a kernel body that names the buffer
+// builtins would fail the host compilation pass, which then drops the launch
+// stub without a diagnostic)
 template <int HD>
-__global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv,
-                                                                        float *__restrict__ ws,
-                                                                        float *__restrict__ dsout,
-                                                                        const float *__restrict__ dout,
-                                                                        const float *__restrict__ qkv,
-                                                                        const float *__restrict__ lse,
-                                                                        const float *__restrict__ Dbuf, int T, int C,
-                                                                        int NH, int BH, float scale) {
+__device__ __forceinline__ void dkdv_body(float *__restrict__ dqkv, float *__restrict__ ws, float *__restrict__ dsout,
+                                          const float *__restrict__ dout, const float *__restrict__ qkv,
+                                          const float *__restrict__ lse, const float *__restrict__ Dbuf, int T, int C,
+                                          int NH, int BH, float scale) {
     constexpr int KS = HD / 4;   // k steps of the s and dp products: lane group c takes head dims KS c ..
     constexpr int NB = HD / 16;  // 16-column blocks of dk and dv: column j of block nb is head dim NB j + nb
     constexpr int CH = HD / 4;        // 16-byte chunks per tile row
@@ -460,18 +459,17 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
     constexpr int NI = (TB * PC + 63) / 64;  // 64-lane loads per tile
     constexpr int TS = 64 * NI * 4;   // floats per tile buffer (the last load's tail is slack)
     // Q and dO tiles of TB queries (rows of HD floats, P apart, so that the
-    // reads below meet every bank evenly), and [lse of the TB queries | their
-    // D]; two buffers, in separate arrays: the next block's tiles are loaded
-    // into one while the other is read, and one barrier per block suffices
-    // (one array: every LDS read is a per-lane base plus a constant offset)
-    // The key block's k rows (QBLK rows, P apart): one 64-lane load per 64 chunk positions.
-    constexpr int NKI = (QBLK * PC + 63) / 64;
+    // reads below meet every bank evenly) and [lse of the TB queries | their
+    // D], two buffers: the next block's tiles are loaded into one while the
+    // other is read, and one barrier per block suffices.  The key block's k
+    // rows (QBLK rows, P apart) follow.  One array: every LDS read is a
+    // per-lane base plus a constant offset.
+    constexpr int NKI = (QBLK * PC + 63) / 64;  // 64-lane loads of the k rows
     constexpr int KT = 64 * NKI * 4;
     // buffer b: Q at 2 TS b, dO at 2 TS b + TS, [lse | D] at 4 TS + 2 TB b; the
     // k rows at 4 TS + 4 TB
     __shared__ __attribute__((aligned(16))) float sm[4 * TS + 4 * TB + KT];
     float *const Kt = sm + 4 * TS + 4 * TB;
-    // (the wavefront index as a scalar: everything derived from it stays in scalar registers)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane >> 4, j = lane & 15;
     const int G = gridDim.x, g = xcd_run(blockIdx.x, G);
@@ -481,44 +479,43 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
     const long long rs = 3LL * C;
     const int Tp = (T + 3) & ~3;  // ds row pitch
     // Loads of the tiles of the block of queries t0 .. t0 + TB - 1 into buffer
-    // BUF: load I < NI of the Q tile (I >= NI: of the dO tile) fills chunk
-    // positions 64 I .. 64 I + 63 of its buffer (row p / PC, chunk p % PC) and
-    // is made by wavefront I % NWB; the lse and D values by the last
-    // wavefront.  A padding chunk or a position past the tile reads a valid
-    // chunk of the tile's rows and is never read back; a row past T reads row
-    // T - 1: the probabilities of such rows are masked to zero, so that their
-    // values never reach a result.  Offsets are 32-bit from the (batch, head)
-    // bases (a batch's rows span fewer than 2^31 floats).
+    // buf, as buffer loads straight into LDS: load I of a tile fills chunk
+    // positions 64 I .. 64 I + 63 of its buffer (row p / PC, chunk p % PC; a
+    // padding chunk or a position past the tile reads a chunk of the tile's
+    // rows and is never read back).  Wavefront w makes load w of the Q and of
+    // the dO tile (wavefront 0 also the loads from NWB on), the last
+    // wavefront the lse and D values.  The resources start at row t0 and end
+    // at row T: rows past T read as zeros.  A lane's offset within a load is
+    // the same for every block: computed once.
+    auto lane_off = [&](int inst, long long stride) {
+        const int p = 64 * inst + lane, t = min(p / PC, TB - 1), k = min(p % PC, CH - 1);
+        return (unsigned)(4 * (t * stride + 4 * k));
+    };
+    const unsigned offq = lane_off(wave, rs), offo = lane_off(wave, C);
     auto issue = [&](int buf, int bh, int t0) {
         float *const Qd = sm + 2 * TS * buf, *const Od = Qd + TS, *const Ld = sm + 4 * TS + 2 * TB * buf;
         const int b = bh / NH, hd_off = (bh % NH) * HD;
-        // scalar bases and 32-bit per-lane byte offsets: no per-lane pointers held across the loop
-        const char *const qbase = (const char *)(qkv + (long long)b * T * rs + hd_off);
-        const char *const obase = (const char *)(dout + (long long)b * T * C + hd_off);
-        // the lane's positions are formed here on every call (an opaque copy of the
-        // lane index): hoisted out of the loop they would be held, or spilled, throughout
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-#pragma unroll
-        for (int I0 = 0; I0 < 2 * NI; I0 += NWB) {
-            const int I = I0 + wave;
-            const int inst = I < NI ? I : I - NI;
-            const int p = 64 * inst + ln, t = min(p / PC, TB - 1), k = min(p % PC, CH - 1);
-            const int tg = min(t0 + t, T - 1);
-            if (I < NI) {
-                const unsigned off = (unsigned)(tg * (int)rs + 4 * k) * 4u;
-                __builtin_amdgcn_global_load_lds(qbase + off, (lds_void *)(Qd + 256 * inst), 16, 0, 0);
-            } else if (I < 2 * NI) {
-                const unsigned off = (unsigned)(tg * C + 4 * k) * 4u;
-                __builtin_amdgcn_global_load_lds(obase + off, (lds_void *)(Od + 256 * inst), 16, 0, 0);
+        const auto qr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(qkv + ((long long)b * T + t0) * rs + hd_off), (short)0, (int)(4 * (T - t0) * rs), 0x00020000);
+        const auto orr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(dout + ((long long)b * T + t0) * C + hd_off), (short)0, 4 * (T - t0) * C, 0x00020000);
+        if (wave < NI) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(Qd + 256 * wave), 16, offq, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_void *)(Od + 256 * wave), 16, offo, 0, 0, 0);
+        }
+        if (wave == 0) {
+            for (int I = NWB; I < NI; I++) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(Qd + 256 * I), 16, lane_off(I, rs), 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_void *)(Od + 256 * I), 16, lane_off(I, C), 0, 0, 0);
             }
         }
         if (wave == NWB - 1) {
-            const unsigned off = (unsigned)(min(t0 + (ln & 31), T - 1)) * 4u;
-            const char *const lbase = (const char *)(lse + (long long)bh * T);
-            const char *const dbase = (const char *)(Dbuf + (long long)bh * T);
-            if (ln < 32) __builtin_amdgcn_global_load_lds(lbase + off, (lds_void *)Ld, 4, 0, 0);
-            else __builtin_amdgcn_global_load_lds(dbase + off, (lds_void *)Ld, 4, 0, 0);
+            const auto lr = __builtin_amdgcn_make_buffer_rsrc((void *)(lse + (long long)bh * T + t0), (short)0,
+                                                              4 * (T - t0), 0x00020000);
+            const auto dr = __builtin_amdgcn_make_buffer_rsrc((void *)(Dbuf + (long long)bh * T + t0), (short)0,
+                                                              4 * (T - t0), 0x00020000);
+            if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void *)Ld, 4, 4 * lane, 0, 0, 0);
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void *)Ld, 4, 4 * (lane - 32), 0, 0, 0);
         }
     };
     // this wavefront's tile loads have landed (other wavefronts': after the barrier that follows)
@@ -588,12 +585,17 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
             for (int r = 0; r < 4; r++) dk[nb][r] = dv[nb][r] = 0.0f;
 
         const int tc0 = u0w + qfirst * TB, tc1 = min(T, u0w + qend * TB);
-        // ds[t][u] of register r of half qh: query t0 + 16 qh + 4 c + r, key u;
-        // a 32-bit offset from the head's ds matrix (T Tp < 2^31).  Rows are Tp
+        // ds[t][u] of register r of half qh: query t0 + 16 qh + 4 c + r, key u,
+        // written with buffer stores into the head's ds matrix (a resource that
+        // ends at row T: rows past T are dropped; T Tp < 2^29).  Rows are Tp
         // floats apart; columns T .. Tp - 1 take the zeros of the keys past T,
-        // and nothing is written at or past Tp or at rows past T.
-        float *const dsh = dsout + (long long)bh * T * Tp;
+        // and nothing is written at or past column Tp.
+        const auto dsr = __builtin_amdgcn_make_buffer_rsrc((void *)(dsout + (long long)bh * T * Tp), (short)0,
+                                                           4 * T * Tp, 0x00020000);
         const bool col_ok = u < Tp;
+        auto ds_store = [&](float v, unsigned voff, int row) {
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), dsr, voff, 4 * row * Tp, 0);
+        };
         // the segment's first tiles (buffer 0) were requested with its k and v rows
         loads_done();
         __syncthreads();
@@ -604,18 +606,15 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
             const float *const Qc = sm + 2 * TS * cur, *const Oc = Qc + TS, *const Lc = sm + 4 * TS + 2 * TB * cur;
             if (t0 + TB < tc1) issue(cur ^ 1, bh, t0 + TB);
             const bool edge = t0 + TB > T || u0 + KW > T;
-            // (opaque to the compiler: the store addresses are formed from it in
-            // each block instead of being kept as sixteen induction pointers)
-            unsigned dso = (unsigned)((t0 + 4 * c) * Tp + u);
-            asm volatile("" : "+v"(dso));
+            // the lane's byte offset of row t0 + 4 c, column u (rows 16 qh + r further
+            // on are the stores' scalar offsets)
+            const unsigned dso = (unsigned)(4 * ((t0 + 4 * c) * Tp + u));
             if (t0 + TB - 1 < u0) {  // every query of the block precedes this wave's keys
-                if (t0 < u0w + QBLK) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
+                if (t0 < u0w + QBLK && col_ok) {  // inside the diagonal 128 x 128 tile: ds = 0 for the dq product
 #pragma unroll
                     for (int qh = 0; qh < 2; qh++)
 #pragma unroll
-                        for (int r = 0; r < 4; r++)
-                            if (!edge || (col_ok && t0 + 16 * qh + 4 * c + r < T))
-                                dsh[dso + (unsigned)((16 * qh + r) * Tp)] = 0.0f;
+                        for (int r = 0; r < 4; r++) ds_store(0.0f, dso, 16 * qh + r);
                 }
             } else {
                 // The two 16-query halves of the block, one after the other (so that
@@ -640,25 +639,30 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
                     // queries of a lane's registers are consecutive: one 16-byte read each
                     const floatx4 L4 = *(const floatx4 *)&Lc[16 * qh + 4 * c];
                     const floatx4 D4 = *(const floatx4 *)&Lc[TB + 16 * qh + 4 * c];
+                    if (mask) {
 #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int tt = t0 + 16 * qh + 4 * c + r;
-                        // masked entries take 2^-inf = 0 (a select of the argument, so
-                        // that the exponential is not put under a branch)
-                        // (bitwise operators: no short-circuit branches)
-                        const bool off = mask & ((tt < u) | (tt >= T) | (u >= T));
-                        const float x = off ? -INFINITY : sv[r] * sl2e - L4[r] * LOG2E;
-                        const float p = exp2_fast(x);
-                        sv[r] = p;
-                        dpv[r] = p * (dpv[r] - D4[r]);
-                    }
-                    if (!edge) {
-#pragma unroll
-                        for (int r = 0; r < 4; r++) dsh[dso + (unsigned)((16 * qh + r) * Tp)] = dpv[r];
+                        for (int r = 0; r < 4; r++) {
+                            const int tt = t0 + 16 * qh + 4 * c + r;
+                            // masked entries take 2^-inf = 0 (a select of the argument, so
+                            // that the exponential is not put under a branch; bitwise
+                            // operators: no short-circuit branches)
+                            const bool off = (tt < u) | (tt >= T) | (u >= T);
+                            const float x = off ? -INFINITY : sv[r] * sl2e - L4[r] * LOG2E;
+                            const float p = exp2_fast(x);
+                            sv[r] = p;
+                            dpv[r] = p * (dpv[r] - D4[r]);
+                        }
                     } else {
 #pragma unroll
-                        for (int r = 0; r < 4; r++)
-                            if (col_ok && t0 + 16 * qh + 4 * c + r < T) dsh[dso + (unsigned)((16 * qh + r) * Tp)] = dpv[r];
+                        for (int r = 0; r < 4; r++) {
+                            const float p = exp2_fast(sv[r] * sl2e - L4[r] * LOG2E);
+                            sv[r] = p;
+                            dpv[r] = p * (dpv[r] - D4[r]);
+                        }
+                    }
+                    if (col_ok) {
+#pragma unroll
+                        for (int r = 0; r < 4; r++) ds_store(dpv[r], dso, 16 * qh + r);
                     }
                     // dv[u][d] += sum_t p[t][u] dO[t][d], dk[u][d] += sum_t ds[t][u] Q[t][d]:
                     // register r is the A operand for the queries 16 qh + 4 c' + r
@@ -731,6 +735,18 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
         if (nxt >= hi_g) break;
         it = nxt;
     }  // segments
+}
+
+template <int HD>
+__global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *__restrict__ dqkv,
+                                                                        float *__restrict__ ws,
+                                                                        float *__restrict__ dsout,
+                                                                        const float *__restrict__ dout,
+                                                                        const float *__restrict__ qkv,
+                                                                        const float *__restrict__ lse,
+                                                                        const float *__restrict__ Dbuf, int T, int C,
+                                                                        int NH, int BH, float scale) {
+    dkdv_body<HD>(dqkv, ws, dsout, dout, qkv, lse, Dbuf, T, C, NH, BH, scale);
 }
 
 // D[bh][t] = dO_t . O_t over the head's HD dims, one thread per (b, t, head):
