@@ -53,35 +53,38 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Load `rows` rows of HD floats (row stride `rs` floats, rows >= nvalid are
-// zero) into registers: thread tid of NT owns float4 number tid + NT*i.  The loads
-// are issued unconditionally (a thread out of range reads row 0, which is
-// always valid) and the zeroing is applied when the tile is stored, so that
-// nothing waits for the loads until then: the next tile is in flight while
-// the current one is consumed.
-template <int HD, int ROWS, int NT = 256>
+// 16 bytes at byte offset voff + soff of base through a buffer resource of
+// nbytes bytes: zeros past nbytes.  (A device function: a kernel body that
+// names the buffer builtins fails the host compilation pass, which then
+// drops the kernel's launch stub without a diagnostic.)
+__device__ __forceinline__ floatx4 buf_load4(const float *base, int nbytes, unsigned voff, int soff) {
+    const auto r = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, nbytes, 0x00020000);
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Load ROWS rows of HD floats (row stride rs floats) from row row0 into
+// registers, rows at or past nrows as zeros: thread tid owns float4 number
+// tid + 256 i, at row tid / (HD / 4) + i 256 / (HD / 4).  Buffer loads: one
+// per-thread offset (the same for every tile), a scalar offset per load, no
+// vector instructions for addresses.  The loads are issued at once and
+// nothing waits for them until the tile is stored, so that the next tile is
+// in flight while the current one is consumed.
+template <int HD, int ROWS>
 struct TileLoader {
-    static constexpr int F4 = ROWS * HD / 4 / NT > 0 ? ROWS * HD / 4 / NT : 1;
+    static constexpr int F4 = ROWS * HD / 4 / 256 > 0 ? ROWS * HD / 4 / 256 : 1;
+    static constexpr int RPI = 256 / (HD / 4);  // rows per load index
     floatx4 r[F4];
-    bool ok[F4];
     __device__ __forceinline__ void load(const float *base, long long rs, int row0, int nrows, int tid) {
+        const unsigned voff = (unsigned)(4 * ((tid / (HD / 4)) * rs + 4 * (tid % (HD / 4))));
+        const int nb = (int)(4 * (nrows - row0) * rs);
 #pragma unroll
-        for (int i = 0; i < F4; i++) {
-            const int f = tid + NT * i;
-            const int row = f / (HD / 4), c4 = f % (HD / 4);
-            ok[i] = f < ROWS * HD / 4 && row0 + row < nrows;
-            r[i] = *(const floatx4 *)(base + (ok[i] ? (long long)(row0 + row) * rs + 4 * c4 : 0));
-        }
-    }
-    __device__ __forceinline__ floatx4 value(int i) const {
-        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-        return ok[i] ? r[i] : z;
+        for (int i = 0; i < F4; i++) r[i] = buf_load4(base + row0 * rs, nb, voff, (int)(4 * i * RPI * rs));
     }
     __device__ __forceinline__ void store(float *lds, int pitch, int tid) const {
 #pragma unroll
         for (int i = 0; i < F4; i++) {
-            int f = tid + NT * i;
-            if (f < ROWS * HD / 4) *(floatx4 *)&lds[(f / (HD / 4)) * pitch + 4 * (f % (HD / 4))] = value(i);
+            const int f = tid + 256 * i;
+            if (f < ROWS * HD / 4) *(floatx4 *)&lds[(f / (HD / 4)) * pitch + 4 * (f % (HD / 4))] = r[i];
         }
     }
 };
@@ -92,29 +95,24 @@ struct TileLoader {
 // lane / 16 (i < HD / 16): the 64 lanes of one transposed store then write
 // 16 rows of 4 columns, each of 32 banks twice (with 4 rows of 16 column
 // groups per store, as in the row-major order, one bank takes 8 lanes).
-// A row past nrows reads row 0 (always valid) and is zeroed when stored.
+// Rows at or past nrows read as zeros (buffer loads, as above).
 template <int HD>
 struct TileLoaderT {
     static constexpr int F4 = HD / 16;
     floatx4 r[F4];
-    bool ok;
     __device__ __forceinline__ void load(const float *base, long long rs, int row0, int nrows, int tid) {
         const int row = 16 * (tid >> 6) + (tid & 15), c0 = (tid >> 4) & 3;
-        ok = row0 + row < nrows;
-        // a 32-bit offset from the workgroup's base (rows < 1024, rs <= 6144): one register
-        const int off = (ok ? (row0 + row) * (int)rs : 0) + 4 * c0;
+        const unsigned voff = (unsigned)(4 * (row * rs + 4 * c0));
+        const int nb = (int)(4 * (nrows - row0) * rs);
 #pragma unroll
-        for (int i = 0; i < F4; i++) r[i] = *(const floatx4 *)(base + off + 16 * i);
+        for (int i = 0; i < F4; i++) r[i] = buf_load4(base + row0 * rs, nb, voff, 64 * i);
     }
     __device__ __forceinline__ void store_t(float *lds, int pitch, int tid) const {
         const int row = 16 * (tid >> 6) + (tid & 15), c0 = (tid >> 4) & 3;
-        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < F4; i++) {
-            const floatx4 v = ok ? r[i] : z;
+        for (int i = 0; i < F4; i++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) lds[(4 * (4 * i + c0) + e) * pitch + row] = v[e];
-        }
+            for (int e = 0; e < 4; e++) lds[(4 * (4 * i + c0) + e) * pitch + row] = r[i][e];
     }
 };
 
@@ -339,10 +337,17 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
             const float2 hp = half_pair(ps);
             ps = hp.x + hp.y;
         }
+        // alpha is exactly 1 for a query whose running maximum did not move: when
+        // that holds for the whole wavefront the rescaling of o is skipped (a
+        // multiplication by 1 either way; the vector instructions it saves would
+        // take issue cycles from the matrix unit)
+        const bool moved = __ballot(mx != m) != 0;
         lsum = lsum * alpha + ps;
         m = mx;
+        if (moved) {
 #pragma unroll
-        for (int md = 0; md < HeadBlocks<HD>::N; md++) o[md] *= alpha;
+            for (int md = 0; md < HeadBlocks<HD>::N; md++) o[md] *= alpha;
+        }
         accum_xt_pt_any<HD>(o, Vs, s, l32, h);
     }
     __syncthreads();  // the K/V tiles become per-wave transpose space
