@@ -173,7 +173,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, steps: int, copy_mib: int, comma
     ck = max(cands, key=lambda k: max(fetch.get(k, [0])))
     f_scale = copy_kib / max(fetch[ck])
     w_scale = copy_kib / max(write[ck])
-    lib_kernels = [k for k in dur if "elementwise" not in k and "rocclr" not in k]
+    # (the step's kernels: not the copy, the runtime's fills or the matrix-unit peak probe)
+    lib_kernels = [k for k in dur if "elementwise" not in k and "rocclr" not in k and "probe" not in k]
     tot = {k: sum(dur[k]) for k in lib_kernels}
     dom = max(tot, key=tot.get)
     rows = []

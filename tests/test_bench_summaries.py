@@ -49,6 +49,8 @@ def test_traffic_summary_scales_by_the_copy_and_gates_on_sources(bench, tmp_path
         write.append((PAIR, 500.0, 10**7 * i, 10**7 * (i + 1)))
     fetch.append(("adamw_kernel", 9000.0, 0, 10**6))  # larger traffic, shorter in total: not dominant
     write.append(("adamw_kernel", 9000.0, 0, 10**6))
+    fetch.append(("mfma_probe_kernel", 0.0, 0, 10**8))  # the peak probe, longest of all, is not a step kernel
+    write.append(("mfma_probe_kernel", 0.0, 0, 10**8))
     write_pmc(tmp_path / "f.csv", "FETCH_SIZE", fetch)
     write_pmc(tmp_path / "w.csv", "WRITE_SIZE", write)
     bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 3, 1024, "cmd", "124m")
