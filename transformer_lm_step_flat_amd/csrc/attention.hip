@@ -627,6 +627,15 @@ __device__ __forceinline__ void dkdv_body(float *__restrict__ dqkv, float *__res
                 const bool mask = t0 < u0 + KW - 1 || edge;  // crosses the diagonal or an end
 #pragma unroll
                 for (int qh = 0; qh < 2; qh++) {
+                    // the first half when all its 16 queries precede this wave's keys (the
+                    // block's second half starts the diagonal): p = ds = 0, stored as such
+                    if (qh == 0 && t0 + 16 <= u0) {
+                        if (col_ok) {
+#pragma unroll
+                            for (int r = 0; r < 4; r++) ds_store(0.0f, dso, r);
+                        }
+                        continue;
+                    }
                     // s = Q K^T and dp = dO V^T: two accumulation chains
                     floatx4 sv = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -754,26 +763,34 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
     dkdv_body<HD>(dqkv, ws, dsout, dout, qkv, lse, Dbuf, T, C, NH, BH, scale);
 }
 
-// D[bh][t] = dO_t . O_t over the head's HD dims, one thread per (b, t, head):
-// consecutive threads take consecutive heads of a row.
+// D[bh][t] = dO_t . O_t over the head's HD dims: HD / 4 consecutive threads
+// per (b, t, head), one 16-byte piece of each operand each (coalesced rows,
+// many loads in flight), summed across those lanes by a fixed xor
+// butterfly.  Every lane takes part in the exchanges; lanes past the end
+// contribute zeros and write nothing.
 template <int HD>
 __global__ __launch_bounds__(256) void flash_bwd_D_kernel(float *__restrict__ Dbuf, const float *__restrict__ dout,
                                                           const float *__restrict__ out, int T, int C, int NH,
                                                           long long rows) {
+    constexpr int G = HD / 4;
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= rows * NH) return;
-    const long long bt = i / NH;
-    const int hh = (int)(i % NH);
-    const floatx4 *a = (const floatx4 *)(dout + bt * C + hh * HD);
-    const floatx4 *o = (const floatx4 *)(out + bt * C + hh * HD);
+    const bool ok = i < rows * NH * G;
+    const long long r = ok ? i / G : 0;
+    const int d4 = (int)(i % G);
+    const long long bt = r / NH;
+    const int hh = (int)(r % NH);
     float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < HD / 4; j++) {
-        const floatx4 x = a[j], y = o[j];
-        acc += (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
+    if (ok) {
+        const floatx4 x = *(const floatx4 *)(dout + bt * C + hh * HD + 4 * d4);
+        const floatx4 y = *(const floatx4 *)(out + bt * C + hh * HD + 4 * d4);
+        acc = (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
     }
-    const long long b = bt / T, t = bt % T;
-    Dbuf[(b * NH + hh) * T + t] = acc;
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o);
+    if (ok && d4 == 0) {
+        const long long b = bt / T, t = bt % T;
+        Dbuf[(b * NH + hh) * T + t] = acc;
+    }
 }
 
 // Sum the partials of dk and dv of the key blocks that were split between
@@ -882,7 +899,7 @@ hipError_t launch_bwd_dkdv(float *dqkv, float *ws, float *Dbuf, const float *dou
         audit(au, "flash_bwd_sum_kernel", "dqkv", dqkv, 3 * BTC, true);
         return hipSuccess;
     }
-    hipLaunchKernelGGL(flash_bwd_D_kernel<HD>, dim3((unsigned)((rows * NH + 255) / 256)), dim3(256), 0, s, Dbuf, dout,
+    hipLaunchKernelGGL(flash_bwd_D_kernel<HD>, dim3((unsigned)((rows * NH * (HD / 4) + 255) / 256)), dim3(256), 0, s, Dbuf, dout,
                        out, T, C, NH, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
