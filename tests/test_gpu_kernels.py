@@ -91,7 +91,8 @@ def test_linear_full_head_shape_sampled_rows(g, oracle_lib):
 
 # ---------------------------------------------------------------- layernorm
 
-@pytest.mark.parametrize("N,C", [(64, 64), (37, 20), (200, 768), (33, 1600), (4096, 768)])
+@pytest.mark.parametrize("N,C", [(64, 64), (37, 20), (200, 768), (33, 1600), (4096, 768), (1000, 1600), (129, 1540),
+                                 (300, 2048)])
 def test_layernorm(g, oracle_lib, N, C):
     import torch
     rng = np.random.default_rng(N + C)

@@ -366,7 +366,9 @@ __global__ __launch_bounds__(256, 3) void flash_fwd_kernel(float *__restrict__ o
 
 // Merge the chunk partials of the forward: lse = log sum_c exp(lse_c);
 // out = sum_c exp(lse_c - lse) out_c (chunks in order).  One thread per
-// (row, 4 head dims) of the blocks that were split.
+// (row, 4 head dims) of the blocks that were split.  Up to MCH chunks (all of
+// them for T <= MCH KCH) are loaded at once, more in a loop.
+constexpr int MCH = 4;
 template <int HD>
 __global__ __launch_bounds__(256) void flash_fwd_merge_kernel(float *__restrict__ out, float *__restrict__ lse,
                                                               const float *__restrict__ ws,
@@ -383,15 +385,40 @@ __global__ __launch_bounds__(256) void flash_fwd_merge_kernel(float *__restrict_
     for (int q = 0; q < qb; q++) first += q_items(q, T);
     const long long base = (long long)bh * items + first;
     const int row = t % QBLK;
-    float mx = -INFINITY;
-    for (int c = 0; c < nch; c++) mx = fmaxf(mx, wlse[(base + c) * QBLK + row]);
-    float ssum = 0.0f;
-    for (int c = 0; c < nch; c++) ssum += __expf(wlse[(base + c) * QBLK + row] - mx);
-    const float L = mx + __logf(ssum);
+    float L;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nch; c++) {
-        const float w = __expf(wlse[(base + c) * QBLK + row] - L);
-        acc += w * *(const floatx4 *)(ws + ((base + c) * QBLK + row) * HD + 4 * d4);
+    if (nch <= MCH) {
+        // every chunk's lse and partial row requested before the first use
+        float l[MCH];
+        floatx4 v[MCH];
+#pragma unroll
+        for (int c = 0; c < MCH; c++)
+            if (c < nch) {
+                l[c] = wlse[(base + c) * QBLK + row];
+                v[c] = *(const floatx4 *)(ws + ((base + c) * QBLK + row) * HD + 4 * d4);
+            }
+        float mx = l[0];
+#pragma unroll
+        for (int c = 1; c < MCH; c++)
+            if (c < nch) mx = fmaxf(mx, l[c]);
+        float ssum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MCH; c++)
+            if (c < nch) ssum += __expf(l[c] - mx);
+        L = mx + __logf(ssum);
+#pragma unroll
+        for (int c = 0; c < MCH; c++)
+            if (c < nch) acc += __expf(l[c] - L) * v[c];
+    } else {
+        float mx = -INFINITY;
+        for (int c = 0; c < nch; c++) mx = fmaxf(mx, wlse[(base + c) * QBLK + row]);
+        float ssum = 0.0f;
+        for (int c = 0; c < nch; c++) ssum += __expf(wlse[(base + c) * QBLK + row] - mx);
+        L = mx + __logf(ssum);
+        for (int c = 0; c < nch; c++) {
+            const float w = __expf(wlse[(base + c) * QBLK + row] - L);
+            acc += w * *(const floatx4 *)(ws + ((base + c) * QBLK + row) * HD + 4 * d4);
+        }
     }
     const int b = bh / NH, hd_off = (bh % NH) * HD;
     *(floatx4 *)(out + ((long long)b * T + t) * C + hd_off + 4 * d4) = acc;
@@ -765,8 +792,8 @@ __global__ __launch_bounds__(BWD_THREADS, 4) void flash_bwd_dkdv_kernel(float *_
 
 // D[bh][t] = dO_t . O_t over the head's HD dims: HD / 4 consecutive threads
 // per (b, t, head), one 16-byte piece of each operand each (coalesced rows,
-// many loads in flight), summed across those lanes by a fixed xor
-// butterfly.  Every lane takes part in the exchanges; lanes past the end
+// many loads in flight), summed across those lanes by DPP exchanges in a
+// fixed order.  Every lane takes part in the exchanges; lanes past the end
 // contribute zeros and write nothing.
 template <int HD>
 __global__ __launch_bounds__(256) void flash_bwd_D_kernel(float *__restrict__ Dbuf, const float *__restrict__ dout,
@@ -785,8 +812,12 @@ __global__ __launch_bounds__(256) void flash_bwd_D_kernel(float *__restrict__ Db
         const floatx4 y = *(const floatx4 *)(out + bt * C + hh * HD + 4 * d4);
         acc = (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
     }
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o);
+    // sum over the G = 4, 8 or 16 lanes of the row (an aligned quad, half-row
+    // or row of 16 lanes): DPP exchanges, every lane active
+    acc += dpp_move<0xB1>(acc);
+    acc += dpp_move<0x4E>(acc);
+    if (G >= 8) acc += dpp_move<0x141>(acc);
+    if (G >= 16) acc += dpp_move<0x140>(acc);
     if (ok && d4 == 0) {
         const long long b = bt / T, t = bt % T;
         Dbuf[(b * NH + hh) * T + t] = acc;

@@ -170,8 +170,10 @@ __global__ void encoder_forward_kernel(float *out, const int32_t *inp, const flo
 // summed in position order and stored at part[first sorted index of the
 // segment].  Phase 2: each run of equal ids adds its segments (its first one
 // and one per chunk boundary inside the run, in order) to the id's row.  No
-// run is walked by one thread, so the cost does not grow with the longest run.
-constexpr int ENC_CHUNK = 64;
+// thread adds a run's rows one by one: phase 1 is one round of loads per
+// chunk, phase 2 one per ENC_RUN_BATCH chunks of a run.
+constexpr int ENC_CHUNK = 16;  // a chunk's rows are all requested at once
+constexpr int ENC_RUN_BATCH = 8;  // chunk boundaries of a run examined together in phase 2
 
 __global__ __launch_bounds__(64) void encoder_backward_segments_kernel(floatx4 *part, const float *dout,
                                                                         const int32_t *inp, const int32_t *order,
@@ -191,20 +193,17 @@ __global__ __launch_bounds__(64) void encoder_backward_segments_kernel(floatx4 *
     const floatx4 *src = (const floatx4 *)dout + c4;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     int seg = 0;
-    for (int e0 = 0; e0 < n; e0 += 8) {
-        floatx4 v[8];
+    floatx4 v[ENC_CHUNK];
 #pragma unroll
-        for (int u = 0; u < 8; u++) v[u] = e0 + u < n ? src[(long long)pos[e0 + u] * C4] : floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < ENC_CHUNK; e++) v[e] = e < n ? src[(long long)pos[e] * C4] : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int e = e0 + u;
-            if (e < n) {
-                acc += v[u];
-                if (ids[e + 1] != ids[e]) {
-                    part[(long long)(base + seg) * C4 + c4] = acc;
-                    acc = floatx4{0.f, 0.f, 0.f, 0.f};
-                    seg = e + 1;
-                }
+    for (int e = 0; e < ENC_CHUNK; e++) {
+        if (e < n) {
+            acc += v[e];
+            if (ids[e + 1] != ids[e]) {
+                part[(long long)(base + seg) * C4 + c4] = acc;
+                acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                seg = e + 1;
             }
         }
     }
@@ -219,8 +218,30 @@ __global__ __launch_bounds__(64) void encoder_backward_runs_kernel(float *dwte, 
     const int C4 = C / 4, c4 = blockIdx.y * 64 + threadIdx.x;
     if (c4 >= C4) return;
     floatx4 acc = part[(long long)i * C4 + c4];
-    for (int k = (i / ENC_CHUNK + 1) * ENC_CHUNK; k < BT && clamp_id(inp[order[k]], V) == id; k += ENC_CHUNK)
-        acc += part[(long long)k * C4 + c4];
+    // The run's later segments start at the chunk boundaries inside it.  The
+    // ids and segment sums at ENC_RUN_BATCH boundaries are requested together
+    // (every chunk start below BT holds a segment sum), then added in order
+    // while the id still matches.
+    int k = (i / ENC_CHUNK + 1) * ENC_CHUNK;
+    bool more = k < BT;
+    while (more) {
+        int pk[ENC_RUN_BATCH];
+        floatx4 v[ENC_RUN_BATCH];
+#pragma unroll
+        for (int u = 0; u < ENC_RUN_BATCH; u++) {
+            const int kk = k + u * ENC_CHUNK;
+            pk[u] = kk < BT ? order[kk] : 0;
+            v[u] = kk < BT ? part[(long long)kk * C4 + c4] : floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < ENC_RUN_BATCH; u++) {
+            const int kk = k + u * ENC_CHUNK;
+            more = more && kk < BT && clamp_id(inp[pk[u]], V) == id;
+            if (more) acc += v[u];
+        }
+        k += ENC_RUN_BATCH * ENC_CHUNK;
+        more = more && k < BT;
+    }
     floatx4 *dst = (floatx4 *)(dwte + (long long)id * C) + c4;
     *dst = *dst + acc;
 }
@@ -289,7 +310,10 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(float *out, floa
 
 constexpr int COL_CHUNK = 16;  // rows per LayerNorm-backward block (and per partial row)
 
-// LayerNorm backward.  Block b takes rows [16b, 16b+16) with nw = 4 or 8
+// whether nw wavefronts' column sums of dw and db fit in 64 KB of LDS together
+__host__ __device__ inline bool ln_bwd_one_pass(int nw, int C) { return (size_t)nw * 2 * C * sizeof(float) <= 65536; }
+
+// LayerNorm backward.  Block b takes rows [16b, 16b+16) with nw = 8
 // wavefronts (blockDim.x / 64), wavefront w the rows 16b + w + nw k, one at a
 // time with the next row's loads issued before the current row's reductions:
 //   xhat = (x - mean) rstd, g = dy * w,
@@ -302,7 +326,7 @@ __global__ __launch_bounds__(512) void layernorm_backward_kernel(float *dinp, fl
                                                                  const float *inp, const float *w,
                                                                  const float *mean, const float *rstd, int N, int C,
                                                                  int accumulate) {
-    extern __shared__ floatx4 lds4[];  // [nw][2C/4]
+    extern __shared__ floatx4 lds4[];  // [nw][2C/4] or [nw][C/4]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int C4 = C / 4;
     floatx4 wv[NV], dwacc[NV], dbacc[NV];
@@ -313,80 +337,155 @@ __global__ __launch_bounds__(512) void layernorm_backward_kernel(float *dinp, fl
         dwacc[i] = dbacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     const int r0 = blockIdx.x * COL_CHUNK + wave;
-    floatx4 xn[NV], dn[NV], on[NV] = {};
-    float mun = 0.f, rsn = 0.f;
-    // The loads read only valid addresses (a row past the end is never used,
-    // lanes past the row end read its last float4) and the zeros of lanes
-    // past the row end are applied when the row is used, so the next row's
-    // loads stay in flight while the current row is reduced.
-    auto fetch = [&](int row) {
-        const int rr = row < N ? row : N - 1;
-        const floatx4 *x = (const floatx4 *)(inp + (long long)rr * C);
-        const floatx4 *dy = (const floatx4 *)(dout + (long long)rr * C);
-        const floatx4 *dx = (const floatx4 *)(dinp + (long long)rr * C);
+    if constexpr (NV <= 4) {
+        floatx4 xn[NV], dn[NV], on[NV] = {};
+        float mun = 0.f, rsn = 0.f;
+        // The loads read only valid addresses (a row past the end is never used,
+        // lanes past the row end read its last float4) and the zeros of lanes
+        // past the row end are applied when the row is used, so the next row's
+        // loads stay in flight while the current row is reduced.
+        auto fetch = [&](int row) {
+            const int rr = row < N ? row : N - 1;
+            const floatx4 *x = (const floatx4 *)(inp + (long long)rr * C);
+            const floatx4 *dy = (const floatx4 *)(dout + (long long)rr * C);
+            const floatx4 *dx = (const floatx4 *)(dinp + (long long)rr * C);
 #pragma unroll
-        for (int i = 0; i < NV; i++) {
-            const int k = lane + 64 * i, kc = k < C4 ? k : C4 - 1;
-            xn[i] = x[kc];
-            dn[i] = dy[kc];
-            if (accumulate) on[i] = dx[kc];
-        }
-        mun = mean[rr];
-        rsn = rstd[rr];
-    };
-    fetch(r0);
-    for (int k = 0; k < COL_CHUNK / nw; k++) {
-        const int row = r0 + nw * k;
-        if (row >= N) break;
-        floatx4 xc[NV], dc[NV], oc[NV];
-        const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < NV; i++) {
+                const int k = lane + 64 * i, kc = k < C4 ? k : C4 - 1;
+                xn[i] = x[kc];
+                dn[i] = dy[kc];
+                if (accumulate) on[i] = dx[kc];
+            }
+            mun = mean[rr];
+            rsn = rstd[rr];
+        };
+        fetch(r0);
+        for (int k = 0; k < COL_CHUNK / nw; k++) {
+            const int row = r0 + nw * k;
+            if (row >= N) break;
+            floatx4 xc[NV], dc[NV], oc[NV];
+            const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < NV; i++) {
-            const bool kk = lane + 64 * i < C4;
-            xc[i] = kk ? xn[i] : z4;
-            dc[i] = kk ? dn[i] : z4;
-            oc[i] = (kk && accumulate) ? on[i] : z4;
-        }
-        const float mu = mun, rs = rsn;
-        // prefetch the next row while reducing this one (wide rows: registers
-        // would spill, so they load each row when it is reached)
-        constexpr bool kPrefetch = NV <= 4;
-        if (kPrefetch && k + 1 < COL_CHUNK / nw) fetch(row + nw);
-        floatx4 xh[NV], g[NV];
-        float sg = 0.f, sgx = 0.f;
+            for (int i = 0; i < NV; i++) {
+                const bool kk = lane + 64 * i < C4;
+                xc[i] = kk ? xn[i] : z4;
+                dc[i] = kk ? dn[i] : z4;
+                oc[i] = (kk && accumulate) ? on[i] : z4;
+            }
+            const float mu = mun, rs = rsn;
+            // prefetch the next row while reducing this one (wide rows: registers
+            // would spill, so they load each row when it is reached)
+            constexpr bool kPrefetch = NV <= 4;
+            if (kPrefetch && k + 1 < COL_CHUNK / nw) fetch(row + nw);
+            floatx4 xh[NV], g[NV];
+            float sg = 0.f, sgx = 0.f;
 #pragma unroll
-        for (int i = 0; i < NV; i++) {
-            xh[i] = (xc[i] - mu) * rs;
-            g[i] = dc[i] * wv[i];
-            const floatx4 gx = g[i] * xh[i];
-            sg += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
-            sgx += (gx[0] + gx[1]) + (gx[2] + gx[3]);
-            dwacc[i] += dc[i] * xh[i];
-            dbacc[i] += dc[i];
-        }
-        const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
-        floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
+            for (int i = 0; i < NV; i++) {
+                xh[i] = (xc[i] - mu) * rs;
+                g[i] = dc[i] * wv[i];
+                const floatx4 gx = g[i] * xh[i];
+                sg += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
+                sgx += (gx[0] + gx[1]) + (gx[2] + gx[3]);
+                dwacc[i] += dc[i] * xh[i];
+                dbacc[i] += dc[i];
+            }
+            const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+            floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
 #pragma unroll
-        for (int i = 0; i < NV; i++) {
-            const int kk = lane + 64 * i;
-            if (kk < C4) dx[kk] = oc[i] + rs * (g[i] - mg - xh[i] * mgx);
+            for (int i = 0; i < NV; i++) {
+                const int kk = lane + 64 * i;
+                if (kk < C4) dx[kk] = oc[i] + rs * (g[i] - mg - xh[i] * mgx);
+            }
+            if (!kPrefetch && k + 1 < COL_CHUNK / nw) fetch(row + nw);
         }
-        if (!kPrefetch && k + 1 < COL_CHUNK / nw) fetch(row + nw);
+    } else {
+        // Wide rows: only x and dy of the next row are prefetched, the
+        // affine weight is read again per row (from cache) and dx is read
+        // where it is written, so that the row state fits without spills.
+        floatx4 xn[NV], dn[NV];
+        float mun = 0.f, rsn = 0.f;
+        auto fetch = [&](int row) {
+            const int rr = row < N ? row : N - 1;
+            const floatx4 *x = (const floatx4 *)(inp + (long long)rr * C);
+            const floatx4 *dy = (const floatx4 *)(dout + (long long)rr * C);
+#pragma unroll
+            for (int i = 0; i < NV; i++) {
+                const int k = lane + 64 * i, kc = k < C4 ? k : C4 - 1;
+                xn[i] = x[kc];
+                dn[i] = dy[kc];
+            }
+            mun = mean[rr];
+            rsn = rstd[rr];
+        };
+        fetch(r0);
+        for (int k = 0; k < COL_CHUNK / nw; k++) {
+            const int row = r0 + nw * k;
+            if (row >= N) break;
+            const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+            floatx4 xh[NV], g[NV];
+            const float mu = mun, rs = rsn;
+            float sg = 0.f, sgx = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; i++) {
+                const int kk = lane + 64 * i;
+                const bool in = kk < C4;
+                const floatx4 d = in ? dn[i] : z4;
+                xh[i] = in ? (xn[i] - mu) * rs : z4;
+                g[i] = d * (in ? ((const floatx4 *)w)[kk] : z4);
+                const floatx4 gx = g[i] * xh[i];
+                sg += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
+                sgx += (gx[0] + gx[1]) + (gx[2] + gx[3]);
+                dwacc[i] += d * xh[i];
+                dbacc[i] += d;
+            }
+            if (k + 1 < COL_CHUNK / nw) fetch(row + nw);
+            const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+            floatx4 *dx = (floatx4 *)(dinp + (long long)row * C);
+#pragma unroll
+            for (int i = 0; i < NV; i++) {
+                const int kk = lane + 64 * i;
+                if (kk < C4) {
+                    const floatx4 v = rs * (g[i] - mg - xh[i] * mgx);
+                    dx[kk] = accumulate ? dx[kk] + v : v;
+                }
+            }
+        }
     }
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int k = lane + 64 * i;
-        if (k < C4) {
-            lds4[wave * 2 * C4 + k] = dwacc[i];
-            lds4[wave * 2 * C4 + C4 + k] = dbacc[i];
-        }
-    }
-    __syncthreads();
+    // the wavefronts' column sums are combined in a fixed order through LDS:
+    // [nw][2C] at once where that fits in 64 KB, else in two passes through
+    // [nw][C] (the dw half, then the db half)
     floatx4 *out = (floatx4 *)(partial + (long long)blockIdx.x * 2 * C);
-    for (int c = threadIdx.x; c < 2 * C4; c += blockDim.x) {
-        floatx4 t = lds4[c];
-        for (int q = 1; q < nw; q++) t += lds4[q * 2 * C4 + c];
-        out[c] = t;
+    if (ln_bwd_one_pass(nw, C)) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int k = lane + 64 * i;
+            if (k < C4) {
+                lds4[wave * 2 * C4 + k] = dwacc[i];
+                lds4[wave * 2 * C4 + C4 + k] = dbacc[i];
+            }
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < 2 * C4; c += blockDim.x) {
+            floatx4 t = lds4[c];
+            for (int q = 1; q < nw; q++) t += lds4[q * 2 * C4 + c];
+            out[c] = t;
+        }
+        return;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+        if (half) __syncthreads();  // the dw half has been read
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int k = lane + 64 * i;
+            if (k < C4) lds4[wave * C4 + k] = half ? dbacc[i] : dwacc[i];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < C4; c += blockDim.x) {
+            floatx4 t = lds4[c];
+            for (int q = 1; q < nw; q++) t += lds4[q * C4 + c];
+            out[half * C4 + c] = t;
+        }
     }
 }
 
@@ -472,10 +571,18 @@ __global__ __launch_bounds__(256) void sum_layers_kernel(floatx4 *dst1, const fl
 // dst (n floats) and dst2 (n2 floats) += the column sums of partial rows of
 // n + n2 floats (fixed order): used for the [dw | db] partials of LayerNorm.
 // sum of src[p * ld] over p = p0, p0 + 16, ... < P, added in that order; the
-// loads are issued eight at a time so that their latencies overlap.
+// loads are issued sixteen (then eight) at a time so that their latencies
+// overlap.
 __device__ __forceinline__ floatx4 sum_rows_strided(const floatx4 *src, int p0, int P, size_t ld) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     int p = p0;
+    for (; p + 16 * 15 < P; p += 16 * 16) {
+        floatx4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) v[u] = src[(size_t)(p + 16 * u) * ld];
+#pragma unroll
+        for (int u = 0; u < 16; u++) acc += v[u];
+    }
     for (; p + 16 * 7 < P; p += 16 * 8) {
         floatx4 v[8];
 #pragma unroll
@@ -760,17 +867,30 @@ __global__ __launch_bounds__(1024) void crossentropy_reg_kernel(float *logits, f
     }
 }
 
-__global__ __launch_bounds__(256) void mean_kernel(float *loss, const float *losses, int n) {
-    __shared__ float part[256];
-    float acc = 0.f;
-    for (int i = threadIdx.x; i < n; i += 256) acc += losses[i];
-    part[threadIdx.x] = acc;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-        __syncthreads();
+// loss[0] = mean of losses[0..n): 1024 threads, four loads in flight per
+// thread per round, wavefront sums by lane exchanges, then the 16 wavefront
+// sums in order.
+__global__ __launch_bounds__(1024) void mean_kernel(float *loss, const float *losses, int n) {
+    __shared__ float part[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int i = tid; i < n; i += 4096) {
+        const float v0 = losses[i];
+        const float v1 = i + 1024 < n ? losses[i + 1024] : 0.f;
+        const float v2 = i + 2048 < n ? losses[i + 2048] : 0.f;
+        const float v3 = i + 3072 < n ? losses[i + 3072] : 0.f;
+        a0 += v0;
+        a1 += v1;
+        a2 += v2;
+        a3 += v3;
     }
-    if (threadIdx.x == 0) loss[0] = part[0] / n;
+    const float w = wave_sum((a0 + a1) + (a2 + a3));
+    if (lane == 0) part[wave] = w;
+    __syncthreads();
+    if (wave == 0) {
+        const float t = wave_sum(lane < 16 ? part[lane] : 0.f);
+        if (lane == 0) loss[0] = t / n;
+    }
 }
 
 __global__ __launch_bounds__(256) void gelu_forward_kernel(floatx4 *out, const floatx4 *inp, size_t n4) {
@@ -1007,10 +1127,11 @@ hipError_t k_layernorm_backward(float *dinp, float *dw, float *db, float *partia
     if (C % 4 || C > 2048) return hipErrorInvalidValue;
     int nv = (C / 4 + 63) / 64;
     const int P = ln_partials(N);
-    // eight wavefronts per block where their column sums fit in 64 KB of LDS
-    // (twice the rows in flight per CU), else four
-    const int nw = (size_t)8 * 2 * C * sizeof(float) <= 65536 ? 8 : 4;
-    const size_t lds = (size_t)nw * 2 * C * sizeof(float);
+    // eight wavefronts per block (two rows each); their column sums pass
+    // through nw x 2C floats of LDS, or nw x C in two passes (C <= 2048: at
+    // most 64 KB)
+    const int nw = 8;
+    const size_t lds = (size_t)nw * (ln_bwd_one_pass(nw, C) ? 2 : 1) * C * sizeof(float);
     if (nv < 1 || nv > 8) return hipErrorInvalidValue;
     if (AuditSink *au = audit_sink()) {
         // rows are clamped to N - 1; block x writes partial row x (P rows of 2C)
@@ -1157,7 +1278,7 @@ hipError_t k_mean(float *loss, const float *losses, int n, hipStream_t s) {
         audit(au, "mean_kernel", "loss", loss, 1, true);
         return hipSuccess;
     }
-    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, loss, losses, n);
+    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, loss, losses, n);
     return hipGetLastError();
 }
 
