@@ -484,8 +484,9 @@ __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_fold_kernel(GemmArgs p)
 // partial sums) and all of row tile i into C.  fold_split_sum_kernel then
 // adds the partials into the row tiles j >= tiles_m / 2.  Same result as one
 // workgroup per pair up to the order of two partial sums; twice the
-// workgroups for products with few row tiles.
-template <int BM, int BN, bool AK, bool BKC, int BK, int LB>
+// workgroups for products with few row tiles.  FULL: whole tiles and K a
+// whole number of slices (every range above is then whole slices too).
+template <int BM, int BN, bool AK, bool BKC, int BK, int LB, bool FULL>
 __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_fold_split_kernel(GemmArgs p, GemmArgs pp) {
     using L = TileLds<BM, BN, AK, BKC, BK>;
     __shared__ __attribute__((aligned(16))) float As[L::A];
@@ -498,10 +499,10 @@ __global__ __launch_bounds__(GEMM_THREADS, LB) void gemm_fold_split_kernel(GemmA
     const int tot = i == j ? kj : kj + ki;
     const int hk = min(kj, (tot / 2 + BK - 1) / BK * BK);
     if (s == 0) {
-        gemm_tile<BM, BN, AK, BKC, BK>(p, j, tn, blockIdx.z, As, Bs, 0, hk);
+        gemm_tile<BM, BN, AK, BKC, BK, FULL>(p, j, tn, blockIdx.z, As, Bs, 0, hk);
     } else {
-        gemm_tile<BM, BN, AK, BKC, BK>(pp, j, tn, blockIdx.z, As, Bs, hk, kj);
-        if (i != j) gemm_tile<BM, BN, AK, BKC, BK>(p, i, tn, blockIdx.z, As, Bs, 0, ki);
+        gemm_tile<BM, BN, AK, BKC, BK, FULL>(pp, j, tn, blockIdx.z, As, Bs, hk, kj);
+        if (i != j) gemm_tile<BM, BN, AK, BKC, BK, FULL>(p, i, tn, blockIdx.z, As, Bs, 0, ki);
     }
 }
 
@@ -581,6 +582,11 @@ void set_tiles(const GemmDesc &d, GemmArgs &a) {
 bool gemm_full(const GemmDesc &d, int bm, int bn, int bk) {
     return d.causal == 0 && d.M % bm == 0 && d.N % bn == 0 && d.K % bk == 0;
 }
+// the folded causal product's ranges are whole slices when its tiles are whole
+// and K is whole slices (row-tile ends are multiples of bm, itself of bk)
+bool fold_split_full(const GemmDesc &d, int bm, int bn, int bk) {
+    return d.M % bm == 0 && d.N % bn == 0 && d.K % bk == 0 && bm % bk == 0;
+}
 
 template <int BM, int BN, bool AKV, bool BKV, int BK, int LB>
 void launch_gemm_kernel(bool full, int prec, dim3 grid, hipStream_t stream, const GemmArgs &a) {
@@ -613,11 +619,13 @@ hipError_t launch_tile(const GemmDesc &d, const GemmArgs &a0, hipStream_t stream
         pp.sCi = (long long)d.M * d.N;
         pp.sCo = pp.sCi * d.nbi;
         dim3 g(2 * half * a.tiles_n, 1, (unsigned)nb);
-        if (d.a_kcontig && !d.b_kcontig)
-            hipLaunchKernelGGL((gemm_fold_split_kernel<BM, BN, true, false, BK, LB>), g, dim3(GEMM_THREADS), 0, stream,
-                               a, pp);
+        if (!d.a_kcontig || d.b_kcontig) return hipErrorInvalidValue;
+        if (fold_split_full(d, BM, BN, BK))
+            hipLaunchKernelGGL((gemm_fold_split_kernel<BM, BN, true, false, BK, LB, true>), g, dim3(GEMM_THREADS), 0,
+                               stream, a, pp);
         else
-            return hipErrorInvalidValue;
+            hipLaunchKernelGGL((gemm_fold_split_kernel<BM, BN, true, false, BK, LB, false>), g, dim3(GEMM_THREADS), 0,
+                               stream, a, pp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int m0 = a.tiles_m / 2 * BM;
@@ -853,10 +861,15 @@ const char *gemm_kernel_name(const GemmDesc &d) {
     const int tile = resolve_tile(d);
     const int t = tile >= 1 && tile <= 4 ? tile - 1 : 0;
     const int l = d.a_kcontig ? (d.b_kcontig ? 0 : 1) : 2;
-    static const char *split_names[4] = {"gemm_fold_split_kernel<128, 128, true, false, 32, 3>",
-                                         "gemm_fold_split_kernel<128, 64, true, false, 32, 3>",
-                                         "gemm_fold_split_kernel<64, 64, true, false, 32, 3>",
-                                         "gemm_fold_split_kernel<64, 192, true, false, 32, 3>"};
+    static const char *split_names[4][2] = {
+        {"gemm_fold_split_kernel<128, 128, true, false, 32, 3, false>",
+         "gemm_fold_split_kernel<128, 128, true, false, 32, 3, true>"},
+        {"gemm_fold_split_kernel<128, 64, true, false, 32, 3, false>",
+         "gemm_fold_split_kernel<128, 64, true, false, 32, 3, true>"},
+        {"gemm_fold_split_kernel<64, 64, true, false, 32, 3, false>",
+         "gemm_fold_split_kernel<64, 64, true, false, 32, 3, true>"},
+        {"gemm_fold_split_kernel<64, 192, true, false, 32, 3, false>",
+         "gemm_fold_split_kernel<64, 192, true, false, 32, 3, true>"}};
     static const char *bf16_names[4][3][2] = {
         {{"gemm_bf16_kernel<128, 128, true, true, 32, 3, false>", "gemm_bf16_kernel<128, 128, true, true, 32, 3, true>"},
          {"gemm_bf16_kernel<128, 128, true, false, 32, 3, false>", "gemm_bf16_kernel<128, 128, true, false, 32, 3, true>"},
@@ -874,7 +887,8 @@ const char *gemm_kernel_name(const GemmDesc &d) {
           "gemm_bf16_kernel<64, 192, false, false, 32, 3, true>"}}};
     if (d.prec) return bf16_names[t][l][gemm_full(d, bm[t], bn[t], 32) ? 1 : 0];
     // causal products with a growing or shrinking K range run with folded row tiles
-    if (d.part && d.causal == CAUSAL_KEND && d.M > bm[t] && l == 1) return split_names[t];
+    if (d.part && d.causal == CAUSAL_KEND && d.M > bm[t] && l == 1)
+        return split_names[t][fold_split_full(d, bm[t], bn[t], 32) ? 1 : 0];
     if ((d.causal == CAUSAL_KEND || d.causal == CAUSAL_KSTART) && d.M > bm[t] && l > 0) return fold_names[t][l];
     return names[t][l][gemm_full(d, bm[t], bn[t], 32) ? 1 : 0];
 }
