@@ -593,12 +593,15 @@ hipError_t copy_ids(int32_t *dst, const int32_t *src, int n, hipStream_t s) {
 // 6400).  There 128 x 64 tiles make 800 workgroups for 1024 resident slots,
 // so a quarter of the CUs hold a fourth tile while the rest hold three;
 // 64 x 64 tiles make 1600, six or seven per CU (9.48 against 10.44 and
-// 36.52 against 40.00 ms per step).
+// 36.52 against 40.00 ms per step).  And its MLP input projection (4096 x
+// 6400 outputs), where 128 x 64 tiles beat the model's 64 x 64 (32.9
+// against 34.2 ms); for the QKV projection the model's 128 x 64 stayed
+// faster than 64 x 64 (25.3 against 26.2 ms).
 int forward_tile(int N, int OC, int K) {
     struct Hint {
         int N, OC, K, tile;
     };
-    static const Hint kHints[] = {{4096, 1600, 1600, 3}, {4096, 1600, 6400, 3}};
+    static const Hint kHints[] = {{4096, 1600, 1600, 3}, {4096, 1600, 6400, 3}, {4096, 6400, 1600, 2}};
     for (const Hint &h : kHints)
         if (h.N == N && h.OC == OC && h.K == K) return h.tile;
     return plan_gemm(N, OC, K, 1, false).tile;

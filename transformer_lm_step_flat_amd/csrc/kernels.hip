@@ -171,7 +171,8 @@ __global__ void encoder_forward_kernel(float *out, const int32_t *inp, const flo
 // segment].  Phase 2: each run of equal ids adds its segments (its first one
 // and one per chunk boundary inside the run, in order) to the id's row.  No
 // thread adds a run's rows one by one: phase 1 is one round of loads per
-// chunk, phase 2 one per ENC_RUN_BATCH chunks of a run.
+// chunk, phase 2 three per ENC_RUN_BATCH chunks of a run (positions, ids,
+// segment sums).
 constexpr int ENC_CHUNK = 16;  // a chunk's rows are all requested at once
 constexpr int ENC_RUN_BATCH = 8;  // chunk boundaries of a run examined together in phase 2
 
@@ -219,28 +220,34 @@ __global__ __launch_bounds__(64) void encoder_backward_runs_kernel(float *dwte, 
     if (c4 >= C4) return;
     floatx4 acc = part[(long long)i * C4 + c4];
     // The run's later segments start at the chunk boundaries inside it.  The
-    // ids and segment sums at ENC_RUN_BATCH boundaries are requested together
-    // (every chunk start below BT holds a segment sum), then added in order
-    // while the id still matches.
+    // ids at ENC_RUN_BATCH boundaries are requested together; the segment
+    // sums of the boundaries still inside the run (every chunk start below
+    // BT holds one) are then requested together and added in order.
     int k = (i / ENC_CHUNK + 1) * ENC_CHUNK;
-    bool more = k < BT;
-    while (more) {
+    while (k < BT) {
         int pk[ENC_RUN_BATCH];
-        floatx4 v[ENC_RUN_BATCH];
 #pragma unroll
         for (int u = 0; u < ENC_RUN_BATCH; u++) {
             const int kk = k + u * ENC_CHUNK;
             pk[u] = kk < BT ? order[kk] : 0;
-            v[u] = kk < BT ? part[(long long)kk * C4 + c4] : floatx4{0.f, 0.f, 0.f, 0.f};
         }
+        int n = 0;  // leading boundaries of the batch inside the run
+        bool in = true;
 #pragma unroll
         for (int u = 0; u < ENC_RUN_BATCH; u++) {
             const int kk = k + u * ENC_CHUNK;
-            more = more && kk < BT && clamp_id(inp[pk[u]], V) == id;
-            if (more) acc += v[u];
+            in = in && kk < BT && clamp_id(inp[pk[u]], V) == id;
+            n += in ? 1 : 0;
         }
+        floatx4 v[ENC_RUN_BATCH];
+#pragma unroll
+        for (int u = 0; u < ENC_RUN_BATCH; u++)
+            v[u] = u < n ? part[(long long)(k + u * ENC_CHUNK) * C4 + c4] : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < ENC_RUN_BATCH; u++)
+            if (u < n) acc += v[u];
+        if (n < ENC_RUN_BATCH) break;
         k += ENC_RUN_BATCH * ENC_CHUNK;
-        more = more && k < BT;
     }
     floatx4 *dst = (floatx4 *)(dwte + (long long)id * C) + c4;
     *dst = *dst + acc;
