@@ -227,7 +227,11 @@ PairPlan plan_pair(int N, int K, int OC, bool split_dinp) {
     // beat the 128 x 128 tiles the model prefers (3.52 against 4.05 ms per
     // step at B = 4, 13.60 against 13.91 at B = 16); the MLP input
     // projection of GPT-2 XL, where 64 x 64 tiles (4100 workgroups, six per
-    // CU) beat the model's 128 x 64 (63.2 against 73.9 ms per step).  At the
+    // CU) beat the model's 128 x 64 (63.2 against 73.9 ms per step); at
+    // 124M B = 16, 128 x 64 tiles with four K splits of the weight gradient
+    // for the MLP input and QKV projections and 64 x 64 tiles for the
+    // attention projection (14.63 against 15.47, 10.98 against 11.09 on a
+    // box 3 % slower, 3.74 against 3.83 ms per step).  At the
     // 124M B = 4 layer shapes the model's plans stayed faster than the
     // alternatives tried (64 x 64 for fc: 3.83 against 3.72 ms; 128 x 64
     // for qkv: 3.12 against 2.93; 64 x 64 for attproj: 1.06 against 1.02).
@@ -238,7 +242,10 @@ PairPlan plan_pair(int N, int K, int OC, bool split_dinp) {
     };
     static const Hint kHints[] = {{4096, 3072, 768, false, {true, 2, 2, 1}},
                                   {16384, 3072, 768, false, {true, 2, 2, 1}},
-                                  {4096, 1600, 6400, false, {true, 3, 1, 1}}};
+                                  {4096, 1600, 6400, false, {true, 3, 1, 1}},
+                                  {16384, 768, 3072, false, {true, 2, 4, 1}},
+                                  {16384, 768, 768, false, {true, 3, 4, 1}},
+                                  {16384, 768, 2304, false, {true, 2, 4, 1}}};
     for (const Hint &h : kHints)
         if (h.N == N && h.K == K && h.OC == OC && h.split_dinp == split_dinp) return cache[key] = h.plan;
     double best = 1e30;
