@@ -171,8 +171,8 @@ __global__ void encoder_forward_kernel(float *out, const int32_t *inp, const flo
 // segment].  Phase 2: each run of equal ids adds its segments (its first one
 // and one per chunk boundary inside the run, in order) to the id's row.  No
 // thread adds a run's rows one by one: phase 1 is one round of loads per
-// chunk, phase 2 three per ENC_RUN_BATCH chunks of a run (positions, ids,
-// segment sums).
+// chunk, phase 2 three per ENC_RUN_BATCH chunks of a long run (positions,
+// ids, segment sums).
 constexpr int ENC_CHUNK = 16;  // a chunk's rows are all requested at once
 constexpr int ENC_RUN_BATCH = 8;  // chunk boundaries of a run examined together in phase 2
 
@@ -210,20 +210,33 @@ __global__ __launch_bounds__(64) void encoder_backward_segments_kernel(floatx4 *
     }
 }
 
+// (one sorted position per workgroup: the position, its id and the run's
+// boundaries are the same for the whole wavefront, so their loads are
+// scalar loads; most positions are not the first of their run and end
+// after two of them)
 __global__ __launch_bounds__(64) void encoder_backward_runs_kernel(float *dwte, const floatx4 *part,
                                                                     const int32_t *inp, const int32_t *order, int BT,
                                                                     int C, int V) {
     const int i = blockIdx.x;
-    const int id = clamp_id(inp[order[i]], V);
-    if (i > 0 && clamp_id(inp[order[i - 1]], V) == id) return;  // not the first entry of its run
+    // (loads without short-circuit conditions, so that they issue together)
+    const int pc = order[i], pp = order[i > 0 ? i - 1 : 0];
+    const int id = clamp_id(inp[pc], V), idp = clamp_id(inp[pp], V);
+    if (i > 0 && idp == id) return;  // not the first entry of its run
     const int C4 = C / 4, c4 = blockIdx.y * 64 + threadIdx.x;
     if (c4 >= C4) return;
     floatx4 acc = part[(long long)i * C4 + c4];
-    // The run's later segments start at the chunk boundaries inside it.  The
-    // ids at ENC_RUN_BATCH boundaries are requested together; the segment
-    // sums of the boundaries still inside the run (every chunk start below
-    // BT holds one) are then requested together and added in order.
+    // The run's later segments start at the chunk boundaries inside it (every
+    // chunk start below BT holds a segment sum).  The first boundary is
+    // examined alone: most runs end before it.  Beyond it the ids at
+    // ENC_RUN_BATCH boundaries are requested together, then the segment sums
+    // of those still inside the run, added in order.
     int k = (i / ENC_CHUNK + 1) * ENC_CHUNK;
+    if (k < BT && clamp_id(inp[order[k]], V) == id) {
+        acc += part[(long long)k * C4 + c4];
+        k += ENC_CHUNK;
+    } else {
+        k = BT;
+    }
     while (k < BT) {
         int pk[ENC_RUN_BATCH];
 #pragma unroll
@@ -231,18 +244,23 @@ __global__ __launch_bounds__(64) void encoder_backward_runs_kernel(float *dwte, 
             const int kk = k + u * ENC_CHUNK;
             pk[u] = kk < BT ? order[kk] : 0;
         }
+        int idu[ENC_RUN_BATCH];
+#pragma unroll
+        for (int u = 0; u < ENC_RUN_BATCH; u++) idu[u] = clamp_id(inp[pk[u]], V);
         int n = 0;  // leading boundaries of the batch inside the run
         bool in = true;
 #pragma unroll
         for (int u = 0; u < ENC_RUN_BATCH; u++) {
-            const int kk = k + u * ENC_CHUNK;
-            in = in && kk < BT && clamp_id(inp[pk[u]], V) == id;
+            in = in & (k + u * ENC_CHUNK < BT) & (idu[u] == id);
             n += in ? 1 : 0;
         }
+        if (n == 0) break;
+        // (indices clamped to the last boundary inside the run: every load is
+        // valid and they issue together; only the first n are added)
         floatx4 v[ENC_RUN_BATCH];
 #pragma unroll
         for (int u = 0; u < ENC_RUN_BATCH; u++)
-            v[u] = u < n ? part[(long long)(k + u * ENC_CHUNK) * C4 + c4] : floatx4{0.f, 0.f, 0.f, 0.f};
+            v[u] = part[(long long)(k + min(u, n - 1) * ENC_CHUNK) * C4 + c4];
 #pragma unroll
         for (int u = 0; u < ENC_RUN_BATCH; u++)
             if (u < n) acc += v[u];
