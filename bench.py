@@ -205,7 +205,9 @@ def pmc_summary(fetch_csv: str, write_csv: str, steps: int, copy_mib: int, comma
 def kt_summary(stats_csv: str, command: str, config: str):
     """Summarise a rocprofv3 --kernel-trace --stats run of this script
     (its kernel_stats.csv): per kernel, launches and average duration.
-    Writes Markdown to stdout and the per-kernel averages to KTRACE_FILE."""
+    Writes Markdown to stdout and the per-kernel averages to KTRACE_FILE (the
+    headline configuration, whose figures the bench line uses) or, for another
+    configuration, to profiles/kernel_trace_<workload>.json."""
     import csv
     rows = []
     for r in csv.DictReader(open(stats_csv)):
@@ -222,9 +224,12 @@ def kt_summary(stats_csv: str, command: str, config: str):
     out = {"config": config, "sources_sha256": sources_sha256(), "command": command,
            "kernels": {name: {"launches": n, "avg_ms": avg, "min_ms": mn, "max_ms": mx}
                        for name, n, tot, avg, mn, mx in rows}}
-    with open(KTRACE_FILE, "w") as fh:
+    names = {"124m_b16": "gpt2_124m_b16_t1024", "xl": "gpt2_xl_b4_t1024"}
+    path = KTRACE_FILE if config == "124m" else os.path.join(
+        ROOT, "profiles", f"kernel_trace_{names.get(config, config)}.json")
+    with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
-    print(f"\nPer-kernel averages written to {os.path.relpath(KTRACE_FILE, ROOT)}.")
+    print(f"\nPer-kernel averages written to {os.path.relpath(path, ROOT)}.")
 
 
 def sq_summary(sq_csv: str, command: str, config: str):
