@@ -83,6 +83,23 @@ def test_trace_summary_averages_and_gates_on_sources(bench, tmp_path, capsys):
     assert bench.traced_duration(PAIR, "124m") is None
 
 
+def test_trace_summary_of_another_workload_leaves_the_headline_figures(bench, tmp_path, monkeypatch, capsys):
+    with open(tmp_path / "stats.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writerow(["void (anonymous namespace)::adamw_kernel(float*)", 2, 1.6e7, 8.0e6, 7.9e6, 8.1e6, 100.0])
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "sources_sha256", lambda: "a" * 64)
+    os.makedirs(tmp_path / "profiles")
+    bench.kt_summary(str(tmp_path / "stats.csv"), "cmd", "xl")
+    capsys.readouterr()
+    with open(tmp_path / "profiles" / "kernel_trace_gpt2_xl_b4_t1024.json") as fh:
+        t = json.load(fh)
+    assert t["config"] == "xl" and t["kernels"]["adamw_kernel"]["avg_ms"] == pytest.approx(8.0)
+    assert not os.path.exists(tmp_path / "ktrace.json")  # the headline's summary is not written
+    assert bench.traced_duration("adamw_kernel", "xl") is None  # nor read for another workload
+
+
 def test_step_roofline_takes_each_site_at_its_slower_bound(bench):
     ms_flops, ms_bytes = 157.3e9, 8e9  # one ms at the fp32 matrix peak, one ms at the HBM peak
     sites = [dict(flops=2 * ms_flops, bytes=0.1 * ms_bytes),
